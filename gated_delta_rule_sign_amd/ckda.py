@@ -1,0 +1,231 @@
+"""Thin Python binding over libckda.so (see include/ckda.h).
+
+Argument marshalling only: checks dtypes / devices / contiguity, allocates
+outputs with torch (device memory), passes raw pointers and the current HIP
+stream.  Every step of the computation runs in the library's HIP kernels;
+there is no Python or CPU fallback.  If the library is missing or fails to
+load, every entry point raises ``CkdaError``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("CKDA_LIB", os.path.join(_HERE, "libckda.so"))
+
+CKDA_F32 = 0
+CKDA_BF16 = 1
+CHUNK = 64
+
+
+class CkdaError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libckda.so (raises CkdaError if it is missing or broken)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise CkdaError(f"libckda.so not found at {LIB_PATH}: build it with "
+                        "`python -m gated_delta_rule_sign_amd.build`")
+    try:
+        L = ctypes.CDLL(LIB_PATH)
+    except OSError as e:  # pragma: no cover - depends on the machine
+        raise CkdaError(f"cannot load {LIB_PATH}: {e}") from e
+    P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.ckda_abi_version.restype = I
+    L.ckda_status_string.argtypes = [I]
+    L.ckda_status_string.restype = ctypes.c_char_p
+    L.ckda_last_error.restype = ctypes.c_char_p
+    L.ckda_chunk_prep.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P]
+    L.ckda_chunk_prep.restype = I
+    L.ckda_fwd_workspace_bytes.argtypes = [I, I, I, I, I]
+    L.ckda_fwd_workspace_bytes.restype = S
+    L.ckda_fwd_chunked.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P, P]
+    L.ckda_fwd_chunked.restype = I
+    L.ckda_fwd_varlen.argtypes = [I, I, P, P, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P]
+    L.ckda_fwd_varlen.restype = I
+    L.ckda_decode_step.argtypes = [I, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P]
+    L.ckda_decode_step.restype = I
+    L.ckda_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
+    L.ckda_bwd_workspace_bytes.restype = S
+    L.ckda_bwd.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P,
+                           P, P, P, P, P, P, P, S, P]
+    L.ckda_bwd.restype = I
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        L = lib()
+        raise CkdaError(f"{L.ckda_status_string(status).decode()}: {L.ckda_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return CKDA_BF16
+    if t.dtype == torch.float32:
+        return CKDA_F32
+    raise CkdaError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _need(t: Optional[torch.Tensor], name: str, dtype=None, shape=None, device=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise CkdaError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise CkdaError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise CkdaError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise CkdaError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise CkdaError(f"{name} must be contiguous")
+
+
+def _token_inputs(q, k, v, g, s, beta, lead):
+    dt = q.dtype
+    DK, DV = q.shape[-1], v.shape[-1]
+    H = q.shape[-2]
+    dev = q.device
+    _need(q, "q", dt, lead + (H, DK))
+    _need(k, "k", dt, lead + (H, DK), dev)
+    _need(v, "v", dt, lead + (H, DV), dev)
+    _need(g, "g", torch.float32, lead + (H, DK), dev)
+    _need(s, "s", torch.int8, lead + (H, DK), dev)
+    _need(beta, "beta", torch.float32, lead + (H,), dev)
+    return _dtype_code(q), H, DK, DV, dev
+
+
+def chunk_prep(q, k, g, s):
+    """Gate / sign-fold prep of every 64-token chunk (ckda_chunk_prep).
+    Returns (b [B,T,H,DK] f32, p [B,T,H,DK] int8, qf, kf)."""
+    B, T, H, DK = q.shape
+    dt = _dtype_code(q)
+    _need(q, "q", q.dtype, (B, T, H, DK))
+    _need(k, "k", q.dtype, (B, T, H, DK), q.device)
+    _need(g, "g", torch.float32, (B, T, H, DK), q.device)
+    _need(s, "s", torch.int8, (B, T, H, DK), q.device)
+    b = torch.empty((B, T, H, DK), dtype=torch.float32, device=q.device)
+    p = torch.empty((B, T, H, DK), dtype=torch.int8, device=q.device)
+    qf = torch.empty_like(q)
+    kf = torch.empty_like(k)
+    _check(lib().ckda_chunk_prep(B, T, H, DK, dt, _ptr(q), _ptr(k), _ptr(g), _ptr(s), _ptr(b),
+                                 _ptr(p), _ptr(qf), _ptr(kf), _stream()))
+    return b, p, qf, kf
+
+
+def fwd(q, k, v, g, s, beta, scale: float = 1.0, h0=None, want_ht: bool = True,
+        want_ckpt: bool = False, o=None, ht=None, h_ckpt=None):
+    """Chunked forward (ckda_fwd_chunked).  Inputs [B,T,H,D]; returns
+    (o [B,T,H,DV] f32, ht [B,H,DK,DV] f32 or None, h_ckpt or None)."""
+    B, T = q.shape[0], q.shape[1]
+    dt, H, DK, DV, dev = _token_inputs(q, k, v, g, s, beta, (B, T))
+    _need(h0, "h0", torch.float32, (B, H, DK, DV), dev)
+    NT = (T + CHUNK - 1) // CHUNK
+    if o is None:
+        o = torch.empty((B, T, H, DV), dtype=torch.float32, device=dev)
+    _need(o, "o", torch.float32, (B, T, H, DV), dev)
+    if want_ht and ht is None:
+        ht = torch.empty((B, H, DK, DV), dtype=torch.float32, device=dev)
+    _need(ht, "ht", torch.float32, (B, H, DK, DV), dev)
+    if want_ckpt and h_ckpt is None:
+        h_ckpt = torch.empty((B, H, NT, DK, DV), dtype=torch.float32, device=dev)
+    _need(h_ckpt, "h_ckpt", torch.float32, (B, H, NT, DK, DV), dev)
+    _check(lib().ckda_fwd_chunked(B, T, H, DK, DV, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
+                                  _ptr(beta), float(scale), _ptr(h0), _ptr(o), _ptr(ht),
+                                  _ptr(h_ckpt), _stream()))
+    return o, ht, h_ckpt
+
+
+def fwd_varlen(q, k, v, g, s, beta, cu_seqlens, scale: float = 1.0, h0=None,
+               want_ht: bool = True, cu_seqlens_dev=None, o=None, ht=None):
+    """Packed-document forward (ckda_fwd_varlen).  q etc. are [T_total,H,D]
+    (a leading 1 is accepted); cu_seqlens is an int32 CPU tensor [N+1]."""
+    if q.dim() == 4:
+        q, k, v, g, s, beta = (x[0] for x in (q, k, v, g, s, beta))
+    Tt = q.shape[0]
+    dt, H, DK, DV, dev = _token_inputs(q, k, v, g, s, beta, (Tt,))
+    cu = cu_seqlens
+    if cu.is_cuda or cu.dtype != torch.int32 or not cu.is_contiguous():
+        raise CkdaError("cu_seqlens must be a contiguous int32 CPU tensor")
+    N = cu.numel() - 1
+    if cu_seqlens_dev is None:
+        cu_seqlens_dev = cu.to(dev)
+    _need(cu_seqlens_dev, "cu_seqlens_dev", torch.int32, (N + 1,), dev)
+    _need(h0, "h0", torch.float32, (N, H, DK, DV), dev)
+    if o is None:
+        o = torch.empty((Tt, H, DV), dtype=torch.float32, device=dev)
+    _need(o, "o", torch.float32, (Tt, H, DV), dev)
+    if want_ht and ht is None:
+        ht = torch.empty((N, H, DK, DV), dtype=torch.float32, device=dev)
+    _need(ht, "ht", torch.float32, (N, H, DK, DV), dev)
+    _check(lib().ckda_fwd_varlen(N, Tt, _ptr(cu), _ptr(cu_seqlens_dev), H, DK, DV, dt, _ptr(q),
+                                 _ptr(k), _ptr(v), _ptr(g), _ptr(s), _ptr(beta), float(scale),
+                                 _ptr(h0), _ptr(o), _ptr(ht), _stream()))
+    return o, ht
+
+
+def decode_step(q, k, v, g, s, beta, state, sign_prod, scale: float = 1.0, o=None):
+    """One recurrent step (ckda_decode_step); state [N,H,DK,DV] f32 and
+    sign_prod [N,H,DK] int8 are updated in place.  Returns o [N,H,DV] f32."""
+    N = q.shape[0]
+    dt, H, DK, DV, dev = _token_inputs(q, k, v, g, s, beta, (N,))
+    _need(state, "state", torch.float32, (N, H, DK, DV), dev)
+    _need(sign_prod, "sign_prod", torch.int8, (N, H, DK), dev)
+    if o is None:
+        o = torch.empty((N, H, DV), dtype=torch.float32, device=dev)
+    _need(o, "o", torch.float32, (N, H, DV), dev)
+    _check(lib().ckda_decode_step(N, H, DK, DV, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
+                                  _ptr(beta), float(scale), _ptr(state), _ptr(sign_prod), _ptr(o),
+                                  _stream()))
+    return o
+
+
+def bwd_workspace_bytes(B, T, H, DK, DV) -> int:
+    return int(lib().ckda_bwd_workspace_bytes(B, T, H, DK, DV))
+
+
+def bwd(q, k, v, g, s, beta, h_ckpt, do, scale: float = 1.0, h0=None, dht=None,
+        want_dh0: bool = True, workspace=None):
+    """Backward (ckda_bwd).  Returns dict dq, dk, dv, dg, dbeta, dh0 (f32)."""
+    B, T = q.shape[0], q.shape[1]
+    dt, H, DK, DV, dev = _token_inputs(q, k, v, g, s, beta, (B, T))
+    NT = (T + CHUNK - 1) // CHUNK
+    _need(h_ckpt, "h_ckpt", torch.float32, (B, H, NT, DK, DV), dev)
+    _need(do, "do", q.dtype, (B, T, H, DV), dev)
+    _need(h0, "h0", torch.float32, (B, H, DK, DV), dev)
+    _need(dht, "dht", torch.float32, (B, H, DK, DV), dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dq=torch.empty((B, T, H, DK), **f32), dk=torch.empty((B, T, H, DK), **f32),
+               dv=torch.empty((B, T, H, DV), **f32), dg=torch.empty((B, T, H, DK), **f32),
+               dbeta=torch.empty((B, T, H), **f32),
+               dh0=torch.empty((B, H, DK, DV), **f32) if want_dh0 else None)
+    need = bwd_workspace_bytes(B, T, H, DK, DV)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().ckda_bwd(B, T, H, DK, DV, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
+                          _ptr(beta), float(scale), _ptr(h0), _ptr(h_ckpt), _ptr(do), _ptr(dht),
+                          _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+                          _ptr(out["dbeta"]), _ptr(out["dh0"]), _ptr(workspace), wsb, _stream()))
+    return out

@@ -1,0 +1,49 @@
+// ckda_device.h -- small device helpers shared by the CKDA kernels (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ckda {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kChunk = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// element types of the token tensors
+// ---------------------------------------------------------------------------
+struct bf16_t { uint16_t bits; };
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// round-to-nearest-even float -> bf16 (hardware v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+    __bf16 h = static_cast<__bf16>(x);
+    return __builtin_bit_cast(uint16_t, h);
+}
+// two floats -> packed bf16 pair (lo in bits 0..15)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float load(const float* p, size_t i) { return p[i]; }
+    static __device__ __forceinline__ void store(float* p, size_t i, float x) { p[i] = x; }
+};
+template <> struct Elem<bf16_t> {
+    static __device__ __forceinline__ float load(const bf16_t* p, size_t i) { return bf16_to_f32(p[i].bits); }
+    static __device__ __forceinline__ void store(bf16_t* p, size_t i, float x) { p[i].bits = f32_to_bf16(x); }
+};
+
+// exp(x) through the hardware base-2 exponential; the argument is clamped so
+// that no infinity can be produced (exp2(126) is finite in fp32)
+__device__ __forceinline__ float exp2_clamped(float x2) {
+    return __builtin_amdgcn_exp2f(fminf(x2, 126.0f));
+}
+
+}  // namespace ckda

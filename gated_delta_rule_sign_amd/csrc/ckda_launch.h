@@ -1,0 +1,74 @@
+// ckda_launch.h -- host-side launcher interfaces between the C ABI layer and
+// the kernel translation units.  Arguments are validated by the caller.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ckda {
+
+struct DecodeArgs {
+    int N, H, DK, DV;
+    bool bf16;
+    const void *q, *k, *v;
+    const float* g;
+    const int8_t* s;
+    const float* beta;
+    float scale;
+    float* state;
+    int8_t* sign_prod;
+    float* o;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+struct PrepArgs {
+    int B, T, H, DK;
+    bool bf16;
+    const void *q, *k;
+    const float* g;
+    const int8_t* s;
+    float* b_out;
+    int8_t* p_out;
+    void *qf_out, *kf_out;
+};
+hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
+
+struct FwdArgs {
+    // equal-length mode: B sequences of T tokens; varlen mode: nchains docs
+    int B, T, H, DK, DV;
+    bool bf16;
+    const void *q, *k, *v;
+    const float* g;
+    const int8_t* s;
+    const float* beta;
+    float scale;
+    const float* h0;
+    float* o;
+    float* ht;
+    float* h_ckpt;
+    // varlen: document n covers tokens cu[n] .. cu[n+1]-1 (device pointer);
+    // nullptr selects the equal-length mode
+    const int32_t* cu;
+    int ndocs;
+};
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+
+struct BwdArgs {
+    int B, T, H, DK, DV;
+    bool bf16;
+    const void *q, *k, *v;
+    const float* g;
+    const int8_t* s;
+    const float* beta;
+    float scale;
+    const float* h0;
+    const float* h_ckpt;
+    const void* dout;
+    const float* dht;
+    float *dq, *dk, *dv, *dg, *dbeta, *dh0;
+    void* ws;
+};
+size_t bwd_workspace_bytes(int B, int T, int H, int DK, int DV);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+
+}  // namespace ckda

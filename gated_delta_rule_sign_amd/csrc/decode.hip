@@ -1,0 +1,135 @@
+// decode.hip -- one recurrent CKDA step for N independent sequences.
+//
+// Recurrent form of the recurrence (paper page, section 1: the models are
+// purely recurrent; model card "complex-kda-1.3B-100B": log-magnitude gate,
+// sign product pushed onto q and k).  The state is kept in the folded frame
+// St = Diag(P) S, so only |alpha| = exp(g) ever multiplies it:
+//
+//   P  <- P * s                       (running sign product, int8 +-1)
+//   kf  = P * k,  qf = P * q,  a = exp(g)
+//   x   = St^T (a * kf),  y = St^T (a * qf)        (one read of St)
+//   u   = beta * (v - x)
+//   o   = scale * (y + (kf . qf) u)
+//   St <- Diag(a) St + kf u^T                     (one write of St)
+//
+// Work split: one 256-thread workgroup per (sequence, head).  Thread t owns
+// value columns 4*(t % (DV/4)) .. +3 and a band of DK/RG rows, RG = 256/(DV/4)
+// row bands; partial column sums are combined through LDS.  Each state row
+// band is streamed with 16-byte loads/stores, a wave covering whole rows.
+#include "ckda_device.h"
+#include "ckda_launch.h"
+
+namespace ckda {
+
+template <typename Tin, int DK, int DV>
+__global__ void __launch_bounds__(256)
+decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
+                   const float* __restrict__ g, const int8_t* __restrict__ s,
+                   const float* __restrict__ beta, float scale, float* __restrict__ state,
+                   int8_t* __restrict__ sign_prod, float* __restrict__ o)
+{
+    constexpr int CG = DV / 4;          // column groups (4 columns each)
+    constexpr int RG = 256 / CG;        // row bands
+    constexpr int R = DK / RG;          // rows per thread
+    static_assert(CG * RG == 256 && R * RG == DK && R >= 1, "tile");
+
+    __shared__ float4 red_x[RG][CG];
+    __shared__ float4 red_y[RG][CG];
+    __shared__ float red_kq[RG];
+
+    const int nh = blockIdx.x;                   // n * H + h
+    const int t = threadIdx.x;
+    const int cg = t % CG;
+    const int rg = t / CG;
+    const int r0 = rg * R;
+
+    const size_t kbase = static_cast<size_t>(nh) * DK;
+    const size_t vbase = static_cast<size_t>(nh) * DV;
+    float4* st = reinterpret_cast<float4*>(state + static_cast<size_t>(nh) * DK * DV);
+
+    float a[R], kf[R];
+    float kq = 0.f;
+    float4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+    float4 S[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) S[i] = st[(r0 + i) * CG + cg];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int r = r0 + i;
+        const int p = static_cast<int>(sign_prod[kbase + r]) * static_cast<int>(s[kbase + r]);
+        if (cg == 0) sign_prod[kbase + r] = static_cast<int8_t>(p);
+        const float pf = static_cast<float>(p);
+        a[i] = __builtin_amdgcn_exp2f(g[kbase + r] * kLog2e);
+        kf[i] = pf * Elem<Tin>::load(k, kbase + r);
+        const float qf = pf * Elem<Tin>::load(q, kbase + r);
+        kq += kf[i] * qf;
+        const float ak = a[i] * kf[i];
+        const float aq = a[i] * qf;
+        x.x += ak * S[i].x; x.y += ak * S[i].y; x.z += ak * S[i].z; x.w += ak * S[i].w;
+        y.x += aq * S[i].x; y.y += aq * S[i].y; y.z += aq * S[i].z; y.w += aq * S[i].w;
+    }
+    red_x[rg][cg] = x;
+    red_y[rg][cg] = y;
+    if (cg == 0) red_kq[rg] = kq;
+    __syncthreads();
+    float4 X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
+    float KQ = 0.f;
+#pragma unroll
+    for (int j = 0; j < RG; ++j) {
+        const float4 a4 = red_x[j][cg], b4 = red_y[j][cg];
+        X.x += a4.x; X.y += a4.y; X.z += a4.z; X.w += a4.w;
+        Y.x += b4.x; Y.y += b4.y; Y.z += b4.z; Y.w += b4.w;
+        KQ += red_kq[j];
+    }
+    const float bt = beta[nh];
+    const int c0 = 4 * cg;
+    float4 u;
+    u.x = bt * (Elem<Tin>::load(v, vbase + c0 + 0) - X.x);
+    u.y = bt * (Elem<Tin>::load(v, vbase + c0 + 1) - X.y);
+    u.z = bt * (Elem<Tin>::load(v, vbase + c0 + 2) - X.z);
+    u.w = bt * (Elem<Tin>::load(v, vbase + c0 + 3) - X.w);
+    if (rg == 0) {
+        float4 ov;
+        ov.x = scale * (Y.x + KQ * u.x);
+        ov.y = scale * (Y.y + KQ * u.y);
+        ov.z = scale * (Y.z + KQ * u.z);
+        ov.w = scale * (Y.w + KQ * u.w);
+        reinterpret_cast<float4*>(o + vbase)[cg] = ov;
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        float4 n;
+        n.x = a[i] * S[i].x + kf[i] * u.x;
+        n.y = a[i] * S[i].y + kf[i] * u.y;
+        n.z = a[i] * S[i].z + kf[i] * u.z;
+        n.w = a[i] * S[i].w + kf[i] * u.w;
+        st[(r0 + i) * CG + cg] = n;
+    }
+}
+
+template <typename Tin, int DK, int DV>
+static hipError_t launch_decode_t(const DecodeArgs& A, hipStream_t stream) {
+    hipLaunchKernelGGL((decode_step_kernel<Tin, DK, DV>), dim3(A.N * A.H), dim3(256), 0, stream,
+                       static_cast<const Tin*>(A.q), static_cast<const Tin*>(A.k),
+                       static_cast<const Tin*>(A.v), A.g, A.s, A.beta, A.scale, A.state,
+                       A.sign_prod, A.o);
+    return hipGetLastError();
+}
+
+template <typename Tin>
+static hipError_t launch_decode_dt(const DecodeArgs& A, hipStream_t stream) {
+#define CKDA_DEC(DK_, DV_) \
+    if (A.DK == DK_ && A.DV == DV_) return launch_decode_t<Tin, DK_, DV_>(A, stream);
+    CKDA_DEC(32, 32) CKDA_DEC(32, 64) CKDA_DEC(32, 128)
+    CKDA_DEC(64, 32) CKDA_DEC(64, 64) CKDA_DEC(64, 128)
+    CKDA_DEC(128, 32) CKDA_DEC(128, 64) CKDA_DEC(128, 128)
+#undef CKDA_DEC
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const DecodeArgs& A, hipStream_t stream) {
+    if (A.N == 0 || A.H == 0) return hipSuccess;
+    return A.bf16 ? launch_decode_dt<bf16_t>(A, stream) : launch_decode_dt<float>(A, stream);
+}
+
+}  // namespace ckda

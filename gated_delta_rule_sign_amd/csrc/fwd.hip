@@ -1,0 +1,720 @@
+// fwd.hip -- chunked CKDA forward (equal-length and packed varlen) and the
+// standalone gate / sign-fold prep kernel.
+//
+// Method: KDA-style WY/UT chunk-wise form of the recurrence (Complex KDA paper
+// page, section 2 "Linear RNNs": DeltaNet/KDA admit WY-based chunk-wise
+// implementations; section 1: the kernels are a small change to KDA's) with
+// the signed gate carried as log-magnitude plus a sign product pushed onto q
+// and k ("complex-kda-1.3B-100B" model card).  Per chunk of 64 tokens, in the
+// chunk-local folded frame (sign product restarting at +1 each chunk):
+//
+//   b_r = sum_{i<=r} g_i,  P_r = prod_{i<=r} s_i,  qf = P q,  kf = P k
+//   A_ri = sum_c kf_rc kf_ic e^{b_rc - b_ic}  (i < r),  M_ri likewise with qf_r (i <= r)
+//   U = (I + Diag(beta) A)^{-1} Diag(beta) (V - (kf e^b) S)
+//   O = scale ((qf e^b) S + M U)
+//   S <- Diag(P_L e^{b_L}) S + Diag(P_L) (kf e^{b_L - b})^T U
+//
+// S is the true-frame state at the chunk start; nothing about the sign
+// crosses a chunk boundary except through S itself.
+//
+// Work decomposition (gfx950): one 256-thread workgroup per (sequence or
+// document, head, 64-wide value slice).  All four waves share the
+// value-independent chunk work (prep, the A/M products, the 16x16 diagonal
+// inverses of I + Diag(beta)A); wave w then owns value columns
+// [16w, 16w+16) of the slice and keeps that 128x16 column block of S in
+// MFMA accumulator registers for the whole sequence (value columns of S
+// evolve independently).  Every product runs on bf16 MFMA with hi/lo split
+// operands (see ckda_mfma.h).
+//
+// Exponent anchoring: e^{b_r - b_i} is factored as e^{b_r - m} e^{m - b_i}
+// with m the cumulative gate at token 15 (tokens 0..31) or 47 (tokens 32..63);
+// the cross-half block uses e^{b_r - m1} and e^{m1 - b_i}, both <= 1.
+#include "ckda_device.h"
+#include "ckda_launch.h"
+#include "ckda_mfma.h"
+
+namespace ckda {
+
+template <int DK, int DV>
+struct FwdShape {
+    static constexpr int BV = DV < 64 ? DV : 64;   // value columns per workgroup
+    static constexpr int NSLICE = DV / BV;
+    static constexpr int NWC = BV / 16;            // waves owning a value-column tile
+    static constexpr int NOCT = DK / 8;            // channel octets
+    static constexpr int TG = 64 / NOCT;           // token groups per wave in the prep
+    static constexpr int TPL = 16 / TG;            // tokens per lane in the prep
+    static constexpr int KS = DK / 32;             // 32-channel k-steps
+    static constexpr int RT = DK / 16;             // 16-channel row tiles of the state
+    static constexpr int PK = DK + 8;              // pitch of token-major operand rows (bf16)
+    static constexpr int PM = 64 + 4;              // pitch of M rows / channel-major rows (bf16)
+    static constexpr int PY = 16 + 4;              // pitch of 16x16 block rows (bf16)
+    // LDS carve-up (bytes).  Phase A (prep + A/M/S products) and phase B
+    // (solve + output + state update) alias the same region.
+    static constexpr int SZ_OP = 64 * PK * 2;      // one 64 x DK bf16 operand
+    static constexpr int SZ_OPF = 32 * PK * 2;     // 32 x DK
+    // column operands first: they stay live while phase B is written
+    static constexpr int A_COLK = 0;
+    static constexpr int A_COLKF = 2 * SZ_OP;
+    static constexpr int A_ROWK = 2 * SZ_OP + 2 * SZ_OPF;
+    static constexpr int A_ROWQ = A_ROWK + 2 * SZ_OP;
+    static constexpr int A_END = A_ROWQ + 2 * SZ_OP;
+    static constexpr int SZ_M = 64 * PM * 2;
+    static constexpr int SZ_LOFF = 6 * 16 * PY * 2;
+    static constexpr int SZ_Y = 4 * 16 * PY * 2;
+    static constexpr int SZ_CKT = DK * PM * 2;
+    static constexpr int B_M = A_ROWK;              // phase B aliases the row operands only
+    static constexpr int B_LOFF = B_M + 2 * SZ_M;
+    static constexpr int B_Y = B_LOFF + 2 * SZ_LOFF;
+    static constexpr int B_CKT = B_Y + 2 * SZ_Y;
+    static constexpr int B_LDIAG = B_CKT + 2 * SZ_CKT;
+    static constexpr int B_END = B_LDIAG + 4 * 16 * 17 * 4;
+    static constexpr int UNION = A_END > B_END ? A_END : B_END;
+    static constexpr int F_WTOT = UNION;                     // float [2][4][DK]
+    static constexpr int F_CH = F_WTOT + 2 * 4 * DK * 4;     // float [5][DK]
+    static constexpr int F_BETA = F_CH + 5 * DK * 4;         // float [64]
+    static constexpr int LDS_BYTES = F_BETA + 64 * 4;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert((A_COLKF % 16) == 0 && (A_ROWK % 16) == 0 && (B_CKT % 16) == 0 &&
+                  (B_LOFF % 16) == 0 && (B_Y % 16) == 0 && (B_LDIAG % 16) == 0 && (F_WTOT % 16) == 0,
+                  "align");
+};
+
+// keep the scheduler from hoisting the next work unit's loads above this point
+// (occupancy is one wave per SIMD, so unbounded hoisting only spills)
+#define CKDA_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// A zero the compiler cannot see through.  Adding it to the LDS base
+// pointers at the start of every phase keeps their (loop-invariant) address
+// arithmetic inside the chunk loop instead of hoisting hundreds of addresses
+// into registers for the whole kernel.
+__device__ __forceinline__ int opaque_zero() {
+    int z = 0;
+    asm volatile("" : "+s"(z));
+    return z;
+}
+
+// off-diagonal 16x16 block index of (J, K), K < J
+__device__ __forceinline__ int loff_index(int J, int K) { return (J * (J - 1)) / 2 + K; }
+
+// 8 consecutive elements of a token row, kept in their storage form until use
+template <typename Tin>
+struct Raw8;
+template <>
+struct Raw8<bf16_t> {
+    uint4 u;
+    __device__ __forceinline__ void load(const bf16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
+    __device__ __forceinline__ void zero() { u = make_uint4(0u, 0u, 0u, 0u); }
+    __device__ __forceinline__ float get(int e) const {
+        const uint32_t w = (e < 2) ? u.x : (e < 4) ? u.y : (e < 6) ? u.z : u.w;
+        return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+    }
+};
+template <>
+struct Raw8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = reinterpret_cast<const float4*>(p)[0];
+        b = reinterpret_cast<const float4*>(p)[1];
+    }
+    __device__ __forceinline__ void zero() { a = make_float4(0.f, 0.f, 0.f, 0.f); b = a; }
+    __device__ __forceinline__ float get(int e) const {
+        switch (e) {
+            case 0: return a.x; case 1: return a.y; case 2: return a.z; case 3: return a.w;
+            case 4: return b.x; case 5: return b.y; case 6: return b.z; default: return b.w;
+        }
+    }
+};
+
+__device__ __forceinline__ void store_split8(uint16_t* hi, uint16_t* lo, const float (&x)[8]) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint16_t h0, l0, h1, l1;
+        split1(x[2 * i], h0, l0);
+        split1(x[2 * i + 1], h1, l1);
+        h[i] = h0 | (static_cast<uint32_t>(h1) << 16);
+        l[i] = l0 | (static_cast<uint32_t>(l1) << 16);
+    }
+    *reinterpret_cast<uint4*>(hi) = make_uint4(h[0], h[1], h[2], h[3]);
+    *reinterpret_cast<uint4*>(lo) = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+__device__ __forceinline__ void store_split4(uint16_t* hi, uint16_t* lo, f32x4 x) {
+    uint16_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split1(x[i], h[i], l[i]);
+    *reinterpret_cast<uint2*>(hi) = make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
+    *reinterpret_cast<uint2*>(lo) = make_uint2(l[0] | (uint32_t(l[1]) << 16), l[2] | (uint32_t(l[3]) << 16));
+}
+
+struct FwdParams {
+    const void *q, *k, *v;
+    const float* g;
+    const int8_t* s;
+    const float* beta;
+    float scale;
+    const float* h0;
+    float* o;
+    float* ht;
+    float* h_ckpt;
+    const int32_t* cu;
+    int B, T, H, ndocs;
+};
+
+template <typename Tin, int DK, int DV>
+__global__ void __launch_bounds__(256, 1) ckda_fwd_kernel(FwdParams p)
+{
+    using SH = FwdShape<DK, DV>;
+    constexpr int NOCT = SH::NOCT, TG = SH::TG, TPL = SH::TPL, KS = SH::KS, RT = SH::RT;
+    constexpr int PK = SH::PK, PM = SH::PM, PY = SH::PY;
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    // LDS views; CKDA_LDS_VIEWS() re-derives them from an opaque base (see opaque_zero)
+#define CKDA_LDS_VIEWS()                                                                 \
+    unsigned char* const sm_ = smem + opaque_zero();                                     \
+    uint16_t* const rowk_hi = reinterpret_cast<uint16_t*>(sm_ + SH::A_ROWK);             \
+    uint16_t* const rowk_lo = rowk_hi + 64 * PK;                                         \
+    uint16_t* const rowq_hi = reinterpret_cast<uint16_t*>(sm_ + SH::A_ROWQ);             \
+    uint16_t* const rowq_lo = rowq_hi + 64 * PK;                                         \
+    uint16_t* const colk_hi = reinterpret_cast<uint16_t*>(sm_ + SH::A_COLK);             \
+    uint16_t* const colk_lo = colk_hi + 64 * PK;                                         \
+    uint16_t* const colkf_hi = reinterpret_cast<uint16_t*>(sm_ + SH::A_COLKF);           \
+    uint16_t* const colkf_lo = colkf_hi + 32 * PK;                                       \
+    uint16_t* const m_hi = reinterpret_cast<uint16_t*>(sm_ + SH::B_M);                   \
+    uint16_t* const m_lo = m_hi + 64 * PM;                                               \
+    uint16_t* const loff_hi = reinterpret_cast<uint16_t*>(sm_ + SH::B_LOFF);             \
+    uint16_t* const loff_lo = loff_hi + 6 * 16 * PY;                                     \
+    uint16_t* const y_hi = reinterpret_cast<uint16_t*>(sm_ + SH::B_Y);                   \
+    uint16_t* const y_lo = y_hi + 4 * 16 * PY;                                           \
+    uint16_t* const ckt_hi = reinterpret_cast<uint16_t*>(sm_ + SH::B_CKT);               \
+    uint16_t* const ckt_lo = ckt_hi + DK * PM;                                           \
+    float* const ldiag = reinterpret_cast<float*>(sm_ + SH::B_LDIAG);   /* [4][16][17] */\
+    float* const wtot_b = reinterpret_cast<float*>(sm_ + SH::F_WTOT);   /* [4][DK] */    \
+    float* const wtot_p = wtot_b + 4 * DK;                              /* [4][DK] */    \
+    float* const ch_em0 = reinterpret_cast<float*>(sm_ + SH::F_CH);     /* e^{m0} */     \
+    float* const ch_em1 = ch_em0 + DK;                                  /* e^{m1} */     \
+    float* const ch_d = ch_em1 + DK;                                    /* P_L e^{b_L} */\
+    float* const ch_f0 = ch_d + DK;                           /* P_L e^{b_L - m0} */     \
+    float* const ch_f1 = ch_f0 + DK;                          /* P_L e^{b_L - m1} */     \
+    float* const beta_s = reinterpret_cast<float*>(sm_ + SH::F_BETA);                    \
+    (void)rowk_hi; (void)rowk_lo; (void)rowq_hi; (void)rowq_lo; (void)colk_hi;           \
+    (void)colk_lo; (void)colkf_hi; (void)colkf_lo; (void)m_hi; (void)m_lo; (void)loff_hi;\
+    (void)loff_lo; (void)y_hi; (void)y_lo; (void)ckt_hi; (void)ckt_lo; (void)ldiag;      \
+    (void)wtot_b; (void)wtot_p; (void)ch_em0; (void)ch_em1; (void)ch_d; (void)ch_f0;     \
+    (void)ch_f1; (void)beta_s
+
+    const Tin* __restrict__ q = static_cast<const Tin*>(p.q);
+    const Tin* __restrict__ k = static_cast<const Tin*>(p.k);
+    const Tin* __restrict__ v = static_cast<const Tin*>(p.v);
+    const int H = p.H;
+
+    // ---- which (chain, value slice) this workgroup owns -------------------
+    const int nchains = p.cu ? p.ndocs * H : p.B * H;
+    int chain, slice;
+    {
+        const int bid = blockIdx.x;
+        if (SH::NSLICE == 1) {
+            chain = bid;
+            slice = 0;
+        } else {
+            // the slices of one chain land on the same XCD (blocks are dealt
+            // round-robin over 8 XCDs), so its shared inputs hit one L2
+            const int grp = 8 * SH::NSLICE;
+            const int full = (nchains / 8) * grp;
+            if (bid < full) {
+                const int r = bid % grp;
+                chain = (bid / grp) * 8 + (r % 8);
+                slice = r / 8;
+            } else {
+                const int r = bid - full;
+                chain = (nchains / 8) * 8 + r / SH::NSLICE;
+                slice = r % SH::NSLICE;
+            }
+        }
+    }
+    const int h = chain % H;
+    int tok0, len, sidx;
+    if (p.cu) {
+        sidx = chain / H;
+        tok0 = p.cu[sidx];
+        len = p.cu[sidx + 1] - tok0;
+    } else {
+        tok0 = (chain / H) * p.T; len = p.T; sidx = chain / H;
+    }
+    const size_t st_off = (static_cast<size_t>(sidx) * H + h) * DK * DV;
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int l = tid & 63;
+    const int n = l & 15;
+    const int gq = l >> 4;
+    const int co = l % NOCT;          // prep: channel octet
+    const int tg = l / NOCT;          // prep: token group
+    const bool has_col = w < SH::NWC;
+    const int col = slice * SH::BV + 16 * w + n;   // value column owned in the state phase
+
+    // ---- state: 16-column block, C layout (rows 16rt + 4gq + i) -----------
+    f32x4 S[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            S[rt][i] = (has_col && p.h0) ? p.h0[st_off + static_cast<size_t>(16 * rt + 4 * gq + i) * DV + col] : 0.f;
+
+    const int nchunks = (len + 63) / 64;
+    for (int j = 0; j < nchunks; ++j) {
+        const int c0 = j * 64;
+        const int L = min(64, len - c0);
+        if (p.h_ckpt && has_col) {
+            float* hc = p.h_ckpt + (static_cast<size_t>(sidx) * H + h) * static_cast<size_t>(nchunks) * DK * DV +
+                        static_cast<size_t>(j) * DK * DV;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) hc[static_cast<size_t>(16 * rt + 4 * gq + i) * DV + col] = S[rt][i];
+        }
+
+        // ================= P1: gate / sign-fold prep ========================
+        {
+        CKDA_LDS_VIEWS();
+        // lane: channels 8co..8co+7 of tokens 16w + tg*TPL + tt (tt < TPL)
+        float bl[TPL][8];
+        uint32_t negmask = 0;         // bit 8*tt+e: running sign product is -1
+        Raw8<Tin> qr[TPL], kr[TPL];
+        float run[8];
+        uint32_t par = 0;             // bit e: parity of negative signs so far
+#pragma unroll
+        for (int e = 0; e < 8; ++e) run[e] = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < TPL; ++tt) {
+            const int t = 16 * w + tg * TPL + tt;
+            if (t < L) {
+                const size_t base = (static_cast<size_t>(tok0 + c0 + t) * H + h) * DK + 8 * co;
+                const float4 g0 = reinterpret_cast<const float4*>(p.g + base)[0];
+                const float4 g1 = reinterpret_cast<const float4*>(p.g + base)[1];
+                const uint2 s8 = *reinterpret_cast<const uint2*>(p.s + base);
+                run[0] += g0.x; run[1] += g0.y; run[2] += g0.z; run[3] += g0.w;
+                run[4] += g1.x; run[5] += g1.y; run[6] += g1.z; run[7] += g1.w;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t byte = ((e < 4 ? s8.x : s8.y) >> (8 * (e & 3))) & 0xffu;
+                    par ^= (byte >> 7) << e;      // s = -1 has its sign bit set
+                }
+                qr[tt].load(q + base);
+                kr[tt].load(k + base);
+            } else {
+                qr[tt].zero();
+                kr[tt].zero();
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bl[tt][e] = run[e];
+            negmask |= par << (8 * tt);
+            if (co == 0) beta_s[t] = (t < L) ? p.beta[static_cast<size_t>(tok0 + c0 + t) * H + h] : 0.f;
+        }
+        // inclusive scan of the per-lane totals across the token groups of the wave
+        float inc[8];
+        uint32_t pinc = par;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) inc[e] = run[e];
+#pragma unroll
+        for (int d = 1; d < TG; d *= 2) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float ob = __shfl_up(inc[e], d * NOCT, 64);
+                if (tg >= d) inc[e] += ob;
+            }
+            const uint32_t op = static_cast<uint32_t>(__shfl_up(static_cast<int>(pinc), d * NOCT, 64));
+            if (tg >= d) pinc ^= op;
+        }
+        if (tg == TG - 1) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                wtot_b[w * DK + 8 * co + e] = inc[e];
+                wtot_p[w * DK + 8 * co + e] = ((pinc >> e) & 1u) ? -1.f : 1.f;
+            }
+        }
+        __syncthreads();
+        float m0[8], m1[8], mh[8], bpre[8];
+        uint32_t ppre = pinc ^ par;   // parity of the tokens before this lane's, inside the wave
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int c = 8 * co + e;
+            const float B0 = wtot_b[c], B1 = wtot_b[DK + c], B2 = wtot_b[2 * DK + c], B3 = wtot_b[3 * DK + c];
+            const float Q0 = wtot_p[c], Q1 = wtot_p[DK + c], Q2 = wtot_p[2 * DK + c], Q3 = wtot_p[3 * DK + c];
+            m0[e] = B0;
+            const float a = B0 + B1;
+            m1[e] = a + B2;
+            const float bL = m1[e] + B3;
+            const float PL = Q0 * Q1 * Q2 * Q3;
+            float bp = 0.f, pp = 1.f;
+            if (w > 0) { bp += B0; pp *= Q0; }
+            if (w > 1) { bp += B1; pp *= Q1; }
+            if (w > 2) { bp += B2; pp *= Q2; }
+            bpre[e] = bp + (inc[e] - run[e]);
+            if (pp < 0.f) ppre ^= 1u << e;
+            mh[e] = (w >= 2) ? m1[e] : m0[e];
+            if (w == 0 && tg == 0) {
+                ch_em0[c] = exp2_clamped(m0[e] * kLog2e);
+                ch_em1[c] = exp2_clamped(m1[e] * kLog2e);
+                ch_d[c] = PL * exp2_clamped(bL * kLog2e);
+                ch_f0[c] = PL * exp2_clamped((bL - m0[e]) * kLog2e);
+                ch_f1[c] = PL * exp2_clamped((bL - m1[e]) * kLog2e);
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < TPL; ++tt) {
+            const int t = 16 * w + tg * TPL + tt;
+            float rk[8], rq[8], ck[8];
+            const uint32_t neg = ppre ^ ((negmask >> (8 * tt)) & 0xffu);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float b = bpre[e] + bl[tt][e];
+                const float P = ((neg >> e) & 1u) ? -1.f : 1.f;
+                const float e1 = exp2_clamped((b - mh[e]) * kLog2e);
+                const float e2 = exp2_clamped((mh[e] - b) * kLog2e);
+                const float kf = P * kr[tt].get(e);
+                rk[e] = kf * e1;
+                rq[e] = (P * qr[tt].get(e)) * e1;
+                ck[e] = kf * e2;
+            }
+            store_split8(rowk_hi + t * PK + 8 * co, rowk_lo + t * PK + 8 * co, rk);
+            store_split8(rowq_hi + t * PK + 8 * co, rowq_lo + t * PK + 8 * co, rq);
+            store_split8(colk_hi + t * PK + 8 * co, colk_lo + t * PK + 8 * co, ck);
+            if (w < 2) {
+                float cf[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) cf[e] = ck[e] * exp2_clamped((m1[e] - m0[e]) * kLog2e);
+                store_split8(colkf_hi + t * PK + 8 * co, colkf_lo + t * PK + 8 * co, cf);
+            }
+            CKDA_FENCE();
+        }
+        __syncthreads();
+
+        }
+        // ================= P2: A / M tiles and the S products ===============
+        f32x4 tacc[5];                 // A^T / M^T tiles of this wave
+        int tR[5], tI[5], tIsA[5];
+        f32x4 Rt[4], OQ[4];            // V - K^S and Q^S for this wave's value columns
+        {
+        CKDA_LDS_VIEWS();
+        // A^T and M^T tiles: wave w takes A row-block w and M row-block 3-w.
+        {
+#pragma unroll
+            for (int x = 0; x < 5; ++x) {
+                int R, I, isA;
+                if (x <= w) { R = w; I = x; isA = 1; }
+                else { R = 3 - w; I = x - w - 1; isA = 0; }
+                tR[x] = R; tI[x] = I; tIsA[x] = isA;
+                const bool cross = (R >= 2) && (I < 2);
+                const uint16_t* ch = cross ? colkf_hi : colk_hi;
+                const uint16_t* cl = cross ? colkf_lo : colk_lo;
+                const uint16_t* rh = isA ? rowk_hi : rowq_hi;
+                const uint16_t* rl = isA ? rowk_lo : rowq_lo;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int ko = 32 * ks + 8 * gq;
+                    const bf16x8 ah = lds8(ch + (16 * I + n) * PK + ko);
+                    const bf16x8 al = lds8(cl + (16 * I + n) * PK + ko);
+                    const bf16x8 bh = lds8(rh + (16 * R + n) * PK + ko);
+                    const bf16x8 bl8 = lds8(rl + (16 * R + n) * PK + ko);
+                    acc = mfma32x3(ah, al, bh, bl8, acc);
+                }
+                tacc[x] = acc;
+                CKDA_FENCE();
+            }
+        }
+        // S' = Diag(e^{m_h}) S as split B operands, then K^S and Q^S
+        if (has_col) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const float* em = hh ? ch_em1 : ch_em0;
+                Split8 Bs[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    f32x4 a, b;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        a[i] = em[32 * ks + 4 * gq + i] * S[2 * ks][i];
+                        b[i] = em[32 * ks + 16 + 4 * gq + i] * S[2 * ks + 1][i];
+                    }
+                    Bs[ks] = split8(a, b);
+                }
+#pragma unroll
+                for (int R = 2 * hh; R < 2 * hh + 2; ++R) {
+                    f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const int r = 16 * R + n;
+                        const int ka = 32 * ks + 4 * gq, kb = 32 * ks + 16 + 4 * gq;
+                        const bf16x8 kh = lds4x2(rowk_hi + r * PK + ka, rowk_hi + r * PK + kb);
+                        const bf16x8 kl = lds4x2(rowk_lo + r * PK + ka, rowk_lo + r * PK + kb);
+                        const bf16x8 qh = lds4x2(rowq_hi + r * PK + ka, rowq_hi + r * PK + kb);
+                        const bf16x8 ql = lds4x2(rowq_lo + r * PK + ka, rowq_lo + r * PK + kb);
+                        ak = mfma32x3(kh, kl, Bs[ks].hi, Bs[ks].lo, ak);
+                        aq = mfma32x3(qh, ql, Bs[ks].hi, Bs[ks].lo, aq);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = 16 * R + 4 * gq + i;
+                        const float vv = (t < L) ? Elem<Tin>::load(v, (static_cast<size_t>(tok0 + c0 + t) * H + h) * DV + col) : 0.f;
+                        Rt[R][i] = vv - ak[i];
+                    }
+                    OQ[R] = aq;
+                    CKDA_FENCE();
+                }
+            }
+        }
+        __syncthreads();
+
+        }
+        // ================= P2.5: publish -beta*A blocks, M, and kf^T ========
+        {
+        CKDA_LDS_VIEWS();
+#pragma unroll
+        for (int x = 0; x < 5; ++x) {
+            const int R = tR[x], I = tI[x];
+            const int r = 16 * R + n;
+            f32x4 val = tacc[x];
+            if (tIsA[x]) {
+                const float br = beta_s[r];
+                if (R == I) {
+                    float4 o4;
+                    o4.x = (4 * gq + 0 < n) ? br * val[0] : 0.f;
+                    o4.y = (4 * gq + 1 < n) ? br * val[1] : 0.f;
+                    o4.z = (4 * gq + 2 < n) ? br * val[2] : 0.f;
+                    o4.w = (4 * gq + 3 < n) ? br * val[3] : 0.f;
+                    float* dst = ldiag + (R * 16 + n) * 17 + 4 * gq;
+                    dst[0] = o4.x; dst[1] = o4.y; dst[2] = o4.z; dst[3] = o4.w;
+                } else {
+                    f32x4 nv;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) nv[i] = -br * val[i];
+                    const int blk = loff_index(R, I);
+                    store_split4(loff_hi + (blk * 16 + n) * PY + 4 * gq, loff_lo + (blk * 16 + n) * PY + 4 * gq, nv);
+                }
+            } else {
+                f32x4 mv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mv[i] = (R > I || 4 * gq + i <= n) ? val[i] : 0.f;
+                store_split4(m_hi + r * PM + 16 * I + 4 * gq, m_lo + r * PM + 16 * I + 4 * gq, mv);
+            }
+        }
+        // M . U reads the upper blocks (0,1) and (2,3) of M as part of its
+        // 32-token k-steps: they must hold zeros
+        if (w == 3 || w == 1) {
+            const int R = (w == 3) ? 0 : 2;
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            store_split4(m_hi + (16 * R + n) * PM + 16 * (R + 1) + 4 * gq,
+                         m_lo + (16 * R + n) * PM + 16 * (R + 1) + 4 * gq, zero);
+        }
+        // transposed copy of the column operand (phase B leaves colk intact)
+#pragma unroll
+        for (int tt = 0; tt < TPL; ++tt) {
+            const int t = 16 * w + tg * TPL + tt;
+            const uint4 hv = *reinterpret_cast<const uint4*>(colk_hi + t * PK + 8 * co);
+            const uint4 lv = *reinterpret_cast<const uint4*>(colk_lo + t * PK + 8 * co);
+            const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
+            const uint32_t lw[4] = {lv.x, lv.y, lv.z, lv.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int c = 8 * co + e;
+                ckt_hi[c * PM + t] = static_cast<uint16_t>(hw[e >> 1] >> (16 * (e & 1)));
+                ckt_lo[c * PM + t] = static_cast<uint16_t>(lw[e >> 1] >> (16 * (e & 1)));
+            }
+        }
+        __syncthreads();
+
+        }
+        // ================= P3: inverses of the 16x16 diagonal blocks ========
+        {
+        CKDA_LDS_VIEWS();
+        if (l < 16) {
+            const int J = w;
+            const int c = l;
+            float y[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = (r == c) ? 1.f : 0.f;
+#pragma unroll
+                for (int i = 0; i < r; ++i) acc -= ldiag[(J * 16 + r) * 17 + i] * y[i];
+                y[r] = acc;
+                CKDA_FENCE();
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                uint16_t hh, ll;
+                split1(y[r], hh, ll);
+                y_hi[(J * 16 + r) * PY + c] = hh;
+                y_lo[(J * 16 + r) * PY + c] = ll;
+            }
+        }
+        __syncthreads();
+
+        }
+        // ================= P4: U, O, state update ==========================
+        {
+        CKDA_LDS_VIEWS();
+        if (has_col) {
+            f32x4 U[4];
+            Split4 Us[4];
+#pragma unroll
+            for (int J = 0; J < 4; ++J) {
+                f32x4 z;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) z[i] = beta_s[16 * J + 4 * gq + i] * Rt[J][i];
+#pragma unroll
+                for (int K = 0; K < J; ++K) {
+                    const int blk = loff_index(J, K);
+                    const s16x4 ah = lds4s(loff_hi + (blk * 16 + n) * PY + 4 * gq);
+                    const s16x4 al = lds4s(loff_lo + (blk * 16 + n) * PY + 4 * gq);
+                    z = mfma16x3(ah, al, Us[K].hi, Us[K].lo, z);
+                }
+                const Split4 zs = split4(z);
+                const s16x4 yh = lds4s(y_hi + (J * 16 + n) * PY + 4 * gq);
+                const s16x4 yl = lds4s(y_lo + (J * 16 + n) * PY + 4 * gq);
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                U[J] = mfma16x3(yh, yl, zs.hi, zs.lo, zero);
+                Us[J] = split4(U[J]);
+                CKDA_FENCE();
+            }
+            const Split8 U01 = split8(U[0], U[1]);
+            const Split8 U23 = split8(U[2], U[3]);
+            // O = Q^S + M U
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+                f32x4 acc = OQ[R];
+                const int r = 16 * R + n;
+                {
+                    const bf16x8 mh8 = lds4x2(m_hi + r * PM + 4 * gq, m_hi + r * PM + 16 + 4 * gq);
+                    const bf16x8 ml8 = lds4x2(m_lo + r * PM + 4 * gq, m_lo + r * PM + 16 + 4 * gq);
+                    acc = mfma32x3(mh8, ml8, U01.hi, U01.lo, acc);
+                }
+                if (R >= 2) {
+                    const bf16x8 mh8 = lds4x2(m_hi + r * PM + 32 + 4 * gq, m_hi + r * PM + 48 + 4 * gq);
+                    const bf16x8 ml8 = lds4x2(m_lo + r * PM + 32 + 4 * gq, m_lo + r * PM + 48 + 4 * gq);
+                    acc = mfma32x3(mh8, ml8, U23.hi, U23.lo, acc);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * R + 4 * gq + i;
+                    if (t < L) p.o[(static_cast<size_t>(tok0 + c0 + t) * H + h) * DV + col] = p.scale * acc[i];
+                }
+                CKDA_FENCE();
+            }
+            // S <- Diag(d) S + Diag(f0) kf[0:32]^T U[0:32] + Diag(f1) kf[32:64]^T U[32:64]
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const int c = 16 * rt + n;
+                const bf16x8 a0h = lds4x2(ckt_hi + c * PM + 4 * gq, ckt_hi + c * PM + 16 + 4 * gq);
+                const bf16x8 a0l = lds4x2(ckt_lo + c * PM + 4 * gq, ckt_lo + c * PM + 16 + 4 * gq);
+                const bf16x8 a1h = lds4x2(ckt_hi + c * PM + 32 + 4 * gq, ckt_hi + c * PM + 48 + 4 * gq);
+                const bf16x8 a1l = lds4x2(ckt_lo + c * PM + 32 + 4 * gq, ckt_lo + c * PM + 48 + 4 * gq);
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                const f32x4 acc0 = mfma32x3(a0h, a0l, U01.hi, U01.lo, zero);
+                const f32x4 acc1 = mfma32x3(a1h, a1l, U23.hi, U23.lo, zero);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int cc = 16 * rt + 4 * gq + i;
+                    S[rt][i] = ch_d[cc] * S[rt][i] + ch_f0[cc] * acc0[i] + ch_f1[cc] * acc1[i];
+                }
+                CKDA_FENCE();
+            }
+        }
+        __syncthreads();
+        }
+    }
+
+    if (p.ht && has_col) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                p.ht[st_off + static_cast<size_t>(16 * rt + 4 * gq + i) * DV + col] = S[rt][i];
+    }
+}
+
+template <typename Tin, int DK, int DV>
+static hipError_t launch_fwd_t(const FwdArgs& A, hipStream_t stream) {
+    using SH = FwdShape<DK, DV>;
+    FwdParams p;
+    p.q = A.q; p.k = A.k; p.v = A.v; p.g = A.g; p.s = A.s; p.beta = A.beta; p.scale = A.scale;
+    p.h0 = A.h0; p.o = A.o; p.ht = A.ht; p.h_ckpt = A.h_ckpt; p.cu = A.cu;
+    p.B = A.B; p.T = A.T; p.H = A.H; p.ndocs = A.ndocs;
+    const int nchains = A.cu ? A.ndocs * A.H : A.B * A.H;
+    const int grid = nchains * SH::NSLICE;
+    if (grid == 0) return hipSuccess;
+    auto kern = ckda_fwd_kernel<Tin, DK, DV>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, SH::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), SH::LDS_BYTES, stream, p);
+    return hipGetLastError();
+}
+
+template <typename Tin>
+static hipError_t launch_fwd_dt(const FwdArgs& A, hipStream_t stream) {
+#define CKDA_FWD(DK_, DV_) \
+    if (A.DK == DK_ && A.DV == DV_) return launch_fwd_t<Tin, DK_, DV_>(A, stream);
+    CKDA_FWD(32, 32) CKDA_FWD(32, 64) CKDA_FWD(32, 128)
+    CKDA_FWD(64, 32) CKDA_FWD(64, 64) CKDA_FWD(64, 128)
+    CKDA_FWD(128, 32) CKDA_FWD(128, 64) CKDA_FWD(128, 128)
+#undef CKDA_FWD
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd(const FwdArgs& A, hipStream_t stream) {
+    return A.bf16 ? launch_fwd_dt<bf16_t>(A, stream) : launch_fwd_dt<float>(A, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Standalone prep: one thread per (chunk, head, channel), serial over the
+// chunk's tokens.  Same definitions as the fused prep above.
+// ---------------------------------------------------------------------------
+template <typename Tin>
+__global__ void ckda_prep_kernel(int B, int T, int H, int DK, const Tin* __restrict__ q,
+                                 const Tin* __restrict__ k, const float* __restrict__ g,
+                                 const int8_t* __restrict__ s, float* __restrict__ b_out,
+                                 int8_t* __restrict__ p_out, Tin* __restrict__ qf_out,
+                                 Tin* __restrict__ kf_out)
+{
+    const int nt = (T + 63) / 64;
+    const int c = blockIdx.y * blockDim.x + threadIdx.x;
+    if (c >= DK) return;
+    const int idx = blockIdx.x;            // (b * H + h) * nt + chunk
+    const int chunk = idx % nt;
+    const int bh = idx / nt;
+    const int hh = bh % H, bb = bh / H;
+    float run = 0.f;
+    int sp = 1;
+    const int t1 = min(T, chunk * 64 + 64);
+    for (int t = chunk * 64; t < t1; ++t) {
+        const size_t e = ((static_cast<size_t>(bb) * T + t) * H + hh) * DK + c;
+        run += g[e];
+        sp *= static_cast<int>(s[e]);
+        b_out[e] = run;
+        p_out[e] = static_cast<int8_t>(sp);
+        const float pf = static_cast<float>(sp);
+        Elem<Tin>::store(qf_out, e, pf * Elem<Tin>::load(q, e));
+        Elem<Tin>::store(kf_out, e, pf * Elem<Tin>::load(k, e));
+    }
+}
+
+hipError_t launch_prep(const PrepArgs& A, hipStream_t stream) {
+    const int nt = (A.T + 63) / 64;
+    const long long grid = static_cast<long long>(A.B) * A.H * nt;
+    if (grid == 0) return hipSuccess;
+    const int bs = A.DK < 128 ? A.DK : 128;
+    dim3 gdim(static_cast<unsigned>(grid), (A.DK + bs - 1) / bs);
+    if (A.bf16)
+        hipLaunchKernelGGL(ckda_prep_kernel<bf16_t>, gdim, dim3(bs), 0, stream, A.B, A.T, A.H, A.DK,
+                           static_cast<const bf16_t*>(A.q), static_cast<const bf16_t*>(A.k), A.g, A.s,
+                           A.b_out, A.p_out, static_cast<bf16_t*>(A.qf_out), static_cast<bf16_t*>(A.kf_out));
+    else
+        hipLaunchKernelGGL(ckda_prep_kernel<float>, gdim, dim3(bs), 0, stream, A.B, A.T, A.H, A.DK,
+                           static_cast<const float*>(A.q), static_cast<const float*>(A.k), A.g, A.s,
+                           A.b_out, A.p_out, static_cast<float*>(A.qf_out), static_cast<float*>(A.kf_out));
+    return hipGetLastError();
+}
+
+}  // namespace ckda

@@ -1,0 +1,167 @@
+/*
+ * ckda.h -- C ABI of libckda.so: the Complex KDA (CKDA) token-mixing
+ * recurrence on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (per head; Complex KDA paper page, section 3 "CKDA."
+ * paragraph, with DeltaNet's transition from section 2 "Linear RNNs"):
+ *
+ *     alpha_t = s_t * exp(g_t)          s_t in {+1,-1}^DK, g_t = log|alpha_t|
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t
+ *
+ * S_t in R^{DK x DV} (row = key channel, column = value channel).  The gate
+ * magnitude is passed in log space and the sign separately, and the running
+ * product of the signs is pushed onto q and k inside the kernels, as the
+ * "complex-kda-1.3B-100B" model card describes; callers always see the true
+ * (signed) state unless a call says otherwise.  The pages' ranges are
+ * alpha in [-1, 1] and beta in [0, 2] with unit-norm keys; the library does
+ * not clamp or normalise anything.
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers (except cu_seqlens_host), dense
+ *    and row-major in the layouts stated.  Token tensors: [B, T, H, D];
+ *    per-head scalars: [B, T, H]; states: [B, H, DK, DV] float32.
+ *  - The caller owns every buffer, the workspace included.  The library never
+ *    allocates, frees, or keeps a pointer after the enqueued work is done.
+ *  - Work is enqueued on `stream` and the call returns without waiting for it.
+ *  - Every argument check runs before anything is enqueued.  On any error
+ *    nothing is enqueued, no output is touched and a non-zero status is
+ *    returned; ckda_last_error() then describes it (per calling thread).
+ *    There is no fallback path: a shape or dtype the kernels do not support
+ *    is an error (CKDA_ERR_UNSUPPORTED), never a silent substitute.
+ *  - Supported head sizes: DK, DV in {32, 64, 128}.  Chunk length is 64.
+ *  - Outputs must not alias inputs (except the in/out decode state).
+ *  - Accuracy: the intra-chunk products factor exp(b_r - b_i) through
+ *    anchors at the middle of each half chunk, so every run of 16
+ *    consecutive log-gates inside a chunk half should sum to more than -80
+ *    per channel (an average |alpha| above ~0.007).  g must be finite.
+ */
+#ifndef CKDA_H
+#define CKDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CKDA_ABI_VERSION 1
+
+typedef enum {
+    CKDA_OK = 0,
+    CKDA_ERR_NULL = 1,        /* a required pointer is NULL */
+    CKDA_ERR_SHAPE = 2,       /* a size is negative / inconsistent */
+    CKDA_ERR_DTYPE = 3,       /* unknown dtype code */
+    CKDA_ERR_UNSUPPORTED = 4, /* valid request the kernels do not implement */
+    CKDA_ERR_SEQLENS = 5,     /* cu_seqlens not 0-based, monotone, ending at T */
+    CKDA_ERR_WORKSPACE = 6,   /* workspace missing or too small */
+    CKDA_ERR_HIP = 7          /* the HIP runtime reported an error */
+} ckda_status_t;
+
+typedef enum {
+    CKDA_F32 = 0,
+    CKDA_BF16 = 1
+} ckda_dtype_t;
+
+/* opaque HIP stream (hipStream_t); NULL = the default stream */
+typedef void* ckda_stream_t;
+
+int ckda_abi_version(void);
+const char* ckda_status_string(ckda_status_t status);
+/* Message of the last failing call on this thread ("" if none). */
+const char* ckda_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Gate / sign-fold prep (the first step of every chunk; exposed on its own
+ * for testing).  Model card "complex-kda-1.3B-100B": |alpha| is carried in
+ * log space and the +-1 part as a running product pushed onto q and k.
+ * Per chunk of 64 tokens (the chunk restarts both scans):
+ *     b_t  = sum of g over the chunk up to and including t      (float32)
+ *     P_t  = product of s over the chunk up to and including t   (+-1)
+ *     qf_t = P_t * q_t,  kf_t = P_t * k_t                        (exact)
+ * q, k: [B,T,H,DK] in_dtype; g: [B,T,H,DK] f32; s: [B,T,H,DK] int8.
+ * Outputs (all [B,T,H,DK]): b f32, p int8 (+-1), qf, kf in_dtype.
+ * ---------------------------------------------------------------------- */
+ckda_status_t ckda_chunk_prep(int B, int T, int H, int DK, ckda_dtype_t in_dtype,
+                              const void* q, const void* k, const float* g, const int8_t* s,
+                              float* b_out, int8_t* p_out, void* qf_out, void* kf_out,
+                              ckda_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Chunked forward over B equal-length sequences.
+ *   q, k: [B,T,H,DK] in_dtype     v: [B,T,H,DV] in_dtype
+ *   g: [B,T,H,DK] f32 (log|alpha|) s: [B,T,H,DK] int8 (+1/-1)
+ *   beta: [B,T,H] f32             scale: output multiplier
+ *   h0: [B,H,DK,DV] f32 or NULL (zero initial state)
+ *   o: [B,T,H,DV] f32 (written)   ht: [B,H,DK,DV] f32 or NULL (final state)
+ *   h_ckpt: [B,H,NT,DK,DV] f32 or NULL, NT = ceil(T/64): the state at the
+ *           start of every chunk (checkpoints for ckda_bwd)
+ * No workspace is needed (ckda_fwd_workspace_bytes returns 0 for it).
+ * ---------------------------------------------------------------------- */
+size_t ckda_fwd_workspace_bytes(int B, int T, int H, int DK, int DV);
+ckda_status_t ckda_fwd_chunked(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype,
+                               const void* q, const void* k, const void* v,
+                               const float* g, const int8_t* s, const float* beta, float scale,
+                               const float* h0, float* o, float* ht, float* h_ckpt,
+                               ckda_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Varlen forward over N packed documents (training packs documents back to
+ * back, "complex-kda-ladder" model card, tokenizer section).  Document n
+ * covers tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 of the packed tensors;
+ * it starts from h0[n] (or zero) and its final state goes to ht[n].  No state
+ * or sign product crosses a document boundary.
+ *   cu_seqlens_host: int32 [N+1] in host memory, read during the call to
+ *                    validate it (0-based, non-decreasing, ends at T_total)
+ *   cu_seqlens_dev:  the same N+1 values in device memory, read by the kernel
+ *   q, k, g, s: [T_total,H,DK]; v, o: [T_total,H,DV]; beta: [T_total,H]
+ *   h0, ht: [N,H,DK,DV] f32, each nullable.  Documents may be empty (their
+ *   ht is their h0, or zero).  No workspace is needed.
+ * ---------------------------------------------------------------------- */
+ckda_status_t ckda_fwd_varlen(int N, int T_total, const int32_t* cu_seqlens_host,
+                              const int32_t* cu_seqlens_dev, int H, int DK, int DV,
+                              ckda_dtype_t in_dtype, const void* q, const void* k, const void* v,
+                              const float* g, const int8_t* s, const float* beta, float scale,
+                              const float* h0, float* o, float* ht, ckda_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * One recurrent (decode) step for N independent sequences.  The state is
+ * carried in the folded frame: the true state is Diag(sign_prod) * state.
+ * A prefill's final state enters as state = ht, sign_prod = +1.
+ *   q, k: [N,H,DK] in_dtype;  v: [N,H,DV] in_dtype
+ *   g, s: [N,H,DK] f32 / int8;  beta: [N,H] f32
+ *   state: [N,H,DK,DV] f32, updated in place
+ *   sign_prod: [N,H,DK] int8 (+1/-1), updated in place (times s)
+ *   o: [N,H,DV] f32
+ * Each state element is read once and written once.
+ * ---------------------------------------------------------------------- */
+ckda_status_t ckda_decode_step(int N, int H, int DK, int DV, ckda_dtype_t in_dtype,
+                               const void* q, const void* k, const void* v, const float* g,
+                               const int8_t* s, const float* beta, float scale, float* state,
+                               int8_t* sign_prod, float* o, ckda_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Backward of the chunked forward: gradients of L = <do, o> + <dht, ht>.
+ *   inputs as in ckda_fwd_chunked; h0 nullable (zero)
+ *   h_ckpt: [B,H,NT,DK,DV] f32 written by ckda_fwd_chunked on the same
+ *           inputs (required)
+ *   dout: [B,T,H,DV] in_dtype;  dht: [B,H,DK,DV] f32 or NULL (zero)
+ *   dq, dk, dg: [B,T,H,DK] f32;  dv: [B,T,H,DV] f32;  dbeta: [B,T,H] f32
+ *   dh0: [B,H,DK,DV] f32 or NULL
+ *   workspace: ckda_bwd_workspace_bytes(...) bytes of device memory
+ * dg is the gradient w.r.t. g = log|alpha| (alpha * dL/dalpha); s gets none.
+ * ---------------------------------------------------------------------- */
+size_t ckda_bwd_workspace_bytes(int B, int T, int H, int DK, int DV);
+ckda_status_t ckda_bwd(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype,
+                       const void* q, const void* k, const void* v, const float* g,
+                       const int8_t* s, const float* beta, float scale, const float* h0,
+                       const float* h_ckpt, const void* dout, const float* dht,
+                       float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0,
+                       void* workspace, size_t workspace_bytes, ckda_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CKDA_H */

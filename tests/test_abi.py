@@ -1,0 +1,89 @@
+"""The C ABI: the library loads without a GPU, exports what include/ckda.h
+declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ckda.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ckda_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from gated_delta_rule_sign_amd import ckda
+    return ckda.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert L.ckda_abi_version() == 1
+    assert L.ckda_status_string(0) == b"ok"
+    for st in range(1, 8):
+        assert L.ckda_status_string(st) not in (b"ok", b"unknown status")
+    assert L.ckda_status_string(99) == b"unknown status"
+
+
+P = ctypes.c_void_p
+FAKE = P(0x1000)          # never dereferenced: every call below fails validation first
+
+
+def fwd(L, B=1, T=8, H=1, DK=32, DV=32, dt=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE, s=FAKE, beta=FAKE, o=FAKE):
+    return L.ckda_fwd_chunked(B, T, H, DK, DV, dt, q, k, v, g, s, beta, ctypes.c_float(1.0),
+                              None, o, None, None, None)
+
+
+def test_fwd_rejects_bad_arguments(L):
+    assert fwd(L, DK=48) == 4                    # unsupported head size
+    assert fwd(L, DV=256) == 4
+    assert fwd(L, DK=0) == 2
+    assert fwd(L, B=-1) == 2
+    assert fwd(L, dt=7) == 3
+    assert fwd(L, q=None) == 1
+    assert b"'q'" in L.ckda_last_error()
+    assert fwd(L, o=None) == 1
+    assert fwd(L, g=P(0x1004)) == 4              # misaligned
+    assert fwd(L, B=0) == 0                      # empty problem: nothing to do
+    assert L.ckda_last_error() == b""
+
+
+def test_varlen_rejects_bad_cu_seqlens(L):
+    def call(cu, N, Tt):
+        arr = (ctypes.c_int32 * len(cu))(*cu)
+        return L.ckda_fwd_varlen(N, Tt, arr, FAKE, 1, 32, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 ctypes.c_float(1.0), None, FAKE, None, None)
+    assert call([1, 5], 1, 5) == 5              # does not start at 0
+    assert call([0, 5, 3], 2, 3) == 5           # decreasing
+    assert call([0, 5, 9], 2, 10) == 5          # does not end at T_total
+    assert L.ckda_fwd_varlen(2, 4, None, FAKE, 1, 32, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             ctypes.c_float(1.0), None, FAKE, None, None) == 1
+
+
+def test_decode_and_bwd_reject_bad_arguments(L):
+    f = ctypes.c_float(1.0)
+    assert L.ckda_decode_step(4, 2, 96, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, f, FAKE, FAKE, FAKE, None) == 4
+    assert L.ckda_decode_step(4, 2, 32, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, f, None, FAKE, FAKE, None) == 1
+    assert L.ckda_bwd(1, 8, 1, 32, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, f, None, None, FAKE, None,
+                      FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 1   # h_ckpt missing
+    assert L.ckda_chunk_prep(1, 8, 1, 100, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 4
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from gated_delta_rule_sign_amd import ckda
+    monkeypatch.setattr(ckda, "_lib", None)
+    monkeypatch.setattr(ckda, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ckda.CkdaError):
+        ckda.lib()
