@@ -1,0 +1,247 @@
+"""Throughput of the CKDA hot path on one MI355X.
+
+A step is one chunked forward (gate/sign-fold prep, chunk-local UT/WY
+products, state passing and output, fused in one kernel) over the mixer
+workload of the 1.36B model: B=8, T=4096, H=16, dk=dv=128, bf16 q/k/v,
+fp32 gates, state and outputs.  The JSON line's ``value`` is that forward's
+tokens/s; the decode workload (256 sequences x 16 heads, 512 recurrent
+steps) is reported in the same line as state-streaming GB/s, and the
+backward (when built) as tokens/s.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+       [--only fwd|decode|bwd|copy]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix peak
+METRIC = "CKDA chunked fwd tokens/s (H16,d128,T4096) + decode GB/s; % of roofline"
+
+# algorithmic bytes per token-head of the forward: q,k,v bf16 (768) + g f32 (512)
+# + s int8 (128) + beta f32 (4) + o f32 (512)
+FWD_BYTES_PER_TOKEN_HEAD = 768 + 512 + 128 + 4 + 512
+# algorithmic flops per token-head of the 64-token chunked method (dense count)
+FWD_FLOPS_PER_TOKEN_HEAD = 181.6e3
+# decode, per head-step: state read+write (2*64 KiB) + q,k,v bf16 + g + s +
+# sign_prod read+write + beta + o
+DEC_BYTES_PER_HEAD_STEP = 2 * 128 * 128 * 4 + 3 * 256 + 512 + 128 + 2 * 128 + 4 + 512
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def dev_tensor(torch, arr):
+    t = torch.from_numpy(np.ascontiguousarray(arr))
+    if arr.dtype == np.uint16:
+        t = t.view(torch.bfloat16)
+    return t.to("cuda:0")
+
+
+def time_kernel_launches(torch, fn, steps, warmup):
+    """Run fn warmup+steps times; time the steps with HIP events on the
+    current stream (the stream the library launches on).  Returns (total
+    wall ms, per-launch event ms list)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    return wall, [a.elapsed_time(b) for a, b in evs]
+
+
+def bench_fwd(torch, steps, warmup):
+    from gated_delta_rule_sign_amd import ckda
+    from gated_delta_rule_sign_amd import inputs as I
+    log("generating layer_bf16 inputs")
+    w = I.make_workload("layer_bf16")
+    tok = w.tok
+    d = {k: dev_tensor(torch, getattr(tok, k)) for k in ("q", "k", "v", "g", "s", "beta")}
+    B, T, H, DK = tok.q.shape
+    o = torch.empty((B, T, H, 128), dtype=torch.float32, device="cuda:0")
+    ht = torch.empty((B, H, 128, 128), dtype=torch.float32, device="cuda:0")
+    fn = lambda: ckda.fwd(**d, o=o, ht=ht)
+    log("timing forward")
+    wall, per = time_kernel_launches(torch, fn, steps, warmup)
+    tokens = B * T
+    th = B * T * H
+    ms = wall / steps
+    avg_launch = float(np.mean(per))
+    return dict(w=w, tokens=tokens, ms=ms, launch_ms=avg_launch, launch_all=per,
+                bytes=th * FWD_BYTES_PER_TOKEN_HEAD, flops=th * FWD_FLOPS_PER_TOKEN_HEAD)
+
+
+def bench_decode(torch, nsteps=512, distinct=64):
+    """256 sequences x 16 heads, nsteps sequential steps from a state drawn
+    N(0, 0.02).  Step inputs are drawn for `distinct` steps and reused
+    cyclically (same shapes and distributions; the state still evolves
+    over all nsteps)."""
+    from gated_delta_rule_sign_amd import ckda
+    from gated_delta_rule_sign_amd import inputs as I
+    cfg = I.WORKLOADS["decode_b256"]
+    N, H, D = cfg["N"], cfg["H"], cfg["DK"]
+    seed = I.SEED_BASE + cfg["index"]
+    log(f"generating decode inputs ({distinct} distinct steps)")
+    rng = np.random.default_rng(seed)
+    state0 = I.draw_state(rng, (N, H, D, D), 0.02)
+    tok = I.decode_steps(seed, 0, distinct, N, H, D, D, "bf16")
+    dq = {k: dev_tensor(torch, getattr(tok, k)) for k in ("q", "k", "v", "g", "s", "beta")}
+    state = dev_tensor(torch, state0)
+    sp = torch.ones((N, H, D), dtype=torch.int8, device="cuda:0")
+    o = torch.empty((N, H, D), dtype=torch.float32, device="cuda:0")
+    it = [0]
+
+    def step():
+        t = it[0] % distinct
+        it[0] += 1
+        ckda.decode_step(dq["q"][t], dq["k"][t], dq["v"][t], dq["g"][t], dq["s"][t], dq["beta"][t],
+                         state, sp, o=o)
+
+    log("timing decode")
+    wall, per = time_kernel_launches(torch, step, nsteps, 8)
+    per_step = wall / nsteps
+    bytes_step = N * H * DEC_BYTES_PER_HEAD_STEP
+    return dict(ms_per_step=per_step, launch_ms=float(np.mean(per)), bytes_per_step=bytes_step,
+                gbs=bytes_step / (float(np.mean(per)) * 1e-3) / 1e9,
+                seq_steps_per_s=N / (per_step * 1e-3), steps=nsteps)
+
+
+def bench_bwd(torch, w, steps, warmup):
+    from gated_delta_rule_sign_amd import ckda
+    tok = w.tok
+    d = {k: dev_tensor(torch, getattr(tok, k)) for k in ("q", "k", "v", "g", "s", "beta")}
+    from gated_delta_rule_sign_amd import inputs as I
+    rng = np.random.default_rng(I.SEED_BASE + I.WORKLOADS["layer_bwd"]["index"])
+    do = dev_tensor(torch, I.to_storage(rng.standard_normal(tok.v.shape), "bf16"))
+    _, _, hc = ckda.fwd(**d, want_ckpt=True)
+    try:
+        fn = lambda: ckda.bwd(**d, h_ckpt=hc, do=do)
+        fn()
+    except ckda.CkdaError as e:
+        log(f"backward not available: {e}")
+        return None
+    wall, per = time_kernel_launches(torch, fn, steps, warmup)
+    B, T, H, _ = tok.q.shape
+    return dict(ms=wall / steps, tokens_per_s=B * T / (wall / steps * 1e-3))
+
+
+def bench_copy(torch, nbytes=1 << 30, reps=5):
+    """A plain device copy of known size (calibration for HBM byte counters)."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").uniform_()
+    dst = torch.empty_like(src)
+    wall, per = time_kernel_launches(torch, lambda: dst.copy_(src), reps, 2)
+    return dict(bytes_read=nbytes, bytes_written=nbytes, launch_ms=float(np.mean(per)),
+                gbs=2 * nbytes / (float(np.mean(per)) * 1e-3) / 1e9)
+
+
+def cpu_baseline(w, nchains=32):
+    """The float64 CPU oracle on a bounded sample of the same workload:
+    `nchains` of the 128 (sequence, head) chains, all 4096 tokens and all
+    128 value columns."""
+    import oracle
+    f = w.tok.f64()
+    B, T, H, _ = f["q"].shape
+    rng = np.random.default_rng(0)
+    idx = rng.choice(B * H, size=nchains, replace=False)
+    chains = [(int(i) // H, int(i) % H) for i in idx]
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.fwd(**f, chains=chains)
+    dt = time.perf_counter() - t0
+    # a layer token carries H heads: chain-tokens / H = layer tokens
+    return dict(value=nchains * T / H / dt, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{nchains} of {B * H} (sequence, head) chains of layer_bf16, all {T} tokens "
+                       f"and 128 value columns; float64 token recurrence; {dt:.1f} s; "
+                       f"value = chain-tokens / {H} heads / seconds",
+                seconds=dt)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", choices=["fwd", "decode", "bwd", "copy"], default=None)
+    ap.add_argument("--decode-steps", type=int, default=512)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the path shards over "
+              "(sequence, head) chains with no exchange, so N GPUs is N independent copies.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    from gated_delta_rule_sign_amd import ckda
+    ckda.lib()
+
+    if args.only == "copy":
+        print(json.dumps(bench_copy(torch)))
+        return
+    if args.only == "decode":
+        print(json.dumps(bench_decode(torch, args.decode_steps)))
+        return
+
+    fw = bench_fwd(torch, args.steps, args.warmup)
+    if args.only == "fwd":
+        print(json.dumps({k: v for k, v in fw.items() if k not in ("w", "launch_all")}))
+        return
+    dec = bench_decode(torch, args.decode_steps)
+    bw = bench_bwd(torch, fw["w"], max(3, args.steps // 4), 1)
+    cpu = None if args.no_cpu else cpu_baseline(fw["w"])
+
+    achieved = fw["bytes"] / (fw["launch_ms"] * 1e-3) / 1e9
+    value = fw["tokens"] / (fw["ms"] * 1e-3)
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": fw["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "layer_bf16: one CKDA mixer of the 1.36B model, forward prefill",
+                   "B": 8, "T": 4096, "H": 16, "dk": 128, "dv": 128, "chunk": 64,
+                   "inputs": "q,k,v bf16; g,beta f32; s int8", "state_and_outputs": "f32"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "ckda_fwd_kernel<bf16,128,128>",
+                     "algorithmic_bytes_per_launch": fw["bytes"],
+                     "avg_launch_ms": fw["launch_ms"],
+                     "mfma_algorithmic_frac": fw["flops"] / (fw["launch_ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "decode": {"workload": "decode_b256: 256 seqs x 16 heads, dk=dv=128, 512 steps",
+                   "unit": "GB/s", "value": dec["gbs"], "frac_of_hbm_peak": dec["gbs"] / HBM_PEAK_GBS,
+                   "ms_per_step": dec["ms_per_step"], "seq_steps_per_s": dec["seq_steps_per_s"],
+                   "algorithmic_bytes_per_step": dec["bytes_per_step"]},
+        "backward": None if bw is None else {"workload": "layer_bwd (layer_bf16 shapes, do bf16)",
+                                             "unit": "tokens/s", "value": bw["tokens_per_s"], "ms": bw["ms"]},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

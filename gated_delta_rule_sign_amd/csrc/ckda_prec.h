@@ -1,0 +1,155 @@
+// ckda_prec.h -- matrix-core precision policies for the chunked kernels.
+//
+// Operands staged in LDS take 4 bytes per element in both policies:
+//  * Prec<false> (bf16 inputs): two bf16 planes, hi = bf16(x) and
+//    lo = bf16(x - hi); a product is hi*hi + hi*lo + lo*hi on the bf16
+//    matrix cores (v_mfma_f32_16x16x32_bf16 / 16x16x16), fp32 accumulate.
+//  * Prec<true> (fp32 inputs): one fp32 plane; products on the fp32 matrix
+//    cores (v_mfma_f32_16x16x4_f32), one instruction per K-slot.
+//
+// Fragment conventions (wave64, lane L, n = L % 16, g = L / 16):
+//  * Frag8: 8 K-slots per lane.  A lane (n, g) supplies row n, B lane (n, g)
+//    column n; slot j of A lane (., g) meets slot j of B lane (., g).  Each
+//    call site picks which K index each (g, j) carries, identically for A
+//    and B.
+//  * Frag4: 4 K-slots, for 16x16x16 products.  Its B layout equals the C/D
+//    layout of a 16x16 result (lane (n, g) holds rows 4g..4g+3, column n).
+//  * C/D: lane (n, g) holds rows 4g + i (i = 0..3) of column n.
+#pragma once
+#include "ckda_mfma.h"
+
+namespace ckda {
+
+// An LDS operand region: `rows x pitch` elements; in the bf16 policy the lo
+// plane follows the hi plane at `plane` elements.
+struct LdsMat {
+    unsigned char* base;
+    int pitch;   // elements per row
+    int plane;   // elements between the hi and lo planes (bf16 policy)
+};
+
+template <bool F32>
+struct Prec;
+
+template <>
+struct Prec<false> {
+    struct F8 { bf16x8 hi, lo; };
+    struct F4 { s16x4 hi, lo; };
+    static constexpr int kBytes = 4;   // per element, both planes together
+
+    static __device__ __forceinline__ uint16_t* hp(const LdsMat& m, int r, int c) {
+        return reinterpret_cast<uint16_t*>(m.base) + r * m.pitch + c;
+    }
+    static __device__ __forceinline__ uint16_t* lp(const LdsMat& m, int r, int c) {
+        return reinterpret_cast<uint16_t*>(m.base) + m.plane + r * m.pitch + c;
+    }
+    // 8 consecutive elements (16-byte aligned in each plane)
+    static __device__ __forceinline__ void store8(const LdsMat& m, int r, int c, const float (&x)[8]) {
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint16_t h0, l0, h1, l1;
+            split1(x[2 * i], h0, l0);
+            split1(x[2 * i + 1], h1, l1);
+            h[i] = h0 | (static_cast<uint32_t>(h1) << 16);
+            l[i] = l0 | (static_cast<uint32_t>(l1) << 16);
+        }
+        *reinterpret_cast<uint4*>(hp(m, r, c)) = make_uint4(h[0], h[1], h[2], h[3]);
+        *reinterpret_cast<uint4*>(lp(m, r, c)) = make_uint4(l[0], l[1], l[2], l[3]);
+    }
+    // 4 consecutive elements (8-byte aligned)
+    static __device__ __forceinline__ void store4(const LdsMat& m, int r, int c, f32x4 x) {
+        uint16_t h[4], l[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) split1(x[i], h[i], l[i]);
+        *reinterpret_cast<uint2*>(hp(m, r, c)) =
+            make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
+        *reinterpret_cast<uint2*>(lp(m, r, c)) =
+            make_uint2(l[0] | (uint32_t(l[1]) << 16), l[2] | (uint32_t(l[3]) << 16));
+    }
+    static __device__ __forceinline__ void store1(const LdsMat& m, int r, int c, float x) {
+        uint16_t h, l;
+        split1(x, h, l);
+        *hp(m, r, c) = h;
+        *lp(m, r, c) = l;
+    }
+    // copy one element between regions without re-rounding
+    static __device__ __forceinline__ void copy1(const LdsMat& d, int dr, int dc, const LdsMat& s, int sr, int sc) {
+        *hp(d, dr, dc) = *hp(s, sr, sc);
+        *lp(d, dr, dc) = *lp(s, sr, sc);
+    }
+    static __device__ __forceinline__ F8 load8(const LdsMat& m, int r, int c) {
+        return F8{lds8(hp(m, r, c)), lds8(lp(m, r, c))};
+    }
+    static __device__ __forceinline__ F8 load4x2(const LdsMat& m, int r, int ca, int cb) {
+        return F8{lds4x2(hp(m, r, ca), hp(m, r, cb)), lds4x2(lp(m, r, ca), lp(m, r, cb))};
+    }
+    static __device__ __forceinline__ F4 load4(const LdsMat& m, int r, int c) {
+        return F4{lds4s(hp(m, r, c)), lds4s(lp(m, r, c))};
+    }
+    static __device__ __forceinline__ F8 regs8(f32x4 a, f32x4 b) {
+        const Split8 s = split8(a, b);
+        return F8{s.hi, s.lo};
+    }
+    static __device__ __forceinline__ F4 regs4(f32x4 a) {
+        const Split4 s = split4(a);
+        return F4{s.hi, s.lo};
+    }
+    static __device__ __forceinline__ f32x4 mma8(const F8& a, const F8& b, f32x4 acc) {
+        return mfma32x3(a.hi, a.lo, b.hi, b.lo, acc);
+    }
+    static __device__ __forceinline__ f32x4 mma4(const F4& a, const F4& b, f32x4 acc) {
+        return mfma16x3(a.hi, a.lo, b.hi, b.lo, acc);
+    }
+};
+
+template <>
+struct Prec<true> {
+    struct F8 { f32x4 a, b; };
+    struct F4 { f32x4 a; };
+    static constexpr int kBytes = 4;
+
+    static __device__ __forceinline__ float* fp(const LdsMat& m, int r, int c) {
+        return reinterpret_cast<float*>(m.base) + r * m.pitch + c;
+    }
+    static __device__ __forceinline__ void store8(const LdsMat& m, int r, int c, const float (&x)[8]) {
+        float4* p = reinterpret_cast<float4*>(fp(m, r, c));
+        p[0] = make_float4(x[0], x[1], x[2], x[3]);
+        p[1] = make_float4(x[4], x[5], x[6], x[7]);
+    }
+    static __device__ __forceinline__ void store4(const LdsMat& m, int r, int c, f32x4 x) {
+        *reinterpret_cast<float4*>(fp(m, r, c)) = make_float4(x[0], x[1], x[2], x[3]);
+    }
+    static __device__ __forceinline__ void store1(const LdsMat& m, int r, int c, float x) { *fp(m, r, c) = x; }
+    static __device__ __forceinline__ void copy1(const LdsMat& d, int dr, int dc, const LdsMat& s, int sr, int sc) {
+        *fp(d, dr, dc) = *fp(s, sr, sc);
+    }
+    static __device__ __forceinline__ f32x4 ld4(const float* p) {
+        const float4 v = *reinterpret_cast<const float4*>(p);
+        f32x4 r = {v.x, v.y, v.z, v.w};
+        return r;
+    }
+    static __device__ __forceinline__ F8 load8(const LdsMat& m, int r, int c) {
+        return F8{ld4(fp(m, r, c)), ld4(fp(m, r, c + 4))};
+    }
+    static __device__ __forceinline__ F8 load4x2(const LdsMat& m, int r, int ca, int cb) {
+        return F8{ld4(fp(m, r, ca)), ld4(fp(m, r, cb))};
+    }
+    static __device__ __forceinline__ F4 load4(const LdsMat& m, int r, int c) { return F4{ld4(fp(m, r, c))}; }
+    static __device__ __forceinline__ F8 regs8(f32x4 a, f32x4 b) { return F8{a, b}; }
+    static __device__ __forceinline__ F4 regs4(f32x4 a) { return F4{a}; }
+    static __device__ __forceinline__ f32x4 mma8(const F8& x, const F8& y, f32x4 acc) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.a[j], y.a[j], acc, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.b[j], y.b[j], acc, 0, 0, 0);
+        return acc;
+    }
+    static __device__ __forceinline__ f32x4 mma4(const F4& x, const F4& y, f32x4 acc) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.a[j], y.a[j], acc, 0, 0, 0);
+        return acc;
+    }
+};
+
+}  // namespace ckda

@@ -32,6 +32,7 @@
 #include "ckda_device.h"
 #include "ckda_launch.h"
 #include "ckda_mfma.h"
+#include "ckda_prec.h"
 
 namespace ckda {
 
@@ -125,28 +126,6 @@ struct Raw8<float> {
     }
 };
 
-__device__ __forceinline__ void store_split8(uint16_t* hi, uint16_t* lo, const float (&x)[8]) {
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint16_t h0, l0, h1, l1;
-        split1(x[2 * i], h0, l0);
-        split1(x[2 * i + 1], h1, l1);
-        h[i] = h0 | (static_cast<uint32_t>(h1) << 16);
-        l[i] = l0 | (static_cast<uint32_t>(l1) << 16);
-    }
-    *reinterpret_cast<uint4*>(hi) = make_uint4(h[0], h[1], h[2], h[3]);
-    *reinterpret_cast<uint4*>(lo) = make_uint4(l[0], l[1], l[2], l[3]);
-}
-
-__device__ __forceinline__ void store_split4(uint16_t* hi, uint16_t* lo, f32x4 x) {
-    uint16_t h[4], l[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) split1(x[i], h[i], l[i]);
-    *reinterpret_cast<uint2*>(hi) = make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
-    *reinterpret_cast<uint2*>(lo) = make_uint2(l[0] | (uint32_t(l[1]) << 16), l[2] | (uint32_t(l[3]) << 16));
-}
-
 struct FwdParams {
     const void *q, *k, *v;
     const float* g;
@@ -165,43 +144,36 @@ template <typename Tin, int DK, int DV>
 __global__ void __launch_bounds__(256, 1) ckda_fwd_kernel(FwdParams p)
 {
     using SH = FwdShape<DK, DV>;
+    // fp32 inputs run the fp32 matrix cores, bf16 inputs the split bf16 ones
+    using PR = Prec<sizeof(Tin) == 4>;
     constexpr int NOCT = SH::NOCT, TG = SH::TG, TPL = SH::TPL, KS = SH::KS, RT = SH::RT;
     constexpr int PK = SH::PK, PM = SH::PM, PY = SH::PY;
     extern __shared__ __align__(16) unsigned char smem[];
 
     // LDS views; CKDA_LDS_VIEWS() re-derives them from an opaque base (see opaque_zero)
-#define CKDA_LDS_VIEWS()                                                                 \
-    unsigned char* const sm_ = smem + opaque_zero();                                     \
-    uint16_t* const rowk_hi = reinterpret_cast<uint16_t*>(sm_ + SH::A_ROWK);             \
-    uint16_t* const rowk_lo = rowk_hi + 64 * PK;                                         \
-    uint16_t* const rowq_hi = reinterpret_cast<uint16_t*>(sm_ + SH::A_ROWQ);             \
-    uint16_t* const rowq_lo = rowq_hi + 64 * PK;                                         \
-    uint16_t* const colk_hi = reinterpret_cast<uint16_t*>(sm_ + SH::A_COLK);             \
-    uint16_t* const colk_lo = colk_hi + 64 * PK;                                         \
-    uint16_t* const colkf_hi = reinterpret_cast<uint16_t*>(sm_ + SH::A_COLKF);           \
-    uint16_t* const colkf_lo = colkf_hi + 32 * PK;                                       \
-    uint16_t* const m_hi = reinterpret_cast<uint16_t*>(sm_ + SH::B_M);                   \
-    uint16_t* const m_lo = m_hi + 64 * PM;                                               \
-    uint16_t* const loff_hi = reinterpret_cast<uint16_t*>(sm_ + SH::B_LOFF);             \
-    uint16_t* const loff_lo = loff_hi + 6 * 16 * PY;                                     \
-    uint16_t* const y_hi = reinterpret_cast<uint16_t*>(sm_ + SH::B_Y);                   \
-    uint16_t* const y_lo = y_hi + 4 * 16 * PY;                                           \
-    uint16_t* const ckt_hi = reinterpret_cast<uint16_t*>(sm_ + SH::B_CKT);               \
-    uint16_t* const ckt_lo = ckt_hi + DK * PM;                                           \
-    float* const ldiag = reinterpret_cast<float*>(sm_ + SH::B_LDIAG);   /* [4][16][17] */\
-    float* const wtot_b = reinterpret_cast<float*>(sm_ + SH::F_WTOT);   /* [4][DK] */    \
-    float* const wtot_p = wtot_b + 4 * DK;                              /* [4][DK] */    \
-    float* const ch_em0 = reinterpret_cast<float*>(sm_ + SH::F_CH);     /* e^{m0} */     \
-    float* const ch_em1 = ch_em0 + DK;                                  /* e^{m1} */     \
-    float* const ch_d = ch_em1 + DK;                                    /* P_L e^{b_L} */\
-    float* const ch_f0 = ch_d + DK;                           /* P_L e^{b_L - m0} */     \
-    float* const ch_f1 = ch_f0 + DK;                          /* P_L e^{b_L - m1} */     \
-    float* const beta_s = reinterpret_cast<float*>(sm_ + SH::F_BETA);                    \
-    (void)rowk_hi; (void)rowk_lo; (void)rowq_hi; (void)rowq_lo; (void)colk_hi;           \
-    (void)colk_lo; (void)colkf_hi; (void)colkf_lo; (void)m_hi; (void)m_lo; (void)loff_hi;\
-    (void)loff_lo; (void)y_hi; (void)y_lo; (void)ckt_hi; (void)ckt_lo; (void)ldiag;      \
-    (void)wtot_b; (void)wtot_p; (void)ch_em0; (void)ch_em1; (void)ch_d; (void)ch_f0;     \
-    (void)ch_f1; (void)beta_s
+    // LDS views; CKDA_LDS_VIEWS() re-derives them from an opaque base (see opaque_zero)
+#define CKDA_LDS_VIEWS()                                                                   \
+    unsigned char* const sm_ = smem + opaque_zero();                                       \
+    const LdsMat colk{sm_ + SH::A_COLK, PK, 64 * PK};                                      \
+    const LdsMat colkf{sm_ + SH::A_COLKF, PK, 32 * PK};                                    \
+    const LdsMat rowk{sm_ + SH::A_ROWK, PK, 64 * PK};                                      \
+    const LdsMat rowq{sm_ + SH::A_ROWQ, PK, 64 * PK};                                      \
+    const LdsMat mmat{sm_ + SH::B_M, PM, 64 * PM};                                         \
+    const LdsMat loff{sm_ + SH::B_LOFF, PY, 6 * 16 * PY};                                  \
+    const LdsMat ymat{sm_ + SH::B_Y, PY, 4 * 16 * PY};                                     \
+    const LdsMat ckt{sm_ + SH::B_CKT, PM, DK * PM};                                        \
+    float* const ldiag = reinterpret_cast<float*>(sm_ + SH::B_LDIAG);   /* [4][16][17] */  \
+    float* const wtot_b = reinterpret_cast<float*>(sm_ + SH::F_WTOT);   /* [4][DK] */      \
+    float* const wtot_p = wtot_b + 4 * DK;                              /* [4][DK] */      \
+    float* const ch_em0 = reinterpret_cast<float*>(sm_ + SH::F_CH);     /* e^{m0} */       \
+    float* const ch_em1 = ch_em0 + DK;                                  /* e^{m1} */       \
+    float* const ch_d = ch_em1 + DK;                                    /* P_L e^{b_L} */  \
+    float* const ch_f0 = ch_d + DK;                           /* P_L e^{b_L - m0} */       \
+    float* const ch_f1 = ch_f0 + DK;                          /* P_L e^{b_L - m1} */       \
+    float* const beta_s = reinterpret_cast<float*>(sm_ + SH::F_BETA);                      \
+    (void)colk; (void)colkf; (void)rowk; (void)rowq; (void)mmat; (void)loff; (void)ymat;   \
+    (void)ckt; (void)ldiag; (void)wtot_b; (void)wtot_p; (void)ch_em0; (void)ch_em1;        \
+    (void)ch_d; (void)ch_f0; (void)ch_f1; (void)beta_s
 
     const Tin* __restrict__ q = static_cast<const Tin*>(p.q);
     const Tin* __restrict__ k = static_cast<const Tin*>(p.k);
@@ -377,14 +349,14 @@ __global__ void __launch_bounds__(256, 1) ckda_fwd_kernel(FwdParams p)
                 rq[e] = (P * qr[tt].get(e)) * e1;
                 ck[e] = kf * e2;
             }
-            store_split8(rowk_hi + t * PK + 8 * co, rowk_lo + t * PK + 8 * co, rk);
-            store_split8(rowq_hi + t * PK + 8 * co, rowq_lo + t * PK + 8 * co, rq);
-            store_split8(colk_hi + t * PK + 8 * co, colk_lo + t * PK + 8 * co, ck);
+            PR::store8(rowk, t, 8 * co, rk);
+            PR::store8(rowq, t, 8 * co, rq);
+            PR::store8(colk, t, 8 * co, ck);
             if (w < 2) {
                 float cf[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) cf[e] = ck[e] * exp2_clamped((m1[e] - m0[e]) * kLog2e);
-                store_split8(colkf_hi + t * PK + 8 * co, colkf_lo + t * PK + 8 * co, cf);
+                PR::store8(colkf, t, 8 * co, cf);
             }
             CKDA_FENCE();
         }
@@ -406,19 +378,13 @@ __global__ void __launch_bounds__(256, 1) ckda_fwd_kernel(FwdParams p)
                 else { R = 3 - w; I = x - w - 1; isA = 0; }
                 tR[x] = R; tI[x] = I; tIsA[x] = isA;
                 const bool cross = (R >= 2) && (I < 2);
-                const uint16_t* ch = cross ? colkf_hi : colk_hi;
-                const uint16_t* cl = cross ? colkf_lo : colk_lo;
-                const uint16_t* rh = isA ? rowk_hi : rowq_hi;
-                const uint16_t* rl = isA ? rowk_lo : rowq_lo;
+                const LdsMat& cm = cross ? colkf : colk;
+                const LdsMat& rm = isA ? rowk : rowq;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const int ko = 32 * ks + 8 * gq;
-                    const bf16x8 ah = lds8(ch + (16 * I + n) * PK + ko);
-                    const bf16x8 al = lds8(cl + (16 * I + n) * PK + ko);
-                    const bf16x8 bh = lds8(rh + (16 * R + n) * PK + ko);
-                    const bf16x8 bl8 = lds8(rl + (16 * R + n) * PK + ko);
-                    acc = mfma32x3(ah, al, bh, bl8, acc);
+                    acc = PR::mma8(PR::load8(cm, 16 * I + n, ko), PR::load8(rm, 16 * R + n, ko), acc);
                 }
                 tacc[x] = acc;
                 CKDA_FENCE();
@@ -429,7 +395,7 @@ __global__ void __launch_bounds__(256, 1) ckda_fwd_kernel(FwdParams p)
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const float* em = hh ? ch_em1 : ch_em0;
-                Split8 Bs[KS];
+                typename PR::F8 Bs[KS];
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     f32x4 a, b;
@@ -438,7 +404,7 @@ __global__ void __launch_bounds__(256, 1) ckda_fwd_kernel(FwdParams p)
                         a[i] = em[32 * ks + 4 * gq + i] * S[2 * ks][i];
                         b[i] = em[32 * ks + 16 + 4 * gq + i] * S[2 * ks + 1][i];
                     }
-                    Bs[ks] = split8(a, b);
+                    Bs[ks] = PR::regs8(a, b);
                 }
 #pragma unroll
                 for (int R = 2 * hh; R < 2 * hh + 2; ++R) {
@@ -447,12 +413,8 @@ __global__ void __launch_bounds__(256, 1) ckda_fwd_kernel(FwdParams p)
                     for (int ks = 0; ks < KS; ++ks) {
                         const int r = 16 * R + n;
                         const int ka = 32 * ks + 4 * gq, kb = 32 * ks + 16 + 4 * gq;
-                        const bf16x8 kh = lds4x2(rowk_hi + r * PK + ka, rowk_hi + r * PK + kb);
-                        const bf16x8 kl = lds4x2(rowk_lo + r * PK + ka, rowk_lo + r * PK + kb);
-                        const bf16x8 qh = lds4x2(rowq_hi + r * PK + ka, rowq_hi + r * PK + kb);
-                        const bf16x8 ql = lds4x2(rowq_lo + r * PK + ka, rowq_lo + r * PK + kb);
-                        ak = mfma32x3(kh, kl, Bs[ks].hi, Bs[ks].lo, ak);
-                        aq = mfma32x3(qh, ql, Bs[ks].hi, Bs[ks].lo, aq);
+                        ak = PR::mma8(PR::load4x2(rowk, r, ka, kb), Bs[ks], ak);
+                        aq = PR::mma8(PR::load4x2(rowq, r, ka, kb), Bs[ks], aq);
                     }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -490,14 +452,13 @@ __global__ void __launch_bounds__(256, 1) ckda_fwd_kernel(FwdParams p)
                     f32x4 nv;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) nv[i] = -br * val[i];
-                    const int blk = loff_index(R, I);
-                    store_split4(loff_hi + (blk * 16 + n) * PY + 4 * gq, loff_lo + (blk * 16 + n) * PY + 4 * gq, nv);
+                    PR::store4(loff, loff_index(R, I) * 16 + n, 4 * gq, nv);
                 }
             } else {
                 f32x4 mv;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) mv[i] = (R > I || 4 * gq + i <= n) ? val[i] : 0.f;
-                store_split4(m_hi + r * PM + 16 * I + 4 * gq, m_lo + r * PM + 16 * I + 4 * gq, mv);
+                PR::store4(mmat, r, 16 * I + 4 * gq, mv);
             }
         }
         // M . U reads the upper blocks (0,1) and (2,3) of M as part of its
@@ -505,23 +466,14 @@ __global__ void __launch_bounds__(256, 1) ckda_fwd_kernel(FwdParams p)
         if (w == 3 || w == 1) {
             const int R = (w == 3) ? 0 : 2;
             const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-            store_split4(m_hi + (16 * R + n) * PM + 16 * (R + 1) + 4 * gq,
-                         m_lo + (16 * R + n) * PM + 16 * (R + 1) + 4 * gq, zero);
+            PR::store4(mmat, 16 * R + n, 16 * (R + 1) + 4 * gq, zero);
         }
         // transposed copy of the column operand (phase B leaves colk intact)
 #pragma unroll
         for (int tt = 0; tt < TPL; ++tt) {
             const int t = 16 * w + tg * TPL + tt;
-            const uint4 hv = *reinterpret_cast<const uint4*>(colk_hi + t * PK + 8 * co);
-            const uint4 lv = *reinterpret_cast<const uint4*>(colk_lo + t * PK + 8 * co);
-            const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
-            const uint32_t lw[4] = {lv.x, lv.y, lv.z, lv.w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int c = 8 * co + e;
-                ckt_hi[c * PM + t] = static_cast<uint16_t>(hw[e >> 1] >> (16 * (e & 1)));
-                ckt_lo[c * PM + t] = static_cast<uint16_t>(lw[e >> 1] >> (16 * (e & 1)));
-            }
+            for (int e = 0; e < 8; ++e) PR::copy1(ckt, 8 * co + e, t, colk, t, 8 * co + e);
         }
         __syncthreads();
 
@@ -542,12 +494,7 @@ __global__ void __launch_bounds__(256, 1) ckda_fwd_kernel(FwdParams p)
                 CKDA_FENCE();
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                uint16_t hh, ll;
-                split1(y[r], hh, ll);
-                y_hi[(J * 16 + r) * PY + c] = hh;
-                y_lo[(J * 16 + r) * PY + c] = ll;
-            }
+            for (int r = 0; r < 16; ++r) PR::store1(ymat, J * 16 + r, c, y[r]);
         }
         __syncthreads();
 
@@ -557,44 +504,29 @@ __global__ void __launch_bounds__(256, 1) ckda_fwd_kernel(FwdParams p)
         CKDA_LDS_VIEWS();
         if (has_col) {
             f32x4 U[4];
-            Split4 Us[4];
+            typename PR::F4 Us[4];
 #pragma unroll
             for (int J = 0; J < 4; ++J) {
                 f32x4 z;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) z[i] = beta_s[16 * J + 4 * gq + i] * Rt[J][i];
 #pragma unroll
-                for (int K = 0; K < J; ++K) {
-                    const int blk = loff_index(J, K);
-                    const s16x4 ah = lds4s(loff_hi + (blk * 16 + n) * PY + 4 * gq);
-                    const s16x4 al = lds4s(loff_lo + (blk * 16 + n) * PY + 4 * gq);
-                    z = mfma16x3(ah, al, Us[K].hi, Us[K].lo, z);
-                }
-                const Split4 zs = split4(z);
-                const s16x4 yh = lds4s(y_hi + (J * 16 + n) * PY + 4 * gq);
-                const s16x4 yl = lds4s(y_lo + (J * 16 + n) * PY + 4 * gq);
+                for (int K = 0; K < J; ++K)
+                    z = PR::mma4(PR::load4(loff, loff_index(J, K) * 16 + n, 4 * gq), Us[K], z);
                 const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                U[J] = mfma16x3(yh, yl, zs.hi, zs.lo, zero);
-                Us[J] = split4(U[J]);
+                U[J] = PR::mma4(PR::load4(ymat, J * 16 + n, 4 * gq), PR::regs4(z), zero);
+                Us[J] = PR::regs4(U[J]);
                 CKDA_FENCE();
             }
-            const Split8 U01 = split8(U[0], U[1]);
-            const Split8 U23 = split8(U[2], U[3]);
+            const typename PR::F8 U01 = PR::regs8(U[0], U[1]);
+            const typename PR::F8 U23 = PR::regs8(U[2], U[3]);
             // O = Q^S + M U
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
                 f32x4 acc = OQ[R];
                 const int r = 16 * R + n;
-                {
-                    const bf16x8 mh8 = lds4x2(m_hi + r * PM + 4 * gq, m_hi + r * PM + 16 + 4 * gq);
-                    const bf16x8 ml8 = lds4x2(m_lo + r * PM + 4 * gq, m_lo + r * PM + 16 + 4 * gq);
-                    acc = mfma32x3(mh8, ml8, U01.hi, U01.lo, acc);
-                }
-                if (R >= 2) {
-                    const bf16x8 mh8 = lds4x2(m_hi + r * PM + 32 + 4 * gq, m_hi + r * PM + 48 + 4 * gq);
-                    const bf16x8 ml8 = lds4x2(m_lo + r * PM + 32 + 4 * gq, m_lo + r * PM + 48 + 4 * gq);
-                    acc = mfma32x3(mh8, ml8, U23.hi, U23.lo, acc);
-                }
+                acc = PR::mma8(PR::load4x2(mmat, r, 4 * gq, 16 + 4 * gq), U01, acc);
+                if (R >= 2) acc = PR::mma8(PR::load4x2(mmat, r, 32 + 4 * gq, 48 + 4 * gq), U23, acc);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int t = 16 * R + 4 * gq + i;
@@ -606,13 +538,9 @@ __global__ void __launch_bounds__(256, 1) ckda_fwd_kernel(FwdParams p)
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 const int c = 16 * rt + n;
-                const bf16x8 a0h = lds4x2(ckt_hi + c * PM + 4 * gq, ckt_hi + c * PM + 16 + 4 * gq);
-                const bf16x8 a0l = lds4x2(ckt_lo + c * PM + 4 * gq, ckt_lo + c * PM + 16 + 4 * gq);
-                const bf16x8 a1h = lds4x2(ckt_hi + c * PM + 32 + 4 * gq, ckt_hi + c * PM + 48 + 4 * gq);
-                const bf16x8 a1l = lds4x2(ckt_lo + c * PM + 32 + 4 * gq, ckt_lo + c * PM + 48 + 4 * gq);
                 const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                const f32x4 acc0 = mfma32x3(a0h, a0l, U01.hi, U01.lo, zero);
-                const f32x4 acc1 = mfma32x3(a1h, a1l, U23.hi, U23.lo, zero);
+                const f32x4 acc0 = PR::mma8(PR::load4x2(ckt, c, 4 * gq, 16 + 4 * gq), U01, zero);
+                const f32x4 acc1 = PR::mma8(PR::load4x2(ckt, c, 32 + 4 * gq, 48 + 4 * gq), U23, zero);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int cc = 16 * rt + 4 * gq + i;

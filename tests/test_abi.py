@@ -55,6 +55,7 @@ def test_fwd_rejects_bad_arguments(L):
     assert fwd(L, q=None) == 1
     assert b"'q'" in L.ckda_last_error()
     assert fwd(L, o=None) == 1
+    assert fwd(L, T=0, o=None, q=None) != 1      # no tokens: o and q are not needed
     assert fwd(L, g=P(0x1004)) == 4              # misaligned
     assert fwd(L, B=0) == 0                      # empty problem: nothing to do
     assert L.ckda_last_error() == b""
