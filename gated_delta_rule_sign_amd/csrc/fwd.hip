@@ -94,6 +94,15 @@ __device__ __forceinline__ int opaque_zero() {
     return z;
 }
 
+// Workgroup barrier that orders LDS only: waits for this wave's LDS traffic,
+// not for its global loads/stores still in flight (those are prefetches of
+// the next chunk and output stores nobody in the workgroup reads).
+__device__ __forceinline__ void lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // off-diagonal 16x16 block index of (J, K), K < J
 __device__ __forceinline__ int loff_index(int J, int K) { return (J * (J - 1)) / 2 + K; }
 
@@ -124,6 +133,16 @@ struct Raw8<float> {
             case 4: return b.x; case 5: return b.y; case 6: return b.z; default: return b.w;
         }
     }
+};
+
+// The prep inputs of one lane for one chunk: channels 8co..8co+7 of the
+// lane's TPL tokens (loaded one chunk ahead of use).
+template <typename Tin, int TPL>
+struct PrepIn {
+    float4 g0[TPL], g1[TPL];
+    uint2 s8[TPL];
+    Raw8<Tin> q[TPL], k[TPL];
+    float beta[TPL];
 };
 
 struct FwdParams {
@@ -234,9 +253,53 @@ __global__ void __launch_bounds__(256, 1) ckda_fwd_kernel(FwdParams p)
             S[rt][i] = (has_col && p.h0) ? p.h0[st_off + static_cast<size_t>(16 * rt + 4 * gq + i) * DV + col] : 0.f;
 
     const int nchunks = (len + 63) / 64;
+
+    // ---- global loads, issued one chunk ahead of their use ----------------
+    auto load_prep = [&](PrepIn<Tin, TPL>& in, int cc0, int LL) {
+#pragma unroll
+        for (int tt = 0; tt < TPL; ++tt) {
+            const int t = 16 * w + tg * TPL + tt;
+            if (t < LL) {
+                const size_t row = static_cast<size_t>(tok0 + cc0 + t) * H + h;
+                const size_t base = row * DK + 8 * co;
+                in.g0[tt] = reinterpret_cast<const float4*>(p.g + base)[0];
+                in.g1[tt] = reinterpret_cast<const float4*>(p.g + base)[1];
+                in.s8[tt] = *reinterpret_cast<const uint2*>(p.s + base);
+                in.q[tt].load(q + base);
+                in.k[tt].load(k + base);
+                in.beta[tt] = (co == 0) ? p.beta[row] : 0.f;
+            } else {   // padding token: g = 0, s = +1, q = k = 0, beta = 0
+                in.g0[tt] = make_float4(0.f, 0.f, 0.f, 0.f);
+                in.g1[tt] = in.g0[tt];
+                in.s8[tt] = make_uint2(0x01010101u, 0x01010101u);
+                in.q[tt].zero();
+                in.k[tt].zero();
+                in.beta[tt] = 0.f;
+            }
+        }
+    };
+    auto load_v = [&](float (&vv)[4][4], int cc0, int LL) {
+#pragma unroll
+        for (int R = 0; R < 4; ++R)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * R + 4 * gq + i;
+                vv[R][i] = (has_col && t < LL)
+                               ? Elem<Tin>::load(v, (static_cast<size_t>(tok0 + cc0 + t) * H + h) * DV + col)
+                               : 0.f;
+            }
+    };
+    PrepIn<Tin, TPL> pin;
+    float vin[4][4];
+    if (nchunks > 0) {
+        load_prep(pin, 0, min(64, len));
+        load_v(vin, 0, min(64, len));
+    }
+
     for (int j = 0; j < nchunks; ++j) {
         const int c0 = j * 64;
         const int L = min(64, len - c0);
+        const int Ln = min(64, len - c0 - 64);   // next chunk (<= 0: none)
         if (p.h_ckpt && has_col) {
             float* hc = p.h_ckpt + (static_cast<size_t>(sidx) * H + h) * static_cast<size_t>(nchunks) * DK * DV +
                         static_cast<size_t>(j) * DK * DV;
@@ -252,7 +315,6 @@ __global__ void __launch_bounds__(256, 1) ckda_fwd_kernel(FwdParams p)
         // lane: channels 8co..8co+7 of tokens 16w + tg*TPL + tt (tt < TPL)
         float bl[TPL][8];
         uint32_t negmask = 0;         // bit 8*tt+e: running sign product is -1
-        Raw8<Tin> qr[TPL], kr[TPL];
         float run[8];
         uint32_t par = 0;             // bit e: parity of negative signs so far
 #pragma unroll
@@ -260,28 +322,19 @@ __global__ void __launch_bounds__(256, 1) ckda_fwd_kernel(FwdParams p)
 #pragma unroll
         for (int tt = 0; tt < TPL; ++tt) {
             const int t = 16 * w + tg * TPL + tt;
-            if (t < L) {
-                const size_t base = (static_cast<size_t>(tok0 + c0 + t) * H + h) * DK + 8 * co;
-                const float4 g0 = reinterpret_cast<const float4*>(p.g + base)[0];
-                const float4 g1 = reinterpret_cast<const float4*>(p.g + base)[1];
-                const uint2 s8 = *reinterpret_cast<const uint2*>(p.s + base);
-                run[0] += g0.x; run[1] += g0.y; run[2] += g0.z; run[3] += g0.w;
-                run[4] += g1.x; run[5] += g1.y; run[6] += g1.z; run[7] += g1.w;
+            const float4 g0 = pin.g0[tt], g1 = pin.g1[tt];
+            const uint2 s8 = pin.s8[tt];
+            run[0] += g0.x; run[1] += g0.y; run[2] += g0.z; run[3] += g0.w;
+            run[4] += g1.x; run[5] += g1.y; run[6] += g1.z; run[7] += g1.w;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t byte = ((e < 4 ? s8.x : s8.y) >> (8 * (e & 3))) & 0xffu;
-                    par ^= (byte >> 7) << e;      // s = -1 has its sign bit set
-                }
-                qr[tt].load(q + base);
-                kr[tt].load(k + base);
-            } else {
-                qr[tt].zero();
-                kr[tt].zero();
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t byte = ((e < 4 ? s8.x : s8.y) >> (8 * (e & 3))) & 0xffu;
+                par ^= (byte >> 7) << e;      // s = -1 has its sign bit set
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) bl[tt][e] = run[e];
             negmask |= par << (8 * tt);
-            if (co == 0) beta_s[t] = (t < L) ? p.beta[static_cast<size_t>(tok0 + c0 + t) * H + h] : 0.f;
+            if (co == 0) beta_s[t] = pin.beta[tt];
         }
         // inclusive scan of the per-lane totals across the token groups of the wave
         float inc[8];
@@ -305,7 +358,7 @@ __global__ void __launch_bounds__(256, 1) ckda_fwd_kernel(FwdParams p)
                 wtot_p[w * DK + 8 * co + e] = ((pinc >> e) & 1u) ? -1.f : 1.f;
             }
         }
-        __syncthreads();
+        lds_sync();
         float m0[8], m1[8], mh[8], bpre[8];
         uint32_t ppre = pinc ^ par;   // parity of the tokens before this lane's, inside the wave
 #pragma unroll
@@ -344,9 +397,9 @@ __global__ void __launch_bounds__(256, 1) ckda_fwd_kernel(FwdParams p)
                 const float P = ((neg >> e) & 1u) ? -1.f : 1.f;
                 const float e1 = exp2_clamped((b - mh[e]) * kLog2e);
                 const float e2 = exp2_clamped((mh[e] - b) * kLog2e);
-                const float kf = P * kr[tt].get(e);
+                const float kf = P * pin.k[tt].get(e);
                 rk[e] = kf * e1;
-                rq[e] = (P * qr[tt].get(e)) * e1;
+                rq[e] = (P * pin.q[tt].get(e)) * e1;
                 ck[e] = kf * e2;
             }
             PR::store8(rowk, t, 8 * co, rk);
@@ -358,9 +411,9 @@ __global__ void __launch_bounds__(256, 1) ckda_fwd_kernel(FwdParams p)
                 for (int e = 0; e < 8; ++e) cf[e] = ck[e] * exp2_clamped((m1[e] - m0[e]) * kLog2e);
                 PR::store8(colkf, t, 8 * co, cf);
             }
-            CKDA_FENCE();
         }
-        __syncthreads();
+        if (Ln > 0) load_prep(pin, c0 + 64, Ln);
+        lds_sync();
 
         }
         // ================= P2: A / M tiles and the S products ===============
@@ -387,7 +440,6 @@ __global__ void __launch_bounds__(256, 1) ckda_fwd_kernel(FwdParams p)
                     acc = PR::mma8(PR::load8(cm, 16 * I + n, ko), PR::load8(rm, 16 * R + n, ko), acc);
                 }
                 tacc[x] = acc;
-                CKDA_FENCE();
             }
         }
         // S' = Diag(e^{m_h}) S as split B operands, then K^S and Q^S
@@ -417,17 +469,13 @@ __global__ void __launch_bounds__(256, 1) ckda_fwd_kernel(FwdParams p)
                         aq = PR::mma8(PR::load4x2(rowq, r, ka, kb), Bs[ks], aq);
                     }
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int t = 16 * R + 4 * gq + i;
-                        const float vv = (t < L) ? Elem<Tin>::load(v, (static_cast<size_t>(tok0 + c0 + t) * H + h) * DV + col) : 0.f;
-                        Rt[R][i] = vv - ak[i];
-                    }
+                    for (int i = 0; i < 4; ++i) Rt[R][i] = vin[R][i] - ak[i];
                     OQ[R] = aq;
-                    CKDA_FENCE();
                 }
             }
         }
-        __syncthreads();
+        if (Ln > 0) load_v(vin, c0 + 64, Ln);
+        lds_sync();
 
         }
         // ================= P2.5: publish -beta*A blocks, M, and kf^T ========
@@ -475,7 +523,7 @@ __global__ void __launch_bounds__(256, 1) ckda_fwd_kernel(FwdParams p)
 #pragma unroll
             for (int e = 0; e < 8; ++e) PR::copy1(ckt, 8 * co + e, t, colk, t, 8 * co + e);
         }
-        __syncthreads();
+        lds_sync();
 
         }
         // ================= P3: inverses of the 16x16 diagonal blocks ========
@@ -496,7 +544,7 @@ __global__ void __launch_bounds__(256, 1) ckda_fwd_kernel(FwdParams p)
 #pragma unroll
             for (int r = 0; r < 16; ++r) PR::store1(ymat, J * 16 + r, c, y[r]);
         }
-        __syncthreads();
+        lds_sync();
 
         }
         // ================= P4: U, O, state update ==========================
@@ -549,7 +597,7 @@ __global__ void __launch_bounds__(256, 1) ckda_fwd_kernel(FwdParams p)
                 CKDA_FENCE();
             }
         }
-        __syncthreads();
+        lds_sync();
         }
     }
 
