@@ -1,11 +1,540 @@
-// bwd.hip -- CKDA backward (placeholder until the kernels land).
+// bwd.hip -- CKDA backward: gradients of L = <do, o> + <dht, ht> through the
+// chunked forward.
+//
+// Chunk-level reverse mode of the WY/UT form (Complex KDA paper page,
+// section 2: WY-based chunk-wise implementations; the training backward
+// itself is specified in an appendix missing from the pages, so the gradient
+// here is the plain derivative of the forward: no gradient flows to the
+// sign s, and dg = alpha * dL/dalpha for g = log|alpha|).
+//
+// Per chunk (64 tokens, chunk-local sign fold, anchor m = b at token 31):
+//   K1 = kf e^{b-m}, K2 = kf e^{m-b}, Q1 = qf e^{b-m}, KB = kf e^{b_L-b}
+//   A = strict_lower(K1 K2^T), M = lower(Q1 K2^T), X = I + Diag(beta) A,
+//   Xi = X^{-1}, T = Xi Diag(beta), S' = Diag(e^m) S, U = T (V - K1 S')
+// Reverse recurrence over chunks (the only sequential part), G = dL/dS at the
+// chunk end in the true frame, dSt = Diag(P_L) G:
+//   dU = M^T dO + KB dSt,  Z = T^T dU,
+//   G_prev = Diag(e^m) (Q1^T dO - K1^T Z) + Diag(e^{b_L}) dSt
+// Chunk-parallel gradients:
+//   dM = lower(dO U^T), dKB = U dSt^T, dW' = -dU S'^T, dV = T^T dU,
+//   dT = dU V^T + dW' K1^T, dK1 = T^T dW', dbeta1_i = sum_r dT_ri Xi_ri,
+//   dX = -Xi^T (dT Diag(beta)) Xi^T, dXs = strict_lower(dX),
+//   dbeta2_r = sum_i dXs_ri A_ri, dA = Diag(beta) dXs,
+//   dK1 += dA K2, dK2 = dA^T K1 + dM^T Q1, dQ1 = dM K2 + dO S'^T,
+//   dq~ = dQ1 e^{b-m}, dk~ = dK1 e^{b-m} + dK2 e^{m-b} + dKB e^{b_L-b},
+//   db = Q1 dQ1 + K1 dK1 - K2 dK2 - KB dKB (+ sum(KB dKB) + e^{b_L} sum_v dSt S
+//   at the chunk's last token), dg = reverse cumulative sum of db,
+//   dq = P dq~, dk = P dk~.
+//
+// Implementation: every product is a batched fp32 matrix-core GEMM
+// (v_mfma_f32_16x16x4_f32) over all chunk-heads at once, with intermediates
+// in the caller's workspace; the reverse recurrence runs one workgroup per
+// (sequence, head, 32-column slice) over the chunks.
 #include "ckda_device.h"
 #include "ckda_launch.h"
+#include "ckda_mfma.h"
 
 namespace ckda {
 
-size_t bwd_workspace_bytes(int, int, int, int, int) { return 0; }
+namespace {
 
-hipError_t launch_bwd(const BwdArgs&, hipStream_t) { return hipErrorNotSupported; }
+constexpr int kBV = 32;   // value columns per reverse-pass workgroup
+
+// Workgroup (4 waves) matrix product on fp32 operands with arbitrary strides
+// (global or LDS): for each 16x16 output tile owned by this wave,
+//   acc(i, j) = sum_k A[i*ar + k*ac] * B[k*br + j*bc]
+// and epi(i, j, acc) is called for every element.  M, N multiples of 16,
+// K multiple of 16.
+template <typename Epi>
+__device__ __forceinline__ void wg_mm(int M, int N, int K, const float* A, int ar, int ac,
+                                      const float* B, int br, int bc, int tile0, int tstride,
+                                      Epi epi) {
+    const int l = threadIdx.x & 63;
+    const int n = l & 15, g = l >> 4;
+    const int tn = N / 16;
+    const int ntile = (M / 16) * tn;
+    for (int tile = tile0; tile < ntile; tile += tstride) {
+        const int ti = tile / tn, tj = tile % tn;
+        const float* a = A + (16 * ti + n) * ar + g * ac;
+        const float* b = B + g * br + (16 * tj + n) * bc;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < K; k0 += 16) {
+            float av[4], bv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                av[u] = a[(k0 + 4 * u) * ac];
+                bv[u] = b[(k0 + 4 * u) * br];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], bv[u], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) epi(16 * ti + 4 * g + i, 16 * tj + n, acc[i]);
+    }
+}
+
+// Workspace layout (floats), per chunk-head ch (NC = B*H*NT of them).
+struct BwdWs {
+    int NC, DK, DV;
+    float* base;
+    // [NC][64][DK]
+    float *K1, *K2, *Q1, *KB, *Bb, *Pp, *dKB, *dW, *dK1, *dK2, *dQ1;
+    // [NC][64][DV]
+    float *V, *dO, *R, *U, *dU, *dV;
+    // [NC][DK][DV]
+    float *Sp, *dSt;
+    // [NC][64][64]
+    float *A, *M, *Xi, *T, *dM, *dT, *Y1, *Tmp, *dX, *dA;
+    // [NC][DK]
+    float *em, *gC, *pC;
+    // [NC][64]
+    float *beta, *dbeta1, *dbeta2;
+
+    __host__ __device__ static size_t floats(size_t NC, int DK, int DV) {
+        return NC * (11ull * 64 * DK + 6ull * 64 * DV + 2ull * DK * DV + 10ull * 64 * 64 + 3ull * DK + 3ull * 64);
+    }
+    __host__ void carve(float* p, int nc, int dk, int dv) {
+        NC = nc; DK = dk; DV = dv; base = p;
+        const size_t n = nc;
+        auto take = [&](size_t cnt) { float* r = p; p += cnt; return r; };
+        K1 = take(n * 64 * dk); K2 = take(n * 64 * dk); Q1 = take(n * 64 * dk); KB = take(n * 64 * dk);
+        Bb = take(n * 64 * dk); Pp = take(n * 64 * dk); dKB = take(n * 64 * dk); dW = take(n * 64 * dk);
+        dK1 = take(n * 64 * dk); dK2 = take(n * 64 * dk); dQ1 = take(n * 64 * dk);
+        V = take(n * 64 * dv); dO = take(n * 64 * dv); R = take(n * 64 * dv); U = take(n * 64 * dv);
+        dU = take(n * 64 * dv); dV = take(n * 64 * dv);
+        Sp = take(n * dk * dv); dSt = take(n * dk * dv);
+        A = take(n * 4096); M = take(n * 4096); Xi = take(n * 4096); T = take(n * 4096); dM = take(n * 4096);
+        dT = take(n * 4096); Y1 = take(n * 4096); Tmp = take(n * 4096); dX = take(n * 4096); dA = take(n * 4096);
+        em = take(n * dk); gC = take(n * dk); pC = take(n * dk);
+        beta = take(n * 64); dbeta1 = take(n * 64); dbeta2 = take(n * 64);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// batched GEMM: for every batch element z (chunk-head),
+//   C_z(i,j) = alpha * sum_k A_z(i,k) B_z(k,j) + beta * D_z(i,j)   (then mask)
+// A_z(i,k) = A[z*sA + i*ar + k*ac], etc.; mask 1: keep j < i, 2: keep j <= i.
+// ---------------------------------------------------------------------------
+struct Gemm {
+    int M, N, K;
+    const float* A; long long sA; int ar, ac;
+    const float* B; long long sB; int br, bc;
+    float* C; long long sC; int cr;
+    const float* D; long long sD; int dr;
+    float alpha, beta;
+    int mask;
+};
+
+__global__ void __launch_bounds__(256) bgemm_kernel(Gemm p) {
+    const long long z = blockIdx.x;
+    const int w = threadIdx.x >> 6;
+    const float* A = p.A + z * p.sA;
+    const float* B = p.B + z * p.sB;
+    float* C = p.C + z * p.sC;
+    const float* D = p.D ? p.D + z * p.sD : nullptr;
+    const int tile0 = blockIdx.y * 4 + w;
+    wg_mm(p.M, p.N, p.K, A, p.ar, p.ac, B, p.br, p.bc, tile0, 4 * gridDim.y, [&](int i, int j, float acc) {
+        float val = p.alpha * acc;
+        if (D) val += p.beta * D[i * p.dr + j];
+        if (p.mask == 1 && j >= i) val = 0.f;
+        if (p.mask == 2 && j > i) val = 0.f;
+        C[i * p.cr + j] = val;
+    });
+}
+
+hipError_t gemm(const Gemm& g, int nbatch, hipStream_t st) {
+    const int ntile = (g.M / 16) * (g.N / 16);
+    const int gy = (ntile + 15) / 16;   // 4 tiles per block-step, each block loops
+    hipLaunchKernelGGL(bgemm_kernel, dim3(nbatch, gy), dim3(256), 0, st, g);
+    return hipGetLastError();
+}
+
+// C = alpha * op(A) op(B) (+ beta * D), all operands [NC][rows][cols] row-major.
+// tA/tB: use the transpose of the stored matrix.
+Gemm mk(int M, int N, int K, const float* A, int lda, long long sA, bool tA, const float* B, int ldb,
+        long long sB, bool tB, float* C, int ldc, long long sC, float alpha = 1.f, const float* D = nullptr,
+        float beta = 0.f, int mask = 0) {
+    Gemm g{};
+    g.M = M; g.N = N; g.K = K;
+    g.A = A; g.sA = sA; g.ar = tA ? 1 : lda; g.ac = tA ? lda : 1;
+    g.B = B; g.sB = sB; g.br = tB ? 1 : ldb; g.bc = tB ? ldb : 1;
+    g.C = C; g.sC = sC; g.cr = ldc;
+    g.D = D; g.sD = sC; g.dr = ldc;
+    g.alpha = alpha; g.beta = beta; g.mask = mask;
+    return g;
+}
+
+struct BwdParams {
+    const void *q, *k, *v, *dout;
+    const float *g, *beta;
+    const int8_t* s;
+    const float *h_ckpt, *dht, *h0;
+    float scale;
+    float *dq, *dk, *dv, *dg, *dbeta, *dh0;
+    int B, T, H, NT;
+};
+
+// chunk-head ch -> (b, h, chunk j, first token, valid tokens)
+struct ChunkIdx {
+    int b, h, j, t0, L;
+    __device__ ChunkIdx(int ch, int H, int NT, int T) {
+        j = ch % NT;
+        const int bh = ch / NT;
+        h = bh % H;
+        b = bh / H;
+        t0 = j * 64;
+        L = min(64, T - t0);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// prep: chunk-local cumulative gate, sign product and anchored operands
+// ---------------------------------------------------------------------------
+template <typename Tin>
+__global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p, BwdWs W) {
+    const int ch = blockIdx.x;
+    const int DK = W.DK, DV = W.DV;
+    const ChunkIdx ci(ch, p.H, p.NT, p.T);
+    const int c = threadIdx.x;
+    const size_t trow0 = static_cast<size_t>(ci.b) * p.T + ci.t0;   // token row of the chunk start
+    const size_t o64k = static_cast<size_t>(ch) * 64 * DK;
+    const size_t o64v = static_cast<size_t>(ch) * 64 * DV;
+    if (c < DK) {
+        float run = 0.f, par = 1.f;
+        for (int t = 0; t < 64; ++t) {
+            if (t < ci.L) {
+                const size_t e = ((trow0 + t) * p.H + ci.h) * DK + c;
+                run += p.g[e];
+                par *= static_cast<float>(p.s[e]);
+            }
+            W.Bb[o64k + t * DK + c] = run;
+            W.Pp[o64k + t * DK + c] = par;
+        }
+        const float m = W.Bb[o64k + min(31, ci.L - 1) * DK + c];
+        const float bL = run;
+        for (int t = 0; t < 64; ++t) {
+            float K1 = 0.f, K2 = 0.f, Q1 = 0.f, KB = 0.f;
+            if (t < ci.L) {
+                const size_t e = ((trow0 + t) * p.H + ci.h) * DK + c;
+                const float b = W.Bb[o64k + t * DK + c];
+                const float P = W.Pp[o64k + t * DK + c];
+                const float kf = P * Elem<Tin>::load(static_cast<const Tin*>(p.k), e);
+                const float qf = P * Elem<Tin>::load(static_cast<const Tin*>(p.q), e);
+                const float e1 = exp2_clamped((b - m) * kLog2e);
+                K1 = kf * e1;
+                K2 = kf * exp2_clamped((m - b) * kLog2e);
+                Q1 = qf * e1;
+                KB = kf * exp2_clamped((bL - b) * kLog2e);
+            }
+            W.K1[o64k + t * DK + c] = K1;
+            W.K2[o64k + t * DK + c] = K2;
+            W.Q1[o64k + t * DK + c] = Q1;
+            W.KB[o64k + t * DK + c] = KB;
+        }
+        W.em[static_cast<size_t>(ch) * DK + c] = exp2_clamped(m * kLog2e);
+        W.gC[static_cast<size_t>(ch) * DK + c] = exp2_clamped(bL * kLog2e);
+        W.pC[static_cast<size_t>(ch) * DK + c] = par;
+    }
+    if (c < DV) {
+        for (int t = 0; t < 64; ++t) {
+            float vv = 0.f, dd = 0.f;
+            if (t < ci.L) {
+                const size_t e = ((trow0 + t) * p.H + ci.h) * DV + c;
+                vv = Elem<Tin>::load(static_cast<const Tin*>(p.v), e);
+                dd = p.scale * Elem<Tin>::load(static_cast<const Tin*>(p.dout), e);
+            }
+            W.V[o64v + t * DV + c] = vv;
+            W.dO[o64v + t * DV + c] = dd;
+        }
+    }
+    if (c < 64) W.beta[static_cast<size_t>(ch) * 64 + c] = (c < ci.L) ? p.beta[(trow0 + c) * p.H + ci.h] : 0.f;
+    // S' = Diag(e^m) S for the chunk-start state (h_ckpt is [B,H,NT,DK,DV] = [NC][DK][DV])
+    __syncthreads();
+    const float* S = p.h_ckpt + static_cast<size_t>(ch) * DK * DV;
+    float* Sp = W.Sp + static_cast<size_t>(ch) * DK * DV;
+    const float* em = W.em + static_cast<size_t>(ch) * DK;
+    for (int e = threadIdx.x; e < DK * DV; e += blockDim.x) Sp[e] = em[e / DV] * S[e];
+}
+
+// ---------------------------------------------------------------------------
+// Xi = (I + Diag(beta) A)^{-1} (unit lower triangular) and T = Xi Diag(beta):
+// 16x16 diagonal blocks by forward substitution, off-diagonal blocks by
+// Xi_IJ = -Xi_II sum_{K=J}^{I-1} X_IK Xi_KJ.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) bwd_inverse_kernel(BwdWs W) {
+    __shared__ float X[64][65];
+    __shared__ float Y[64][65];
+    __shared__ float Tm[16][17];
+    const int ch = blockIdx.x;
+    const float* A = W.A + static_cast<size_t>(ch) * 4096;
+    const float* bt = W.beta + static_cast<size_t>(ch) * 64;
+    for (int e = threadIdx.x; e < 4096; e += 256) {
+        const int r = e / 64, i = e % 64;
+        X[r][i] = (i < r) ? bt[r] * A[e] : 0.f;
+        Y[r][i] = 0.f;
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const int J = threadIdx.x / 16, c = threadIdx.x % 16;
+        float y[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = (r == c) ? 1.f : 0.f;
+#pragma unroll
+            for (int i = 0; i < r; ++i) acc -= X[16 * J + r][16 * J + i] * y[i];
+            y[r] = acc;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Y[16 * J + r][16 * J + c] = y[r];
+    }
+    __syncthreads();
+    const int r = threadIdx.x / 16, c = threadIdx.x % 16;
+    for (int d = 1; d < 4; ++d) {
+        for (int J = 0; J + d < 4; ++J) {
+            const int I = J + d;
+            float acc = 0.f;
+            for (int K = J; K < I; ++K)
+                for (int k = 0; k < 16; ++k) acc += X[16 * I + r][16 * K + k] * Y[16 * K + k][16 * J + c];
+            Tm[r][c] = acc;
+            __syncthreads();
+            float o = 0.f;
+            for (int k = 0; k < 16; ++k) o -= Y[16 * I + r][16 * I + k] * Tm[k][c];
+            Y[16 * I + r][16 * J + c] = o;
+            __syncthreads();
+        }
+    }
+    float* Xi = W.Xi + static_cast<size_t>(ch) * 4096;
+    float* T = W.T + static_cast<size_t>(ch) * 4096;
+    for (int e = threadIdx.x; e < 4096; e += 256) {
+        const int rr = e / 64, i = e % 64;
+        Xi[e] = Y[rr][i];
+        T[e] = Y[rr][i] * bt[i];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Reverse recurrence over chunks, one workgroup per (b, h, 32-column slice).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) bwd_reverse_kernel(BwdParams p, BwdWs W) {
+    __shared__ float G[128 * kBV];     // [DK][kBV]
+    __shared__ float dSt[128 * kBV];
+    __shared__ float dU[64 * kBV];
+    __shared__ float Z[64 * kBV];
+    const int DK = W.DK, DV = W.DV;
+    const int nsl = DV / kBV;
+    const int bh = blockIdx.x / nsl;
+    const int v0 = (blockIdx.x % nsl) * kBV;
+    const int w = threadIdx.x >> 6;
+    // G = dht (or 0)
+    for (int e = threadIdx.x; e < DK * kBV; e += 256) {
+        const int c = e / kBV, v = e % kBV;
+        G[e] = p.dht ? p.dht[(static_cast<size_t>(bh) * DK + c) * DV + v0 + v] : 0.f;
+    }
+    __syncthreads();
+    for (int j = p.NT - 1; j >= 0; --j) {
+        const size_t ch = static_cast<size_t>(bh) * p.NT + j;
+        const float* pC = W.pC + ch * DK;
+        const float* em = W.em + ch * DK;
+        const float* gC = W.gC + ch * DK;
+        float* dSt_g = W.dSt + ch * DK * DV;
+        for (int e = threadIdx.x; e < DK * kBV; e += 256) {
+            const int c = e / kBV, v = e % kBV;
+            const float x = pC[c] * G[e];
+            dSt[e] = x;
+            dSt_g[c * DV + v0 + v] = x;
+        }
+        __syncthreads();
+        // dU = M^T dO + KB dSt     [64 x kBV]
+        const float* M = W.M + ch * 4096;
+        const float* dO = W.dO + ch * 64 * DV + v0;
+        const float* KB = W.KB + ch * 64 * DK;
+        wg_mm(64, kBV, 64, M, 1, 64, dO, DV, 1, w, 4, [&](int i, int jj, float acc) { dU[i * kBV + jj] = acc; });
+        wg_mm(64, kBV, DK, KB, DK, 1, dSt, kBV, 1, w, 4, [&](int i, int jj, float acc) { dU[i * kBV + jj] += acc; });
+        __syncthreads();
+        {
+            float* dU_g = W.dU + ch * 64 * DV + v0;
+            for (int e = threadIdx.x; e < 64 * kBV; e += 256) dU_g[(e / kBV) * DV + e % kBV] = dU[e];
+        }
+        // Z = T^T dU
+        const float* T = W.T + ch * 4096;
+        wg_mm(64, kBV, 64, T, 1, 64, dU, kBV, 1, w, 4, [&](int i, int jj, float acc) { Z[i * kBV + jj] = acc; });
+        __syncthreads();
+        // G = Diag(e^m) (Q1^T dO - K1^T Z) + Diag(e^{b_L}) dSt
+        const float* Q1 = W.Q1 + ch * 64 * DK;
+        const float* K1 = W.K1 + ch * 64 * DK;
+        wg_mm(DK, kBV, 64, Q1, 1, DK, dO, DV, 1, w, 4, [&](int i, int jj, float acc) { G[i * kBV + jj] = acc; });
+        wg_mm(DK, kBV, 64, K1, 1, DK, Z, kBV, 1, w, 4, [&](int i, int jj, float acc) {
+            G[i * kBV + jj] = em[i] * (G[i * kBV + jj] - acc) + gC[i] * dSt[i * kBV + jj];
+        });
+        __syncthreads();
+    }
+    if (p.dh0) {
+        for (int e = threadIdx.x; e < DK * kBV; e += 256) {
+            const int c = e / kBV, v = e % kBV;
+            p.dh0[(static_cast<size_t>(bh) * DK + c) * DV + v0 + v] = G[e];
+        }
+    }
+}
+
+// dbeta1_i = sum_r dT_ri Xi_ri ; Y1 = dT Diag(beta)
+__global__ void __launch_bounds__(256) bwd_dbeta1_kernel(BwdWs W) {
+    const size_t ch = blockIdx.x;
+    const float* dT = W.dT + ch * 4096;
+    const float* Xi = W.Xi + ch * 4096;
+    const float* bt = W.beta + ch * 64;
+    float* Y1 = W.Y1 + ch * 4096;
+    for (int e = threadIdx.x; e < 4096; e += 256) Y1[e] = dT[e] * bt[e % 64];
+    if (threadIdx.x < 64) {
+        const int i = threadIdx.x;
+        float acc = 0.f;
+        for (int r = 0; r < 64; ++r) acc += dT[r * 64 + i] * Xi[r * 64 + i];
+        W.dbeta1[ch * 64 + i] = acc;
+    }
+}
+
+// dXs = strict_lower(dX); dbeta2_r = sum_i dXs_ri A_ri; dA = Diag(beta) dXs
+__global__ void __launch_bounds__(256) bwd_dA_kernel(BwdWs W) {
+    const size_t ch = blockIdx.x;
+    const float* dX = W.dX + ch * 4096;
+    const float* A = W.A + ch * 4096;
+    const float* bt = W.beta + ch * 64;
+    float* dA = W.dA + ch * 4096;
+    for (int e = threadIdx.x; e < 4096; e += 256) {
+        const int r = e / 64, i = e % 64;
+        dA[e] = (i < r) ? bt[r] * dX[e] : 0.f;
+    }
+    if (threadIdx.x < 64) {
+        const int r = threadIdx.x;
+        float acc = 0.f;
+        for (int i = 0; i < r; ++i) acc += dX[r * 64 + i] * A[r * 64 + i];
+        W.dbeta2[ch * 64 + r] = acc;
+    }
+}
+
+// gate gradient, unfold of the sign product, scatter to [B,T,H,.]
+__global__ void __launch_bounds__(256) bwd_final_kernel(BwdParams p, BwdWs W) {
+    const int ch = blockIdx.x;
+    const int DK = W.DK, DV = W.DV;
+    const ChunkIdx ci(ch, p.H, p.NT, p.T);
+    const size_t trow0 = static_cast<size_t>(ci.b) * p.T + ci.t0;
+    const size_t o64k = static_cast<size_t>(ch) * 64 * DK;
+    const size_t o64v = static_cast<size_t>(ch) * 64 * DV;
+    const int c = threadIdx.x;
+    if (c < DK) {
+        const float* S = p.h_ckpt + static_cast<size_t>(ch) * DK * DV;
+        const float* dSt = W.dSt + static_cast<size_t>(ch) * DK * DV;
+        float dGL = 0.f;
+        for (int v = 0; v < DV; ++v) dGL += dSt[c * DV + v] * S[c * DV + v];
+        const float m = W.Bb[o64k + min(31, ci.L - 1) * DK + c];
+        const float bL = W.Bb[o64k + (ci.L - 1) * DK + c];
+        float kbsum = 0.f;
+        for (int t = 0; t < ci.L; ++t) kbsum += W.KB[o64k + t * DK + c] * W.dKB[o64k + t * DK + c];
+        float acc = 0.f;
+        for (int t = ci.L - 1; t >= 0; --t) {
+            const size_t o = o64k + t * DK + c;
+            const float b = W.Bb[o], P = W.Pp[o];
+            const float e1 = exp2_clamped((b - m) * kLog2e);
+            const float e2 = exp2_clamped((m - b) * kLog2e);
+            const float e3 = exp2_clamped((bL - b) * kLog2e);
+            const float dq = W.dQ1[o] * e1;
+            const float dk = W.dK1[o] * e1 + W.dK2[o] * e2 + W.dKB[o] * e3;
+            float db = W.Q1[o] * W.dQ1[o] + W.K1[o] * W.dK1[o] - W.K2[o] * W.dK2[o] - W.KB[o] * W.dKB[o];
+            if (t == ci.L - 1) db += kbsum + exp2_clamped(bL * kLog2e) * dGL;
+            acc += db;
+            const size_t e = ((trow0 + t) * p.H + ci.h) * DK + c;
+            p.dq[e] = P * dq;
+            p.dk[e] = P * dk;
+            p.dg[e] = acc;
+        }
+    }
+    if (c < DV) {
+        for (int t = 0; t < ci.L; ++t) p.dv[((trow0 + t) * p.H + ci.h) * DV + c] = W.dV[o64v + t * DV + c];
+    }
+    if (c < ci.L) {
+        const size_t o = static_cast<size_t>(ch) * 64 + c;
+        p.dbeta[(trow0 + c) * p.H + ci.h] = W.dbeta1[o] + W.dbeta2[o];
+    }
+}
+
+// dst = src (or 0 when src is null), n floats
+__global__ void fill_copy_kernel(float* dst, const float* src, size_t n) {
+    for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+         i += static_cast<size_t>(gridDim.x) * blockDim.x)
+        dst[i] = src ? src[i] : 0.f;
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int B, int T, int H, int DK, int DV) {
+    const size_t NC = static_cast<size_t>(B) * H * ((T + 63) / 64);
+    return BwdWs::floats(NC, DK, DV) * sizeof(float);
+}
+
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
+    const int NT = (a.T + 63) / 64;
+    const int NC = a.B * a.H * NT;
+    const int DK = a.DK, DV = a.DV;
+    BwdParams p{};
+    p.q = a.q; p.k = a.k; p.v = a.v; p.dout = a.dout; p.g = a.g; p.beta = a.beta; p.s = a.s;
+    p.h_ckpt = a.h_ckpt; p.dht = a.dht; p.h0 = a.h0; p.scale = a.scale;
+    p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dg = a.dg; p.dbeta = a.dbeta; p.dh0 = a.dh0;
+    p.B = a.B; p.T = a.T; p.H = a.H; p.NT = NT;
+    if (NC == 0) {
+        // no tokens: dh0 = dht (or 0)
+        const size_t n = static_cast<size_t>(a.B) * a.H * DK * DV;
+        if (a.dh0 && n > 0) {
+            hipLaunchKernelGGL(fill_copy_kernel, dim3(static_cast<unsigned>((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096)),
+                               dim3(256), 0, st, a.dh0, a.dht, n);
+            return hipGetLastError();
+        }
+        return hipSuccess;
+    }
+    BwdWs W;
+    W.carve(static_cast<float*>(a.ws), NC, DK, DV);
+    hipError_t e;
+#define CKDA_CHECK(x) do { e = (x); if (e != hipSuccess) return e; } while (0)
+    if (a.bf16)
+        hipLaunchKernelGGL(bwd_prep_kernel<bf16_t>, dim3(NC), dim3(256), 0, st, p, W);
+    else
+        hipLaunchKernelGGL(bwd_prep_kernel<float>, dim3(NC), dim3(256), 0, st, p, W);
+    CKDA_CHECK(hipGetLastError());
+    const long long s64k = 64LL * DK, s64v = 64LL * DV, skv = 1LL * DK * DV, s44 = 4096;
+    // A = strict_lower(K1 K2^T), M = lower(Q1 K2^T)
+    CKDA_CHECK(gemm(mk(64, 64, DK, W.K1, DK, s64k, false, W.K2, DK, s64k, true, W.A, 64, s44, 1.f, nullptr, 0.f, 1), NC, st));
+    CKDA_CHECK(gemm(mk(64, 64, DK, W.Q1, DK, s64k, false, W.K2, DK, s64k, true, W.M, 64, s44, 1.f, nullptr, 0.f, 2), NC, st));
+    hipLaunchKernelGGL(bwd_inverse_kernel, dim3(NC), dim3(256), 0, st, W);
+    CKDA_CHECK(hipGetLastError());
+    // U = T (V - K1 S')
+    CKDA_CHECK(gemm(mk(64, DV, DK, W.K1, DK, s64k, false, W.Sp, DV, skv, false, W.R, DV, s64v, -1.f, W.V, 1.f), NC, st));
+    CKDA_CHECK(gemm(mk(64, DV, 64, W.T, 64, s44, false, W.R, DV, s64v, false, W.U, DV, s64v), NC, st));
+    // reverse recurrence: dSt, dU per chunk, dh0
+    hipLaunchKernelGGL(bwd_reverse_kernel, dim3(a.B * a.H * (DV / kBV)), dim3(256), 0, st, p, W);
+    CKDA_CHECK(hipGetLastError());
+    // chunk-parallel gradients
+    CKDA_CHECK(gemm(mk(64, 64, DV, W.dO, DV, s64v, false, W.U, DV, s64v, true, W.dM, 64, s44, 1.f, nullptr, 0.f, 2), NC, st));
+    CKDA_CHECK(gemm(mk(64, DK, DV, W.U, DV, s64v, false, W.dSt, DV, skv, true, W.dKB, DK, s64k), NC, st));
+    CKDA_CHECK(gemm(mk(64, DK, DV, W.dU, DV, s64v, false, W.Sp, DV, skv, true, W.dW, DK, s64k, -1.f), NC, st));
+    CKDA_CHECK(gemm(mk(64, DV, 64, W.T, 64, s44, true, W.dU, DV, s64v, false, W.dV, DV, s64v), NC, st));
+    CKDA_CHECK(gemm(mk(64, 64, DV, W.dU, DV, s64v, false, W.V, DV, s64v, true, W.dT, 64, s44), NC, st));
+    CKDA_CHECK(gemm(mk(64, 64, DK, W.dW, DK, s64k, false, W.K1, DK, s64k, true, W.dT, 64, s44, 1.f, W.dT, 1.f), NC, st));
+    CKDA_CHECK(gemm(mk(64, DK, 64, W.T, 64, s44, true, W.dW, DK, s64k, false, W.dK1, DK, s64k), NC, st));
+    hipLaunchKernelGGL(bwd_dbeta1_kernel, dim3(NC), dim3(256), 0, st, W);
+    CKDA_CHECK(hipGetLastError());
+    // dX = -Xi^T (Y1 Xi^T)
+    CKDA_CHECK(gemm(mk(64, 64, 64, W.Y1, 64, s44, false, W.Xi, 64, s44, true, W.Tmp, 64, s44), NC, st));
+    CKDA_CHECK(gemm(mk(64, 64, 64, W.Xi, 64, s44, true, W.Tmp, 64, s44, false, W.dX, 64, s44, -1.f), NC, st));
+    hipLaunchKernelGGL(bwd_dA_kernel, dim3(NC), dim3(256), 0, st, W);
+    CKDA_CHECK(hipGetLastError());
+    // dK1 += dA K2 ; dK2 = dA^T K1 + dM^T Q1 ; dQ1 = dM K2 + dO S'^T
+    CKDA_CHECK(gemm(mk(64, DK, 64, W.dA, 64, s44, false, W.K2, DK, s64k, false, W.dK1, DK, s64k, 1.f, W.dK1, 1.f), NC, st));
+    CKDA_CHECK(gemm(mk(64, DK, 64, W.dA, 64, s44, true, W.K1, DK, s64k, false, W.dK2, DK, s64k), NC, st));
+    CKDA_CHECK(gemm(mk(64, DK, 64, W.dM, 64, s44, true, W.Q1, DK, s64k, false, W.dK2, DK, s64k, 1.f, W.dK2, 1.f), NC, st));
+    CKDA_CHECK(gemm(mk(64, DK, 64, W.dM, 64, s44, false, W.K2, DK, s64k, false, W.dQ1, DK, s64k), NC, st));
+    CKDA_CHECK(gemm(mk(64, DK, DV, W.dO, DV, s64v, false, W.Sp, DV, skv, true, W.dQ1, DK, s64k, 1.f, W.dQ1, 1.f), NC, st));
+    hipLaunchKernelGGL(bwd_final_kernel, dim3(NC), dim3(256), 0, st, p, W);
+    CKDA_CHECK(hipGetLastError());
+#undef CKDA_CHECK
+    return hipSuccess;
+}
 
 }  // namespace ckda

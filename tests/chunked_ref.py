@@ -147,3 +147,77 @@ def bwd_chain(q, k, v, g, s, beta, do, scale=1.0, S0=None, dST=None, C=64):
         dS = dS_prev
     out["dS0"] = dS
     return out
+
+
+def bwd_chain_anchored(q, k, v, g, s, beta, do, scale=1.0, S0=None, dST=None, C=64):
+    """The same reverse mode written in the anchored variables the GPU
+    backward uses: with m = b at the chunk's token 31,
+        K1 = kf e^{b-m},  K2 = kf e^{m-b},  Q1 = qf e^{b-m},  KB = kf e^{b_L-b},
+        S' = Diag(e^m) S.
+    e^{b_r - b_i} = (K1 K2^T)_ri / (kf kf) etc.; every factor stays within the
+    span of half a chunk, and the gate gradient db keeps its form because
+    the anchors cancel."""
+    T, DK = q.shape
+    DV = v.shape[1]
+    S = np.zeros((DK, DV)) if S0 is None else np.array(S0, dtype=np.float64)
+    starts = list(range(0, T, C))
+    hs = []
+    for c0 in starts:
+        hs.append(S.copy())
+        c1 = min(T, c0 + C)
+        _, S = fwd_chain(q[c0:c1], k[c0:c1], v[c0:c1], g[c0:c1], s[c0:c1], beta[c0:c1],
+                         scale, S, C=C, anchored=False)
+    out = dict(dq=np.zeros_like(q), dk=np.zeros_like(k), dv=np.zeros_like(v),
+               dg=np.zeros_like(g), dbeta=np.zeros_like(beta))
+    G = np.zeros((DK, DV)) if dST is None else np.array(dST, dtype=np.float64)
+    for ci in range(len(starts) - 1, -1, -1):
+        c0 = starts[ci]
+        c1 = min(T, c0 + C)
+        L = c1 - c0
+        S = hs[ci]
+        b = np.cumsum(g[c0:c1], axis=0)
+        P = np.cumprod(s[c0:c1], axis=0)
+        qt, kt = P * q[c0:c1], P * k[c0:c1]
+        m = b[min(31, L - 1)]
+        bL, PL = b[-1], P[-1]
+        K1, K2, Q1 = kt * np.exp(b - m), kt * np.exp(m - b), qt * np.exp(b - m)
+        KB = kt * np.exp(bL - b)
+        Sp = np.exp(m)[:, None] * S
+        A = np.tril(K1 @ K2.T, -1)
+        M = np.tril(Q1 @ K2.T, 0)
+        bt = beta[c0:c1]
+        V = v[c0:c1]
+        Xi = np.linalg.inv(np.eye(L) + bt[:, None] * A)
+        Tm = Xi * bt[None, :]
+        U = Tm @ (V - K1 @ Sp)
+        dO = scale * do[c0:c1]
+        dSt = PL[:, None] * G
+        dU = M.T @ dO + KB @ dSt
+        Z = Tm.T @ dU
+        G = np.exp(m)[:, None] * (Q1.T @ dO - K1.T @ Z) + np.exp(bL)[:, None] * dSt
+        dM = np.tril(dO @ U.T, 0)
+        dKB = U @ dSt.T
+        dGL = np.sum(dSt * S, axis=1)
+        dWp = -dU @ Sp.T
+        dV = Tm.T @ dU
+        dT = dU @ V.T + dWp @ K1.T
+        dK1 = Tm.T @ dWp
+        dbeta = np.sum(dT * Xi, axis=0)
+        dX = -Xi.T @ (dT * bt[None, :]) @ Xi.T
+        dXs = np.tril(dX, -1)
+        dbeta += np.sum(dXs * A, axis=1)
+        dA = bt[:, None] * dXs
+        dK1 += dA @ K2
+        dK2 = dA.T @ K1 + dM.T @ Q1
+        dQ1 = dM @ K2 + dO @ Sp.T
+        dqt = dQ1 * np.exp(b - m)
+        dkt = dK1 * np.exp(b - m) + dK2 * np.exp(m - b) + dKB * np.exp(bL - b)
+        db = Q1 * dQ1 + K1 * dK1 - K2 * dK2 - KB * dKB
+        db[-1] += np.sum(KB * dKB, axis=0) + np.exp(bL) * dGL
+        out["dq"][c0:c1] = P * dqt
+        out["dk"][c0:c1] = P * dkt
+        out["dv"][c0:c1] = dV
+        out["dg"][c0:c1] = np.cumsum(db[::-1], axis=0)[::-1]
+        out["dbeta"][c0:c1] = dbeta
+    out["dS0"] = G
+    return out

@@ -31,3 +31,17 @@ def test_chunked_backward_equals_token_oracle():
         ref = r[name][0]
         np.testing.assert_allclose(rc[name], ref, rtol=0, atol=1e-11 * (1 + np.abs(ref).max()),
                                    err_msg=name)
+
+
+def test_anchored_chunked_backward_equals_token_oracle():
+    rng = np.random.default_rng(23)
+    q, k, v, g, s, beta = rand_inputs(rng, 1, 150, 8, 6, p_neg=0.3)
+    S0 = rng.standard_normal((1, 8, 6))
+    do = rng.standard_normal((1, 150, 6))
+    dST = rng.standard_normal((1, 8, 6))
+    r = oracle.bwd_chain_arrays(q, k, v, g, s, beta, do, 0.9, S0, dST)
+    rc = CR.bwd_chain_anchored(q[0], k[0], v[0], g[0], s[0], beta[0], do[0], 0.9, S0[0], dST[0])
+    for name in ("dq", "dk", "dv", "dg", "dbeta", "dS0"):
+        ref = r[name][0]
+        np.testing.assert_allclose(rc[name], ref, rtol=0, atol=1e-11 * (1 + np.abs(ref).max()),
+                                   err_msg=name)
