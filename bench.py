@@ -77,7 +77,9 @@ def bench_fwd(torch, steps, warmup):
     B, T, H, DK = tok.q.shape
     o = torch.empty((B, T, H, 128), dtype=torch.float32, device="cuda:0")
     ht = torch.empty((B, H, 128, 128), dtype=torch.float32, device="cuda:0")
-    fn = lambda: ckda.fwd(**d, o=o, ht=ht)
+    ws = torch.empty(ckda.fwd_workspace_bytes(B, T, H, DK, 128, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda:0")
+    fn = lambda: ckda.fwd(**d, o=o, ht=ht, workspace=ws)
     log("timing forward")
     wall, per = time_kernel_launches(torch, fn, steps, warmup)
     tokens = B * T

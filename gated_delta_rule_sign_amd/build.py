@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libckda.so")
-SOURCES = ["api.cpp", "decode.hip", "fwd.hip", "bwd.hip"]
+SOURCES = ["api.cpp", "decode.hip", "chunk.hip", "state.hip", "bwd.hip"]
 ARCH = os.environ.get("CKDA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -48,11 +48,13 @@ def lib() -> ctypes.CDLL:
     L.ckda_last_error.restype = ctypes.c_char_p
     L.ckda_chunk_prep.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P]
     L.ckda_chunk_prep.restype = I
-    L.ckda_fwd_workspace_bytes.argtypes = [I, I, I, I, I]
+    L.ckda_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
     L.ckda_fwd_workspace_bytes.restype = S
-    L.ckda_fwd_chunked.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P, P]
+    L.ckda_fwd_varlen_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    L.ckda_fwd_varlen_workspace_bytes.restype = S
+    L.ckda_fwd_chunked.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P, P, S, P]
     L.ckda_fwd_chunked.restype = I
-    L.ckda_fwd_varlen.argtypes = [I, I, P, P, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P]
+    L.ckda_fwd_varlen.argtypes = [I, I, P, P, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P, S, P]
     L.ckda_fwd_varlen.restype = I
     L.ckda_decode_step.argtypes = [I, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P]
     L.ckda_decode_step.restype = I
@@ -79,12 +81,14 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _dtype_code(t: torch.Tensor) -> int:
-    if t.dtype == torch.bfloat16:
+def _dtype_code(t) -> int:
+    """Code of a tensor's dtype (or of a torch.dtype)."""
+    dt = t if isinstance(t, torch.dtype) else t.dtype
+    if dt == torch.bfloat16:
         return CKDA_BF16
-    if t.dtype == torch.float32:
+    if dt == torch.float32:
         return CKDA_F32
-    raise CkdaError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+    raise CkdaError(f"q/k/v must be bfloat16 or float32, got {dt}")
 
 
 def _need(t: Optional[torch.Tensor], name: str, dtype=None, shape=None, device=None):
@@ -134,10 +138,29 @@ def chunk_prep(q, k, g, s):
     return b, p, qf, kf
 
 
+def fwd_workspace_bytes(B, T, H, DK, DV, dtype) -> int:
+    return int(lib().ckda_fwd_workspace_bytes(B, T, H, DK, DV, _dtype_code(dtype)))
+
+
+def fwd_varlen_workspace_bytes(N, T_total, H, DK, DV, dtype) -> int:
+    return int(lib().ckda_fwd_varlen_workspace_bytes(N, T_total, H, DK, DV, _dtype_code(dtype)))
+
+
+def _workspace(workspace, need, dev):
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _need(workspace, "workspace", device=dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return workspace, wsb
+
+
 def fwd(q, k, v, g, s, beta, scale: float = 1.0, h0=None, want_ht: bool = True,
-        want_ckpt: bool = False, o=None, ht=None, h_ckpt=None):
+        want_ckpt: bool = False, o=None, ht=None, h_ckpt=None, workspace=None):
     """Chunked forward (ckda_fwd_chunked).  Inputs [B,T,H,D]; returns
-    (o [B,T,H,DV] f32, ht [B,H,DK,DV] f32 or None, h_ckpt or None)."""
+    (o [B,T,H,DV] f32, ht [B,H,DK,DV] f32 or None, h_ckpt or None).
+    ``workspace`` (uint8 GPU tensor of fwd_workspace_bytes) is allocated per
+    call if not given."""
     B, T = q.shape[0], q.shape[1]
     dt, H, DK, DV, dev = _token_inputs(q, k, v, g, s, beta, (B, T))
     _need(h0, "h0", torch.float32, (B, H, DK, DV), dev)
@@ -151,14 +174,15 @@ def fwd(q, k, v, g, s, beta, scale: float = 1.0, h0=None, want_ht: bool = True,
     if want_ckpt and h_ckpt is None:
         h_ckpt = torch.empty((B, H, NT, DK, DV), dtype=torch.float32, device=dev)
     _need(h_ckpt, "h_ckpt", torch.float32, (B, H, NT, DK, DV), dev)
+    workspace, wsb = _workspace(workspace, fwd_workspace_bytes(B, T, H, DK, DV, q.dtype), dev)
     _check(lib().ckda_fwd_chunked(B, T, H, DK, DV, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
                                   _ptr(beta), float(scale), _ptr(h0), _ptr(o), _ptr(ht),
-                                  _ptr(h_ckpt), _stream()))
+                                  _ptr(h_ckpt), _ptr(workspace), wsb, _stream()))
     return o, ht, h_ckpt
 
 
 def fwd_varlen(q, k, v, g, s, beta, cu_seqlens, scale: float = 1.0, h0=None,
-               want_ht: bool = True, cu_seqlens_dev=None, o=None, ht=None):
+               want_ht: bool = True, cu_seqlens_dev=None, o=None, ht=None, workspace=None):
     """Packed-document forward (ckda_fwd_varlen).  q etc. are [T_total,H,D]
     (a leading 1 is accepted); cu_seqlens is an int32 CPU tensor [N+1]."""
     if q.dim() == 4:
@@ -179,9 +203,10 @@ def fwd_varlen(q, k, v, g, s, beta, cu_seqlens, scale: float = 1.0, h0=None,
     if want_ht and ht is None:
         ht = torch.empty((N, H, DK, DV), dtype=torch.float32, device=dev)
     _need(ht, "ht", torch.float32, (N, H, DK, DV), dev)
+    workspace, wsb = _workspace(workspace, fwd_varlen_workspace_bytes(N, Tt, H, DK, DV, q.dtype), dev)
     _check(lib().ckda_fwd_varlen(N, Tt, _ptr(cu), _ptr(cu_seqlens_dev), H, DK, DV, dt, _ptr(q),
                                  _ptr(k), _ptr(v), _ptr(g), _ptr(s), _ptr(beta), float(scale),
-                                 _ptr(h0), _ptr(o), _ptr(ht), _stream()))
+                                 _ptr(h0), _ptr(o), _ptr(ht), _ptr(workspace), wsb, _stream()))
     return o, ht
 
 

@@ -72,6 +72,10 @@ ckda_status_t check_heads(int DK, int DV) {
 // token-tensor element counts must fit the kernels' 32-bit chain/token indices
 bool too_big(long long tokens, int H) { return tokens * static_cast<long long>(H) >= (1LL << 31); }
 
+// chunk slots of the forward workspace (one record per slot and head)
+int fwd_slots(int B, int T) { return B * ((T + 63) / 64); }
+int varlen_slots(int N, int T_total) { return (T_total + 63) / 64 + N; }
+
 }  // namespace
 
 extern "C" {
@@ -110,35 +114,57 @@ ckda_status_t ckda_chunk_prep(int B, int T, int H, int DK, ckda_dtype_t in_dtype
     return hip_status(ckda::launch_prep(a, static_cast<hipStream_t>(stream)), "ckda_chunk_prep launch");
 }
 
-size_t ckda_fwd_workspace_bytes(int, int, int, int, int) { return 0; }
+size_t ckda_fwd_workspace_bytes(int B, int T, int H, int DK, int DV, ckda_dtype_t dt) {
+    if (B < 0 || T < 0 || H < 0 || !head_ok(DK) || !head_ok(DV) || (dt != CKDA_F32 && dt != CKDA_BF16)) return 0;
+    return ckda::fwd_workspace_bytes(fwd_slots(B, T), H, DK, DV, dt == CKDA_BF16);
+}
+
+size_t ckda_fwd_varlen_workspace_bytes(int N, int T_total, int H, int DK, int DV, ckda_dtype_t dt) {
+    if (N < 0 || T_total < 0 || H < 0 || !head_ok(DK) || !head_ok(DV) || (dt != CKDA_F32 && dt != CKDA_BF16))
+        return 0;
+    return ckda::fwd_workspace_bytes(varlen_slots(N, T_total), H, DK, DV, dt == CKDA_BF16);
+}
 
 ckda_status_t ckda_fwd_chunked(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype,
                                const void* q, const void* k, const void* v, const float* g,
                                const int8_t* s, const float* beta, float scale, const float* h0,
-                               float* o, float* ht, float* h_ckpt, ckda_stream_t stream) {
+                               float* o, float* ht, float* h_ckpt, void* workspace,
+                               size_t workspace_bytes, ckda_stream_t stream) {
     CKDA_TRY(check_dtype(in_dtype));
     if (B < 0 || T < 0 || H < 0) return fail(CKDA_ERR_SHAPE, "negative size (B=%d, T=%d, H=%d)", B, T, H);
     CKDA_TRY(check_heads(DK, DV));
     if (too_big(static_cast<long long>(B) * T, H)) return fail(CKDA_ERR_UNSUPPORTED, "tensor too large");
+    if (static_cast<long long>(B) * ((T + 63) / 64) * H >= (1LL << 31))
+        return fail(CKDA_ERR_UNSUPPORTED, "too many chunks");
     if (B * H == 0) return ok();
     if (T > 0) { CKDA_REQUIRE(q); CKDA_REQUIRE(k); CKDA_REQUIRE(v); CKDA_REQUIRE(g); CKDA_REQUIRE(s); CKDA_REQUIRE(beta); CKDA_REQUIRE(o); }
-    CKDA_ALIGNED(q); CKDA_ALIGNED(k); CKDA_ALIGNED(g); CKDA_ALIGNED(s);
+    CKDA_ALIGNED(q); CKDA_ALIGNED(k); CKDA_ALIGNED(g); CKDA_ALIGNED(s); CKDA_ALIGNED(workspace);
+    const int nslots = fwd_slots(B, T);
+    const size_t need = ckda::fwd_workspace_bytes(nslots, H, DK, DV, in_dtype == CKDA_BF16);
+    if (need > 0) {
+        CKDA_REQUIRE(workspace);
+        if (workspace_bytes < need)
+            return fail(CKDA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+    }
     ckda::FwdArgs a{};
     a.B = B; a.T = T; a.H = H; a.DK = DK; a.DV = DV; a.bf16 = in_dtype == CKDA_BF16;
     a.q = q; a.k = k; a.v = v; a.g = g; a.s = s; a.beta = beta; a.scale = scale;
-    a.h0 = h0; a.o = o; a.ht = ht; a.h_ckpt = h_ckpt; a.cu = nullptr; a.ndocs = 0;
-    return hip_status(ckda::launch_fwd(a, static_cast<hipStream_t>(stream)), "ckda_fwd_chunked launch");
+    a.h0 = h0; a.o = o; a.ht = ht; a.h_ckpt = h_ckpt; a.cu = nullptr; a.ndocs = 0; a.ws = workspace;
+    return hip_status(ckda::launch_fwd(a, nslots, static_cast<hipStream_t>(stream)), "ckda_fwd_chunked launch");
 }
 
 ckda_status_t ckda_fwd_varlen(int N, int T_total, const int32_t* cu, const int32_t* cu_dev, int H,
                               int DK, int DV, ckda_dtype_t in_dtype, const void* q, const void* k,
                               const void* v, const float* g, const int8_t* s, const float* beta,
-                              float scale, const float* h0, float* o, float* ht, ckda_stream_t stream) {
+                              float scale, const float* h0, float* o, float* ht, void* workspace,
+                              size_t workspace_bytes, ckda_stream_t stream) {
     CKDA_TRY(check_dtype(in_dtype));
     if (N < 0 || T_total < 0 || H < 0) return fail(CKDA_ERR_SHAPE, "negative size (N=%d, T=%d, H=%d)", N, T_total, H);
     CKDA_TRY(check_heads(DK, DV));
     if (too_big(T_total, H)) return fail(CKDA_ERR_UNSUPPORTED, "tensor too large");
     if (static_cast<long long>(N) * H >= (1LL << 31) / 2) return fail(CKDA_ERR_UNSUPPORTED, "too many documents");
+    if (static_cast<long long>(varlen_slots(N, T_total)) * H >= (1LL << 31))
+        return fail(CKDA_ERR_UNSUPPORTED, "too many chunks");
     CKDA_REQUIRE(cu);
     if (cu[0] != 0) return fail(CKDA_ERR_SEQLENS, "cu_seqlens[0] = %d, expected 0", cu[0]);
     for (int i = 0; i < N; ++i)
@@ -147,13 +173,20 @@ ckda_status_t ckda_fwd_varlen(int N, int T_total, const int32_t* cu, const int32
     if (N * H == 0) return ok();
     CKDA_REQUIRE(cu_dev);
     if (T_total > 0) { CKDA_REQUIRE(q); CKDA_REQUIRE(k); CKDA_REQUIRE(v); CKDA_REQUIRE(g); CKDA_REQUIRE(s); CKDA_REQUIRE(beta); CKDA_REQUIRE(o); }
-    CKDA_ALIGNED(q); CKDA_ALIGNED(k); CKDA_ALIGNED(g); CKDA_ALIGNED(s);
+    CKDA_ALIGNED(q); CKDA_ALIGNED(k); CKDA_ALIGNED(g); CKDA_ALIGNED(s); CKDA_ALIGNED(workspace);
+    const int nslots = varlen_slots(N, T_total);
+    const size_t need = ckda::fwd_workspace_bytes(nslots, H, DK, DV, in_dtype == CKDA_BF16);
+    if (need > 0) {
+        CKDA_REQUIRE(workspace);
+        if (workspace_bytes < need)
+            return fail(CKDA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+    }
     ckda::FwdArgs a{};
     a.B = 1; a.T = T_total; a.H = H; a.DK = DK; a.DV = DV; a.bf16 = in_dtype == CKDA_BF16;
     a.q = q; a.k = k; a.v = v; a.g = g; a.s = s; a.beta = beta; a.scale = scale;
     a.h0 = h0; a.o = o; a.ht = ht; a.h_ckpt = nullptr;
-    a.cu = cu_dev; a.ndocs = N;
-    return hip_status(ckda::launch_fwd(a, static_cast<hipStream_t>(stream)), "ckda_fwd_varlen launch");
+    a.cu = cu_dev; a.ndocs = N; a.ws = workspace;
+    return hip_status(ckda::launch_fwd(a, nslots, static_cast<hipStream_t>(stream)), "ckda_fwd_varlen launch");
 }
 
 ckda_status_t ckda_decode_step(int N, int H, int DK, int DV, ckda_dtype_t in_dtype, const void* q,

@@ -8,6 +8,7 @@ namespace ckda {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kChunk = 64;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -38,6 +39,35 @@ template <> struct Elem<float> {
 template <> struct Elem<bf16_t> {
     static __device__ __forceinline__ float load(const bf16_t* p, size_t i) { return bf16_to_f32(p[i].bits); }
     static __device__ __forceinline__ void store(bf16_t* p, size_t i, float x) { p[i].bits = f32_to_bf16(x); }
+};
+
+// 8 consecutive elements of a token row, kept in their storage form until use
+template <typename Tin>
+struct Raw8;
+template <>
+struct Raw8<bf16_t> {
+    uint4 u;
+    __device__ __forceinline__ void load(const bf16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
+    __device__ __forceinline__ void zero() { u = make_uint4(0u, 0u, 0u, 0u); }
+    __device__ __forceinline__ float get(int e) const {
+        const uint32_t w = (e < 2) ? u.x : (e < 4) ? u.y : (e < 6) ? u.z : u.w;
+        return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+    }
+};
+template <>
+struct Raw8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = reinterpret_cast<const float4*>(p)[0];
+        b = reinterpret_cast<const float4*>(p)[1];
+    }
+    __device__ __forceinline__ void zero() { a = make_float4(0.f, 0.f, 0.f, 0.f); b = a; }
+    __device__ __forceinline__ float get(int e) const {
+        switch (e) {
+            case 0: return a.x; case 1: return a.y; case 2: return a.z; case 3: return a.w;
+            case 4: return b.x; case 5: return b.y; case 6: return b.z; default: return b.w;
+        }
+    }
 };
 
 // exp(x) through the hardware base-2 exponential; the argument is clamped so

@@ -50,8 +50,13 @@ struct FwdArgs {
     // nullptr selects the equal-length mode
     const int32_t* cu;
     int ndocs;
+    void* ws;   // fwd_workspace_bytes(nslots, ...) bytes
 };
-hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+// nslots: chunk slots (equal-length: B * ceil(T/64); varlen: ceil(T/64) + N)
+size_t fwd_workspace_bytes(int nslots, int H, int DK, int DV, bool bf16);
+hipError_t launch_chunk(const FwdArgs& a, int nslots, hipStream_t stream);
+hipError_t launch_state(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd(const FwdArgs& a, int nslots, hipStream_t stream);
 
 struct BwdArgs {
     int B, T, H, DK, DV;

@@ -78,6 +78,10 @@ struct Prec<false> {
         *hp(d, dr, dc) = *hp(s, sr, sc);
         *lp(d, dr, dc) = *lp(s, sr, sc);
     }
+    // one element back as hi + lo
+    static __device__ __forceinline__ float get1(const LdsMat& m, int r, int c) {
+        return bf16_to_f32(*hp(m, r, c)) + bf16_to_f32(*lp(m, r, c));
+    }
     static __device__ __forceinline__ F8 load8(const LdsMat& m, int r, int c) {
         return F8{lds8(hp(m, r, c)), lds8(lp(m, r, c))};
     }
@@ -100,6 +104,44 @@ struct Prec<false> {
     }
     static __device__ __forceinline__ f32x4 mma4(const F4& a, const F4& b, f32x4 acc) {
         return mfma16x3(a.hi, a.lo, b.hi, b.lo, acc);
+    }
+
+    // single-plane A operand (a value stored once, already rounded to bf16)
+    typedef s16x4 A4s;
+    static __device__ __forceinline__ A4s load4s(const LdsMat& m, int r, int c) { return lds4s(hp(m, r, c)); }
+    static __device__ __forceinline__ f32x4 mma4s(const A4s& a, const F4& b, f32x4 acc) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b.lo, acc, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b.hi, acc, 0, 0, 0);
+    }
+
+    // global (workspace) stores: row-major planes of `row` bytes per row,
+    // lo plane `plane` bytes after the hi plane
+    static __device__ __forceinline__ void gstore8(unsigned char* base, size_t plane, int row, int r, int c,
+                                                   const float (&x)[8]) {
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint16_t h0, l0, h1, l1;
+            split1(x[2 * i], h0, l0);
+            split1(x[2 * i + 1], h1, l1);
+            h[i] = h0 | (static_cast<uint32_t>(h1) << 16);
+            l[i] = l0 | (static_cast<uint32_t>(l1) << 16);
+        }
+        unsigned char* p = base + static_cast<size_t>(r) * row + 2 * c;
+        *reinterpret_cast<uint4*>(p) = make_uint4(h[0], h[1], h[2], h[3]);
+        *reinterpret_cast<uint4*>(p + plane) = make_uint4(l[0], l[1], l[2], l[3]);
+    }
+    static __device__ __forceinline__ void gstore4(unsigned char* base, size_t plane, int row, int r, int c, f32x4 x) {
+        uint16_t h[4], l[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) split1(x[i], h[i], l[i]);
+        unsigned char* p = base + static_cast<size_t>(r) * row + 2 * c;
+        *reinterpret_cast<uint2*>(p) = make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
+        *reinterpret_cast<uint2*>(p + plane) = make_uint2(l[0] | (uint32_t(l[1]) << 16), l[2] | (uint32_t(l[3]) << 16));
+    }
+    // one element of a single-plane matrix, rounded to bf16
+    static __device__ __forceinline__ void gstore1s(unsigned char* base, int row, int r, int c, float x) {
+        *reinterpret_cast<uint16_t*>(base + static_cast<size_t>(r) * row + 2 * c) = f32_to_bf16(x);
     }
 };
 
@@ -124,6 +166,7 @@ struct Prec<true> {
     static __device__ __forceinline__ void copy1(const LdsMat& d, int dr, int dc, const LdsMat& s, int sr, int sc) {
         *fp(d, dr, dc) = *fp(s, sr, sc);
     }
+    static __device__ __forceinline__ float get1(const LdsMat& m, int r, int c) { return *fp(m, r, c); }
     static __device__ __forceinline__ f32x4 ld4(const float* p) {
         const float4 v = *reinterpret_cast<const float4*>(p);
         f32x4 r = {v.x, v.y, v.z, v.w};
@@ -149,6 +192,27 @@ struct Prec<true> {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.a[j], y.a[j], acc, 0, 0, 0);
         return acc;
+    }
+
+    typedef f32x4 A4s;
+    static __device__ __forceinline__ A4s load4s(const LdsMat& m, int r, int c) { return ld4(fp(m, r, c)); }
+    static __device__ __forceinline__ f32x4 mma4s(const A4s& x, const F4& y, f32x4 acc) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[j], y.a[j], acc, 0, 0, 0);
+        return acc;
+    }
+
+    static __device__ __forceinline__ void gstore8(unsigned char* base, size_t, int row, int r, int c,
+                                                   const float (&x)[8]) {
+        float4* p = reinterpret_cast<float4*>(base + static_cast<size_t>(r) * row + 4 * c);
+        p[0] = make_float4(x[0], x[1], x[2], x[3]);
+        p[1] = make_float4(x[4], x[5], x[6], x[7]);
+    }
+    static __device__ __forceinline__ void gstore4(unsigned char* base, size_t, int row, int r, int c, f32x4 x) {
+        *reinterpret_cast<float4*>(base + static_cast<size_t>(r) * row + 4 * c) = make_float4(x[0], x[1], x[2], x[3]);
+    }
+    static __device__ __forceinline__ void gstore1s(unsigned char* base, int row, int r, int c, float x) {
+        *reinterpret_cast<float*>(base + static_cast<size_t>(r) * row + 4 * c) = x;
     }
 };
 

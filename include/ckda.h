@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define CKDA_ABI_VERSION 1
+#define CKDA_ABI_VERSION 2
 
 typedef enum {
     CKDA_OK = 0,
@@ -97,14 +97,20 @@ ckda_status_t ckda_chunk_prep(int B, int T, int H, int DK, ckda_dtype_t in_dtype
  *   o: [B,T,H,DV] f32 (written)   ht: [B,H,DK,DV] f32 or NULL (final state)
  *   h_ckpt: [B,H,NT,DK,DV] f32 or NULL, NT = ceil(T/64): the state at the
  *           start of every chunk (checkpoints for ckda_bwd)
- * No workspace is needed (ckda_fwd_workspace_bytes returns 0 for it).
+ *   workspace: at least ckda_fwd_workspace_bytes(B, T, H, DK, DV, in_dtype)
+ *           bytes of device memory, 16-byte aligned, owned by the caller;
+ *           the call overwrites it (it carries one record per (chunk, head)
+ *           from the chunk-local pass to the state pass).  Calls that share
+ *           a workspace must be ordered on one stream.
+ * Two kernels are enqueued: the chunk-local pass over every (chunk, head)
+ * at once, then the state pass that walks the chunks of each sequence.
  * ---------------------------------------------------------------------- */
-size_t ckda_fwd_workspace_bytes(int B, int T, int H, int DK, int DV);
+size_t ckda_fwd_workspace_bytes(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype);
 ckda_status_t ckda_fwd_chunked(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype,
                                const void* q, const void* k, const void* v,
                                const float* g, const int8_t* s, const float* beta, float scale,
                                const float* h0, float* o, float* ht, float* h_ckpt,
-                               ckda_stream_t stream);
+                               void* workspace, size_t workspace_bytes, ckda_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Varlen forward over N packed documents (training packs documents back to
@@ -117,13 +123,17 @@ ckda_status_t ckda_fwd_chunked(int B, int T, int H, int DK, int DV, ckda_dtype_t
  *   cu_seqlens_dev:  the same N+1 values in device memory, read by the kernel
  *   q, k, g, s: [T_total,H,DK]; v, o: [T_total,H,DV]; beta: [T_total,H]
  *   h0, ht: [N,H,DK,DV] f32, each nullable.  Documents may be empty (their
- *   ht is their h0, or zero).  No workspace is needed.
+ *   ht is their h0, or zero).
+ *   workspace: at least ckda_fwd_varlen_workspace_bytes(N, T_total, H, DK,
+ *   DV, in_dtype) bytes, as for ckda_fwd_chunked.
  * ---------------------------------------------------------------------- */
+size_t ckda_fwd_varlen_workspace_bytes(int N, int T_total, int H, int DK, int DV, ckda_dtype_t in_dtype);
 ckda_status_t ckda_fwd_varlen(int N, int T_total, const int32_t* cu_seqlens_host,
                               const int32_t* cu_seqlens_dev, int H, int DK, int DV,
                               ckda_dtype_t in_dtype, const void* q, const void* k, const void* v,
                               const float* g, const int8_t* s, const float* beta, float scale,
-                              const float* h0, float* o, float* ht, ckda_stream_t stream);
+                              const float* h0, float* o, float* ht, void* workspace,
+                              size_t workspace_bytes, ckda_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * One recurrent (decode) step for N independent sequences.  The state is

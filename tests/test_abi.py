@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.ckda_abi_version() == 1
+    assert L.ckda_abi_version() == 2
     assert L.ckda_status_string(0) == b"ok"
     for st in range(1, 8):
         assert L.ckda_status_string(st) not in (b"ok", b"unknown status")
@@ -41,9 +41,13 @@ P = ctypes.c_void_p
 FAKE = P(0x1000)          # never dereferenced: every call below fails validation first
 
 
-def fwd(L, B=1, T=8, H=1, DK=32, DV=32, dt=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE, s=FAKE, beta=FAKE, o=FAKE):
+BIG = 1 << 40
+
+
+def fwd(L, B=1, T=8, H=1, DK=32, DV=32, dt=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE, s=FAKE, beta=FAKE, o=FAKE,
+        ws=FAKE, wsb=BIG):
     return L.ckda_fwd_chunked(B, T, H, DK, DV, dt, q, k, v, g, s, beta, ctypes.c_float(1.0),
-                              None, o, None, None, None)
+                              None, o, None, None, ws, ctypes.c_size_t(wsb), None)
 
 
 def test_fwd_rejects_bad_arguments(L):
@@ -61,16 +65,31 @@ def test_fwd_rejects_bad_arguments(L):
     assert L.ckda_last_error() == b""
 
 
+def test_fwd_workspace(L):
+    need = L.ckda_fwd_workspace_bytes(2, 100, 3, 64, 32, 1)
+    # one record per (chunk, head): bf16 keeps W in one plane, Qh/KbT/M in two
+    rec = 64 * 64 * 2 + 2 * (64 * 64 * 2) * 3 + 64 * 4 + 64 * 32 * 4
+    assert need == 2 * 2 * 3 * rec
+    assert L.ckda_fwd_workspace_bytes(2, 100, 3, 64, 32, 0) > need      # fp32 records are larger
+    assert L.ckda_fwd_workspace_bytes(2, 100, 3, 48, 32, 1) == 0       # unsupported head size
+    assert L.ckda_fwd_workspace_bytes(2, 0, 3, 64, 32, 1) == 0         # no chunks
+    assert L.ckda_fwd_varlen_workspace_bytes(3, 100, 3, 64, 32, 1) == (2 + 3) * 3 * rec
+    assert fwd(L, ws=None) == 1
+    assert b"workspace" in L.ckda_last_error()
+    assert fwd(L, wsb=L.ckda_fwd_workspace_bytes(1, 8, 1, 32, 32, 0) - 16) == 6
+    assert fwd(L, ws=P(0x1008)) == 4             # misaligned workspace
+
+
 def test_varlen_rejects_bad_cu_seqlens(L):
     def call(cu, N, Tt):
         arr = (ctypes.c_int32 * len(cu))(*cu)
         return L.ckda_fwd_varlen(N, Tt, arr, FAKE, 1, 32, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                 ctypes.c_float(1.0), None, FAKE, None, None)
+                                 ctypes.c_float(1.0), None, FAKE, None, FAKE, ctypes.c_size_t(BIG), None)
     assert call([1, 5], 1, 5) == 5              # does not start at 0
     assert call([0, 5, 3], 2, 3) == 5           # decreasing
     assert call([0, 5, 9], 2, 10) == 5          # does not end at T_total
     assert L.ckda_fwd_varlen(2, 4, None, FAKE, 1, 32, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                             ctypes.c_float(1.0), None, FAKE, None, None) == 1
+                             ctypes.c_float(1.0), None, FAKE, None, FAKE, ctypes.c_size_t(BIG), None) == 1
 
 
 def test_decode_and_bwd_reject_bad_arguments(L):

@@ -10,9 +10,10 @@ from tests.gpu_utils import banner, dev_tensor, host, rel_max, require_gpu, tok_
 pytestmark = pytest.mark.gpu
 
 # contract tolerances (max|diff| / RMS of the oracle): fp32 inputs 1e-4,
-# bf16 inputs 1e-2.  The hi/lo split products keep bf16-input runs near 1e-4
-# (float64 rounding model of the chunked algorithm), so small cases are also
-# held to a tighter design bound to catch regressions early.
+# bf16 inputs 1e-2.  For bf16 inputs the chunk records keep Qh, KbT and M as
+# hi/lo bf16 pairs and W as one bf16 rounding; a float64 rounding model of
+# that arithmetic stays near 1.3e-3 at T = 4096, so small cases are also held
+# to a tighter design bound to catch regressions early.
 TOL = {"f32": 1e-4, "bf16": 1e-2}
 DESIGN = {"f32": 1e-4, "bf16": 2e-3}
 
@@ -155,8 +156,10 @@ def test_split_call_composition():
         oc = torch.cat([oa, ob], dim=1)
         if exact:   # chunk-aligned cut: identical chunking, identical arithmetic
             assert torch.equal(oc, o) and torch.equal(htb, ht)
-        else:
-            assert rel_max(host(oc), host(o)) < 1e-3 and rel_max(host(htb), host(ht)) < 1e-3
+        else:       # other chunk boundaries: both runs within the design bound of the oracle
+            o_ref, ht_ref = oracle.fwd(**w.tok.f64(), h0=w.h0.astype(np.float64))
+            assert rel_max(host(oc), o_ref) < DESIGN["bf16"] and rel_max(host(htb), ht_ref) < DESIGN["bf16"]
+            assert rel_max(host(o), o_ref) < DESIGN["bf16"] and rel_max(host(ht), ht_ref) < DESIGN["bf16"]
 
 
 def test_layer_workload_sampled():
