@@ -53,10 +53,11 @@ struct ChunkShape {
     static constexpr int NE = 8 * KSW;             // elements per lane
     static_assert(NCG <= 2, "at most two channel groups");
     static constexpr int PC = DK + 8;              // column-operand pitch (elements)
-    static constexpr int PKH = DK + 4;             // K-hat pitch (floats)
     static constexpr int PY = 16 + 4;              // diagonal-inverse pitch
     // LDS (bytes).  Phase A: totals, beta, column operands, partial tiles;
-    // phase B (after the A/M tiles) reuses the column-operand space.
+    // phase B (after the A/M tiles) reuses the column-operand space: the row
+    // operand kf e^{b - m} over colk, the diagonal blocks, off-diagonal blocks
+    // and diagonal inverses over colkf.
     static constexpr int L_TOTB = 0;                          // float [4][DK]
     static constexpr int L_TOTP = L_TOTB + 4 * DK * 4;        // uint32 [4][DK/4]
     static constexpr int L_BETA = L_TOTP + 4 * (DK / 4) * 4;  // float [64]
@@ -64,8 +65,8 @@ struct ChunkShape {
     static constexpr int L_COLKF = L_COLK + 64 * PC * 4;      // operand [32][PC]
     static constexpr int L_PART = L_COLKF + 32 * PC * 4;      // f32x4 [20][64]
     static constexpr int SZ_PART = NCG > 1 ? 20 * 64 * 16 : 0;
-    static constexpr int L_KH = L_COLK;                       // float [64][PKH]
-    static constexpr int L_LDIAG = L_KH + 64 * PKH * 4;       // float [4][16][17]
+    static constexpr int L_RK = L_COLK;                       // operand [64][PC]: kf e^{b - m}
+    static constexpr int L_LDIAG = L_COLKF;                   // float [4][16][17]
     static constexpr int L_LOFF = L_LDIAG + 4 * 16 * 17 * 4;  // operand [6*64][4]
     static constexpr int L_Y = L_LOFF + 6 * 64 * 4 * 4;       // operand [64][PY]
     static constexpr int L_BEND = L_Y + 64 * PY * 4;
@@ -148,22 +149,23 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
     float bs[NE];
     uint32_t par[2 * KSW];   // sign bytes; bit 7 of byte e set <=> s = -1
     {
-        const size_t trow = static_cast<size_t>(tok0 + t) * H + h;
+        // padding tokens (t >= L) read the chunk's last token and are then
+        // replaced by g = 0, s = +1, q = k = 0, beta = 0 (unconditional loads)
+        const size_t trow = static_cast<size_t>(tok0 + min(t, L - 1)) * H + h;
 #pragma unroll
         for (int ks = 0; ks < KSW; ++ks) {
             const int c0 = CG * cgi + 32 * ks + 8 * gq;
-            if (valid) {
-                const size_t base = trow * DK + c0;
-                q8[ks].load(q + base);
-                k8[ks].load(k + base);
-                const float4 a = reinterpret_cast<const float4*>(p.g + base)[0];
-                const float4 b = reinterpret_cast<const float4*>(p.g + base)[1];
-                bs[8 * ks + 0] = a.x; bs[8 * ks + 1] = a.y; bs[8 * ks + 2] = a.z; bs[8 * ks + 3] = a.w;
-                bs[8 * ks + 4] = b.x; bs[8 * ks + 5] = b.y; bs[8 * ks + 6] = b.z; bs[8 * ks + 7] = b.w;
-                const uint2 sv = *reinterpret_cast<const uint2*>(p.s + base);
-                par[2 * ks] = sv.x;
-                par[2 * ks + 1] = sv.y;
-            } else {   // padding token: g = 0, s = +1, q = k = 0, beta = 0
+            const size_t base = trow * DK + c0;
+            q8[ks].load(q + base);
+            k8[ks].load(k + base);
+            const float4 a = reinterpret_cast<const float4*>(p.g + base)[0];
+            const float4 b = reinterpret_cast<const float4*>(p.g + base)[1];
+            const uint2 sv = *reinterpret_cast<const uint2*>(p.s + base);
+            bs[8 * ks + 0] = a.x; bs[8 * ks + 1] = a.y; bs[8 * ks + 2] = a.z; bs[8 * ks + 3] = a.w;
+            bs[8 * ks + 4] = b.x; bs[8 * ks + 5] = b.y; bs[8 * ks + 6] = b.z; bs[8 * ks + 7] = b.w;
+            par[2 * ks] = sv.x;
+            par[2 * ks + 1] = sv.y;
+            if (!valid) {
                 q8[ks].zero();
                 k8[ks].zero();
 #pragma unroll
@@ -172,10 +174,9 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
                 par[2 * ks + 1] = 0x01010101u;
             }
         }
-        const float bt = valid ? p.beta[trow] : 0.f;
-        if (cgi == 0 && gq == 0) beta_s[t] = bt;
+        const float bt = p.beta[trow];
+        if (cgi == 0 && gq == 0) beta_s[t] = valid ? bt : 0.f;
     }
-
     // ---- 1. in-tile scans (log2 units), tile totals to LDS -----------------
 #pragma unroll
     for (int i = 0; i < NE; ++i) bs[i] = row_scan_add(bs[i] * kLog2e);
@@ -195,65 +196,118 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
 
     // ---- 2. exponentials and operands -------------------------------------
     typename PR::F8 rkB[KSW], rqB[KSW];   // row operands (B side of the A/M tiles)
-    float kh[NE];                         // kf e^b, kept for the substitution
 #pragma unroll
     for (int ks = 0; ks < KSW; ++ks) {
         const int c0 = CG * cgi + 32 * ks + 8 * gq;
-        float4 Bt[4][2];
+        // anchors per channel (log2 units): b at token 15 (m0) and 47 (m1),
+        // and the sum over the earlier tiles of this wave's token tile
+        float b[8], mh[8], m1[8];
+        {
+            float4 Tt[3][2];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            Bt[x][0] = reinterpret_cast<const float4*>(totb + x * DK + c0)[0];
-            Bt[x][1] = reinterpret_cast<const float4*>(totb + x * DK + c0)[1];
-        }
-        uint32_t pw0 = 0, pw1 = 0;   // parity of the earlier tiles
+            for (int x = 0; x < 3; ++x) {
+                Tt[x][0] = reinterpret_cast<const float4*>(totb + x * DK + c0)[0];
+                Tt[x][1] = reinterpret_cast<const float4*>(totb + x * DK + c0)[1];
+            }
 #pragma unroll
-        for (int x = 0; x < 3; ++x) {
-            if (x < R) {
-                const uint2 pv = *reinterpret_cast<const uint2*>(totp + x * (DK / 4) + c0 / 4);
-                pw0 ^= pv.x;
-                pw1 ^= pv.y;
+            for (int e = 0; e < 8; ++e) {
+                auto pick = [&](const float4 (&v2)[2]) {
+                    const float4 vv = v2[e >> 2];
+                    return (e & 3) == 0 ? vv.x : (e & 3) == 1 ? vv.y : (e & 3) == 2 ? vv.z : vv.w;
+                };
+                const float t0 = pick(Tt[0]), t1 = pick(Tt[1]), t2 = pick(Tt[2]);
+                b[e] = bs[8 * ks + e] + ((R > 0 ? t0 : 0.f) + (R > 1 ? t1 : 0.f) + (R > 2 ? t2 : 0.f));
+                m1[e] = t0 + t1 + t2;
+                mh[e] = R < 2 ? t0 : m1[e];
             }
         }
-        float rk[8], rq[8], ck[8], ckf[8], qh[8], dd[8];
+        // sign-folded q and k (running product over the earlier tiles and this one)
+        float kf[8], qf[8];
+        {
+            uint32_t pw0 = par[2 * ks], pw1 = par[2 * ks + 1];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            auto pick = [&](const float4 (&v2)[2]) {
-                const float4 vv = v2[e >> 2];
-                return (e & 3) == 0 ? vv.x : (e & 3) == 1 ? vv.y : (e & 3) == 2 ? vv.z : vv.w;
-            };
-            const float t0 = pick(Bt[0]), t1 = pick(Bt[1]), t2 = pick(Bt[2]);
-            const float pre = (R > 0 ? t0 : 0.f) + (R > 1 ? t1 : 0.f) + (R > 2 ? t2 : 0.f);
-            const float b = bs[8 * ks + e] + pre;     // b_t * log2(e)
-            const float m1 = t0 + t1 + t2;            // b at token 47
-            const float mh = R < 2 ? t0 : m1;         // anchor of this half
-            const uint32_t word = par[2 * ks + (e >> 2)] ^ ((e >> 2) ? pw1 : pw0);
-            const uint32_t sgn = (word << (24 - 8 * (e & 3))) & 0x80000000u;
-            const float kf = __uint_as_float(__float_as_uint(k8[ks].get(e)) ^ sgn);
-            const float qf = __uint_as_float(__float_as_uint(q8[ks].get(e)) ^ sgn);
-            const float x = fminf(fmaxf(b - mh, -126.f), 126.f);
-            const float e1 = __builtin_amdgcn_exp2f(x);
-            const float e2 = __builtin_amdgcn_exp2f(-x);
-            const float e0 = __builtin_amdgcn_exp2f(fminf(b, 126.f));
-            rk[e] = kf * e1;
-            rq[e] = qf * e1;
-            ck[e] = kf * e2;
-            kh[8 * ks + e] = kf * e0;
-            qh[e] = qf * e0;
-            ckf[e] = (R < 2) ? kf * __builtin_amdgcn_exp2f(fminf(m1 - b, 126.f)) : 0.f;
-            dd[e] = __uint_as_float(__float_as_uint(e0) ^ sgn);   // P_L e^{b_L} at token 63
+            for (int x = 0; x < 3; ++x) {
+                if (x < R) {
+                    const uint2 pv = *reinterpret_cast<const uint2*>(totp + x * (DK / 4) + c0 / 4);
+                    pw0 ^= pv.x;
+                    pw1 ^= pv.y;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t sgn = (((e >> 2) ? pw1 : pw0) << (24 - 8 * (e & 3))) & 0x80000000u;
+                kf[e] = __uint_as_float(__float_as_uint(k8[ks].get(e)) ^ sgn);
+                qf[e] = __uint_as_float(__float_as_uint(q8[ks].get(e)) ^ sgn);
+            }
         }
-        rkB[ks] = PR::regs8(f32x4{rk[0], rk[1], rk[2], rk[3]}, f32x4{rk[4], rk[5], rk[6], rk[7]});
-        rqB[ks] = PR::regs8(f32x4{rq[0], rq[1], rq[2], rq[3]}, f32x4{rq[4], rq[5], rq[6], rq[7]});
-        PR::store8(colk, t, c0, ck);
-        if (R < 2) PR::store8(colkf, t, c0, ckf);
-        PR::gstore8(rec + RC::OFF_Q, RC::Q_PLANE, RC::Q_ROW, t, c0, qh);
-        if (t == 63) {
-            float4* dp = reinterpret_cast<float4*>(rec + RC::OFF_D + 4 * c0);
-            dp[0] = make_float4(dd[0], dd[1], dd[2], dd[3]);
-            dp[1] = make_float4(dd[4], dd[5], dd[6], dd[7]);
+        CKDA_FENCE();
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = fminf(fmaxf(b[e] - mh[e], -126.f), 126.f);
+        {   // column operand kf e^{m - b}
+            float ck[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ck[e] = kf[e] * __builtin_amdgcn_exp2f(-x[e]);
+            PR::store8(colk, t, c0, ck);
+        }
+        if (R < 2) {   // its cross-half version kf e^{m1 - b} for the half-1 rows
+            float ckf[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ckf[e] = kf[e] * __builtin_amdgcn_exp2f(fminf(m1[e] - b[e], 126.f));
+            PR::store8(colkf, t, c0, ckf);
+        }
+        CKDA_FENCE();
+        {   // Qh = qf e^b to the record; d = P_L e^{b_L} from token 63
+            float qh[8], e0[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                e0[e] = __builtin_amdgcn_exp2f(fminf(b[e], 126.f));
+                qh[e] = qf[e] * e0[e];
+            }
+            PR::gstore8(rec + RC::OFF_Q, RC::Q_PLANE, RC::Q_ROW, t, c0, qh);
+            if (t == 63) {   // the sign of P_L: kf and k differ exactly in it (also for k = +-0)
+                float dd[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t sg = (__float_as_uint(kf[e]) ^ __float_as_uint(k8[ks].get(e))) & 0x80000000u;
+                    dd[e] = __uint_as_float(__float_as_uint(e0[e]) ^ sg);
+                }
+                float4* dp = reinterpret_cast<float4*>(rec + RC::OFF_D + 4 * c0);
+                dp[0] = make_float4(dd[0], dd[1], dd[2], dd[3]);
+                dp[1] = make_float4(dd[4], dd[5], dd[6], dd[7]);
+            }
+        }
+        CKDA_FENCE();
+        {   // row operands kf e^{b - m}, qf e^{b - m} (registers)
+            float rk[8], rq[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float e1 = __builtin_amdgcn_exp2f(x[e]);
+                rk[e] = kf[e] * e1;
+                rq[e] = qf[e] * e1;
+            }
+            rkB[ks] = PR::regs8(f32x4{rk[0], rk[1], rk[2], rk[3]}, f32x4{rk[4], rk[5], rk[6], rk[7]});
+            rqB[ks] = PR::regs8(f32x4{rq[0], rq[1], rq[2], rq[3]}, f32x4{rq[4], rq[5], rq[6], rq[7]});
         }
     }
     lds_sync();
+
+    // ---- KbT = (P_L kf e^{b_L - b})^T from the column operand --------------
+    // task = (channel c, 8-token group tg); the column operand of a half is
+    // kf e^{m - b}, so KbT = that times P_L e^{b_L - m}
+    for (int task = tid; task < DK * 8; task += NW * 64) {
+        const int c = task % DK, tg = task / DK;
+        const float B0 = totb[c], B1 = totb[DK + c], B2 = totb[2 * DK + c], B3 = totb[3 * DK + c];
+        const float m = (tg >= 4) ? (B0 + B1 + B2) : B0;
+        const uint32_t pw = totp[c / 4] ^ totp[DK / 4 + c / 4] ^ totp[DK / 2 + c / 4] ^ totp[3 * (DK / 4) + c / 4];
+        const uint32_t sgn = (pw << (24 - 8 * (c & 3))) & 0x80000000u;
+        const float f = __uint_as_float(
+            __float_as_uint(__builtin_amdgcn_exp2f(fminf(B0 + B1 + B2 + B3 - m, 126.f))) ^ sgn);
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = f * PR::get1(colk, 8 * tg + j, c);
+        PR::gstore8(rec + RC::OFF_K, RC::K_PLANE, RC::K_ROW, c, 8 * tg, x);
+    }
 
     // ---- 3. A^T / M^T tiles (I, R), I <= R, over this wave's channels -------
     // lane (n, g) ends with row 16R + n, columns 16I + 4g .. +3 of A and M
@@ -276,23 +330,6 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
             }
         }
     }
-
-    // ---- KbT = (P_L kf e^{b_L - b})^T from the column operand --------------
-    // task = (channel c, 8-token group tg); the column operand of a half is
-    // kf e^{m - b}, so KbT = that times P_L e^{b_L - m}
-    for (int task = tid; task < DK * 8; task += NW * 64) {
-        const int c = task % DK, tg = task / DK;
-        const float B0 = totb[c], B1 = totb[DK + c], B2 = totb[2 * DK + c], B3 = totb[3 * DK + c];
-        const float m = (tg >= 4) ? (B0 + B1 + B2) : B0;
-        const uint32_t pw = totp[c / 4] ^ totp[DK / 4 + c / 4] ^ totp[DK / 2 + c / 4] ^ totp[3 * (DK / 4) + c / 4];
-        const uint32_t sgn = (pw << (24 - 8 * (c & 3))) & 0x80000000u;
-        const float f = __uint_as_float(
-            __float_as_uint(__builtin_amdgcn_exp2f(fminf(B0 + B1 + B2 + B3 - m, 126.f))) ^ sgn);
-        float x[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = f * PR::get1(colk, 8 * tg + j, c);
-        PR::gstore8(rec + RC::OFF_K, RC::K_PLANE, RC::K_ROW, c, 8 * tg, x);
-    }
     f32x4* const part = reinterpret_cast<f32x4*>(smem + SH::L_PART);
     if (SH::NCG > 1 && cgi == 1) {
 #pragma unroll
@@ -305,14 +342,44 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
     }
     lds_sync();
 
-    // ---- 4. publish M (record), -beta A blocks and diagonals (LDS) ---------
+    // V for this wave's value tiles of the substitution.  Vector memory
+    // loads and stores retire in order, so these loads go out before the M
+    // stores below (and long after the Qh / KbT stores), and their latency
+    // hides behind the diagonal inverses; each value keeps its own register
+    // until use (combining two loads would wait for both here).  Lane (n, g)
+    // holds rows 16J + 4g + i of column 16vt + n (the C/D layout).
+    constexpr int VPW = (DV / 16 + NW - 1) / NW;   // value tiles per wave
+    uint32_t vpre[VPW][4][4];
+    // (addresses are clamped into the chunk so every load is unconditional:
+    // a guarded load becomes a branch that waits for its result in place)
+#pragma unroll
+    for (int vi = 0; vi < VPW; ++vi) {
+        const int vtc = min(w + NW * vi, DV / 16 - 1);
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tt = 16 * J + 4 * gq + i;
+                const size_t idx = (static_cast<size_t>(tok0 + min(tt, L - 1)) * H + h) * DV + 16 * vtc + n;
+                vpre[vi][J][i] = F32 ? __float_as_uint(reinterpret_cast<const float*>(v)[idx])
+                                     : static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(v)[idx]);
+            }
+    }
+    // ---- 4. row operand kf e^{b - m} to LDS (over colk) for the right-hand
+    // sides; M to the record; -beta A blocks and diagonals to LDS (over colkf)
+    const LdsMat rkm{smem + SH::L_RK, PC, 64 * PC};
     const LdsMat loffm{smem + SH::L_LOFF, 4, 6 * 64 * 4};
     const LdsMat ym{smem + SH::L_Y, SH::PY, 64 * SH::PY};
     float* const ldiag = reinterpret_cast<float*>(smem + SH::L_LDIAG);
-    float* const khs = reinterpret_cast<float*>(smem + SH::L_KH);
+#pragma unroll
+    for (int ks = 0; ks < KSW; ++ks) PR::store8f(rkm, t, CG * cgi + 32 * ks + 8 * gq, rkB[ks]);
     if (cgi == 0) {
         const int r = 16 * R + n;
         const float br = beta_s[r];
+        if ((R & 1) == 0) {   // blocks (0,1), (2,3): read by the 32-token steps of the state pass
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            PR::gstore4(rec + RC::OFF_M, RC::M_PLANE, RC::M_ROW, r, 16 * (R + 1) + 4 * gq, zero);
+        }
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             if (I <= R) {
@@ -338,14 +405,6 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
             }
         }
     }
-    // kf e^b, token-major, for the right-hand sides of the substitution
-#pragma unroll
-    for (int ks = 0; ks < KSW; ++ks) {
-        const int c0 = CG * cgi + 32 * ks + 8 * gq;
-        float4* dst = reinterpret_cast<float4*>(khs + t * SH::PKH + c0);
-        dst[0] = make_float4(kh[8 * ks + 0], kh[8 * ks + 1], kh[8 * ks + 2], kh[8 * ks + 3]);
-        dst[1] = make_float4(kh[8 * ks + 4], kh[8 * ks + 5], kh[8 * ks + 6], kh[8 * ks + 7]);
-    }
     lds_sync();
 
     // ---- inverses of the diagonal blocks I + Ldiag_J (wave 0: J = g, column n)
@@ -365,46 +424,59 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
     lds_sync();
 
     // ---- block forward substitution, one 16-column tile of [W | u] at a time
-    constexpr int NCT = DK / 16 + DV / 16;
-    for (int ct = w; ct < NCT; ct += NW) {
-        const bool isk = ct < DK / 16;
-        const int vt = ct - DK / 16;
-        float rhs[4][4];
+    // wave w: channel tiles w, w + NW, ... of W and value tiles w, w + NW, ... of u
+    {
+        auto substitute = [&](const float (&rhs)[4][4], f32x4 (&X)[4]) {
+            typename PR::F4 Xb[4];
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int J = 0; J < 4; ++J)
+            for (int J = 0; J < 4; ++J) {
+                f32x4 z;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tt = 16 * J + 4 * gq + i;
-                if (isk) {
-                    rhs[J][i] = khs[tt * SH::PKH + 16 * ct + n];
-                } else {
-                    rhs[J][i] = (tt < L) ? Elem<Tin>::load(v, (static_cast<size_t>(tok0 + tt) * H + h) * DV + 16 * vt + n)
-                                         : 0.f;
-                }
+                for (int i = 0; i < 4; ++i) z[i] = beta_s[16 * J + 4 * gq + i] * rhs[J][i];
+#pragma unroll
+                for (int K = 0; K < J; ++K) z = PR::mma4(PR::load4(loffm, loff_index(J, K) * 64 + l, 0), Xb[K], z);
+                X[J] = PR::mma4(PR::load4(ym, 16 * J + n, 4 * gq), PR::regs4(z), zero);
+                Xb[J] = PR::regs4(X[J]);
             }
-        f32x4 X[4];
-        typename PR::F4 Xb[4];
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        };
 #pragma unroll
-        for (int J = 0; J < 4; ++J) {
-            f32x4 z;
+        for (int vi = 0; vi < VPW; ++vi) {
+            const int vt = w + NW * vi;
+            if (vt < DV / 16) {
+                float rhs[4][4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) z[i] = beta_s[16 * J + 4 * gq + i] * rhs[J][i];
+                for (int J = 0; J < 4; ++J)
 #pragma unroll
-            for (int K = 0; K < J; ++K) z = PR::mma4(PR::load4(loffm, loff_index(J, K) * 64 + l, 0), Xb[K], z);
-            X[J] = PR::mma4(PR::load4(ym, 16 * J + n, 4 * gq), PR::regs4(z), zero);
-            Xb[J] = PR::regs4(X[J]);
+                    for (int i = 0; i < 4; ++i) {
+                        const float x = __uint_as_float(F32 ? vpre[vi][J][i] : (vpre[vi][J][i] << 16));
+                        rhs[J][i] = (16 * J + 4 * gq + i < L) ? x : 0.f;   // padding rows of V are zero
+                    }
+                f32x4 X[4];
+                substitute(rhs, X);
+#pragma unroll
+                for (int J = 0; J < 4; ++J)
+                    *reinterpret_cast<f32x4*>(rec + RC::OFF_U + ((J * (DV / 16) + vt) * 64 + l) * 16) = X[J];
+            }
         }
-        if (isk) {
+        for (int ct = w; ct < DK / 16; ct += NW) {
+            // kf e^b = (kf e^{b - m}) e^m, m the anchor of the token's half
+            const int c = 16 * ct + n;
+            const float m0 = totb[c], m1 = m0 + totb[DK + c] + totb[2 * DK + c];
+            const float em0 = __builtin_amdgcn_exp2f(fminf(m0, 126.f));
+            const float em1 = __builtin_amdgcn_exp2f(fminf(m1, 126.f));
+            float rhs[4][4];
+#pragma unroll
+            for (int J = 0; J < 4; ++J)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) rhs[J][i] = PR::get1(rkm, 16 * J + 4 * gq + i, c) * (J < 2 ? em0 : em1);
+            f32x4 X[4];
+            substitute(rhs, X);
 #pragma unroll
             for (int J = 0; J < 4; ++J)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     PR::gstore1s(rec + RC::OFF_W, RC::W_ROW, 16 * J + 4 * gq + i, 16 * ct + n, X[J][i]);
-        } else {
-#pragma unroll
-            for (int J = 0; J < 4; ++J)
-                *reinterpret_cast<f32x4*>(rec + RC::OFF_U + ((J * (DV / 16) + vt) * 64 + l) * 16) = X[J];
         }
     }
 }

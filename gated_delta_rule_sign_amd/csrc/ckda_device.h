@@ -70,6 +70,19 @@ struct Raw8<float> {
     }
 };
 
+// A raw buffer resource over `bytes` bytes at `base`: buffer stores beyond
+// the range are dropped by the hardware range check and loads return 0, so
+// a partially valid tile is written with unconditional stores (a guarded
+// store is a branch, which also hides the count of outstanding vector memory
+// operations from the compiler's wait insertion).  Dword 3 = 0x00020000 is
+// the gfx9-family raw 32-bit format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ void buffer_store_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, static_cast<int>(byte_off), 0, 0);
+}
+
 // exp(x) through the hardware base-2 exponential; the argument is clamped so
 // that no infinity can be produced (exp2(126) is finite in fp32)
 __device__ __forceinline__ float exp2_clamped(float x2) {

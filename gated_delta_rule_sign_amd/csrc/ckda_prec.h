@@ -78,6 +78,11 @@ struct Prec<false> {
         *hp(d, dr, dc) = *hp(s, sr, sc);
         *lp(d, dr, dc) = *lp(s, sr, sc);
     }
+    // an 8-slot fragment (elements c .. c+7 of row r) back to LDS
+    static __device__ __forceinline__ void store8f(const LdsMat& m, int r, int c, const F8& x) {
+        *reinterpret_cast<bf16x8*>(hp(m, r, c)) = x.hi;
+        *reinterpret_cast<bf16x8*>(lp(m, r, c)) = x.lo;
+    }
     // one element back as hi + lo
     static __device__ __forceinline__ float get1(const LdsMat& m, int r, int c) {
         return bf16_to_f32(*hp(m, r, c)) + bf16_to_f32(*lp(m, r, c));
@@ -106,7 +111,15 @@ struct Prec<false> {
         return mfma16x3(a.hi, a.lo, b.hi, b.lo, acc);
     }
 
-    // single-plane A operand (a value stored once, already rounded to bf16)
+    // single-plane A operands (a value stored once, already rounded to bf16)
+    typedef bf16x8 A8s;
+    static __device__ __forceinline__ A8s load4x2s(const LdsMat& m, int r, int ca, int cb) {
+        return lds4x2(hp(m, r, ca), hp(m, r, cb));
+    }
+    static __device__ __forceinline__ f32x4 mma8s(const A8s& a, const F8& b, f32x4 acc) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b.lo, acc, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b.hi, acc, 0, 0, 0);
+    }
     typedef s16x4 A4s;
     static __device__ __forceinline__ A4s load4s(const LdsMat& m, int r, int c) { return lds4s(hp(m, r, c)); }
     static __device__ __forceinline__ f32x4 mma4s(const A4s& a, const F4& b, f32x4 acc) {
@@ -167,6 +180,11 @@ struct Prec<true> {
         *fp(d, dr, dc) = *fp(s, sr, sc);
     }
     static __device__ __forceinline__ float get1(const LdsMat& m, int r, int c) { return *fp(m, r, c); }
+    static __device__ __forceinline__ void store8f(const LdsMat& m, int r, int c, const F8& x) {
+        float4* p = reinterpret_cast<float4*>(fp(m, r, c));
+        p[0] = make_float4(x.a[0], x.a[1], x.a[2], x.a[3]);
+        p[1] = make_float4(x.b[0], x.b[1], x.b[2], x.b[3]);
+    }
     static __device__ __forceinline__ f32x4 ld4(const float* p) {
         const float4 v = *reinterpret_cast<const float4*>(p);
         f32x4 r = {v.x, v.y, v.z, v.w};
@@ -194,6 +212,9 @@ struct Prec<true> {
         return acc;
     }
 
+    typedef F8 A8s;
+    static __device__ __forceinline__ A8s load4x2s(const LdsMat& m, int r, int ca, int cb) { return load4x2(m, r, ca, cb); }
+    static __device__ __forceinline__ f32x4 mma8s(const A8s& x, const F8& y, f32x4 acc) { return mma8(x, y, acc); }
     typedef f32x4 A4s;
     static __device__ __forceinline__ A4s load4s(const LdsMat& m, int r, int c) { return ld4(fp(m, r, c)); }
     static __device__ __forceinline__ f32x4 mma4s(const A4s& x, const F4& y, f32x4 acc) {

@@ -8,7 +8,8 @@
 //   W   = X^{-1} Diag(beta) (kf e^b)          [64][DK]  token-major
 //   Qh  = qf e^b                               [64][DK]  token-major
 //   KbT = (P_L kf e^{b_L - b})^T               [DK][64]  channel-major
-//   M   (lower triangle; blocks above the diagonal are never read)
+//   M   (lower triangle, zero above the diagonal inside the 32x32 diagonal
+//        blocks; blocks (0..31, 32..63) are never read)
 //                                              [64][64]  row = output token
 //   d   = P_L e^{b_L}                          [DK]      float32
 //   u   = X^{-1} Diag(beta) V                  [64][DV]  float32, stored as

@@ -14,11 +14,16 @@
 // document, head, 64-wide value slice); wave w owns value columns
 // [16w, 16w+16) of the slice and keeps that DK x 16 block of S in MFMA
 // accumulator registers for the whole sequence (value columns of S evolve
-// independently, so the waves never exchange state).  Each chunk's record
-// (W, Qh, KbT, M, d) is read from HBM once per workgroup into registers one
-// chunk ahead, then staged in LDS and shared by the four waves; u is read by
-// each wave straight into its C-layout registers.  All products are 16x16x16
-// matrix-core tiles: the C/D layout of S and U doubles as the B operand.
+// independently, so the waves never exchange state).  Four more waves only
+// move data: they hold the next chunk's record (W, Qh, KbT, M, d and the
+// slice's u tiles) in registers, read one chunk ahead from HBM, and write it
+// to LDS at the chunk boundary.  A wave that issues global loads stalls
+// whenever the memory pipe is full; keeping those loads on separate waves
+// lets the matrix-core waves run while the next record streams in.  Products are 16x16x32
+// matrix-core tiles whose 8 K-slots per lane are two 4-row groups of the C/D
+// layout (rows 4g..4g+3 of tiles 2k and 2k+1), so S and U feed the B side
+// straight from their accumulator layout; the A side reads the matching
+// elements (columns 32k + 4g .. +3 and 32k + 16 + 4g .. +3).
 #include "ckda_device.h"
 #include "ckda_launch.h"
 #include "ckda_mfma.h"
@@ -32,7 +37,7 @@ template <typename Tin, int DK, int DV>
 struct StateShape {
     static constexpr bool F32 = sizeof(Tin) == 4;
     using RC = Record<DK, DV, F32>;
-    static constexpr int NT = 256;                 // threads
+    static constexpr int NT = 256;                 // threads per role (4 compute + 4 loader waves)
     static constexpr int BV = DV < 64 ? DV : 64;   // value columns per workgroup
     static constexpr int NSLICE = DV / BV;
     static constexpr int NWC = BV / 16;            // waves that own columns
@@ -48,7 +53,8 @@ struct StateShape {
     static constexpr int L_K = L_Q + NP * 64 * PQ * ES;
     static constexpr int L_M = L_K + NP * DK * PKR * ES;
     static constexpr int L_D = L_M + NP * 64 * PMR * ES;
-    static constexpr int LDS = L_D + DK * 4;
+    static constexpr int L_U = L_D + DK * 4;            // u tiles of the slice [4][NWC][64 lanes][4]
+    static constexpr int LDS = L_U + 4 * NWC * 64 * 16;
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -78,13 +84,13 @@ struct StateParams {
     int B, T, H, ndocs;
 };
 
-template <typename Tin, int DK, int DV>
-__global__ void __launch_bounds__(256, 1) ckda_state_kernel(StateParams p)
+template <typename Tin, int DK, int DV, bool CKPT>
+__global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
 {
     using SH = StateShape<Tin, DK, DV>;
     using RC = typename SH::RC;
     using PR = Prec<SH::F32>;
-    constexpr int RT = SH::RT, NP = SH::NP, NT = SH::NT;
+    constexpr int RT = SH::RT, NP = SH::NP, NT = SH::NT, NWC = SH::NWC;
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int H = p.H;
@@ -125,17 +131,111 @@ __global__ void __launch_bounds__(256, 1) ckda_state_kernel(StateParams p)
         slot0 = sidx * ((p.T + 63) / 64);
     }
     const int nchunks = (len + 63) / 64;
-    const size_t st_off = (static_cast<size_t>(sidx) * H + h) * DK * DV;
+    const int vt0 = (slice * SH::BV) / 16;   // first 16-column tile of the slice
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
 
-    const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool has_col = w < SH::NWC;
-    const int vt = (slice * SH::BV) / 16 + w;   // the wave's 16-column tile of DV
+    if (w >= 4) {
+        // ================= loader waves ====================================
+        // Two register groups: A = W, Qh (read by the first products of a
+        // chunk), B = KbT, M, d, u (read by the rest).  Per chunk j:
+        //   barrier 0 (record j complete) -> issue B loads of j+1
+        //   barrier 1 (W, Qh of j no longer read) -> write A of j+1, issue A loads of j+2
+        //   barrier 2 (chunk j done) -> write B of j+1
+        // so only the write of group B lies between two chunks.
+        using StW = Stage<64, RC::W_ROW / 16, 16, NT>;
+        using StQ = Stage<NP * 64, RC::Q_ROW / 16, 16, NT>;
+        using StK = Stage<NP * DK, RC::K_ROW / 16, 16, NT>;
+        using StM = Stage<NP * 64, RC::M_ROW / 16, 16, NT>;
+        using StD = Stage<1, DK * 4 / 16, 0, NT>;
+        using StU = Stage<4, NWC * 64, 0, NT>;   // per J: the slice's NWC tiles, 64 lanes each
+        constexpr int NW_ = StW::N, NQ_ = StQ::N, NK_ = StK::N, NM_ = StM::N, ND_ = StD::N, NU_ = StU::N;
+        constexpr int O_Q = NW_, NA = NW_ + NQ_;
+        constexpr int O_M = NK_, O_D = O_M + NM_, O_U = O_D + ND_, NB = O_U + NU_;
+        static_assert(StW::FULL && StQ::FULL && StK::FULL && StM::FULL && StU::FULL, "unguarded staging loads");
+        u32x4 ga[NA], gb[NB];   // native vectors (a struct copy would keep them in scratch)
+#define CKDA_REC(J) reinterpret_cast<const u32x4*>(p.ws + (static_cast<size_t>(slot0 + (J)) * H + h) * RC::BYTES + opaque_zero())
+#define CKDA_LOAD_A(J)                                                                                       \
+        {                                                                                                    \
+            const u32x4* g_ = CKDA_REC(J);                                                                   \
+            const int t_ = opaque_tid() - NT;                                                                \
+            _Pragma("unroll") for (int i_ = 0; i_ < NW_; ++i_) ga[i_] = g_[RC::OFF_W / 16 + t_ + NT * i_];   \
+            _Pragma("unroll") for (int i_ = 0; i_ < NQ_; ++i_) ga[O_Q + i_] = g_[RC::OFF_Q / 16 + t_ + NT * i_]; \
+        }
+#define CKDA_LOAD_B(J)                                                                                       \
+        {                                                                                                    \
+            const u32x4* g_ = CKDA_REC(J);                                                                   \
+            const int t_ = opaque_tid() - NT;                                                                \
+            _Pragma("unroll") for (int i_ = 0; i_ < NK_; ++i_) gb[i_] = g_[RC::OFF_K / 16 + t_ + NT * i_];   \
+            _Pragma("unroll") for (int i_ = 0; i_ < NM_; ++i_) gb[O_M + i_] = g_[RC::OFF_M / 16 + t_ + NT * i_]; \
+            _Pragma("unroll") for (int i_ = 0; i_ < ND_; ++i_)                                               \
+                if (StD::has(t_, i_)) gb[O_D + i_] = g_[RC::OFF_D / 16 + t_ + NT * i_];                       \
+            _Pragma("unroll") for (int i_ = 0; i_ < NU_; ++i_) {                                             \
+                const int u_ = t_ + NT * i_;                                                                 \
+                const int J_ = u_ / (NWC * 64), r_ = u_ % (NWC * 64);                                        \
+                gb[O_U + i_] = g_[RC::OFF_U / 16 + (J_ * (DV / 16) + vt0) * 64 + r_];                        \
+            }                                                                                                \
+        }
+#define CKDA_STORE_A()                                                                                       \
+        {                                                                                                    \
+            unsigned char* const sm_ = smem + opaque_zero();                                                 \
+            const int t_ = opaque_tid() - NT;                                                                \
+            _Pragma("unroll") for (int i_ = 0; i_ < NW_; ++i_)                                               \
+                *reinterpret_cast<u32x4*>(sm_ + SH::L_W + StW::lds_off(t_, i_)) = ga[i_];                    \
+            _Pragma("unroll") for (int i_ = 0; i_ < NQ_; ++i_)                                               \
+                *reinterpret_cast<u32x4*>(sm_ + SH::L_Q + StQ::lds_off(t_, i_)) = ga[O_Q + i_];              \
+        }
+#define CKDA_STORE_B()                                                                                       \
+        {                                                                                                    \
+            unsigned char* const sm_ = smem + opaque_zero();                                                 \
+            const int t_ = opaque_tid() - NT;                                                                \
+            _Pragma("unroll") for (int i_ = 0; i_ < NK_; ++i_)                                               \
+                *reinterpret_cast<u32x4*>(sm_ + SH::L_K + StK::lds_off(t_, i_)) = gb[i_];                    \
+            _Pragma("unroll") for (int i_ = 0; i_ < NM_; ++i_)                                               \
+                *reinterpret_cast<u32x4*>(sm_ + SH::L_M + StM::lds_off(t_, i_)) = gb[O_M + i_];              \
+            _Pragma("unroll") for (int i_ = 0; i_ < ND_; ++i_)                                               \
+                if (StD::has(t_, i_)) *reinterpret_cast<u32x4*>(sm_ + SH::L_D + StD::lds_off(t_, i_)) = gb[O_D + i_]; \
+            _Pragma("unroll") for (int i_ = 0; i_ < NU_; ++i_)                                               \
+                *reinterpret_cast<u32x4*>(sm_ + SH::L_U + StU::lds_off(t_, i_)) = gb[O_U + i_];              \
+        }
+        if (nchunks > 0) {
+            CKDA_LOAD_A(0)
+            CKDA_LOAD_B(0)
+            CKDA_STORE_A()
+            CKDA_STORE_B()
+            CKDA_LOAD_A(min(1, nchunks - 1))
+        }
+        // (the last chunks re-read the final record: no branches)
+        for (int j = 0; j < nchunks; ++j) {
+            lds_sync();   // 0: record j complete in LDS
+            CKDA_LOAD_B(min(j + 1, nchunks - 1))
+            lds_sync();   // 1: W, Qh of chunk j consumed
+            CKDA_STORE_A()
+            CKDA_LOAD_A(min(j + 2, nchunks - 1))
+            lds_sync();   // 2: chunk j consumed
+            CKDA_STORE_B()
+        }
+#undef CKDA_REC
+#undef CKDA_LOAD_A
+#undef CKDA_LOAD_B
+#undef CKDA_STORE_A
+#undef CKDA_STORE_B
+        return;
+    }
+
+    // ================= compute waves ==========================================
+    const size_t st_off = (static_cast<size_t>(sidx) * H + h) * DK * DV;
+    const bool has_col = w < NWC;
+    // the wave's 16-column tile of DV; waves without columns (DV < 64) run
+    // the slice's last tile again with their stores switched off, so the
+    // loop body has no branches around vector memory (the compiler's wait
+    // insertion then knows how many stores are in flight)
+    const int wt = min(w, NWC - 1);
+    const int vt = vt0 + wt;
 
     // ---- state: lane (n, g) holds rows 16rt + 4g + i of column 16vt + n ----
     f32x4 S[RT];
     {
-        const int l = tid & 63, gq = l >> 4, col = 16 * vt + (l & 15);
+        const int l = threadIdx.x & 63, gq = l >> 4, col = 16 * vt + (l & 15);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -143,67 +243,11 @@ __global__ void __launch_bounds__(256, 1) ckda_state_kernel(StateParams p)
                 S[rt][i] = (has_col && p.h0) ? p.h0[st_off + static_cast<size_t>(16 * rt + 4 * gq + i) * DV + col] : 0.f;
     }
 
-    // one chunk's record, staged through registers: W, Qh, KbT, M, d are
-    // consecutive in the record and in LDS (with padded rows)
-    using StW = Stage<64, RC::W_ROW / 16, 16, NT>;
-    using StQ = Stage<NP * 64, RC::Q_ROW / 16, 16, NT>;
-    using StK = Stage<NP * DK, RC::K_ROW / 16, 16, NT>;
-    using StM = Stage<NP * 64, RC::M_ROW / 16, 16, NT>;
-    using StD = Stage<1, DK * 4 / 16, 0, NT>;
-    constexpr int NW_ = StW::N, NQ_ = StQ::N, NK_ = StK::N, NM_ = StM::N, ND_ = StD::N;
-    constexpr int NREG = NW_ + NQ_ + NK_ + NM_ + ND_;
-    static_assert(StW::FULL && StQ::FULL && StK::FULL && StM::FULL, "unguarded staging loads");
-    u32x4 stg[NREG];   // native vectors (a struct copy would keep them in scratch)
-    f32x4 uin[4];
-    // issue the global loads of chunk J's record (registers, one chunk ahead)
-#define CKDA_LOAD_CHUNK(J)                                                                         \
-    {                                                                                              \
-        const unsigned char* rc_ =                                                                 \
-            p.ws + (static_cast<size_t>(slot0 + (J)) * H + h) * RC::BYTES + opaque_zero();         \
-        const int t_ = opaque_tid();                                                               \
-        const u32x4* g_ = reinterpret_cast<const u32x4*>(rc_);                                     \
-        _Pragma("unroll") for (int i_ = 0; i_ < NW_; ++i_) stg[i_] = g_[RC::OFF_W / 16 + t_ + NT * i_]; \
-        _Pragma("unroll") for (int i_ = 0; i_ < NQ_; ++i_) stg[NW_ + i_] = g_[RC::OFF_Q / 16 + t_ + NT * i_]; \
-        _Pragma("unroll") for (int i_ = 0; i_ < NK_; ++i_) stg[NW_ + NQ_ + i_] = g_[RC::OFF_K / 16 + t_ + NT * i_]; \
-        _Pragma("unroll") for (int i_ = 0; i_ < NM_; ++i_) stg[NW_ + NQ_ + NK_ + i_] = g_[RC::OFF_M / 16 + t_ + NT * i_]; \
-        _Pragma("unroll") for (int i_ = 0; i_ < ND_; ++i_)                                         \
-            if (StD::has(t_, i_)) stg[NW_ + NQ_ + NK_ + NM_ + i_] = g_[RC::OFF_D / 16 + t_ + NT * i_]; \
-        if (has_col) {                                                                             \
-            const int l_ = t_ & 63;                                                                \
-            _Pragma("unroll") for (int J_ = 0; J_ < 4; ++J_) uin[J_] =                             \
-                *reinterpret_cast<const f32x4*>(rc_ + RC::OFF_U + ((J_ * (DV / 16) + vt) * 64 + l_) * 16); \
-        }                                                                                          \
-    }
-    if (nchunks > 0) CKDA_LOAD_CHUNK(0)
-
     for (int j = 0; j < nchunks; ++j) {
         const int c0 = 64 * j;
         const int L = min(64, len - c0);
+        lds_sync();   // 0: record of chunk j in LDS
         {
-            unsigned char* const sm = smem + opaque_zero();
-            const int t = opaque_tid();
-#pragma unroll
-            for (int i = 0; i < NW_; ++i) *reinterpret_cast<u32x4*>(sm + SH::L_W + StW::lds_off(t, i)) = stg[i];
-#pragma unroll
-            for (int i = 0; i < NQ_; ++i) *reinterpret_cast<u32x4*>(sm + SH::L_Q + StQ::lds_off(t, i)) = stg[NW_ + i];
-#pragma unroll
-            for (int i = 0; i < NK_; ++i)
-                *reinterpret_cast<u32x4*>(sm + SH::L_K + StK::lds_off(t, i)) = stg[NW_ + NQ_ + i];
-#pragma unroll
-            for (int i = 0; i < NM_; ++i)
-                *reinterpret_cast<u32x4*>(sm + SH::L_M + StM::lds_off(t, i)) = stg[NW_ + NQ_ + NK_ + i];
-#pragma unroll
-            for (int i = 0; i < ND_; ++i)
-                if (StD::has(t, i))
-                    *reinterpret_cast<u32x4*>(sm + SH::L_D + StD::lds_off(t, i)) = stg[NW_ + NQ_ + NK_ + NM_ + i];
-        }
-        f32x4 u[4];
-#pragma unroll
-        for (int J = 0; J < 4; ++J) u[J] = uin[J];
-        lds_sync();
-        if (j + 1 < nchunks) CKDA_LOAD_CHUNK(j + 1)
-
-        if (has_col) {
             unsigned char* const sm = smem + opaque_zero();
             const LdsMat Wm{sm + SH::L_W, SH::PW, 0};
             const LdsMat Qm{sm + SH::L_Q, SH::PQ, 64 * SH::PQ};
@@ -212,73 +256,127 @@ __global__ void __launch_bounds__(256, 1) ckda_state_kernel(StateParams p)
             const float* dl = reinterpret_cast<const float*>(sm + SH::L_D);
             const int l = opaque_tid() & 63, n = l & 15, gq = l >> 4;
             const int col = 16 * vt + n;
-            if (p.h_ckpt) {
-                float* hc = p.h_ckpt + (static_cast<size_t>(sidx) * H + h) * static_cast<size_t>(nchunks) * DK * DV +
-                            static_cast<size_t>(j) * DK * DV;
+            f32x4 u[4];
+#pragma unroll
+            for (int J = 0; J < 4; ++J) u[J] = *reinterpret_cast<const f32x4*>(sm + SH::L_U + ((J * NWC + wt) * 64 + l) * 16);
+            if (CKPT) {   // the state at the chunk start (waves without columns store nothing)
+                const float* hc = p.h_ckpt + (static_cast<size_t>(sidx) * H + h) * static_cast<size_t>(nchunks) * DK * DV +
+                                  static_cast<size_t>(j) * DK * DV;
+                const __amdgpu_buffer_rsrc_t hrc = buffer_rsrc(hc, has_col ? DK * DV * 4 : 0);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) hc[static_cast<size_t>(16 * rt + 4 * gq + i) * DV + col] = S[rt][i];
+                    for (int i = 0; i < 4; ++i)
+                        buffer_store_f32(hrc, static_cast<uint32_t>(((16 * rt + 4 * gq + i) * DV + col) * 4), S[rt][i]);
             }
-            // W S and Qh S
-            typename PR::F4 Sb[RT];
+            // The LDS fragments of step k+1 are read while the products of
+            // step k run (fences keep the scheduler from sinking each read
+            // next to its use, which would expose every LDS round trip: one
+            // wave per SIMD has no other wave to hide it behind).
+            constexpr int KS = RT / 2;
+            // W S and Qh S, 32 channels per step
+            typename PR::F8 Sb[KS];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) Sb[rt] = PR::regs4(S[rt]);
+            for (int ks = 0; ks < KS; ++ks) Sb[ks] = PR::regs8(S[2 * ks], S[2 * ks + 1]);
             f32x4 X[4], Y[4];
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
                 X[R] = f32x4{0.f, 0.f, 0.f, 0.f};
                 Y[R] = X[R];
             }
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
+            {
+                typename PR::A8s wa[2][4];
+                typename PR::F8 qa[2][4];
 #pragma unroll
                 for (int R = 0; R < 4; ++R) {
-                    X[R] = PR::mma4s(PR::load4s(Wm, 16 * R + n, 16 * rt + 4 * gq), Sb[rt], X[R]);
-                    Y[R] = PR::mma4(PR::load4(Qm, 16 * R + n, 16 * rt + 4 * gq), Sb[rt], Y[R]);
+                    wa[0][R] = PR::load4x2s(Wm, 16 * R + n, 4 * gq, 16 + 4 * gq);
+                    qa[0][R] = PR::load4x2(Qm, 16 * R + n, 4 * gq, 16 + 4 * gq);
                 }
-            // U = u - W S
-            typename PR::F4 Ub[4];
 #pragma unroll
-            for (int R = 0; R < 4; ++R) Ub[R] = PR::regs4(u[R] - X[R]);
-            // O = scale (Qh S + M U)
+                for (int ks = 0; ks < KS; ++ks) {
+                    if (ks + 1 < KS) {
+                        const int ca = 32 * (ks + 1) + 4 * gq, cb = ca + 16;
 #pragma unroll
-            for (int R = 0; R < 4; ++R) {
+                        for (int R = 0; R < 4; ++R) {
+                            wa[(ks + 1) & 1][R] = PR::load4x2s(Wm, 16 * R + n, ca, cb);
+                            qa[(ks + 1) & 1][R] = PR::load4x2(Qm, 16 * R + n, ca, cb);
+                        }
+                    }
+                    CKDA_FENCE();
+#pragma unroll
+                    for (int R = 0; R < 4; ++R) {
+                        X[R] = PR::mma8s(wa[ks & 1][R], Sb[ks], X[R]);
+                        Y[R] = PR::mma8(qa[ks & 1][R], Sb[ks], Y[R]);
+                    }
+                    CKDA_FENCE();
+                }
+            }
+            lds_sync();   // 1: W, Qh consumed (the loaders refill them for chunk j+1)
+            // M fragments for the output and the first KbT fragments, read
+            // while U is formed
+            typename PR::F8 ma[6];
+#pragma unroll
+            for (int R = 0, x = 0; R < 4; ++R)
+#pragma unroll
+                for (int kt = 0; kt <= R / 2; ++kt, ++x)
+                    ma[x] = PR::load4x2(Mm, 16 * R + n, 32 * kt + 4 * gq, 32 * kt + 16 + 4 * gq);
+            typename PR::F8 ka[2][2];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) ka[0][kt] = PR::load4x2(Km, n, 32 * kt + 4 * gq, 32 * kt + 16 + 4 * gq);
+            CKDA_FENCE();
+            // U = u - W S, as B operands over 32 tokens per step
+            typename PR::F8 Ub[2];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) Ub[kt] = PR::regs8(u[2 * kt] - X[2 * kt], u[2 * kt + 1] - X[2 * kt + 1]);
+            // O = scale (Qh S + M U) (M is zero above its diagonal, also in
+            // blocks (0,1) and (2,3) that the 32-token steps read); the
+            // buffer covers the chunk's L valid rows
+            const __amdgpu_buffer_rsrc_t orc = buffer_rsrc(p.o + static_cast<size_t>(tok0 + c0) * H * DV,
+                                                           has_col ? static_cast<uint32_t>(L * H * DV * 4) : 0u);
+#pragma unroll
+            for (int R = 0, x = 0; R < 4; ++R) {
                 f32x4 acc = Y[R];
 #pragma unroll
-                for (int K = 0; K <= R; ++K) acc = PR::mma4(PR::load4(Mm, 16 * R + n, 16 * K + 4 * gq), Ub[K], acc);
+                for (int kt = 0; kt <= R / 2; ++kt, ++x) acc = PR::mma8(ma[x], Ub[kt], acc);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tt = 16 * R + 4 * gq + i;
-                    if (tt < L) p.o[(static_cast<size_t>(tok0 + c0 + tt) * H + h) * DV + col] = p.scale * acc[i];
+                    buffer_store_f32(orc, static_cast<uint32_t>(((tt * H + h) * DV + col) * 4), p.scale * acc[i]);
                 }
             }
             // S <- Diag(d) S + KbT U
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
+                if (rt + 1 < RT) {
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt)
+                        ka[(rt + 1) & 1][kt] =
+                            PR::load4x2(Km, 16 * (rt + 1) + n, 32 * kt + 4 * gq, 32 * kt + 16 + 4 * gq);
+                }
+                const f32x4 dd = *reinterpret_cast<const f32x4*>(dl + 16 * rt + 4 * gq);
+                CKDA_FENCE();
                 f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int K = 0; K < 4; ++K) acc = PR::mma4(PR::load4(Km, 16 * rt + n, 16 * K + 4 * gq), Ub[K], acc);
-                const f32x4 dd = *reinterpret_cast<const f32x4*>(dl + 16 * rt + 4 * gq);
+                for (int kt = 0; kt < 2; ++kt) acc = PR::mma8(ka[rt & 1][kt], Ub[kt], acc);
                 S[rt] = dd * S[rt] + acc;
+                CKDA_FENCE();
             }
         }
-        lds_sync();
+        lds_sync();   // 2: chunk j consumed
     }
 
     if (p.ht && has_col) {
-        const int l = tid & 63, gq = l >> 4, col = 16 * vt + (l & 15);
+        const int l = threadIdx.x & 63, gq = l >> 4, col = 16 * vt + (l & 15);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 p.ht[st_off + opaque_zero() + static_cast<size_t>(16 * rt + 4 * gq + i) * DV + col] = S[rt][i];
     }
-#undef CKDA_LOAD_CHUNK
 }
 
-template <typename Tin, int DK, int DV>
-static hipError_t launch_state_t(const FwdArgs& A, hipStream_t stream) {
+template <typename Tin, int DK, int DV, bool CKPT>
+static hipError_t launch_state_c(const FwdArgs& A, hipStream_t stream) {
     using SH = StateShape<Tin, DK, DV>;
     StateParams p;
     p.ws = static_cast<const unsigned char*>(A.ws);
@@ -287,12 +385,17 @@ static hipError_t launch_state_t(const FwdArgs& A, hipStream_t stream) {
     const int nchains = A.cu ? A.ndocs * A.H : A.B * A.H;
     const int grid = nchains * SH::NSLICE;
     if (grid == 0) return hipSuccess;
-    auto kern = ckda_state_kernel<Tin, DK, DV>;
+    auto kern = ckda_state_kernel<Tin, DK, DV, CKPT>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, SH::LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(SH::NT), SH::LDS, stream, p);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(2 * SH::NT), SH::LDS, stream, p);
     return hipGetLastError();
+}
+
+template <typename Tin, int DK, int DV>
+static hipError_t launch_state_t(const FwdArgs& A, hipStream_t stream) {
+    return A.h_ckpt ? launch_state_c<Tin, DK, DV, true>(A, stream) : launch_state_c<Tin, DK, DV, false>(A, stream);
 }
 
 template <typename Tin>
