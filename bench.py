@@ -1,9 +1,11 @@
 """Throughput of the CKDA hot path on one MI355X.
 
-A step is one chunked forward (gate/sign-fold prep, chunk-local UT/WY
-products, state passing and output, fused in one kernel) over the mixer
-workload of the 1.36B model: B=8, T=4096, H=16, dk=dv=128, bf16 q/k/v,
-fp32 gates, state and outputs.  The JSON line's ``value`` is that forward's
+A step is one chunked forward, i.e. one ckda_fwd_chunked call: the
+chunk-local kernel (gate/sign-fold prep, intra-chunk products, UT/WY
+substitution, over every (chunk, head) at once) followed by the
+state-passing kernel (state products, output, state update, chunk by
+chunk), over the mixer workload of the 1.36B model: B=8, T=4096, H=16,
+dk=dv=128, bf16 q/k/v, fp32 gates, state and outputs.  The JSON line's ``value`` is that forward's
 tokens/s; the decode workload (256 sequences x 16 heads, 512 recurrent
 steps) is reported in the same line as state-streaming GB/s, and the
 backward (when built) as tokens/s.
@@ -87,7 +89,8 @@ def bench_fwd(torch, steps, warmup):
     ms = wall / steps
     avg_launch = float(np.mean(per))
     return dict(w=w, tokens=tokens, ms=ms, launch_ms=avg_launch, launch_all=per,
-                bytes=th * FWD_BYTES_PER_TOKEN_HEAD, flops=th * FWD_FLOPS_PER_TOKEN_HEAD)
+                bytes=th * FWD_BYTES_PER_TOKEN_HEAD, flops=th * FWD_FLOPS_PER_TOKEN_HEAD,
+                workspace_bytes=int(ws.numel()))
 
 
 def bench_decode(torch, nsteps=512, distinct=64):
@@ -243,9 +246,11 @@ def main():
                    "inputs": "q,k,v bf16; g,beta f32; s int8", "state_and_outputs": "f32"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "ckda_fwd_kernel<bf16,128,128>",
+                     "kernel": "ckda_fwd_chunked call = ckda_chunk_kernel<bf16,128,128> + "
+                               "ckda_state_kernel<bf16,128,128,false>",
                      "algorithmic_bytes_per_launch": fw["bytes"],
                      "avg_launch_ms": fw["launch_ms"],
+                     "workspace_bytes": fw["workspace_bytes"],
                      "mfma_algorithmic_frac": fw["flops"] / (fw["launch_ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
         "decode": {"workload": "decode_b256: 256 seqs x 16 heads, dk=dv=128, 512 steps",
                    "unit": "GB/s", "value": dec["gbs"], "frac_of_hbm_peak": dec["gbs"] / HBM_PEAK_GBS,

@@ -75,6 +75,37 @@ def fwd_chain(q, k, v, g, s, beta, scale=1.0, S0=None, C=64, anchored=True):
     return o, S
 
 
+def chunk_record(q, k, v, g, s, beta, C=64):
+    """The per-chunk record of the two-kernel forward, for one chunk (L <= C
+    tokens): everything that does not depend on the state.
+        W = T (kf e^b),  u = T V,  Qh = qf e^b,  KbT = (P_L kf e^{b_L - b})^T,
+        M (lower),  d = P_L e^{b_L},   T = (I + Diag(beta) A)^{-1} Diag(beta)"""
+    b = np.cumsum(g, axis=0)
+    P = np.cumprod(s, axis=0)
+    qt, kt = P * q, P * k
+    A, M = _intra(qt, kt, b, anchored=True)
+    L = q.shape[0]
+    Tm = np.linalg.solve(np.eye(L) + beta[:, None] * A, np.diag(beta))
+    return dict(W=Tm @ (kt * np.exp(b)), u=Tm @ v, Qh=qt * np.exp(b),
+                KbT=(P[-1] * kt * np.exp(b[-1] - b)).T, M=M, d=P[-1] * np.exp(b[-1]))
+
+
+def fwd_chain_record(q, k, v, g, s, beta, scale=1.0, S0=None, C=64):
+    """The state pass over chunk records: U = u - W S, O = scale (Qh S + M U),
+    S <- Diag(d) S + KbT U.  Returns (o, S_T)."""
+    T, DK = q.shape
+    DV = v.shape[1]
+    S = np.zeros((DK, DV)) if S0 is None else np.array(S0, dtype=np.float64)
+    o = np.zeros((T, DV))
+    for c0 in range(0, T, C):
+        c1 = min(T, c0 + C)
+        r = chunk_record(q[c0:c1], k[c0:c1], v[c0:c1], g[c0:c1], s[c0:c1], beta[c0:c1], C)
+        U = r["u"] - r["W"] @ S
+        o[c0:c1] = scale * (r["Qh"] @ S + r["M"] @ U)
+        S = r["d"][:, None] * S + r["KbT"] @ U
+    return o, S
+
+
 def bwd_chain(q, k, v, g, s, beta, do, scale=1.0, S0=None, dST=None, C=64):
     """Chunk-wise reverse mode of L = <do, o> + <dST, S_T>, same notation as
     fwd_chain (unanchored exponentials; float64 only).  Returns dict dq, dk,

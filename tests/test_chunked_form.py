@@ -19,6 +19,19 @@ def test_chunked_forward_equals_token_oracle():
             np.testing.assert_allclose(Sc, ST[i], rtol=0, atol=1e-12)
 
 
+def test_record_form_equals_token_oracle():
+    """The split forward: a state-independent record per chunk, then the
+    state pass U = u - W S, O = Qh S + M U, S <- Diag(d) S + KbT U."""
+    rng = np.random.default_rng(24)
+    q, k, v, g, s, beta = rand_inputs(rng, 2, 150, 16, 8, p_neg=0.3)
+    S0 = rng.standard_normal((2, 16, 8))
+    o, ST = oracle.fwd_chain_arrays(q, k, v, g, s, beta, 0.8, S0)
+    for i in range(2):
+        oc, Sc = CR.fwd_chain_record(q[i], k[i], v[i], g[i], s[i], beta[i], 0.8, S0[i])
+        np.testing.assert_allclose(oc, o[i], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(Sc, ST[i], rtol=0, atol=1e-12)
+
+
 def test_chunked_backward_equals_token_oracle():
     rng = np.random.default_rng(22)
     q, k, v, g, s, beta = rand_inputs(rng, 1, 140, 8, 6, p_neg=0.3)
