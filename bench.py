@@ -40,6 +40,27 @@ FWD_FLOPS_PER_TOKEN_HEAD = 181.6e3
 DEC_BYTES_PER_HEAD_STEP = 2 * 128 * 128 * 4 + 3 * 256 + 512 + 128 + 2 * 128 + 4 + 512
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ckda_fwd_traffic__layer_bf16.json")
+
+
+def measured_traffic():
+    """HBM bytes per forward call from the committed FETCH_SIZE / WRITE_SIZE
+    runs (calibrated on a plain copy), or None when the forward kernel sources
+    have changed since those counters were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in rec.get("sources", []):
+        with open(os.path.join(ROOT, "gated_delta_rule_sign_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != rec.get("sources_sha256"):
+        return None
+    return float(rec["traffic_bytes_per_call"])
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -245,7 +266,7 @@ def main():
                    "B": 8, "T": 4096, "H": 16, "dk": 128, "dv": 128, "chunk": 64,
                    "inputs": "q,k,v bf16; g,beta f32; s int8", "state_and_outputs": "f32"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "ckda_fwd_chunked call = ckda_chunk_kernel<bf16,128,128> + "
                                "ckda_state_kernel<bf16,128,128,false>",
                      "algorithmic_bytes_per_launch": fw["bytes"],
