@@ -125,27 +125,95 @@ struct Gemm {
     int mask;
 };
 
+// One workgroup per batch element: C (64 x N) = A (64 x K) B (K x N), N, K in
+// {32, 64, 128}.  K is processed in slabs of 32: both operands of a slab are
+// read with coalesced 16-byte loads into LDS in the layout their storage
+// gives (row-major or transposed), then wave w forms rows 16w..16w+15 for all
+// N/16 column tiles, so each A fragment serves every tile of the row block.
+// About 28 KB of LDS, so several workgroups share a CU and hide each other's
+// load latency.
+constexpr int kKS = 32;          // slab width (K)
+constexpr int kPK = kKS + 4;     // pitch of rows that run along K
+constexpr int kPN = 64 + 4;      // pitch of rows that run along M or N (64-wide blocks)
+
+__device__ __forceinline__ void stage_slab(float* dst, int pitch, const float* src, int rows, int cols, int ld, int r0,
+                                           int c0) {
+    // copy src[(r0 + r) * ld + c0 + c] for r < rows, c < cols (a multiple of 4) into dst[r * pitch + c]
+    const int q = cols / 4;
+    for (int e = threadIdx.x; e < rows * q; e += 256) {
+        const int r = e / q, c4 = (e % q) * 4;
+        const float4 v = *reinterpret_cast<const float4*>(src + static_cast<size_t>(r0 + r) * ld + c0 + c4);
+        *reinterpret_cast<float4*>(dst + r * pitch + c4) = v;
+    }
+}
+
+template <bool aT, bool bT, int NT>   // aT: A stored transposed, bT: B stored transposed, NT = N / 16
 __global__ void __launch_bounds__(256) bgemm_kernel(Gemm p) {
+    __shared__ __align__(16) float As[64 * kPK > kKS * kPN ? 64 * kPK : kKS * kPN];
+    __shared__ __align__(16) float Bs[128 * kPK > 2 * kKS * kPN ? 128 * kPK : 2 * kKS * kPN];
     const long long z = blockIdx.x;
-    const int w = threadIdx.x >> 6;
     const float* A = p.A + z * p.sA;
     const float* B = p.B + z * p.sB;
     float* C = p.C + z * p.sC;
     const float* D = p.D ? p.D + z * p.sD : nullptr;
-    const int tile0 = blockIdx.y * 4 + w;
-    wg_mm(p.M, p.N, p.K, A, p.ar, p.ac, B, p.br, p.bc, tile0, 4 * gridDim.y, [&](int i, int j, float acc) {
-        float val = p.alpha * acc;
-        if (D) val += p.beta * D[i * p.dr + j];
-        if (p.mask == 1 && j >= i) val = 0.f;
-        if (p.mask == 2 && j > i) val = 0.f;
-        C[i * p.cr + j] = val;
-    });
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 15, g = l >> 4;
+    // A transposed: element (i, k) at k * ac + i; B transposed: element (k, j) at j * bc + k
+    f32x4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < p.K; k0 += kKS) {
+        if constexpr (!aT) stage_slab(As, kPK, A, 64, kKS, p.ar, 0, k0);      // As[i][k]
+        else stage_slab(As, kPN, A, kKS, 64, p.ac, k0, 0);                    // As[k][i]
+        if constexpr (!bT) {                                                   // Bs[k][j], 64-wide blocks of j
+#pragma unroll
+            for (int h = 0; h < 16 * NT; h += 64)
+                stage_slab(Bs + (h / 64) * kKS * kPN, kPN, B, kKS, 16 * NT - h < 64 ? 16 * NT - h : 64, p.br, k0, h);
+        } else {                                                               // Bs[j][k]
+            stage_slab(Bs, kPK, B, 16 * NT, kKS, p.bc, 0, k0);
+        }
+        __syncthreads();
+#pragma unroll 2
+        for (int kk = 0; kk < kKS; kk += 4) {
+            const int i = 16 * w + n, k = kk + g;
+            const float a = aT ? As[k * kPN + i] : As[i * kPK + k];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int j = 16 * t + n;
+                const float b = bT ? Bs[j * kPK + k] : Bs[(t / 4) * kKS * kPN + k * kPN + (j % 64)];
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[t], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * w + 4 * g + r, j = 16 * t + n;
+            float val = p.alpha * acc[t][r];
+            if (D) val += p.beta * D[i * p.dr + j];
+            if (p.mask == 1 && j >= i) val = 0.f;
+            if (p.mask == 2 && j > i) val = 0.f;
+            C[i * p.cr + j] = val;
+        }
+    }
 }
 
 hipError_t gemm(const Gemm& g, int nbatch, hipStream_t st) {
-    const int ntile = (g.M / 16) * (g.N / 16);
-    const int gy = (ntile + 15) / 16;   // 4 tiles per block-step, each block loops
-    hipLaunchKernelGGL(bgemm_kernel, dim3(nbatch, gy), dim3(256), 0, st, g);
+    // shapes used by the backward: M = 64, N and K in {32, 64, 128}
+    auto ok = [](int x) { return x == 32 || x == 64 || x == 128; };
+    if (g.M != 64 || !ok(g.N) || !ok(g.K)) return hipErrorInvalidValue;
+    const bool aT = g.ar == 1, bT = g.bc != 1;
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, dim3(nbatch), dim3(256), 0, st, g); };
+#define CKDA_GEMM_N(AT, BT)                                                  \
+    if (g.N == 32) go(bgemm_kernel<AT, BT, 2>);                              \
+    else if (g.N == 64) go(bgemm_kernel<AT, BT, 4>);                         \
+    else go(bgemm_kernel<AT, BT, 8>);
+    if (aT && bT) { CKDA_GEMM_N(true, true) }
+    else if (aT) { CKDA_GEMM_N(true, false) }
+    else if (bT) { CKDA_GEMM_N(false, true) }
+    else { CKDA_GEMM_N(false, false) }
+#undef CKDA_GEMM_N
     return hipGetLastError();
 }
 
@@ -420,11 +488,24 @@ __global__ void __launch_bounds__(256) bwd_final_kernel(BwdParams p, BwdWs W) {
     const size_t o64k = static_cast<size_t>(ch) * 64 * DK;
     const size_t o64v = static_cast<size_t>(ch) * 64 * DV;
     const int c = threadIdx.x;
-    if (c < DK) {
+    // dGL_c = sum_v dSt[c][v] S[c][v]: row sums read along the rows (coalesced),
+    // one wave per row, reduced across the wave
+    __shared__ float dgl[128];
+    {
         const float* S = p.h_ckpt + static_cast<size_t>(ch) * DK * DV;
         const float* dSt = W.dSt + static_cast<size_t>(ch) * DK * DV;
-        float dGL = 0.f;
-        for (int v = 0; v < DV; ++v) dGL += dSt[c * DV + v] * S[c * DV + v];
+        const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+        for (int r = w; r < DK; r += 4) {
+            float x = 0.f;
+            for (int v = l; v < DV; v += 64) x += dSt[r * DV + v] * S[r * DV + v];
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+            if (l == 0) dgl[r] = x;
+        }
+    }
+    __syncthreads();
+    if (c < DK) {
+        const float dGL = dgl[c];
         const float m = W.Bb[o64k + min(31, ci.L - 1) * DK + c];
         const float bL = W.Bb[o64k + (ci.L - 1) * DK + c];
         float kbsum = 0.f;
