@@ -16,13 +16,15 @@
 // value columns 4*(t % (DV/4)) .. +3 and a band of DK/RG rows, RG = 256/(DV/4)
 // row bands; partial column sums are combined through LDS.  Each state row
 // band is streamed with 16-byte loads/stores, a wave covering whole rows.
+// The per-row parameters (a, kf, a*kf, a*qf) are formed once, by the first
+// DK threads while the state loads are in flight, and shared through LDS.
 #include "ckda_device.h"
 #include "ckda_launch.h"
 
 namespace ckda {
 
 template <typename Tin, int DK, int DV>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 4)
 decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
                    const float* __restrict__ g, const int8_t* __restrict__ s,
                    const float* __restrict__ beta, float scale, float* __restrict__ state,
@@ -31,11 +33,13 @@ decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
     constexpr int CG = DV / 4;          // column groups (4 columns each)
     constexpr int RG = 256 / CG;        // row bands
     constexpr int R = DK / RG;          // rows per thread
+    constexpr int NWK = (DK + 63) / 64; // waves that hold a row
     static_assert(CG * RG == 256 && R * RG == DK && R >= 1, "tile");
 
     __shared__ float4 red_x[RG][CG];
     __shared__ float4 red_y[RG][CG];
-    __shared__ float red_kq[RG];
+    __shared__ __align__(16) float row_a[DK], row_kf[DK], row_ak[DK], row_aq[DK];
+    __shared__ float red_kq[NWK];
 
     const int nh = blockIdx.x;                   // n * H + h
     const int t = threadIdx.x;
@@ -47,40 +51,55 @@ decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
     const size_t vbase = static_cast<size_t>(nh) * DV;
     float4* st = reinterpret_cast<float4*>(state + static_cast<size_t>(nh) * DK * DV);
 
-    float a[R], kf[R];
-    float kq = 0.f;
-    float4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+    // row parameters: every thread loads row min(t, DK - 1) (unconditional, so
+    // these loads are issued ahead of the state stream and retire first)
+    const int tr = t < DK ? t : DK - 1;
+    const int sp0 = sign_prod[kbase + tr], s0 = s[kbase + tr];
+    const float g0 = g[kbase + tr];
+    const float k0 = Elem<Tin>::load(k, kbase + tr), q0 = Elem<Tin>::load(q, kbase + tr);
     float4 S[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) S[i] = st[(r0 + i) * CG + cg];
+    if (t < NWK * 64) {
+        float kq = 0.f;
+        if (t < DK) {
+            const int p = sp0 * s0;
+            sign_prod[kbase + t] = static_cast<int8_t>(p);
+            const float pf = static_cast<float>(p);
+            const float a = __builtin_amdgcn_exp2f(g0 * kLog2e);
+            const float kf = pf * k0;
+            const float qf = pf * q0;
+            row_a[t] = a;
+            row_kf[t] = kf;
+            row_ak[t] = a * kf;
+            row_aq[t] = a * qf;
+            kq = kf * qf;
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) kq += __shfl_xor(kq, off, 64);
+        if ((t & 63) == 0) red_kq[t >> 6] = kq;
+    }
+    __syncthreads();
+    float4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-        const int r = r0 + i;
-        const int p = static_cast<int>(sign_prod[kbase + r]) * static_cast<int>(s[kbase + r]);
-        if (cg == 0) sign_prod[kbase + r] = static_cast<int8_t>(p);
-        const float pf = static_cast<float>(p);
-        a[i] = __builtin_amdgcn_exp2f(g[kbase + r] * kLog2e);
-        kf[i] = pf * Elem<Tin>::load(k, kbase + r);
-        const float qf = pf * Elem<Tin>::load(q, kbase + r);
-        kq += kf[i] * qf;
-        const float ak = a[i] * kf[i];
-        const float aq = a[i] * qf;
+        const float ak = row_ak[r0 + i], aq = row_aq[r0 + i];
         x.x += ak * S[i].x; x.y += ak * S[i].y; x.z += ak * S[i].z; x.w += ak * S[i].w;
         y.x += aq * S[i].x; y.y += aq * S[i].y; y.z += aq * S[i].z; y.w += aq * S[i].w;
     }
     red_x[rg][cg] = x;
     red_y[rg][cg] = y;
-    if (cg == 0) red_kq[rg] = kq;
     __syncthreads();
     float4 X = {0.f, 0.f, 0.f, 0.f}, Y = {0.f, 0.f, 0.f, 0.f};
-    float KQ = 0.f;
 #pragma unroll
     for (int j = 0; j < RG; ++j) {
         const float4 a4 = red_x[j][cg], b4 = red_y[j][cg];
         X.x += a4.x; X.y += a4.y; X.z += a4.z; X.w += a4.w;
         Y.x += b4.x; Y.y += b4.y; Y.z += b4.z; Y.w += b4.w;
-        KQ += red_kq[j];
     }
+    float KQ = 0.f;
+#pragma unroll
+    for (int j = 0; j < NWK; ++j) KQ += red_kq[j];
     const float bt = beta[nh];
     const int c0 = 4 * cg;
     float4 u;
@@ -98,11 +117,12 @@ decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
     }
 #pragma unroll
     for (int i = 0; i < R; ++i) {
+        const float a = row_a[r0 + i], kf = row_kf[r0 + i];
         float4 n;
-        n.x = a[i] * S[i].x + kf[i] * u.x;
-        n.y = a[i] * S[i].y + kf[i] * u.y;
-        n.z = a[i] * S[i].z + kf[i] * u.z;
-        n.w = a[i] * S[i].w + kf[i] * u.w;
+        n.x = a * S[i].x + kf * u.x;
+        n.y = a * S[i].y + kf * u.y;
+        n.z = a * S[i].z + kf * u.z;
+        n.w = a * S[i].w + kf * u.w;
         st[(r0 + i) * CG + cg] = n;
     }
 }
