@@ -43,11 +43,16 @@ struct StateShape {
     static constexpr int NWC = BV / 16;            // waves that own columns
     static constexpr int RT = DK / 16;             // 16-row tiles of S
     static constexpr int ES = RC::ES, NP = RC::NP;
-    // LDS rows carry 16 bytes of padding (row pitch = 4 banks mod 64)
-    static constexpr int PW = (RC::W_ROW + 16) / ES;   // pitches in elements
-    static constexpr int PQ = (RC::Q_ROW + 16) / ES;
-    static constexpr int PKR = (RC::K_ROW + 16) / ES;
-    static constexpr int PMR = (RC::M_ROW + 16) / ES;
+    // Row padding of the staged matrices, chosen from bank-conflict counts on
+    // gfx950: the bf16 fragments are two 8-byte reads 32 bytes apart (merged
+    // into one ds_read2_b64), conflict-free when the row pitch is 2 mod 4
+    // dwords; the fp32 fragments are 16-byte reads, conflict-free at 8 mod 16
+    // dwords.  (Rows of 64 or 32 data dwords plus 6 or 8.)
+    static constexpr int PADB = F32 ? 32 : 24;
+    static constexpr int PW = (RC::W_ROW + PADB) / ES;   // pitches in elements
+    static constexpr int PQ = (RC::Q_ROW + PADB) / ES;
+    static constexpr int PKR = (RC::K_ROW + PADB) / ES;
+    static constexpr int PMR = (RC::M_ROW + PADB) / ES;
     static constexpr int L_W = 0;
     static constexpr int L_Q = L_W + 64 * PW * ES;
     static constexpr int L_K = L_Q + NP * 64 * PQ * ES;
@@ -70,6 +75,15 @@ struct Stage {
     static __device__ __forceinline__ int lds_off(int tid, int i) {
         const int u = tid + NT * i;
         return (u / UPR) * (UPR * 16 + PAD) + (u % UPR) * 16;
+    }
+    // write one unit (rows padded by a multiple of 8 bytes only: two 8-byte writes)
+    static __device__ __forceinline__ void put(unsigned char* p, u32x4 v) {
+        if constexpr (PAD % 16 == 0) {
+            *reinterpret_cast<u32x4*>(p) = v;
+        } else {
+            *reinterpret_cast<u32x2*>(p) = v.xy;
+            *reinterpret_cast<u32x2*>(p + 8) = v.zw;
+        }
     }
 };
 
@@ -142,10 +156,10 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
         //   barrier 1 (W, Qh of j no longer read) -> write A of j+1, issue A loads of j+2
         //   barrier 2 (chunk j done) -> write B of j+1
         // so only the write of group B lies between two chunks.
-        using StW = Stage<64, RC::W_ROW / 16, 16, NT>;
-        using StQ = Stage<NP * 64, RC::Q_ROW / 16, 16, NT>;
-        using StK = Stage<NP * DK, RC::K_ROW / 16, 16, NT>;
-        using StM = Stage<NP * 64, RC::M_ROW / 16, 16, NT>;
+        using StW = Stage<64, RC::W_ROW / 16, SH::PADB, NT>;
+        using StQ = Stage<NP * 64, RC::Q_ROW / 16, SH::PADB, NT>;
+        using StK = Stage<NP * DK, RC::K_ROW / 16, SH::PADB, NT>;
+        using StM = Stage<NP * 64, RC::M_ROW / 16, SH::PADB, NT>;
         using StD = Stage<1, DK * 4 / 16, 0, NT>;
         using StU = Stage<4, NWC * 64, 0, NT>;   // per J: the slice's NWC tiles, 64 lanes each
         constexpr int NW_ = StW::N, NQ_ = StQ::N, NK_ = StK::N, NM_ = StM::N, ND_ = StD::N, NU_ = StU::N;
@@ -180,18 +194,18 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
             unsigned char* const sm_ = smem + opaque_zero();                                                 \
             const int t_ = opaque_tid() - NT;                                                                \
             _Pragma("unroll") for (int i_ = 0; i_ < NW_; ++i_)                                               \
-                *reinterpret_cast<u32x4*>(sm_ + SH::L_W + StW::lds_off(t_, i_)) = ga[i_];                    \
+                StW::put(sm_ + SH::L_W + StW::lds_off(t_, i_), ga[i_]);                                      \
             _Pragma("unroll") for (int i_ = 0; i_ < NQ_; ++i_)                                               \
-                *reinterpret_cast<u32x4*>(sm_ + SH::L_Q + StQ::lds_off(t_, i_)) = ga[O_Q + i_];              \
+                StQ::put(sm_ + SH::L_Q + StQ::lds_off(t_, i_), ga[O_Q + i_]);                                \
         }
 #define CKDA_STORE_B()                                                                                       \
         {                                                                                                    \
             unsigned char* const sm_ = smem + opaque_zero();                                                 \
             const int t_ = opaque_tid() - NT;                                                                \
             _Pragma("unroll") for (int i_ = 0; i_ < NK_; ++i_)                                               \
-                *reinterpret_cast<u32x4*>(sm_ + SH::L_K + StK::lds_off(t_, i_)) = gb[i_];                    \
+                StK::put(sm_ + SH::L_K + StK::lds_off(t_, i_), gb[i_]);                                      \
             _Pragma("unroll") for (int i_ = 0; i_ < NM_; ++i_)                                               \
-                *reinterpret_cast<u32x4*>(sm_ + SH::L_M + StM::lds_off(t_, i_)) = gb[O_M + i_];              \
+                StM::put(sm_ + SH::L_M + StM::lds_off(t_, i_), gb[O_M + i_]);                                \
             _Pragma("unroll") for (int i_ = 0; i_ < ND_; ++i_)                                               \
                 if (StD::has(t_, i_)) *reinterpret_cast<u32x4*>(sm_ + SH::L_D + StD::lds_off(t_, i_)) = gb[O_D + i_]; \
             _Pragma("unroll") for (int i_ = 0; i_ < NU_; ++i_)                                               \
