@@ -27,9 +27,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
     __bf16 h = static_cast<__bf16>(x);
     return __builtin_bit_cast(uint16_t, h);
 }
-// two floats -> packed bf16 pair (lo in bits 0..15)
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+// two floats -> packed bf16 pair, a in bits 0..15 (one v_cvt_pk_bf16_f32)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 template <typename T> struct Elem;

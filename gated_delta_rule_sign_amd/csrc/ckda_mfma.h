@@ -30,31 +30,30 @@ __device__ __forceinline__ void split1(float x, uint16_t& h, uint16_t& l) {
     l = f32_to_bf16(x - bf16_to_f32(h));
 }
 
+// two floats at once (one packed conversion per plane): hi and lo pairs,
+// element a in bits 0..15
+struct SplitPair { uint32_t hi, lo; };
+__device__ __forceinline__ SplitPair split2(float a, float b) {
+    const uint32_t h = cvt_pk_bf16(a, b);
+    const float ha = __uint_as_float(h << 16), hb = __uint_as_float(h & 0xffff0000u);
+    return SplitPair{h, cvt_pk_bf16(a - ha, b - hb)};
+}
+
 __device__ __forceinline__ Split4 split4(f32x4 x) {
+    const SplitPair p0 = split2(x[0], x[1]), p1 = split2(x[2], x[3]);
     Split4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint16_t h, l;
-        split1(x[i], h, l);
-        r.hi[i] = static_cast<short>(h);
-        r.lo[i] = static_cast<short>(l);
-    }
+    r.hi = __builtin_bit_cast(s16x4, u32x2{p0.hi, p1.hi});
+    r.lo = __builtin_bit_cast(s16x4, u32x2{p0.lo, p1.lo});
     return r;
 }
 
 // slots 0..3 from a, 4..7 from b
 __device__ __forceinline__ Split8 split8(f32x4 a, f32x4 b) {
+    const SplitPair p0 = split2(a[0], a[1]), p1 = split2(a[2], a[3]);
+    const SplitPair p2 = split2(b[0], b[1]), p3 = split2(b[2], b[3]);
     Split8 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint16_t h, l;
-        split1(a[i], h, l);
-        r.hi[i] = __builtin_bit_cast(__bf16, h);
-        r.lo[i] = __builtin_bit_cast(__bf16, l);
-        split1(b[i], h, l);
-        r.hi[4 + i] = __builtin_bit_cast(__bf16, h);
-        r.lo[4 + i] = __builtin_bit_cast(__bf16, l);
-    }
+    r.hi = __builtin_bit_cast(bf16x8, u32x4{p0.hi, p1.hi, p2.hi, p3.hi});
+    r.lo = __builtin_bit_cast(bf16x8, u32x4{p0.lo, p1.lo, p2.lo, p3.lo});
     return r;
 }
 

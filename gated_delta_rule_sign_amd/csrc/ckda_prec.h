@@ -45,27 +45,17 @@ struct Prec<false> {
     }
     // 8 consecutive elements (16-byte aligned in each plane)
     static __device__ __forceinline__ void store8(const LdsMat& m, int r, int c, const float (&x)[8]) {
-        uint32_t h[4], l[4];
+        SplitPair sp[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint16_t h0, l0, h1, l1;
-            split1(x[2 * i], h0, l0);
-            split1(x[2 * i + 1], h1, l1);
-            h[i] = h0 | (static_cast<uint32_t>(h1) << 16);
-            l[i] = l0 | (static_cast<uint32_t>(l1) << 16);
-        }
-        *reinterpret_cast<uint4*>(hp(m, r, c)) = make_uint4(h[0], h[1], h[2], h[3]);
-        *reinterpret_cast<uint4*>(lp(m, r, c)) = make_uint4(l[0], l[1], l[2], l[3]);
+        for (int i = 0; i < 4; ++i) sp[i] = split2(x[2 * i], x[2 * i + 1]);
+        *reinterpret_cast<u32x4*>(hp(m, r, c)) = u32x4{sp[0].hi, sp[1].hi, sp[2].hi, sp[3].hi};
+        *reinterpret_cast<u32x4*>(lp(m, r, c)) = u32x4{sp[0].lo, sp[1].lo, sp[2].lo, sp[3].lo};
     }
     // 4 consecutive elements (8-byte aligned)
     static __device__ __forceinline__ void store4(const LdsMat& m, int r, int c, f32x4 x) {
-        uint16_t h[4], l[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) split1(x[i], h[i], l[i]);
-        *reinterpret_cast<uint2*>(hp(m, r, c)) =
-            make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
-        *reinterpret_cast<uint2*>(lp(m, r, c)) =
-            make_uint2(l[0] | (uint32_t(l[1]) << 16), l[2] | (uint32_t(l[3]) << 16));
+        const SplitPair p0 = split2(x[0], x[1]), p1 = split2(x[2], x[3]);
+        *reinterpret_cast<u32x2*>(hp(m, r, c)) = u32x2{p0.hi, p1.hi};
+        *reinterpret_cast<u32x2*>(lp(m, r, c)) = u32x2{p0.lo, p1.lo};
     }
     static __device__ __forceinline__ void store1(const LdsMat& m, int r, int c, float x) {
         uint16_t h, l;
@@ -131,26 +121,18 @@ struct Prec<false> {
     // lo plane `plane` bytes after the hi plane
     static __device__ __forceinline__ void gstore8(unsigned char* base, size_t plane, int row, int r, int c,
                                                    const float (&x)[8]) {
-        uint32_t h[4], l[4];
+        SplitPair sp[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint16_t h0, l0, h1, l1;
-            split1(x[2 * i], h0, l0);
-            split1(x[2 * i + 1], h1, l1);
-            h[i] = h0 | (static_cast<uint32_t>(h1) << 16);
-            l[i] = l0 | (static_cast<uint32_t>(l1) << 16);
-        }
+        for (int i = 0; i < 4; ++i) sp[i] = split2(x[2 * i], x[2 * i + 1]);
         unsigned char* p = base + static_cast<size_t>(r) * row + 2 * c;
-        *reinterpret_cast<uint4*>(p) = make_uint4(h[0], h[1], h[2], h[3]);
-        *reinterpret_cast<uint4*>(p + plane) = make_uint4(l[0], l[1], l[2], l[3]);
+        *reinterpret_cast<u32x4*>(p) = u32x4{sp[0].hi, sp[1].hi, sp[2].hi, sp[3].hi};
+        *reinterpret_cast<u32x4*>(p + plane) = u32x4{sp[0].lo, sp[1].lo, sp[2].lo, sp[3].lo};
     }
     static __device__ __forceinline__ void gstore4(unsigned char* base, size_t plane, int row, int r, int c, f32x4 x) {
-        uint16_t h[4], l[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) split1(x[i], h[i], l[i]);
+        const SplitPair p0 = split2(x[0], x[1]), p1 = split2(x[2], x[3]);
         unsigned char* p = base + static_cast<size_t>(r) * row + 2 * c;
-        *reinterpret_cast<uint2*>(p) = make_uint2(h[0] | (uint32_t(h[1]) << 16), h[2] | (uint32_t(h[3]) << 16));
-        *reinterpret_cast<uint2*>(p + plane) = make_uint2(l[0] | (uint32_t(l[1]) << 16), l[2] | (uint32_t(l[3]) << 16));
+        *reinterpret_cast<u32x2*>(p) = u32x2{p0.hi, p1.hi};
+        *reinterpret_cast<u32x2*>(p + plane) = u32x2{p0.lo, p1.lo};
     }
     // one element of a single-plane matrix, rounded to bf16
     static __device__ __forceinline__ void gstore1s(unsigned char* base, int row, int r, int c, float x) {
