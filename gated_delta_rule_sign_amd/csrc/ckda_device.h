@@ -49,28 +49,23 @@ template <typename Tin>
 struct Raw8;
 template <>
 struct Raw8<bf16_t> {
-    uint4 u;
-    __device__ __forceinline__ void load(const bf16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
-    __device__ __forceinline__ void zero() { u = make_uint4(0u, 0u, 0u, 0u); }
+    u32x4 u;   // a native vector: a HIP_vector_type copy is a memcpy that can pin it in scratch
+    __device__ __forceinline__ void load(const bf16_t* p) { u = *reinterpret_cast<const u32x4*>(p); }
+    __device__ __forceinline__ void zero() { u = u32x4{0u, 0u, 0u, 0u}; }
     __device__ __forceinline__ float get(int e) const {
-        const uint32_t w = (e < 2) ? u.x : (e < 4) ? u.y : (e < 6) ? u.z : u.w;
+        const uint32_t w = u[e >> 1];
         return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
     }
 };
 template <>
 struct Raw8<float> {
-    float4 a, b;
+    f32x4 a, b;
     __device__ __forceinline__ void load(const float* p) {
-        a = reinterpret_cast<const float4*>(p)[0];
-        b = reinterpret_cast<const float4*>(p)[1];
+        a = reinterpret_cast<const f32x4*>(p)[0];
+        b = reinterpret_cast<const f32x4*>(p)[1];
     }
-    __device__ __forceinline__ void zero() { a = make_float4(0.f, 0.f, 0.f, 0.f); b = a; }
-    __device__ __forceinline__ float get(int e) const {
-        switch (e) {
-            case 0: return a.x; case 1: return a.y; case 2: return a.z; case 3: return a.w;
-            case 4: return b.x; case 5: return b.y; case 6: return b.z; default: return b.w;
-        }
-    }
+    __device__ __forceinline__ void zero() { a = f32x4{0.f, 0.f, 0.f, 0.f}; b = a; }
+    __device__ __forceinline__ float get(int e) const { return e < 4 ? a[e] : b[e - 4]; }
 };
 
 // A raw buffer resource over `bytes` bytes at `base`: buffer stores beyond
