@@ -29,7 +29,7 @@
 // Implementation: every product is a batched fp32 matrix-core GEMM
 // (v_mfma_f32_16x16x4_f32) over all chunk-heads at once, with intermediates
 // in the caller's workspace; the reverse recurrence runs one workgroup per
-// (sequence, head, 32-column slice) over the chunks.
+// (sequence, head, 64-column slice) over the chunks, its operands staged in LDS.
 #include "ckda_device.h"
 #include "ckda_launch.h"
 #include "ckda_mfma.h"
@@ -37,41 +37,6 @@
 namespace ckda {
 
 namespace {
-
-constexpr int kBV = 32;   // value columns per reverse-pass workgroup
-
-// Workgroup (4 waves) matrix product on fp32 operands with arbitrary strides
-// (global or LDS): for each 16x16 output tile owned by this wave,
-//   acc(i, j) = sum_k A[i*ar + k*ac] * B[k*br + j*bc]
-// and epi(i, j, acc) is called for every element.  M, N multiples of 16,
-// K multiple of 16.
-template <typename Epi>
-__device__ __forceinline__ void wg_mm(int M, int N, int K, const float* A, int ar, int ac,
-                                      const float* B, int br, int bc, int tile0, int tstride,
-                                      Epi epi) {
-    const int l = threadIdx.x & 63;
-    const int n = l & 15, g = l >> 4;
-    const int tn = N / 16;
-    const int ntile = (M / 16) * tn;
-    for (int tile = tile0; tile < ntile; tile += tstride) {
-        const int ti = tile / tn, tj = tile % tn;
-        const float* a = A + (16 * ti + n) * ar + g * ac;
-        const float* b = B + g * br + (16 * tj + n) * bc;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < K; k0 += 16) {
-            float av[4], bv[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                av[u] = a[(k0 + 4 * u) * ac];
-                bv[u] = b[(k0 + 4 * u) * br];
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], bv[u], acc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) epi(16 * ti + 4 * g + i, 16 * tj + n, acc[i]);
-    }
-}
 
 // Workspace layout (floats), per chunk-head ch (NC = B*H*NT of them).
 struct BwdWs {
@@ -381,67 +346,282 @@ __global__ void __launch_bounds__(256) bwd_inverse_kernel(BwdWs W) {
 }
 
 // ---------------------------------------------------------------------------
-// Reverse recurrence over chunks, one workgroup per (b, h, 32-column slice).
+// Reverse recurrence over chunks, one 512-thread workgroup per (sequence,
+// head, BV-column slice), BV = min(DV, 64).  Per chunk j (last to first), with
+// G = dL/dS at the chunk end and dSt = Diag(pC) G:
+//   dU = M^T dO + KB dSt,   Z = T^T dU,
+//   G <- Diag(e^m) (Q1^T dO - K1^T Z) + Diag(e^{b_L}) dSt.
+// Every operand is staged in LDS (fp32, rows padded so the fragment reads of
+// v_mfma_f32_16x16x4_f32 are free of bank conflicts); G lives in LDS and is
+// updated in place.  The chunk's Q1, K1 are read into registers while dU and
+// Z are formed, and the next chunk's M, T, KB, dO while G is formed, so HBM
+// latency hides behind the products.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) bwd_reverse_kernel(BwdParams p, BwdWs W) {
-    __shared__ float G[128 * kBV];     // [DK][kBV]
-    __shared__ float dSt[128 * kBV];
-    __shared__ float dU[64 * kBV];
-    __shared__ float Z[64 * kBV];
-    const int DK = W.DK, DV = W.DV;
-    const int nsl = DV / kBV;
-    const int bh = blockIdx.x / nsl;
-    const int v0 = (blockIdx.x % nsl) * kBV;
-    const int w = threadIdx.x >> 6;
+template <int DK, int DV>
+struct RevShape {
+    static constexpr int BV = DV < 64 ? DV : 64;
+    static constexpr int NSL = DV / BV;
+    static constexpr int CT = BV / 16;               // column tiles
+    // pitches (floats): rows read as "k = lane group" need 16 mod 64, rows
+    // read as "row = lane % 16" need 4 mod 64
+    static constexpr int P64 = 64 + 16;              // M, T (64 x 64, read transposed)
+    static constexpr int PKB = DK + 4;               // KB (64 x DK, row = token)
+    static constexpr int PQK = DK + 16;              // Q1, K1 (64 x DK, read transposed)
+    static constexpr int PV = BV + 16;               // dO, G, dU, Z (row = k)
+    static constexpr int S1 = 2 * 64 * P64 + 64 * PKB;   // stage 1 of the shared region: M, T, KB
+    static constexpr int S2 = 2 * 64 * PQK;              // stage 2: Q1, K1
+    static constexpr int L_X = 0;
+    static constexpr int L_DO = L_X + (S1 > S2 ? S1 : S2);
+    static constexpr int L_G = L_DO + 64 * PV;
+    static constexpr int L_UZ = L_G + DK * PV;
+    static constexpr int L_SM = L_UZ + 64 * PV;      // pC, em, gC
+    static constexpr int FLOATS = L_SM + 3 * DK;
+    static constexpr int BYTES = FLOATS * 4;
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+    // 16-byte units each thread moves per chunk
+    static constexpr int NM = 64 * 64 / 4 / 512;     // M and T: 2 each
+    static constexpr int NKB = 64 * DK / 4 / 512;    // KB, Q1, K1
+    static constexpr int NDO = 64 * BV / 4 / 512;    // dO slice
+    static_assert(NKB >= 1 && NDO >= 1, "units");
+};
+
+template <int DK, int DV>
+__global__ void __launch_bounds__(512) bwd_reverse_kernel(BwdParams p, BwdWs W) {
+    using SH = RevShape<DK, DV>;
+    constexpr int BV = SH::BV, CT = SH::CT, NM = SH::NM, NKB = SH::NKB, NDO = SH::NDO;
+    constexpr int P64 = SH::P64, PKB = SH::PKB, PQK = SH::PQK, PV = SH::PV;
+    extern __shared__ __align__(16) float lds[];
+    float* const Xs = lds + SH::L_X;
+    float* const Ms = Xs;                      // stage 1
+    float* const Ts = Xs + 64 * P64;
+    float* const KBs = Xs + 2 * 64 * P64;
+    float* const Q1s = Xs;                     // stage 2
+    float* const K1s = Xs + 64 * PQK;
+    float* const dOs = lds + SH::L_DO;
+    float* const Gs = lds + SH::L_G;
+    float* const UZs = lds + SH::L_UZ;
+    float* const pCs = lds + SH::L_SM;
+    float* const ems = pCs + DK;
+    float* const gCs = ems + DK;
+
+    const int bh = blockIdx.x / SH::NSL;
+    const int v0 = (blockIdx.x % SH::NSL) * BV;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63, n = l & 15, g = l >> 4;
+    const int NT = p.NT;
+
+    // ---- register staging ---------------------------------------------------
+    f32x4 rM[NM], rT[NM], rKB[NKB], rDO[NDO], rSM;
+    f32x4 rQ[NKB], rK[NKB];
+    auto load1 = [&](int j) {   // M, T, KB, dO slice, pC / em / gC of chunk j
+        const size_t ch = static_cast<size_t>(bh) * NT + j;
+        const f32x4* M4 = reinterpret_cast<const f32x4*>(W.M + ch * 4096);
+        const f32x4* T4 = reinterpret_cast<const f32x4*>(W.T + ch * 4096);
+        const f32x4* KB4 = reinterpret_cast<const f32x4*>(W.KB + ch * 64 * DK);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) { rM[i] = M4[tid + 512 * i]; rT[i] = T4[tid + 512 * i]; }
+#pragma unroll
+        for (int i = 0; i < NKB; ++i) rKB[i] = KB4[tid + 512 * i];
+#pragma unroll
+        for (int i = 0; i < NDO; ++i) {
+            const int u = tid + 512 * i, r = u / (BV / 4), c4 = u % (BV / 4);
+            rDO[i] = *reinterpret_cast<const f32x4*>(W.dO + ch * 64 * DV + static_cast<size_t>(r) * DV + v0 + 4 * c4);
+        }
+        // pC, em, gC: DK / 4 units each (clamped, so the load is unconditional)
+        const int us = min(tid, 3 * (DK / 4) - 1), arr = us / (DK / 4), c4 = us % (DK / 4);
+        const float* src = arr == 0 ? W.pC : arr == 1 ? W.em : W.gC;
+        rSM = *reinterpret_cast<const f32x4*>(src + ch * DK + 4 * c4);
+    };
+    auto store1 = [&]() {
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+            const int u = tid + 512 * i, r = u / 16, c4 = u % 16;
+            *reinterpret_cast<f32x4*>(Ms + r * P64 + 4 * c4) = rM[i];
+            *reinterpret_cast<f32x4*>(Ts + r * P64 + 4 * c4) = rT[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NKB; ++i) {
+            const int u = tid + 512 * i, r = u / (DK / 4), c4 = u % (DK / 4);
+            *reinterpret_cast<f32x4*>(KBs + r * PKB + 4 * c4) = rKB[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NDO; ++i) {
+            const int u = tid + 512 * i, r = u / (BV / 4), c4 = u % (BV / 4);
+            *reinterpret_cast<f32x4*>(dOs + r * PV + 4 * c4) = rDO[i];
+        }
+        if (tid < 3 * (DK / 4)) *reinterpret_cast<f32x4*>(pCs + 4 * tid) = rSM;
+    };
+    auto load2 = [&](int j) {   // Q1, K1 of chunk j
+        const size_t ch = static_cast<size_t>(bh) * NT + j;
+        const f32x4* Q4 = reinterpret_cast<const f32x4*>(W.Q1 + ch * 64 * DK);
+        const f32x4* K4 = reinterpret_cast<const f32x4*>(W.K1 + ch * 64 * DK);
+#pragma unroll
+        for (int i = 0; i < NKB; ++i) { rQ[i] = Q4[tid + 512 * i]; rK[i] = K4[tid + 512 * i]; }
+    };
+    auto store2 = [&]() {
+#pragma unroll
+        for (int i = 0; i < NKB; ++i) {
+            const int u = tid + 512 * i, r = u / (DK / 4), c4 = u % (DK / 4);
+            *reinterpret_cast<f32x4*>(Q1s + r * PQK + 4 * c4) = rQ[i];
+            *reinterpret_cast<f32x4*>(K1s + r * PQK + 4 * c4) = rK[i];
+        }
+    };
+
+    // ---- tiles: wave w owns TPW consecutive 16x16 tiles of a product ------
+    constexpr int TU = 4 * CT, TPU = TU >= 8 ? TU / 8 : 1;             // 64 x BV products
+    constexpr int TG = (DK / 16) * CT, TPG = TG >= 8 ? TG / 8 : 1;     // DK x BV product
+    const bool actU = w * TPU < TU, actG = w * TPG < TG;
+
     // G = dht (or 0)
-    for (int e = threadIdx.x; e < DK * kBV; e += 256) {
-        const int c = e / kBV, v = e % kBV;
-        G[e] = p.dht ? p.dht[(static_cast<size_t>(bh) * DK + c) * DV + v0 + v] : 0.f;
+    for (int e = tid; e < DK * BV; e += 512) {
+        const int c = e / BV, v = e % BV;
+        Gs[c * PV + v] = p.dht ? p.dht[(static_cast<size_t>(bh) * DK + c) * DV + v0 + v] : 0.f;
     }
+    load1(NT - 1);
+    store1();
     __syncthreads();
-    for (int j = p.NT - 1; j >= 0; --j) {
-        const size_t ch = static_cast<size_t>(bh) * p.NT + j;
-        const float* pC = W.pC + ch * DK;
-        const float* em = W.em + ch * DK;
-        const float* gC = W.gC + ch * DK;
-        float* dSt_g = W.dSt + ch * DK * DV;
-        for (int e = threadIdx.x; e < DK * kBV; e += 256) {
-            const int c = e / kBV, v = e % kBV;
-            const float x = pC[c] * G[e];
-            dSt[e] = x;
-            dSt_g[c * DV + v0 + v] = x;
+    for (int j = NT - 1; j >= 0; --j) {
+        const size_t ch = static_cast<size_t>(bh) * NT + j;
+        load2(j);
+        // dSt = Diag(pC) G to the workspace (slice columns)
+        for (int e = tid; e < DK * (BV / 4); e += 512) {
+            const int c = e / (BV / 4), c4 = e % (BV / 4);
+            const f32x4 gv = *reinterpret_cast<const f32x4*>(Gs + c * PV + 4 * c4);
+            *reinterpret_cast<f32x4*>(W.dSt + ch * DK * DV + static_cast<size_t>(c) * DV + v0 + 4 * c4) = pCs[c] * gv;
+        }
+        // dU = M^T dO + KB dSt
+        if (actU) {
+            f32x4 acc[TPU];
+            int ti[TPU], tj[TPU];
+#pragma unroll
+            for (int u = 0; u < TPU; ++u) {
+                const int tt = w * TPU + u;
+                ti[u] = tt / CT; tj[u] = tt % CT;
+                acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll 4
+            for (int k0 = 0; k0 < 64; k0 += 4) {
+#pragma unroll
+                for (int u = 0; u < TPU; ++u) {
+                    const float a = Ms[(k0 + g) * P64 + 16 * ti[u] + n];
+                    const float b = dOs[(k0 + g) * PV + 16 * tj[u] + n];
+                    acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[u], 0, 0, 0);
+                }
+            }
+#pragma unroll 4
+            for (int k0 = 0; k0 < DK; k0 += 4) {
+                const float pc = pCs[k0 + g];
+#pragma unroll
+                for (int u = 0; u < TPU; ++u) {
+                    const float a = KBs[(16 * ti[u] + n) * PKB + k0 + g];
+                    const float b = pc * Gs[(k0 + g) * PV + 16 * tj[u] + n];
+                    acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[u], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < TPU; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) UZs[(16 * ti[u] + 4 * g + i) * PV + 16 * tj[u] + n] = acc[u][i];
         }
         __syncthreads();
-        // dU = M^T dO + KB dSt     [64 x kBV]
-        const float* M = W.M + ch * 4096;
-        const float* dO = W.dO + ch * 64 * DV + v0;
-        const float* KB = W.KB + ch * 64 * DK;
-        wg_mm(64, kBV, 64, M, 1, 64, dO, DV, 1, w, 4, [&](int i, int jj, float acc) { dU[i * kBV + jj] = acc; });
-        wg_mm(64, kBV, DK, KB, DK, 1, dSt, kBV, 1, w, 4, [&](int i, int jj, float acc) { dU[i * kBV + jj] += acc; });
-        __syncthreads();
-        {
-            float* dU_g = W.dU + ch * 64 * DV + v0;
-            for (int e = threadIdx.x; e < 64 * kBV; e += 256) dU_g[(e / kBV) * DV + e % kBV] = dU[e];
+        // dU to the workspace; Z = T^T dU (held in registers until dU is no longer read)
+        for (int e = tid; e < 64 * (BV / 4); e += 512) {
+            const int r = e / (BV / 4), c4 = e % (BV / 4);
+            *reinterpret_cast<f32x4*>(W.dU + ch * 64 * DV + static_cast<size_t>(r) * DV + v0 + 4 * c4) =
+                *reinterpret_cast<const f32x4*>(UZs + r * PV + 4 * c4);
         }
-        // Z = T^T dU
-        const float* T = W.T + ch * 4096;
-        wg_mm(64, kBV, 64, T, 1, 64, dU, kBV, 1, w, 4, [&](int i, int jj, float acc) { Z[i * kBV + jj] = acc; });
+        f32x4 zacc[TPU];
+        int zti[TPU], ztj[TPU];
+        if (actU) {
+#pragma unroll
+            for (int u = 0; u < TPU; ++u) {
+                const int tt = w * TPU + u;
+                zti[u] = tt / CT; ztj[u] = tt % CT;
+                zacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll 4
+            for (int k0 = 0; k0 < 64; k0 += 4) {
+#pragma unroll
+                for (int u = 0; u < TPU; ++u) {
+                    const float a = Ts[(k0 + g) * P64 + 16 * zti[u] + n];
+                    const float b = UZs[(k0 + g) * PV + 16 * ztj[u] + n];
+                    zacc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, zacc[u], 0, 0, 0);
+                }
+            }
+        }
         __syncthreads();
-        // G = Diag(e^m) (Q1^T dO - K1^T Z) + Diag(e^{b_L}) dSt
-        const float* Q1 = W.Q1 + ch * 64 * DK;
-        const float* K1 = W.K1 + ch * 64 * DK;
-        wg_mm(DK, kBV, 64, Q1, 1, DK, dO, DV, 1, w, 4, [&](int i, int jj, float acc) { G[i * kBV + jj] = acc; });
-        wg_mm(DK, kBV, 64, K1, 1, DK, Z, kBV, 1, w, 4, [&](int i, int jj, float acc) {
-            G[i * kBV + jj] = em[i] * (G[i * kBV + jj] - acc) + gC[i] * dSt[i * kBV + jj];
-        });
+        // Z and this chunk's Q1, K1 to LDS; the next chunk's stage-1 loads go out
+        if (actU) {
+#pragma unroll
+            for (int u = 0; u < TPU; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) UZs[(16 * zti[u] + 4 * g + i) * PV + 16 * ztj[u] + n] = zacc[u][i];
+        }
+        store2();
+        load1(j > 0 ? j - 1 : 0);
+        __syncthreads();
+        // G <- Diag(e^m) (Q1^T dO - K1^T Z) + Diag(e^{b_L} pC) G   (each wave its own tiles, in place)
+        if (actG) {
+            f32x4 acc[TPG];
+            int ti[TPG], tj[TPG];
+#pragma unroll
+            for (int u = 0; u < TPG; ++u) {
+                const int tt = w * TPG + u;
+                ti[u] = tt / CT; tj[u] = tt % CT;
+                acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll 4
+            for (int k0 = 0; k0 < 64; k0 += 4) {
+#pragma unroll
+                for (int u = 0; u < TPG; ++u) {
+                    const float aq = Q1s[(k0 + g) * PQK + 16 * ti[u] + n];
+                    const float ak = -K1s[(k0 + g) * PQK + 16 * ti[u] + n];
+                    const float bo = dOs[(k0 + g) * PV + 16 * tj[u] + n];
+                    const float bz = UZs[(k0 + g) * PV + 16 * tj[u] + n];
+                    acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(aq, bo, acc[u], 0, 0, 0);
+                    acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak, bz, acc[u], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < TPG; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * ti[u] + 4 * g + i, c = 16 * tj[u] + n;
+                    Gs[r * PV + c] = ems[r] * acc[u][i] + gCs[r] * pCs[r] * Gs[r * PV + c];
+                }
+        }
+        __syncthreads();
+        store1();   // chunk j - 1 (on the last chunk: chunk 0 again, unused)
         __syncthreads();
     }
     if (p.dh0) {
-        for (int e = threadIdx.x; e < DK * kBV; e += 256) {
-            const int c = e / kBV, v = e % kBV;
-            p.dh0[(static_cast<size_t>(bh) * DK + c) * DV + v0 + v] = G[e];
+        for (int e = tid; e < DK * BV; e += 512) {
+            const int c = e / BV, v = e % BV;
+            p.dh0[(static_cast<size_t>(bh) * DK + c) * DV + v0 + v] = Gs[c * PV + v];
         }
     }
+}
+
+template <int DK, int DV>
+static hipError_t launch_reverse_t(const BwdParams& p, const BwdWs& W, hipStream_t st) {
+    using SH = RevShape<DK, DV>;
+    auto kern = bwd_reverse_kernel<DK, DV>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, SH::BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(p.B * p.H * SH::NSL), dim3(512), SH::BYTES, st, p, W);
+    return hipGetLastError();
+}
+
+static hipError_t launch_reverse(const BwdParams& p, const BwdWs& W, hipStream_t st) {
+#define CKDA_REV(DK_, DV_) \
+    if (W.DK == DK_ && W.DV == DV_) return launch_reverse_t<DK_, DV_>(p, W, st);
+    CKDA_REV(32, 32) CKDA_REV(32, 64) CKDA_REV(32, 128)
+    CKDA_REV(64, 32) CKDA_REV(64, 64) CKDA_REV(64, 128)
+    CKDA_REV(128, 32) CKDA_REV(128, 64) CKDA_REV(128, 128)
+#undef CKDA_REV
+    return hipErrorInvalidValue;
 }
 
 // dbeta1_i = sum_r dT_ri Xi_ri ; Y1 = dT Diag(beta)
@@ -589,8 +769,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
     CKDA_CHECK(gemm(mk(64, DV, DK, W.K1, DK, s64k, false, W.Sp, DV, skv, false, W.R, DV, s64v, -1.f, W.V, 1.f), NC, st));
     CKDA_CHECK(gemm(mk(64, DV, 64, W.T, 64, s44, false, W.R, DV, s64v, false, W.U, DV, s64v), NC, st));
     // reverse recurrence: dSt, dU per chunk, dh0
-    hipLaunchKernelGGL(bwd_reverse_kernel, dim3(a.B * a.H * (DV / kBV)), dim3(256), 0, st, p, W);
-    CKDA_CHECK(hipGetLastError());
+    CKDA_CHECK(launch_reverse(p, W, st));
     // chunk-parallel gradients
     CKDA_CHECK(gemm(mk(64, 64, DV, W.dO, DV, s64v, false, W.U, DV, s64v, true, W.dM, 64, s44, 1.f, nullptr, 0.f, 2), NC, st));
     CKDA_CHECK(gemm(mk(64, DK, DV, W.U, DV, s64v, false, W.dSt, DV, skv, true, W.dKB, DK, s64k), NC, st));
