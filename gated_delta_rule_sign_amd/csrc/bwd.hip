@@ -43,7 +43,7 @@ struct BwdWs {
     int NC, DK, DV;
     float* base;
     // [NC][64][DK]
-    float *K1, *K2, *Q1, *KB, *Bb, *Pp, *dKB, *dW, *dK1, *dK2, *dQ1;
+    float *K1, *K2, *Q1, *KB, *dKB, *dW, *dK1, *dK2, *dQ1;
     // [NC][64][DV]
     float *V, *dO, *R, *U, *dU, *dV;
     // [NC][DK][DV]
@@ -56,14 +56,14 @@ struct BwdWs {
     float *beta, *dbeta1, *dbeta2;
 
     __host__ __device__ static size_t floats(size_t NC, int DK, int DV) {
-        return NC * (11ull * 64 * DK + 6ull * 64 * DV + 2ull * DK * DV + 10ull * 64 * 64 + 3ull * DK + 3ull * 64);
+        return NC * (9ull * 64 * DK + 6ull * 64 * DV + 2ull * DK * DV + 10ull * 64 * 64 + 3ull * DK + 3ull * 64);
     }
     __host__ void carve(float* p, int nc, int dk, int dv) {
         NC = nc; DK = dk; DV = dv; base = p;
         const size_t n = nc;
         auto take = [&](size_t cnt) { float* r = p; p += cnt; return r; };
         K1 = take(n * 64 * dk); K2 = take(n * 64 * dk); Q1 = take(n * 64 * dk); KB = take(n * 64 * dk);
-        Bb = take(n * 64 * dk); Pp = take(n * 64 * dk); dKB = take(n * 64 * dk); dW = take(n * 64 * dk);
+        dKB = take(n * 64 * dk); dW = take(n * 64 * dk);
         dK1 = take(n * 64 * dk); dK2 = take(n * 64 * dk); dQ1 = take(n * 64 * dk);
         V = take(n * 64 * dv); dO = take(n * 64 * dv); R = take(n * 64 * dv); U = take(n * 64 * dv);
         dU = take(n * 64 * dv); dV = take(n * 64 * dv);
@@ -221,72 +221,140 @@ struct ChunkIdx {
 };
 
 // ---------------------------------------------------------------------------
-// prep: chunk-local cumulative gate, sign product and anchored operands
+// Chunk-local scans shared by the prep and final passes.  Thread layout: 4
+// consecutive channels (a "quad") by a segment of NTOK consecutive tokens;
+// a wave covers whole 512-byte token rows.  Every load is issued up front
+// (rows past the chunk end read the last token and are masked at use), the
+// per-segment inclusive scans meet through LDS, and
+//   b = cumulative g (natural log),  P = cumulative sign product,
+//   m = b at token 31 (the anchor),  bL = b at the last token,
+// padding tokens carrying g = 0 and s = +1 (so m = b[min(31, L-1)]).
 // ---------------------------------------------------------------------------
-template <typename Tin>
-__global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p, BwdWs W) {
+template <int DK, int NTHR>
+struct QuadSeg {
+    static constexpr int CQ = DK / 4;          // channel quads
+    static constexpr int SEGS = NTHR / CQ;     // token segments
+    static constexpr int NTOK = 64 / SEGS;     // tokens per thread
+    static_assert(SEGS * NTOK == 64 && SEGS % 2 == 0, "segments");
+};
+
+template <typename T> __device__ __forceinline__ f32x4 load_quad(const T* p, size_t e);
+template <> __device__ __forceinline__ f32x4 load_quad<float>(const float* p, size_t e) {
+    return *reinterpret_cast<const f32x4*>(p + e);
+}
+template <> __device__ __forceinline__ f32x4 load_quad<bf16_t>(const bf16_t* p, size_t e) {
+    const u32x2 u = *reinterpret_cast<const u32x2*>(p + e);
+    return f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u),
+                 __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xffff0000u)};
+}
+__device__ __forceinline__ f32x4 signs_quad(const int8_t* p, size_t e) {
+    const uint32_t u = *reinterpret_cast<const uint32_t*>(p + e);
+    return f32x4{static_cast<float>(static_cast<int8_t>(u)), static_cast<float>(static_cast<int8_t>(u >> 8)),
+                 static_cast<float>(static_cast<int8_t>(u >> 16)), static_cast<float>(static_cast<int8_t>(u >> 24))};
+}
+__device__ __forceinline__ f32x4 exp2c4(f32x4 x) {
+    return f32x4{exp2_clamped(x[0]), exp2_clamped(x[1]), exp2_clamped(x[2]), exp2_clamped(x[3])};
+}
+
+// prep: cumulative gate and sign product, anchored operands, V / dO copies
+// and S' = Diag(e^m) S
+template <typename Tin, int DK, int DV>
+__global__ void __launch_bounds__(512) bwd_prep_kernel(BwdParams p, BwdWs W) {
+    using QS = QuadSeg<DK, 512>;
+    using QV = QuadSeg<DV, 512>;
+    constexpr int CQ = QS::CQ, SEGS = QS::SEGS, NTOK = QS::NTOK;
+    constexpr int S4 = DK * DV / 4;                 // float4 of the chunk-start state
+    constexpr int NS4 = (S4 + 511) / 512;           // per thread
+    __shared__ f32x4 segb[SEGS][CQ], segp[SEGS][CQ];
+    __shared__ __align__(16) float em_s[DK];
     const int ch = blockIdx.x;
-    const int DK = W.DK, DV = W.DV;
     const ChunkIdx ci(ch, p.H, p.NT, p.T);
-    const int c = threadIdx.x;
+    const int tid = threadIdx.x, q4 = tid % CQ, seg = tid / CQ, tb = seg * NTOK;
     const size_t trow0 = static_cast<size_t>(ci.b) * p.T + ci.t0;   // token row of the chunk start
     const size_t o64k = static_cast<size_t>(ch) * 64 * DK;
     const size_t o64v = static_cast<size_t>(ch) * 64 * DV;
-    if (c < DK) {
-        float run = 0.f, par = 1.f;
-        for (int t = 0; t < 64; ++t) {
-            if (t < ci.L) {
-                const size_t e = ((trow0 + t) * p.H + ci.h) * DK + c;
-                run += p.g[e];
-                par *= static_cast<float>(p.s[e]);
-            }
-            W.Bb[o64k + t * DK + c] = run;
-            W.Pp[o64k + t * DK + c] = par;
-        }
-        const float m = W.Bb[o64k + min(31, ci.L - 1) * DK + c];
-        const float bL = run;
-        for (int t = 0; t < 64; ++t) {
-            float K1 = 0.f, K2 = 0.f, Q1 = 0.f, KB = 0.f;
-            if (t < ci.L) {
-                const size_t e = ((trow0 + t) * p.H + ci.h) * DK + c;
-                const float b = W.Bb[o64k + t * DK + c];
-                const float P = W.Pp[o64k + t * DK + c];
-                const float kf = P * Elem<Tin>::load(static_cast<const Tin*>(p.k), e);
-                const float qf = P * Elem<Tin>::load(static_cast<const Tin*>(p.q), e);
-                const float e1 = exp2_clamped((b - m) * kLog2e);
-                K1 = kf * e1;
-                K2 = kf * exp2_clamped((m - b) * kLog2e);
-                Q1 = qf * e1;
-                KB = kf * exp2_clamped((bL - b) * kLog2e);
-            }
-            W.K1[o64k + t * DK + c] = K1;
-            W.K2[o64k + t * DK + c] = K2;
-            W.Q1[o64k + t * DK + c] = Q1;
-            W.KB[o64k + t * DK + c] = KB;
-        }
-        W.em[static_cast<size_t>(ch) * DK + c] = exp2_clamped(m * kLog2e);
-        W.gC[static_cast<size_t>(ch) * DK + c] = exp2_clamped(bL * kLog2e);
-        W.pC[static_cast<size_t>(ch) * DK + c] = par;
+    const Tin* qp = static_cast<const Tin*>(p.q);
+    const Tin* kp = static_cast<const Tin*>(p.k);
+    f32x4 gv[NTOK], sg[NTOK], kv[NTOK], qv[NTOK];
+#pragma unroll
+    for (int i = 0; i < NTOK; ++i) {
+        const size_t e = ((trow0 + min(tb + i, ci.L - 1)) * p.H + ci.h) * DK + 4 * q4;
+        gv[i] = *reinterpret_cast<const f32x4*>(p.g + e);
+        sg[i] = signs_quad(p.s, e);
+        kv[i] = load_quad(kp, e);
+        qv[i] = load_quad(qp, e);
     }
-    if (c < DV) {
-        for (int t = 0; t < 64; ++t) {
-            float vv = 0.f, dd = 0.f;
-            if (t < ci.L) {
-                const size_t e = ((trow0 + t) * p.H + ci.h) * DV + c;
-                vv = Elem<Tin>::load(static_cast<const Tin*>(p.v), e);
-                dd = p.scale * Elem<Tin>::load(static_cast<const Tin*>(p.dout), e);
-            }
-            W.V[o64v + t * DV + c] = vv;
-            W.dO[o64v + t * DV + c] = dd;
-        }
+    const int qv4 = tid % QV::CQ, segv = tid / QV::CQ;
+    f32x4 vv[QV::NTOK], dd[QV::NTOK];
+#pragma unroll
+    for (int i = 0; i < QV::NTOK; ++i) {
+        const size_t e = ((trow0 + min(segv * QV::NTOK + i, ci.L - 1)) * p.H + ci.h) * DV + 4 * qv4;
+        vv[i] = load_quad(static_cast<const Tin*>(p.v), e);
+        dd[i] = load_quad(static_cast<const Tin*>(p.dout), e);
     }
-    if (c < 64) W.beta[static_cast<size_t>(ch) * 64 + c] = (c < ci.L) ? p.beta[(trow0 + c) * p.H + ci.h] : 0.f;
+    f32x4 run = {0.f, 0.f, 0.f, 0.f}, par = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+    for (int i = 0; i < NTOK; ++i) {
+        const bool valid = tb + i < ci.L;
+        run += valid ? gv[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+        par *= valid ? sg[i] : f32x4{1.f, 1.f, 1.f, 1.f};
+        gv[i] = run;
+        sg[i] = par;
+        if (!valid) kv[i] = qv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    segb[seg][q4] = run;
+    segp[seg][q4] = par;
+    __syncthreads();
+    f32x4 off = {0.f, 0.f, 0.f, 0.f}, poff = {1.f, 1.f, 1.f, 1.f}, m = off, bL = off, ptot = poff;
+#pragma unroll 2
+    for (int s2 = 0; s2 < SEGS; ++s2) {
+        const f32x4 x = segb[s2][q4], y = segp[s2][q4];
+        if (s2 < seg) { off += x; poff *= y; }
+        if (s2 < SEGS / 2) m += x;
+        bL += x;
+        ptot *= y;
+    }
+    // the chunk-start state, read before this thread's stores go out
+    const f32x4* Sg = reinterpret_cast<const f32x4*>(p.h_ckpt + static_cast<size_t>(ch) * DK * DV);
+    f32x4 hs[NS4];
+#pragma unroll
+    for (int i = 0; i < NS4; ++i) hs[i] = Sg[min(tid + 512 * i, S4 - 1)];
+#pragma unroll
+    for (int i = 0; i < NTOK; ++i) {
+        const int t = tb + i;
+        const f32x4 b = gv[i] + off, P = sg[i] * poff;
+        const f32x4 kf = P * kv[i], qf = P * qv[i];
+        const f32x4 e1 = exp2c4((b - m) * kLog2e);
+        const size_t o = o64k + static_cast<size_t>(t) * DK + 4 * q4;
+        *reinterpret_cast<f32x4*>(W.K1 + o) = kf * e1;
+        *reinterpret_cast<f32x4*>(W.K2 + o) = kf * exp2c4((m - b) * kLog2e);
+        *reinterpret_cast<f32x4*>(W.Q1 + o) = qf * e1;
+        *reinterpret_cast<f32x4*>(W.KB + o) = kf * exp2c4((bL - b) * kLog2e);
+    }
+    if (seg == 0) {
+        const f32x4 em = exp2c4(m * kLog2e);
+        *reinterpret_cast<f32x4*>(W.em + static_cast<size_t>(ch) * DK + 4 * q4) = em;
+        *reinterpret_cast<f32x4*>(W.gC + static_cast<size_t>(ch) * DK + 4 * q4) = exp2c4(bL * kLog2e);
+        *reinterpret_cast<f32x4*>(W.pC + static_cast<size_t>(ch) * DK + 4 * q4) = ptot;
+        *reinterpret_cast<f32x4*>(em_s + 4 * q4) = em;
+    }
+#pragma unroll
+    for (int i = 0; i < QV::NTOK; ++i) {
+        const int t = segv * QV::NTOK + i;
+        const bool valid = t < ci.L;
+        const size_t o = o64v + static_cast<size_t>(t) * DV + 4 * qv4;
+        *reinterpret_cast<f32x4*>(W.V + o) = valid ? vv[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4*>(W.dO + o) = valid ? p.scale * dd[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (tid < 64) W.beta[static_cast<size_t>(ch) * 64 + tid] = (tid < ci.L) ? p.beta[(trow0 + tid) * p.H + ci.h] : 0.f;
     // S' = Diag(e^m) S for the chunk-start state (h_ckpt is [B,H,NT,DK,DV] = [NC][DK][DV])
     __syncthreads();
-    const float* S = p.h_ckpt + static_cast<size_t>(ch) * DK * DV;
-    float* Sp = W.Sp + static_cast<size_t>(ch) * DK * DV;
-    const float* em = W.em + static_cast<size_t>(ch) * DK;
-    for (int e = threadIdx.x; e < DK * DV; e += blockDim.x) Sp[e] = em[e / DV] * S[e];
+    f32x4* Sp4 = reinterpret_cast<f32x4*>(W.Sp + static_cast<size_t>(ch) * DK * DV);
+#pragma unroll
+    for (int i = 0; i < NS4; ++i) {
+        const int u = tid + 512 * i;
+        if (S4 % 512 == 0 || u < S4) Sp4[u] = em_s[(4 * u) / DV] * hs[i];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -660,60 +728,142 @@ __global__ void __launch_bounds__(256) bwd_dA_kernel(BwdWs W) {
 }
 
 // gate gradient, unfold of the sign product, scatter to [B,T,H,.]
-__global__ void __launch_bounds__(256) bwd_final_kernel(BwdParams p, BwdWs W) {
+//   dq = P dQ1 e^{b-m},  dk = P (dK1 e^{b-m} + dK2 e^{m-b} + dKB e^{b_L-b}),
+//   db = Q1 dQ1 + K1 dK1 - K2 dK2 - KB dKB  (+ sum_t KB dKB + e^{b_L} sum_v dSt S
+//   at the last token),  dg = reverse cumulative sum of db over the chunk;
+// b, P and the anchored operands are recomputed from g, s, q, k (the same
+// scans as the prep).
+template <int DK> constexpr int final_threads() { return 512; }   // the prep's segmentation: identical b
+
+template <typename Tin, int DK, int DV>
+__global__ void __launch_bounds__(final_threads<DK>()) bwd_final_kernel(BwdParams p, BwdWs W) {
+    constexpr int NTHR = final_threads<DK>();
+    using QS = QuadSeg<DK, NTHR>;
+    constexpr int CQ = QS::CQ, SEGS = QS::SEGS, NTOK = QS::NTOK;
+    // segment totals: (b, P) of the scans, then (db, KB dKB) in the same space
+    __shared__ f32x4 segb[SEGS][CQ], segp[SEGS][CQ];
+    __shared__ __align__(16) float dgl[DK];
+    f32x4 (&segdb)[SEGS][CQ] = segb;
+    f32x4 (&segkb)[SEGS][CQ] = segp;
     const int ch = blockIdx.x;
-    const int DK = W.DK, DV = W.DV;
     const ChunkIdx ci(ch, p.H, p.NT, p.T);
+    const int tid = threadIdx.x, q4 = tid % CQ, seg = tid / CQ, tb = seg * NTOK;
     const size_t trow0 = static_cast<size_t>(ci.b) * p.T + ci.t0;
     const size_t o64k = static_cast<size_t>(ch) * 64 * DK;
     const size_t o64v = static_cast<size_t>(ch) * 64 * DV;
-    const int c = threadIdx.x;
-    // dGL_c = sum_v dSt[c][v] S[c][v]: row sums read along the rows (coalesced),
-    // one wave per row, reduced across the wave
-    __shared__ float dgl[128];
-    {
-        const float* S = p.h_ckpt + static_cast<size_t>(ch) * DK * DV;
-        const float* dSt = W.dSt + static_cast<size_t>(ch) * DK * DV;
-        const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-        for (int r = w; r < DK; r += 4) {
-            float x = 0.f;
-            for (int v = l; v < DV; v += 64) x += dSt[r * DV + v] * S[r * DV + v];
+    f32x4 gv[NTOK], sg[NTOK], kv[NTOK], qv[NTOK], dq1[NTOK], dk1[NTOK], dk2[NTOK], dkb[NTOK];
 #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-            if (l == 0) dgl[r] = x;
+    for (int i = 0; i < NTOK; ++i) {
+        const size_t e = ((trow0 + min(tb + i, ci.L - 1)) * p.H + ci.h) * DK + 4 * q4;
+        gv[i] = *reinterpret_cast<const f32x4*>(p.g + e);
+        sg[i] = signs_quad(p.s, e);
+        kv[i] = load_quad(static_cast<const Tin*>(p.k), e);
+        qv[i] = load_quad(static_cast<const Tin*>(p.q), e);
+        const size_t o = o64k + static_cast<size_t>(tb + i) * DK + 4 * q4;
+        dq1[i] = *reinterpret_cast<const f32x4*>(W.dQ1 + o);
+        dk1[i] = *reinterpret_cast<const f32x4*>(W.dK1 + o);
+        dk2[i] = *reinterpret_cast<const f32x4*>(W.dK2 + o);
+        dkb[i] = *reinterpret_cast<const f32x4*>(W.dKB + o);
+    }
+    f32x4 run = {0.f, 0.f, 0.f, 0.f}, par = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+    for (int i = 0; i < NTOK; ++i) {
+        const bool valid = tb + i < ci.L;
+        run += valid ? gv[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+        par *= valid ? sg[i] : f32x4{1.f, 1.f, 1.f, 1.f};
+        gv[i] = run;
+        sg[i] = par;
+    }
+    segb[seg][q4] = run;
+    segp[seg][q4] = par;
+    __syncthreads();
+    f32x4 off = {0.f, 0.f, 0.f, 0.f}, poff = {1.f, 1.f, 1.f, 1.f}, m = off, bL = off;
+#pragma unroll 2
+    for (int s2 = 0; s2 < SEGS; ++s2) {
+        const f32x4 x = segb[s2][q4];
+        if (s2 < seg) { off += x; poff *= segp[s2][q4]; }
+        if (s2 < SEGS / 2) m += x;
+        bL += x;
+    }
+    f32x4 dbv[NTOK];
+    f32x4 kbs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NTOK; ++i) {
+        const bool valid = tb + i < ci.L;
+        const f32x4 b = gv[i] + off, P = sg[i] * poff;
+        const f32x4 kf = P * kv[i], qf = P * qv[i];
+        const f32x4 e1 = exp2c4((b - m) * kLog2e), e2 = exp2c4((m - b) * kLog2e), e3 = exp2c4((bL - b) * kLog2e);
+        const f32x4 kb = kf * e3;
+        const f32x4 dbi = qf * e1 * dq1[i] + kf * e1 * dk1[i] - kf * e2 * dk2[i] - kb * dkb[i];
+        // dq = P dq~ and dk = P dk~
+        if (valid) {
+            const size_t e = ((trow0 + tb + i) * p.H + ci.h) * DK + 4 * q4;
+            *reinterpret_cast<f32x4*>(p.dq + e) = P * (dq1[i] * e1);
+            *reinterpret_cast<f32x4*>(p.dk + e) = P * (dk1[i] * e1 + dk2[i] * e2 + dkb[i] * e3);
         }
+        dbv[i] = valid ? dbi : f32x4{0.f, 0.f, 0.f, 0.f};
+        kbs += valid ? kb * dkb[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // dGL_c = sum_v dSt[c][v] S[c][v]: TPR threads per row, NQ 16-byte units each,
+    // read once the token operands are consumed (registers are free again)
+    constexpr int TPR = (DV / 4) < (NTHR / DK) ? (DV / 4) : (NTHR / DK), NQ = (DV / 4) / TPR;
+    const int gr = tid / TPR, gj = tid % TPR;
+    f32x4 gs[NQ], gd[NQ];
+    {
+        const f32x4* S4 = reinterpret_cast<const f32x4*>(p.h_ckpt + static_cast<size_t>(ch) * DK * DV);
+        const f32x4* D4 = reinterpret_cast<const f32x4*>(W.dSt + static_cast<size_t>(ch) * DK * DV);
+        const int r = min(gr, DK - 1);
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            gs[i] = S4[r * (DV / 4) + i * TPR + gj];
+            gd[i] = D4[r * (DV / 4) + i * TPR + gj];
+        }
+    }
+    // suffix sums of db inside the segment
+    f32x4 suf = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = NTOK - 1; i >= 0; --i) {
+        suf += dbv[i];
+        dbv[i] = suf;
+    }
+    __syncthreads();   // every thread has read the scan totals
+    segdb[seg][q4] = suf;
+    segkb[seg][q4] = kbs;
+    {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) acc += gs[i] * gd[i];
+        float x = acc[0] + acc[1] + acc[2] + acc[3];
+#pragma unroll
+        for (int o = 1; o < TPR; o <<= 1) x += __shfl_xor(x, o, 64);
+        if (gj == 0 && gr < DK) dgl[gr] = x;
     }
     __syncthreads();
-    if (c < DK) {
-        const float dGL = dgl[c];
-        const float m = W.Bb[o64k + min(31, ci.L - 1) * DK + c];
-        const float bL = W.Bb[o64k + (ci.L - 1) * DK + c];
-        float kbsum = 0.f;
-        for (int t = 0; t < ci.L; ++t) kbsum += W.KB[o64k + t * DK + c] * W.dKB[o64k + t * DK + c];
-        float acc = 0.f;
-        for (int t = ci.L - 1; t >= 0; --t) {
-            const size_t o = o64k + t * DK + c;
-            const float b = W.Bb[o], P = W.Pp[o];
-            const float e1 = exp2_clamped((b - m) * kLog2e);
-            const float e2 = exp2_clamped((m - b) * kLog2e);
-            const float e3 = exp2_clamped((bL - b) * kLog2e);
-            const float dq = W.dQ1[o] * e1;
-            const float dk = W.dK1[o] * e1 + W.dK2[o] * e2 + W.dKB[o] * e3;
-            float db = W.Q1[o] * W.dQ1[o] + W.K1[o] * W.dK1[o] - W.K2[o] * W.dK2[o] - W.KB[o] * W.dKB[o];
-            if (t == ci.L - 1) db += kbsum + exp2_clamped(bL * kLog2e) * dGL;
-            acc += db;
-            const size_t e = ((trow0 + t) * p.H + ci.h) * DK + c;
-            p.dq[e] = P * dq;
-            p.dk[e] = P * dk;
-            p.dg[e] = acc;
+    f32x4 later = {0.f, 0.f, 0.f, 0.f}, kbsum = later;
+#pragma unroll 2
+    for (int s2 = 0; s2 < SEGS; ++s2) {
+        if (s2 > seg) later += segdb[s2][q4];
+        kbsum += segkb[s2][q4];
+    }
+    const f32x4 dgl4 = *reinterpret_cast<const f32x4*>(dgl + 4 * q4);
+    const f32x4 extra = kbsum + exp2c4(bL * kLog2e) * dgl4;   // at the last token, so in every dg
+#pragma unroll
+    for (int i = 0; i < NTOK; ++i) {
+        const int t = tb + i;
+        if (t < ci.L) {
+            const size_t e = ((trow0 + t) * p.H + ci.h) * DK + 4 * q4;
+            *reinterpret_cast<f32x4*>(p.dg + e) = dbv[i] + later + extra;
         }
     }
-    if (c < DV) {
-        for (int t = 0; t < ci.L; ++t) p.dv[((trow0 + t) * p.H + ci.h) * DV + c] = W.dV[o64v + t * DV + c];
+    for (int u = tid; u < 64 * (DV / 4); u += NTHR) {
+        const int t = u / (DV / 4), c4 = u % (DV / 4);
+        if (t < ci.L)
+            *reinterpret_cast<f32x4*>(p.dv + ((trow0 + t) * p.H + ci.h) * DV + 4 * c4) =
+                *reinterpret_cast<const f32x4*>(W.dV + o64v + static_cast<size_t>(t) * DV + 4 * c4);
     }
-    if (c < ci.L) {
-        const size_t o = static_cast<size_t>(ch) * 64 + c;
-        p.dbeta[(trow0 + c) * p.H + ci.h] = W.dbeta1[o] + W.dbeta2[o];
+    if (tid < ci.L) {
+        const size_t o = static_cast<size_t>(ch) * 64 + tid;
+        p.dbeta[(trow0 + tid) * p.H + ci.h] = W.dbeta1[o] + W.dbeta2[o];
     }
 }
 
@@ -722,6 +872,29 @@ __global__ void fill_copy_kernel(float* dst, const float* src, size_t n) {
     for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
          i += static_cast<size_t>(gridDim.x) * blockDim.x)
         dst[i] = src ? src[i] : 0.f;
+}
+
+template <typename Tin, int DK, int DV>
+static hipError_t launch_chunk_pass_t(bool final_pass, const BwdParams& p, const BwdWs& W, int NC, hipStream_t st) {
+    if (final_pass)
+        hipLaunchKernelGGL((bwd_final_kernel<Tin, DK, DV>), dim3(NC), dim3(final_threads<DK>()), 0, st, p, W);
+    else
+        hipLaunchKernelGGL((bwd_prep_kernel<Tin, DK, DV>), dim3(NC), dim3(512), 0, st, p, W);
+    return hipGetLastError();
+}
+
+// the prep (final_pass false) or final pass over every chunk-head
+static hipError_t launch_chunk_pass(bool bf16, bool final_pass, const BwdParams& p, const BwdWs& W, int NC,
+                                    hipStream_t st) {
+#define CKDA_PASS(DK_, DV_)                                                                           \
+    if (W.DK == DK_ && W.DV == DV_)                                                                   \
+        return bf16 ? launch_chunk_pass_t<bf16_t, DK_, DV_>(final_pass, p, W, NC, st)                 \
+                    : launch_chunk_pass_t<float, DK_, DV_>(final_pass, p, W, NC, st);
+    CKDA_PASS(32, 32) CKDA_PASS(32, 64) CKDA_PASS(32, 128)
+    CKDA_PASS(64, 32) CKDA_PASS(64, 64) CKDA_PASS(64, 128)
+    CKDA_PASS(128, 32) CKDA_PASS(128, 64) CKDA_PASS(128, 128)
+#undef CKDA_PASS
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -754,11 +927,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
     W.carve(static_cast<float*>(a.ws), NC, DK, DV);
     hipError_t e;
 #define CKDA_CHECK(x) do { e = (x); if (e != hipSuccess) return e; } while (0)
-    if (a.bf16)
-        hipLaunchKernelGGL(bwd_prep_kernel<bf16_t>, dim3(NC), dim3(256), 0, st, p, W);
-    else
-        hipLaunchKernelGGL(bwd_prep_kernel<float>, dim3(NC), dim3(256), 0, st, p, W);
-    CKDA_CHECK(hipGetLastError());
+    CKDA_CHECK(launch_chunk_pass(a.bf16, false, p, W, NC, st));
     const long long s64k = 64LL * DK, s64v = 64LL * DV, skv = 1LL * DK * DV, s44 = 4096;
     // A = strict_lower(K1 K2^T), M = lower(Q1 K2^T)
     CKDA_CHECK(gemm(mk(64, 64, DK, W.K1, DK, s64k, false, W.K2, DK, s64k, true, W.A, 64, s44, 1.f, nullptr, 0.f, 1), NC, st));
@@ -791,7 +960,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
     CKDA_CHECK(gemm(mk(64, DK, 64, W.dM, 64, s44, true, W.Q1, DK, s64k, false, W.dK2, DK, s64k, 1.f, W.dK2, 1.f), NC, st));
     CKDA_CHECK(gemm(mk(64, DK, 64, W.dM, 64, s44, false, W.K2, DK, s64k, false, W.dQ1, DK, s64k), NC, st));
     CKDA_CHECK(gemm(mk(64, DK, DV, W.dO, DV, s64v, false, W.Sp, DV, skv, true, W.dQ1, DK, s64k, 1.f, W.dQ1, 1.f), NC, st));
-    hipLaunchKernelGGL(bwd_final_kernel, dim3(NC), dim3(256), 0, st, p, W);
+    CKDA_CHECK(launch_chunk_pass(a.bf16, true, p, W, NC, st));
     CKDA_CHECK(hipGetLastError());
 #undef CKDA_CHECK
     return hipSuccess;
