@@ -112,20 +112,15 @@ __device__ __forceinline__ void stage_slab(float* dst, int pitch, const float* s
     }
 }
 
-template <bool aT, bool bT, int NT>   // aT: A stored transposed, bT: B stored transposed, NT = N / 16
-__global__ void __launch_bounds__(256) bgemm_kernel(Gemm p) {
-    __shared__ __align__(16) float As[64 * kPK > kKS * kPN ? 64 * kPK : kKS * kPN];
-    __shared__ __align__(16) float Bs[128 * kPK > 2 * kKS * kPN ? 128 * kPK : 2 * kKS * kPN];
-    const long long z = blockIdx.x;
+// acc += sa * A_z B_z over the product's K (aT: A stored transposed, bT: B
+// stored transposed, NT = N / 16); both slabs staged through LDS
+template <bool aT, bool bT, int NT>
+__device__ __forceinline__ void bgemm_accumulate(const Gemm& p, long long z, float sa, f32x4 (&acc)[NT], float* As,
+                                                 float* Bs) {
     const float* A = p.A + z * p.sA;
     const float* B = p.B + z * p.sB;
-    float* C = p.C + z * p.sC;
-    const float* D = p.D ? p.D + z * p.sD : nullptr;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 15, g = l >> 4;
     // A transposed: element (i, k) at k * ac + i; B transposed: element (k, j) at j * bc + k
-    f32x4 acc[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int k0 = 0; k0 < p.K; k0 += kKS) {
         if constexpr (!aT) stage_slab(As, kPK, A, 64, kKS, p.ar, 0, k0);      // As[i][k]
         else stage_slab(As, kPN, A, kKS, 64, p.ac, k0, 0);                    // As[k][i]
@@ -140,7 +135,7 @@ __global__ void __launch_bounds__(256) bgemm_kernel(Gemm p) {
 #pragma unroll 2
         for (int kk = 0; kk < kKS; kk += 4) {
             const int i = 16 * w + n, k = kk + g;
-            const float a = aT ? As[k * kPN + i] : As[i * kPK + k];
+            const float a = sa * (aT ? As[k * kPN + i] : As[i * kPK + k]);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 const int j = 16 * t + n;
@@ -150,6 +145,23 @@ __global__ void __launch_bounds__(256) bgemm_kernel(Gemm p) {
         }
         __syncthreads();
     }
+}
+
+// C = p.alpha * (A1 B1 + (q.alpha / p.alpha) A2 B2) + p.beta * D, masked;
+// the second product only when DUAL
+template <bool aT, bool bT, int NT, bool DUAL = false, bool aT2 = false, bool bT2 = false>
+__global__ void __launch_bounds__(256) bgemm_kernel(Gemm p, Gemm q) {
+    __shared__ __align__(16) float As[64 * kPK > kKS * kPN ? 64 * kPK : kKS * kPN];
+    __shared__ __align__(16) float Bs[128 * kPK > 2 * kKS * kPN ? 128 * kPK : 2 * kKS * kPN];
+    const long long z = blockIdx.x;
+    float* C = p.C + z * p.sC;
+    const float* D = p.D ? p.D + z * p.sD : nullptr;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 15, g = l >> 4;
+    f32x4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bgemm_accumulate<aT, bT, NT>(p, z, 1.f, acc, As, Bs);
+    if constexpr (DUAL) bgemm_accumulate<aT2, bT2, NT>(q, z, q.alpha / p.alpha, acc, As, Bs);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
@@ -164,12 +176,16 @@ __global__ void __launch_bounds__(256) bgemm_kernel(Gemm p) {
     }
 }
 
-hipError_t gemm(const Gemm& g, int nbatch, hipStream_t st) {
+static bool gemm_shape_ok(const Gemm& g) {
     // shapes used by the backward: M = 64, N and K in {32, 64, 128}
     auto ok = [](int x) { return x == 32 || x == 64 || x == 128; };
-    if (g.M != 64 || !ok(g.N) || !ok(g.K)) return hipErrorInvalidValue;
+    return g.M == 64 && ok(g.N) && ok(g.K);
+}
+
+hipError_t gemm(const Gemm& g, int nbatch, hipStream_t st) {
+    if (!gemm_shape_ok(g)) return hipErrorInvalidValue;
     const bool aT = g.ar == 1, bT = g.bc != 1;
-    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, dim3(nbatch), dim3(256), 0, st, g); };
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, dim3(nbatch), dim3(256), 0, st, g, g); };
 #define CKDA_GEMM_N(AT, BT)                                                  \
     if (g.N == 32) go(bgemm_kernel<AT, BT, 2>);                              \
     else if (g.N == 64) go(bgemm_kernel<AT, BT, 4>);                         \
@@ -180,6 +196,27 @@ hipError_t gemm(const Gemm& g, int nbatch, hipStream_t st) {
     else { CKDA_GEMM_N(false, false) }
 #undef CKDA_GEMM_N
     return hipGetLastError();
+}
+
+// C = g.alpha A1 B1 + h.alpha A2 B2 (+ g.beta D) into g's output; the operand
+// layouts of the pairs the backward fuses
+hipError_t gemm2(const Gemm& g, const Gemm& h, int nbatch, hipStream_t st) {
+    if (!gemm_shape_ok(g) || !gemm_shape_ok(h) || g.N != h.N || g.alpha == 0.f) return hipErrorInvalidValue;
+    const bool a1 = g.ar == 1, b1 = g.bc != 1, a2 = h.ar == 1, b2 = h.bc != 1;
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, dim3(nbatch), dim3(256), 0, st, g, h); };
+#define CKDA_GEMM2(A1, B1, A2, B2)                                                   \
+    if (a1 == A1 && b1 == B1 && a2 == A2 && b2 == B2) {                              \
+        if (g.N == 32) go(bgemm_kernel<A1, B1, 2, true, A2, B2>);                    \
+        else if (g.N == 64) go(bgemm_kernel<A1, B1, 4, true, A2, B2>);               \
+        else go(bgemm_kernel<A1, B1, 8, true, A2, B2>);                              \
+        return hipGetLastError();                                                    \
+    }
+    CKDA_GEMM2(false, true, false, true)     // dT = dU V^T + dW K1^T
+    CKDA_GEMM2(true, false, false, false)    // dK1 = T^T dW + dA K2
+    CKDA_GEMM2(true, false, true, false)     // dK2 = dA^T K1 + dM^T Q1
+    CKDA_GEMM2(false, false, false, true)    // dQ1 = dM K2 + dO S'^T
+#undef CKDA_GEMM2
+    return hipErrorInvalidValue;
 }
 
 // C = alpha * op(A) op(B) (+ beta * D), all operands [NC][rows][cols] row-major.
@@ -944,9 +981,9 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
     CKDA_CHECK(gemm(mk(64, DK, DV, W.U, DV, s64v, false, W.dSt, DV, skv, true, W.dKB, DK, s64k), NC, st));
     CKDA_CHECK(gemm(mk(64, DK, DV, W.dU, DV, s64v, false, W.Sp, DV, skv, true, W.dW, DK, s64k, -1.f), NC, st));
     CKDA_CHECK(gemm(mk(64, DV, 64, W.T, 64, s44, true, W.dU, DV, s64v, false, W.dV, DV, s64v), NC, st));
-    CKDA_CHECK(gemm(mk(64, 64, DV, W.dU, DV, s64v, false, W.V, DV, s64v, true, W.dT, 64, s44), NC, st));
-    CKDA_CHECK(gemm(mk(64, 64, DK, W.dW, DK, s64k, false, W.K1, DK, s64k, true, W.dT, 64, s44, 1.f, W.dT, 1.f), NC, st));
-    CKDA_CHECK(gemm(mk(64, DK, 64, W.T, 64, s44, true, W.dW, DK, s64k, false, W.dK1, DK, s64k), NC, st));
+    // dT = dU V^T + dW K1^T
+    CKDA_CHECK(gemm2(mk(64, 64, DV, W.dU, DV, s64v, false, W.V, DV, s64v, true, W.dT, 64, s44),
+                     mk(64, 64, DK, W.dW, DK, s64k, false, W.K1, DK, s64k, true, W.dT, 64, s44), NC, st));
     hipLaunchKernelGGL(bwd_dbeta1_kernel, dim3(NC), dim3(256), 0, st, W);
     CKDA_CHECK(hipGetLastError());
     // dX = -Xi^T (Y1 Xi^T)
@@ -954,12 +991,13 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
     CKDA_CHECK(gemm(mk(64, 64, 64, W.Xi, 64, s44, true, W.Tmp, 64, s44, false, W.dX, 64, s44, -1.f), NC, st));
     hipLaunchKernelGGL(bwd_dA_kernel, dim3(NC), dim3(256), 0, st, W);
     CKDA_CHECK(hipGetLastError());
-    // dK1 += dA K2 ; dK2 = dA^T K1 + dM^T Q1 ; dQ1 = dM K2 + dO S'^T
-    CKDA_CHECK(gemm(mk(64, DK, 64, W.dA, 64, s44, false, W.K2, DK, s64k, false, W.dK1, DK, s64k, 1.f, W.dK1, 1.f), NC, st));
-    CKDA_CHECK(gemm(mk(64, DK, 64, W.dA, 64, s44, true, W.K1, DK, s64k, false, W.dK2, DK, s64k), NC, st));
-    CKDA_CHECK(gemm(mk(64, DK, 64, W.dM, 64, s44, true, W.Q1, DK, s64k, false, W.dK2, DK, s64k, 1.f, W.dK2, 1.f), NC, st));
-    CKDA_CHECK(gemm(mk(64, DK, 64, W.dM, 64, s44, false, W.K2, DK, s64k, false, W.dQ1, DK, s64k), NC, st));
-    CKDA_CHECK(gemm(mk(64, DK, DV, W.dO, DV, s64v, false, W.Sp, DV, skv, true, W.dQ1, DK, s64k, 1.f, W.dQ1, 1.f), NC, st));
+    // dK1 = T^T dW + dA K2 ; dK2 = dA^T K1 + dM^T Q1 ; dQ1 = dM K2 + dO S'^T
+    CKDA_CHECK(gemm2(mk(64, DK, 64, W.T, 64, s44, true, W.dW, DK, s64k, false, W.dK1, DK, s64k),
+                     mk(64, DK, 64, W.dA, 64, s44, false, W.K2, DK, s64k, false, W.dK1, DK, s64k), NC, st));
+    CKDA_CHECK(gemm2(mk(64, DK, 64, W.dA, 64, s44, true, W.K1, DK, s64k, false, W.dK2, DK, s64k),
+                     mk(64, DK, 64, W.dM, 64, s44, true, W.Q1, DK, s64k, false, W.dK2, DK, s64k), NC, st));
+    CKDA_CHECK(gemm2(mk(64, DK, 64, W.dM, 64, s44, false, W.K2, DK, s64k, false, W.dQ1, DK, s64k),
+                     mk(64, DK, DV, W.dO, DV, s64v, false, W.Sp, DV, skv, true, W.dQ1, DK, s64k), NC, st));
     CKDA_CHECK(launch_chunk_pass(a.bf16, true, p, W, NC, st));
     CKDA_CHECK(hipGetLastError());
 #undef CKDA_CHECK
