@@ -729,39 +729,60 @@ static hipError_t launch_reverse(const BwdParams& p, const BwdWs& W, hipStream_t
     return hipErrorInvalidValue;
 }
 
-// dbeta1_i = sum_r dT_ri Xi_ri ; Y1 = dT Diag(beta)
+// 64x64 per chunk-head, 256 threads: thread t owns row r = t / 4 and the
+// 16 columns 16 (t % 4) .. +15 as four 16-byte units (coalesced rows).
+
+// dbeta1_i = sum_r dT_ri Xi_ri (column sums) ; Y1 = dT Diag(beta)
 __global__ void __launch_bounds__(256) bwd_dbeta1_kernel(BwdWs W) {
+    __shared__ f32x4 part[64][16];
     const size_t ch = blockIdx.x;
-    const float* dT = W.dT + ch * 4096;
-    const float* Xi = W.Xi + ch * 4096;
-    const float* bt = W.beta + ch * 64;
-    float* Y1 = W.Y1 + ch * 4096;
-    for (int e = threadIdx.x; e < 4096; e += 256) Y1[e] = dT[e] * bt[e % 64];
-    if (threadIdx.x < 64) {
-        const int i = threadIdx.x;
-        float acc = 0.f;
-        for (int r = 0; r < 64; ++r) acc += dT[r * 64 + i] * Xi[r * 64 + i];
-        W.dbeta1[ch * 64 + i] = acc;
+    const int t = threadIdx.x, r = t >> 2, c0 = 16 * (t & 3);
+    const f32x4* dT = reinterpret_cast<const f32x4*>(W.dT + ch * 4096 + r * 64 + c0);
+    const f32x4* Xi = reinterpret_cast<const f32x4*>(W.Xi + ch * 4096 + r * 64 + c0);
+    const f32x4* bt = reinterpret_cast<const f32x4*>(W.beta + ch * 64 + c0);
+    f32x4* Y1 = reinterpret_cast<f32x4*>(W.Y1 + ch * 4096 + r * 64 + c0);
+    f32x4 d[4], x[4], b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) { d[u] = dT[u]; x[u] = Xi[u]; b[u] = bt[u]; }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        Y1[u] = d[u] * b[u];
+        part[r][4 * (t & 3) + u] = d[u] * x[u];
+    }
+    __syncthreads();
+    if (t < 64) {   // column t: sum over the 64 rows
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const int unit = t >> 2, lane = t & 3;
+        for (int rr = 0; rr < 64; ++rr) acc += part[rr][unit];
+        W.dbeta1[ch * 64 + t] = acc[lane];
     }
 }
 
-// dXs = strict_lower(dX); dbeta2_r = sum_i dXs_ri A_ri; dA = Diag(beta) dXs
+// dXs = strict_lower(dX); dbeta2_r = sum_i dXs_ri A_ri (row sums); dA = Diag(beta) dXs
 __global__ void __launch_bounds__(256) bwd_dA_kernel(BwdWs W) {
     const size_t ch = blockIdx.x;
-    const float* dX = W.dX + ch * 4096;
-    const float* A = W.A + ch * 4096;
-    const float* bt = W.beta + ch * 64;
-    float* dA = W.dA + ch * 4096;
-    for (int e = threadIdx.x; e < 4096; e += 256) {
-        const int r = e / 64, i = e % 64;
-        dA[e] = (i < r) ? bt[r] * dX[e] : 0.f;
+    const int t = threadIdx.x, r = t >> 2, c0 = 16 * (t & 3);
+    const f32x4* dX = reinterpret_cast<const f32x4*>(W.dX + ch * 4096 + r * 64 + c0);
+    const f32x4* A = reinterpret_cast<const f32x4*>(W.A + ch * 4096 + r * 64 + c0);
+    f32x4* dA = reinterpret_cast<f32x4*>(W.dA + ch * 4096 + r * 64 + c0);
+    const float br = W.beta[ch * 64 + r];
+    f32x4 x[4], a[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) { x[u] = dX[u]; a[u] = A[u]; }
+    float rs = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        f32x4 m;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m[e] = (c0 + 4 * u + e < r) ? x[u][e] : 0.f;
+        dA[u] = br * m;
+        const f32x4 pa = m * a[u];
+        rs += pa[0] + pa[1] + pa[2] + pa[3];
     }
-    if (threadIdx.x < 64) {
-        const int r = threadIdx.x;
-        float acc = 0.f;
-        for (int i = 0; i < r; ++i) acc += dX[r * 64 + i] * A[r * 64 + i];
-        W.dbeta2[ch * 64 + r] = acc;
-    }
+    // the row's four threads are adjacent lanes
+    rs += __shfl_xor(rs, 1, 64);
+    rs += __shfl_xor(rs, 2, 64);
+    if ((t & 3) == 0) W.dbeta2[ch * 64 + r] = rs;
 }
 
 // gate gradient, unfold of the sign product, scatter to [B,T,H,.]
