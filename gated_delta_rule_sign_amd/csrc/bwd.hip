@@ -101,37 +101,59 @@ constexpr int kKS = 32;          // slab width (K)
 constexpr int kPK = kKS + 4;     // pitch of rows that run along K
 constexpr int kPN = 64 + 4;      // pitch of rows that run along M or N (64-wide blocks)
 
-__device__ __forceinline__ void stage_slab(float* dst, int pitch, const float* src, int rows, int cols, int ld, int r0,
-                                           int c0) {
-    // copy src[(r0 + r) * ld + c0 + c] for r < rows, c < cols (a multiple of 4) into dst[r * pitch + c]
-    const int q = cols / 4;
-    for (int e = threadIdx.x; e < rows * q; e += 256) {
-        const int r = e / q, c4 = (e % q) * 4;
-        const float4 v = *reinterpret_cast<const float4*>(src + static_cast<size_t>(r0 + r) * ld + c0 + c4);
-        *reinterpret_cast<float4*>(dst + r * pitch + c4) = v;
-    }
-}
 
 // acc += sa * A_z B_z over the product's K (aT: A stored transposed, bT: B
-// stored transposed, NT = N / 16); both slabs staged through LDS
+// stored transposed, NT = N / 16).  Both operands go through LDS in 32-wide
+// K slabs in the layout their storage gives; the next slab is read into
+// registers (16-byte units, coalesced along rows) while the current one is
+// multiplied.
 template <bool aT, bool bT, int NT>
 __device__ __forceinline__ void bgemm_accumulate(const Gemm& p, long long z, float sa, f32x4 (&acc)[NT], float* As,
                                                  float* Bs) {
+    constexpr int NB = NT / 2 > 0 ? NT / 2 : 1;   // B units per thread (A: 2)
     const float* A = p.A + z * p.sA;
     const float* B = p.B + z * p.sB;
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 15, g = l >> 4;
-    // A transposed: element (i, k) at k * ac + i; B transposed: element (k, j) at j * bc + k
-    for (int k0 = 0; k0 < p.K; k0 += kKS) {
-        if constexpr (!aT) stage_slab(As, kPK, A, 64, kKS, p.ar, 0, k0);      // As[i][k]
-        else stage_slab(As, kPN, A, kKS, 64, p.ac, k0, 0);                    // As[k][i]
-        if constexpr (!bT) {                                                   // Bs[k][j], 64-wide blocks of j
-#pragma unroll
-            for (int h = 0; h < 16 * NT; h += 64)
-                stage_slab(Bs + (h / 64) * kKS * kPN, kPN, B, kKS, 16 * NT - h < 64 ? 16 * NT - h : 64, p.br, k0, h);
-        } else {                                                               // Bs[j][k]
-            stage_slab(Bs, kPK, B, 16 * NT, kKS, p.bc, 0, k0);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, n = l & 15, g = l >> 4;
+    // unit e of a slab -> (row, 4-column group) of the staged block
+    auto a_src = [&](int e, int k0) -> const float* {
+        if constexpr (!aT) return A + static_cast<size_t>(e / 8) * p.ar + k0 + 4 * (e % 8);   // As[i][k], 64 x 32
+        else return A + static_cast<size_t>(k0 + e / 16) * p.ac + 4 * (e % 16);              // As[k][i], 32 x 64
+    };
+    auto a_dst = [&](int e) -> float* {
+        if constexpr (!aT) return As + (e / 8) * kPK + 4 * (e % 8);
+        else return As + (e / 16) * kPN + 4 * (e % 16);
+    };
+    // B: bT -> Bs[j][k] (16 NT x 32); else Bs[k][j] in 64-wide blocks of j
+    constexpr int BW = 16 * NT < 64 ? 16 * NT : 64;   // block width (not transposed)
+    auto b_src = [&](int e, int k0) -> const float* {
+        if constexpr (bT) return B + static_cast<size_t>(e / 8) * p.bc + k0 + 4 * (e % 8);
+        else {
+            const int blk = e / (32 * BW / 4), u = e % (32 * BW / 4);
+            return B + static_cast<size_t>(k0 + u / (BW / 4)) * p.br + 64 * blk + 4 * (u % (BW / 4));
         }
+    };
+    auto b_dst = [&](int e) -> float* {
+        if constexpr (bT) return Bs + (e / 8) * kPK + 4 * (e % 8);
+        else {
+            const int blk = e / (32 * BW / 4), u = e % (32 * BW / 4);
+            return Bs + blk * kKS * kPN + (u / (BW / 4)) * kPN + 4 * (u % (BW / 4));
+        }
+    };
+    f32x4 ra[2], rb[NB];
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) ra[i] = *reinterpret_cast<const f32x4*>(a_src(tid + 256 * i, k0));
+#pragma unroll
+        for (int i = 0; i < NB; ++i) rb[i] = *reinterpret_cast<const f32x4*>(b_src(tid + 256 * i, k0));
+    };
+    load(0);
+    for (int k0 = 0; k0 < p.K; k0 += kKS) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) *reinterpret_cast<f32x4*>(a_dst(tid + 256 * i)) = ra[i];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) *reinterpret_cast<f32x4*>(b_dst(tid + 256 * i)) = rb[i];
         __syncthreads();
+        if (k0 + kKS < p.K) load(k0 + kKS);
 #pragma unroll 2
         for (int kk = 0; kk < kKS; kk += 4) {
             const int i = 16 * w + n, k = kk + g;
