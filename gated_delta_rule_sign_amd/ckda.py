@@ -54,8 +54,10 @@ def lib() -> ctypes.CDLL:
     L.ckda_fwd_varlen_workspace_bytes.restype = S
     L.ckda_fwd_chunked.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P, P, S, P]
     L.ckda_fwd_chunked.restype = I
-    L.ckda_fwd_varlen.argtypes = [I, I, P, P, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P, S, P]
+    L.ckda_fwd_varlen.argtypes = [I, I, P, P, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P, P, S, P]
     L.ckda_fwd_varlen.restype = I
+    L.ckda_varlen_chunk_slots.argtypes = [I, I]
+    L.ckda_varlen_chunk_slots.restype = I
     L.ckda_decode_step.argtypes = [I, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P]
     L.ckda_decode_step.restype = I
     L.ckda_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
@@ -63,6 +65,11 @@ def lib() -> ctypes.CDLL:
     L.ckda_bwd.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P,
                            P, P, P, P, P, P, P, S, P]
     L.ckda_bwd.restype = I
+    L.ckda_bwd_varlen_workspace_bytes.argtypes = [I, I, I, I, I]
+    L.ckda_bwd_varlen_workspace_bytes.restype = S
+    L.ckda_bwd_varlen.argtypes = [I, I, P, P, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P,
+                                  P, P, P, P, P, P, P, S, P]
+    L.ckda_bwd_varlen.restype = I
     _lib = L
     return L
 
@@ -181,10 +188,17 @@ def fwd(q, k, v, g, s, beta, scale: float = 1.0, h0=None, want_ht: bool = True,
     return o, ht, h_ckpt
 
 
+def varlen_chunk_slots(N, T_total) -> int:
+    return int(lib().ckda_varlen_chunk_slots(N, T_total))
+
+
 def fwd_varlen(q, k, v, g, s, beta, cu_seqlens, scale: float = 1.0, h0=None,
-               want_ht: bool = True, cu_seqlens_dev=None, o=None, ht=None, workspace=None):
+               want_ht: bool = True, cu_seqlens_dev=None, o=None, ht=None, workspace=None,
+               want_ckpt: bool = False):
     """Packed-document forward (ckda_fwd_varlen).  q etc. are [T_total,H,D]
-    (a leading 1 is accepted); cu_seqlens is an int32 CPU tensor [N+1]."""
+    (a leading 1 is accepted); cu_seqlens is an int32 CPU tensor [N+1].
+    Returns (o, ht), or (o, ht, h_ckpt) with want_ckpt: the chunk-start
+    states per chunk slot [varlen_chunk_slots(N, T_total), H, DK, DV]."""
     if q.dim() == 4:
         q, k, v, g, s, beta = (x[0] for x in (q, k, v, g, s, beta))
     Tt = q.shape[0]
@@ -203,11 +217,14 @@ def fwd_varlen(q, k, v, g, s, beta, cu_seqlens, scale: float = 1.0, h0=None,
     if want_ht and ht is None:
         ht = torch.empty((N, H, DK, DV), dtype=torch.float32, device=dev)
     _need(ht, "ht", torch.float32, (N, H, DK, DV), dev)
+    hc = None
+    if want_ckpt:
+        hc = torch.empty((varlen_chunk_slots(N, Tt), H, DK, DV), dtype=torch.float32, device=dev)
     workspace, wsb = _workspace(workspace, fwd_varlen_workspace_bytes(N, Tt, H, DK, DV, q.dtype), dev)
     _check(lib().ckda_fwd_varlen(N, Tt, _ptr(cu), _ptr(cu_seqlens_dev), H, DK, DV, dt, _ptr(q),
                                  _ptr(k), _ptr(v), _ptr(g), _ptr(s), _ptr(beta), float(scale),
-                                 _ptr(h0), _ptr(o), _ptr(ht), _ptr(workspace), wsb, _stream()))
-    return o, ht
+                                 _ptr(h0), _ptr(o), _ptr(ht), _ptr(hc), _ptr(workspace), wsb, _stream()))
+    return (o, ht, hc) if want_ckpt else (o, ht)
 
 
 def decode_step(q, k, v, g, s, beta, state, sign_prod, scale: float = 1.0, o=None):
@@ -253,4 +270,44 @@ def bwd(q, k, v, g, s, beta, h_ckpt, do, scale: float = 1.0, h0=None, dht=None,
                           _ptr(beta), float(scale), _ptr(h0), _ptr(h_ckpt), _ptr(do), _ptr(dht),
                           _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
                           _ptr(out["dbeta"]), _ptr(out["dh0"]), _ptr(workspace), wsb, _stream()))
+    return out
+
+
+def bwd_varlen_workspace_bytes(N, T_total, H, DK, DV) -> int:
+    return int(lib().ckda_bwd_varlen_workspace_bytes(N, T_total, H, DK, DV))
+
+
+def bwd_varlen(q, k, v, g, s, beta, cu_seqlens, h_ckpt, do, scale: float = 1.0, h0=None, dht=None,
+               want_dh0: bool = True, cu_seqlens_dev=None, workspace=None):
+    """Backward of the packed-document forward (ckda_bwd_varlen).  Shapes as
+    in fwd_varlen; h_ckpt from fwd_varlen(..., want_ckpt=True); do
+    [T_total,H,DV]; dht, dh0 [N,H,DK,DV].  Returns dict dq, dk, dv, dg,
+    dbeta, dh0 (f32)."""
+    if q.dim() == 4:
+        q, k, v, g, s, beta = (x[0] for x in (q, k, v, g, s, beta))
+        do = do[0] if do.dim() == 4 else do
+    Tt = q.shape[0]
+    dt, H, DK, DV, dev = _token_inputs(q, k, v, g, s, beta, (Tt,))
+    cu = cu_seqlens
+    if cu.is_cuda or cu.dtype != torch.int32 or not cu.is_contiguous():
+        raise CkdaError("cu_seqlens must be a contiguous int32 CPU tensor")
+    N = cu.numel() - 1
+    if cu_seqlens_dev is None:
+        cu_seqlens_dev = cu.to(dev)
+    _need(cu_seqlens_dev, "cu_seqlens_dev", torch.int32, (N + 1,), dev)
+    _need(h_ckpt, "h_ckpt", torch.float32, (varlen_chunk_slots(N, Tt), H, DK, DV), dev)
+    _need(do, "do", q.dtype, (Tt, H, DV), dev)
+    _need(h0, "h0", torch.float32, (N, H, DK, DV), dev)
+    _need(dht, "dht", torch.float32, (N, H, DK, DV), dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dq=torch.empty((Tt, H, DK), **f32), dk=torch.empty((Tt, H, DK), **f32),
+               dv=torch.empty((Tt, H, DV), **f32), dg=torch.empty((Tt, H, DK), **f32),
+               dbeta=torch.empty((Tt, H), **f32),
+               dh0=torch.empty((N, H, DK, DV), **f32) if want_dh0 else None)
+    workspace, wsb = _workspace(workspace, bwd_varlen_workspace_bytes(N, Tt, H, DK, DV), dev)
+    _check(lib().ckda_bwd_varlen(N, Tt, _ptr(cu), _ptr(cu_seqlens_dev), H, DK, DV, dt, _ptr(q),
+                                 _ptr(k), _ptr(v), _ptr(g), _ptr(s), _ptr(beta), float(scale),
+                                 _ptr(h0), _ptr(h_ckpt), _ptr(do), _ptr(dht), _ptr(out["dq"]),
+                                 _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
+                                 _ptr(out["dh0"]), _ptr(workspace), wsb, _stream()))
     return out

@@ -76,11 +76,34 @@ bool too_big(long long tokens, int H) { return tokens * static_cast<long long>(H
 int fwd_slots(int B, int T) { return B * ((T + 63) / 64); }
 int varlen_slots(int N, int T_total) { return (T_total + 63) / 64 + N; }
 
+// cu_seqlens (host copy): N+1 values, starts at 0, non-decreasing, ends at T_total
+ckda_status_t check_cu(int N, int T_total, const int32_t* cu) {
+    CKDA_REQUIRE(cu);
+    if (cu[0] != 0) return fail(CKDA_ERR_SEQLENS, "cu_seqlens[0] = %d, expected 0", cu[0]);
+    for (int i = 0; i < N; ++i)
+        if (cu[i + 1] < cu[i]) return fail(CKDA_ERR_SEQLENS, "cu_seqlens decreases at %d", i);
+    if (cu[N] != T_total) return fail(CKDA_ERR_SEQLENS, "cu_seqlens[N] = %d, expected T_total = %d", cu[N], T_total);
+    return CKDA_OK;
+}
+
+ckda_status_t check_varlen_sizes(int N, int T_total, int H) {
+    if (too_big(T_total, H)) return fail(CKDA_ERR_UNSUPPORTED, "tensor too large");
+    if (static_cast<long long>(N) * H >= (1LL << 31) / 2) return fail(CKDA_ERR_UNSUPPORTED, "too many documents");
+    if (static_cast<long long>(varlen_slots(N, T_total)) * H >= (1LL << 31))
+        return fail(CKDA_ERR_UNSUPPORTED, "too many chunks");
+    return CKDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 int ckda_abi_version(void) { return CKDA_ABI_VERSION; }
+
+int ckda_varlen_chunk_slots(int N, int T_total) {
+    if (N < 0 || T_total < 0) return 0;
+    return varlen_slots(N, T_total);
+}
 
 const char* ckda_status_string(ckda_status_t s) {
     switch (s) {
@@ -156,20 +179,13 @@ ckda_status_t ckda_fwd_chunked(int B, int T, int H, int DK, int DV, ckda_dtype_t
 ckda_status_t ckda_fwd_varlen(int N, int T_total, const int32_t* cu, const int32_t* cu_dev, int H,
                               int DK, int DV, ckda_dtype_t in_dtype, const void* q, const void* k,
                               const void* v, const float* g, const int8_t* s, const float* beta,
-                              float scale, const float* h0, float* o, float* ht, void* workspace,
-                              size_t workspace_bytes, ckda_stream_t stream) {
+                              float scale, const float* h0, float* o, float* ht, float* h_ckpt,
+                              void* workspace, size_t workspace_bytes, ckda_stream_t stream) {
     CKDA_TRY(check_dtype(in_dtype));
     if (N < 0 || T_total < 0 || H < 0) return fail(CKDA_ERR_SHAPE, "negative size (N=%d, T=%d, H=%d)", N, T_total, H);
     CKDA_TRY(check_heads(DK, DV));
-    if (too_big(T_total, H)) return fail(CKDA_ERR_UNSUPPORTED, "tensor too large");
-    if (static_cast<long long>(N) * H >= (1LL << 31) / 2) return fail(CKDA_ERR_UNSUPPORTED, "too many documents");
-    if (static_cast<long long>(varlen_slots(N, T_total)) * H >= (1LL << 31))
-        return fail(CKDA_ERR_UNSUPPORTED, "too many chunks");
-    CKDA_REQUIRE(cu);
-    if (cu[0] != 0) return fail(CKDA_ERR_SEQLENS, "cu_seqlens[0] = %d, expected 0", cu[0]);
-    for (int i = 0; i < N; ++i)
-        if (cu[i + 1] < cu[i]) return fail(CKDA_ERR_SEQLENS, "cu_seqlens decreases at %d", i);
-    if (cu[N] != T_total) return fail(CKDA_ERR_SEQLENS, "cu_seqlens[N] = %d, expected T_total = %d", cu[N], T_total);
+    CKDA_TRY(check_varlen_sizes(N, T_total, H));
+    CKDA_TRY(check_cu(N, T_total, cu));
     if (N * H == 0) return ok();
     CKDA_REQUIRE(cu_dev);
     if (T_total > 0) { CKDA_REQUIRE(q); CKDA_REQUIRE(k); CKDA_REQUIRE(v); CKDA_REQUIRE(g); CKDA_REQUIRE(s); CKDA_REQUIRE(beta); CKDA_REQUIRE(o); }
@@ -184,7 +200,7 @@ ckda_status_t ckda_fwd_varlen(int N, int T_total, const int32_t* cu, const int32
     ckda::FwdArgs a{};
     a.B = 1; a.T = T_total; a.H = H; a.DK = DK; a.DV = DV; a.bf16 = in_dtype == CKDA_BF16;
     a.q = q; a.k = k; a.v = v; a.g = g; a.s = s; a.beta = beta; a.scale = scale;
-    a.h0 = h0; a.o = o; a.ht = ht; a.h_ckpt = nullptr;
+    a.h0 = h0; a.o = o; a.ht = ht; a.h_ckpt = h_ckpt;
     a.cu = cu_dev; a.ndocs = N; a.ws = workspace;
     return hip_status(ckda::launch_fwd(a, nslots, static_cast<hipStream_t>(stream)), "ckda_fwd_varlen launch");
 }
@@ -207,8 +223,39 @@ ckda_status_t ckda_decode_step(int N, int H, int DK, int DV, ckda_dtype_t in_dty
 
 size_t ckda_bwd_workspace_bytes(int B, int T, int H, int DK, int DV) {
     if (B < 0 || T < 0 || H < 0 || !head_ok(DK) || !head_ok(DV)) return 0;
-    return ckda::bwd_workspace_bytes(B, T, H, DK, DV);
+    return ckda::bwd_workspace_bytes(fwd_slots(B, T), H, DK, DV);
 }
+
+size_t ckda_bwd_varlen_workspace_bytes(int N, int T_total, int H, int DK, int DV) {
+    if (N < 0 || T_total < 0 || H < 0 || !head_ok(DK) || !head_ok(DV)) return 0;
+    return ckda::bwd_workspace_bytes(varlen_slots(N, T_total), H, DK, DV);
+}
+
+namespace {
+
+// shared tail of ckda_bwd / ckda_bwd_varlen: pointer checks, workspace, launch
+ckda_status_t bwd_common(ckda::BwdArgs& a, int nslots, bool any_tokens, const void* workspace,
+                         size_t workspace_bytes, ckda_stream_t stream, const char* what) {
+    if (any_tokens) {
+        CKDA_REQUIRE(a.q); CKDA_REQUIRE(a.k); CKDA_REQUIRE(a.v); CKDA_REQUIRE(a.g); CKDA_REQUIRE(a.s);
+        CKDA_REQUIRE(a.beta); CKDA_REQUIRE(a.h_ckpt); CKDA_REQUIRE(a.dout);
+        CKDA_REQUIRE(a.dq); CKDA_REQUIRE(a.dk); CKDA_REQUIRE(a.dv); CKDA_REQUIRE(a.dg); CKDA_REQUIRE(a.dbeta);
+    }
+    CKDA_ALIGNED(a.q); CKDA_ALIGNED(a.k); CKDA_ALIGNED(a.v); CKDA_ALIGNED(a.g); CKDA_ALIGNED(a.s);
+    CKDA_ALIGNED(a.dout); CKDA_ALIGNED(a.h_ckpt);
+    CKDA_ALIGNED(a.dq); CKDA_ALIGNED(a.dk); CKDA_ALIGNED(a.dv); CKDA_ALIGNED(a.dg);
+    const size_t need = ckda::bwd_workspace_bytes(nslots, a.H, a.DK, a.DV);
+    if (need > 0) {
+        CKDA_REQUIRE(workspace);
+        CKDA_ALIGNED(workspace);
+        if (workspace_bytes < need)
+            return fail(CKDA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+    }
+    a.ws = const_cast<void*>(workspace);
+    return hip_status(ckda::launch_bwd(a, nslots, static_cast<hipStream_t>(stream)), what);
+}
+
+}  // namespace
 
 ckda_status_t ckda_bwd(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype, const void* q,
                        const void* k, const void* v, const float* g, const int8_t* s,
@@ -221,24 +268,35 @@ ckda_status_t ckda_bwd(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtyp
     CKDA_TRY(check_heads(DK, DV));
     if (too_big(static_cast<long long>(B) * T, H)) return fail(CKDA_ERR_UNSUPPORTED, "tensor too large");
     if (B * H == 0) return ok();
-    if (T > 0) {
-        CKDA_REQUIRE(q); CKDA_REQUIRE(k); CKDA_REQUIRE(v); CKDA_REQUIRE(g); CKDA_REQUIRE(s);
-        CKDA_REQUIRE(beta); CKDA_REQUIRE(h_ckpt); CKDA_REQUIRE(dout);
-        CKDA_REQUIRE(dq); CKDA_REQUIRE(dk); CKDA_REQUIRE(dv); CKDA_REQUIRE(dg); CKDA_REQUIRE(dbeta);
-    }
-    CKDA_ALIGNED(q); CKDA_ALIGNED(k); CKDA_ALIGNED(g); CKDA_ALIGNED(s); CKDA_ALIGNED(dout);
-    const size_t need = ckda::bwd_workspace_bytes(B, T, H, DK, DV);
-    if (need > 0) {
-        CKDA_REQUIRE(workspace);
-        if (workspace_bytes < need)
-            return fail(CKDA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
-    }
     ckda::BwdArgs a{};
     a.B = B; a.T = T; a.H = H; a.DK = DK; a.DV = DV; a.bf16 = in_dtype == CKDA_BF16;
     a.q = q; a.k = k; a.v = v; a.g = g; a.s = s; a.beta = beta; a.scale = scale; a.h0 = h0;
     a.h_ckpt = h_ckpt; a.dout = dout; a.dht = dht; a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg;
-    a.dbeta = dbeta; a.dh0 = dh0; a.ws = workspace;
-    return hip_status(ckda::launch_bwd(a, static_cast<hipStream_t>(stream)), "ckda_bwd launch");
+    a.dbeta = dbeta; a.dh0 = dh0; a.cu = nullptr; a.ndocs = 0;
+    return bwd_common(a, fwd_slots(B, T), T > 0, workspace, workspace_bytes, stream, "ckda_bwd launch");
+}
+
+ckda_status_t ckda_bwd_varlen(int N, int T_total, const int32_t* cu, const int32_t* cu_dev, int H,
+                              int DK, int DV, ckda_dtype_t in_dtype, const void* q, const void* k,
+                              const void* v, const float* g, const int8_t* s, const float* beta,
+                              float scale, const float* h0, const float* h_ckpt, const void* dout,
+                              const float* dht, float* dq, float* dk, float* dv, float* dg,
+                              float* dbeta, float* dh0, void* workspace, size_t workspace_bytes,
+                              ckda_stream_t stream) {
+    CKDA_TRY(check_dtype(in_dtype));
+    if (N < 0 || T_total < 0 || H < 0) return fail(CKDA_ERR_SHAPE, "negative size (N=%d, T=%d, H=%d)", N, T_total, H);
+    CKDA_TRY(check_heads(DK, DV));
+    CKDA_TRY(check_varlen_sizes(N, T_total, H));
+    CKDA_TRY(check_cu(N, T_total, cu));
+    if (N * H == 0) return ok();
+    CKDA_REQUIRE(cu_dev);
+    ckda::BwdArgs a{};
+    a.B = 1; a.T = T_total; a.H = H; a.DK = DK; a.DV = DV; a.bf16 = in_dtype == CKDA_BF16;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.s = s; a.beta = beta; a.scale = scale; a.h0 = h0;
+    a.h_ckpt = h_ckpt; a.dout = dout; a.dht = dht; a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg;
+    a.dbeta = dbeta; a.dh0 = dh0; a.cu = cu_dev; a.ndocs = N;
+    return bwd_common(a, varlen_slots(N, T_total), T_total > 0, workspace, workspace_bytes, stream,
+                      "ckda_bwd_varlen launch");
 }
 
 }  // extern "C"

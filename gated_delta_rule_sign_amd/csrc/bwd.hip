@@ -33,6 +33,7 @@
 #include "ckda_device.h"
 #include "ckda_launch.h"
 #include "ckda_mfma.h"
+#include "ckda_record.h"
 
 namespace ckda {
 
@@ -264,18 +265,36 @@ struct BwdParams {
     float scale;
     float *dq, *dk, *dv, *dg, *dbeta, *dh0;
     int B, T, H, NT;
+    const int32_t* cu;   // varlen document starts (device), or nullptr
+    int ndocs;
 };
 
-// chunk-head ch -> (b, h, chunk j, first token, valid tokens)
+// chunk-head ch -> (head, token row of the chunk start, valid tokens).
+// Equal-length: ch = (b H + h) NT + j.  Varlen: ch = slot H + h, chunk j of
+// document d in slot floor(cu[d]/64) + d + j (unused slots have L = 0).
+// Checkpoints and workspace rows are indexed by ch in both modes.
 struct ChunkIdx {
-    int b, h, j, t0, L;
-    __device__ ChunkIdx(int ch, int H, int NT, int T) {
-        j = ch % NT;
-        const int bh = ch / NT;
-        h = bh % H;
-        b = bh / H;
-        t0 = j * 64;
-        L = min(64, T - t0);
+    int h, L;
+    size_t trow0;
+    __device__ ChunkIdx(int ch, const BwdParams& p) {
+        if (p.cu) {
+            const int slot = ch / p.H;
+            h = ch % p.H;
+            int lo = 0, hi = p.ndocs - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (varlen_slot(p.cu[mid], mid, 0) <= slot) lo = mid; else hi = mid - 1;
+            }
+            const int j = slot - varlen_slot(p.cu[lo], lo, 0);
+            const int len = p.cu[lo + 1] - p.cu[lo];
+            trow0 = static_cast<size_t>(__builtin_amdgcn_readfirstlane(p.cu[lo] + 64 * j));
+            L = __builtin_amdgcn_readfirstlane(max(0, min(64, len - 64 * j)));
+        } else {
+            const int j = ch % p.NT, bh = ch / p.NT;
+            h = bh % p.H;
+            trow0 = static_cast<size_t>(bh / p.H) * p.T + 64 * j;
+            L = min(64, p.T - 64 * j);
+        }
     }
 };
 
@@ -327,11 +346,32 @@ __global__ void __launch_bounds__(512) bwd_prep_kernel(BwdParams p, BwdWs W) {
     __shared__ f32x4 segb[SEGS][CQ], segp[SEGS][CQ];
     __shared__ __align__(16) float em_s[DK];
     const int ch = blockIdx.x;
-    const ChunkIdx ci(ch, p.H, p.NT, p.T);
+    const ChunkIdx ci(ch, p);
     const int tid = threadIdx.x, q4 = tid % CQ, seg = tid / CQ, tb = seg * NTOK;
-    const size_t trow0 = static_cast<size_t>(ci.b) * p.T + ci.t0;   // token row of the chunk start
+    const size_t trow0 = ci.trow0;   // token row of the chunk start
     const size_t o64k = static_cast<size_t>(ch) * 64 * DK;
     const size_t o64v = static_cast<size_t>(ch) * 64 * DV;
+    if (ci.L <= 0) {   // unused varlen slot: zero operands, so every later pass stays finite
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        for (int u = tid; u < 16 * DK; u += 512) {
+            reinterpret_cast<f32x4*>(W.K1 + o64k)[u] = z;
+            reinterpret_cast<f32x4*>(W.K2 + o64k)[u] = z;
+            reinterpret_cast<f32x4*>(W.Q1 + o64k)[u] = z;
+            reinterpret_cast<f32x4*>(W.KB + o64k)[u] = z;
+        }
+        for (int u = tid; u < 16 * DV; u += 512) {
+            reinterpret_cast<f32x4*>(W.V + o64v)[u] = z;
+            reinterpret_cast<f32x4*>(W.dO + o64v)[u] = z;
+        }
+        for (int u = tid; u < DK * DV / 4; u += 512) reinterpret_cast<f32x4*>(W.Sp + static_cast<size_t>(ch) * DK * DV)[u] = z;
+        if (tid < 64) W.beta[static_cast<size_t>(ch) * 64 + tid] = 0.f;
+        if (tid < DK) {
+            W.em[static_cast<size_t>(ch) * DK + tid] = 1.f;
+            W.gC[static_cast<size_t>(ch) * DK + tid] = 1.f;
+            W.pC[static_cast<size_t>(ch) * DK + tid] = 1.f;
+        }
+        return;
+    }
     const Tin* qp = static_cast<const Tin*>(p.q);
     const Tin* kp = static_cast<const Tin*>(p.k);
     f32x4 gv[NTOK], sg[NTOK], kv[NTOK], qv[NTOK];
@@ -531,18 +571,30 @@ __global__ void __launch_bounds__(512) bwd_reverse_kernel(BwdParams p, BwdWs W) 
     float* const ems = pCs + DK;
     float* const gCs = ems + DK;
 
-    const int bh = blockIdx.x / SH::NSL;
+    const int bh = blockIdx.x / SH::NSL;   // chain: b H + h, or (varlen) document H + h
     const int v0 = (blockIdx.x % SH::NSL) * BV;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63, n = l & 15, g = l >> 4;
-    const int NT = p.NT;
+    // the chain's chunks: chunk j is chunk-head chj(j)
+    int NT, slot0 = 0;
+    if (p.cu) {
+        const int d = bh / p.H;
+        NT = __builtin_amdgcn_readfirstlane((p.cu[d + 1] - p.cu[d] + 63) / 64);
+        slot0 = __builtin_amdgcn_readfirstlane(varlen_slot(p.cu[d], d, 0));
+    } else {
+        NT = p.NT;
+    }
+    const int hh = bh % p.H;
+    auto chj = [&](int j) -> size_t {
+        return p.cu ? static_cast<size_t>(slot0 + j) * p.H + hh : static_cast<size_t>(bh) * NT + j;
+    };
 
     // ---- register staging ---------------------------------------------------
     f32x4 rM[NM], rT[NM], rKB[NKB], rDO[NDO], rSM;
     f32x4 rQ[NKB], rK[NKB];
     auto load1 = [&](int j) {   // M, T, KB, dO slice, pC / em / gC of chunk j
-        const size_t ch = static_cast<size_t>(bh) * NT + j;
+        const size_t ch = chj(j);
         const f32x4* M4 = reinterpret_cast<const f32x4*>(W.M + ch * 4096);
         const f32x4* T4 = reinterpret_cast<const f32x4*>(W.T + ch * 4096);
         const f32x4* KB4 = reinterpret_cast<const f32x4*>(W.KB + ch * 64 * DK);
@@ -580,7 +632,7 @@ __global__ void __launch_bounds__(512) bwd_reverse_kernel(BwdParams p, BwdWs W) 
         if (tid < 3 * (DK / 4)) *reinterpret_cast<f32x4*>(pCs + 4 * tid) = rSM;
     };
     auto load2 = [&](int j) {   // Q1, K1 of chunk j
-        const size_t ch = static_cast<size_t>(bh) * NT + j;
+        const size_t ch = chj(j);
         const f32x4* Q4 = reinterpret_cast<const f32x4*>(W.Q1 + ch * 64 * DK);
         const f32x4* K4 = reinterpret_cast<const f32x4*>(W.K1 + ch * 64 * DK);
 #pragma unroll
@@ -605,11 +657,13 @@ __global__ void __launch_bounds__(512) bwd_reverse_kernel(BwdParams p, BwdWs W) 
         const int c = e / BV, v = e % BV;
         Gs[c * PV + v] = p.dht ? p.dht[(static_cast<size_t>(bh) * DK + c) * DV + v0 + v] : 0.f;
     }
-    load1(NT - 1);
-    store1();
+    if (NT > 0) {   // (an empty document has no chunks: dh0 = dht)
+        load1(NT - 1);
+        store1();
+    }
     __syncthreads();
     for (int j = NT - 1; j >= 0; --j) {
-        const size_t ch = static_cast<size_t>(bh) * NT + j;
+        const size_t ch = chj(j);
         load2(j);
         // dSt = Diag(pC) G to the workspace (slice columns)
         for (int e = tid; e < DK * (BV / 4); e += 512) {
@@ -737,7 +791,8 @@ static hipError_t launch_reverse_t(const BwdParams& p, const BwdWs& W, hipStream
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, SH::BYTES);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(p.B * p.H * SH::NSL), dim3(512), SH::BYTES, st, p, W);
+    const int nchains = (p.cu ? p.ndocs : p.B) * p.H;
+    hipLaunchKernelGGL(kern, dim3(nchains * SH::NSL), dim3(512), SH::BYTES, st, p, W);
     return hipGetLastError();
 }
 
@@ -826,9 +881,10 @@ __global__ void __launch_bounds__(final_threads<DK>()) bwd_final_kernel(BwdParam
     f32x4 (&segdb)[SEGS][CQ] = segb;
     f32x4 (&segkb)[SEGS][CQ] = segp;
     const int ch = blockIdx.x;
-    const ChunkIdx ci(ch, p.H, p.NT, p.T);
+    const ChunkIdx ci(ch, p);
+    if (ci.L <= 0) return;   // unused varlen slot
     const int tid = threadIdx.x, q4 = tid % CQ, seg = tid / CQ, tb = seg * NTOK;
-    const size_t trow0 = static_cast<size_t>(ci.b) * p.T + ci.t0;
+    const size_t trow0 = ci.trow0;
     const size_t o64k = static_cast<size_t>(ch) * 64 * DK;
     const size_t o64v = static_cast<size_t>(ch) * 64 * DV;
     f32x4 gv[NTOK], sg[NTOK], kv[NTOK], qv[NTOK], dq1[NTOK], dk1[NTOK], dk2[NTOK], dkb[NTOK];
@@ -979,23 +1035,23 @@ static hipError_t launch_chunk_pass(bool bf16, bool final_pass, const BwdParams&
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int B, int T, int H, int DK, int DV) {
-    const size_t NC = static_cast<size_t>(B) * H * ((T + 63) / 64);
-    return BwdWs::floats(NC, DK, DV) * sizeof(float);
+size_t bwd_workspace_bytes(int nslots, int H, int DK, int DV) {
+    return BwdWs::floats(static_cast<size_t>(nslots) * H, DK, DV) * sizeof(float);
 }
 
-hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
+hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t st) {
     const int NT = (a.T + 63) / 64;
-    const int NC = a.B * a.H * NT;
+    const int NC = nslots * a.H;
+    const int nchains = (a.cu ? a.ndocs : a.B) * a.H;
     const int DK = a.DK, DV = a.DV;
     BwdParams p{};
     p.q = a.q; p.k = a.k; p.v = a.v; p.dout = a.dout; p.g = a.g; p.beta = a.beta; p.s = a.s;
     p.h_ckpt = a.h_ckpt; p.dht = a.dht; p.h0 = a.h0; p.scale = a.scale;
     p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dg = a.dg; p.dbeta = a.dbeta; p.dh0 = a.dh0;
-    p.B = a.B; p.T = a.T; p.H = a.H; p.NT = NT;
+    p.B = a.B; p.T = a.T; p.H = a.H; p.NT = NT; p.cu = a.cu; p.ndocs = a.ndocs;
     if (NC == 0) {
         // no tokens: dh0 = dht (or 0)
-        const size_t n = static_cast<size_t>(a.B) * a.H * DK * DV;
+        const size_t n = static_cast<size_t>(nchains) * DK * DV;
         if (a.dh0 && n > 0) {
             hipLaunchKernelGGL(fill_copy_kernel, dim3(static_cast<unsigned>((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096)),
                                dim3(256), 0, st, a.dh0, a.dht, n);

@@ -71,9 +71,14 @@ struct BwdArgs {
     const void* dout;
     const float* dht;
     float *dq, *dk, *dv, *dg, *dbeta, *dh0;
+    // varlen: as in FwdArgs (documents from cu, h0 / dht / dh0 per document,
+    // checkpoints per chunk slot); nullptr selects the equal-length mode
+    const int32_t* cu;
+    int ndocs;
     void* ws;
 };
-size_t bwd_workspace_bytes(int B, int T, int H, int DK, int DV);
-hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+// nslots: chunk slots, as for the forward
+size_t bwd_workspace_bytes(int nslots, int H, int DK, int DV);
+hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t stream);
 
 }  // namespace ckda

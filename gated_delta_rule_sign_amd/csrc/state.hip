@@ -274,8 +274,10 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
 #pragma unroll
             for (int J = 0; J < 4; ++J) u[J] = *reinterpret_cast<const f32x4*>(sm + SH::L_U + ((J * NWC + wt) * 64 + l) * 16);
             if (CKPT) {   // the state at the chunk start (waves without columns store nothing)
-                const float* hc = p.h_ckpt + (static_cast<size_t>(sidx) * H + h) * static_cast<size_t>(nchunks) * DK * DV +
-                                  static_cast<size_t>(j) * DK * DV;
+                // equal-length: [B,H,NT,DK,DV]; varlen: [slot][H][DK][DV] (the record's slot)
+                const size_t ci = p.cu ? static_cast<size_t>(slot0 + j) * H + h
+                                       : (static_cast<size_t>(sidx) * H + h) * static_cast<size_t>(nchunks) + j;
+                const float* hc = p.h_ckpt + ci * DK * DV;
                 const __amdgpu_buffer_rsrc_t hrc = buffer_rsrc(hc, has_col ? DK * DV * 4 : 0);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define CKDA_ABI_VERSION 2
+#define CKDA_ABI_VERSION 3
 
 typedef enum {
     CKDA_OK = 0,
@@ -124,15 +124,21 @@ ckda_status_t ckda_fwd_chunked(int B, int T, int H, int DK, int DV, ckda_dtype_t
  *   q, k, g, s: [T_total,H,DK]; v, o: [T_total,H,DV]; beta: [T_total,H]
  *   h0, ht: [N,H,DK,DV] f32, each nullable.  Documents may be empty (their
  *   ht is their h0, or zero).
+ *   h_ckpt: nullable; else [ckda_varlen_chunk_slots(N, T_total), H, DK, DV]
+ *           f32 receiving the true-frame state at the start of every chunk:
+ *           chunk j of document n (tokens cu[n] + 64j ..) is chunk slot
+ *           floor(cu[n] / 64) + n + j.  Slots no chunk maps to are not
+ *           written.  (Checkpoints for ckda_bwd_varlen.)
  *   workspace: at least ckda_fwd_varlen_workspace_bytes(N, T_total, H, DK,
  *   DV, in_dtype) bytes, as for ckda_fwd_chunked.
  * ---------------------------------------------------------------------- */
+int ckda_varlen_chunk_slots(int N, int T_total);
 size_t ckda_fwd_varlen_workspace_bytes(int N, int T_total, int H, int DK, int DV, ckda_dtype_t in_dtype);
 ckda_status_t ckda_fwd_varlen(int N, int T_total, const int32_t* cu_seqlens_host,
                               const int32_t* cu_seqlens_dev, int H, int DK, int DV,
                               ckda_dtype_t in_dtype, const void* q, const void* k, const void* v,
                               const float* g, const int8_t* s, const float* beta, float scale,
-                              const float* h0, float* o, float* ht, void* workspace,
+                              const float* h0, float* o, float* ht, float* h_ckpt, void* workspace,
                               size_t workspace_bytes, ckda_stream_t stream);
 
 /* ------------------------------------------------------------------------
@@ -169,6 +175,28 @@ ckda_status_t ckda_bwd(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtyp
                        const float* h_ckpt, const void* dout, const float* dht,
                        float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0,
                        void* workspace, size_t workspace_bytes, ckda_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Backward of the varlen forward: per document n, gradients of
+ * <do, o> + <dht[n], ht[n]> with documents as independent sequences.
+ *   cu_seqlens_host / _dev, q .. beta, scale: as in ckda_fwd_varlen
+ *   h_ckpt: the per-chunk-slot checkpoints ckda_fwd_varlen wrote on the same
+ *           inputs (required when T_total > 0)
+ *   dout: [T_total,H,DV] in_dtype;  dht: [N,H,DK,DV] f32 or NULL (zero)
+ *   dq, dk, dg: [T_total,H,DK] f32;  dv: [T_total,H,DV];  dbeta: [T_total,H]
+ *   dh0: [N,H,DK,DV] f32 or NULL
+ *   workspace: ckda_bwd_varlen_workspace_bytes(...) bytes of device memory
+ * Conventions and errors as for ckda_bwd and ckda_fwd_varlen.
+ * ---------------------------------------------------------------------- */
+size_t ckda_bwd_varlen_workspace_bytes(int N, int T_total, int H, int DK, int DV);
+ckda_status_t ckda_bwd_varlen(int N, int T_total, const int32_t* cu_seqlens_host,
+                              const int32_t* cu_seqlens_dev, int H, int DK, int DV,
+                              ckda_dtype_t in_dtype, const void* q, const void* k, const void* v,
+                              const float* g, const int8_t* s, const float* beta, float scale,
+                              const float* h0, const float* h_ckpt, const void* dout,
+                              const float* dht, float* dq, float* dk, float* dv, float* dg,
+                              float* dbeta, float* dh0, void* workspace, size_t workspace_bytes,
+                              ckda_stream_t stream);
 
 #ifdef __cplusplus
 }

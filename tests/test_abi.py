@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.ckda_abi_version() == 2
+    assert L.ckda_abi_version() == 3
     assert L.ckda_status_string(0) == b"ok"
     for st in range(1, 8):
         assert L.ckda_status_string(st) not in (b"ok", b"unknown status")
@@ -84,12 +84,40 @@ def test_varlen_rejects_bad_cu_seqlens(L):
     def call(cu, N, Tt):
         arr = (ctypes.c_int32 * len(cu))(*cu)
         return L.ckda_fwd_varlen(N, Tt, arr, FAKE, 1, 32, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                 ctypes.c_float(1.0), None, FAKE, None, FAKE, ctypes.c_size_t(BIG), None)
+                                 ctypes.c_float(1.0), None, FAKE, None, None, FAKE, ctypes.c_size_t(BIG), None)
     assert call([1, 5], 1, 5) == 5              # does not start at 0
     assert call([0, 5, 3], 2, 3) == 5           # decreasing
     assert call([0, 5, 9], 2, 10) == 5          # does not end at T_total
     assert L.ckda_fwd_varlen(2, 4, None, FAKE, 1, 32, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                             ctypes.c_float(1.0), None, FAKE, None, FAKE, ctypes.c_size_t(BIG), None) == 1
+                             ctypes.c_float(1.0), None, FAKE, None, None, FAKE, ctypes.c_size_t(BIG), None) == 1
+
+
+def bwd_varlen(L, cu, N, Tt, DK=32, DV=32, dt=0, ws=FAKE, wsb=BIG, q=FAKE, hc=FAKE):
+    arr = None if cu is None else (ctypes.c_int32 * len(cu))(*cu)
+    f = ctypes.c_float(1.0)
+    return L.ckda_bwd_varlen(N, Tt, arr, FAKE, 1, DK, DV, dt, q, FAKE, FAKE, FAKE, FAKE, FAKE, f, None,
+                             hc, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, ws, ctypes.c_size_t(wsb), None)
+
+
+def test_varlen_backward_boundary(L):
+    # chunk slots: ceil(T_total / 64) + N; one workspace block per (slot, head)
+    assert L.ckda_varlen_chunk_slots(3, 100) == 2 + 3
+    assert L.ckda_varlen_chunk_slots(-1, 100) == 0
+    one = L.ckda_bwd_workspace_bytes(1, 64, 1, 64, 32)           # one chunk-head
+    assert one > 0
+    assert L.ckda_bwd_varlen_workspace_bytes(3, 100, 2, 64, 32) == (2 + 3) * 2 * one
+    assert L.ckda_bwd_varlen_workspace_bytes(3, 100, 2, 48, 32) == 0
+    assert bwd_varlen(L, [1, 5], 1, 5) == 5                       # does not start at 0
+    assert bwd_varlen(L, [0, 5, 3], 2, 3) == 5                    # decreasing
+    assert bwd_varlen(L, None, 2, 4) == 1
+    assert bwd_varlen(L, [0, 5], 1, 5, DK=96) == 4
+    assert bwd_varlen(L, [0, 5], 1, 5, dt=9) == 3
+    assert bwd_varlen(L, [0, 5], 1, 5, hc=None) == 1              # checkpoints required
+    assert b"h_ckpt" in L.ckda_last_error()
+    assert bwd_varlen(L, [0, 5], 1, 5, q=P(0x1004)) == 4          # misaligned
+    need = L.ckda_bwd_varlen_workspace_bytes(1, 5, 1, 32, 32)
+    assert bwd_varlen(L, [0, 5], 1, 5, wsb=need - 16) == 6
+    assert bwd_varlen(L, [0], 0, 0) == 0                          # no documents
 
 
 def test_decode_and_bwd_reject_bad_arguments(L):
