@@ -52,22 +52,22 @@ def lib() -> ctypes.CDLL:
     L.ckda_fwd_workspace_bytes.restype = S
     L.ckda_fwd_varlen_workspace_bytes.argtypes = [I, I, I, I, I, I]
     L.ckda_fwd_varlen_workspace_bytes.restype = S
-    L.ckda_fwd_chunked.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P, P, S, P]
+    L.ckda_fwd_chunked.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P, P, S, P]
     L.ckda_fwd_chunked.restype = I
-    L.ckda_fwd_varlen.argtypes = [I, I, P, P, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P, P, S, P]
+    L.ckda_fwd_varlen.argtypes = [I, I, P, P, I, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P, P, S, P]
     L.ckda_fwd_varlen.restype = I
     L.ckda_varlen_chunk_slots.argtypes = [I, I]
     L.ckda_varlen_chunk_slots.restype = I
-    L.ckda_decode_step.argtypes = [I, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P]
+    L.ckda_decode_step.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P]
     L.ckda_decode_step.restype = I
     L.ckda_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
     L.ckda_bwd_workspace_bytes.restype = S
-    L.ckda_bwd.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P,
+    L.ckda_bwd.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P,
                            P, P, P, P, P, P, P, S, P]
     L.ckda_bwd.restype = I
     L.ckda_bwd_varlen_workspace_bytes.argtypes = [I, I, I, I, I]
     L.ckda_bwd_varlen_workspace_bytes.restype = S
-    L.ckda_bwd_varlen.argtypes = [I, I, P, P, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P,
+    L.ckda_bwd_varlen.argtypes = [I, I, P, P, I, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P,
                                   P, P, P, P, P, P, P, S, P]
     L.ckda_bwd_varlen.restype = I
     _lib = L
@@ -113,6 +113,14 @@ def _need(t: Optional[torch.Tensor], name: str, dtype=None, shape=None, device=N
         raise CkdaError(f"{name} must be contiguous")
 
 
+CKDA_GATE_CHANNEL, CKDA_GATE_HEAD = 0, 1
+
+
+def _gate_code(g, lead) -> int:
+    """CKDA_GATE_HEAD when g is [.., H] (one gate per head), else per channel."""
+    return CKDA_GATE_HEAD if g.dim() == len(lead) + 1 else CKDA_GATE_CHANNEL
+
+
 def _token_inputs(q, k, v, g, s, beta, lead):
     dt = q.dtype
     DK, DV = q.shape[-1], v.shape[-1]
@@ -121,8 +129,10 @@ def _token_inputs(q, k, v, g, s, beta, lead):
     _need(q, "q", dt, lead + (H, DK))
     _need(k, "k", dt, lead + (H, DK), dev)
     _need(v, "v", dt, lead + (H, DV), dev)
-    _need(g, "g", torch.float32, lead + (H, DK), dev)
-    _need(s, "s", torch.int8, lead + (H, DK), dev)
+    # gate layout from g's shape: [.., H, DK] per channel, [.., H] per head
+    gshape = lead + (H,) if g is not None and g.dim() == len(lead) + 1 else lead + (H, DK)
+    _need(g, "g", torch.float32, gshape, dev)
+    _need(s, "s", torch.int8, gshape, dev)
     _need(beta, "beta", torch.float32, lead + (H,), dev)
     return _dtype_code(q), H, DK, DV, dev
 
@@ -182,7 +192,7 @@ def fwd(q, k, v, g, s, beta, scale: float = 1.0, h0=None, want_ht: bool = True,
         h_ckpt = torch.empty((B, H, NT, DK, DV), dtype=torch.float32, device=dev)
     _need(h_ckpt, "h_ckpt", torch.float32, (B, H, NT, DK, DV), dev)
     workspace, wsb = _workspace(workspace, fwd_workspace_bytes(B, T, H, DK, DV, q.dtype), dev)
-    _check(lib().ckda_fwd_chunked(B, T, H, DK, DV, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
+    _check(lib().ckda_fwd_chunked(B, T, H, DK, DV, dt, _gate_code(g, (B, T)), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
                                   _ptr(beta), float(scale), _ptr(h0), _ptr(o), _ptr(ht),
                                   _ptr(h_ckpt), _ptr(workspace), wsb, _stream()))
     return o, ht, h_ckpt
@@ -221,7 +231,7 @@ def fwd_varlen(q, k, v, g, s, beta, cu_seqlens, scale: float = 1.0, h0=None,
     if want_ckpt:
         hc = torch.empty((varlen_chunk_slots(N, Tt), H, DK, DV), dtype=torch.float32, device=dev)
     workspace, wsb = _workspace(workspace, fwd_varlen_workspace_bytes(N, Tt, H, DK, DV, q.dtype), dev)
-    _check(lib().ckda_fwd_varlen(N, Tt, _ptr(cu), _ptr(cu_seqlens_dev), H, DK, DV, dt, _ptr(q),
+    _check(lib().ckda_fwd_varlen(N, Tt, _ptr(cu), _ptr(cu_seqlens_dev), H, DK, DV, dt, _gate_code(g, (Tt,)), _ptr(q),
                                  _ptr(k), _ptr(v), _ptr(g), _ptr(s), _ptr(beta), float(scale),
                                  _ptr(h0), _ptr(o), _ptr(ht), _ptr(hc), _ptr(workspace), wsb, _stream()))
     return (o, ht, hc) if want_ckpt else (o, ht)
@@ -237,7 +247,7 @@ def decode_step(q, k, v, g, s, beta, state, sign_prod, scale: float = 1.0, o=Non
     if o is None:
         o = torch.empty((N, H, DV), dtype=torch.float32, device=dev)
     _need(o, "o", torch.float32, (N, H, DV), dev)
-    _check(lib().ckda_decode_step(N, H, DK, DV, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
+    _check(lib().ckda_decode_step(N, H, DK, DV, dt, _gate_code(g, (N,)), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
                                   _ptr(beta), float(scale), _ptr(state), _ptr(sign_prod), _ptr(o),
                                   _stream()))
     return o
@@ -258,15 +268,16 @@ def bwd(q, k, v, g, s, beta, h_ckpt, do, scale: float = 1.0, h0=None, dht=None,
     _need(h0, "h0", torch.float32, (B, H, DK, DV), dev)
     _need(dht, "dht", torch.float32, (B, H, DK, DV), dev)
     f32 = dict(dtype=torch.float32, device=dev)
+    gsh = (B, T, H) if _gate_code(g, (B, T)) == CKDA_GATE_HEAD else (B, T, H, DK)
     out = dict(dq=torch.empty((B, T, H, DK), **f32), dk=torch.empty((B, T, H, DK), **f32),
-               dv=torch.empty((B, T, H, DV), **f32), dg=torch.empty((B, T, H, DK), **f32),
+               dv=torch.empty((B, T, H, DV), **f32), dg=torch.empty(gsh, **f32),
                dbeta=torch.empty((B, T, H), **f32),
                dh0=torch.empty((B, H, DK, DV), **f32) if want_dh0 else None)
     need = bwd_workspace_bytes(B, T, H, DK, DV)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().ckda_bwd(B, T, H, DK, DV, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
+    _check(lib().ckda_bwd(B, T, H, DK, DV, dt, _gate_code(g, (B, T)), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
                           _ptr(beta), float(scale), _ptr(h0), _ptr(h_ckpt), _ptr(do), _ptr(dht),
                           _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
                           _ptr(out["dbeta"]), _ptr(out["dh0"]), _ptr(workspace), wsb, _stream()))
@@ -300,12 +311,13 @@ def bwd_varlen(q, k, v, g, s, beta, cu_seqlens, h_ckpt, do, scale: float = 1.0, 
     _need(h0, "h0", torch.float32, (N, H, DK, DV), dev)
     _need(dht, "dht", torch.float32, (N, H, DK, DV), dev)
     f32 = dict(dtype=torch.float32, device=dev)
+    gsh = (Tt, H) if _gate_code(g, (Tt,)) == CKDA_GATE_HEAD else (Tt, H, DK)
     out = dict(dq=torch.empty((Tt, H, DK), **f32), dk=torch.empty((Tt, H, DK), **f32),
-               dv=torch.empty((Tt, H, DV), **f32), dg=torch.empty((Tt, H, DK), **f32),
+               dv=torch.empty((Tt, H, DV), **f32), dg=torch.empty(gsh, **f32),
                dbeta=torch.empty((Tt, H), **f32),
                dh0=torch.empty((N, H, DK, DV), **f32) if want_dh0 else None)
     workspace, wsb = _workspace(workspace, bwd_varlen_workspace_bytes(N, Tt, H, DK, DV), dev)
-    _check(lib().ckda_bwd_varlen(N, Tt, _ptr(cu), _ptr(cu_seqlens_dev), H, DK, DV, dt, _ptr(q),
+    _check(lib().ckda_bwd_varlen(N, Tt, _ptr(cu), _ptr(cu_seqlens_dev), H, DK, DV, dt, _gate_code(g, (Tt,)), _ptr(q),
                                  _ptr(k), _ptr(v), _ptr(g), _ptr(s), _ptr(beta), float(scale),
                                  _ptr(h0), _ptr(h_ckpt), _ptr(do), _ptr(dht), _ptr(out["dq"]),
                                  _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),

@@ -267,6 +267,7 @@ struct BwdParams {
     int B, T, H, NT;
     const int32_t* cu;   // varlen document starts (device), or nullptr
     int ndocs;
+    bool head_gate;      // g, s, dg per (token, head)
 };
 
 // chunk-head ch -> (head, token row of the chunk start, valid tokens).
@@ -330,13 +331,30 @@ __device__ __forceinline__ f32x4 signs_quad(const int8_t* p, size_t e) {
     return f32x4{static_cast<float>(static_cast<int8_t>(u)), static_cast<float>(static_cast<int8_t>(u >> 8)),
                  static_cast<float>(static_cast<int8_t>(u >> 16)), static_cast<float>(static_cast<int8_t>(u >> 24))};
 }
+// g and s of token row `row` (chunk token t), channels 4 q4 .. +3: per channel,
+// or (HG) the head's one gate broadcast
+template <bool HG>
+__device__ __forceinline__ void gate_quad(const BwdParams& p, size_t row, int h, int DK, int q4, f32x4& gq,
+                                          f32x4& sq) {
+    if constexpr (HG) {
+        const size_t e = row * p.H + h;
+        const float gt = p.g[e], st = static_cast<float>(p.s[e]);
+        gq = f32x4{gt, gt, gt, gt};
+        sq = f32x4{st, st, st, st};
+    } else {
+        const size_t e = (row * p.H + h) * DK + 4 * q4;
+        gq = *reinterpret_cast<const f32x4*>(p.g + e);
+        sq = signs_quad(p.s, e);
+    }
+}
+
 __device__ __forceinline__ f32x4 exp2c4(f32x4 x) {
     return f32x4{exp2_clamped(x[0]), exp2_clamped(x[1]), exp2_clamped(x[2]), exp2_clamped(x[3])};
 }
 
 // prep: cumulative gate and sign product, anchored operands, V / dO copies
 // and S' = Diag(e^m) S
-template <typename Tin, int DK, int DV>
+template <typename Tin, int DK, int DV, bool HG>
 __global__ void __launch_bounds__(512) bwd_prep_kernel(BwdParams p, BwdWs W) {
     using QS = QuadSeg<DK, 512>;
     using QV = QuadSeg<DV, 512>;
@@ -377,9 +395,9 @@ __global__ void __launch_bounds__(512) bwd_prep_kernel(BwdParams p, BwdWs W) {
     f32x4 gv[NTOK], sg[NTOK], kv[NTOK], qv[NTOK];
 #pragma unroll
     for (int i = 0; i < NTOK; ++i) {
-        const size_t e = ((trow0 + min(tb + i, ci.L - 1)) * p.H + ci.h) * DK + 4 * q4;
-        gv[i] = *reinterpret_cast<const f32x4*>(p.g + e);
-        sg[i] = signs_quad(p.s, e);
+        const size_t row = trow0 + min(tb + i, ci.L - 1);
+        const size_t e = (row * p.H + ci.h) * DK + 4 * q4;
+        gate_quad<HG>(p, row, ci.h, DK, q4, gv[i], sg[i]);
         kv[i] = load_quad(kp, e);
         qv[i] = load_quad(qp, e);
     }
@@ -870,7 +888,7 @@ __global__ void __launch_bounds__(256) bwd_dA_kernel(BwdWs W) {
 // scans as the prep).
 template <int DK> constexpr int final_threads() { return 512; }   // the prep's segmentation: identical b
 
-template <typename Tin, int DK, int DV>
+template <typename Tin, int DK, int DV, bool HG>
 __global__ void __launch_bounds__(final_threads<DK>()) bwd_final_kernel(BwdParams p, BwdWs W) {
     constexpr int NTHR = final_threads<DK>();
     using QS = QuadSeg<DK, NTHR>;
@@ -890,9 +908,9 @@ __global__ void __launch_bounds__(final_threads<DK>()) bwd_final_kernel(BwdParam
     f32x4 gv[NTOK], sg[NTOK], kv[NTOK], qv[NTOK], dq1[NTOK], dk1[NTOK], dk2[NTOK], dkb[NTOK];
 #pragma unroll
     for (int i = 0; i < NTOK; ++i) {
-        const size_t e = ((trow0 + min(tb + i, ci.L - 1)) * p.H + ci.h) * DK + 4 * q4;
-        gv[i] = *reinterpret_cast<const f32x4*>(p.g + e);
-        sg[i] = signs_quad(p.s, e);
+        const size_t row = trow0 + min(tb + i, ci.L - 1);
+        const size_t e = (row * p.H + ci.h) * DK + 4 * q4;
+        gate_quad<HG>(p, row, ci.h, DK, q4, gv[i], sg[i]);
         kv[i] = load_quad(static_cast<const Tin*>(p.k), e);
         qv[i] = load_quad(static_cast<const Tin*>(p.q), e);
         const size_t o = o64k + static_cast<size_t>(tb + i) * DK + 4 * q4;
@@ -986,9 +1004,15 @@ __global__ void __launch_bounds__(final_threads<DK>()) bwd_final_kernel(BwdParam
 #pragma unroll
     for (int i = 0; i < NTOK; ++i) {
         const int t = tb + i;
-        if (t < ci.L) {
+        const f32x4 dgv = dbv[i] + later + extra;
+        if constexpr (HG) {   // the head's gate: the sum over its channels
+            float x = dgv[0] + dgv[1] + dgv[2] + dgv[3];
+#pragma unroll
+            for (int o = 1; o < CQ; o <<= 1) x += __shfl_xor(x, o, 64);   // the row's quads are adjacent lanes
+            if (q4 == 0 && t < ci.L) p.dg[(trow0 + t) * p.H + ci.h] = x;
+        } else if (t < ci.L) {
             const size_t e = ((trow0 + t) * p.H + ci.h) * DK + 4 * q4;
-            *reinterpret_cast<f32x4*>(p.dg + e) = dbv[i] + later + extra;
+            *reinterpret_cast<f32x4*>(p.dg + e) = dgv;
         }
     }
     for (int u = tid; u < 64 * (DV / 4); u += NTHR) {
@@ -1010,13 +1034,20 @@ __global__ void fill_copy_kernel(float* dst, const float* src, size_t n) {
         dst[i] = src ? src[i] : 0.f;
 }
 
+template <typename Tin, int DK, int DV, bool HG>
+static hipError_t launch_chunk_pass_hg(bool final_pass, const BwdParams& p, const BwdWs& W, int NC,
+                                       hipStream_t st) {
+    if (final_pass)
+        hipLaunchKernelGGL((bwd_final_kernel<Tin, DK, DV, HG>), dim3(NC), dim3(final_threads<DK>()), 0, st, p, W);
+    else
+        hipLaunchKernelGGL((bwd_prep_kernel<Tin, DK, DV, HG>), dim3(NC), dim3(512), 0, st, p, W);
+    return hipGetLastError();
+}
+
 template <typename Tin, int DK, int DV>
 static hipError_t launch_chunk_pass_t(bool final_pass, const BwdParams& p, const BwdWs& W, int NC, hipStream_t st) {
-    if (final_pass)
-        hipLaunchKernelGGL((bwd_final_kernel<Tin, DK, DV>), dim3(NC), dim3(final_threads<DK>()), 0, st, p, W);
-    else
-        hipLaunchKernelGGL((bwd_prep_kernel<Tin, DK, DV>), dim3(NC), dim3(512), 0, st, p, W);
-    return hipGetLastError();
+    return p.head_gate ? launch_chunk_pass_hg<Tin, DK, DV, true>(final_pass, p, W, NC, st)
+                       : launch_chunk_pass_hg<Tin, DK, DV, false>(final_pass, p, W, NC, st);
 }
 
 // the prep (final_pass false) or final pass over every chunk-head
@@ -1048,7 +1079,7 @@ hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t st) {
     p.q = a.q; p.k = a.k; p.v = a.v; p.dout = a.dout; p.g = a.g; p.beta = a.beta; p.s = a.s;
     p.h_ckpt = a.h_ckpt; p.dht = a.dht; p.h0 = a.h0; p.scale = a.scale;
     p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dg = a.dg; p.dbeta = a.dbeta; p.dh0 = a.dh0;
-    p.B = a.B; p.T = a.T; p.H = a.H; p.NT = NT; p.cu = a.cu; p.ndocs = a.ndocs;
+    p.B = a.B; p.T = a.T; p.H = a.H; p.NT = NT; p.cu = a.cu; p.ndocs = a.ndocs; p.head_gate = a.head_gate;
     if (NC == 0) {
         // no tokens: dh0 = dht (or 0)
         const size_t n = static_cast<size_t>(nchains) * DK * DV;

@@ -92,7 +92,8 @@ struct ChunkParams {
     int T, H, ndocs;
 };
 
-template <typename Tin, int DK, int DV>
+// HG: one gate per (token, head) (g, s [.., H]), broadcast over the channels
+template <typename Tin, int DK, int DV, bool HG>
 // second bound: waves per SIMD (two 8-wave workgroups per CU -> 4, at most 128 VGPRs)
 __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(ChunkParams p)
 {
@@ -158,13 +159,22 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
             const size_t base = trow * DK + c0;
             q8[ks].load(q + base);
             k8[ks].load(k + base);
-            const float4 a = reinterpret_cast<const float4*>(p.g + base)[0];
-            const float4 b = reinterpret_cast<const float4*>(p.g + base)[1];
-            const uint2 sv = *reinterpret_cast<const uint2*>(p.s + base);
-            bs[8 * ks + 0] = a.x; bs[8 * ks + 1] = a.y; bs[8 * ks + 2] = a.z; bs[8 * ks + 3] = a.w;
-            bs[8 * ks + 4] = b.x; bs[8 * ks + 5] = b.y; bs[8 * ks + 6] = b.z; bs[8 * ks + 7] = b.w;
-            par[2 * ks] = sv.x;
-            par[2 * ks + 1] = sv.y;
+            if constexpr (HG) {
+                const float gt = p.g[trow];
+                const uint32_t sw = static_cast<uint32_t>(static_cast<uint8_t>(p.s[trow])) * 0x01010101u;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) bs[8 * ks + e] = gt;
+                par[2 * ks] = sw;
+                par[2 * ks + 1] = sw;
+            } else {
+                const float4 a = reinterpret_cast<const float4*>(p.g + base)[0];
+                const float4 b = reinterpret_cast<const float4*>(p.g + base)[1];
+                const uint2 sv = *reinterpret_cast<const uint2*>(p.s + base);
+                bs[8 * ks + 0] = a.x; bs[8 * ks + 1] = a.y; bs[8 * ks + 2] = a.z; bs[8 * ks + 3] = a.w;
+                bs[8 * ks + 4] = b.x; bs[8 * ks + 5] = b.y; bs[8 * ks + 6] = b.z; bs[8 * ks + 7] = b.w;
+                par[2 * ks] = sv.x;
+                par[2 * ks + 1] = sv.y;
+            }
             if (!valid) {
                 q8[ks].zero();
                 k8[ks].zero();
@@ -481,7 +491,7 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
     }
 }
 
-template <typename Tin, int DK, int DV>
+template <typename Tin, int DK, int DV, bool HG>
 static hipError_t launch_chunk_t(const FwdArgs& A, int nslots, hipStream_t stream) {
     using SH = ChunkShape<DK>;
     ChunkParams p;
@@ -489,7 +499,7 @@ static hipError_t launch_chunk_t(const FwdArgs& A, int nslots, hipStream_t strea
     p.ws = static_cast<unsigned char*>(A.ws); p.cu = A.cu; p.T = A.T; p.H = A.H; p.ndocs = A.ndocs;
     const long long grid = static_cast<long long>(nslots) * A.H;
     if (grid == 0) return hipSuccess;
-    auto kern = ckda_chunk_kernel<Tin, DK, DV>;
+    auto kern = ckda_chunk_kernel<Tin, DK, DV, HG>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, SH::LDS);
     if (e != hipSuccess) return e;
@@ -499,8 +509,10 @@ static hipError_t launch_chunk_t(const FwdArgs& A, int nslots, hipStream_t strea
 
 template <typename Tin>
 static hipError_t launch_chunk_dt(const FwdArgs& A, int nslots, hipStream_t stream) {
-#define CKDA_CHUNK(DK_, DV_) \
-    if (A.DK == DK_ && A.DV == DV_) return launch_chunk_t<Tin, DK_, DV_>(A, nslots, stream);
+#define CKDA_CHUNK(DK_, DV_)                                                                      \
+    if (A.DK == DK_ && A.DV == DV_)                                                               \
+        return A.head_gate ? launch_chunk_t<Tin, DK_, DV_, true>(A, nslots, stream)               \
+                           : launch_chunk_t<Tin, DK_, DV_, false>(A, nslots, stream);
     CKDA_CHUNK(32, 32) CKDA_CHUNK(32, 64) CKDA_CHUNK(32, 128)
     CKDA_CHUNK(64, 32) CKDA_CHUNK(64, 64) CKDA_CHUNK(64, 128)
     CKDA_CHUNK(128, 32) CKDA_CHUNK(128, 64) CKDA_CHUNK(128, 128)

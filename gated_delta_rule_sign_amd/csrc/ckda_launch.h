@@ -10,6 +10,7 @@ namespace ckda {
 struct DecodeArgs {
     int N, H, DK, DV;
     bool bf16;
+    bool head_gate;   // g, s per head ([N,H]) instead of per channel
     const void *q, *k, *v;
     const float* g;
     const int8_t* s;
@@ -37,6 +38,7 @@ struct FwdArgs {
     // equal-length mode: B sequences of T tokens; varlen mode: nchains docs
     int B, T, H, DK, DV;
     bool bf16;
+    bool head_gate;   // g, s per (token, head) instead of per channel
     const void *q, *k, *v;
     const float* g;
     const int8_t* s;
@@ -61,6 +63,7 @@ hipError_t launch_fwd(const FwdArgs& a, int nslots, hipStream_t stream);
 struct BwdArgs {
     int B, T, H, DK, DV;
     bool bf16;
+    bool head_gate;   // g, s, dg per (token, head) instead of per channel
     const void *q, *k, *v;
     const float* g;
     const int8_t* s;

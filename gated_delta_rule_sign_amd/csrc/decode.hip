@@ -23,7 +23,8 @@
 
 namespace ckda {
 
-template <typename Tin, int DK, int DV>
+// HG: one gate per head (g, s [N,H]), broadcast over the channels
+template <typename Tin, int DK, int DV, bool HG>
 __global__ void __launch_bounds__(256, 4)
 decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
                    const float* __restrict__ g, const int8_t* __restrict__ s,
@@ -54,8 +55,8 @@ decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
     // row parameters: every thread loads row min(t, DK - 1) (unconditional, so
     // these loads are issued ahead of the state stream and retire first)
     const int tr = t < DK ? t : DK - 1;
-    const int sp0 = sign_prod[kbase + tr], s0 = s[kbase + tr];
-    const float g0 = g[kbase + tr];
+    const int sp0 = sign_prod[kbase + tr], s0 = HG ? s[nh] : s[kbase + tr];
+    const float g0 = HG ? g[nh] : g[kbase + tr];
     const float k0 = Elem<Tin>::load(k, kbase + tr), q0 = Elem<Tin>::load(q, kbase + tr);
     float4 S[R];
 #pragma unroll
@@ -129,7 +130,8 @@ decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
 
 template <typename Tin, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs& A, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_step_kernel<Tin, DK, DV>), dim3(A.N * A.H), dim3(256), 0, stream,
+    auto kern = A.head_gate ? decode_step_kernel<Tin, DK, DV, true> : decode_step_kernel<Tin, DK, DV, false>;
+    hipLaunchKernelGGL(kern, dim3(A.N * A.H), dim3(256), 0, stream,
                        static_cast<const Tin*>(A.q), static_cast<const Tin*>(A.k),
                        static_cast<const Tin*>(A.v), A.g, A.s, A.beta, A.scale, A.state,
                        A.sign_prod, A.o);

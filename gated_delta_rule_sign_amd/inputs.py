@@ -44,6 +44,9 @@ WORKLOADS = {
     "decode_b256": dict(index=3, N=256, H=16, DK=128, DV=128, steps=512, dtype="bf16"),
     "varlen_64k": dict(index=4, T=65536, ndocs=16, min_len=256, H=16, DK=128, DV=128,
                        dtype="bf16"),
+    # layer_bf16 with one signed gate per (token, head): the head-scalar gate
+    "layer_bf16_head_gate": dict(index=5, B=8, T=4096, H=16, DK=128, DV=128, dtype="bf16",
+                                 gate="head"),
 }
 
 
@@ -104,8 +107,8 @@ class TokenInputs:
     q: np.ndarray      # storage dtype (float32 or bf16 bits), [..., H, DK]
     k: np.ndarray      # [..., H, DK]
     v: np.ndarray      # [..., H, DV]
-    g: np.ndarray      # float32 log|alpha| <= 0, [..., H, DK]
-    s: np.ndarray      # int8 +-1, [..., H, DK]
+    g: np.ndarray      # float32 log|alpha| <= 0, [..., H, DK] (head gate: [..., H])
+    s: np.ndarray      # int8 +-1, same shape as g
     beta: np.ndarray   # float32 in [0, 2], [..., H]
     dtype: str
 
@@ -116,14 +119,16 @@ class TokenInputs:
 
 
 def draw_tokens(rng: np.random.Generator, lead: tuple, H: int, DK: int, DV: int,
-                dtype: str, p_neg: float = 0.3) -> TokenInputs:
-    """Draw order: z, sign mask, q, k, v, beta."""
+                dtype: str, p_neg: float = 0.3, gate: str = "channel") -> TokenInputs:
+    """Draw order: z, sign mask, q, k, v, beta.  gate="head" draws one g
+    and one s per (token, head) instead of per channel."""
     shp_k = tuple(lead) + (H, DK)
     shp_v = tuple(lead) + (H, DV)
-    z = rng.standard_normal(shp_k)
+    shp_g = shp_k if gate == "channel" else tuple(lead) + (H,)
+    z = rng.standard_normal(shp_g)
     g = (-_softplus(z)).astype(np.float32)
     del z
-    neg = rng.random(shp_k) < p_neg
+    neg = rng.random(shp_g) < p_neg
     s = np.where(neg, -1, 1).astype(np.int8)
     del neg
     q = to_storage(_l2norm_last(rng.standard_normal(shp_k)), dtype)
@@ -178,9 +183,9 @@ class Workload:
     cu_seqlens: Optional[np.ndarray] = None  # int32 [ndocs+1]
 
 
-def make_forward(B, T, H, DK, DV, dtype, seed, with_do=False, h0_std=None) -> Workload:
+def make_forward(B, T, H, DK, DV, dtype, seed, with_do=False, h0_std=None, gate="channel") -> Workload:
     rng = np.random.default_rng(seed)
-    tok = draw_tokens(rng, (B, T), H, DK, DV, dtype)
+    tok = draw_tokens(rng, (B, T), H, DK, DV, dtype, gate=gate)
     h0 = draw_state(rng, (B, H, DK, DV), h0_std) if h0_std else None
     do = to_storage(rng.standard_normal((B, T, H, DV)), dtype) if with_do else None
     cfg = dict(B=B, T=T, H=H, DK=DK, DV=DV, dtype=dtype)
@@ -195,9 +200,9 @@ def make_workload(name: str, **override) -> Workload:
     seed = cfg.pop("seed", SEED_BASE + cfg["index"])
     rng = np.random.default_rng(seed)
     H, DK, DV, dt = cfg["H"], cfg["DK"], cfg["DV"], cfg["dtype"]
-    if name in ("tiny_fp32", "layer_bf16", "layer_bwd"):
+    if name in ("tiny_fp32", "layer_bf16", "layer_bwd", "layer_bf16_head_gate"):
         B, T = cfg["B"], cfg["T"]
-        tok = draw_tokens(rng, (B, T), H, DK, DV, dt)
+        tok = draw_tokens(rng, (B, T), H, DK, DV, dt, gate=cfg.get("gate", "channel"))
         do = None
         if name == "layer_bwd":
             do = to_storage(rng.standard_normal((B, T, H, DV)), dt)

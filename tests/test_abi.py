@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.ckda_abi_version() == 3
+    assert L.ckda_abi_version() == 4
     assert L.ckda_status_string(0) == b"ok"
     for st in range(1, 8):
         assert L.ckda_status_string(st) not in (b"ok", b"unknown status")
@@ -45,8 +45,8 @@ BIG = 1 << 40
 
 
 def fwd(L, B=1, T=8, H=1, DK=32, DV=32, dt=0, q=FAKE, k=FAKE, v=FAKE, g=FAKE, s=FAKE, beta=FAKE, o=FAKE,
-        ws=FAKE, wsb=BIG):
-    return L.ckda_fwd_chunked(B, T, H, DK, DV, dt, q, k, v, g, s, beta, ctypes.c_float(1.0),
+        ws=FAKE, wsb=BIG, gate=0):
+    return L.ckda_fwd_chunked(B, T, H, DK, DV, dt, gate, q, k, v, g, s, beta, ctypes.c_float(1.0),
                               None, o, None, None, ws, ctypes.c_size_t(wsb), None)
 
 
@@ -61,6 +61,7 @@ def test_fwd_rejects_bad_arguments(L):
     assert fwd(L, o=None) == 1
     assert fwd(L, T=0, o=None, q=None) != 1      # no tokens: o and q are not needed
     assert fwd(L, g=P(0x1004)) == 4              # misaligned
+    assert fwd(L, gate=2) == 4                   # unknown gate layout
     assert fwd(L, B=0) == 0                      # empty problem: nothing to do
     assert L.ckda_last_error() == b""
 
@@ -83,19 +84,19 @@ def test_fwd_workspace(L):
 def test_varlen_rejects_bad_cu_seqlens(L):
     def call(cu, N, Tt):
         arr = (ctypes.c_int32 * len(cu))(*cu)
-        return L.ckda_fwd_varlen(N, Tt, arr, FAKE, 1, 32, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+        return L.ckda_fwd_varlen(N, Tt, arr, FAKE, 1, 32, 32, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                  ctypes.c_float(1.0), None, FAKE, None, None, FAKE, ctypes.c_size_t(BIG), None)
     assert call([1, 5], 1, 5) == 5              # does not start at 0
     assert call([0, 5, 3], 2, 3) == 5           # decreasing
     assert call([0, 5, 9], 2, 10) == 5          # does not end at T_total
-    assert L.ckda_fwd_varlen(2, 4, None, FAKE, 1, 32, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+    assert L.ckda_fwd_varlen(2, 4, None, FAKE, 1, 32, 32, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                              ctypes.c_float(1.0), None, FAKE, None, None, FAKE, ctypes.c_size_t(BIG), None) == 1
 
 
 def bwd_varlen(L, cu, N, Tt, DK=32, DV=32, dt=0, ws=FAKE, wsb=BIG, q=FAKE, hc=FAKE):
     arr = None if cu is None else (ctypes.c_int32 * len(cu))(*cu)
     f = ctypes.c_float(1.0)
-    return L.ckda_bwd_varlen(N, Tt, arr, FAKE, 1, DK, DV, dt, q, FAKE, FAKE, FAKE, FAKE, FAKE, f, None,
+    return L.ckda_bwd_varlen(N, Tt, arr, FAKE, 1, DK, DV, dt, 0, q, FAKE, FAKE, FAKE, FAKE, FAKE, f, None,
                              hc, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, ws, ctypes.c_size_t(wsb), None)
 
 
@@ -122,9 +123,11 @@ def test_varlen_backward_boundary(L):
 
 def test_decode_and_bwd_reject_bad_arguments(L):
     f = ctypes.c_float(1.0)
-    assert L.ckda_decode_step(4, 2, 96, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, f, FAKE, FAKE, FAKE, None) == 4
-    assert L.ckda_decode_step(4, 2, 32, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, f, None, FAKE, FAKE, None) == 1
-    assert L.ckda_bwd(1, 8, 1, 32, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, f, None, None, FAKE, None,
+    assert L.ckda_decode_step(4, 2, 96, 32, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, f, FAKE, FAKE, FAKE, None) == 4
+    assert L.ckda_decode_step(4, 2, 32, 32, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, f, None, FAKE, FAKE, None) == 1
+    assert L.ckda_decode_step(4, 2, 32, 32, 0, 5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, f, FAKE, FAKE, FAKE, None) == 4
+    assert b"gate" in L.ckda_last_error()
+    assert L.ckda_bwd(1, 8, 1, 32, 32, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, f, None, None, FAKE, None,
                       FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 1   # h_ckpt missing
     assert L.ckda_chunk_prep(1, 8, 1, 100, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 4
 
