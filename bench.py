@@ -7,11 +7,11 @@ state-passing kernel (state products, output, state update, chunk by
 chunk), over the mixer workload of the 1.36B model: B=8, T=4096, H=16,
 dk=dv=128, bf16 q/k/v, fp32 gates, state and outputs.  The JSON line's ``value`` is that forward's
 tokens/s; the decode workload (256 sequences x 16 heads, 512 recurrent
-steps) is reported in the same line as state-streaming GB/s, and the
-backward (when built) as tokens/s.
+steps) is reported in the same line as state-streaming GB/s, the backward as
+tokens/s, and the same forward with one gate per (token, head) as tokens/s.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       [--only fwd|decode|bwd|copy]
+       [--only fwd|fwd_head_gate|decode|bwd|copy]
 """
 from __future__ import annotations
 
@@ -90,11 +90,15 @@ def time_kernel_launches(torch, fn, steps, warmup):
     return wall, [a.elapsed_time(b) for a, b in evs]
 
 
-def bench_fwd(torch, steps, warmup):
+# head-scalar gate: g f32 and s int8 once per token-head (5 bytes instead of 640)
+FWD_HG_BYTES_PER_TOKEN_HEAD = 768 + 4 + 1 + 4 + 512
+
+
+def bench_fwd(torch, steps, warmup, workload="layer_bf16"):
     from gated_delta_rule_sign_amd import ckda
     from gated_delta_rule_sign_amd import inputs as I
-    log("generating layer_bf16 inputs")
-    w = I.make_workload("layer_bf16")
+    log(f"generating {workload} inputs")
+    w = I.make_workload(workload)
     tok = w.tok
     d = {k: dev_tensor(torch, getattr(tok, k)) for k in ("q", "k", "v", "g", "s", "beta")}
     B, T, H, DK = tok.q.shape
@@ -109,8 +113,9 @@ def bench_fwd(torch, steps, warmup):
     th = B * T * H
     ms = wall / steps
     avg_launch = float(np.mean(per))
+    per_th = FWD_HG_BYTES_PER_TOKEN_HEAD if tok.g.ndim == 3 else FWD_BYTES_PER_TOKEN_HEAD
     return dict(w=w, tokens=tokens, ms=ms, launch_ms=avg_launch, launch_all=per,
-                bytes=th * FWD_BYTES_PER_TOKEN_HEAD, flops=th * FWD_FLOPS_PER_TOKEN_HEAD,
+                bytes=th * per_th, flops=th * FWD_FLOPS_PER_TOKEN_HEAD,
                 workspace_bytes=int(ws.numel()))
 
 
@@ -216,7 +221,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "decode", "bwd", "copy"], default=None)
+    ap.add_argument("--only", choices=["fwd", "fwd_head_gate", "decode", "bwd", "copy"], default=None)
     ap.add_argument("--decode-steps", type=int, default=512)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -240,12 +245,17 @@ def main():
         print(json.dumps(bench_bwd(torch, args.steps, args.warmup)))
         return
 
+    if args.only == "fwd_head_gate":
+        fh = bench_fwd(torch, args.steps, args.warmup, "layer_bf16_head_gate")
+        print(json.dumps({k: v for k, v in fh.items() if k not in ("w", "launch_all")}))
+        return
     fw = bench_fwd(torch, args.steps, args.warmup)
     if args.only == "fwd":
         print(json.dumps({k: v for k, v in fw.items() if k not in ("w", "launch_all")}))
         return
     dec = bench_decode(torch, args.decode_steps)
     bw = bench_bwd(torch, max(3, args.steps // 4), 1)
+    fh = bench_fwd(torch, args.steps, args.warmup, "layer_bf16_head_gate")
     cpu = None if args.no_cpu else cpu_baseline(fw["w"])
 
     achieved = fw["bytes"] / (fw["launch_ms"] * 1e-3) / 1e9
@@ -282,6 +292,12 @@ def main():
                      "unit": "tokens/s", "value": bw["tokens_per_s"], "ms": bw["ms"],
                      "algorithmic_bytes": bw["bytes"], "achieved_gbs": bw["gbs"],
                      "frac_of_hbm_peak": bw["gbs"] / HBM_PEAK_GBS, "workspace_bytes": bw["workspace_bytes"]},
+        "forward_head_gate": {"workload": "layer_bf16_head_gate: layer_bf16 with one signed gate per "
+                                          "(token, head) (g f32, s int8 [B,T,H])",
+                              "unit": "tokens/s", "value": fh["tokens"] / (fh["ms"] * 1e-3), "ms": fh["ms"],
+                              "avg_launch_ms": fh["launch_ms"], "algorithmic_bytes": fh["bytes"],
+                              "achieved_gbs": fh["bytes"] / (fh["launch_ms"] * 1e-3) / 1e9,
+                              "frac_of_hbm_peak": fh["bytes"] / (fh["launch_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

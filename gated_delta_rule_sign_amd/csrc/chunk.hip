@@ -188,10 +188,19 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
         if (cgi == 0 && gq == 0) beta_s[t] = valid ? bt : 0.f;
     }
     // ---- 1. in-tile scans (log2 units), tile totals to LDS -----------------
+    if constexpr (HG) {   // every channel carries the head's gate: one scan per lane
+        const float b1 = row_scan_add(bs[0] * kLog2e);
+        const uint32_t p1 = row_scan_xor(par[0]);
 #pragma unroll
-    for (int i = 0; i < NE; ++i) bs[i] = row_scan_add(bs[i] * kLog2e);
+        for (int i = 0; i < NE; ++i) bs[i] = b1;
 #pragma unroll
-    for (int i = 0; i < 2 * KSW; ++i) par[i] = row_scan_xor(par[i]);
+        for (int i = 0; i < 2 * KSW; ++i) par[i] = p1;
+    } else {
+#pragma unroll
+        for (int i = 0; i < NE; ++i) bs[i] = row_scan_add(bs[i] * kLog2e);
+#pragma unroll
+        for (int i = 0; i < 2 * KSW; ++i) par[i] = row_scan_xor(par[i]);
+    }
     if (n == 15) {
 #pragma unroll
         for (int ks = 0; ks < KSW; ++ks) {
@@ -212,7 +221,17 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
         // anchors per channel (log2 units): b at token 15 (m0) and 47 (m1),
         // and the sum over the earlier tiles of this wave's token tile
         float b[8], mh[8], m1[8];
-        {
+        if constexpr (HG) {   // equal across channels: one value per lane (the rest folds away)
+            const float t0 = totb[c0], t1 = totb[DK + c0], t2 = totb[2 * DK + c0];
+            const float pre = (R > 0 ? t0 : 0.f) + (R > 1 ? t1 : 0.f) + (R > 2 ? t2 : 0.f);
+            const float m1v = t0 + t1 + t2, mhv = R < 2 ? t0 : m1v, bv = bs[8 * ks] + pre;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                b[e] = bv;
+                m1[e] = m1v;
+                mh[e] = mhv;
+            }
+        } else {
             float4 Tt[3][2];
 #pragma unroll
             for (int x = 0; x < 3; ++x) {
@@ -245,7 +264,8 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const uint32_t sgn = (((e >> 2) ? pw1 : pw0) << (24 - 8 * (e & 3))) & 0x80000000u;
+                const uint32_t sgn = HG ? ((pw0 << 24) & 0x80000000u)   // all bytes equal
+                                        : ((((e >> 2) ? pw1 : pw0) << (24 - 8 * (e & 3))) & 0x80000000u);
                 kf[e] = __uint_as_float(__float_as_uint(k8[ks].get(e)) ^ sgn);
                 qf[e] = __uint_as_float(__float_as_uint(q8[ks].get(e)) ^ sgn);
             }
