@@ -147,10 +147,31 @@ def bwd_chain_arrays(q, k, v, g, s, beta, do, scale=1.0, S0=None, dST=None, ever
 
 
 # ----------------------------------------------------------------------------
-# tensor-level entry points ([B, T, H, D] layout)
+# per-head L2 normalisation of q and k (the unit keys of the Complex KDA paper
+# page, sections 3-4), written out: y = x / ||x|| over the key channels, with
+# a zero vector left at zero; its reverse mode dx = (dy - y (y . dy)) / ||x||.
+# ----------------------------------------------------------------------------
+def l2norm(x) -> np.ndarray:
+    x = np.asarray(x, np.float64)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return np.divide(x, n, out=np.zeros_like(x), where=n > 0)
+
+
+def l2norm_bwd(x, dy) -> np.ndarray:
+    x = np.asarray(x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    y = np.divide(x, n, out=np.zeros_like(x), where=n > 0)
+    r = dy - y * np.sum(y * dy, axis=-1, keepdims=True)
+    return np.divide(r, n, out=np.zeros_like(x), where=n > 0)
+
+
+# ----------------------------------------------------------------------------
+# tensor-level entry points ([B, T, H, D] layout); qk_norm=True runs the
+# recurrence on l2norm(q), l2norm(k)
 # ----------------------------------------------------------------------------
 def fwd(q, k, v, g, s, beta, scale=1.0, h0=None,
-        chains: Optional[Sequence] = None, cols: Optional[Sequence[int]] = None):
+        chains: Optional[Sequence] = None, cols: Optional[Sequence[int]] = None, qk_norm: bool = False):
     """Forward over [B,T,H,D] tensors.  Returns (o [B,T,H,DV], ht [B,H,DK,DV]).
 
     ``chains``: optional list of (b, h) pairs; ``cols``: optional list of value
@@ -159,6 +180,8 @@ def fwd(q, k, v, g, s, beta, scale=1.0, h0=None,
     Every value column evolves on its own (u_j depends only on column j of the
     state and on v_j), so restricting v and h0 to a set of columns gives
     exactly those columns of the full problem."""
+    if qk_norm:
+        q, k = l2norm(q), l2norm(k)
     B, T, H, DK = q.shape
     if chains is None and cols is None:
         S0 = None if h0 is None else np.asarray(h0, np.float64).reshape(B * H, DK, -1)
@@ -187,7 +210,7 @@ def _drop_lead(x, nd: int) -> np.ndarray:
 
 def varlen(q, k, v, g, s, beta, cu_seqlens, scale=1.0, h0=None,
            docs: Optional[Sequence[int]] = None, heads: Optional[Sequence[int]] = None,
-           cols: Optional[Sequence[int]] = None):
+           cols: Optional[Sequence[int]] = None, qk_norm: bool = False):
     """Packed documents: q etc. are [1, Ttot, H, D] (or [Ttot, H, D]); document
     n covers tokens cu[n]..cu[n+1]-1 and starts from h0[n] (or 0).  Each
     (document, head) is an independent chain.  Returns (o [Ttot, H, DV'],
@@ -195,6 +218,8 @@ def varlen(q, k, v, g, s, beta, cu_seqlens, scale=1.0, h0=None,
     unselected documents are NaN)."""
     q, k, v, g, s = (_drop_lead(a, 3) for a in (q, k, v, g, s))
     beta = _drop_lead(beta, 2)
+    if qk_norm:
+        q, k = l2norm(q), l2norm(k)
     Ttot, H, DK = q.shape
     DV = v.shape[2]
     cu = np.asarray(cu_seqlens, np.int64)
@@ -221,12 +246,14 @@ def varlen(q, k, v, g, s, beta, cu_seqlens, scale=1.0, h0=None,
 
 
 def decode(q, k, v, g, s, beta, state0, sign0=None, scale=1.0,
-           pairs: Optional[Sequence] = None, cols: Optional[Sequence[int]] = None):
+           pairs: Optional[Sequence] = None, cols: Optional[Sequence[int]] = None, qk_norm: bool = False):
     """Sequential single-token steps.  q etc. are [steps, N, H, D]; the decode
     state is carried as (state, sign product) with true state
     Diag(sign) * state.  Returns (o [steps, npairs, DV'], true final state
     [npairs, DK, DV'], final sign product [npairs, DK]) for the selected (n, h)
     pairs (default: all, in n-major order)."""
+    if qk_norm:
+        q, k = l2norm(q), l2norm(k)
     steps, N, H, DK = np.asarray(q).shape
     DV = np.asarray(v).shape[3]
     pairs = [(n, h) for n in range(N) for h in range(H)] if pairs is None else list(pairs)
@@ -244,7 +271,7 @@ def decode(q, k, v, g, s, beta, state0, sign0=None, scale=1.0,
 
 
 def bwd(q, k, v, g, s, beta, do, scale=1.0, h0=None, dht=None, every=64,
-        chains: Optional[Sequence] = None):
+        chains: Optional[Sequence] = None, qk_norm: bool = False):
     """Gradients of L = <do, o> + <dht, ht> for the [B,T,H,D] forward.
     Returns dict with dq, dk, dg [n,T,DK], dv [n,T,DV], dbeta [n,T], dh0
     [n,DK,DV] over the selected (b, h) chains (default: all, b-major)."""
@@ -256,6 +283,11 @@ def bwd(q, k, v, g, s, beta, do, scale=1.0, h0=None, dht=None, every=64,
     bb = np.ascontiguousarray(np.asarray(beta)[bi, :, hi], np.float64)
     S0 = None if h0 is None else np.ascontiguousarray(np.asarray(h0)[bi, hi], np.float64)
     dST = None if dht is None else np.ascontiguousarray(np.asarray(dht)[bi, hi], np.float64)
-    r = bwd_chain_arrays(sel(q), sel(k), sel(v), sel(g), sel(s), bb, sel(do), scale, S0, dST, every)
+    if qk_norm:   # gradients reach the raw q, k through the normalisation
+        qr, kr = sel(q), sel(k)
+        r = bwd_chain_arrays(l2norm(qr), l2norm(kr), sel(v), sel(g), sel(s), bb, sel(do), scale, S0, dST, every)
+        r["dq"], r["dk"] = l2norm_bwd(qr, r["dq"]), l2norm_bwd(kr, r["dk"])
+    else:
+        r = bwd_chain_arrays(sel(q), sel(k), sel(v), sel(g), sel(s), bb, sel(do), scale, S0, dST, every)
     r["dh0"] = r.pop("dS0")
     return r

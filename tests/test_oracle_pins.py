@@ -376,3 +376,63 @@ def test_tensor_layout_wrappers_agree_with_chain_calls():
     od, Sd, Pd = oracle.decode(**dq, state0=np.zeros((1, 2, 32, 32)))
     assert np.array_equal(od.reshape(70, 2, 32), o[0])
     assert np.array_equal(Pd, np.prod(f["s"][0].transpose(1, 0, 2), axis=1))
+
+
+# ---------------------------------------------------------------------------
+# per-head L2 normalisation of q and k (unit keys, paper page sections 3-4)
+# ---------------------------------------------------------------------------
+def test_qk_norm_backward_matches_central_finite_differences():
+    """The normalised path's gradient w.r.t. the raw q and k against central
+    finite differences of the composed forward (raw inputs far from unit)."""
+    rng = np.random.default_rng(21)
+    B, T, H, DK, DV = 1, 7, 1, 4, 3
+    q = 3.0 * rng.standard_normal((B, T, H, DK))
+    k = 0.5 * rng.standard_normal((B, T, H, DK))
+    v = rng.standard_normal((B, T, H, DV))
+    g = -np.log1p(np.exp(rng.standard_normal((B, T, H, DK))))
+    s = np.where(rng.random((B, T, H, DK)) < 0.3, -1.0, 1.0)
+    beta = 2.0 * rng.random((B, T, H))
+    do = rng.standard_normal((B, T, H, DV))
+
+    def loss(q, k):
+        o, _ = oracle.fwd(q, k, v, g, s, beta, scale=0.8, qk_norm=True)
+        return float(np.sum(o * do))
+
+    r = oracle.bwd(q, k, v, g, s, beta, do, scale=0.8, qk_norm=True)
+    h = 1e-6
+    for name, x, gr in (("q", q, r["dq"][0]), ("k", k, r["dk"][0])):
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            a = (xp, k) if name == "q" else (q, xp)
+            b = (xm, k) if name == "q" else (q, xm)
+            fd[idx] = (loss(*a) - loss(*b)) / (2 * h)
+        err = np.abs(fd[0, :, 0] - gr).max() / np.abs(fd).max()
+        assert err < 1e-6, (name, err)
+
+
+def test_qk_norm_is_scale_free_and_identity_on_unit_vectors():
+    rng = np.random.default_rng(22)
+    B, T, H, DK, DV = 1, 40, 2, 8, 3
+    q = rng.standard_normal((B, T, H, DK))
+    k = rng.standard_normal((B, T, H, DK))
+    v = rng.standard_normal((B, T, H, DV))
+    g = -np.log1p(np.exp(rng.standard_normal((B, T, H, DK))))
+    s = np.where(rng.random((B, T, H, DK)) < 0.3, -1.0, 1.0)
+    beta = 2.0 * rng.random((B, T, H))
+    c = np.exp(rng.standard_normal((B, T, H, 1)))       # positive per-token scales
+    o1, s1 = oracle.fwd(q, k, v, g, s, beta, qk_norm=True)
+    o2, s2 = oracle.fwd(c * q, 3.0 * c * k, v, g, s, beta, qk_norm=True)
+    assert np.allclose(o1, o2, rtol=0, atol=1e-12) and np.allclose(s1, s2, rtol=0, atol=1e-12)
+    qu = q / np.linalg.norm(q, axis=-1, keepdims=True)
+    ku = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    o3, _ = oracle.fwd(qu, ku, v, g, s, beta)
+    assert np.allclose(o1, o3, rtol=0, atol=1e-12)
+    # a zero key leaves the state untouched by that token's write
+    kz = k.copy(); kz[0, 5] = 0.0
+    o4, _ = oracle.fwd(q, kz, v, g, s, beta, qk_norm=True)
+    assert np.isfinite(o4).all()
