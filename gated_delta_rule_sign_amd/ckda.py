@@ -41,7 +41,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
     except OSError as e:  # pragma: no cover - depends on the machine
         raise CkdaError(f"cannot load {LIB_PATH}: {e}") from e
-    P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    P, I, F, S, U = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_uint32
     L.ckda_abi_version.restype = I
     L.ckda_status_string.argtypes = [I]
     L.ckda_status_string.restype = ctypes.c_char_p
@@ -52,22 +52,22 @@ def lib() -> ctypes.CDLL:
     L.ckda_fwd_workspace_bytes.restype = S
     L.ckda_fwd_varlen_workspace_bytes.argtypes = [I, I, I, I, I, I]
     L.ckda_fwd_varlen_workspace_bytes.restype = S
-    L.ckda_fwd_chunked.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P, P, S, P]
+    L.ckda_fwd_chunked.argtypes = [I, I, I, I, I, I, U, P, P, P, P, P, P, F, P, P, P, P, P, S, P]
     L.ckda_fwd_chunked.restype = I
-    L.ckda_fwd_varlen.argtypes = [I, I, P, P, I, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P, P, S, P]
+    L.ckda_fwd_varlen.argtypes = [I, I, P, P, I, I, I, I, U, P, P, P, P, P, P, F, P, P, P, P, P, S, P]
     L.ckda_fwd_varlen.restype = I
     L.ckda_varlen_chunk_slots.argtypes = [I, I]
     L.ckda_varlen_chunk_slots.restype = I
-    L.ckda_decode_step.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P]
+    L.ckda_decode_step.argtypes = [I, I, I, I, I, U, P, P, P, P, P, P, F, P, P, P, P]
     L.ckda_decode_step.restype = I
     L.ckda_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
     L.ckda_bwd_workspace_bytes.restype = S
-    L.ckda_bwd.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P,
+    L.ckda_bwd.argtypes = [I, I, I, I, I, I, U, P, P, P, P, P, P, F, P, P, P, P,
                            P, P, P, P, P, P, P, S, P]
     L.ckda_bwd.restype = I
     L.ckda_bwd_varlen_workspace_bytes.argtypes = [I, I, I, I, I]
     L.ckda_bwd_varlen_workspace_bytes.restype = S
-    L.ckda_bwd_varlen.argtypes = [I, I, P, P, I, I, I, I, I, P, P, P, P, P, P, F, P, P, P, P,
+    L.ckda_bwd_varlen.argtypes = [I, I, P, P, I, I, I, I, U, P, P, P, P, P, P, F, P, P, P, P,
                                   P, P, P, P, P, P, P, S, P]
     L.ckda_bwd_varlen.restype = I
     _lib = L
@@ -113,12 +113,17 @@ def _need(t: Optional[torch.Tensor], name: str, dtype=None, shape=None, device=N
         raise CkdaError(f"{name} must be contiguous")
 
 
-CKDA_GATE_CHANNEL, CKDA_GATE_HEAD = 0, 1
+CKDA_GATE_CHANNEL, CKDA_GATE_HEAD, CKDA_QK_L2NORM = 0, 1, 2
 
 
 def _gate_code(g, lead) -> int:
     """CKDA_GATE_HEAD when g is [.., H] (one gate per head), else per channel."""
     return CKDA_GATE_HEAD if g.dim() == len(lead) + 1 else CKDA_GATE_CHANNEL
+
+
+def _flags(g, lead, qk_norm: bool) -> int:
+    """The flags word: gate layout from g's shape, plus CKDA_QK_L2NORM."""
+    return _gate_code(g, lead) | (CKDA_QK_L2NORM if qk_norm else 0)
 
 
 def _token_inputs(q, k, v, g, s, beta, lead):
@@ -173,11 +178,13 @@ def _workspace(workspace, need, dev):
 
 
 def fwd(q, k, v, g, s, beta, scale: float = 1.0, h0=None, want_ht: bool = True,
-        want_ckpt: bool = False, o=None, ht=None, h_ckpt=None, workspace=None):
+        want_ckpt: bool = False, o=None, ht=None, h_ckpt=None, workspace=None,
+        qk_norm: bool = False):
     """Chunked forward (ckda_fwd_chunked).  Inputs [B,T,H,D]; returns
     (o [B,T,H,DV] f32, ht [B,H,DK,DV] f32 or None, h_ckpt or None).
     ``workspace`` (uint8 GPU tensor of fwd_workspace_bytes) is allocated per
-    call if not given."""
+    call if not given.  ``qk_norm`` L2-normalises q and k per (token, head)
+    inside the kernels (every entry point takes it)."""
     B, T = q.shape[0], q.shape[1]
     dt, H, DK, DV, dev = _token_inputs(q, k, v, g, s, beta, (B, T))
     _need(h0, "h0", torch.float32, (B, H, DK, DV), dev)
@@ -192,7 +199,7 @@ def fwd(q, k, v, g, s, beta, scale: float = 1.0, h0=None, want_ht: bool = True,
         h_ckpt = torch.empty((B, H, NT, DK, DV), dtype=torch.float32, device=dev)
     _need(h_ckpt, "h_ckpt", torch.float32, (B, H, NT, DK, DV), dev)
     workspace, wsb = _workspace(workspace, fwd_workspace_bytes(B, T, H, DK, DV, q.dtype), dev)
-    _check(lib().ckda_fwd_chunked(B, T, H, DK, DV, dt, _gate_code(g, (B, T)), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
+    _check(lib().ckda_fwd_chunked(B, T, H, DK, DV, dt, _flags(g, (B, T), qk_norm), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
                                   _ptr(beta), float(scale), _ptr(h0), _ptr(o), _ptr(ht),
                                   _ptr(h_ckpt), _ptr(workspace), wsb, _stream()))
     return o, ht, h_ckpt
@@ -204,7 +211,7 @@ def varlen_chunk_slots(N, T_total) -> int:
 
 def fwd_varlen(q, k, v, g, s, beta, cu_seqlens, scale: float = 1.0, h0=None,
                want_ht: bool = True, cu_seqlens_dev=None, o=None, ht=None, workspace=None,
-               want_ckpt: bool = False):
+               want_ckpt: bool = False, qk_norm: bool = False):
     """Packed-document forward (ckda_fwd_varlen).  q etc. are [T_total,H,D]
     (a leading 1 is accepted); cu_seqlens is an int32 CPU tensor [N+1].
     Returns (o, ht), or (o, ht, h_ckpt) with want_ckpt: the chunk-start
@@ -231,13 +238,14 @@ def fwd_varlen(q, k, v, g, s, beta, cu_seqlens, scale: float = 1.0, h0=None,
     if want_ckpt:
         hc = torch.empty((varlen_chunk_slots(N, Tt), H, DK, DV), dtype=torch.float32, device=dev)
     workspace, wsb = _workspace(workspace, fwd_varlen_workspace_bytes(N, Tt, H, DK, DV, q.dtype), dev)
-    _check(lib().ckda_fwd_varlen(N, Tt, _ptr(cu), _ptr(cu_seqlens_dev), H, DK, DV, dt, _gate_code(g, (Tt,)), _ptr(q),
+    _check(lib().ckda_fwd_varlen(N, Tt, _ptr(cu), _ptr(cu_seqlens_dev), H, DK, DV, dt, _flags(g, (Tt,), qk_norm),
+                                 _ptr(q),
                                  _ptr(k), _ptr(v), _ptr(g), _ptr(s), _ptr(beta), float(scale),
                                  _ptr(h0), _ptr(o), _ptr(ht), _ptr(hc), _ptr(workspace), wsb, _stream()))
     return (o, ht, hc) if want_ckpt else (o, ht)
 
 
-def decode_step(q, k, v, g, s, beta, state, sign_prod, scale: float = 1.0, o=None):
+def decode_step(q, k, v, g, s, beta, state, sign_prod, scale: float = 1.0, o=None, qk_norm: bool = False):
     """One recurrent step (ckda_decode_step); state [N,H,DK,DV] f32 and
     sign_prod [N,H,DK] int8 are updated in place.  Returns o [N,H,DV] f32."""
     N = q.shape[0]
@@ -247,7 +255,7 @@ def decode_step(q, k, v, g, s, beta, state, sign_prod, scale: float = 1.0, o=Non
     if o is None:
         o = torch.empty((N, H, DV), dtype=torch.float32, device=dev)
     _need(o, "o", torch.float32, (N, H, DV), dev)
-    _check(lib().ckda_decode_step(N, H, DK, DV, dt, _gate_code(g, (N,)), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
+    _check(lib().ckda_decode_step(N, H, DK, DV, dt, _flags(g, (N,), qk_norm), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
                                   _ptr(beta), float(scale), _ptr(state), _ptr(sign_prod), _ptr(o),
                                   _stream()))
     return o
@@ -258,7 +266,7 @@ def bwd_workspace_bytes(B, T, H, DK, DV) -> int:
 
 
 def bwd(q, k, v, g, s, beta, h_ckpt, do, scale: float = 1.0, h0=None, dht=None,
-        want_dh0: bool = True, workspace=None):
+        want_dh0: bool = True, workspace=None, qk_norm: bool = False):
     """Backward (ckda_bwd).  Returns dict dq, dk, dv, dg, dbeta, dh0 (f32)."""
     B, T = q.shape[0], q.shape[1]
     dt, H, DK, DV, dev = _token_inputs(q, k, v, g, s, beta, (B, T))
@@ -277,7 +285,7 @@ def bwd(q, k, v, g, s, beta, h_ckpt, do, scale: float = 1.0, h0=None, dht=None,
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().ckda_bwd(B, T, H, DK, DV, dt, _gate_code(g, (B, T)), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
+    _check(lib().ckda_bwd(B, T, H, DK, DV, dt, _flags(g, (B, T), qk_norm), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
                           _ptr(beta), float(scale), _ptr(h0), _ptr(h_ckpt), _ptr(do), _ptr(dht),
                           _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
                           _ptr(out["dbeta"]), _ptr(out["dh0"]), _ptr(workspace), wsb, _stream()))
@@ -289,7 +297,7 @@ def bwd_varlen_workspace_bytes(N, T_total, H, DK, DV) -> int:
 
 
 def bwd_varlen(q, k, v, g, s, beta, cu_seqlens, h_ckpt, do, scale: float = 1.0, h0=None, dht=None,
-               want_dh0: bool = True, cu_seqlens_dev=None, workspace=None):
+               want_dh0: bool = True, cu_seqlens_dev=None, workspace=None, qk_norm: bool = False):
     """Backward of the packed-document forward (ckda_bwd_varlen).  Shapes as
     in fwd_varlen; h_ckpt from fwd_varlen(..., want_ckpt=True); do
     [T_total,H,DV]; dht, dh0 [N,H,DK,DV].  Returns dict dq, dk, dv, dg,
@@ -317,7 +325,8 @@ def bwd_varlen(q, k, v, g, s, beta, cu_seqlens, h_ckpt, do, scale: float = 1.0, 
                dbeta=torch.empty((Tt, H), **f32),
                dh0=torch.empty((N, H, DK, DV), **f32) if want_dh0 else None)
     workspace, wsb = _workspace(workspace, bwd_varlen_workspace_bytes(N, Tt, H, DK, DV), dev)
-    _check(lib().ckda_bwd_varlen(N, Tt, _ptr(cu), _ptr(cu_seqlens_dev), H, DK, DV, dt, _gate_code(g, (Tt,)), _ptr(q),
+    _check(lib().ckda_bwd_varlen(N, Tt, _ptr(cu), _ptr(cu_seqlens_dev), H, DK, DV, dt, _flags(g, (Tt,), qk_norm),
+                                 _ptr(q),
                                  _ptr(k), _ptr(v), _ptr(g), _ptr(s), _ptr(beta), float(scale),
                                  _ptr(h0), _ptr(h_ckpt), _ptr(do), _ptr(dht), _ptr(out["dq"]),
                                  _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),

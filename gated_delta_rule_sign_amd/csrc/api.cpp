@@ -45,9 +45,9 @@ ckda_status_t check_dtype(ckda_dtype_t dt) {
     return CKDA_OK;
 }
 
-ckda_status_t check_gate(ckda_gate_t gate) {
-    if (gate != CKDA_GATE_CHANNEL && gate != CKDA_GATE_HEAD)
-        return fail(CKDA_ERR_UNSUPPORTED, "unknown gate layout %d", int(gate));
+ckda_status_t check_flags(ckda_flags_t flags) {
+    if (flags & ~(CKDA_GATE_HEAD | CKDA_QK_L2NORM))
+        return fail(CKDA_ERR_UNSUPPORTED, "unknown option flags 0x%x", unsigned(flags));
     return CKDA_OK;
 }
 
@@ -155,12 +155,12 @@ size_t ckda_fwd_varlen_workspace_bytes(int N, int T_total, int H, int DK, int DV
 }
 
 ckda_status_t ckda_fwd_chunked(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype,
-                               ckda_gate_t gate, const void* q, const void* k, const void* v,
+                               ckda_flags_t flags, const void* q, const void* k, const void* v,
                                const float* g, const int8_t* s, const float* beta, float scale,
                                const float* h0, float* o, float* ht, float* h_ckpt, void* workspace,
                                size_t workspace_bytes, ckda_stream_t stream) {
     CKDA_TRY(check_dtype(in_dtype));
-    CKDA_TRY(check_gate(gate));
+    CKDA_TRY(check_flags(flags));
     if (B < 0 || T < 0 || H < 0) return fail(CKDA_ERR_SHAPE, "negative size (B=%d, T=%d, H=%d)", B, T, H);
     CKDA_TRY(check_heads(DK, DV));
     if (too_big(static_cast<long long>(B) * T, H)) return fail(CKDA_ERR_UNSUPPORTED, "tensor too large");
@@ -178,20 +178,20 @@ ckda_status_t ckda_fwd_chunked(int B, int T, int H, int DK, int DV, ckda_dtype_t
     }
     ckda::FwdArgs a{};
     a.B = B; a.T = T; a.H = H; a.DK = DK; a.DV = DV; a.bf16 = in_dtype == CKDA_BF16;
-    a.head_gate = gate == CKDA_GATE_HEAD;
+    a.head_gate = (flags & CKDA_GATE_HEAD) != 0; a.qk_norm = (flags & CKDA_QK_L2NORM) != 0;
     a.q = q; a.k = k; a.v = v; a.g = g; a.s = s; a.beta = beta; a.scale = scale;
     a.h0 = h0; a.o = o; a.ht = ht; a.h_ckpt = h_ckpt; a.cu = nullptr; a.ndocs = 0; a.ws = workspace;
     return hip_status(ckda::launch_fwd(a, nslots, static_cast<hipStream_t>(stream)), "ckda_fwd_chunked launch");
 }
 
 ckda_status_t ckda_fwd_varlen(int N, int T_total, const int32_t* cu, const int32_t* cu_dev, int H,
-                              int DK, int DV, ckda_dtype_t in_dtype, ckda_gate_t gate, const void* q,
+                              int DK, int DV, ckda_dtype_t in_dtype, ckda_flags_t flags, const void* q,
                               const void* k, const void* v, const float* g, const int8_t* s,
                               const float* beta, float scale, const float* h0, float* o, float* ht,
                               float* h_ckpt, void* workspace, size_t workspace_bytes,
                               ckda_stream_t stream) {
     CKDA_TRY(check_dtype(in_dtype));
-    CKDA_TRY(check_gate(gate));
+    CKDA_TRY(check_flags(flags));
     if (N < 0 || T_total < 0 || H < 0) return fail(CKDA_ERR_SHAPE, "negative size (N=%d, T=%d, H=%d)", N, T_total, H);
     CKDA_TRY(check_heads(DK, DV));
     CKDA_TRY(check_varlen_sizes(N, T_total, H));
@@ -209,20 +209,20 @@ ckda_status_t ckda_fwd_varlen(int N, int T_total, const int32_t* cu, const int32
     }
     ckda::FwdArgs a{};
     a.B = 1; a.T = T_total; a.H = H; a.DK = DK; a.DV = DV; a.bf16 = in_dtype == CKDA_BF16;
-    a.head_gate = gate == CKDA_GATE_HEAD;
+    a.head_gate = (flags & CKDA_GATE_HEAD) != 0; a.qk_norm = (flags & CKDA_QK_L2NORM) != 0;
     a.q = q; a.k = k; a.v = v; a.g = g; a.s = s; a.beta = beta; a.scale = scale;
     a.h0 = h0; a.o = o; a.ht = ht; a.h_ckpt = h_ckpt;
     a.cu = cu_dev; a.ndocs = N; a.ws = workspace;
     return hip_status(ckda::launch_fwd(a, nslots, static_cast<hipStream_t>(stream)), "ckda_fwd_varlen launch");
 }
 
-ckda_status_t ckda_decode_step(int N, int H, int DK, int DV, ckda_dtype_t in_dtype, ckda_gate_t gate,
+ckda_status_t ckda_decode_step(int N, int H, int DK, int DV, ckda_dtype_t in_dtype, ckda_flags_t flags,
                                const void* q,
                                const void* k, const void* v, const float* g, const int8_t* s,
                                const float* beta, float scale, float* state, int8_t* sign_prod,
                                float* o, ckda_stream_t stream) {
     CKDA_TRY(check_dtype(in_dtype));
-    CKDA_TRY(check_gate(gate));
+    CKDA_TRY(check_flags(flags));
     if (N < 0 || H < 0) return fail(CKDA_ERR_SHAPE, "negative size (N=%d, H=%d)", N, H);
     CKDA_TRY(check_heads(DK, DV));
     if (static_cast<long long>(N) * H >= (1LL << 31)) return fail(CKDA_ERR_UNSUPPORTED, "too many heads");
@@ -230,7 +230,8 @@ ckda_status_t ckda_decode_step(int N, int H, int DK, int DV, ckda_dtype_t in_dty
     CKDA_REQUIRE(q); CKDA_REQUIRE(k); CKDA_REQUIRE(v); CKDA_REQUIRE(g); CKDA_REQUIRE(s);
     CKDA_REQUIRE(beta); CKDA_REQUIRE(state); CKDA_REQUIRE(sign_prod); CKDA_REQUIRE(o);
     CKDA_ALIGNED(state); CKDA_ALIGNED(o);
-    ckda::DecodeArgs a{N, H, DK, DV, in_dtype == CKDA_BF16, gate == CKDA_GATE_HEAD, q, k, v, g, s, beta,
+    ckda::DecodeArgs a{N, H, DK, DV, in_dtype == CKDA_BF16, (flags & CKDA_GATE_HEAD) != 0,
+                       (flags & CKDA_QK_L2NORM) != 0, q, k, v, g, s, beta,
                        scale, state, sign_prod, o};
     return hip_status(ckda::launch_decode(a, static_cast<hipStream_t>(stream)), "ckda_decode_step launch");
 }
@@ -271,21 +272,21 @@ ckda_status_t bwd_common(ckda::BwdArgs& a, int nslots, bool any_tokens, const vo
 
 }  // namespace
 
-ckda_status_t ckda_bwd(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype, ckda_gate_t gate,
+ckda_status_t ckda_bwd(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype, ckda_flags_t flags,
                        const void* q, const void* k, const void* v, const float* g, const int8_t* s,
                        const float* beta, float scale, const float* h0, const float* h_ckpt,
                        const void* dout, const float* dht, float* dq, float* dk, float* dv,
                        float* dg, float* dbeta, float* dh0, void* workspace, size_t workspace_bytes,
                        ckda_stream_t stream) {
     CKDA_TRY(check_dtype(in_dtype));
-    CKDA_TRY(check_gate(gate));
+    CKDA_TRY(check_flags(flags));
     if (B < 0 || T < 0 || H < 0) return fail(CKDA_ERR_SHAPE, "negative size (B=%d, T=%d, H=%d)", B, T, H);
     CKDA_TRY(check_heads(DK, DV));
     if (too_big(static_cast<long long>(B) * T, H)) return fail(CKDA_ERR_UNSUPPORTED, "tensor too large");
     if (B * H == 0) return ok();
     ckda::BwdArgs a{};
     a.B = B; a.T = T; a.H = H; a.DK = DK; a.DV = DV; a.bf16 = in_dtype == CKDA_BF16;
-    a.head_gate = gate == CKDA_GATE_HEAD;
+    a.head_gate = (flags & CKDA_GATE_HEAD) != 0; a.qk_norm = (flags & CKDA_QK_L2NORM) != 0;
     a.q = q; a.k = k; a.v = v; a.g = g; a.s = s; a.beta = beta; a.scale = scale; a.h0 = h0;
     a.h_ckpt = h_ckpt; a.dout = dout; a.dht = dht; a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg;
     a.dbeta = dbeta; a.dh0 = dh0; a.cu = nullptr; a.ndocs = 0;
@@ -293,7 +294,7 @@ ckda_status_t ckda_bwd(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtyp
 }
 
 ckda_status_t ckda_bwd_varlen(int N, int T_total, const int32_t* cu, const int32_t* cu_dev, int H,
-                              int DK, int DV, ckda_dtype_t in_dtype, ckda_gate_t gate, const void* q,
+                              int DK, int DV, ckda_dtype_t in_dtype, ckda_flags_t flags, const void* q,
                               const void* k,
                               const void* v, const float* g, const int8_t* s, const float* beta,
                               float scale, const float* h0, const float* h_ckpt, const void* dout,
@@ -301,7 +302,7 @@ ckda_status_t ckda_bwd_varlen(int N, int T_total, const int32_t* cu, const int32
                               float* dbeta, float* dh0, void* workspace, size_t workspace_bytes,
                               ckda_stream_t stream) {
     CKDA_TRY(check_dtype(in_dtype));
-    CKDA_TRY(check_gate(gate));
+    CKDA_TRY(check_flags(flags));
     if (N < 0 || T_total < 0 || H < 0) return fail(CKDA_ERR_SHAPE, "negative size (N=%d, T=%d, H=%d)", N, T_total, H);
     CKDA_TRY(check_heads(DK, DV));
     CKDA_TRY(check_varlen_sizes(N, T_total, H));
@@ -310,7 +311,7 @@ ckda_status_t ckda_bwd_varlen(int N, int T_total, const int32_t* cu, const int32
     CKDA_REQUIRE(cu_dev);
     ckda::BwdArgs a{};
     a.B = 1; a.T = T_total; a.H = H; a.DK = DK; a.DV = DV; a.bf16 = in_dtype == CKDA_BF16;
-    a.head_gate = gate == CKDA_GATE_HEAD;
+    a.head_gate = (flags & CKDA_GATE_HEAD) != 0; a.qk_norm = (flags & CKDA_QK_L2NORM) != 0;
     a.q = q; a.k = k; a.v = v; a.g = g; a.s = s; a.beta = beta; a.scale = scale; a.h0 = h0;
     a.h_ckpt = h_ckpt; a.dout = dout; a.dht = dht; a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg;
     a.dbeta = dbeta; a.dh0 = dh0; a.cu = cu_dev; a.ndocs = N;

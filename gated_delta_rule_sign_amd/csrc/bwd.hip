@@ -268,6 +268,7 @@ struct BwdParams {
     const int32_t* cu;   // varlen document starts (device), or nullptr
     int ndocs;
     bool head_gate;      // g, s, dg per (token, head)
+    bool qk_norm;        // q, k L2-normalised per (token, head) inside the path
 };
 
 // chunk-head ch -> (head, token row of the chunk start, valid tokens).
@@ -348,13 +349,31 @@ __device__ __forceinline__ void gate_quad(const BwdParams& p, size_t row, int h,
     }
 }
 
+// sum of x over the CQ quads of one token row (adjacent lanes, CQ <= 32)
+template <int CQ>
+__device__ __forceinline__ float row_sum(float x) {
+#pragma unroll
+    for (int o = 1; o < CQ; o <<= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3]; }
+// x <- x / ||x|| per token row (every lane of the row calls it), inv <- 1 / ||x||
+template <int CQ, int NTOK>
+__device__ __forceinline__ void normalise_rows(f32x4 (&x)[NTOK], float (&inv)[NTOK]) {
+#pragma unroll
+    for (int i = 0; i < NTOK; ++i) {
+        inv[i] = inv_norm(row_sum<CQ>(dot4(x[i], x[i])));
+        x[i] *= inv[i];
+    }
+}
+
 __device__ __forceinline__ f32x4 exp2c4(f32x4 x) {
     return f32x4{exp2_clamped(x[0]), exp2_clamped(x[1]), exp2_clamped(x[2]), exp2_clamped(x[3])};
 }
 
 // prep: cumulative gate and sign product, anchored operands, V / dO copies
 // and S' = Diag(e^m) S
-template <typename Tin, int DK, int DV, bool HG>
+template <typename Tin, int DK, int DV, bool HG, bool NQK>
 __global__ void __launch_bounds__(512) bwd_prep_kernel(BwdParams p, BwdWs W) {
     using QS = QuadSeg<DK, 512>;
     using QV = QuadSeg<DV, 512>;
@@ -418,6 +437,11 @@ __global__ void __launch_bounds__(512) bwd_prep_kernel(BwdParams p, BwdWs W) {
         gv[i] = run;
         sg[i] = par;
         if (!valid) kv[i] = qv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if constexpr (NQK) {
+        float ik[NTOK], iq[NTOK];
+        normalise_rows<CQ>(kv, ik);
+        normalise_rows<CQ>(qv, iq);
     }
     segb[seg][q4] = run;
     segp[seg][q4] = par;
@@ -885,10 +909,12 @@ __global__ void __launch_bounds__(256) bwd_dA_kernel(BwdWs W) {
 //   db = Q1 dQ1 + K1 dK1 - K2 dK2 - KB dKB  (+ sum_t KB dKB + e^{b_L} sum_v dSt S
 //   at the last token),  dg = reverse cumulative sum of db over the chunk;
 // b, P and the anchored operands are recomputed from g, s, q, k (the same
-// scans as the prep).
+// scans as the prep).  With q and k normalised in the path (q^ = q/||q||),
+// the gradients above are those of q^ and k^, and the chain rule through the
+// normalisation gives dq = (dq^ - q^ (q^ . dq^)) / ||q||, the same for k.
 template <int DK> constexpr int final_threads() { return 512; }   // the prep's segmentation: identical b
 
-template <typename Tin, int DK, int DV, bool HG>
+template <typename Tin, int DK, int DV, bool HG, bool NQK>
 __global__ void __launch_bounds__(final_threads<DK>()) bwd_final_kernel(BwdParams p, BwdWs W) {
     constexpr int NTHR = final_threads<DK>();
     using QS = QuadSeg<DK, NTHR>;
@@ -918,6 +944,11 @@ __global__ void __launch_bounds__(final_threads<DK>()) bwd_final_kernel(BwdParam
         dk1[i] = *reinterpret_cast<const f32x4*>(W.dK1 + o);
         dk2[i] = *reinterpret_cast<const f32x4*>(W.dK2 + o);
         dkb[i] = *reinterpret_cast<const f32x4*>(W.dKB + o);
+    }
+    float ik[NTOK], iq[NTOK];
+    if constexpr (NQK) {
+        normalise_rows<CQ>(kv, ik);
+        normalise_rows<CQ>(qv, iq);
     }
     f32x4 run = {0.f, 0.f, 0.f, 0.f}, par = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
@@ -949,11 +980,17 @@ __global__ void __launch_bounds__(final_threads<DK>()) bwd_final_kernel(BwdParam
         const f32x4 e1 = exp2c4((b - m) * kLog2e), e2 = exp2c4((m - b) * kLog2e), e3 = exp2c4((bL - b) * kLog2e);
         const f32x4 kb = kf * e3;
         const f32x4 dbi = qf * e1 * dq1[i] + kf * e1 * dk1[i] - kf * e2 * dk2[i] - kb * dkb[i];
-        // dq = P dq~ and dk = P dk~
+        // dq = P dq~ and dk = P dk~ (then through the normalisation)
+        f32x4 dqo = P * (dq1[i] * e1), dko = P * (dk1[i] * e1 + dk2[i] * e2 + dkb[i] * e3);
+        if constexpr (NQK) {   // every lane of the row takes part in the sums
+            const float pq = row_sum<CQ>(dot4(qv[i], dqo)), pk = row_sum<CQ>(dot4(kv[i], dko));
+            dqo = iq[i] * (dqo - pq * qv[i]);
+            dko = ik[i] * (dko - pk * kv[i]);
+        }
         if (valid) {
             const size_t e = ((trow0 + tb + i) * p.H + ci.h) * DK + 4 * q4;
-            *reinterpret_cast<f32x4*>(p.dq + e) = P * (dq1[i] * e1);
-            *reinterpret_cast<f32x4*>(p.dk + e) = P * (dk1[i] * e1 + dk2[i] * e2 + dkb[i] * e3);
+            *reinterpret_cast<f32x4*>(p.dq + e) = dqo;
+            *reinterpret_cast<f32x4*>(p.dk + e) = dko;
         }
         dbv[i] = valid ? dbi : f32x4{0.f, 0.f, 0.f, 0.f};
         kbs += valid ? kb * dkb[i] : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1034,20 +1071,24 @@ __global__ void fill_copy_kernel(float* dst, const float* src, size_t n) {
         dst[i] = src ? src[i] : 0.f;
 }
 
-template <typename Tin, int DK, int DV, bool HG>
+template <typename Tin, int DK, int DV, bool HG, bool NQK>
 static hipError_t launch_chunk_pass_hg(bool final_pass, const BwdParams& p, const BwdWs& W, int NC,
                                        hipStream_t st) {
     if (final_pass)
-        hipLaunchKernelGGL((bwd_final_kernel<Tin, DK, DV, HG>), dim3(NC), dim3(final_threads<DK>()), 0, st, p, W);
+        hipLaunchKernelGGL((bwd_final_kernel<Tin, DK, DV, HG, NQK>), dim3(NC), dim3(final_threads<DK>()), 0, st, p,
+                           W);
     else
-        hipLaunchKernelGGL((bwd_prep_kernel<Tin, DK, DV, HG>), dim3(NC), dim3(512), 0, st, p, W);
+        hipLaunchKernelGGL((bwd_prep_kernel<Tin, DK, DV, HG, NQK>), dim3(NC), dim3(512), 0, st, p, W);
     return hipGetLastError();
 }
 
 template <typename Tin, int DK, int DV>
 static hipError_t launch_chunk_pass_t(bool final_pass, const BwdParams& p, const BwdWs& W, int NC, hipStream_t st) {
-    return p.head_gate ? launch_chunk_pass_hg<Tin, DK, DV, true>(final_pass, p, W, NC, st)
-                       : launch_chunk_pass_hg<Tin, DK, DV, false>(final_pass, p, W, NC, st);
+    if (p.qk_norm)
+        return p.head_gate ? launch_chunk_pass_hg<Tin, DK, DV, true, true>(final_pass, p, W, NC, st)
+                           : launch_chunk_pass_hg<Tin, DK, DV, false, true>(final_pass, p, W, NC, st);
+    return p.head_gate ? launch_chunk_pass_hg<Tin, DK, DV, true, false>(final_pass, p, W, NC, st)
+                       : launch_chunk_pass_hg<Tin, DK, DV, false, false>(final_pass, p, W, NC, st);
 }
 
 // the prep (final_pass false) or final pass over every chunk-head
@@ -1080,6 +1121,7 @@ hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t st) {
     p.h_ckpt = a.h_ckpt; p.dht = a.dht; p.h0 = a.h0; p.scale = a.scale;
     p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dg = a.dg; p.dbeta = a.dbeta; p.dh0 = a.dh0;
     p.B = a.B; p.T = a.T; p.H = a.H; p.NT = NT; p.cu = a.cu; p.ndocs = a.ndocs; p.head_gate = a.head_gate;
+    p.qk_norm = a.qk_norm;
     if (NC == 0) {
         // no tokens: dh0 = dht (or 0)
         const size_t n = static_cast<size_t>(nchains) * DK * DV;

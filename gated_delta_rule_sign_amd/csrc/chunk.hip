@@ -61,7 +61,8 @@ struct ChunkShape {
     static constexpr int L_TOTB = 0;                          // float [4][DK]
     static constexpr int L_TOTP = L_TOTB + 4 * DK * 4;        // uint32 [4][DK/4]
     static constexpr int L_BETA = L_TOTP + 4 * (DK / 4) * 4;  // float [64]
-    static constexpr int L_COLK = L_BETA + 64 * 4;            // operand [64][PC]
+    static constexpr int L_NRM = L_BETA + 64 * 4;             // float2 [NCG][64]: sum k^2, sum q^2
+    static constexpr int L_COLK = L_NRM + NCG * 64 * 8;       // operand [64][PC]
     static constexpr int L_COLKF = L_COLK + 64 * PC * 4;      // operand [32][PC]
     static constexpr int L_PART = L_COLKF + 32 * PC * 4;      // f32x4 [20][64]
     static constexpr int SZ_PART = NCG > 1 ? 20 * 64 * 16 : 0;
@@ -92,8 +93,9 @@ struct ChunkParams {
     int T, H, ndocs;
 };
 
-// HG: one gate per (token, head) (g, s [.., H]), broadcast over the channels
-template <typename Tin, int DK, int DV, bool HG>
+// HG: one gate per (token, head) (g, s [.., H]), broadcast over the channels;
+// NQK: q and k normalised per (token, head) over the key channels
+template <typename Tin, int DK, int DV, bool HG, bool NQK>
 // second bound: waves per SIMD (two 8-wave workgroups per CU -> 4, at most 128 VGPRs)
 __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(ChunkParams p)
 {
@@ -187,6 +189,23 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
         const float bt = p.beta[trow];
         if (cgi == 0 && gq == 0) beta_s[t] = valid ? bt : 0.f;
     }
+    float2* const nrm = reinterpret_cast<float2*>(smem + SH::L_NRM);
+    if constexpr (NQK) {   // sums of squares of the token's k and q: lanes, then channel groups
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KSW; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float kv = k8[ks].get(e), qv = q8[ks].get(e);
+                sk += kv * kv;
+                sq += qv * qv;
+            }
+        sk += __shfl_xor(sk, 16, 64);
+        sk += __shfl_xor(sk, 32, 64);
+        sq += __shfl_xor(sq, 16, 64);
+        sq += __shfl_xor(sq, 32, 64);
+        if (gq == 0) nrm[cgi * 64 + t] = make_float2(sk, sq);
+    }
     // ---- 1. in-tile scans (log2 units), tile totals to LDS -----------------
     if constexpr (HG) {   // every channel carries the head's gate: one scan per lane
         const float b1 = row_scan_add(bs[0] * kLog2e);
@@ -214,6 +233,17 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
     lds_sync();
 
     // ---- 2. exponentials and operands -------------------------------------
+    float ik = 1.f, iq = 1.f;   // 1 / ||k||, 1 / ||q|| (a zero vector stays zero)
+    if constexpr (NQK) {
+        float2 a = nrm[t];
+        if (SH::NCG > 1) {
+            const float2 b2 = nrm[64 + t];
+            a.x += b2.x;
+            a.y += b2.y;
+        }
+        ik = inv_norm(a.x);
+        iq = inv_norm(a.y);
+    }
     typename PR::F8 rkB[KSW], rqB[KSW];   // row operands (B side of the A/M tiles)
 #pragma unroll
     for (int ks = 0; ks < KSW; ++ks) {
@@ -266,8 +296,8 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
             for (int e = 0; e < 8; ++e) {
                 const uint32_t sgn = HG ? ((pw0 << 24) & 0x80000000u)   // all bytes equal
                                         : ((((e >> 2) ? pw1 : pw0) << (24 - 8 * (e & 3))) & 0x80000000u);
-                kf[e] = __uint_as_float(__float_as_uint(k8[ks].get(e)) ^ sgn);
-                qf[e] = __uint_as_float(__float_as_uint(q8[ks].get(e)) ^ sgn);
+                kf[e] = __uint_as_float(__float_as_uint(NQK ? k8[ks].get(e) * ik : k8[ks].get(e)) ^ sgn);
+                qf[e] = __uint_as_float(__float_as_uint(NQK ? q8[ks].get(e) * iq : q8[ks].get(e)) ^ sgn);
             }
         }
         CKDA_FENCE();
@@ -511,7 +541,7 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
     }
 }
 
-template <typename Tin, int DK, int DV, bool HG>
+template <typename Tin, int DK, int DV, bool HG, bool NQK>
 static hipError_t launch_chunk_t(const FwdArgs& A, int nslots, hipStream_t stream) {
     using SH = ChunkShape<DK>;
     ChunkParams p;
@@ -519,7 +549,7 @@ static hipError_t launch_chunk_t(const FwdArgs& A, int nslots, hipStream_t strea
     p.ws = static_cast<unsigned char*>(A.ws); p.cu = A.cu; p.T = A.T; p.H = A.H; p.ndocs = A.ndocs;
     const long long grid = static_cast<long long>(nslots) * A.H;
     if (grid == 0) return hipSuccess;
-    auto kern = ckda_chunk_kernel<Tin, DK, DV, HG>;
+    auto kern = ckda_chunk_kernel<Tin, DK, DV, HG, NQK>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, SH::LDS);
     if (e != hipSuccess) return e;
@@ -530,9 +560,13 @@ static hipError_t launch_chunk_t(const FwdArgs& A, int nslots, hipStream_t strea
 template <typename Tin>
 static hipError_t launch_chunk_dt(const FwdArgs& A, int nslots, hipStream_t stream) {
 #define CKDA_CHUNK(DK_, DV_)                                                                      \
-    if (A.DK == DK_ && A.DV == DV_)                                                               \
-        return A.head_gate ? launch_chunk_t<Tin, DK_, DV_, true>(A, nslots, stream)               \
-                           : launch_chunk_t<Tin, DK_, DV_, false>(A, nslots, stream);
+    if (A.DK == DK_ && A.DV == DV_) {                                                             \
+        if (A.qk_norm)                                                                            \
+            return A.head_gate ? launch_chunk_t<Tin, DK_, DV_, true, true>(A, nslots, stream)     \
+                               : launch_chunk_t<Tin, DK_, DV_, false, true>(A, nslots, stream);   \
+        return A.head_gate ? launch_chunk_t<Tin, DK_, DV_, true, false>(A, nslots, stream)        \
+                           : launch_chunk_t<Tin, DK_, DV_, false, false>(A, nslots, stream);      \
+    }
     CKDA_CHUNK(32, 32) CKDA_CHUNK(32, 64) CKDA_CHUNK(32, 128)
     CKDA_CHUNK(64, 32) CKDA_CHUNK(64, 64) CKDA_CHUNK(64, 128)
     CKDA_CHUNK(128, 32) CKDA_CHUNK(128, 64) CKDA_CHUNK(128, 128)

@@ -87,4 +87,12 @@ __device__ __forceinline__ float exp2_clamped(float x2) {
     return __builtin_amdgcn_exp2f(fminf(x2, 126.0f));
 }
 
+// 1 / sqrt(ss) for a vector's sum of squares ss, through the hardware
+// reciprocal square root (about 1 ulp on normal inputs).  A squared norm below
+// fp32's normal range (the zero vector among them) gives 0, so such a vector
+// normalises to zero instead of to infinities.
+__device__ __forceinline__ float inv_norm(float ss) {
+    return ss >= 1.17549435e-38f ? __builtin_amdgcn_rsqf(ss) : 0.f;
+}
+
 }  // namespace ckda

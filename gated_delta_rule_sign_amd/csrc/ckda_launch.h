@@ -11,6 +11,7 @@ struct DecodeArgs {
     int N, H, DK, DV;
     bool bf16;
     bool head_gate;   // g, s per head ([N,H]) instead of per channel
+    bool qk_norm;     // q, k normalised per head before use
     const void *q, *k, *v;
     const float* g;
     const int8_t* s;
@@ -39,6 +40,7 @@ struct FwdArgs {
     int B, T, H, DK, DV;
     bool bf16;
     bool head_gate;   // g, s per (token, head) instead of per channel
+    bool qk_norm;     // q, k normalised per (token, head) before use
     const void *q, *k, *v;
     const float* g;
     const int8_t* s;
@@ -64,6 +66,7 @@ struct BwdArgs {
     int B, T, H, DK, DV;
     bool bf16;
     bool head_gate;   // g, s, dg per (token, head) instead of per channel
+    bool qk_norm;     // q, k normalised per (token, head); dq, dk w.r.t. the raw q, k
     const void *q, *k, *v;
     const float* g;
     const int8_t* s;

@@ -18,13 +18,19 @@
 // band is streamed with 16-byte loads/stores, a wave covering whole rows.
 // The per-row parameters (a, kf, a*kf, a*qf) are formed once, by the first
 // DK threads while the state loads are in flight, and shared through LDS.
+//
+// With q and k normalised in the step (x/||x|| over the key channels, a zero
+// vector left at zero) the row parameters keep the raw q and k and the two
+// inverse norms ik, iq scale the column sums instead: x and y by ik and iq,
+// kf . qf by ik iq, and the state update's kf u^T through u ik.
 #include "ckda_device.h"
 #include "ckda_launch.h"
 
 namespace ckda {
 
-// HG: one gate per head (g, s [N,H]), broadcast over the channels
-template <typename Tin, int DK, int DV, bool HG>
+// HG: one gate per head (g, s [N,H]), broadcast over the channels;
+// NQK: q and k L2-normalised per (sequence, head)
+template <typename Tin, int DK, int DV, bool HG, bool NQK>
 __global__ void __launch_bounds__(256, 4)
 decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
                    const float* __restrict__ g, const int8_t* __restrict__ s,
@@ -40,7 +46,7 @@ decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
     __shared__ float4 red_x[RG][CG];
     __shared__ float4 red_y[RG][CG];
     __shared__ __align__(16) float row_a[DK], row_kf[DK], row_ak[DK], row_aq[DK];
-    __shared__ float red_kq[NWK];
+    __shared__ float red_kq[NWK], red_kk[NWK], red_qq[NWK];
 
     const int nh = blockIdx.x;                   // n * H + h
     const int t = threadIdx.x;
@@ -62,7 +68,7 @@ decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
 #pragma unroll
     for (int i = 0; i < R; ++i) S[i] = st[(r0 + i) * CG + cg];
     if (t < NWK * 64) {
-        float kq = 0.f;
+        float kq = 0.f, kk = 0.f, qq = 0.f;
         if (t < DK) {
             const int p = sp0 * s0;
             sign_prod[kbase + t] = static_cast<int8_t>(p);
@@ -75,10 +81,24 @@ decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
             row_ak[t] = a * kf;
             row_aq[t] = a * qf;
             kq = kf * qf;
+            kk = k0 * k0;
+            qq = q0 * q0;
         }
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) kq += __shfl_xor(kq, off, 64);
-        if ((t & 63) == 0) red_kq[t >> 6] = kq;
+        for (int off = 32; off > 0; off >>= 1) {
+            kq += __shfl_xor(kq, off, 64);
+            if constexpr (NQK) {
+                kk += __shfl_xor(kk, off, 64);
+                qq += __shfl_xor(qq, off, 64);
+            }
+        }
+        if ((t & 63) == 0) {
+            red_kq[t >> 6] = kq;
+            if constexpr (NQK) {
+                red_kk[t >> 6] = kk;
+                red_qq[t >> 6] = qq;
+            }
+        }
     }
     __syncthreads();
     float4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
@@ -101,6 +121,20 @@ decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
     float KQ = 0.f;
 #pragma unroll
     for (int j = 0; j < NWK; ++j) KQ += red_kq[j];
+    float ik = 1.f;
+    if constexpr (NQK) {
+        float KK = 0.f, QQ = 0.f;
+#pragma unroll
+        for (int j = 0; j < NWK; ++j) {
+            KK += red_kk[j];
+            QQ += red_qq[j];
+        }
+        ik = inv_norm(KK);
+        const float iq = inv_norm(QQ);
+        X.x *= ik; X.y *= ik; X.z *= ik; X.w *= ik;
+        Y.x *= iq; Y.y *= iq; Y.z *= iq; Y.w *= iq;
+        KQ *= ik * iq;
+    }
     const float bt = beta[nh];
     const int c0 = 4 * cg;
     float4 u;
@@ -116,6 +150,9 @@ decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
         ov.w = scale * (Y.w + KQ * u.w);
         reinterpret_cast<float4*>(o + vbase)[cg] = ov;
     }
+    if constexpr (NQK) {   // kf ik u^T
+        u.x *= ik; u.y *= ik; u.z *= ik; u.w *= ik;
+    }
 #pragma unroll
     for (int i = 0; i < R; ++i) {
         const float a = row_a[r0 + i], kf = row_kf[r0 + i];
@@ -130,7 +167,10 @@ decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
 
 template <typename Tin, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs& A, hipStream_t stream) {
-    auto kern = A.head_gate ? decode_step_kernel<Tin, DK, DV, true> : decode_step_kernel<Tin, DK, DV, false>;
+    auto kern = A.qk_norm ? (A.head_gate ? decode_step_kernel<Tin, DK, DV, true, true>
+                                         : decode_step_kernel<Tin, DK, DV, false, true>)
+                          : (A.head_gate ? decode_step_kernel<Tin, DK, DV, true, false>
+                                         : decode_step_kernel<Tin, DK, DV, false, false>);
     hipLaunchKernelGGL(kern, dim3(A.N * A.H), dim3(256), 0, stream,
                        static_cast<const Tin*>(A.q), static_cast<const Tin*>(A.k),
                        static_cast<const Tin*>(A.v), A.g, A.s, A.beta, A.scale, A.state,

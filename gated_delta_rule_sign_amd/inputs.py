@@ -24,6 +24,10 @@ per token and channel.  The gate is handed over as g = log|alpha| (fp32) and
 s (int8 +-1), the log-magnitude / sign split described on the model card
 ("complex-kda-1.3B-100B", first section).
 
+With qk="raw" (inputs for the in-path normalisation of q and k) q and k are
+not normalised: each (token, head) row is N(0,1) times a factor exp(N(0,1)),
+so row norms spread over about two decades around sqrt(DK).
+
 Values are drawn in float64 and rounded once, round-to-nearest-even, to the
 storage dtype.  bf16 tensors are kept as uint16 bit patterns (numpy has no
 bfloat16); ``widen`` returns the exact float64 value of any stored tensor.
@@ -47,6 +51,9 @@ WORKLOADS = {
     # layer_bf16 with one signed gate per (token, head): the head-scalar gate
     "layer_bf16_head_gate": dict(index=5, B=8, T=4096, H=16, DK=128, DV=128, dtype="bf16",
                                  gate="head"),
+    # layer_bf16 with raw q, k that the path L2-normalises itself
+    "layer_bf16_qk_norm": dict(index=6, B=8, T=4096, H=16, DK=128, DV=128, dtype="bf16",
+                               qk="raw"),
 }
 
 
@@ -118,10 +125,15 @@ class TokenInputs:
                     beta=self.beta.astype(np.float64))
 
 
+def _raw_rows(rng: np.random.Generator, shp: tuple) -> np.ndarray:
+    return rng.standard_normal(shp) * np.exp(rng.standard_normal(shp[:-1] + (1,)))
+
+
 def draw_tokens(rng: np.random.Generator, lead: tuple, H: int, DK: int, DV: int,
-                dtype: str, p_neg: float = 0.3, gate: str = "channel") -> TokenInputs:
+                dtype: str, p_neg: float = 0.3, gate: str = "channel", qk: str = "unit") -> TokenInputs:
     """Draw order: z, sign mask, q, k, v, beta.  gate="head" draws one g
-    and one s per (token, head) instead of per channel."""
+    and one s per (token, head) instead of per channel; qk="raw" leaves q
+    and k unnormalised with spread row norms."""
     shp_k = tuple(lead) + (H, DK)
     shp_v = tuple(lead) + (H, DV)
     shp_g = shp_k if gate == "channel" else tuple(lead) + (H,)
@@ -131,8 +143,12 @@ def draw_tokens(rng: np.random.Generator, lead: tuple, H: int, DK: int, DV: int,
     neg = rng.random(shp_g) < p_neg
     s = np.where(neg, -1, 1).astype(np.int8)
     del neg
-    q = to_storage(_l2norm_last(rng.standard_normal(shp_k)), dtype)
-    k = to_storage(_l2norm_last(rng.standard_normal(shp_k)), dtype)
+    if qk == "raw":
+        q = to_storage(_raw_rows(rng, shp_k), dtype)
+        k = to_storage(_raw_rows(rng, shp_k), dtype)
+    else:
+        q = to_storage(_l2norm_last(rng.standard_normal(shp_k)), dtype)
+        k = to_storage(_l2norm_last(rng.standard_normal(shp_k)), dtype)
     v = to_storage(rng.standard_normal(shp_v), dtype)
     beta = (2.0 * rng.random(tuple(lead) + (H,))).astype(np.float32)
     return TokenInputs(q=q, k=k, v=v, g=g, s=s, beta=beta, dtype=dtype)
@@ -183,9 +199,10 @@ class Workload:
     cu_seqlens: Optional[np.ndarray] = None  # int32 [ndocs+1]
 
 
-def make_forward(B, T, H, DK, DV, dtype, seed, with_do=False, h0_std=None, gate="channel") -> Workload:
+def make_forward(B, T, H, DK, DV, dtype, seed, with_do=False, h0_std=None, gate="channel",
+                 qk="unit") -> Workload:
     rng = np.random.default_rng(seed)
-    tok = draw_tokens(rng, (B, T), H, DK, DV, dtype, gate=gate)
+    tok = draw_tokens(rng, (B, T), H, DK, DV, dtype, gate=gate, qk=qk)
     h0 = draw_state(rng, (B, H, DK, DV), h0_std) if h0_std else None
     do = to_storage(rng.standard_normal((B, T, H, DV)), dtype) if with_do else None
     cfg = dict(B=B, T=T, H=H, DK=DK, DV=DV, dtype=dtype)
@@ -200,9 +217,10 @@ def make_workload(name: str, **override) -> Workload:
     seed = cfg.pop("seed", SEED_BASE + cfg["index"])
     rng = np.random.default_rng(seed)
     H, DK, DV, dt = cfg["H"], cfg["DK"], cfg["DV"], cfg["dtype"]
-    if name in ("tiny_fp32", "layer_bf16", "layer_bwd", "layer_bf16_head_gate"):
+    if name in ("tiny_fp32", "layer_bf16", "layer_bwd", "layer_bf16_head_gate", "layer_bf16_qk_norm"):
         B, T = cfg["B"], cfg["T"]
-        tok = draw_tokens(rng, (B, T), H, DK, DV, dt, gate=cfg.get("gate", "channel"))
+        tok = draw_tokens(rng, (B, T), H, DK, DV, dt, gate=cfg.get("gate", "channel"),
+                          qk=cfg.get("qk", "unit"))
         do = None
         if name == "layer_bwd":
             do = to_storage(rng.standard_normal((B, T, H, DV)), dt)

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define CKDA_ABI_VERSION 4
+#define CKDA_ABI_VERSION 5
 
 typedef enum {
     CKDA_OK = 0,
@@ -64,16 +64,21 @@ typedef enum {
     CKDA_BF16 = 1
 } ckda_dtype_t;
 
-/* Gate layout (the "Scalar Gate" and "Diagonal Gate" of the Complex KDA
- * paper page, section 3): CKDA_GATE_CHANNEL gives every key channel its own
- * g and s ([..., H, DK], the CKDA diagonal gate); CKDA_GATE_HEAD gives one g
- * and one s per head ([..., H], a signed Gated DeltaNet), which is the
- * channel gate with equal entries.  The head layout moves 5 gate bytes per
- * token-head instead of 640. */
-typedef enum {
-    CKDA_GATE_CHANNEL = 0,
-    CKDA_GATE_HEAD = 1
-} ckda_gate_t;
+/* Options of the forward, decode and backward calls (bitwise OR; 0 = the
+ * defaults):
+ *  CKDA_GATE_HEAD: one g and one s per (token, head) ([..., H]) instead of
+ *      per key channel ([..., H, DK], the CKDA diagonal gate): a signed Gated
+ *      DeltaNet (the "Scalar Gate" of the Complex KDA paper page, section 3),
+ *      i.e. the channel gate with equal entries.  5 gate bytes per token-head
+ *      instead of 640.
+ *  CKDA_QK_L2NORM: q and k are normalised per (token, head) over the key
+ *      channels, x / ||x|| (a zero vector stays zero), before the recurrence
+ *      uses them; the unit keys the pages' stability ranges assume.  The
+ *      backward returns gradients w.r.t. the raw q and k. */
+typedef uint32_t ckda_flags_t;
+#define CKDA_GATE_CHANNEL 0u
+#define CKDA_GATE_HEAD 1u
+#define CKDA_QK_L2NORM 2u
 
 /* opaque HIP stream (hipStream_t); NULL = the default stream */
 typedef void* ckda_stream_t;
@@ -103,7 +108,7 @@ ckda_status_t ckda_chunk_prep(int B, int T, int H, int DK, ckda_dtype_t in_dtype
  * Chunked forward over B equal-length sequences.
  *   q, k: [B,T,H,DK] in_dtype     v: [B,T,H,DV] in_dtype
  *   g: [B,T,H,DK] f32 (log|alpha|) s: [B,T,H,DK] int8 (+1/-1)
- *      (gate = CKDA_GATE_HEAD: g [B,T,H] f32, s [B,T,H] int8)
+ *      (flags & CKDA_GATE_HEAD: g [B,T,H] f32, s [B,T,H] int8)
  *   beta: [B,T,H] f32             scale: output multiplier
  *   h0: [B,H,DK,DV] f32 or NULL (zero initial state)
  *   o: [B,T,H,DV] f32 (written)   ht: [B,H,DK,DV] f32 or NULL (final state)
@@ -119,7 +124,7 @@ ckda_status_t ckda_chunk_prep(int B, int T, int H, int DK, ckda_dtype_t in_dtype
  * ---------------------------------------------------------------------- */
 size_t ckda_fwd_workspace_bytes(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype);
 ckda_status_t ckda_fwd_chunked(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype,
-                               ckda_gate_t gate, const void* q, const void* k, const void* v,
+                               ckda_flags_t flags, const void* q, const void* k, const void* v,
                                const float* g, const int8_t* s, const float* beta, float scale,
                                const float* h0, float* o, float* ht, float* h_ckpt,
                                void* workspace, size_t workspace_bytes, ckda_stream_t stream);
@@ -134,7 +139,7 @@ ckda_status_t ckda_fwd_chunked(int B, int T, int H, int DK, int DV, ckda_dtype_t
  *                    validate it (0-based, non-decreasing, ends at T_total)
  *   cu_seqlens_dev:  the same N+1 values in device memory, read by the kernel
  *   q, k, g, s: [T_total,H,DK]; v, o: [T_total,H,DV]; beta: [T_total,H]
- *   (gate = CKDA_GATE_HEAD: g, s [T_total,H])
+ *   (flags & CKDA_GATE_HEAD: g, s [T_total,H])
  *   h0, ht: [N,H,DK,DV] f32, each nullable.  Documents may be empty (their
  *   ht is their h0, or zero).
  *   h_ckpt: nullable; else [ckda_varlen_chunk_slots(N, T_total), H, DK, DV]
@@ -149,7 +154,7 @@ int ckda_varlen_chunk_slots(int N, int T_total);
 size_t ckda_fwd_varlen_workspace_bytes(int N, int T_total, int H, int DK, int DV, ckda_dtype_t in_dtype);
 ckda_status_t ckda_fwd_varlen(int N, int T_total, const int32_t* cu_seqlens_host,
                               const int32_t* cu_seqlens_dev, int H, int DK, int DV,
-                              ckda_dtype_t in_dtype, ckda_gate_t gate, const void* q, const void* k,
+                              ckda_dtype_t in_dtype, ckda_flags_t flags, const void* q, const void* k,
                               const void* v, const float* g, const int8_t* s, const float* beta,
                               float scale, const float* h0, float* o, float* ht, float* h_ckpt,
                               void* workspace,
@@ -160,7 +165,7 @@ ckda_status_t ckda_fwd_varlen(int N, int T_total, const int32_t* cu_seqlens_host
  * carried in the folded frame: the true state is Diag(sign_prod) * state.
  * A prefill's final state enters as state = ht, sign_prod = +1.
  *   q, k: [N,H,DK] in_dtype;  v: [N,H,DV] in_dtype
- *   g, s: [N,H,DK] f32 / int8 (gate = CKDA_GATE_HEAD: [N,H]);  beta: [N,H] f32
+ *   g, s: [N,H,DK] f32 / int8 (flags & CKDA_GATE_HEAD: [N,H]);  beta: [N,H] f32
  *   state: [N,H,DK,DV] f32, updated in place
  *   sign_prod: [N,H,DK] int8 (+1/-1), updated in place (times s; with the
  *              head gate every channel takes the head's s)
@@ -168,7 +173,7 @@ ckda_status_t ckda_fwd_varlen(int N, int T_total, const int32_t* cu_seqlens_host
  * Each state element is read once and written once.
  * ---------------------------------------------------------------------- */
 ckda_status_t ckda_decode_step(int N, int H, int DK, int DV, ckda_dtype_t in_dtype,
-                               ckda_gate_t gate, const void* q, const void* k, const void* v, const float* g,
+                               ckda_flags_t flags, const void* q, const void* k, const void* v, const float* g,
                                const int8_t* s, const float* beta, float scale, float* state,
                                int8_t* sign_prod, float* o, ckda_stream_t stream);
 
@@ -179,7 +184,7 @@ ckda_status_t ckda_decode_step(int N, int H, int DK, int DV, ckda_dtype_t in_dty
  *           inputs (required)
  *   dout: [B,T,H,DV] in_dtype;  dht: [B,H,DK,DV] f32 or NULL (zero)
  *   dq, dk, dg: [B,T,H,DK] f32;  dv: [B,T,H,DV] f32;  dbeta: [B,T,H] f32
- *   (gate = CKDA_GATE_HEAD: g, s and dg are [B,T,H]; dg is then the sum
+ *   (flags & CKDA_GATE_HEAD: g, s and dg are [B,T,H]; dg is then the sum
  *   over channels of the channel-gate gradient)
  *   dh0: [B,H,DK,DV] f32 or NULL
  *   workspace: ckda_bwd_workspace_bytes(...) bytes of device memory
@@ -187,7 +192,7 @@ ckda_status_t ckda_decode_step(int N, int H, int DK, int DV, ckda_dtype_t in_dty
  * ---------------------------------------------------------------------- */
 size_t ckda_bwd_workspace_bytes(int B, int T, int H, int DK, int DV);
 ckda_status_t ckda_bwd(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype,
-                       ckda_gate_t gate, const void* q, const void* k, const void* v, const float* g,
+                       ckda_flags_t flags, const void* q, const void* k, const void* v, const float* g,
                        const int8_t* s, const float* beta, float scale, const float* h0,
                        const float* h_ckpt, const void* dout, const float* dht,
                        float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0,
@@ -201,7 +206,7 @@ ckda_status_t ckda_bwd(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtyp
  *           inputs (required when T_total > 0)
  *   dout: [T_total,H,DV] in_dtype;  dht: [N,H,DK,DV] f32 or NULL (zero)
  *   dq, dk, dg: [T_total,H,DK] f32;  dv: [T_total,H,DV];  dbeta: [T_total,H]
- *   (gate = CKDA_GATE_HEAD: g, s, dg [T_total,H])
+ *   (flags & CKDA_GATE_HEAD: g, s, dg [T_total,H])
  *   dh0: [N,H,DK,DV] f32 or NULL
  *   workspace: ckda_bwd_varlen_workspace_bytes(...) bytes of device memory
  * Conventions and errors as for ckda_bwd and ckda_fwd_varlen.
@@ -209,7 +214,7 @@ ckda_status_t ckda_bwd(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtyp
 size_t ckda_bwd_varlen_workspace_bytes(int N, int T_total, int H, int DK, int DV);
 ckda_status_t ckda_bwd_varlen(int N, int T_total, const int32_t* cu_seqlens_host,
                               const int32_t* cu_seqlens_dev, int H, int DK, int DV,
-                              ckda_dtype_t in_dtype, ckda_gate_t gate, const void* q, const void* k,
+                              ckda_dtype_t in_dtype, ckda_flags_t flags, const void* q, const void* k,
                               const void* v, const float* g, const int8_t* s, const float* beta,
                               float scale, const float* h0, const float* h_ckpt, const void* dout,
                               const float* dht, float* dq, float* dk, float* dv, float* dg,
