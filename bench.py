@@ -8,10 +8,11 @@ chunk), over the mixer workload of the 1.36B model: B=8, T=4096, H=16,
 dk=dv=128, bf16 q/k/v, fp32 gates, state and outputs.  The JSON line's ``value`` is that forward's
 tokens/s; the decode workload (256 sequences x 16 heads, 512 recurrent
 steps) is reported in the same line as state-streaming GB/s, the backward as
-tokens/s, and the same forward with one gate per (token, head) as tokens/s.
+tokens/s, and the same forward with one gate per (token, head), and with
+raw q and k that the path L2-normalises itself, as tokens/s.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       [--only fwd|fwd_head_gate|decode|bwd|copy]
+       [--only fwd|fwd_head_gate|fwd_qk_norm|decode|bwd|copy]
 """
 from __future__ import annotations
 
@@ -106,7 +107,8 @@ def bench_fwd(torch, steps, warmup, workload="layer_bf16"):
     ht = torch.empty((B, H, 128, 128), dtype=torch.float32, device="cuda:0")
     ws = torch.empty(ckda.fwd_workspace_bytes(B, T, H, DK, 128, torch.bfloat16), dtype=torch.uint8,
                      device="cuda:0")
-    fn = lambda: ckda.fwd(**d, o=o, ht=ht, workspace=ws)
+    qk_norm = w.cfg.get("qk") == "raw"   # raw q, k: the path normalises them
+    fn = lambda: ckda.fwd(**d, o=o, ht=ht, workspace=ws, qk_norm=qk_norm)
     log("timing forward")
     wall, per = time_kernel_launches(torch, fn, steps, warmup)
     tokens = B * T
@@ -221,7 +223,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "fwd_head_gate", "decode", "bwd", "copy"], default=None)
+    ap.add_argument("--only", choices=["fwd", "fwd_head_gate", "fwd_qk_norm", "decode", "bwd", "copy"],
+                    default=None)
     ap.add_argument("--decode-steps", type=int, default=512)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -245,8 +248,9 @@ def main():
         print(json.dumps(bench_bwd(torch, args.steps, args.warmup)))
         return
 
-    if args.only == "fwd_head_gate":
-        fh = bench_fwd(torch, args.steps, args.warmup, "layer_bf16_head_gate")
+    if args.only in ("fwd_head_gate", "fwd_qk_norm"):
+        wl = "layer_bf16_head_gate" if args.only == "fwd_head_gate" else "layer_bf16_qk_norm"
+        fh = bench_fwd(torch, args.steps, args.warmup, wl)
         print(json.dumps({k: v for k, v in fh.items() if k not in ("w", "launch_all")}))
         return
     fw = bench_fwd(torch, args.steps, args.warmup)
@@ -256,6 +260,7 @@ def main():
     dec = bench_decode(torch, args.decode_steps)
     bw = bench_bwd(torch, max(3, args.steps // 4), 1)
     fh = bench_fwd(torch, args.steps, args.warmup, "layer_bf16_head_gate")
+    fq = bench_fwd(torch, args.steps, args.warmup, "layer_bf16_qk_norm")
     cpu = None if args.no_cpu else cpu_baseline(fw["w"])
 
     achieved = fw["bytes"] / (fw["launch_ms"] * 1e-3) / 1e9
@@ -298,6 +303,12 @@ def main():
                               "avg_launch_ms": fh["launch_ms"], "algorithmic_bytes": fh["bytes"],
                               "achieved_gbs": fh["bytes"] / (fh["launch_ms"] * 1e-3) / 1e9,
                               "frac_of_hbm_peak": fh["bytes"] / (fh["launch_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "forward_qk_norm": {"workload": "layer_bf16_qk_norm: layer_bf16 with raw q, k (row norms spread "
+                                        "over two decades) L2-normalised inside the path",
+                            "unit": "tokens/s", "value": fq["tokens"] / (fq["ms"] * 1e-3), "ms": fq["ms"],
+                            "avg_launch_ms": fq["launch_ms"], "algorithmic_bytes": fq["bytes"],
+                            "achieved_gbs": fq["bytes"] / (fq["launch_ms"] * 1e-3) / 1e9,
+                            "frac_of_hbm_peak": fq["bytes"] / (fq["launch_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
