@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
     L.ckda_bwd_varlen.argtypes = [I, I, P, P, I, I, I, I, U, P, P, P, P, P, P, F, P, P, P, P,
                                   P, P, P, P, P, P, P, S, P]
     L.ckda_bwd_varlen.restype = I
+    L.ckda_set_segment_chunks.argtypes = [I]
+    L.ckda_set_segment_chunks.restype = I
     _lib = L
     return L
 
@@ -203,6 +205,13 @@ def fwd(q, k, v, g, s, beta, scale: float = 1.0, h0=None, want_ht: bool = True,
                                   _ptr(beta), float(scale), _ptr(h0), _ptr(o), _ptr(ht),
                                   _ptr(h_ckpt), _ptr(workspace), wsb, _stream()))
     return o, ht, h_ckpt
+
+
+def set_segment_chunks(G: int) -> None:
+    """Segment length of the forward's state pass (ckda_set_segment_chunks):
+    0 automatic (default), < 0 whole chains only, >= 16 segments of G chunks
+    for every chain longer than that.  Process-wide."""
+    _check(lib().ckda_set_segment_chunks(int(G)))
 
 
 def varlen_chunk_slots(N, T_total) -> int:

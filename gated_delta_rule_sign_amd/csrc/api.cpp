@@ -145,13 +145,24 @@ ckda_status_t ckda_chunk_prep(int B, int T, int H, int DK, ckda_dtype_t in_dtype
 
 size_t ckda_fwd_workspace_bytes(int B, int T, int H, int DK, int DV, ckda_dtype_t dt) {
     if (B < 0 || T < 0 || H < 0 || !head_ok(DK) || !head_ok(DV) || (dt != CKDA_F32 && dt != CKDA_BF16)) return 0;
-    return ckda::fwd_workspace_bytes(fwd_slots(B, T), H, DK, DV, dt == CKDA_BF16);
+    const int G = ckda::segment_min_chunks();
+    const long long nss = static_cast<long long>(B) * (((T + 63) / 64 + G - 1) / G);
+    return ckda::fwd_workspace_bytes_full(fwd_slots(B, T), static_cast<int>(nss), H, DK, DV, dt == CKDA_BF16);
 }
 
 size_t ckda_fwd_varlen_workspace_bytes(int N, int T_total, int H, int DK, int DV, ckda_dtype_t dt) {
     if (N < 0 || T_total < 0 || H < 0 || !head_ok(DK) || !head_ok(DV) || (dt != CKDA_F32 && dt != CKDA_BF16))
         return 0;
-    return ckda::fwd_workspace_bytes(varlen_slots(N, T_total), H, DK, DV, dt == CKDA_BF16);
+    const int G = ckda::segment_min_chunks();
+    const int nss = (T_total + 64 * G - 1) / (64 * G) + N;
+    return ckda::fwd_workspace_bytes_full(varlen_slots(N, T_total), nss, H, DK, DV, dt == CKDA_BF16);
+}
+
+ckda_status_t ckda_set_segment_chunks(int G) {
+    if (G > 0 && G < ckda::segment_min_chunks())
+        return fail(CKDA_ERR_UNSUPPORTED, "segments of %d chunks: at least %d", G, ckda::segment_min_chunks());
+    ckda::set_segment_chunks(G);
+    return ok();
 }
 
 ckda_status_t ckda_fwd_chunked(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype,
@@ -180,7 +191,8 @@ ckda_status_t ckda_fwd_chunked(int B, int T, int H, int DK, int DV, ckda_dtype_t
     a.B = B; a.T = T; a.H = H; a.DK = DK; a.DV = DV; a.bf16 = in_dtype == CKDA_BF16;
     a.head_gate = (flags & CKDA_GATE_HEAD) != 0; a.qk_norm = (flags & CKDA_QK_L2NORM) != 0;
     a.q = q; a.k = k; a.v = v; a.g = g; a.s = s; a.beta = beta; a.scale = scale;
-    a.h0 = h0; a.o = o; a.ht = ht; a.h_ckpt = h_ckpt; a.cu = nullptr; a.ndocs = 0; a.ws = workspace;
+    a.h0 = h0; a.o = o; a.ht = ht; a.h_ckpt = h_ckpt; a.cu = nullptr; a.cu_host = nullptr; a.ndocs = 0;
+    a.ws = workspace; a.ws_bytes = workspace_bytes;
     return hip_status(ckda::launch_fwd(a, nslots, static_cast<hipStream_t>(stream)), "ckda_fwd_chunked launch");
 }
 
@@ -212,7 +224,7 @@ ckda_status_t ckda_fwd_varlen(int N, int T_total, const int32_t* cu, const int32
     a.head_gate = (flags & CKDA_GATE_HEAD) != 0; a.qk_norm = (flags & CKDA_QK_L2NORM) != 0;
     a.q = q; a.k = k; a.v = v; a.g = g; a.s = s; a.beta = beta; a.scale = scale;
     a.h0 = h0; a.o = o; a.ht = ht; a.h_ckpt = h_ckpt;
-    a.cu = cu_dev; a.ndocs = N; a.ws = workspace;
+    a.cu = cu_dev; a.cu_host = cu; a.ndocs = N; a.ws = workspace; a.ws_bytes = workspace_bytes;
     return hip_status(ckda::launch_fwd(a, nslots, static_cast<hipStream_t>(stream)), "ckda_fwd_varlen launch");
 }
 

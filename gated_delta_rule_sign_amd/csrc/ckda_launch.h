@@ -53,11 +53,20 @@ struct FwdArgs {
     // varlen: document n covers tokens cu[n] .. cu[n+1]-1 (device pointer);
     // nullptr selects the equal-length mode
     const int32_t* cu;
+    const int32_t* cu_host;   // the same offsets on the host (varlen), for the state-pass plan
     int ndocs;
-    void* ws;   // fwd_workspace_bytes(nslots, ...) bytes
+    void* ws;          // at least fwd_workspace_bytes(nslots, ...) bytes
+    size_t ws_bytes;   // its size: room beyond the records enables the segmented state pass
 };
 // nslots: chunk slots (equal-length: B * ceil(T/64); varlen: ceil(T/64) + N)
+// records only (the minimum workspace)
 size_t fwd_workspace_bytes(int nslots, int H, int DK, int DV, bool bf16);
+// records plus the segment buffers for up to nsslots_max segment slots
+size_t fwd_workspace_bytes_full(int nslots, int nsslots_max, int H, int DK, int DV, bool bf16);
+// segment length of the state pass: 0 automatic, < 0 never, >= segment_min_chunks() forced
+void set_segment_chunks(int G);
+int segment_chunks();
+int segment_min_chunks();
 hipError_t launch_chunk(const FwdArgs& a, int nslots, hipStream_t stream);
 hipError_t launch_state(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, int nslots, hipStream_t stream);

@@ -24,6 +24,22 @@
 // layout (rows 4g..4g+3 of tiles 2k and 2k+1), so S and U feed the B side
 // straight from their accumulator layout; the A side reads the matching
 // elements (columns 32k + 4g .. +3 and 32k + 16 + 4g .. +3).
+//
+// Segment mode (chains much longer than the GPU has parallel work for):
+// the chunk maps are affine in the state, S' = A_c S + B_c with
+// A_c = Diag(d) - KbT W, and every column of S evolves on its own.  A chain
+// of chunks is cut into segments of G chunks.  Phase 1 runs the first
+// segment of each chain from its true start (outputs included) and, for
+// every middle segment, the value columns from a zero start (giving H_s,
+// the segment's end state from zero) plus DK "transition" columns started
+// from the identity with u = 0 (giving P_s = the product of the segment's
+// A_c).  Phase 2 (ckda_seg_scan_kernel) chains the starts:
+// start_{s+1} = P_s start_s + H_s.  Phase 3 reruns segments 1 .. n-1 from
+// their true starts and writes their outputs, checkpoints and final state.
+#include <algorithm>
+#include <atomic>
+#include <vector>
+
 #include "ckda_device.h"
 #include "ckda_launch.h"
 #include "ckda_mfma.h"
@@ -40,6 +56,7 @@ struct StateShape {
     static constexpr int NT = 256;                 // threads per role (4 compute + 4 loader waves)
     static constexpr int BV = DV < 64 ? DV : 64;   // value columns per workgroup
     static constexpr int NSLICE = DV / BV;
+    static constexpr int NTS = (DK + BV - 1) / BV;   // transition slices over the DK columns of P_s
     static constexpr int NWC = BV / 16;            // waves that own columns
     static constexpr int RT = DK / 16;             // 16-row tiles of S
     static constexpr int ES = RC::ES, NP = RC::NP;
@@ -96,9 +113,20 @@ struct StateParams {
     const int32_t* cu;   // varlen document starts (device), or nullptr
     float scale;
     int B, T, H, ndocs;
+    // segment mode: G chunks per segment; segment s of chain d sits in
+    // segment slot floor(cu[d] / 64G) + d + s (equal-length: d * nseg + s)
+    int G, phase, nsslots;
+    float* seg_start;   // [nsslots][H][DK][DV] start state of segments s >= 1
+    float* seg_h;       // [nsslots][H][DK][DV] end state from a zero start (middle segments)
+    float* seg_p;       // [nsslots][H][DK][DK] segment map P_s (middle segments)
 };
 
-template <typename Tin, int DK, int DV, bool CKPT>
+// first segment slot of chain d (varlen document start cu_d)
+__host__ __device__ inline int seg_slot0(int cu_d, int d, int G) { return cu_d / (64 * G) + d; }
+
+// SEG: segment mode, phase p.phase (1 or 3); otherwise one workgroup runs a
+// whole chain's value slice
+template <typename Tin, int DK, int DV, bool CKPT, bool SEG>
 __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
 {
     using SH = StateShape<Tin, DK, DV>;
@@ -108,32 +136,55 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int H = p.H;
-    const int nchains = p.cu ? p.ndocs * H : p.B * H;
-    int chain, slice;
+    // work items: chains (or, in segment mode, segment slots) x heads; NS
+    // slices per item: the value slices, then (segment phase 1) the
+    // transition slices over the DK columns of P_s
+    const int NS = (SEG && p.phase == 1) ? SH::NSLICE + SH::NTS : SH::NSLICE;
+    const int nitems = SEG ? p.nsslots * H : (p.cu ? p.ndocs * H : p.B * H);
+    int item, slice;
     {
         const int bid = blockIdx.x;
-        if (SH::NSLICE == 1) {
-            chain = bid;
+        if (NS == 1) {
+            item = bid;
             slice = 0;
         } else {
-            // the slices of one chain land on the same XCD (workgroups are
+            // the slices of one item land on the same XCD (workgroups are
             // dealt round-robin over 8 XCDs), so the record is read from HBM
             // once and the other slices hit that XCD's L2
-            const int grp = 8 * SH::NSLICE;
-            const int full = (nchains / 8) * grp;
+            const int grp = 8 * NS;
+            const int full = (nitems / 8) * grp;
             if (bid < full) {
                 const int r = bid % grp;
-                chain = (bid / grp) * 8 + (r % 8);
+                item = (bid / grp) * 8 + (r % 8);
                 slice = r / 8;
             } else {
                 const int r = bid - full;
-                chain = (nchains / 8) * 8 + r / SH::NSLICE;
-                slice = r % SH::NSLICE;
+                item = (nitems / 8) * 8 + r / NS;
+                slice = r % NS;
             }
         }
     }
-    const int h = chain % H;
-    const int sidx = chain / H;
+    const int h = item % H;
+    const int NTC = (p.T + 63) / 64;   // equal-length chunks per sequence
+    int sidx, seg = 0, ss = 0;
+    if (!SEG) {
+        sidx = item / H;
+    } else {
+        ss = item / H;
+        if (p.cu) {   // the document whose segment slots hold ss
+            int lo = 0, hi = p.ndocs - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (seg_slot0(p.cu[mid], mid, p.G) <= ss) lo = mid; else hi = mid - 1;
+            }
+            sidx = lo;
+            seg = ss - seg_slot0(p.cu[lo], lo, p.G);
+        } else {
+            const int nsegT = (NTC + p.G - 1) / p.G;
+            sidx = ss / nsegT;
+            seg = ss - sidx * nsegT;
+        }
+    }
     int tok0, len, slot0;
     if (p.cu) {
         tok0 = p.cu[sidx];
@@ -142,10 +193,24 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
     } else {
         tok0 = sidx * p.T;
         len = p.T;
-        slot0 = sidx * ((p.T + 63) / 64);
+        slot0 = sidx * NTC;
     }
     const int nchunks = (len + 63) / 64;
-    const int vt0 = (slice * SH::BV) / 16;   // first 16-column tile of the slice
+    int jbeg = 0, nloop = nchunks, nseg = 1;
+    bool trans = false, out_on = true;
+    if (SEG) {
+        nseg = (nchunks + p.G - 1) / p.G;
+        trans = slice >= SH::NSLICE;
+        const bool run = p.phase == 1 ? (seg == 0 ? !trans : seg < nseg - 1) : (seg >= 1 && seg < nseg);
+        if (!run) return;   // the whole workgroup, before any barrier
+        jbeg = seg * p.G;
+        nloop = min(p.G, nchunks - jbeg);
+        out_on = p.phase == 3 || seg == 0;
+    }
+    // first 16-column tile of the slice (transition slices: columns of P_s)
+    const int vt0 = ((trans ? slice - SH::NSLICE : slice) * SH::BV) / 16;
+    const int vtu0 = trans ? 0 : vt0;   // u tiles the loaders stage (unused by transition slices)
+    const int slotb = slot0 + jbeg;     // record slot of the first chunk walked
     const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
 
     if (w >= 4) {
@@ -167,7 +232,7 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
         constexpr int O_M = NK_, O_D = O_M + NM_, O_U = O_D + ND_, NB = O_U + NU_;
         static_assert(StW::FULL && StQ::FULL && StK::FULL && StM::FULL && StU::FULL, "unguarded staging loads");
         u32x4 ga[NA], gb[NB];   // native vectors (a struct copy would keep them in scratch)
-#define CKDA_REC(J) reinterpret_cast<const u32x4*>(p.ws + (static_cast<size_t>(slot0 + (J)) * H + h) * RC::BYTES + opaque_zero())
+#define CKDA_REC(J) reinterpret_cast<const u32x4*>(p.ws + (static_cast<size_t>(slotb + (J)) * H + h) * RC::BYTES + opaque_zero())
 #define CKDA_LOAD_A(J)                                                                                       \
         {                                                                                                    \
             const u32x4* g_ = CKDA_REC(J);                                                                   \
@@ -186,7 +251,7 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
             _Pragma("unroll") for (int i_ = 0; i_ < NU_; ++i_) {                                             \
                 const int u_ = t_ + NT * i_;                                                                 \
                 const int J_ = u_ / (NWC * 64), r_ = u_ % (NWC * 64);                                        \
-                gb[O_U + i_] = g_[RC::OFF_U / 16 + (J_ * (DV / 16) + vt0) * 64 + r_];                        \
+                gb[O_U + i_] = g_[RC::OFF_U / 16 + (J_ * (DV / 16) + vtu0) * 64 + r_];                       \
             }                                                                                                \
         }
 #define CKDA_STORE_A()                                                                                       \
@@ -208,23 +273,29 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
                 StM::put(sm_ + SH::L_M + StM::lds_off(t_, i_), gb[O_M + i_]);                                \
             _Pragma("unroll") for (int i_ = 0; i_ < ND_; ++i_)                                               \
                 if (StD::has(t_, i_)) *reinterpret_cast<u32x4*>(sm_ + SH::L_D + StD::lds_off(t_, i_)) = gb[O_D + i_]; \
-            _Pragma("unroll") for (int i_ = 0; i_ < NU_; ++i_)                                               \
-                *reinterpret_cast<u32x4*>(sm_ + SH::L_U + StU::lds_off(t_, i_)) = gb[O_U + i_];              \
+            if (!(SEG && trans))                                                                             \
+                _Pragma("unroll") for (int i_ = 0; i_ < NU_; ++i_)                                           \
+                    *reinterpret_cast<u32x4*>(sm_ + SH::L_U + StU::lds_off(t_, i_)) = gb[O_U + i_];          \
         }
-        if (nchunks > 0) {
+        // transition slices build P_s, the maps' linear part: their u is zero
+        if (SEG && trans) {
+            for (int u_ = opaque_tid() - NT; u_ < 4 * NWC * 64; u_ += NT)
+                *reinterpret_cast<u32x4*>(smem + SH::L_U + 16 * u_) = u32x4{0u, 0u, 0u, 0u};
+        }
+        if (nloop > 0) {
             CKDA_LOAD_A(0)
             CKDA_LOAD_B(0)
             CKDA_STORE_A()
             CKDA_STORE_B()
-            CKDA_LOAD_A(min(1, nchunks - 1))
+            CKDA_LOAD_A(min(1, nloop - 1))
         }
         // (the last chunks re-read the final record: no branches)
-        for (int j = 0; j < nchunks; ++j) {
+        for (int j = 0; j < nloop; ++j) {
             lds_sync();   // 0: record j complete in LDS
-            CKDA_LOAD_B(min(j + 1, nchunks - 1))
+            CKDA_LOAD_B(min(j + 1, nloop - 1))
             lds_sync();   // 1: W, Qh of chunk j consumed
             CKDA_STORE_A()
-            CKDA_LOAD_A(min(j + 2, nchunks - 1))
+            CKDA_LOAD_A(min(j + 2, nloop - 1))
             lds_sync();   // 2: chunk j consumed
             CKDA_STORE_B()
         }
@@ -238,7 +309,8 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
 
     // ================= compute waves ==========================================
     const size_t st_off = (static_cast<size_t>(sidx) * H + h) * DK * DV;
-    const bool has_col = w < NWC;
+    // (transition slices: only columns below DK exist)
+    const bool has_col = w < NWC && (!trans || 16 * (vt0 + w) < DK);
     // the wave's 16-column tile of DV; waves without columns (DV < 64) run
     // the slice's last tile again with their stores switched off, so the
     // loop body has no branches around vector memory (the compiler's wait
@@ -247,18 +319,30 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
     const int vt = vt0 + wt;
 
     // ---- state: lane (n, g) holds rows 16rt + 4g + i of column 16vt + n ----
+    // start: h0 (or zero); segment mode: the identity for transition slices,
+    // zero for the middle segments of phase 1, the scanned start in phase 3
+    const float* src = p.h0 ? p.h0 + st_off : nullptr;
+    if (SEG && seg > 0) src = p.phase == 3 ? p.seg_start + (static_cast<size_t>(ss) * H + h) * DK * DV : nullptr;
     f32x4 S[RT];
     {
         const int l = threadIdx.x & 63, gq = l >> 4, col = 16 * vt + (l & 15);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S[rt][i] = (has_col && p.h0) ? p.h0[st_off + static_cast<size_t>(16 * rt + 4 * gq + i) * DV + col] : 0.f;
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * rt + 4 * gq + i;
+                S[rt][i] = trans ? (row == col ? 1.f : 0.f)
+                                 : ((has_col && src) ? src[static_cast<size_t>(row) * DV + col] : 0.f);
+            }
     }
 
-    for (int j = 0; j < nchunks; ++j) {
-        const int c0 = 64 * j;
+    // checkpoint of walked chunk j: equal-length [B,H,NT,DK,DV]; varlen
+    // [slot][H][DK][DV] (the record's slot)
+    const size_t ck0 = p.cu ? static_cast<size_t>(slotb) * H + h
+                            : (static_cast<size_t>(sidx) * H + h) * static_cast<size_t>(nchunks) + jbeg;
+    const int ckstep = p.cu ? H : 1;
+    for (int j = 0; j < nloop; ++j) {
+        const int c0 = 64 * (jbeg + j);
         const int L = min(64, len - c0);
         lds_sync();   // 0: record of chunk j in LDS
         {
@@ -273,11 +357,8 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
             f32x4 u[4];
 #pragma unroll
             for (int J = 0; J < 4; ++J) u[J] = *reinterpret_cast<const f32x4*>(sm + SH::L_U + ((J * NWC + wt) * 64 + l) * 16);
-            if (CKPT) {   // the state at the chunk start (waves without columns store nothing)
-                // equal-length: [B,H,NT,DK,DV]; varlen: [slot][H][DK][DV] (the record's slot)
-                const size_t ci = p.cu ? static_cast<size_t>(slot0 + j) * H + h
-                                       : (static_cast<size_t>(sidx) * H + h) * static_cast<size_t>(nchunks) + j;
-                const float* hc = p.h_ckpt + ci * DK * DV;
+            if (CKPT && out_on) {   // the state at the chunk start (waves without columns store nothing)
+                const float* hc = p.h_ckpt + (ck0 + static_cast<size_t>(j) * ckstep) * DK * DV;
                 const __amdgpu_buffer_rsrc_t hrc = buffer_rsrc(hc, has_col ? DK * DV * 4 : 0);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
@@ -348,7 +429,7 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
             // blocks (0,1) and (2,3) that the 32-token steps read); the
             // buffer covers the chunk's L valid rows
             const __amdgpu_buffer_rsrc_t orc = buffer_rsrc(p.o + static_cast<size_t>(tok0 + c0) * H * DV,
-                                                           has_col ? static_cast<uint32_t>(L * H * DV * 4) : 0u);
+                                                           (has_col && out_on) ? static_cast<uint32_t>(L * H * DV * 4) : 0u);
 #pragma unroll
             for (int R = 0, x = 0; R < 4; ++R) {
                 f32x4 acc = Y[R];
@@ -381,27 +462,190 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
         lds_sync();   // 2: chunk j consumed
     }
 
-    if (p.ht && has_col) {
+    // the end state: ht, or in segment mode the next segment's start (first
+    // segments), H_s or P_s (middle segments of phase 1)
+    float* dst = p.ht ? p.ht + st_off : nullptr;
+    int pitch = DV;
+    if (SEG) {
+        if (p.phase == 1 && seg == 0) {
+            if (nseg > 1) dst = p.seg_start + (static_cast<size_t>(ss + 1) * H + h) * DK * DV;
+        } else if (p.phase == 1) {
+            dst = trans ? p.seg_p + (static_cast<size_t>(ss) * H + h) * DK * DK
+                        : p.seg_h + (static_cast<size_t>(ss) * H + h) * DK * DV;
+            pitch = trans ? DK : DV;
+        } else if (seg != nseg - 1) {
+            dst = nullptr;
+        }
+    }
+    if (dst && has_col) {
         const int l = threadIdx.x & 63, gq = l >> 4, col = 16 * vt + (l & 15);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                p.ht[st_off + opaque_zero() + static_cast<size_t>(16 * rt + 4 * gq + i) * DV + col] = S[rt][i];
+                dst[opaque_zero() + static_cast<size_t>(16 * rt + 4 * gq + i) * pitch + col] = S[rt][i];
     }
 }
 
-template <typename Tin, int DK, int DV, bool CKPT>
-static hipError_t launch_state_c(const FwdArgs& A, hipStream_t stream) {
+// Segment phase 2: per (chain, head, value slice) of a chain with more than
+// two segments, start_{s+1} = P_s start_s + H_s for s = 1 .. n-2 (start_1
+// is the first segment's end state, written by phase 1).  fp32 FMA; P_s is
+// staged transposed in LDS and each thread owns a 4 x 8 block of the slice.
+template <int DK, int DV>
+__global__ void __launch_bounds__(256) ckda_seg_scan_kernel(StateParams p)
+{
+    constexpr int BV = DV < 64 ? DV : 64, NSLICE = DV / BV;
+    constexpr int PP = DK + 4, PS = BV + 4;   // LDS pitches (floats)
+    constexpr int CB = BV / 8, NTH = (DK / 4) * CB;   // column blocks, working threads
+    static_assert(NTH <= 256, "threads");
+    __shared__ __align__(16) float PT[DK * PP];   // PT[k][r] = P_s[r][k]
+    __shared__ __align__(16) float Ssl[DK * PS];  // the slice of start_s
+    const int H = p.H;
+    const int slice = blockIdx.x % NSLICE;
+    const int h = (blockIdx.x / NSLICE) % H;
+    const int d = blockIdx.x / (NSLICE * H);
+    const int NTC = (p.T + 63) / 64;
+    int len, ss0;
+    if (p.cu) {
+        len = p.cu[d + 1] - p.cu[d];
+        ss0 = seg_slot0(p.cu[d], d, p.G);
+    } else {
+        len = p.T;
+        ss0 = d * ((NTC + p.G - 1) / p.G);
+    }
+    const int nseg = ((len + 63) / 64 + p.G - 1) / p.G;
+    if (nseg <= 2) return;
+    const int tid = threadIdx.x;
+    const int c0 = slice * BV;
+    const size_t sdv = static_cast<size_t>(DK) * DV;
+    {   // start_1
+        const float* src = p.seg_start + (static_cast<size_t>(ss0 + 1) * H + h) * sdv;
+        for (int e = tid; e < DK * BV; e += 256) Ssl[(e / BV) * PS + e % BV] = src[(e / BV) * DV + c0 + e % BV];
+    }
+    const int rb = tid / CB, cb = tid % CB;   // rows 4 rb .. +3, columns 8 cb .. +7 of the slice
+    for (int sgi = 1; sgi <= nseg - 2; ++sgi) {
+        const size_t it = static_cast<size_t>(ss0 + sgi) * H + h;
+        const float* P = p.seg_p + it * DK * DK;
+        for (int e = tid; e < DK * DK; e += 256) PT[(e % DK) * PP + e / DK] = P[e];
+        __syncthreads();
+        float acc[4][8];
+        if (tid < NTH) {
+            const float* Hs = p.seg_h + it * sdv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[i][c] = Hs[static_cast<size_t>(4 * rb + i) * DV + c0 + 8 * cb + c];
+            for (int k = 0; k < DK; ++k) {
+                const f32x4 pr = *reinterpret_cast<const f32x4*>(PT + k * PP + 4 * rb);
+                const f32x4 s0 = *reinterpret_cast<const f32x4*>(Ssl + k * PS + 8 * cb);
+                const f32x4 s1 = *reinterpret_cast<const f32x4*>(Ssl + k * PS + 8 * cb + 4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        acc[i][c] = fmaf(pr[i], s0[c], acc[i][c]);
+                        acc[i][4 + c] = fmaf(pr[i], s1[c], acc[i][4 + c]);
+                    }
+            }
+        }
+        __syncthreads();   // every read of PT and Ssl done
+        if (tid < NTH) {
+            float* dst = p.seg_start + (static_cast<size_t>(ss0 + sgi + 1) * H + h) * sdv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    Ssl[(4 * rb + i) * PS + 8 * cb + c] = acc[i][c];
+                    dst[static_cast<size_t>(4 * rb + i) * DV + c0 + 8 * cb + c] = acc[i][c];
+                }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+namespace {
+
+std::atomic<int> g_seg_chunks{0};   // 0: automatic, < 0: never, >= kSegMinChunks: that length
+constexpr int kSegMinChunks = 16;
+
+// segment slots for segments of G chunks
+int seg_slots(const FwdArgs& A, int G) {
+    if (A.cu) return (A.T + 64 * G - 1) / (64 * G) + A.ndocs;
+    return A.B * (((A.T + 63) / 64 + G - 1) / G);
+}
+
+size_t seg_buffer_bytes(size_t nsslots, int H, int DK, int DV) {
+    return nsslots * H * (2 * static_cast<size_t>(DK) * DV + static_cast<size_t>(DK) * DK) * sizeof(float);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// compute units of the current device (state workgroups run two per CU)
+int device_cus() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load();
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev].store(n);
+    }
+    return n;
+}
+
+// Segment length for the state pass, 0 for whole chains.  Cost model in
+// chunk-steps of one workgroup: a phase takes at least its longest item and
+// at least its total work over the concurrent workgroups (two per CU).
+// Whole chains: max(longest chain, work / Z).  Segments of G chunks:
+// phase 1 (first segments, and value + transition slices of the middle
+// segments) + phase 3 (segments 1 .. n-1) + one step per scan step.  The
+// segment plan is taken when it is below 0.7 of the whole-chain estimate.
+int plan_segments(const FwdArgs& A, int nslice, int ntrans, size_t rec_bytes) {
+    const int forced = g_seg_chunks.load();
+    if (forced < 0 || A.H == 0) return 0;
+    std::vector<int> nch;
+    if (A.cu) {
+        if (!A.cu_host) return 0;
+        for (int d = 0; d < A.ndocs; ++d) nch.push_back((A.cu_host[d + 1] - A.cu_host[d] + 63) / 64);
+    } else {
+        nch.assign(A.B, (A.T + 63) / 64);
+    }
+    int maxn = 0;
+    double tot = 0;
+    for (int n : nch) { maxn = n > maxn ? n : maxn; tot += n; }
+    const size_t avail = A.ws_bytes > align256(rec_bytes) ? A.ws_bytes - align256(rec_bytes) : 0;
+    auto fits = [&](int G) { return seg_buffer_bytes(seg_slots(A, G), A.H, A.DK, A.DV) <= avail; };
+    if (forced > 0) return (maxn > forced && fits(forced)) ? forced : 0;
+    const double Z = 2.0 * device_cus();
+    const double t0 = std::max(static_cast<double>(maxn), tot * A.H * nslice / Z);
+    int best = 0;
+    double tbest = 0.7 * t0;
+    for (int G = kSegMinChunks; G < maxn; G *= 2) {
+        if (!fits(G)) continue;
+        double w1 = 0, w3 = 0;
+        int maxseg = 0;
+        for (int n : nch) {
+            const int ns = (n + G - 1) / G;
+            maxseg = std::max(maxseg, ns);
+            if (ns <= 1) { w1 += static_cast<double>(nslice) * n; continue; }
+            w1 += static_cast<double>(nslice) * G + static_cast<double>(ns - 2) * (nslice + ntrans) * G;
+            w3 += static_cast<double>(nslice) * (n - G);
+        }
+        const double t = std::max(static_cast<double>(G), w1 * A.H / Z) + std::max(static_cast<double>(G), w3 * A.H / Z) +
+                         std::max(0, maxseg - 2) + 1.0;
+        if (t < tbest) { tbest = t; best = G; }
+    }
+    return best;
+}
+
+template <typename Tin, int DK, int DV, bool CKPT, bool SEG>
+hipError_t launch_state_kernel(const StateParams& p, int grid, hipStream_t stream) {
     using SH = StateShape<Tin, DK, DV>;
-    StateParams p;
-    p.ws = static_cast<const unsigned char*>(A.ws);
-    p.h0 = A.h0; p.o = A.o; p.ht = A.ht; p.h_ckpt = A.h_ckpt; p.cu = A.cu; p.scale = A.scale;
-    p.B = A.B; p.T = A.T; p.H = A.H; p.ndocs = A.ndocs;
-    const int nchains = A.cu ? A.ndocs * A.H : A.B * A.H;
-    const int grid = nchains * SH::NSLICE;
     if (grid == 0) return hipSuccess;
-    auto kern = ckda_state_kernel<Tin, DK, DV, CKPT>;
+    auto kern = ckda_state_kernel<Tin, DK, DV, CKPT, SEG>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, SH::LDS);
     if (e != hipSuccess) return e;
@@ -409,13 +653,44 @@ static hipError_t launch_state_c(const FwdArgs& A, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <typename Tin, int DK, int DV, bool CKPT>
+hipError_t launch_state_c(const FwdArgs& A, size_t rec_bytes, hipStream_t stream) {
+    using SH = StateShape<Tin, DK, DV>;
+    StateParams p{};
+    p.ws = static_cast<const unsigned char*>(A.ws);
+    p.h0 = A.h0; p.o = A.o; p.ht = A.ht; p.h_ckpt = A.h_ckpt; p.cu = A.cu; p.scale = A.scale;
+    p.B = A.B; p.T = A.T; p.H = A.H; p.ndocs = A.ndocs;
+    const int nchains = A.cu ? A.ndocs * A.H : A.B * A.H;
+    constexpr int NTS = SH::NTS;
+    const int G = plan_segments(A, SH::NSLICE, NTS, rec_bytes);
+    if (G == 0) return launch_state_kernel<Tin, DK, DV, CKPT, false>(p, nchains * SH::NSLICE, stream);
+    p.G = G;
+    p.nsslots = seg_slots(A, G);
+    float* sb = reinterpret_cast<float*>(static_cast<unsigned char*>(A.ws) + align256(rec_bytes));
+    const size_t per = static_cast<size_t>(p.nsslots) * A.H * DK * DV;
+    p.seg_start = sb;
+    p.seg_h = sb + per;
+    p.seg_p = sb + 2 * per;
+    p.phase = 1;
+    hipError_t e = launch_state_kernel<Tin, DK, DV, CKPT, true>(p, p.nsslots * A.H * (SH::NSLICE + NTS), stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((ckda_seg_scan_kernel<DK, DV>), dim3(nchains * SH::NSLICE), dim3(256), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    p.phase = 3;
+    return launch_state_kernel<Tin, DK, DV, CKPT, true>(p, p.nsslots * A.H * SH::NSLICE, stream);
+}
+
 template <typename Tin, int DK, int DV>
-static hipError_t launch_state_t(const FwdArgs& A, hipStream_t stream) {
-    return A.h_ckpt ? launch_state_c<Tin, DK, DV, true>(A, stream) : launch_state_c<Tin, DK, DV, false>(A, stream);
+hipError_t launch_state_t(const FwdArgs& A, hipStream_t stream) {
+    const size_t rec = static_cast<size_t>(A.cu ? (A.T + 63) / 64 + A.ndocs : A.B * ((A.T + 63) / 64)) * A.H *
+                       Record<DK, DV, sizeof(Tin) == 4>::BYTES;
+    return A.h_ckpt ? launch_state_c<Tin, DK, DV, true>(A, rec, stream)
+                    : launch_state_c<Tin, DK, DV, false>(A, rec, stream);
 }
 
 template <typename Tin>
-static hipError_t launch_state_dt(const FwdArgs& A, hipStream_t stream) {
+hipError_t launch_state_dt(const FwdArgs& A, hipStream_t stream) {
 #define CKDA_STATE(DK_, DV_) \
     if (A.DK == DK_ && A.DV == DV_) return launch_state_t<Tin, DK_, DV_>(A, stream);
     CKDA_STATE(32, 32) CKDA_STATE(32, 64) CKDA_STATE(32, 128)
@@ -425,12 +700,7 @@ static hipError_t launch_state_dt(const FwdArgs& A, hipStream_t stream) {
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_state(const FwdArgs& A, hipStream_t stream) {
-    return A.bf16 ? launch_state_dt<bf16_t>(A, stream) : launch_state_dt<float>(A, stream);
-}
-
-// forward = chunk-local kernel over every (chunk, head), then the state pass
-size_t fwd_workspace_bytes(int nslots, int H, int DK, int DV, bool bf16) {
+size_t record_bytes(int DK, int DV, bool bf16) {
     size_t rec = 0;
 #define CKDA_REC(DK_, DV_) \
     if (DK == DK_ && DV == DV_) rec = bf16 ? Record<DK_, DV_, false>::BYTES : Record<DK_, DV_, true>::BYTES;
@@ -438,7 +708,27 @@ size_t fwd_workspace_bytes(int nslots, int H, int DK, int DV, bool bf16) {
     CKDA_REC(64, 32) CKDA_REC(64, 64) CKDA_REC(64, 128)
     CKDA_REC(128, 32) CKDA_REC(128, 64) CKDA_REC(128, 128)
 #undef CKDA_REC
-    return static_cast<size_t>(nslots) * H * rec;
+    return rec;
+}
+
+}  // namespace
+
+hipError_t launch_state(const FwdArgs& A, hipStream_t stream) {
+    return A.bf16 ? launch_state_dt<bf16_t>(A, stream) : launch_state_dt<float>(A, stream);
+}
+
+void set_segment_chunks(int G) { g_seg_chunks.store(G); }
+int segment_chunks() { return g_seg_chunks.load(); }
+int segment_min_chunks() { return kSegMinChunks; }
+
+// forward = chunk-local kernel over every (chunk, head), then the state pass
+size_t fwd_workspace_bytes(int nslots, int H, int DK, int DV, bool bf16) {
+    return static_cast<size_t>(nslots) * H * record_bytes(DK, DV, bf16);
+}
+
+size_t fwd_workspace_bytes_full(int nslots, int nsslots_max, int H, int DK, int DV, bool bf16) {
+    const size_t rec = fwd_workspace_bytes(nslots, H, DK, DV, bf16);
+    return align256(rec) + seg_buffer_bytes(nsslots_max, H, DK, DV);
 }
 
 hipError_t launch_fwd(const FwdArgs& A, int nslots, hipStream_t stream) {

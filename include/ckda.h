@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define CKDA_ABI_VERSION 5
+#define CKDA_ABI_VERSION 6
 
 typedef enum {
     CKDA_OK = 0,
@@ -114,13 +114,21 @@ ckda_status_t ckda_chunk_prep(int B, int T, int H, int DK, ckda_dtype_t in_dtype
  *   o: [B,T,H,DV] f32 (written)   ht: [B,H,DK,DV] f32 or NULL (final state)
  *   h_ckpt: [B,H,NT,DK,DV] f32 or NULL, NT = ceil(T/64): the state at the
  *           start of every chunk (checkpoints for ckda_bwd)
- *   workspace: at least ckda_fwd_workspace_bytes(B, T, H, DK, DV, in_dtype)
- *           bytes of device memory, 16-byte aligned, owned by the caller;
- *           the call overwrites it (it carries one record per (chunk, head)
- *           from the chunk-local pass to the state pass).  Calls that share
- *           a workspace must be ordered on one stream.
- * Two kernels are enqueued: the chunk-local pass over every (chunk, head)
- * at once, then the state pass that walks the chunks of each sequence.
+ *   workspace: ckda_fwd_workspace_bytes(B, T, H, DK, DV, in_dtype) bytes of
+ *           device memory, 16-byte aligned, owned by the caller; the call
+ *           overwrites it.  It carries one record per (chunk, head) from the
+ *           chunk-local pass to the state pass, then room for the segmented
+ *           state pass (below).  A smaller workspace that still holds the
+ *           records is accepted, and the state pass then always walks whole
+ *           sequences; less than that fails with CKDA_ERR_WORKSPACE.  Calls
+ *           that share a workspace must be ordered on one stream.
+ * The chunk-local pass runs over every (chunk, head) at once; the state
+ * pass walks the chunks of each sequence.  When a few sequences are much
+ * longer than the GPU has parallel work for, the state pass cuts them into
+ * segments of G chunks (see ckda_set_segment_chunks): segment maps in
+ * parallel, a short scan over the segments, then the segments from their
+ * true start states.  Results agree with the whole-sequence pass to
+ * rounding.
  * ---------------------------------------------------------------------- */
 size_t ckda_fwd_workspace_bytes(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype);
 ckda_status_t ckda_fwd_chunked(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype,
@@ -128,6 +136,21 @@ ckda_status_t ckda_fwd_chunked(int B, int T, int H, int DK, int DV, ckda_dtype_t
                                const float* g, const int8_t* s, const float* beta, float scale,
                                const float* h0, float* o, float* ht, float* h_ckpt,
                                void* workspace, size_t workspace_bytes, ckda_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Segment length of the forward's state pass, process-wide (all devices).
+ * Per chunk the state map is affine, S' = A_c S + B_c, and the columns of
+ * S evolve independently, so a long chain can be split into segments whose
+ * maps (A and B composed over the segment) are built in parallel and then
+ * chained by a scan: the single-GPU form of sequence sharding.
+ *   G = 0   automatic (default): a cost model picks G, or whole chains;
+ *   G < 0   never split;
+ *   G >= 16 split every chain longer than G chunks into segments of G
+ *           chunks (when the workspace has room).
+ * 0 < G < 16 is rejected with CKDA_ERR_UNSUPPORTED.  Not synchronised with
+ * calls in flight on other threads: set it before enqueueing work.
+ * ---------------------------------------------------------------------- */
+ckda_status_t ckda_set_segment_chunks(int G);
 
 /* ------------------------------------------------------------------------
  * Varlen forward over N packed documents (training packs documents back to

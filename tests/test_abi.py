@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.ckda_abi_version() == 5
+    assert L.ckda_abi_version() == 6
     assert L.ckda_status_string(0) == b"ok"
     for st in range(1, 8):
         assert L.ckda_status_string(st) not in (b"ok", b"unknown status")
@@ -67,19 +67,41 @@ def test_fwd_rejects_bad_arguments(L):
     assert L.ckda_last_error() == b""
 
 
+def align256(x):
+    return (x + 255) // 256 * 256
+
+
+def seg_bytes(nsslots, H, DK, DV):
+    """Segment buffers: start states and zero-start end states (DK x DV each)
+    and segment maps (DK x DK), fp32, per segment slot and head."""
+    return nsslots * H * (2 * DK * DV + DK * DK) * 4
+
+
 def test_fwd_workspace(L):
     need = L.ckda_fwd_workspace_bytes(2, 100, 3, 64, 32, 1)
     # one record per (chunk, head): bf16 keeps W in one plane, Qh/KbT/M in two
     rec = 64 * 64 * 2 + 2 * (64 * 64 * 2) * 3 + 64 * 4 + 64 * 32 * 4
-    assert need == 2 * 2 * 3 * rec
+    # then the segment buffers for segments of 16 chunks: ceil(2/16) per sequence
+    assert need == align256(2 * 2 * 3 * rec) + seg_bytes(2 * 1, 3, 64, 32)
     assert L.ckda_fwd_workspace_bytes(2, 100, 3, 64, 32, 0) > need      # fp32 records are larger
     assert L.ckda_fwd_workspace_bytes(2, 100, 3, 48, 32, 1) == 0       # unsupported head size
     assert L.ckda_fwd_workspace_bytes(2, 0, 3, 64, 32, 1) == 0         # no chunks
-    assert L.ckda_fwd_varlen_workspace_bytes(3, 100, 3, 64, 32, 1) == (2 + 3) * 3 * rec
+    # varlen: ceil(100/64) + 3 chunk slots, ceil(100/1024) + 3 segment slots
+    assert L.ckda_fwd_varlen_workspace_bytes(3, 100, 3, 64, 32, 1) == \
+        align256((2 + 3) * 3 * rec) + seg_bytes(1 + 3, 3, 64, 32)
     assert fwd(L, ws=None) == 1
     assert b"workspace" in L.ckda_last_error()
-    assert fwd(L, wsb=L.ckda_fwd_workspace_bytes(1, 8, 1, 32, 32, 0) - 16) == 6
+    # below the records (fp32, DK = DV = 32: W, Qh, KbT, M, d, u) the call fails
+    rec32 = 64 * 32 * 4 * 3 + 64 * 64 * 4 + 32 * 4 + 64 * 32 * 4
+    assert fwd(L, wsb=rec32 - 16) == 6
     assert fwd(L, ws=P(0x1008)) == 4             # misaligned workspace
+
+
+def test_segment_knob(L):
+    assert L.ckda_set_segment_chunks(8) == 4     # shorter than 16 chunks
+    assert b"16" in L.ckda_last_error()
+    for G in (16, 100, -1, 0):
+        assert L.ckda_set_segment_chunks(G) == 0
 
 
 def test_varlen_rejects_bad_cu_seqlens(L):
