@@ -9,10 +9,12 @@ dk=dv=128, bf16 q/k/v, fp32 gates, state and outputs.  The JSON line's ``value``
 tokens/s; the decode workload (256 sequences x 16 heads, 512 recurrent
 steps) is reported in the same line as state-streaming GB/s, the backward as
 tokens/s, and the same forward with one gate per (token, head), and with
-raw q and k that the path L2-normalises itself, as tokens/s.
+raw q and k that the path L2-normalises itself, as tokens/s; the forward
+over few long chains (varlen_64k, long_64k) with and without the segmented
+state pass.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       [--only fwd|fwd_head_gate|fwd_qk_norm|decode|bwd|copy]
+       [--only fwd|fwd_head_gate|fwd_qk_norm|fwd_long|decode|bwd|copy]
 """
 from __future__ import annotations
 
@@ -121,6 +123,53 @@ def bench_fwd(torch, steps, warmup, workload="layer_bf16"):
                 workspace_bytes=int(ws.numel()))
 
 
+def bench_fwd_long(torch, steps, warmup, workload):
+    """Forward over few long chains (varlen_64k: 16 documents, the longest
+    16,637 tokens; long_64k: one 65,536-token sequence), timed with the
+    automatic state-pass plan (segments of long chains when the cost model
+    takes them) and with whole chains only."""
+    from gated_delta_rule_sign_amd import ckda
+    from gated_delta_rule_sign_amd import inputs as I
+    log(f"generating {workload} inputs")
+    w = I.make_workload(workload)
+    tok = w.tok
+    d = {k: dev_tensor(torch, getattr(tok, k)) for k in ("q", "k", "v", "g", "s", "beta")}
+    H, DK, DV = w.cfg["H"], w.cfg["DK"], w.cfg["DV"]
+    if w.cu_seqlens is not None:
+        cu = torch.from_numpy(w.cu_seqlens)
+        cu_dev = cu.to("cuda:0")
+        h0 = dev_tensor(torch, w.h0)
+        Tt = int(w.cu_seqlens[-1])
+        N = len(w.cu_seqlens) - 1
+        o = torch.empty((Tt, H, DV), dtype=torch.float32, device="cuda:0")
+        ht = torch.empty((N, H, DK, DV), dtype=torch.float32, device="cuda:0")
+        ws = torch.empty(ckda.fwd_varlen_workspace_bytes(N, Tt, H, DK, DV, torch.bfloat16), dtype=torch.uint8,
+                         device="cuda:0")
+        fn = lambda: ckda.fwd_varlen(**d, cu_seqlens=cu, cu_seqlens_dev=cu_dev, h0=h0, o=o, ht=ht, workspace=ws)
+        tokens, lens = Tt, np.diff(w.cu_seqlens)
+    else:
+        B, T = w.cfg["B"], w.cfg["T"]
+        o = torch.empty((B, T, H, DV), dtype=torch.float32, device="cuda:0")
+        ht = torch.empty((B, H, DK, DV), dtype=torch.float32, device="cuda:0")
+        ws = torch.empty(ckda.fwd_workspace_bytes(B, T, H, DK, DV, torch.bfloat16), dtype=torch.uint8,
+                         device="cuda:0")
+        fn = lambda: ckda.fwd(**d, o=o, ht=ht, workspace=ws)
+        tokens, lens = B * T, np.full(B, T)
+    res = {"workload": workload, "tokens": tokens, "chains": int(len(lens) * H),
+           "longest_chain_tokens": int(lens.max())}
+    try:
+        for mode, G in (("auto", 0), ("whole_chains", -1)):
+            ckda.set_segment_chunks(G)
+            log(f"timing {workload} forward, state pass {mode}")
+            wall, per = time_kernel_launches(torch, fn, steps, warmup)
+            res[mode] = {"ms": wall / steps, "avg_launch_ms": float(np.mean(per)),
+                         "tokens_per_s": tokens / (wall / steps * 1e-3)}
+    finally:
+        ckda.set_segment_chunks(0)
+    res["speedup_auto_vs_whole"] = res["whole_chains"]["ms"] / res["auto"]["ms"]
+    return res
+
+
 def bench_decode(torch, nsteps=512, distinct=64):
     """256 sequences x 16 heads, nsteps sequential steps from a state drawn
     N(0, 0.02).  Step inputs are drawn for `distinct` steps and reused
@@ -223,7 +272,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "fwd_head_gate", "fwd_qk_norm", "decode", "bwd", "copy"],
+    ap.add_argument("--only", choices=["fwd", "fwd_head_gate", "fwd_qk_norm", "fwd_long", "decode", "bwd", "copy"],
                     default=None)
     ap.add_argument("--decode-steps", type=int, default=512)
     args = ap.parse_args()
@@ -247,6 +296,9 @@ def main():
     if args.only == "bwd":
         print(json.dumps(bench_bwd(torch, args.steps, args.warmup)))
         return
+    if args.only == "fwd_long":
+        print(json.dumps([bench_fwd_long(torch, max(3, args.steps // 4), 3, wl) for wl in ("varlen_64k", "long_64k")]))
+        return
 
     if args.only in ("fwd_head_gate", "fwd_qk_norm"):
         wl = "layer_bf16_head_gate" if args.only == "fwd_head_gate" else "layer_bf16_qk_norm"
@@ -261,6 +313,7 @@ def main():
     bw = bench_bwd(torch, max(3, args.steps // 4), 1)
     fh = bench_fwd(torch, args.steps, args.warmup, "layer_bf16_head_gate")
     fq = bench_fwd(torch, args.steps, args.warmup, "layer_bf16_qk_norm")
+    longs = [bench_fwd_long(torch, max(3, args.steps // 4), 3, wl) for wl in ("varlen_64k", "long_64k")]
     cpu = None if args.no_cpu else cpu_baseline(fw["w"])
 
     achieved = fw["bytes"] / (fw["launch_ms"] * 1e-3) / 1e9
@@ -309,6 +362,7 @@ def main():
                             "avg_launch_ms": fq["launch_ms"], "algorithmic_bytes": fq["bytes"],
                             "achieved_gbs": fq["bytes"] / (fq["launch_ms"] * 1e-3) / 1e9,
                             "frac_of_hbm_peak": fq["bytes"] / (fq["launch_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "forward_long_chains": longs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

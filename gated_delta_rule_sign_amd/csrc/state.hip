@@ -28,14 +28,15 @@
 // Segment mode (chains much longer than the GPU has parallel work for):
 // the chunk maps are affine in the state, S' = A_c S + B_c with
 // A_c = Diag(d) - KbT W, and every column of S evolves on its own.  A chain
-// of chunks is cut into segments of G chunks.  Phase 1 runs the first
-// segment of each chain from its true start (outputs included) and, for
-// every middle segment, the value columns from a zero start (giving H_s,
-// the segment's end state from zero) plus DK "transition" columns started
-// from the identity with u = 0 (giving P_s = the product of the segment's
-// A_c).  Phase 2 (ckda_seg_scan_kernel) chains the starts:
-// start_{s+1} = P_s start_s + H_s.  Phase 3 reruns segments 1 .. n-1 from
-// their true starts and writes their outputs, checkpoints and final state.
+// of chunks is cut into segments of G chunks.  Phase 1 (no outputs, so no
+// Qh S or M U products and no Qh / M staging) walks every segment but a
+// chain's last: the first from the chain's start (its end state is
+// start_1), each middle one with its value columns from zero (giving H_s,
+// the segment's end state from zero) and DK "transition" columns from the
+// identity with u = 0 (giving P_s, the product of the segment's A_c).
+// Phase 2 (ckda_seg_scan_kernel) chains the starts:
+// start_{s+1} = P_s start_s + H_s.  Phase 3 walks every segment from its
+// true start and writes the outputs, checkpoints and final state.
 #include <algorithm>
 #include <atomic>
 #include <vector>
@@ -115,7 +116,7 @@ struct StateParams {
     int B, T, H, ndocs;
     // segment mode: G chunks per segment; segment s of chain d sits in
     // segment slot floor(cu[d] / 64G) + d + s (equal-length: d * nseg + s)
-    int G, phase, nsslots;
+    int G, nsslots;
     float* seg_start;   // [nsslots][H][DK][DV] start state of segments s >= 1
     float* seg_h;       // [nsslots][H][DK][DV] end state from a zero start (middle segments)
     float* seg_p;       // [nsslots][H][DK][DK] segment map P_s (middle segments)
@@ -124,9 +125,9 @@ struct StateParams {
 // first segment slot of chain d (varlen document start cu_d)
 __host__ __device__ inline int seg_slot0(int cu_d, int d, int G) { return cu_d / (64 * G) + d; }
 
-// SEG: segment mode, phase p.phase (1 or 3); otherwise one workgroup runs a
-// whole chain's value slice
-template <typename Tin, int DK, int DV, bool CKPT, bool SEG>
+// SEG: segment mode, phase 3 with OUT, phase 1 without; otherwise (OUT set)
+// one workgroup walks a whole chain's value slice
+template <typename Tin, int DK, int DV, bool CKPT, bool SEG, bool OUT>
 __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
 {
     using SH = StateShape<Tin, DK, DV>;
@@ -139,7 +140,7 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
     // work items: chains (or, in segment mode, segment slots) x heads; NS
     // slices per item: the value slices, then (segment phase 1) the
     // transition slices over the DK columns of P_s
-    const int NS = (SEG && p.phase == 1) ? SH::NSLICE + SH::NTS : SH::NSLICE;
+    constexpr int NS = (SEG && !OUT) ? SH::NSLICE + SH::NTS : SH::NSLICE;
     const int nitems = SEG ? p.nsslots * H : (p.cu ? p.ndocs * H : p.B * H);
     int item, slice;
     {
@@ -197,15 +198,16 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
     }
     const int nchunks = (len + 63) / 64;
     int jbeg = 0, nloop = nchunks, nseg = 1;
-    bool trans = false, out_on = true;
+    bool trans = false;
     if (SEG) {
         nseg = (nchunks + p.G - 1) / p.G;
         trans = slice >= SH::NSLICE;
-        const bool run = p.phase == 1 ? (seg == 0 ? !trans : seg < nseg - 1) : (seg >= 1 && seg < nseg);
+        // phase 1: every segment but the last (transition slices: the middle
+        // ones); phase 3: every segment (a chain of no chunks has one)
+        const bool run = OUT ? seg < max(nseg, 1) : (seg < nseg - 1 && (seg > 0 || !trans));
         if (!run) return;   // the whole workgroup, before any barrier
         jbeg = seg * p.G;
         nloop = min(p.G, nchunks - jbeg);
-        out_on = p.phase == 3 || seg == 0;
     }
     // first 16-column tile of the slice (transition slices: columns of P_s)
     const int vt0 = ((trans ? slice - SH::NSLICE : slice) * SH::BV) / 16;
@@ -238,14 +240,16 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
             const u32x4* g_ = CKDA_REC(J);                                                                   \
             const int t_ = opaque_tid() - NT;                                                                \
             _Pragma("unroll") for (int i_ = 0; i_ < NW_; ++i_) ga[i_] = g_[RC::OFF_W / 16 + t_ + NT * i_];   \
-            _Pragma("unroll") for (int i_ = 0; i_ < NQ_; ++i_) ga[O_Q + i_] = g_[RC::OFF_Q / 16 + t_ + NT * i_]; \
+            if (OUT)                                                                                         \
+                _Pragma("unroll") for (int i_ = 0; i_ < NQ_; ++i_) ga[O_Q + i_] = g_[RC::OFF_Q / 16 + t_ + NT * i_]; \
         }
 #define CKDA_LOAD_B(J)                                                                                       \
         {                                                                                                    \
             const u32x4* g_ = CKDA_REC(J);                                                                   \
             const int t_ = opaque_tid() - NT;                                                                \
             _Pragma("unroll") for (int i_ = 0; i_ < NK_; ++i_) gb[i_] = g_[RC::OFF_K / 16 + t_ + NT * i_];   \
-            _Pragma("unroll") for (int i_ = 0; i_ < NM_; ++i_) gb[O_M + i_] = g_[RC::OFF_M / 16 + t_ + NT * i_]; \
+            if (OUT)                                                                                         \
+                _Pragma("unroll") for (int i_ = 0; i_ < NM_; ++i_) gb[O_M + i_] = g_[RC::OFF_M / 16 + t_ + NT * i_]; \
             _Pragma("unroll") for (int i_ = 0; i_ < ND_; ++i_)                                               \
                 if (StD::has(t_, i_)) gb[O_D + i_] = g_[RC::OFF_D / 16 + t_ + NT * i_];                       \
             _Pragma("unroll") for (int i_ = 0; i_ < NU_; ++i_) {                                             \
@@ -260,8 +264,9 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
             const int t_ = opaque_tid() - NT;                                                                \
             _Pragma("unroll") for (int i_ = 0; i_ < NW_; ++i_)                                               \
                 StW::put(sm_ + SH::L_W + StW::lds_off(t_, i_), ga[i_]);                                      \
-            _Pragma("unroll") for (int i_ = 0; i_ < NQ_; ++i_)                                               \
-                StQ::put(sm_ + SH::L_Q + StQ::lds_off(t_, i_), ga[O_Q + i_]);                                \
+            if (OUT)                                                                                         \
+                _Pragma("unroll") for (int i_ = 0; i_ < NQ_; ++i_)                                           \
+                    StQ::put(sm_ + SH::L_Q + StQ::lds_off(t_, i_), ga[O_Q + i_]);                            \
         }
 #define CKDA_STORE_B()                                                                                       \
         {                                                                                                    \
@@ -269,8 +274,9 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
             const int t_ = opaque_tid() - NT;                                                                \
             _Pragma("unroll") for (int i_ = 0; i_ < NK_; ++i_)                                               \
                 StK::put(sm_ + SH::L_K + StK::lds_off(t_, i_), gb[i_]);                                      \
-            _Pragma("unroll") for (int i_ = 0; i_ < NM_; ++i_)                                               \
-                StM::put(sm_ + SH::L_M + StM::lds_off(t_, i_), gb[O_M + i_]);                                \
+            if (OUT)                                                                                         \
+                _Pragma("unroll") for (int i_ = 0; i_ < NM_; ++i_)                                           \
+                    StM::put(sm_ + SH::L_M + StM::lds_off(t_, i_), gb[O_M + i_]);                            \
             _Pragma("unroll") for (int i_ = 0; i_ < ND_; ++i_)                                               \
                 if (StD::has(t_, i_)) *reinterpret_cast<u32x4*>(sm_ + SH::L_D + StD::lds_off(t_, i_)) = gb[O_D + i_]; \
             if (!(SEG && trans))                                                                             \
@@ -322,7 +328,7 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
     // start: h0 (or zero); segment mode: the identity for transition slices,
     // zero for the middle segments of phase 1, the scanned start in phase 3
     const float* src = p.h0 ? p.h0 + st_off : nullptr;
-    if (SEG && seg > 0) src = p.phase == 3 ? p.seg_start + (static_cast<size_t>(ss) * H + h) * DK * DV : nullptr;
+    if (SEG && seg > 0) src = OUT ? p.seg_start + (static_cast<size_t>(ss) * H + h) * DK * DV : nullptr;
     f32x4 S[RT];
     {
         const int l = threadIdx.x & 63, gq = l >> 4, col = 16 * vt + (l & 15);
@@ -357,7 +363,7 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
             f32x4 u[4];
 #pragma unroll
             for (int J = 0; J < 4; ++J) u[J] = *reinterpret_cast<const f32x4*>(sm + SH::L_U + ((J * NWC + wt) * 64 + l) * 16);
-            if (CKPT && out_on) {   // the state at the chunk start (waves without columns store nothing)
+            if (CKPT && OUT) {   // the state at the chunk start (waves without columns store nothing)
                 const float* hc = p.h_ckpt + (ck0 + static_cast<size_t>(j) * ckstep) * DK * DV;
                 const __amdgpu_buffer_rsrc_t hrc = buffer_rsrc(hc, has_col ? DK * DV * 4 : 0);
 #pragma unroll
@@ -387,7 +393,7 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
 #pragma unroll
                 for (int R = 0; R < 4; ++R) {
                     wa[0][R] = PR::load4x2s(Wm, 16 * R + n, 4 * gq, 16 + 4 * gq);
-                    qa[0][R] = PR::load4x2(Qm, 16 * R + n, 4 * gq, 16 + 4 * gq);
+                    if (OUT) qa[0][R] = PR::load4x2(Qm, 16 * R + n, 4 * gq, 16 + 4 * gq);
                 }
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
@@ -396,14 +402,14 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
 #pragma unroll
                         for (int R = 0; R < 4; ++R) {
                             wa[(ks + 1) & 1][R] = PR::load4x2s(Wm, 16 * R + n, ca, cb);
-                            qa[(ks + 1) & 1][R] = PR::load4x2(Qm, 16 * R + n, ca, cb);
+                            if (OUT) qa[(ks + 1) & 1][R] = PR::load4x2(Qm, 16 * R + n, ca, cb);
                         }
                     }
                     CKDA_FENCE();
 #pragma unroll
                     for (int R = 0; R < 4; ++R) {
                         X[R] = PR::mma8s(wa[ks & 1][R], Sb[ks], X[R]);
-                        Y[R] = PR::mma8(qa[ks & 1][R], Sb[ks], Y[R]);
+                        if (OUT) Y[R] = PR::mma8(qa[ks & 1][R], Sb[ks], Y[R]);
                     }
                     CKDA_FENCE();
                 }
@@ -412,11 +418,13 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
             // M fragments for the output and the first KbT fragments, read
             // while U is formed
             typename PR::F8 ma[6];
+            if (OUT) {
 #pragma unroll
-            for (int R = 0, x = 0; R < 4; ++R)
+                for (int R = 0, x = 0; R < 4; ++R)
 #pragma unroll
-                for (int kt = 0; kt <= R / 2; ++kt, ++x)
-                    ma[x] = PR::load4x2(Mm, 16 * R + n, 32 * kt + 4 * gq, 32 * kt + 16 + 4 * gq);
+                    for (int kt = 0; kt <= R / 2; ++kt, ++x)
+                        ma[x] = PR::load4x2(Mm, 16 * R + n, 32 * kt + 4 * gq, 32 * kt + 16 + 4 * gq);
+            }
             typename PR::F8 ka[2][2];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) ka[0][kt] = PR::load4x2(Km, n, 32 * kt + 4 * gq, 32 * kt + 16 + 4 * gq);
@@ -428,17 +436,19 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
             // O = scale (Qh S + M U) (M is zero above its diagonal, also in
             // blocks (0,1) and (2,3) that the 32-token steps read); the
             // buffer covers the chunk's L valid rows
-            const __amdgpu_buffer_rsrc_t orc = buffer_rsrc(p.o + static_cast<size_t>(tok0 + c0) * H * DV,
-                                                           (has_col && out_on) ? static_cast<uint32_t>(L * H * DV * 4) : 0u);
+            if (OUT) {
+                const __amdgpu_buffer_rsrc_t orc = buffer_rsrc(p.o + static_cast<size_t>(tok0 + c0) * H * DV,
+                                                               has_col ? static_cast<uint32_t>(L * H * DV * 4) : 0u);
 #pragma unroll
-            for (int R = 0, x = 0; R < 4; ++R) {
-                f32x4 acc = Y[R];
+                for (int R = 0, x = 0; R < 4; ++R) {
+                    f32x4 acc = Y[R];
 #pragma unroll
-                for (int kt = 0; kt <= R / 2; ++kt, ++x) acc = PR::mma8(ma[x], Ub[kt], acc);
+                    for (int kt = 0; kt <= R / 2; ++kt, ++x) acc = PR::mma8(ma[x], Ub[kt], acc);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int tt = 16 * R + 4 * gq + i;
-                    buffer_store_f32(orc, static_cast<uint32_t>(((tt * H + h) * DV + col) * 4), p.scale * acc[i]);
+                    for (int i = 0; i < 4; ++i) {
+                        const int tt = 16 * R + 4 * gq + i;
+                        buffer_store_f32(orc, static_cast<uint32_t>(((tt * H + h) * DV + col) * 4), p.scale * acc[i]);
+                    }
                 }
             }
             // S <- Diag(d) S + KbT U
@@ -462,20 +472,20 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
         lds_sync();   // 2: chunk j consumed
     }
 
-    // the end state: ht, or in segment mode the next segment's start (first
-    // segments), H_s or P_s (middle segments of phase 1)
+    // the end state: ht (whole chains; phase 3, a chain's last segment), or
+    // in phase 1 start_1 (first segments), H_s or P_s (middle segments)
     float* dst = p.ht ? p.ht + st_off : nullptr;
     int pitch = DV;
-    if (SEG) {
-        if (p.phase == 1 && seg == 0) {
-            if (nseg > 1) dst = p.seg_start + (static_cast<size_t>(ss + 1) * H + h) * DK * DV;
-        } else if (p.phase == 1) {
+    if (SEG && !OUT) {
+        if (seg == 0) {
+            dst = p.seg_start + (static_cast<size_t>(ss + 1) * H + h) * DK * DV;
+        } else {
             dst = trans ? p.seg_p + (static_cast<size_t>(ss) * H + h) * DK * DK
                         : p.seg_h + (static_cast<size_t>(ss) * H + h) * DK * DV;
             pitch = trans ? DK : DV;
-        } else if (seg != nseg - 1) {
-            dst = nullptr;
         }
+    } else if (SEG && seg < nseg - 1) {
+        dst = nullptr;
     }
     if (dst && has_col) {
         const int l = threadIdx.x & 63, gq = l >> 4, col = 16 * vt + (l & 15);
@@ -487,23 +497,23 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
     }
 }
 
-// Segment phase 2: per (chain, head, value slice) of a chain with more than
-// two segments, start_{s+1} = P_s start_s + H_s for s = 1 .. n-2 (start_1
-// is the first segment's end state, written by phase 1).  fp32 FMA; P_s is
-// staged transposed in LDS and each thread owns a 4 x 8 block of the slice.
+// Segment phase 2: per (chain, head, 16-column slice) of a chain with more
+// than two segments, start_{s+1} = P_s start_s + H_s for s = 1 .. n-2
+// (start_1 is the first segment's end state, written by phase 1).  fp32
+// FMA: thread t owns row t/2, columns 8(t%2) .. +7 of the slice; it streams
+// its row of P_s from L2 and reads the slice of start_s from LDS (two
+// addresses per wave: broadcasts).
+constexpr int kScanCols = 16;
 template <int DK, int DV>
 __global__ void __launch_bounds__(256) ckda_seg_scan_kernel(StateParams p)
 {
-    constexpr int BV = DV < 64 ? DV : 64, NSLICE = DV / BV;
-    constexpr int PP = DK + 4, PS = BV + 4;   // LDS pitches (floats)
-    constexpr int CB = BV / 8, NTH = (DK / 4) * CB;   // column blocks, working threads
+    constexpr int NSL = DV / kScanCols, NTH = 2 * DK;
     static_assert(NTH <= 256, "threads");
-    __shared__ __align__(16) float PT[DK * PP];   // PT[k][r] = P_s[r][k]
-    __shared__ __align__(16) float Ssl[DK * PS];  // the slice of start_s
+    __shared__ __align__(16) float Ssl[DK * kScanCols];   // the slice of start_s
     const int H = p.H;
-    const int slice = blockIdx.x % NSLICE;
-    const int h = (blockIdx.x / NSLICE) % H;
-    const int d = blockIdx.x / (NSLICE * H);
+    const int slice = blockIdx.x % NSL;
+    const int h = (blockIdx.x / NSL) % H;
+    const int d = blockIdx.x / (NSL * H);
     const int NTC = (p.T + 63) / 64;
     int len, ss0;
     if (p.cu) {
@@ -516,48 +526,53 @@ __global__ void __launch_bounds__(256) ckda_seg_scan_kernel(StateParams p)
     const int nseg = ((len + 63) / 64 + p.G - 1) / p.G;
     if (nseg <= 2) return;
     const int tid = threadIdx.x;
-    const int c0 = slice * BV;
+    const int c0 = slice * kScanCols;
     const size_t sdv = static_cast<size_t>(DK) * DV;
     {   // start_1
         const float* src = p.seg_start + (static_cast<size_t>(ss0 + 1) * H + h) * sdv;
-        for (int e = tid; e < DK * BV; e += 256) Ssl[(e / BV) * PS + e % BV] = src[(e / BV) * DV + c0 + e % BV];
+        for (int e = tid; e < DK * kScanCols; e += 256)
+            Ssl[e] = src[static_cast<size_t>(e / kScanCols) * DV + c0 + e % kScanCols];
     }
-    const int rb = tid / CB, cb = tid % CB;   // rows 4 rb .. +3, columns 8 cb .. +7 of the slice
+    __syncthreads();
+    const int r = tid >> 1, cb = 8 * (tid & 1);
     for (int sgi = 1; sgi <= nseg - 2; ++sgi) {
         const size_t it = static_cast<size_t>(ss0 + sgi) * H + h;
-        const float* P = p.seg_p + it * DK * DK;
-        for (int e = tid; e < DK * DK; e += 256) PT[(e % DK) * PP + e / DK] = P[e];
-        __syncthreads();
-        float acc[4][8];
+        float acc[8];
         if (tid < NTH) {
-            const float* Hs = p.seg_h + it * sdv;
+            const float* Hs = p.seg_h + it * sdv + static_cast<size_t>(r) * DV + c0 + cb;
+            const f32x4 h0 = *reinterpret_cast<const f32x4*>(Hs), h1 = *reinterpret_cast<const f32x4*>(Hs + 4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int c = 0; c < 4; ++c) {
+                acc[c] = h0[c];
+                acc[4 + c] = h1[c];
+            }
+            const f32x4* P = reinterpret_cast<const f32x4*>(p.seg_p + it * DK * DK + static_cast<size_t>(r) * DK);
+            f32x4 prow[DK / 4];   // the whole row in flight at once (L2 latency once per step)
 #pragma unroll
-                for (int c = 0; c < 8; ++c) acc[i][c] = Hs[static_cast<size_t>(4 * rb + i) * DV + c0 + 8 * cb + c];
-            for (int k = 0; k < DK; ++k) {
-                const f32x4 pr = *reinterpret_cast<const f32x4*>(PT + k * PP + 4 * rb);
-                const f32x4 s0 = *reinterpret_cast<const f32x4*>(Ssl + k * PS + 8 * cb);
-                const f32x4 s1 = *reinterpret_cast<const f32x4*>(Ssl + k * PS + 8 * cb + 4);
+            for (int k4 = 0; k4 < DK / 4; ++k4) prow[k4] = P[k4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+            for (int k4 = 0; k4 < DK / 4; ++k4) {
+                const f32x4 pr = prow[k4];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const float* sr = Ssl + (4 * k4 + kk) * kScanCols + cb;
+                    const f32x4 s0 = *reinterpret_cast<const f32x4*>(sr), s1 = *reinterpret_cast<const f32x4*>(sr + 4);
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
-                        acc[i][c] = fmaf(pr[i], s0[c], acc[i][c]);
-                        acc[i][4 + c] = fmaf(pr[i], s1[c], acc[i][4 + c]);
+                        acc[c] = fmaf(pr[kk], s0[c], acc[c]);
+                        acc[4 + c] = fmaf(pr[kk], s1[c], acc[4 + c]);
                     }
+                }
             }
         }
-        __syncthreads();   // every read of PT and Ssl done
+        __syncthreads();   // every read of start_s done
         if (tid < NTH) {
-            float* dst = p.seg_start + (static_cast<size_t>(ss0 + sgi + 1) * H + h) * sdv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int c = 0; c < 8; ++c) {
-                    Ssl[(4 * rb + i) * PS + 8 * cb + c] = acc[i][c];
-                    dst[static_cast<size_t>(4 * rb + i) * DV + c0 + 8 * cb + c] = acc[i][c];
-                }
+            float* dst = p.seg_start + (static_cast<size_t>(ss0 + sgi + 1) * H + h) * sdv +
+                         static_cast<size_t>(r) * DV + c0 + cb;
+            *reinterpret_cast<f32x4*>(Ssl + r * kScanCols + cb) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+            *reinterpret_cast<f32x4*>(Ssl + r * kScanCols + cb + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+            *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+            *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
         }
         __syncthreads();
     }
@@ -597,12 +612,18 @@ int device_cus() {
 }
 
 // Segment length for the state pass, 0 for whole chains.  Cost model in
-// chunk-steps of one workgroup: a phase takes at least its longest item and
-// at least its total work over the concurrent workgroups (two per CU).
-// Whole chains: max(longest chain, work / Z).  Segments of G chunks:
-// phase 1 (first segments, and value + transition slices of the middle
-// segments) + phase 3 (segments 1 .. n-1) + one step per scan step.  The
-// segment plan is taken when it is below 0.7 of the whole-chain estimate.
+// units of one chunk-step of a workgroup that has its CU to itself: a phase
+// takes at least its longest item and at least its total work (workgroup
+// chunk-steps) over the GPU's throughput, measured on MI355X (dk = dv = 128,
+// bf16 records) at about 0.64 chunk-steps per CU per unit (a lone chain
+// steps in about 3.1 us; 256 CUs complete about 53 workgroup chunk-steps per
+// us, with one workgroup per CU or two).  Whole chains: max(longest chain,
+// work W / R).  Segments of G chunks: phase 1 (first segments, and value +
+// transition slices of the middle segments, at kNoOut of a step without
+// the output products) + phase 3 (every segment: W again, in items of at
+// most G chunks) + the scan (about three units per step) + launch gaps.
+// The segment plan is taken when it is below 0.8 of the whole-chain one.
+constexpr double kCuRate = 0.64, kNoOut = 0.6, kScanStep = 3.0;
 int plan_segments(const FwdArgs& A, int nslice, int ntrans, size_t rec_bytes) {
     const int forced = g_seg_chunks.load();
     if (forced < 0 || A.H == 0) return 0;
@@ -619,33 +640,32 @@ int plan_segments(const FwdArgs& A, int nslice, int ntrans, size_t rec_bytes) {
     const size_t avail = A.ws_bytes > align256(rec_bytes) ? A.ws_bytes - align256(rec_bytes) : 0;
     auto fits = [&](int G) { return seg_buffer_bytes(seg_slots(A, G), A.H, A.DK, A.DV) <= avail; };
     if (forced > 0) return (maxn > forced && fits(forced)) ? forced : 0;
-    const double Z = 2.0 * device_cus();
-    const double t0 = std::max(static_cast<double>(maxn), tot * A.H * nslice / Z);
+    const double R = kCuRate * device_cus();   // workgroup chunk-steps per unit, whole GPU
+    const double W = tot * A.H * nslice;
+    const double t0 = std::max(static_cast<double>(maxn), W / R);
     int best = 0;
-    double tbest = 0.7 * t0;
+    double tbest = 0.8 * t0;
     for (int G = kSegMinChunks; G < maxn; G *= 2) {
         if (!fits(G)) continue;
-        double w1 = 0, w3 = 0;
+        double w1 = 0;
         int maxseg = 0;
         for (int n : nch) {
             const int ns = (n + G - 1) / G;
             maxseg = std::max(maxseg, ns);
-            if (ns <= 1) { w1 += static_cast<double>(nslice) * n; continue; }
-            w1 += static_cast<double>(nslice) * G + static_cast<double>(ns - 2) * (nslice + ntrans) * G;
-            w3 += static_cast<double>(nslice) * (n - G);
+            if (ns >= 2) w1 += static_cast<double>(nslice) * G + static_cast<double>(ns - 2) * (nslice + ntrans) * G;
         }
-        const double t = std::max(static_cast<double>(G), w1 * A.H / Z) + std::max(static_cast<double>(G), w3 * A.H / Z) +
-                         std::max(0, maxseg - 2) + 1.0;
+        const double t = std::max(static_cast<double>(G), kNoOut * w1 * A.H / R) +
+                         std::max(static_cast<double>(G), W / R) + kScanStep * std::max(0, maxseg - 2) + 2.0;
         if (t < tbest) { tbest = t; best = G; }
     }
     return best;
 }
 
-template <typename Tin, int DK, int DV, bool CKPT, bool SEG>
+template <typename Tin, int DK, int DV, bool CKPT, bool SEG, bool OUT>
 hipError_t launch_state_kernel(const StateParams& p, int grid, hipStream_t stream) {
     using SH = StateShape<Tin, DK, DV>;
     if (grid == 0) return hipSuccess;
-    auto kern = ckda_state_kernel<Tin, DK, DV, CKPT, SEG>;
+    auto kern = ckda_state_kernel<Tin, DK, DV, CKPT && OUT, SEG, OUT>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, SH::LDS);
     if (e != hipSuccess) return e;
@@ -663,7 +683,7 @@ hipError_t launch_state_c(const FwdArgs& A, size_t rec_bytes, hipStream_t stream
     const int nchains = A.cu ? A.ndocs * A.H : A.B * A.H;
     constexpr int NTS = SH::NTS;
     const int G = plan_segments(A, SH::NSLICE, NTS, rec_bytes);
-    if (G == 0) return launch_state_kernel<Tin, DK, DV, CKPT, false>(p, nchains * SH::NSLICE, stream);
+    if (G == 0) return launch_state_kernel<Tin, DK, DV, CKPT, false, true>(p, nchains * SH::NSLICE, stream);
     p.G = G;
     p.nsslots = seg_slots(A, G);
     float* sb = reinterpret_cast<float*>(static_cast<unsigned char*>(A.ws) + align256(rec_bytes));
@@ -671,14 +691,12 @@ hipError_t launch_state_c(const FwdArgs& A, size_t rec_bytes, hipStream_t stream
     p.seg_start = sb;
     p.seg_h = sb + per;
     p.seg_p = sb + 2 * per;
-    p.phase = 1;
-    hipError_t e = launch_state_kernel<Tin, DK, DV, CKPT, true>(p, p.nsslots * A.H * (SH::NSLICE + NTS), stream);
+    hipError_t e = launch_state_kernel<Tin, DK, DV, CKPT, true, false>(p, p.nsslots * A.H * (SH::NSLICE + NTS), stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((ckda_seg_scan_kernel<DK, DV>), dim3(nchains * SH::NSLICE), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((ckda_seg_scan_kernel<DK, DV>), dim3(nchains * (DV / kScanCols)), dim3(256), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    p.phase = 3;
-    return launch_state_kernel<Tin, DK, DV, CKPT, true>(p, p.nsslots * A.H * SH::NSLICE, stream);
+    return launch_state_kernel<Tin, DK, DV, CKPT, true, true>(p, p.nsslots * A.H * SH::NSLICE, stream);
 }
 
 template <typename Tin, int DK, int DV>

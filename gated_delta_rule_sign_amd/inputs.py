@@ -54,6 +54,8 @@ WORKLOADS = {
     # layer_bf16 with raw q, k that the path L2-normalises itself
     "layer_bf16_qk_norm": dict(index=6, B=8, T=4096, H=16, DK=128, DV=128, dtype="bf16",
                                qk="raw"),
+    # one long sequence: 16 (sequence, head) chains of 1024 chunks
+    "long_64k": dict(index=7, B=1, T=65536, H=16, DK=128, DV=128, dtype="bf16"),
 }
 
 
@@ -217,7 +219,7 @@ def make_workload(name: str, **override) -> Workload:
     seed = cfg.pop("seed", SEED_BASE + cfg["index"])
     rng = np.random.default_rng(seed)
     H, DK, DV, dt = cfg["H"], cfg["DK"], cfg["DV"], cfg["dtype"]
-    if name in ("tiny_fp32", "layer_bf16", "layer_bwd", "layer_bf16_head_gate", "layer_bf16_qk_norm"):
+    if name in ("tiny_fp32", "layer_bf16", "layer_bwd", "layer_bf16_head_gate", "layer_bf16_qk_norm", "long_64k"):
         B, T = cfg["B"], cfg["T"]
         tok = draw_tokens(rng, (B, T), H, DK, DV, dt, gate=cfg.get("gate", "channel"),
                           qk=cfg.get("qk", "unit"))
