@@ -122,3 +122,30 @@ def test_head_gate_decode(dtype):
     true_state = (host(sp).astype(np.float64)[..., None] * host(state)).reshape(N * H, DK, DV)
     assert rel_max(true_state, ST) < design
     assert np.array_equal(host(sp).reshape(N * H, DK), PT.astype(np.int8))
+
+
+def test_layer_head_gate_sampled():
+    """layer_bf16_head_gate at full size (B=8, T=4096, H=16, d=128, one gate
+    per token and head), as bench.py times it: sampled chains and value
+    columns against the oracle on the broadcast gates."""
+    torch = require_gpu()
+    banner("fwd layer_bf16_head_gate full size, sampled")
+    from gated_delta_rule_sign_amd import ckda
+    w = I.make_workload("layer_bf16_head_gate")
+    o, ht, _ = ckda.fwd(**tok_to_dev(w.tok))
+    torch.cuda.synchronize()
+    o = host(o); ht = host(ht)
+    chains = [(0, 3), (4, 11), (7, 15)]
+    cols = [0, 31, 64, 127]
+    bi = [c[0] for c in chains]; hi = [c[1] for c in chains]
+    # the sampled chains only ([2 or 3, T, 1, D]), gates broadcast over the channels
+    tk = w.tok
+    sub = {k: I.widen(getattr(tk, k)[bi, :, hi])[:, :, None] for k in ("q", "k", "v")}
+    sub["beta"] = tk.beta[bi, :, hi].astype(np.float64)[:, :, None]
+    for k in ("g", "s"):
+        sub[k] = np.repeat(getattr(tk, k)[bi, :, hi].astype(np.float64)[:, :, None, None], 128, axis=-1)
+    o_ref, ht_ref = oracle.fwd(**sub, cols=cols)
+    e_o = rel_max(o[bi, :, hi, :][:, :, cols], o_ref)
+    e_h = rel_max(ht[bi, hi][:, :, cols], ht_ref)
+    print(f"  head gate max|diff|/rms: o {e_o:.2e}  ht {e_h:.2e}")
+    assert e_o < 1e-2 and e_h < 1e-2

@@ -156,3 +156,28 @@ def test_qk_norm_decode(dtype, DK, DV):
     true_state = (host(sp).astype(np.float64)[..., None] * host(state)).reshape(N * H, DK, DV)
     assert rel_max(true_state, ST) < design
     assert np.array_equal(host(sp).reshape(N * H, DK), PT.astype(np.int8))
+
+
+def test_layer_qk_norm_sampled():
+    """layer_bf16_qk_norm at full size (B=8, T=4096, H=16, d=128, raw q and
+    k normalised in the path), as bench.py times it: sampled chains and value
+    columns against the oracle."""
+    torch = require_gpu()
+    banner("fwd layer_bf16_qk_norm full size, sampled")
+    from gated_delta_rule_sign_amd import ckda
+    w = I.make_workload("layer_bf16_qk_norm")
+    o, ht, _ = ckda.fwd(**tok_to_dev(w.tok), qk_norm=True)
+    torch.cuda.synchronize()
+    o = host(o); ht = host(ht)
+    chains = [(1, 2), (6, 14)]
+    cols = [3, 64, 126]
+    bi = [c[0] for c in chains]; hi = [c[1] for c in chains]
+    # the sampled chains only ([2, T, 1, D]), widened from storage
+    tk = w.tok
+    sub = {k: I.widen(getattr(tk, k)[bi, :, hi])[:, :, None] for k in ("q", "k", "v", "g", "s")}
+    sub["beta"] = tk.beta[bi, :, hi].astype(np.float64)[:, :, None]
+    o_ref, ht_ref = oracle.fwd(**sub, cols=cols, qk_norm=True)
+    e_o = rel_max(o[bi, :, hi, :][:, :, cols], o_ref)
+    e_h = rel_max(ht[bi, hi][:, :, cols], ht_ref)
+    print(f"  qk norm max|diff|/rms: o {e_o:.2e}  ht {e_h:.2e}")
+    assert e_o < 1e-2 and e_h < 1e-2

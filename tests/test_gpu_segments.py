@@ -158,3 +158,38 @@ def test_segmented_varlen_backward(segments):
             print(f"  doc {n} {name} vs oracle: {e:.2e}")
             assert e < TOL[dtype], (n, name, e)
         assert rel_max(host(r["dh0"])[n], ref["dh0"].reshape(H, DK, DV)) < TOL[dtype]
+
+
+def test_long_64k_sampled():
+    """long_64k at full size (one 65,536-token sequence, 16 heads, d = 128,
+    bf16) with the automatic state-pass plan, as bench.py times it (the cost
+    model segments it): sampled heads and value columns against the oracle,
+    and the whole output against the whole-chain pass."""
+    torch = require_gpu()
+    from gated_delta_rule_sign_amd import ckda
+    banner("fwd long_64k full size, automatic plan, sampled")
+    w = I.make_workload("long_64k")
+    d = tok_to_dev(w.tok)
+    ckda.set_segment_chunks(0)
+    o, ht, _ = ckda.fwd(**d)
+    ckda.set_segment_chunks(-1)
+    try:
+        o_w, ht_w, _ = ckda.fwd(**d)
+    finally:
+        ckda.set_segment_chunks(0)
+    torch.cuda.synchronize()
+    e_w = rel_max(host(o), host(o_w))
+    print(f"  o vs whole chains: {e_w:.2e}")
+    assert e_w < SEG_VS_WHOLE
+    o = host(o); ht = host(ht)
+    assert np.isfinite(o).all() and np.isfinite(ht).all()
+    hi = [0, 9, 15]
+    cols = [0, 45, 64, 127]
+    # the sampled heads only, widened from storage ([1, T, 3, D])
+    sub = {k: I.widen(getattr(w.tok, k)[:, :, hi]) for k in ("q", "k", "v", "g", "s")}
+    sub["beta"] = w.tok.beta[:, :, hi].astype(np.float64)
+    o_ref, ht_ref = oracle.fwd(**sub, cols=cols)
+    e_o = rel_max(o[0][:, hi, :][:, :, cols].transpose(1, 0, 2), o_ref)
+    e_h = rel_max(ht[0, hi][:, :, cols], ht_ref)
+    print(f"  long_64k max|diff|/rms: o {e_o:.2e}  ht {e_h:.2e}")
+    assert e_o < TOL["bf16"] and e_h < TOL["bf16"]
