@@ -158,12 +158,17 @@ def bench_fwd_long(torch, steps, warmup, workload):
     res = {"workload": workload, "tokens": tokens, "chains": int(len(lens) * H),
            "longest_chain_tokens": int(lens.max())}
     try:
-        for mode, G in (("auto", 0), ("whole_chains", -1)):
-            ckda.set_segment_chunks(G)
-            log(f"timing {workload} forward, state pass {mode}")
-            wall, per = time_kernel_launches(torch, fn, steps, warmup)
-            res[mode] = {"ms": wall / steps, "avg_launch_ms": float(np.mean(per)),
-                         "tokens_per_s": tokens / (wall / steps * 1e-3)}
+        # the two plans are timed twice, interleaved, and each keeps its faster
+        # pass (the first timed pass after input generation runs slow)
+        for rep in range(2):
+            for mode, G in (("auto", 0), ("whole_chains", -1)):
+                ckda.set_segment_chunks(G)
+                log(f"timing {workload} forward, state pass {mode} (pass {rep + 1} of 2)")
+                wall, per = time_kernel_launches(torch, fn, steps, warmup)
+                r = {"ms": wall / steps, "avg_launch_ms": float(np.mean(per)),
+                     "tokens_per_s": tokens / (wall / steps * 1e-3)}
+                if mode not in res or r["ms"] < res[mode]["ms"]:
+                    res[mode] = r
     finally:
         ckda.set_segment_chunks(0)
     res["speedup_auto_vs_whole"] = res["whole_chains"]["ms"] / res["auto"]["ms"]
