@@ -11,10 +11,11 @@ steps) is reported in the same line as state-streaming GB/s, the backward as
 tokens/s, and the same forward with one gate per (token, head), and with
 raw q and k that the path L2-normalises itself, as tokens/s; the forward
 over few long chains (varlen_64k, long_64k) with and without the segmented
-state pass.
+state pass, and the long_64k backward with and without the segmented
+reverse pass.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       [--only fwd|fwd_head_gate|fwd_qk_norm|fwd_long|decode|bwd|copy]
+       [--only fwd|fwd_head_gate|fwd_qk_norm|fwd_long|bwd_long|decode|bwd|copy]
 """
 from __future__ import annotations
 
@@ -239,6 +240,39 @@ def bench_bwd(torch, steps, warmup):
                 workspace_bytes=int(ws.numel()))
 
 
+def bench_bwd_long(torch, steps=2, warmup=1):
+    """Backward of long_64k (one 65,536-token sequence x 16 heads, bf16, a
+    seeded bf16 upstream gradient): the reverse (dS) pass with the automatic
+    plan (segments of the long chains) and with whole chains, interleaved,
+    each keeping its faster pass.  The forward with checkpoints runs once,
+    outside the timed region."""
+    from gated_delta_rule_sign_amd import ckda
+    from gated_delta_rule_sign_amd import inputs as I
+    log("generating long_64k inputs (backward)")
+    w = I.make_workload("long_64k")
+    tok = w.tok
+    d = {k: dev_tensor(torch, getattr(tok, k)) for k in ("q", "k", "v", "g", "s", "beta")}
+    B, T, H, DK = tok.q.shape
+    do = torch.randn((B, T, H, DK), generator=torch.Generator().manual_seed(77)).to(torch.bfloat16).to("cuda:0")
+    _, _, hc = ckda.fwd(**d, want_ckpt=True)
+    ws = torch.empty(ckda.bwd_workspace_bytes(B, T, H, DK, DK), dtype=torch.uint8, device="cuda:0")
+    fn = lambda: ckda.bwd(**d, h_ckpt=hc, do=do, workspace=ws)
+    res = {"workload": "long_64k backward", "tokens": B * T, "chains": B * H}
+    try:
+        for rep in range(2):
+            for mode, G in (("auto", 0), ("whole_chains", -1)):
+                ckda.set_segment_chunks(G)
+                log(f"timing long_64k backward, reverse pass {mode} (pass {rep + 1} of 2)")
+                wall, per = time_kernel_launches(torch, fn, steps, warmup)
+                r = {"ms": wall / steps, "tokens_per_s": B * T / (wall / steps * 1e-3)}
+                if mode not in res or r["ms"] < res[mode]["ms"]:
+                    res[mode] = r
+    finally:
+        ckda.set_segment_chunks(0)
+    res["speedup_auto_vs_whole"] = res["whole_chains"]["ms"] / res["auto"]["ms"]
+    return res
+
+
 def bench_copy(torch, nbytes=1 << 30, reps=5):
     """A plain device copy of known size (calibration for HBM byte counters)."""
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").uniform_()
@@ -277,8 +311,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "fwd_head_gate", "fwd_qk_norm", "fwd_long", "decode", "bwd", "copy"],
-                    default=None)
+    ap.add_argument("--only", choices=["fwd", "fwd_head_gate", "fwd_qk_norm", "fwd_long", "bwd_long", "decode", "bwd",
+                                       "copy"], default=None)
     ap.add_argument("--decode-steps", type=int, default=512)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -301,6 +335,9 @@ def main():
     if args.only == "bwd":
         print(json.dumps(bench_bwd(torch, args.steps, args.warmup)))
         return
+    if args.only == "bwd_long":
+        print(json.dumps(bench_bwd_long(torch)))
+        return
     if args.only == "fwd_long":
         print(json.dumps([bench_fwd_long(torch, max(3, args.steps // 4), 3, wl) for wl in ("varlen_64k", "long_64k")]))
         return
@@ -319,6 +356,7 @@ def main():
     fh = bench_fwd(torch, args.steps, args.warmup, "layer_bf16_head_gate")
     fq = bench_fwd(torch, args.steps, args.warmup, "layer_bf16_qk_norm")
     longs = [bench_fwd_long(torch, max(3, args.steps // 4), 3, wl) for wl in ("varlen_64k", "long_64k")]
+    bwl = bench_bwd_long(torch)
     cpu = None if args.no_cpu else cpu_baseline(fw["w"])
 
     achieved = fw["bytes"] / (fw["launch_ms"] * 1e-3) / 1e9
@@ -368,6 +406,7 @@ def main():
                             "achieved_gbs": fq["bytes"] / (fq["launch_ms"] * 1e-3) / 1e9,
                             "frac_of_hbm_peak": fq["bytes"] / (fq["launch_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "forward_long_chains": longs,
+        "backward_long_chains": bwl,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

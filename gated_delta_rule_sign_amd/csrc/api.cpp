@@ -250,12 +250,16 @@ ckda_status_t ckda_decode_step(int N, int H, int DK, int DV, ckda_dtype_t in_dty
 
 size_t ckda_bwd_workspace_bytes(int B, int T, int H, int DK, int DV) {
     if (B < 0 || T < 0 || H < 0 || !head_ok(DK) || !head_ok(DV)) return 0;
-    return ckda::bwd_workspace_bytes(fwd_slots(B, T), H, DK, DV);
+    const int G = ckda::segment_min_chunks();
+    const long long nss = static_cast<long long>(B) * (((T + 63) / 64 + G - 1) / G);
+    return ckda::bwd_workspace_bytes_full(fwd_slots(B, T), static_cast<int>(nss), H, DK, DV);
 }
 
 size_t ckda_bwd_varlen_workspace_bytes(int N, int T_total, int H, int DK, int DV) {
     if (N < 0 || T_total < 0 || H < 0 || !head_ok(DK) || !head_ok(DV)) return 0;
-    return ckda::bwd_workspace_bytes(varlen_slots(N, T_total), H, DK, DV);
+    const int G = ckda::segment_min_chunks();
+    const int nss = (T_total + 64 * G - 1) / (64 * G) + N;
+    return ckda::bwd_workspace_bytes_full(varlen_slots(N, T_total), nss, H, DK, DV);
 }
 
 namespace {
@@ -279,6 +283,7 @@ ckda_status_t bwd_common(ckda::BwdArgs& a, int nslots, bool any_tokens, const vo
             return fail(CKDA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
     }
     a.ws = const_cast<void*>(workspace);
+    a.ws_bytes = workspace_bytes;
     return hip_status(ckda::launch_bwd(a, nslots, static_cast<hipStream_t>(stream)), what);
 }
 
@@ -326,7 +331,7 @@ ckda_status_t ckda_bwd_varlen(int N, int T_total, const int32_t* cu, const int32
     a.head_gate = (flags & CKDA_GATE_HEAD) != 0; a.qk_norm = (flags & CKDA_QK_L2NORM) != 0;
     a.q = q; a.k = k; a.v = v; a.g = g; a.s = s; a.beta = beta; a.scale = scale; a.h0 = h0;
     a.h_ckpt = h_ckpt; a.dout = dout; a.dht = dht; a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg;
-    a.dbeta = dbeta; a.dh0 = dh0; a.cu = cu_dev; a.ndocs = N;
+    a.dbeta = dbeta; a.dh0 = dh0; a.cu = cu_dev; a.cu_host = cu; a.ndocs = N;
     return bwd_common(a, varlen_slots(N, T_total), T_total > 0, workspace, workspace_bytes, stream,
                       "ckda_bwd_varlen launch");
 }

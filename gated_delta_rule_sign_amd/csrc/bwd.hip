@@ -34,6 +34,7 @@
 #include "ckda_launch.h"
 #include "ckda_mfma.h"
 #include "ckda_record.h"
+#include "ckda_segments.h"
 
 namespace ckda {
 
@@ -269,6 +270,10 @@ struct BwdParams {
     int ndocs;
     bool head_gate;      // g, s, dg per (token, head)
     bool qk_norm;        // q, k L2-normalised per (token, head) inside the path
+    // segmented reverse pass: G chunks per segment, buffers as in
+    // ckda_segments.h (start = the dS entering a segment from its later end)
+    int G, nsslots;
+    float *seg_start, *seg_h, *seg_p;
 };
 
 // chunk-head ch -> (head, token row of the chunk start, valid tokens).
@@ -570,6 +575,7 @@ template <int DK, int DV>
 struct RevShape {
     static constexpr int BV = DV < 64 ? DV : 64;
     static constexpr int NSL = DV / BV;
+    static constexpr int NTS = (DK + BV - 1) / BV;   // transition slices (segmented pass)
     static constexpr int CT = BV / 16;               // column tiles
     // pitches (floats): rows read as "k = lane group" need 16 mod 64, rows
     // read as "row = lane % 16" need 4 mod 64
@@ -594,7 +600,11 @@ struct RevShape {
     static_assert(NKB >= 1 && NDO >= 1, "units");
 };
 
-template <int DK, int DV>
+// SEG: segmented pass (ckda_segments.h), phase 3 with OUT (dSt, dU and dh0
+// written), phase 1 without (segment maps only); otherwise one workgroup
+// walks a whole chain's value slice.  In the reverse pass the first segment
+// is the chain's last (it starts from dht).
+template <int DK, int DV, bool SEG, bool OUT>
 __global__ void __launch_bounds__(512) bwd_reverse_kernel(BwdParams p, BwdWs W) {
     using SH = RevShape<DK, DV>;
     constexpr int BV = SH::BV, CT = SH::CT, NM = SH::NM, NKB = SH::NKB, NDO = SH::NDO;
@@ -613,8 +623,33 @@ __global__ void __launch_bounds__(512) bwd_reverse_kernel(BwdParams p, BwdWs W) 
     float* const ems = pCs + DK;
     float* const gCs = ems + DK;
 
-    const int bh = blockIdx.x / SH::NSL;   // chain: b H + h, or (varlen) document H + h
-    const int v0 = (blockIdx.x % SH::NSL) * BV;
+    // work item x slice: value slices, then (phase 1) transition slices
+    constexpr int NS = (SEG && !OUT) ? SH::NSL + SH::NTS : SH::NSL;
+    const int item = blockIdx.x / NS, slice = blockIdx.x % NS;
+    const int hh = item % p.H;
+    int bh, seg = 0, ss = 0;   // chain: b H + h, or (varlen) document H + h
+    if (!SEG) {
+        bh = item;
+    } else {
+        ss = item / p.H;
+        int d;
+        if (p.cu) {
+            int lo = 0, hi = p.ndocs - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (seg_slot0(p.cu[mid], mid, p.G) <= ss) lo = mid; else hi = mid - 1;
+            }
+            d = lo;
+            seg = ss - seg_slot0(p.cu[lo], lo, p.G);
+        } else {
+            const int nsegT = (p.NT + p.G - 1) / p.G;
+            d = ss / nsegT;
+            seg = ss - d * nsegT;
+        }
+        bh = d * p.H + hh;
+    }
+    const bool trans = SEG && slice >= SH::NSL;
+    const int v0 = (trans ? slice - SH::NSL : slice) * BV;   // value columns, or columns of P_s
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63, n = l & 15, g = l >> 4;
@@ -627,7 +662,15 @@ __global__ void __launch_bounds__(512) bwd_reverse_kernel(BwdParams p, BwdWs W) 
     } else {
         NT = p.NT;
     }
-    const int hh = bh % p.H;
+    // the chunks walked, jbeg .. jend - 1 (from the end)
+    int jbeg = 0, jend = NT, nseg = 1;
+    if (SEG) {
+        nseg = (NT + p.G - 1) / p.G;
+        const bool run = OUT ? seg < max(nseg, 1) : (seg > 0 && seg < nseg && (seg < nseg - 1 || !trans));
+        if (!run) return;   // the whole workgroup, before any barrier
+        jbeg = seg * p.G;
+        jend = min(NT, jbeg + p.G);
+    }
     auto chj = [&](int j) -> size_t {
         return p.cu ? static_cast<size_t>(slot0 + j) * p.H + hh : static_cast<size_t>(bh) * NT + j;
     };
@@ -635,6 +678,7 @@ __global__ void __launch_bounds__(512) bwd_reverse_kernel(BwdParams p, BwdWs W) 
     // ---- register staging ---------------------------------------------------
     f32x4 rM[NM], rT[NM], rKB[NKB], rDO[NDO], rSM;
     f32x4 rQ[NKB], rK[NKB];
+    const int vl0 = trans ? 0 : v0;   // dO columns staged (transition slices zero them)
     auto load1 = [&](int j) {   // M, T, KB, dO slice, pC / em / gC of chunk j
         const size_t ch = chj(j);
         const f32x4* M4 = reinterpret_cast<const f32x4*>(W.M + ch * 4096);
@@ -647,7 +691,7 @@ __global__ void __launch_bounds__(512) bwd_reverse_kernel(BwdParams p, BwdWs W) 
 #pragma unroll
         for (int i = 0; i < NDO; ++i) {
             const int u = tid + 512 * i, r = u / (BV / 4), c4 = u % (BV / 4);
-            rDO[i] = *reinterpret_cast<const f32x4*>(W.dO + ch * 64 * DV + static_cast<size_t>(r) * DV + v0 + 4 * c4);
+            rDO[i] = *reinterpret_cast<const f32x4*>(W.dO + ch * 64 * DV + static_cast<size_t>(r) * DV + vl0 + 4 * c4);
         }
         // pC, em, gC: DK / 4 units each (clamped, so the load is unconditional)
         const int us = min(tid, 3 * (DK / 4) - 1), arr = us / (DK / 4), c4 = us % (DK / 4);
@@ -667,9 +711,9 @@ __global__ void __launch_bounds__(512) bwd_reverse_kernel(BwdParams p, BwdWs W) 
             *reinterpret_cast<f32x4*>(KBs + r * PKB + 4 * c4) = rKB[i];
         }
 #pragma unroll
-        for (int i = 0; i < NDO; ++i) {
+        for (int i = 0; i < NDO; ++i) {   // (transition slices: the map's linear part, dO = 0)
             const int u = tid + 512 * i, r = u / (BV / 4), c4 = u % (BV / 4);
-            *reinterpret_cast<f32x4*>(dOs + r * PV + 4 * c4) = rDO[i];
+            *reinterpret_cast<f32x4*>(dOs + r * PV + 4 * c4) = trans ? f32x4{0.f, 0.f, 0.f, 0.f} : rDO[i];
         }
         if (tid < 3 * (DK / 4)) *reinterpret_cast<f32x4*>(pCs + 4 * tid) = rSM;
     };
@@ -694,24 +738,30 @@ __global__ void __launch_bounds__(512) bwd_reverse_kernel(BwdParams p, BwdWs W) 
     constexpr int TG = (DK / 16) * CT, TPG = TG >= 8 ? TG / 8 : 1;     // DK x BV product
     const bool actU = w * TPU < TU, actG = w * TPG < TG;
 
-    // G = dht (or 0)
+    // G = dht (or 0) at the chain's end; segmented: the identity for
+    // transition slices, zero for the middle segments of phase 1, the
+    // scanned start in phase 3
+    const float* gsrc = p.dht ? p.dht + static_cast<size_t>(bh) * DK * DV : nullptr;
+    if (SEG && seg < nseg - 1) gsrc = OUT ? p.seg_start + (static_cast<size_t>(ss) * p.H + hh) * DK * DV : nullptr;
     for (int e = tid; e < DK * BV; e += 512) {
         const int c = e / BV, v = e % BV;
-        Gs[c * PV + v] = p.dht ? p.dht[(static_cast<size_t>(bh) * DK + c) * DV + v0 + v] : 0.f;
+        Gs[c * PV + v] = trans ? (c == v0 + v ? 1.f : 0.f) : (gsrc ? gsrc[static_cast<size_t>(c) * DV + v0 + v] : 0.f);
     }
-    if (NT > 0) {   // (an empty document has no chunks: dh0 = dht)
-        load1(NT - 1);
+    if (jend > jbeg) {   // (an empty document has no chunks: dh0 = dht)
+        load1(jend - 1);
         store1();
     }
     __syncthreads();
-    for (int j = NT - 1; j >= 0; --j) {
+    for (int j = jend - 1; j >= jbeg; --j) {
         const size_t ch = chj(j);
         load2(j);
         // dSt = Diag(pC) G to the workspace (slice columns)
-        for (int e = tid; e < DK * (BV / 4); e += 512) {
-            const int c = e / (BV / 4), c4 = e % (BV / 4);
-            const f32x4 gv = *reinterpret_cast<const f32x4*>(Gs + c * PV + 4 * c4);
-            *reinterpret_cast<f32x4*>(W.dSt + ch * DK * DV + static_cast<size_t>(c) * DV + v0 + 4 * c4) = pCs[c] * gv;
+        if (OUT) {
+            for (int e = tid; e < DK * (BV / 4); e += 512) {
+                const int c = e / (BV / 4), c4 = e % (BV / 4);
+                const f32x4 gv = *reinterpret_cast<const f32x4*>(Gs + c * PV + 4 * c4);
+                *reinterpret_cast<f32x4*>(W.dSt + ch * DK * DV + static_cast<size_t>(c) * DV + v0 + 4 * c4) = pCs[c] * gv;
+            }
         }
         // dU = M^T dO + KB dSt
         if (actU) {
@@ -749,10 +799,12 @@ __global__ void __launch_bounds__(512) bwd_reverse_kernel(BwdParams p, BwdWs W) 
         }
         __syncthreads();
         // dU to the workspace; Z = T^T dU (held in registers until dU is no longer read)
-        for (int e = tid; e < 64 * (BV / 4); e += 512) {
-            const int r = e / (BV / 4), c4 = e % (BV / 4);
-            *reinterpret_cast<f32x4*>(W.dU + ch * 64 * DV + static_cast<size_t>(r) * DV + v0 + 4 * c4) =
-                *reinterpret_cast<const f32x4*>(UZs + r * PV + 4 * c4);
+        if (OUT) {
+            for (int e = tid; e < 64 * (BV / 4); e += 512) {
+                const int r = e / (BV / 4), c4 = e % (BV / 4);
+                *reinterpret_cast<f32x4*>(W.dU + ch * 64 * DV + static_cast<size_t>(r) * DV + v0 + 4 * c4) =
+                    *reinterpret_cast<const f32x4*>(UZs + r * PV + 4 * c4);
+            }
         }
         f32x4 zacc[TPU];
         int zti[TPU], ztj[TPU];
@@ -782,7 +834,7 @@ __global__ void __launch_bounds__(512) bwd_reverse_kernel(BwdParams p, BwdWs W) 
                 for (int i = 0; i < 4; ++i) UZs[(16 * zti[u] + 4 * g + i) * PV + 16 * ztj[u] + n] = zacc[u][i];
         }
         store2();
-        load1(j > 0 ? j - 1 : 0);
+        load1(j > jbeg ? j - 1 : jbeg);
         __syncthreads();
         // G <- Diag(e^m) (Q1^T dO - K1^T Z) + Diag(e^{b_L} pC) G   (each wave its own tiles, in place)
         if (actG) {
@@ -815,27 +867,67 @@ __global__ void __launch_bounds__(512) bwd_reverse_kernel(BwdParams p, BwdWs W) 
                 }
         }
         __syncthreads();
-        store1();   // chunk j - 1 (on the last chunk: chunk 0 again, unused)
+        store1();   // chunk j - 1 (on the last chunk walked: that chunk again, unused)
         __syncthreads();
     }
-    if (p.dh0) {
+    // the end state: dh0 (whole chains; phase 3, the chain's first segment),
+    // or in phase 1 the start of the next segment in pass order (the chain's
+    // last segment), H_s or P_s (middle segments)
+    float* dst = p.dh0 ? p.dh0 + static_cast<size_t>(bh) * DK * DV : nullptr;
+    int pitch = DV, ncol = BV;
+    if (SEG && !OUT) {
+        if (seg == nseg - 1) {
+            dst = p.seg_start + (static_cast<size_t>(ss - 1) * p.H + hh) * DK * DV;
+        } else if (trans) {
+            dst = p.seg_p + (static_cast<size_t>(ss) * p.H + hh) * DK * DK;
+            pitch = DK;
+            ncol = min(BV, DK - v0);   // (columns of P_s past DK do not exist)
+        } else {
+            dst = p.seg_h + (static_cast<size_t>(ss) * p.H + hh) * DK * DV;
+        }
+    } else if (SEG && seg > 0) {
+        dst = nullptr;
+    }
+    if (dst) {
         for (int e = tid; e < DK * BV; e += 512) {
             const int c = e / BV, v = e % BV;
-            p.dh0[(static_cast<size_t>(bh) * DK + c) * DV + v0 + v] = Gs[c * PV + v];
+            if (v < ncol) dst[static_cast<size_t>(c) * pitch + v0 + v] = Gs[c * PV + v];
         }
     }
 }
 
-template <int DK, int DV>
-static hipError_t launch_reverse_t(const BwdParams& p, const BwdWs& W, hipStream_t st) {
+template <int DK, int DV, bool SEG, bool OUT>
+static hipError_t launch_reverse_k(const BwdParams& p, const BwdWs& W, int grid, hipStream_t st) {
     using SH = RevShape<DK, DV>;
-    auto kern = bwd_reverse_kernel<DK, DV>;
+    if (grid == 0) return hipSuccess;
+    auto kern = bwd_reverse_kernel<DK, DV, SEG, OUT>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, SH::BYTES);
     if (e != hipSuccess) return e;
-    const int nchains = (p.cu ? p.ndocs : p.B) * p.H;
-    hipLaunchKernelGGL(kern, dim3(nchains * SH::NSL), dim3(512), SH::BYTES, st, p, W);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(512), SH::BYTES, st, p, W);
     return hipGetLastError();
+}
+
+// measured on MI355X (dk = dv = 128): a lone chain's reverse step is the
+// unit (about 14.6 us); the GPU completes about 15.5 workgroup chunk-steps
+// per us (0.88 per CU per unit); phase 1 skips only the dSt / dU stores; a
+// scan step is about 6 us
+constexpr SegCost kReverseCost{0.88, 0.9, 0.5};
+
+// the reverse pass over every chain: whole chains, or segments (p.G > 0,
+// buffers set) in three launches
+template <int DK, int DV>
+static hipError_t launch_reverse_t(const BwdParams& p, const BwdWs& W, hipStream_t st) {
+    using SH = RevShape<DK, DV>;
+    const int nchains = (p.cu ? p.ndocs : p.B) * p.H;
+    if (p.G == 0) return launch_reverse_k<DK, DV, false, true>(p, W, nchains * SH::NSL, st);
+    hipError_t e = launch_reverse_k<DK, DV, true, false>(p, W, p.nsslots * p.H * (SH::NSL + SH::NTS), st);
+    if (e != hipSuccess) return e;
+    const SegScanParams sp{p.cu, p.T, p.H, p.G, p.seg_start, p.seg_h, p.seg_p, 1};
+    hipLaunchKernelGGL((ckda_seg_scan_kernel<DK, DV>), dim3(nchains * (DV / kScanCols)), dim3(256), 0, st, sp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_reverse_k<DK, DV, true, true>(p, W, p.nsslots * p.H * SH::NSL, st);
 }
 
 static hipError_t launch_reverse(const BwdParams& p, const BwdWs& W, hipStream_t st) {
@@ -1111,6 +1203,10 @@ size_t bwd_workspace_bytes(int nslots, int H, int DK, int DV) {
     return BwdWs::floats(static_cast<size_t>(nslots) * H, DK, DV) * sizeof(float);
 }
 
+size_t bwd_workspace_bytes_full(int nslots, int nsslots_max, int H, int DK, int DV) {
+    return align256(bwd_workspace_bytes(nslots, H, DK, DV)) + seg_buffer_bytes(nsslots_max, H, DK, DV);
+}
+
 hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t st) {
     const int NT = (a.T + 63) / 64;
     const int NC = nslots * a.H;
@@ -1122,6 +1218,25 @@ hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t st) {
     p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dg = a.dg; p.dbeta = a.dbeta; p.dh0 = a.dh0;
     p.B = a.B; p.T = a.T; p.H = a.H; p.NT = NT; p.cu = a.cu; p.ndocs = a.ndocs; p.head_gate = a.head_gate;
     p.qk_norm = a.qk_norm;
+    {   // segmented reverse pass when the plan takes it and the workspace has room
+        const bool varlen = a.cu != nullptr;
+        const size_t base = bwd_workspace_bytes(nslots, a.H, DK, DV);
+        const size_t avail = a.ws_bytes > align256(base) ? a.ws_bytes - align256(base) : 0;
+        auto fits = [&](int G) {
+            return seg_buffer_bytes(seg_slots(varlen, a.B, a.T, a.ndocs, G), a.H, DK, DV) <= avail;
+        };
+        const int BVr = DV < 64 ? DV : 64;
+        p.G = plan_segments(chain_chunks(a.cu_host, varlen, a.ndocs, a.B, a.T), a.H, DV / BVr,
+                            (DK + BVr - 1) / BVr, kReverseCost, fits);
+        if (p.G > 0) {
+            p.nsslots = seg_slots(varlen, a.B, a.T, a.ndocs, p.G);
+            float* sb = reinterpret_cast<float*>(static_cast<unsigned char*>(a.ws) + align256(base));
+            const size_t per = static_cast<size_t>(p.nsslots) * a.H * DK * DV;
+            p.seg_start = sb;
+            p.seg_h = sb + per;
+            p.seg_p = sb + 2 * per;
+        }
+    }
     if (NC == 0) {
         // no tokens: dh0 = dht (or 0)
         const size_t n = static_cast<size_t>(nchains) * DK * DV;

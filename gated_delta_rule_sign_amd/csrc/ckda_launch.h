@@ -89,11 +89,15 @@ struct BwdArgs {
     // varlen: as in FwdArgs (documents from cu, h0 / dht / dh0 per document,
     // checkpoints per chunk slot); nullptr selects the equal-length mode
     const int32_t* cu;
+    const int32_t* cu_host;   // the same offsets on the host (varlen), for the reverse-pass plan
     int ndocs;
-    void* ws;
+    void* ws;          // at least bwd_workspace_bytes(nslots, ...) bytes
+    size_t ws_bytes;   // its size: room beyond that enables the segmented reverse pass
 };
-// nslots: chunk slots, as for the forward
+// nslots: chunk slots, as for the forward; the minimum workspace
 size_t bwd_workspace_bytes(int nslots, int H, int DK, int DV);
+// plus the segment buffers for up to nsslots_max segment slots
+size_t bwd_workspace_bytes_full(int nslots, int nsslots_max, int H, int DK, int DV);
 hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t stream);
 
 }  // namespace ckda

@@ -46,6 +46,7 @@
 #include "ckda_mfma.h"
 #include "ckda_prec.h"
 #include "ckda_record.h"
+#include "ckda_segments.h"
 #include "ckda_sync.h"
 
 namespace ckda {
@@ -122,8 +123,6 @@ struct StateParams {
     float* seg_p;       // [nsslots][H][DK][DK] segment map P_s (middle segments)
 };
 
-// first segment slot of chain d (varlen document start cu_d)
-__host__ __device__ inline int seg_slot0(int cu_d, int d, int G) { return cu_d / (64 * G) + d; }
 
 // SEG: segment mode, phase 3 with OUT, phase 1 without; otherwise (OUT set)
 // one workgroup walks a whole chain's value slice
@@ -497,169 +496,16 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
     }
 }
 
-// Segment phase 2: per (chain, head, 16-column slice) of a chain with more
-// than two segments, start_{s+1} = P_s start_s + H_s for s = 1 .. n-2
-// (start_1 is the first segment's end state, written by phase 1).  fp32
-// FMA: thread t owns row t/2, columns 8(t%2) .. +7 of the slice; it streams
-// its row of P_s from L2 and reads the slice of start_s from LDS (two
-// addresses per wave: broadcasts).
-constexpr int kScanCols = 16;
-template <int DK, int DV>
-__global__ void __launch_bounds__(256) ckda_seg_scan_kernel(StateParams p)
-{
-    constexpr int NSL = DV / kScanCols, NTH = 2 * DK;
-    static_assert(NTH <= 256, "threads");
-    __shared__ __align__(16) float Ssl[DK * kScanCols];   // the slice of start_s
-    const int H = p.H;
-    const int slice = blockIdx.x % NSL;
-    const int h = (blockIdx.x / NSL) % H;
-    const int d = blockIdx.x / (NSL * H);
-    const int NTC = (p.T + 63) / 64;
-    int len, ss0;
-    if (p.cu) {
-        len = p.cu[d + 1] - p.cu[d];
-        ss0 = seg_slot0(p.cu[d], d, p.G);
-    } else {
-        len = p.T;
-        ss0 = d * ((NTC + p.G - 1) / p.G);
-    }
-    const int nseg = ((len + 63) / 64 + p.G - 1) / p.G;
-    if (nseg <= 2) return;
-    const int tid = threadIdx.x;
-    const int c0 = slice * kScanCols;
-    const size_t sdv = static_cast<size_t>(DK) * DV;
-    {   // start_1
-        const float* src = p.seg_start + (static_cast<size_t>(ss0 + 1) * H + h) * sdv;
-        for (int e = tid; e < DK * kScanCols; e += 256)
-            Ssl[e] = src[static_cast<size_t>(e / kScanCols) * DV + c0 + e % kScanCols];
-    }
-    __syncthreads();
-    const int r = tid >> 1, cb = 8 * (tid & 1);
-    for (int sgi = 1; sgi <= nseg - 2; ++sgi) {
-        const size_t it = static_cast<size_t>(ss0 + sgi) * H + h;
-        float acc[8];
-        if (tid < NTH) {
-            const float* Hs = p.seg_h + it * sdv + static_cast<size_t>(r) * DV + c0 + cb;
-            const f32x4 h0 = *reinterpret_cast<const f32x4*>(Hs), h1 = *reinterpret_cast<const f32x4*>(Hs + 4);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                acc[c] = h0[c];
-                acc[4 + c] = h1[c];
-            }
-            const f32x4* P = reinterpret_cast<const f32x4*>(p.seg_p + it * DK * DK + static_cast<size_t>(r) * DK);
-            f32x4 prow[DK / 4];   // the whole row in flight at once (L2 latency once per step)
-#pragma unroll
-            for (int k4 = 0; k4 < DK / 4; ++k4) prow[k4] = P[k4];
-#pragma unroll
-            for (int k4 = 0; k4 < DK / 4; ++k4) {
-                const f32x4 pr = prow[k4];
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const float* sr = Ssl + (4 * k4 + kk) * kScanCols + cb;
-                    const f32x4 s0 = *reinterpret_cast<const f32x4*>(sr), s1 = *reinterpret_cast<const f32x4*>(sr + 4);
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        acc[c] = fmaf(pr[kk], s0[c], acc[c]);
-                        acc[4 + c] = fmaf(pr[kk], s1[c], acc[4 + c]);
-                    }
-                }
-            }
-        }
-        __syncthreads();   // every read of start_s done
-        if (tid < NTH) {
-            float* dst = p.seg_start + (static_cast<size_t>(ss0 + sgi + 1) * H + h) * sdv +
-                         static_cast<size_t>(r) * DV + c0 + cb;
-            *reinterpret_cast<f32x4*>(Ssl + r * kScanCols + cb) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-            *reinterpret_cast<f32x4*>(Ssl + r * kScanCols + cb + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
-            *reinterpret_cast<f32x4*>(dst) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-            *reinterpret_cast<f32x4*>(dst + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
-        }
-        __syncthreads();
-    }
-}
-
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 namespace {
 
-std::atomic<int> g_seg_chunks{0};   // 0: automatic, < 0: never, >= kSegMinChunks: that length
-constexpr int kSegMinChunks = 16;
-
-// segment slots for segments of G chunks
-int seg_slots(const FwdArgs& A, int G) {
-    if (A.cu) return (A.T + 64 * G - 1) / (64 * G) + A.ndocs;
-    return A.B * (((A.T + 63) / 64 + G - 1) / G);
-}
-
-size_t seg_buffer_bytes(size_t nsslots, int H, int DK, int DV) {
-    return nsslots * H * (2 * static_cast<size_t>(DK) * DV + static_cast<size_t>(DK) * DK) * sizeof(float);
-}
-
-size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
-
-// compute units of the current device (state workgroups run two per CU)
-int device_cus() {
-    static std::atomic<int> cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int n = cached[dev].load();
-    if (n <= 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev].store(n);
-    }
-    return n;
-}
-
-// Segment length for the state pass, 0 for whole chains.  Cost model in
-// units of one chunk-step of a workgroup that has its CU to itself: a phase
-// takes at least its longest item and at least its total work (workgroup
-// chunk-steps) over the GPU's throughput, measured on MI355X (dk = dv = 128,
-// bf16 records) at about 0.64 chunk-steps per CU per unit (a lone chain
-// steps in about 3.1 us; 256 CUs complete about 53 workgroup chunk-steps per
-// us, with one workgroup per CU or two).  Whole chains: max(longest chain,
-// work W / R).  Segments of G chunks: phase 1 (first segments, and value +
-// transition slices of the middle segments, at kNoOut of a step without
-// the output products) + phase 3 (every segment: W again, in items of at
-// most G chunks) + the scan (about three units per step) + launch gaps.
-// The segment plan is taken when it is below 0.8 of the whole-chain one.
-constexpr double kCuRate = 0.64, kNoOut = 0.6, kScanStep = 3.0;
-int plan_segments(const FwdArgs& A, int nslice, int ntrans, size_t rec_bytes) {
-    const int forced = g_seg_chunks.load();
-    if (forced < 0 || A.H == 0) return 0;
-    std::vector<int> nch;
-    if (A.cu) {
-        if (!A.cu_host) return 0;
-        for (int d = 0; d < A.ndocs; ++d) nch.push_back((A.cu_host[d + 1] - A.cu_host[d] + 63) / 64);
-    } else {
-        nch.assign(A.B, (A.T + 63) / 64);
-    }
-    int maxn = 0;
-    double tot = 0;
-    for (int n : nch) { maxn = n > maxn ? n : maxn; tot += n; }
-    const size_t avail = A.ws_bytes > align256(rec_bytes) ? A.ws_bytes - align256(rec_bytes) : 0;
-    auto fits = [&](int G) { return seg_buffer_bytes(seg_slots(A, G), A.H, A.DK, A.DV) <= avail; };
-    if (forced > 0) return (maxn > forced && fits(forced)) ? forced : 0;
-    const double R = kCuRate * device_cus();   // workgroup chunk-steps per unit, whole GPU
-    const double W = tot * A.H * nslice;
-    const double t0 = std::max(static_cast<double>(maxn), W / R);
-    int best = 0;
-    double tbest = 0.8 * t0;
-    for (int G = kSegMinChunks; G < maxn; G *= 2) {
-        if (!fits(G)) continue;
-        double w1 = 0;
-        int maxseg = 0;
-        for (int n : nch) {
-            const int ns = (n + G - 1) / G;
-            maxseg = std::max(maxseg, ns);
-            if (ns >= 2) w1 += static_cast<double>(nslice) * G + static_cast<double>(ns - 2) * (nslice + ntrans) * G;
-        }
-        const double t = std::max(static_cast<double>(G), kNoOut * w1 * A.H / R) +
-                         std::max(static_cast<double>(G), W / R) + kScanStep * std::max(0, maxseg - 2) + 2.0;
-        if (t < tbest) { tbest = t; best = G; }
-    }
-    return best;
-}
+// measured on MI355X (dk = dv = 128, bf16 records): a lone chain steps in
+// about 3.1 us (the unit); 256 CUs complete about 53 workgroup chunk-steps
+// per us, with one workgroup per CU or two; a step without the output
+// products costs about 0.6 of one; a scan step about 3 units
+constexpr SegCost kStateCost{0.64, 0.6, 3.0};
 
 template <typename Tin, int DK, int DV, bool CKPT, bool SEG, bool OUT>
 hipError_t launch_state_kernel(const StateParams& p, int grid, hipStream_t stream) {
@@ -682,10 +528,16 @@ hipError_t launch_state_c(const FwdArgs& A, size_t rec_bytes, hipStream_t stream
     p.B = A.B; p.T = A.T; p.H = A.H; p.ndocs = A.ndocs;
     const int nchains = A.cu ? A.ndocs * A.H : A.B * A.H;
     constexpr int NTS = SH::NTS;
-    const int G = plan_segments(A, SH::NSLICE, NTS, rec_bytes);
+    const bool varlen = A.cu != nullptr;
+    const size_t avail = A.ws_bytes > align256(rec_bytes) ? A.ws_bytes - align256(rec_bytes) : 0;
+    auto fits = [&](int G) {
+        return seg_buffer_bytes(seg_slots(varlen, A.B, A.T, A.ndocs, G), A.H, DK, DV) <= avail;
+    };
+    const int G = plan_segments(chain_chunks(A.cu_host, varlen, A.ndocs, A.B, A.T), A.H, SH::NSLICE, NTS,
+                                kStateCost, fits);
     if (G == 0) return launch_state_kernel<Tin, DK, DV, CKPT, false, true>(p, nchains * SH::NSLICE, stream);
     p.G = G;
-    p.nsslots = seg_slots(A, G);
+    p.nsslots = seg_slots(varlen, A.B, A.T, A.ndocs, G);
     float* sb = reinterpret_cast<float*>(static_cast<unsigned char*>(A.ws) + align256(rec_bytes));
     const size_t per = static_cast<size_t>(p.nsslots) * A.H * DK * DV;
     p.seg_start = sb;
@@ -693,7 +545,8 @@ hipError_t launch_state_c(const FwdArgs& A, size_t rec_bytes, hipStream_t stream
     p.seg_p = sb + 2 * per;
     hipError_t e = launch_state_kernel<Tin, DK, DV, CKPT, true, false>(p, p.nsslots * A.H * (SH::NSLICE + NTS), stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((ckda_seg_scan_kernel<DK, DV>), dim3(nchains * (DV / kScanCols)), dim3(256), 0, stream, p);
+    const SegScanParams sp{A.cu, A.T, A.H, G, p.seg_start, p.seg_h, p.seg_p, 0};
+    hipLaunchKernelGGL((ckda_seg_scan_kernel<DK, DV>), dim3(nchains * (DV / kScanCols)), dim3(256), 0, stream, sp);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_state_kernel<Tin, DK, DV, CKPT, true, true>(p, p.nsslots * A.H * SH::NSLICE, stream);
@@ -735,9 +588,25 @@ hipError_t launch_state(const FwdArgs& A, hipStream_t stream) {
     return A.bf16 ? launch_state_dt<bf16_t>(A, stream) : launch_state_dt<float>(A, stream);
 }
 
+namespace {
+std::atomic<int> g_seg_chunks{0};   // 0: automatic, < 0: never, >= kSegMinChunks: that length
+}  // namespace
+
 void set_segment_chunks(int G) { g_seg_chunks.store(G); }
 int segment_chunks() { return g_seg_chunks.load(); }
 int segment_min_chunks() { return kSegMinChunks; }
+
+int device_cus() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load();
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev].store(n);
+    }
+    return n;
+}
 
 // forward = chunk-local kernel over every (chunk, head), then the state pass
 size_t fwd_workspace_bytes(int nslots, int H, int DK, int DV, bool bf16) {

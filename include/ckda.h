@@ -138,7 +138,8 @@ ckda_status_t ckda_fwd_chunked(int B, int T, int H, int DK, int DV, ckda_dtype_t
                                void* workspace, size_t workspace_bytes, ckda_stream_t stream);
 
 /* ------------------------------------------------------------------------
- * Segment length of the forward's state pass, process-wide (all devices).
+ * Segment length of the forward's state pass and of the backward's reverse
+ * (state-gradient) pass, process-wide (all devices).
  * Per chunk the state map is affine, S' = A_c S + B_c, and the columns of
  * S evolve independently, so a long chain can be split into segments whose
  * maps (A and B composed over the segment) are built in parallel and then
@@ -210,7 +211,11 @@ ckda_status_t ckda_decode_step(int N, int H, int DK, int DV, ckda_dtype_t in_dty
  *   (flags & CKDA_GATE_HEAD: g, s and dg are [B,T,H]; dg is then the sum
  *   over channels of the channel-gate gradient)
  *   dh0: [B,H,DK,DV] f32 or NULL
- *   workspace: ckda_bwd_workspace_bytes(...) bytes of device memory
+ *   workspace: ckda_bwd_workspace_bytes(...) bytes of device memory: the
+ *           per-(chunk, head) blocks of the chunk-parallel passes, then the
+ *           segment buffers of the reverse pass (see ckda_set_segment_chunks;
+ *           a workspace with only the blocks is accepted and keeps whole
+ *           chains)
  * dg is the gradient w.r.t. g = log|alpha| (alpha * dL/dalpha); s gets none.
  * ---------------------------------------------------------------------- */
 size_t ckda_bwd_workspace_bytes(int B, int T, int H, int DK, int DV);

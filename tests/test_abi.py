@@ -77,6 +77,12 @@ def seg_bytes(nsslots, H, DK, DV):
     return nsslots * H * (2 * DK * DV + DK * DK) * 4
 
 
+def bwd_block_bytes(DK, DV):
+    """Backward workspace per chunk-head: 9 [64 x DK], 6 [64 x DV], 2 [DK x DV]
+    and 10 [64 x 64] fp32 matrices, 3 [DK] and 3 [64] vectors."""
+    return 4 * (9 * 64 * DK + 6 * 64 * DV + 2 * DK * DV + 10 * 64 * 64 + 3 * DK + 3 * 64)
+
+
 def test_fwd_workspace(L):
     need = L.ckda_fwd_workspace_bytes(2, 100, 3, 64, 32, 1)
     # one record per (chunk, head): bf16 keeps W in one plane, Qh/KbT/M in two
@@ -127,9 +133,12 @@ def test_varlen_backward_boundary(L):
     # chunk slots: ceil(T_total / 64) + N; one workspace block per (slot, head)
     assert L.ckda_varlen_chunk_slots(3, 100) == 2 + 3
     assert L.ckda_varlen_chunk_slots(-1, 100) == 0
-    one = L.ckda_bwd_workspace_bytes(1, 64, 1, 64, 32)           # one chunk-head
-    assert one > 0
-    assert L.ckda_bwd_varlen_workspace_bytes(3, 100, 2, 64, 32) == (2 + 3) * 2 * one
+    # one backward workspace block per (chunk slot, head), then the segment
+    # buffers of the reverse pass (segments of 16 chunks)
+    one = bwd_block_bytes(64, 32)
+    assert L.ckda_bwd_workspace_bytes(1, 64, 1, 64, 32) == align256(one) + seg_bytes(1, 1, 64, 32)
+    assert L.ckda_bwd_varlen_workspace_bytes(3, 100, 2, 64, 32) == \
+        align256((2 + 3) * 2 * one) + seg_bytes(1 + 3, 2, 64, 32)
     assert L.ckda_bwd_varlen_workspace_bytes(3, 100, 2, 48, 32) == 0
     assert bwd_varlen(L, [1, 5], 1, 5) == 5                       # does not start at 0
     assert bwd_varlen(L, [0, 5, 3], 2, 3) == 5                    # decreasing
@@ -139,8 +148,8 @@ def test_varlen_backward_boundary(L):
     assert bwd_varlen(L, [0, 5], 1, 5, hc=None) == 1              # checkpoints required
     assert b"h_ckpt" in L.ckda_last_error()
     assert bwd_varlen(L, [0, 5], 1, 5, q=P(0x1004)) == 4          # misaligned
-    need = L.ckda_bwd_varlen_workspace_bytes(1, 5, 1, 32, 32)
-    assert bwd_varlen(L, [0, 5], 1, 5, wsb=need - 16) == 6
+    # below the per-chunk blocks (2 chunk slots) the call fails before any launch
+    assert bwd_varlen(L, [0, 5], 1, 5, wsb=2 * bwd_block_bytes(32, 32) - 16) == 6
     assert bwd_varlen(L, [0], 0, 0) == 0                          # no documents
 
 

@@ -193,3 +193,47 @@ def test_long_64k_sampled():
     e_h = rel_max(ht[0, hi][:, :, cols], ht_ref)
     print(f"  long_64k max|diff|/rms: o {e_o:.2e}  ht {e_h:.2e}")
     assert e_o < TOL["bf16"] and e_h < TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype,DK,DV,T", [("f32", 64, 64, 2500), ("bf16", 128, 128, 3300), ("f32", 32, 128, 1100)])
+def test_segmented_reverse_pass(dtype, DK, DV, T):
+    """The backward's reverse (dS) pass cut into segments of 16 chunks (the
+    map G' = A'_c G + B'_c is affine with independent value columns, as in
+    the forward): the same checkpoints, gradients with segments against
+    gradients with whole chains, and both against the oracle."""
+    torch = require_gpu()
+    from gated_delta_rule_sign_amd import ckda
+    B, H = 2, 2
+    banner(f"segmented reverse pass {dtype} B={B} T={T} H={H} DK={DK} DV={DV}")
+    w = I.make_forward(B, T, H, DK, DV, dtype, seed=53 + T, h0_std=0.3)
+    long_memory(w.tok)
+    rng = np.random.default_rng(T + 7)
+    do_st = I.to_storage(rng.standard_normal((B, T, H, DV)), dtype)
+    do = dev_tensor(do_st)
+    dht = rng.standard_normal((B, H, DK, DV)).astype(np.float32)
+    d = tok_to_dev(w.tok)
+    h0 = dev_tensor(w.h0)
+    try:
+        ckda.set_segment_chunks(-1)
+        _, _, hc = ckda.fwd(**d, scale=0.8, h0=h0, want_ckpt=True)
+        r_w = ckda.bwd(**d, h_ckpt=hc, do=do, scale=0.8, h0=h0, dht=dev_tensor(dht))
+        ckda.set_segment_chunks(16)
+        r = ckda.bwd(**d, h_ckpt=hc, do=do, scale=0.8, h0=h0, dht=dev_tensor(dht))
+    finally:
+        ckda.set_segment_chunks(0)
+    torch.cuda.synchronize()
+    for name in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        e = rel_max(host(r[name]), host(r_w[name]))
+        print(f"  {name} segmented vs whole chains: {e:.2e}")
+        assert e < GRAD_SEG_VS_WHOLE, (name, e)
+    f = w.tok.f64()
+    ref = oracle.bwd(**f, do=I.widen(do_st), scale=0.8, h0=w.h0.astype(np.float64), dht=dht.astype(np.float64))
+    chains = [(b, h) for b in range(B) for h in range(H)]
+    bi = [c[0] for c in chains]; hi = [c[1] for c in chains]
+    for name in ("dq", "dk", "dv", "dg", "dbeta"):
+        g = host(r[name])
+        g = g[bi, :, hi] if g.ndim == 3 else g[bi, :, hi, :]
+        e = rel_max(g, ref[name])
+        print(f"  {name} vs oracle: {e:.2e}")
+        assert e < TOL[dtype], (name, e)
+    assert rel_max(host(r["dh0"]).reshape(B * H, DK, DV), ref["dh0"]) < TOL[dtype]
