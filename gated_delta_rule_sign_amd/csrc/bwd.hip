@@ -571,6 +571,63 @@ __global__ void __launch_bounds__(256) bwd_inverse_kernel(BwdWs W) {
 // Z are formed, and the next chunk's M, T, KB, dO while G is formed, so HBM
 // latency hides behind the products.
 // ---------------------------------------------------------------------------
+// The work of one reverse-pass workgroup: its chain (bh = b H + h, or
+// document H + h), value slice (or, segmented phase 1, slice of P_s's
+// columns), and the chunks it walks, jbeg .. jend - 1 from the end.  NS
+// slices per item: the value slices, then (phase 1) the transition slices.
+struct RevWork {
+    int bh, hh, seg, ss, nseg, v0, NT, slot0, jbeg, jend;
+    bool trans, run;
+    __device__ size_t chj(const BwdParams& p, int j) const {   // chunk j -> chunk-head
+        return p.cu ? static_cast<size_t>(slot0 + j) * p.H + hh : static_cast<size_t>(bh) * NT + j;
+    }
+};
+template <bool SEG, bool OUT>
+__device__ __forceinline__ RevWork rev_work(const BwdParams& p, int NSL, int NS, int BV) {
+    RevWork r{};
+    const int item = blockIdx.x / NS, slice = blockIdx.x % NS;
+    r.hh = item % p.H;
+    if (!SEG) {
+        r.bh = item;
+    } else {
+        r.ss = item / p.H;
+        int d;
+        if (p.cu) {
+            int lo = 0, hi = p.ndocs - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (seg_slot0(p.cu[mid], mid, p.G) <= r.ss) lo = mid; else hi = mid - 1;
+            }
+            d = lo;
+            r.seg = r.ss - seg_slot0(p.cu[lo], lo, p.G);
+        } else {
+            const int nsegT = (p.NT + p.G - 1) / p.G;
+            d = r.ss / nsegT;
+            r.seg = r.ss - d * nsegT;
+        }
+        r.bh = d * p.H + r.hh;
+    }
+    r.trans = SEG && slice >= NSL;
+    r.v0 = (r.trans ? slice - NSL : slice) * BV;
+    if (p.cu) {
+        const int d = r.bh / p.H;
+        r.NT = __builtin_amdgcn_readfirstlane((p.cu[d + 1] - p.cu[d] + 63) / 64);
+        r.slot0 = __builtin_amdgcn_readfirstlane(varlen_slot(p.cu[d], d, 0));
+    } else {
+        r.NT = p.NT;
+    }
+    r.jbeg = 0; r.jend = r.NT; r.nseg = 1; r.run = true;
+    if (SEG) {
+        r.nseg = (r.NT + p.G - 1) / p.G;
+        // phase 3: every segment; phase 1: all but the chain's first (the
+        // pass's last), transition slices only for the middle ones
+        r.run = OUT ? r.seg < max(r.nseg, 1) : (r.seg > 0 && r.seg < r.nseg && (r.seg < r.nseg - 1 || !r.trans));
+        r.jbeg = r.seg * p.G;
+        r.jend = min(r.NT, r.jbeg + p.G);
+    }
+    return r;
+}
+
 template <int DK, int DV>
 struct RevShape {
     static constexpr int BV = DV < 64 ? DV : 64;
@@ -623,57 +680,16 @@ __global__ void __launch_bounds__(512) bwd_reverse_kernel(BwdParams p, BwdWs W) 
     float* const ems = pCs + DK;
     float* const gCs = ems + DK;
 
-    // work item x slice: value slices, then (phase 1) transition slices
     constexpr int NS = (SEG && !OUT) ? SH::NSL + SH::NTS : SH::NSL;
-    const int item = blockIdx.x / NS, slice = blockIdx.x % NS;
-    const int hh = item % p.H;
-    int bh, seg = 0, ss = 0;   // chain: b H + h, or (varlen) document H + h
-    if (!SEG) {
-        bh = item;
-    } else {
-        ss = item / p.H;
-        int d;
-        if (p.cu) {
-            int lo = 0, hi = p.ndocs - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (seg_slot0(p.cu[mid], mid, p.G) <= ss) lo = mid; else hi = mid - 1;
-            }
-            d = lo;
-            seg = ss - seg_slot0(p.cu[lo], lo, p.G);
-        } else {
-            const int nsegT = (p.NT + p.G - 1) / p.G;
-            d = ss / nsegT;
-            seg = ss - d * nsegT;
-        }
-        bh = d * p.H + hh;
-    }
-    const bool trans = SEG && slice >= SH::NSL;
-    const int v0 = (trans ? slice - SH::NSL : slice) * BV;   // value columns, or columns of P_s
+    const RevWork rw = rev_work<SEG, OUT>(p, SH::NSL, NS, BV);
+    if (!rw.run) return;   // the whole workgroup, before any barrier
+    const int bh = rw.bh, hh = rw.hh, seg = rw.seg, ss = rw.ss, nseg = rw.nseg, v0 = rw.v0, jbeg = rw.jbeg,
+              jend = rw.jend;
+    const bool trans = rw.trans;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63, n = l & 15, g = l >> 4;
-    // the chain's chunks: chunk j is chunk-head chj(j)
-    int NT, slot0 = 0;
-    if (p.cu) {
-        const int d = bh / p.H;
-        NT = __builtin_amdgcn_readfirstlane((p.cu[d + 1] - p.cu[d] + 63) / 64);
-        slot0 = __builtin_amdgcn_readfirstlane(varlen_slot(p.cu[d], d, 0));
-    } else {
-        NT = p.NT;
-    }
-    // the chunks walked, jbeg .. jend - 1 (from the end)
-    int jbeg = 0, jend = NT, nseg = 1;
-    if (SEG) {
-        nseg = (NT + p.G - 1) / p.G;
-        const bool run = OUT ? seg < max(nseg, 1) : (seg > 0 && seg < nseg && (seg < nseg - 1 || !trans));
-        if (!run) return;   // the whole workgroup, before any barrier
-        jbeg = seg * p.G;
-        jend = min(NT, jbeg + p.G);
-    }
-    auto chj = [&](int j) -> size_t {
-        return p.cu ? static_cast<size_t>(slot0 + j) * p.H + hh : static_cast<size_t>(bh) * NT + j;
-    };
+    auto chj = [&](int j) -> size_t { return rw.chj(p, j); };
 
     // ---- register staging ---------------------------------------------------
     f32x4 rM[NM], rT[NM], rKB[NKB], rDO[NDO], rSM;
@@ -896,16 +912,347 @@ __global__ void __launch_bounds__(512) bwd_reverse_kernel(BwdParams p, BwdWs W) 
     }
 }
 
+// ---------------------------------------------------------------------------
+// The reverse pass with bf16 x3 matrix-core arithmetic (bf16 inputs): the
+// recurrence of bwd_reverse_kernel, with every product operand staged once
+// per chunk as bf16 hi and lo planes whose rows run along the product's K
+// (x = hi + lo to about 2^-16 of x) and each 16x16 tile taking hi*hi +
+// hi*lo + lo*hi per 32-wide K step (three 16x16x32 bf16 products instead of
+// eight 16x16x4 fp32 ones).  Operands read transposed (M^T, T^T, Q1^T,
+// -K1^T, and dO as the B side) are staged from column loads: a thread reads
+// 8 consecutive rows of one column, coalesced across the wave.  dSt, dU and
+// Z reach their planes straight from the accumulator layout, and G stays in
+// registers in the accumulator layout of each wave's DK x BV tiles.  Lane
+// (n, g) carries K indices 32 ks + 8g .. +7 in both operands.
+template <int DK, int DV>
+struct RevX3Shape {
+    static constexpr int BV = DV < 64 ? DV : 64;
+    static constexpr int NSL = DV / BV, NTS = (DK + BV - 1) / BV;
+    static constexpr int CT = BV / 16;
+    // bytes per staged row: K hi values, K lo values, 32 bytes of pad (a
+    // pitch of 8 mod 16 dwords keeps the 16-byte fragment reads conflict-free)
+    static constexpr int R64 = 64 * 4 + 32;              // K = 64 (tokens)
+    static constexpr int RDK = DK * 4 + 32;              // K = DK
+    static constexpr int LO64 = 64 * 2, LODK = DK * 2;   // lo plane offsets within a row
+    static constexpr int L_MT = 0;                       // stage 1: M^T, T^T [64][64], KB [64][DK]
+    static constexpr int L_TT = L_MT + 64 * R64;
+    static constexpr int L_KB = L_TT + 64 * R64;
+    static constexpr int S1 = L_KB + 64 * RDK;
+    static constexpr int L_Q1T = 0;                      // stage 2: Q1^T, -K1^T [DK][64]
+    static constexpr int L_K1T = L_Q1T + DK * R64;
+    static constexpr int S2 = L_K1T + DK * R64;
+    static constexpr int L_DOT = S1 > S2 ? S1 : S2;      // dO^T [BV][64]
+    static constexpr int L_GT = L_DOT + BV * R64;        // dSt^T [BV][DK]
+    static constexpr int L_UZ = L_GT + BV * RDK;         // dU^T, then Z^T [BV][64]
+    static constexpr int L_SM = L_UZ + BV * R64;         // pC, em, gC: floats [3][DK]
+    static constexpr int BYTES = L_SM + 3 * DK * 4;
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+    static_assert(R64 % 64 == 32 && RDK % 64 == 32, "row pitch 8 mod 16 dwords");
+    // staging units per thread (512 threads)
+    static constexpr int NUM = 64 * 8, NUDO = BV * 8, NUQ = DK * 8, NUKB = 64 * (DK / 8);
+    static constexpr int UM = (NUM + 511) / 512, UDO = (NUDO + 511) / 512, UQ = (NUQ + 511) / 512,
+                         UKB = (NUKB + 511) / 512;
+    static constexpr int TU = 4 * CT, TPU = TU >= 8 ? TU / 8 : 1;           // 64 x BV tiles per wave
+    static constexpr int TG = (DK / 16) * CT, TPG = TG >= 8 ? TG / 8 : 1;   // DK x BV tiles per wave
+};
+
+// 8 (4) values split into bf16 hi / lo planes of a staged row: hi at p, lo at p + lo_off
+__device__ __forceinline__ void put8_x3(unsigned char* p, int lo_off, const float (&x)[8]) {
+    const SplitPair a = split2(x[0], x[1]), b = split2(x[2], x[3]), c = split2(x[4], x[5]), d = split2(x[6], x[7]);
+    *reinterpret_cast<u32x4*>(p) = u32x4{a.hi, b.hi, c.hi, d.hi};
+    *reinterpret_cast<u32x4*>(p + lo_off) = u32x4{a.lo, b.lo, c.lo, d.lo};
+}
+__device__ __forceinline__ void put4_x3(unsigned char* p, int lo_off, f32x4 x) {
+    const SplitPair a = split2(x[0], x[1]), b = split2(x[2], x[3]);
+    *reinterpret_cast<u32x2*>(p) = u32x2{a.hi, b.hi};
+    *reinterpret_cast<u32x2*>(p + lo_off) = u32x2{a.lo, b.lo};
+}
+// acc += A B over one 32-wide K step, fragments at pa / pb (hi; lo at + lo_off)
+__device__ __forceinline__ f32x4 mma_x3(const unsigned char* pa, int alo, const unsigned char* pb, int blo, f32x4 acc) {
+    const bf16x8 ah = *reinterpret_cast<const bf16x8*>(pa), al = *reinterpret_cast<const bf16x8*>(pa + alo);
+    const bf16x8 bh = *reinterpret_cast<const bf16x8*>(pb), bl = *reinterpret_cast<const bf16x8*>(pb + blo);
+    return mfma32x3(ah, al, bh, bl, acc);
+}
+
 template <int DK, int DV, bool SEG, bool OUT>
-static hipError_t launch_reverse_k(const BwdParams& p, const BwdWs& W, int grid, hipStream_t st) {
-    using SH = RevShape<DK, DV>;
+__global__ void __launch_bounds__(512) bwd_reverse_x3_kernel(BwdParams p, BwdWs W) {
+    using SH = RevX3Shape<DK, DV>;
+    constexpr int BV = SH::BV, CT = SH::CT, R64 = SH::R64, RDK = SH::RDK, LO64 = SH::LO64, LODK = SH::LODK;
+    constexpr int TU = SH::TU, TPU = SH::TPU, TG = SH::TG, TPG = SH::TPG;
+    constexpr int UM = SH::UM, UDO = SH::UDO, UQ = SH::UQ, UKB = SH::UKB;
+    extern __shared__ __align__(16) unsigned char smem[];
+    float* const pCs = reinterpret_cast<float*>(smem + SH::L_SM);
+    float* const ems = pCs + DK;
+    float* const gCs = ems + DK;
+
+    constexpr int NS = (SEG && !OUT) ? SH::NSL + SH::NTS : SH::NSL;
+    const RevWork rw = rev_work<SEG, OUT>(p, SH::NSL, NS, BV);
+    if (!rw.run) return;   // the whole workgroup, before any barrier
+    const int bh = rw.bh, hh = rw.hh, seg = rw.seg, ss = rw.ss, nseg = rw.nseg, v0 = rw.v0, jbeg = rw.jbeg,
+              jend = rw.jend;
+    const bool trans = rw.trans;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63, n = l & 15, g = l >> 4;
+    const int vl0 = trans ? 0 : v0;   // dO columns staged (transition slices zero them)
+
+    // ---- staging (loads into registers, then split into the planes) ----------
+    float rM[UM][8], rT[UM][8], rDO[UDO][8], rQ[UQ][8], rK[UQ][8];
+    f32x4 rKB[UKB][2], rSM;
+    auto load1 = [&](int j) {   // M, T, KB, dO slice, pC / em / gC of chunk j (indices clamped)
+        const size_t ch = rw.chj(p, j);
+        const float* M = W.M + ch * 4096;
+        const float* T = W.T + ch * 4096;
+#pragma unroll
+        for (int u = 0; u < UM; ++u) {
+            const int e = min(tid + 512 * u, SH::NUM - 1), col = e % 64, kb = e / 64;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                rM[u][r] = M[(8 * kb + r) * 64 + col];
+                rT[u][r] = T[(8 * kb + r) * 64 + col];
+            }
+        }
+        const float* dO = W.dO + ch * 64 * DV + vl0;
+#pragma unroll
+        for (int u = 0; u < UDO; ++u) {
+            const int e = min(tid + 512 * u, SH::NUDO - 1), col = e % BV, kb = e / BV;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) rDO[u][r] = dO[static_cast<size_t>(8 * kb + r) * DV + col];
+        }
+        const float* KB = W.KB + ch * 64 * DK;
+#pragma unroll
+        for (int u = 0; u < UKB; ++u) {
+            const int e = min(tid + 512 * u, SH::NUKB - 1), row = e / (DK / 8), cb = e % (DK / 8);
+            rKB[u][0] = *reinterpret_cast<const f32x4*>(KB + row * DK + 8 * cb);
+            rKB[u][1] = *reinterpret_cast<const f32x4*>(KB + row * DK + 8 * cb + 4);
+        }
+        const int us = min(tid, 3 * (DK / 4) - 1), arr = us / (DK / 4), c4 = us % (DK / 4);
+        const float* src = arr == 0 ? W.pC : arr == 1 ? W.em : W.gC;
+        rSM = *reinterpret_cast<const f32x4*>(src + ch * DK + 4 * c4);
+    };
+    auto store1 = [&]() {
+#pragma unroll
+        for (int u = 0; u < UM; ++u) {
+            const int e = tid + 512 * u, col = e % 64, kb = e / 64;
+            if (SH::NUM % 512 == 0 || e < SH::NUM) {
+                put8_x3(smem + SH::L_MT + col * R64 + 16 * kb, LO64, rM[u]);
+                put8_x3(smem + SH::L_TT + col * R64 + 16 * kb, LO64, rT[u]);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UDO; ++u) {
+            const int e = tid + 512 * u, col = e % BV, kb = e / BV;
+            if (SH::NUDO % 512 == 0 || e < SH::NUDO) {
+                float x[8];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) x[r] = trans ? 0.f : rDO[u][r];   // (P_s: dO = 0)
+                put8_x3(smem + SH::L_DOT + col * R64 + 16 * kb, LO64, x);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UKB; ++u) {
+            const int e = tid + 512 * u, row = e / (DK / 8), cb = e % (DK / 8);
+            if (SH::NUKB % 512 == 0 || e < SH::NUKB) {
+                const float x[8] = {rKB[u][0][0], rKB[u][0][1], rKB[u][0][2], rKB[u][0][3],
+                                    rKB[u][1][0], rKB[u][1][1], rKB[u][1][2], rKB[u][1][3]};
+                put8_x3(smem + SH::L_KB + row * RDK + 16 * cb, LODK, x);
+            }
+        }
+        if (tid < 3 * (DK / 4)) *reinterpret_cast<f32x4*>(pCs + 4 * tid) = rSM;
+    };
+    auto load2 = [&](int j) {   // Q1, K1 of chunk j (columns)
+        const size_t ch = rw.chj(p, j);
+        const float* Q1 = W.Q1 + ch * 64 * DK;
+        const float* K1 = W.K1 + ch * 64 * DK;
+#pragma unroll
+        for (int u = 0; u < UQ; ++u) {
+            const int e = min(tid + 512 * u, SH::NUQ - 1), col = e % DK, kb = e / DK;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                rQ[u][r] = Q1[(8 * kb + r) * DK + col];
+                rK[u][r] = K1[(8 * kb + r) * DK + col];
+            }
+        }
+    };
+    auto store2 = [&]() {
+#pragma unroll
+        for (int u = 0; u < UQ; ++u) {
+            const int e = tid + 512 * u, col = e % DK, kb = e / DK;
+            if (SH::NUQ % 512 == 0 || e < SH::NUQ) {
+                float nk[8];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) nk[r] = -rK[u][r];
+                put8_x3(smem + SH::L_Q1T + col * R64 + 16 * kb, LO64, rQ[u]);
+                put8_x3(smem + SH::L_K1T + col * R64 + 16 * kb, LO64, nk);
+            }
+        }
+    };
+
+    // ---- tiles of this wave -------------------------------------------------
+    const bool actU = w * TPU < TU, actG = w * TPG < TG;
+    int uti[TPU], utj[TPU], gti[TPG], gtj[TPG];
+#pragma unroll
+    for (int u = 0; u < TPU; ++u) { uti[u] = (w * TPU + u) / CT; utj[u] = (w * TPU + u) % CT; }
+#pragma unroll
+    for (int u = 0; u < TPG; ++u) { gti[u] = (w * TPG + u) / CT; gtj[u] = (w * TPG + u) % CT; }
+
+    // G at the pass's start: dht (or 0) at the chain's end; segmented: the
+    // identity for transition slices, zero for the middle segments of phase
+    // 1, the scanned start in phase 3.  Lane (n, g) of tile u holds rows
+    // 16 gti + 4g + i, column 16 gtj + n.
+    const float* gsrc = p.dht ? p.dht + static_cast<size_t>(bh) * DK * DV : nullptr;
+    if (SEG && seg < nseg - 1) gsrc = OUT ? p.seg_start + (static_cast<size_t>(ss) * p.H + hh) * DK * DV : nullptr;
+    f32x4 Gr[TPG];
+#pragma unroll
+    for (int u = 0; u < TPG; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = 16 * gti[u] + 4 * g + i, v = 16 * gtj[u] + n;
+            Gr[u][i] = !actG ? 0.f
+                     : trans ? (c == v0 + v ? 1.f : 0.f)
+                             : (gsrc ? gsrc[static_cast<size_t>(c) * DV + v0 + v] : 0.f);
+        }
+
+    if (jend > jbeg) {   // (an empty document has no chunks: dh0 = dht)
+        load1(jend - 1);
+        store1();
+    }
+    __syncthreads();
+    for (int j = jend - 1; j >= jbeg; --j) {
+        const size_t ch = rw.chj(p, j);
+        load2(j);
+        // dSt = Diag(pC) G: planes for the dU product, fp32 to the workspace
+        if (actG) {
+#pragma unroll
+            for (int u = 0; u < TPG; ++u) {
+                const int c0 = 16 * gti[u] + 4 * g, v = 16 * gtj[u] + n;
+                const f32x4 ds = *reinterpret_cast<const f32x4*>(pCs + c0) * Gr[u];
+                put4_x3(smem + SH::L_GT + v * RDK + 2 * c0, LODK, ds);
+                if (OUT) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) W.dSt[ch * DK * DV + static_cast<size_t>(c0 + i) * DV + v0 + v] = ds[i];
+                }
+            }
+        }
+        __syncthreads();
+        // dU = M^T dO + KB dSt (64 x BV)
+        f32x4 ua[TPU];
+        if (actU) {
+#pragma unroll
+            for (int u = 0; u < TPU; ++u) {
+                ua[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const unsigned char* am = smem + SH::L_MT + (16 * uti[u] + n) * R64 + 16 * g;
+                const unsigned char* bo = smem + SH::L_DOT + (16 * utj[u] + n) * R64 + 16 * g;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) ua[u] = mma_x3(am + 64 * ks, LO64, bo + 64 * ks, LO64, ua[u]);
+                const unsigned char* ak = smem + SH::L_KB + (16 * uti[u] + n) * RDK + 16 * g;
+                const unsigned char* bg = smem + SH::L_GT + (16 * utj[u] + n) * RDK + 16 * g;
+#pragma unroll
+                for (int ks = 0; ks < DK / 32; ++ks) ua[u] = mma_x3(ak + 64 * ks, LODK, bg + 64 * ks, LODK, ua[u]);
+            }
+            // dU^T planes (for Z), fp32 to the workspace
+#pragma unroll
+            for (int u = 0; u < TPU; ++u) {
+                const int k0 = 16 * uti[u] + 4 * g, v = 16 * utj[u] + n;
+                put4_x3(smem + SH::L_UZ + v * R64 + 2 * k0, LO64, ua[u]);
+                if (OUT) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) W.dU[ch * 64 * DV + static_cast<size_t>(k0 + i) * DV + v0 + v] = ua[u][i];
+                }
+            }
+        }
+        __syncthreads();
+        // Z = T^T dU
+        f32x4 za[TPU];
+        if (actU) {
+#pragma unroll
+            for (int u = 0; u < TPU; ++u) {
+                za[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const unsigned char* at = smem + SH::L_TT + (16 * uti[u] + n) * R64 + 16 * g;
+                const unsigned char* bu = smem + SH::L_UZ + (16 * utj[u] + n) * R64 + 16 * g;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) za[u] = mma_x3(at + 64 * ks, LO64, bu + 64 * ks, LO64, za[u]);
+            }
+        }
+        __syncthreads();   // dU^T, M^T, T^T, KB consumed
+        // Z^T planes; stage 2 (Q1^T, -K1^T) over stage 1; the next chunk's stage-1 loads go out
+        if (actU) {
+#pragma unroll
+            for (int u = 0; u < TPU; ++u) {
+                const int k0 = 16 * uti[u] + 4 * g, v = 16 * utj[u] + n;
+                put4_x3(smem + SH::L_UZ + v * R64 + 2 * k0, LO64, za[u]);
+            }
+        }
+        store2();
+        load1(j > jbeg ? j - 1 : jbeg);
+        __syncthreads();
+        // G <- Diag(e^m) (Q1^T dO - K1^T Z) + Diag(e^{b_L} pC) G
+        if (actG) {
+#pragma unroll
+            for (int u = 0; u < TPG; ++u) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                const unsigned char* aq = smem + SH::L_Q1T + (16 * gti[u] + n) * R64 + 16 * g;
+                const unsigned char* ak = smem + SH::L_K1T + (16 * gti[u] + n) * R64 + 16 * g;
+                const unsigned char* bo = smem + SH::L_DOT + (16 * gtj[u] + n) * R64 + 16 * g;
+                const unsigned char* bz = smem + SH::L_UZ + (16 * gtj[u] + n) * R64 + 16 * g;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    acc = mma_x3(aq + 64 * ks, LO64, bo + 64 * ks, LO64, acc);
+                    acc = mma_x3(ak + 64 * ks, LO64, bz + 64 * ks, LO64, acc);
+                }
+                const int c0 = 16 * gti[u] + 4 * g;
+                const f32x4 em4 = *reinterpret_cast<const f32x4*>(ems + c0);
+                const f32x4 gc4 = *reinterpret_cast<const f32x4*>(gCs + c0);
+                const f32x4 pc4 = *reinterpret_cast<const f32x4*>(pCs + c0);
+                Gr[u] = em4 * acc + gc4 * pc4 * Gr[u];
+            }
+        }
+        __syncthreads();   // Q1^T, K1^T, dO^T, Z^T, pC / em / gC consumed
+        store1();   // chunk j - 1 (on the last chunk walked: that chunk again, unused)
+        __syncthreads();
+    }
+    // the end state: dh0 (whole chains; phase 3, the chain's first segment),
+    // or in phase 1 the start of the next segment in pass order (the chain's
+    // last segment), H_s or P_s (middle segments)
+    float* dst = p.dh0 ? p.dh0 + static_cast<size_t>(bh) * DK * DV : nullptr;
+    int pitch = DV, ncol = BV;
+    if (SEG && !OUT) {
+        if (seg == nseg - 1) {
+            dst = p.seg_start + (static_cast<size_t>(ss - 1) * p.H + hh) * DK * DV;
+        } else if (trans) {
+            dst = p.seg_p + (static_cast<size_t>(ss) * p.H + hh) * DK * DK;
+            pitch = DK;
+            ncol = min(BV, DK - v0);   // (columns of P_s past DK do not exist)
+        } else {
+            dst = p.seg_h + (static_cast<size_t>(ss) * p.H + hh) * DK * DV;
+        }
+    } else if (SEG && seg > 0) {
+        dst = nullptr;
+    }
+    if (dst && actG) {
+#pragma unroll
+        for (int u = 0; u < TPG; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = 16 * gti[u] + 4 * g + i, v = 16 * gtj[u] + n;
+                if (v < ncol) dst[static_cast<size_t>(c) * pitch + v0 + v] = Gr[u][i];
+            }
+    }
+}
+
+// X3: the bf16 x3 variant (bf16 inputs), else fp32 matrix cores
+template <int DK, int DV, bool SEG, bool OUT>
+static hipError_t launch_reverse_k(const BwdParams& p, const BwdWs& W, int grid, bool x3, hipStream_t st) {
     if (grid == 0) return hipSuccess;
-    auto kern = bwd_reverse_kernel<DK, DV, SEG, OUT>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, SH::BYTES);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(512), SH::BYTES, st, p, W);
-    return hipGetLastError();
+    auto go = [&](auto kern, int bytes) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(512), bytes, st, p, W);
+        return hipGetLastError();
+    };
+    if (x3) return go(bwd_reverse_x3_kernel<DK, DV, SEG, OUT>, RevX3Shape<DK, DV>::BYTES);
+    return go(bwd_reverse_kernel<DK, DV, SEG, OUT>, RevShape<DK, DV>::BYTES);
 }
 
 // measured on MI355X (dk = dv = 128): a lone chain's reverse step is the
@@ -917,22 +1264,22 @@ constexpr SegCost kReverseCost{0.88, 0.9, 0.5};
 // the reverse pass over every chain: whole chains, or segments (p.G > 0,
 // buffers set) in three launches
 template <int DK, int DV>
-static hipError_t launch_reverse_t(const BwdParams& p, const BwdWs& W, hipStream_t st) {
+static hipError_t launch_reverse_t(const BwdParams& p, const BwdWs& W, bool x3, hipStream_t st) {
     using SH = RevShape<DK, DV>;
     const int nchains = (p.cu ? p.ndocs : p.B) * p.H;
-    if (p.G == 0) return launch_reverse_k<DK, DV, false, true>(p, W, nchains * SH::NSL, st);
-    hipError_t e = launch_reverse_k<DK, DV, true, false>(p, W, p.nsslots * p.H * (SH::NSL + SH::NTS), st);
+    if (p.G == 0) return launch_reverse_k<DK, DV, false, true>(p, W, nchains * SH::NSL, x3, st);
+    hipError_t e = launch_reverse_k<DK, DV, true, false>(p, W, p.nsslots * p.H * (SH::NSL + SH::NTS), x3, st);
     if (e != hipSuccess) return e;
     const SegScanParams sp{p.cu, p.T, p.H, p.G, p.seg_start, p.seg_h, p.seg_p, 1};
     hipLaunchKernelGGL((ckda_seg_scan_kernel<DK, DV>), dim3(nchains * (DV / kScanCols)), dim3(256), 0, st, sp);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_reverse_k<DK, DV, true, true>(p, W, p.nsslots * p.H * SH::NSL, st);
+    return launch_reverse_k<DK, DV, true, true>(p, W, p.nsslots * p.H * SH::NSL, x3, st);
 }
 
-static hipError_t launch_reverse(const BwdParams& p, const BwdWs& W, hipStream_t st) {
+static hipError_t launch_reverse(const BwdParams& p, const BwdWs& W, bool x3, hipStream_t st) {
 #define CKDA_REV(DK_, DV_) \
-    if (W.DK == DK_ && W.DV == DV_) return launch_reverse_t<DK_, DV_>(p, W, st);
+    if (W.DK == DK_ && W.DV == DV_) return launch_reverse_t<DK_, DV_>(p, W, x3, st);
     CKDA_REV(32, 32) CKDA_REV(32, 64) CKDA_REV(32, 128)
     CKDA_REV(64, 32) CKDA_REV(64, 64) CKDA_REV(64, 128)
     CKDA_REV(128, 32) CKDA_REV(128, 64) CKDA_REV(128, 128)
@@ -1262,7 +1609,7 @@ hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t st) {
     CKDA_CHECK(gemm(mk(64, DV, DK, W.K1, DK, s64k, false, W.Sp, DV, skv, false, W.R, DV, s64v, -1.f, W.V, 1.f), NC, st));
     CKDA_CHECK(gemm(mk(64, DV, 64, W.T, 64, s44, false, W.R, DV, s64v, false, W.U, DV, s64v), NC, st));
     // reverse recurrence: dSt, dU per chunk, dh0
-    CKDA_CHECK(launch_reverse(p, W, st));
+    CKDA_CHECK(launch_reverse(p, W, a.bf16, st));
     // chunk-parallel gradients
     CKDA_CHECK(gemm(mk(64, 64, DV, W.dO, DV, s64v, false, W.U, DV, s64v, true, W.dM, 64, s44, 1.f, nullptr, 0.f, 2), NC, st));
     CKDA_CHECK(gemm(mk(64, DK, DV, W.U, DV, s64v, false, W.dSt, DV, skv, true, W.dKB, DK, s64k), NC, st));
