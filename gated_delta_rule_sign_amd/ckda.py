@@ -276,7 +276,9 @@ def bwd_workspace_bytes(B, T, H, DK, DV) -> int:
 
 def bwd(q, k, v, g, s, beta, h_ckpt, do, scale: float = 1.0, h0=None, dht=None,
         want_dh0: bool = True, workspace=None, qk_norm: bool = False):
-    """Backward (ckda_bwd).  Returns dict dq, dk, dv, dg, dbeta, dh0 (f32)."""
+    """Backward (ckda_bwd).  h_ckpt: the checkpoints of fwd(..., want_ckpt=True)
+    on the same inputs, or None (the call recomputes them).  Returns dict dq,
+    dk, dv, dg, dbeta, dh0 (f32)."""
     B, T = q.shape[0], q.shape[1]
     dt, H, DK, DV, dev = _token_inputs(q, k, v, g, s, beta, (B, T))
     NT = (T + CHUNK - 1) // CHUNK
@@ -308,7 +310,8 @@ def bwd_varlen_workspace_bytes(N, T_total, H, DK, DV) -> int:
 def bwd_varlen(q, k, v, g, s, beta, cu_seqlens, h_ckpt, do, scale: float = 1.0, h0=None, dht=None,
                want_dh0: bool = True, cu_seqlens_dev=None, workspace=None, qk_norm: bool = False):
     """Backward of the packed-document forward (ckda_bwd_varlen).  Shapes as
-    in fwd_varlen; h_ckpt from fwd_varlen(..., want_ckpt=True); do
+    in fwd_varlen; h_ckpt from fwd_varlen(..., want_ckpt=True), or None
+    (recomputed); do
     [T_total,H,DV]; dht, dh0 [N,H,DK,DV].  Returns dict dq, dk, dv, dg,
     dbeta, dh0 (f32)."""
     if q.dim() == 4:

@@ -269,18 +269,22 @@ ckda_status_t bwd_common(ckda::BwdArgs& a, int nslots, bool any_tokens, const vo
                          size_t workspace_bytes, ckda_stream_t stream, const char* what) {
     if (any_tokens) {
         CKDA_REQUIRE(a.q); CKDA_REQUIRE(a.k); CKDA_REQUIRE(a.v); CKDA_REQUIRE(a.g); CKDA_REQUIRE(a.s);
-        CKDA_REQUIRE(a.beta); CKDA_REQUIRE(a.h_ckpt); CKDA_REQUIRE(a.dout);
+        CKDA_REQUIRE(a.beta); CKDA_REQUIRE(a.dout);
         CKDA_REQUIRE(a.dq); CKDA_REQUIRE(a.dk); CKDA_REQUIRE(a.dv); CKDA_REQUIRE(a.dg); CKDA_REQUIRE(a.dbeta);
     }
     CKDA_ALIGNED(a.q); CKDA_ALIGNED(a.k); CKDA_ALIGNED(a.v); CKDA_ALIGNED(a.g); CKDA_ALIGNED(a.s);
     CKDA_ALIGNED(a.dout); CKDA_ALIGNED(a.h_ckpt);
     CKDA_ALIGNED(a.dq); CKDA_ALIGNED(a.dk); CKDA_ALIGNED(a.dv); CKDA_ALIGNED(a.dg);
-    const size_t need = ckda::bwd_workspace_bytes(nslots, a.H, a.DK, a.DV);
+    // h_ckpt nullptr: checkpoints recomputed into the workspace, after the blocks
+    size_t need = ckda::bwd_workspace_bytes(nslots, a.H, a.DK, a.DV);
+    const bool recompute = any_tokens && !a.h_ckpt;
+    if (recompute) need = ((need + 255) & ~static_cast<size_t>(255)) + ckda::bwd_ckpt_bytes(nslots, a.H, a.DK, a.DV);
     if (need > 0) {
         CKDA_REQUIRE(workspace);
         CKDA_ALIGNED(workspace);
         if (workspace_bytes < need)
-            return fail(CKDA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+            return fail(CKDA_ERR_WORKSPACE, "workspace %zu bytes, need %zu%s", workspace_bytes, need,
+                        recompute ? " (checkpoints recomputed)" : "");
     }
     a.ws = const_cast<void*>(workspace);
     a.ws_bytes = workspace_bytes;

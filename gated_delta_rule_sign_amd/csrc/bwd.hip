@@ -1550,8 +1550,15 @@ size_t bwd_workspace_bytes(int nslots, int H, int DK, int DV) {
     return BwdWs::floats(static_cast<size_t>(nslots) * H, DK, DV) * sizeof(float);
 }
 
+// checkpoints recomputed in the call (h_ckpt = nullptr): [nslots][H][DK][DV]
+size_t bwd_ckpt_bytes(int nslots, int H, int DK, int DV) {
+    return static_cast<size_t>(nslots) * H * DK * DV * sizeof(float);
+}
+
+// layout: per-chunk-head blocks | recomputed checkpoints | segment buffers
 size_t bwd_workspace_bytes_full(int nslots, int nsslots_max, int H, int DK, int DV) {
-    return align256(bwd_workspace_bytes(nslots, H, DK, DV)) + seg_buffer_bytes(nsslots_max, H, DK, DV);
+    return align256(bwd_workspace_bytes(nslots, H, DK, DV)) + align256(bwd_ckpt_bytes(nslots, H, DK, DV)) +
+           seg_buffer_bytes(nsslots_max, H, DK, DV);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t st) {
@@ -1565,10 +1572,11 @@ hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t st) {
     p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dg = a.dg; p.dbeta = a.dbeta; p.dh0 = a.dh0;
     p.B = a.B; p.T = a.T; p.H = a.H; p.NT = NT; p.cu = a.cu; p.ndocs = a.ndocs; p.head_gate = a.head_gate;
     p.qk_norm = a.qk_norm;
+    const size_t blocks = bwd_workspace_bytes(nslots, a.H, DK, DV);
+    const size_t seg_off = align256(blocks) + align256(bwd_ckpt_bytes(nslots, a.H, DK, DV));
     {   // segmented reverse pass when the plan takes it and the workspace has room
         const bool varlen = a.cu != nullptr;
-        const size_t base = bwd_workspace_bytes(nslots, a.H, DK, DV);
-        const size_t avail = a.ws_bytes > align256(base) ? a.ws_bytes - align256(base) : 0;
+        const size_t avail = a.ws_bytes > seg_off ? a.ws_bytes - seg_off : 0;
         auto fits = [&](int G) {
             return seg_buffer_bytes(seg_slots(varlen, a.B, a.T, a.ndocs, G), a.H, DK, DV) <= avail;
         };
@@ -1577,7 +1585,7 @@ hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t st) {
                             (DK + BVr - 1) / BVr, kReverseCost, fits);
         if (p.G > 0) {
             p.nsslots = seg_slots(varlen, a.B, a.T, a.ndocs, p.G);
-            float* sb = reinterpret_cast<float*>(static_cast<unsigned char*>(a.ws) + align256(base));
+            float* sb = reinterpret_cast<float*>(static_cast<unsigned char*>(a.ws) + seg_off);
             const size_t per = static_cast<size_t>(p.nsslots) * a.H * DK * DV;
             p.seg_start = sb;
             p.seg_h = sb + per;
@@ -1598,6 +1606,23 @@ hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t st) {
     W.carve(static_cast<float*>(a.ws), NC, DK, DV);
     hipError_t e;
 #define CKDA_CHECK(x) do { e = (x); if (e != hipSuccess) return e; } while (0)
+    if (!a.h_ckpt) {
+        // checkpoints recomputed: a forward pass whose chunk records sit in the
+        // blocks' first regions (K1 .. dV), whose outputs go to the S' / dSt
+        // regions (both free until the prep runs) and whose checkpoints go to
+        // their own area after the blocks; records-only room keeps its state
+        // pass on whole chains
+        FwdArgs f{};
+        f.B = a.B; f.T = a.T; f.H = a.H; f.DK = DK; f.DV = DV; f.bf16 = a.bf16;
+        f.head_gate = a.head_gate; f.qk_norm = a.qk_norm;
+        f.q = a.q; f.k = a.k; f.v = a.v; f.g = a.g; f.s = a.s; f.beta = a.beta; f.scale = a.scale;
+        f.h0 = a.h0; f.o = W.Sp; f.ht = nullptr;
+        f.h_ckpt = reinterpret_cast<float*>(static_cast<unsigned char*>(a.ws) + align256(blocks));
+        f.cu = a.cu; f.cu_host = a.cu_host; f.ndocs = a.ndocs;
+        f.ws = a.ws; f.ws_bytes = fwd_workspace_bytes(nslots, a.H, DK, DV, a.bf16);
+        CKDA_CHECK(launch_fwd(f, nslots, st));
+        p.h_ckpt = f.h_ckpt;
+    }
     CKDA_CHECK(launch_chunk_pass(a.bf16, false, p, W, NC, st));
     const long long s64k = 64LL * DK, s64v = 64LL * DV, skv = 1LL * DK * DV, s44 = 4096;
     // A = strict_lower(K1 K2^T), M = lower(Q1 K2^T)

@@ -82,7 +82,7 @@ struct BwdArgs {
     const float* beta;
     float scale;
     const float* h0;
-    const float* h_ckpt;
+    const float* h_ckpt;   // nullptr: recomputed in the call
     const void* dout;
     const float* dht;
     float *dq, *dk, *dv, *dg, *dbeta, *dh0;
@@ -96,7 +96,10 @@ struct BwdArgs {
 };
 // nslots: chunk slots, as for the forward; the minimum workspace
 size_t bwd_workspace_bytes(int nslots, int H, int DK, int DV);
-// plus the segment buffers for up to nsslots_max segment slots
+// checkpoints recomputed in the call when h_ckpt is nullptr
+size_t bwd_ckpt_bytes(int nslots, int H, int DK, int DV);
+// blocks, then room for recomputed checkpoints, then the segment buffers for
+// up to nsslots_max segment slots
 size_t bwd_workspace_bytes_full(int nslots, int nsslots_max, int H, int DK, int DV);
 hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t stream);
 

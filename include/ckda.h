@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define CKDA_ABI_VERSION 6
+#define CKDA_ABI_VERSION 7
 
 typedef enum {
     CKDA_OK = 0,
@@ -205,17 +205,19 @@ ckda_status_t ckda_decode_step(int N, int H, int DK, int DV, ckda_dtype_t in_dty
  * Backward of the chunked forward: gradients of L = <do, o> + <dht, ht>.
  *   inputs as in ckda_fwd_chunked; h0 nullable (zero)
  *   h_ckpt: [B,H,NT,DK,DV] f32 written by ckda_fwd_chunked on the same
- *           inputs (required)
+ *           inputs, or NULL: the call then recomputes the checkpoints with
+ *           one more forward pass (whole chains) into its workspace
  *   dout: [B,T,H,DV] in_dtype;  dht: [B,H,DK,DV] f32 or NULL (zero)
  *   dq, dk, dg: [B,T,H,DK] f32;  dv: [B,T,H,DV] f32;  dbeta: [B,T,H] f32
  *   (flags & CKDA_GATE_HEAD: g, s and dg are [B,T,H]; dg is then the sum
  *   over channels of the channel-gate gradient)
  *   dh0: [B,H,DK,DV] f32 or NULL
  *   workspace: ckda_bwd_workspace_bytes(...) bytes of device memory: the
- *           per-(chunk, head) blocks of the chunk-parallel passes, then the
- *           segment buffers of the reverse pass (see ckda_set_segment_chunks;
- *           a workspace with only the blocks is accepted and keeps whole
- *           chains)
+ *           per-(chunk, head) blocks of the chunk-parallel passes, room for
+ *           recomputed checkpoints, then the segment buffers of the reverse
+ *           pass (see ckda_set_segment_chunks).  Less is accepted down to the
+ *           blocks (plus the checkpoint room when h_ckpt is NULL); the
+ *           reverse pass then walks whole chains.
  * dg is the gradient w.r.t. g = log|alpha| (alpha * dL/dalpha); s gets none.
  * ---------------------------------------------------------------------- */
 size_t ckda_bwd_workspace_bytes(int B, int T, int H, int DK, int DV);
@@ -231,7 +233,7 @@ ckda_status_t ckda_bwd(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtyp
  * <do, o> + <dht[n], ht[n]> with documents as independent sequences.
  *   cu_seqlens_host / _dev, q .. beta, scale: as in ckda_fwd_varlen
  *   h_ckpt: the per-chunk-slot checkpoints ckda_fwd_varlen wrote on the same
- *           inputs (required when T_total > 0)
+ *           inputs, or NULL (recomputed, as in ckda_bwd)
  *   dout: [T_total,H,DV] in_dtype;  dht: [N,H,DK,DV] f32 or NULL (zero)
  *   dq, dk, dg: [T_total,H,DK] f32;  dv: [T_total,H,DV];  dbeta: [T_total,H]
  *   (flags & CKDA_GATE_HEAD: g, s, dg [T_total,H])

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.ckda_abi_version() == 6
+    assert L.ckda_abi_version() == 7
     assert L.ckda_status_string(0) == b"ok"
     for st in range(1, 8):
         assert L.ckda_status_string(st) not in (b"ok", b"unknown status")
@@ -135,18 +135,21 @@ def test_varlen_backward_boundary(L):
     assert L.ckda_varlen_chunk_slots(-1, 100) == 0
     # one backward workspace block per (chunk slot, head), then the segment
     # buffers of the reverse pass (segments of 16 chunks)
+    # then room for recomputed checkpoints (one DK x DV state per block)
     one = bwd_block_bytes(64, 32)
-    assert L.ckda_bwd_workspace_bytes(1, 64, 1, 64, 32) == align256(one) + seg_bytes(1, 1, 64, 32)
+    assert L.ckda_bwd_workspace_bytes(1, 64, 1, 64, 32) == \
+        align256(one) + align256(64 * 32 * 4) + seg_bytes(1, 1, 64, 32)
     assert L.ckda_bwd_varlen_workspace_bytes(3, 100, 2, 64, 32) == \
-        align256((2 + 3) * 2 * one) + seg_bytes(1 + 3, 2, 64, 32)
+        align256((2 + 3) * 2 * one) + align256((2 + 3) * 2 * 64 * 32 * 4) + seg_bytes(1 + 3, 2, 64, 32)
     assert L.ckda_bwd_varlen_workspace_bytes(3, 100, 2, 48, 32) == 0
     assert bwd_varlen(L, [1, 5], 1, 5) == 5                       # does not start at 0
     assert bwd_varlen(L, [0, 5, 3], 2, 3) == 5                    # decreasing
     assert bwd_varlen(L, None, 2, 4) == 1
     assert bwd_varlen(L, [0, 5], 1, 5, DK=96) == 4
     assert bwd_varlen(L, [0, 5], 1, 5, dt=9) == 3
-    assert bwd_varlen(L, [0, 5], 1, 5, hc=None) == 1              # checkpoints required
-    assert b"h_ckpt" in L.ckda_last_error()
+    # no checkpoints: recomputed, which needs room for them beyond the blocks
+    assert bwd_varlen(L, [0, 5], 1, 5, hc=None, wsb=2 * bwd_block_bytes(32, 32)) == 6
+    assert b"recomputed" in L.ckda_last_error()
     assert bwd_varlen(L, [0, 5], 1, 5, q=P(0x1004)) == 4          # misaligned
     # below the per-chunk blocks (2 chunk slots) the call fails before any launch
     assert bwd_varlen(L, [0, 5], 1, 5, wsb=2 * bwd_block_bytes(32, 32) - 16) == 6

@@ -78,3 +78,40 @@ def test_layer_bwd_sampled():
         e = rel_max(g, ref[name])
         print(f"  layer_bwd {name}: {e:.2e}")
         assert e < TOL["bf16"], (name, e)
+
+
+@pytest.mark.parametrize("dtype,DK,DV", [("f32", 64, 64), ("bf16", 128, 128)])
+def test_backward_recomputes_checkpoints(dtype, DK, DV):
+    """h_ckpt = None: the backward runs the forward itself for the chunk
+    checkpoints; with the same (whole-chain) forward the gradients equal those
+    from the caller's checkpoints, equal-length and varlen."""
+    torch = require_gpu()
+    from gated_delta_rule_sign_amd import ckda
+    import torch as T_
+    banner(f"bwd recomputed checkpoints {dtype} DK={DK} DV={DV}")
+    w = I.make_forward(2, 150, 2, DK, DV, dtype, seed=61, h0_std=0.3)
+    rng = np.random.default_rng(62)
+    do = dev_tensor(I.to_storage(rng.standard_normal((2, 150, 2, DV)), dtype))
+    d = tok_to_dev(w.tok)
+    h0 = dev_tensor(w.h0)
+    try:
+        ckda.set_segment_chunks(-1)
+        _, _, hc = ckda.fwd(**d, h0=h0, want_ckpt=True)
+        r1 = ckda.bwd(**d, h_ckpt=hc, do=do, h0=h0)
+        r2 = ckda.bwd(**d, h_ckpt=None, do=do, h0=h0)
+        lens = [0, 130, 1, 170]
+        cu = I.cu_from_lengths(lens)
+        Tt = int(cu[-1])
+        tok = I.draw_tokens(rng, (Tt,), 2, DK, DV, dtype)
+        dv_ = tok_to_dev(tok)
+        dov = dev_tensor(I.to_storage(rng.standard_normal((Tt, 2, DV)), dtype))
+        cu_t = T_.from_numpy(cu)
+        _, _, hcv = ckda.fwd_varlen(**dv_, cu_seqlens=cu_t, want_ckpt=True)
+        v1 = ckda.bwd_varlen(**dv_, cu_seqlens=cu_t, h_ckpt=hcv, do=dov)
+        v2 = ckda.bwd_varlen(**dv_, cu_seqlens=cu_t, h_ckpt=None, do=dov)
+    finally:
+        ckda.set_segment_chunks(0)
+    torch.cuda.synchronize()
+    for name in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        assert np.array_equal(host(r1[name]), host(r2[name])), name
+        assert np.array_equal(host(v1[name]), host(v2[name])), name
