@@ -49,7 +49,7 @@ struct BwdWs {
     // [NC][64][DV]
     float *V, *dO, *R, *U, *dU, *dV;
     // [NC][DK][DV]
-    float *Sp, *dSt;
+    float* dSt;
     // [NC][64][64]
     float *A, *M, *Xi, *T, *dM, *dT, *Y1, *Tmp, *dX, *dA;
     // [NC][DK]
@@ -58,7 +58,7 @@ struct BwdWs {
     float *beta, *dbeta1, *dbeta2;
 
     __host__ __device__ static size_t floats(size_t NC, int DK, int DV) {
-        return NC * (9ull * 64 * DK + 6ull * 64 * DV + 2ull * DK * DV + 10ull * 64 * 64 + 3ull * DK + 3ull * 64);
+        return NC * (9ull * 64 * DK + 6ull * 64 * DV + 1ull * DK * DV + 10ull * 64 * 64 + 3ull * DK + 3ull * 64);
     }
     __host__ void carve(float* p, int nc, int dk, int dv) {
         NC = nc; DK = dk; DV = dv; base = p;
@@ -69,7 +69,7 @@ struct BwdWs {
         dK1 = take(n * 64 * dk); dK2 = take(n * 64 * dk); dQ1 = take(n * 64 * dk);
         V = take(n * 64 * dv); dO = take(n * 64 * dv); R = take(n * 64 * dv); U = take(n * 64 * dv);
         dU = take(n * 64 * dv); dV = take(n * 64 * dv);
-        Sp = take(n * dk * dv); dSt = take(n * dk * dv);
+        dSt = take(n * dk * dv);
         A = take(n * 4096); M = take(n * 4096); Xi = take(n * 4096); T = take(n * 4096); dM = take(n * 4096);
         dT = take(n * 4096); Y1 = take(n * 4096); Tmp = take(n * 4096); dX = take(n * 4096); dA = take(n * 4096);
         em = take(n * dk); gC = take(n * dk); pC = take(n * dk);
@@ -90,6 +90,10 @@ struct Gemm {
     const float* D; long long sD; int dr;
     float alpha, beta;
     int mask;
+    // optional scale of B's stored rows (row r of the stored matrix times
+    // bs[z * sBs + r]: Diag(bs) B for B read as stored, B Diag(bs) for B
+    // read transposed), applied while the slab is staged
+    const float* bs; long long sBs;
 };
 
 // One workgroup per batch element: C (64 x N) = A (64 x K) B (K x N), N, K in
@@ -142,18 +146,28 @@ __device__ __forceinline__ void bgemm_accumulate(const Gemm& p, long long z, flo
         }
     };
     f32x4 ra[2], rb[NB];
+    float rs[NB];
+    const float* bs = p.bs ? p.bs + z * p.sBs : nullptr;
+    // stored row of B unit e: j (B read transposed) or k (as stored)
+    auto b_row = [&](int e, int k0) -> int {
+        if constexpr (bT) return e / 8;
+        else return k0 + (e % (32 * BW / 4)) / (BW / 4);
+    };
     auto load = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) ra[i] = *reinterpret_cast<const f32x4*>(a_src(tid + 256 * i, k0));
 #pragma unroll
-        for (int i = 0; i < NB; ++i) rb[i] = *reinterpret_cast<const f32x4*>(b_src(tid + 256 * i, k0));
+        for (int i = 0; i < NB; ++i) {
+            rb[i] = *reinterpret_cast<const f32x4*>(b_src(tid + 256 * i, k0));
+            rs[i] = bs ? bs[b_row(tid + 256 * i, k0)] : 1.f;
+        }
     };
     load(0);
     for (int k0 = 0; k0 < p.K; k0 += kKS) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) *reinterpret_cast<f32x4*>(a_dst(tid + 256 * i)) = ra[i];
 #pragma unroll
-        for (int i = 0; i < NB; ++i) *reinterpret_cast<f32x4*>(b_dst(tid + 256 * i)) = rb[i];
+        for (int i = 0; i < NB; ++i) *reinterpret_cast<f32x4*>(b_dst(tid + 256 * i)) = rs[i] * rb[i];
         __syncthreads();
         if (k0 + kKS < p.K) load(k0 + kKS);
 #pragma unroll 2
@@ -377,16 +391,12 @@ __device__ __forceinline__ f32x4 exp2c4(f32x4 x) {
 }
 
 // prep: cumulative gate and sign product, anchored operands, V / dO copies
-// and S' = Diag(e^m) S
 template <typename Tin, int DK, int DV, bool HG, bool NQK>
 __global__ void __launch_bounds__(512) bwd_prep_kernel(BwdParams p, BwdWs W) {
     using QS = QuadSeg<DK, 512>;
     using QV = QuadSeg<DV, 512>;
     constexpr int CQ = QS::CQ, SEGS = QS::SEGS, NTOK = QS::NTOK;
-    constexpr int S4 = DK * DV / 4;                 // float4 of the chunk-start state
-    constexpr int NS4 = (S4 + 511) / 512;           // per thread
     __shared__ f32x4 segb[SEGS][CQ], segp[SEGS][CQ];
-    __shared__ __align__(16) float em_s[DK];
     const int ch = blockIdx.x;
     const ChunkIdx ci(ch, p);
     const int tid = threadIdx.x, q4 = tid % CQ, seg = tid / CQ, tb = seg * NTOK;
@@ -405,7 +415,6 @@ __global__ void __launch_bounds__(512) bwd_prep_kernel(BwdParams p, BwdWs W) {
             reinterpret_cast<f32x4*>(W.V + o64v)[u] = z;
             reinterpret_cast<f32x4*>(W.dO + o64v)[u] = z;
         }
-        for (int u = tid; u < DK * DV / 4; u += 512) reinterpret_cast<f32x4*>(W.Sp + static_cast<size_t>(ch) * DK * DV)[u] = z;
         if (tid < 64) W.beta[static_cast<size_t>(ch) * 64 + tid] = 0.f;
         if (tid < DK) {
             W.em[static_cast<size_t>(ch) * DK + tid] = 1.f;
@@ -460,11 +469,6 @@ __global__ void __launch_bounds__(512) bwd_prep_kernel(BwdParams p, BwdWs W) {
         bL += x;
         ptot *= y;
     }
-    // the chunk-start state, read before this thread's stores go out
-    const f32x4* Sg = reinterpret_cast<const f32x4*>(p.h_ckpt + static_cast<size_t>(ch) * DK * DV);
-    f32x4 hs[NS4];
-#pragma unroll
-    for (int i = 0; i < NS4; ++i) hs[i] = Sg[min(tid + 512 * i, S4 - 1)];
 #pragma unroll
     for (int i = 0; i < NTOK; ++i) {
         const int t = tb + i;
@@ -482,7 +486,6 @@ __global__ void __launch_bounds__(512) bwd_prep_kernel(BwdParams p, BwdWs W) {
         *reinterpret_cast<f32x4*>(W.em + static_cast<size_t>(ch) * DK + 4 * q4) = em;
         *reinterpret_cast<f32x4*>(W.gC + static_cast<size_t>(ch) * DK + 4 * q4) = exp2c4(bL * kLog2e);
         *reinterpret_cast<f32x4*>(W.pC + static_cast<size_t>(ch) * DK + 4 * q4) = ptot;
-        *reinterpret_cast<f32x4*>(em_s + 4 * q4) = em;
     }
 #pragma unroll
     for (int i = 0; i < QV::NTOK; ++i) {
@@ -493,14 +496,6 @@ __global__ void __launch_bounds__(512) bwd_prep_kernel(BwdParams p, BwdWs W) {
         *reinterpret_cast<f32x4*>(W.dO + o) = valid ? p.scale * dd[i] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     if (tid < 64) W.beta[static_cast<size_t>(ch) * 64 + tid] = (tid < ci.L) ? p.beta[(trow0 + tid) * p.H + ci.h] : 0.f;
-    // S' = Diag(e^m) S for the chunk-start state (h_ckpt is [B,H,NT,DK,DV] = [NC][DK][DV])
-    __syncthreads();
-    f32x4* Sp4 = reinterpret_cast<f32x4*>(W.Sp + static_cast<size_t>(ch) * DK * DV);
-#pragma unroll
-    for (int i = 0; i < NS4; ++i) {
-        const int u = tid + 512 * i;
-        if (S4 % 512 == 0 || u < S4) Sp4[u] = em_s[(4 * u) / DV] * hs[i];
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1608,15 +1603,16 @@ hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t st) {
 #define CKDA_CHECK(x) do { e = (x); if (e != hipSuccess) return e; } while (0)
     if (!a.h_ckpt) {
         // checkpoints recomputed: a forward pass whose chunk records sit in the
-        // blocks' first regions (K1 .. dV), whose outputs go to the S' / dSt
-        // regions (both free until the prep runs) and whose checkpoints go to
-        // their own area after the blocks; records-only room keeps its state
-        // pass on whole chains
+        // blocks' first regions (K1 .. dV), whose outputs go to the regions
+        // from dSt on (dSt and the [64 x 64] blocks: at least 64 DV floats per
+        // chunk-head, all free until the backward's own passes run) and whose
+        // checkpoints go to their own area after the blocks; records-only room
+        // keeps its state pass on whole chains
         FwdArgs f{};
         f.B = a.B; f.T = a.T; f.H = a.H; f.DK = DK; f.DV = DV; f.bf16 = a.bf16;
         f.head_gate = a.head_gate; f.qk_norm = a.qk_norm;
         f.q = a.q; f.k = a.k; f.v = a.v; f.g = a.g; f.s = a.s; f.beta = a.beta; f.scale = a.scale;
-        f.h0 = a.h0; f.o = W.Sp; f.ht = nullptr;
+        f.h0 = a.h0; f.o = W.dSt; f.ht = nullptr;
         f.h_ckpt = reinterpret_cast<float*>(static_cast<unsigned char*>(a.ws) + align256(blocks));
         f.cu = a.cu; f.cu_host = a.cu_host; f.ndocs = a.ndocs;
         f.ws = a.ws; f.ws_bytes = fwd_workspace_bytes(nslots, a.H, DK, DV, a.bf16);
@@ -1631,14 +1627,20 @@ hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t st) {
     hipLaunchKernelGGL(bwd_inverse_kernel, dim3(NC), dim3(256), 0, st, W);
     CKDA_CHECK(hipGetLastError());
     // U = T (V - K1 S')
-    CKDA_CHECK(gemm(mk(64, DV, DK, W.K1, DK, s64k, false, W.Sp, DV, skv, false, W.R, DV, s64v, -1.f, W.V, 1.f), NC, st));
+    // S' = Diag(e^m) S of the chunk start, S read from the checkpoints and
+    // scaled while staged (checkpoints of unused varlen slots are never
+    // written; their products feed nothing)
+    const float* ck = p.h_ckpt;
+    auto with_em = [&](Gemm g) { g.bs = W.em; g.sBs = DK; return g; };
+    CKDA_CHECK(gemm(with_em(mk(64, DV, DK, W.K1, DK, s64k, false, ck, DV, skv, false, W.R, DV, s64v, -1.f, W.V, 1.f)),
+                    NC, st));
     CKDA_CHECK(gemm(mk(64, DV, 64, W.T, 64, s44, false, W.R, DV, s64v, false, W.U, DV, s64v), NC, st));
     // reverse recurrence: dSt, dU per chunk, dh0
     CKDA_CHECK(launch_reverse(p, W, a.bf16, st));
     // chunk-parallel gradients
     CKDA_CHECK(gemm(mk(64, 64, DV, W.dO, DV, s64v, false, W.U, DV, s64v, true, W.dM, 64, s44, 1.f, nullptr, 0.f, 2), NC, st));
     CKDA_CHECK(gemm(mk(64, DK, DV, W.U, DV, s64v, false, W.dSt, DV, skv, true, W.dKB, DK, s64k), NC, st));
-    CKDA_CHECK(gemm(mk(64, DK, DV, W.dU, DV, s64v, false, W.Sp, DV, skv, true, W.dW, DK, s64k, -1.f), NC, st));
+    CKDA_CHECK(gemm(with_em(mk(64, DK, DV, W.dU, DV, s64v, false, ck, DV, skv, true, W.dW, DK, s64k, -1.f)), NC, st));
     CKDA_CHECK(gemm(mk(64, DV, 64, W.T, 64, s44, true, W.dU, DV, s64v, false, W.dV, DV, s64v), NC, st));
     // dT = dU V^T + dW K1^T
     CKDA_CHECK(gemm2(mk(64, 64, DV, W.dU, DV, s64v, false, W.V, DV, s64v, true, W.dT, 64, s44),
@@ -1656,7 +1658,7 @@ hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t st) {
     CKDA_CHECK(gemm2(mk(64, DK, 64, W.dA, 64, s44, true, W.K1, DK, s64k, false, W.dK2, DK, s64k),
                      mk(64, DK, 64, W.dM, 64, s44, true, W.Q1, DK, s64k, false, W.dK2, DK, s64k), NC, st));
     CKDA_CHECK(gemm2(mk(64, DK, 64, W.dM, 64, s44, false, W.K2, DK, s64k, false, W.dQ1, DK, s64k),
-                     mk(64, DK, DV, W.dO, DV, s64v, false, W.Sp, DV, skv, true, W.dQ1, DK, s64k), NC, st));
+                     with_em(mk(64, DK, DV, W.dO, DV, s64v, false, ck, DV, skv, true, W.dQ1, DK, s64k)), NC, st));
     CKDA_CHECK(launch_chunk_pass(a.bf16, true, p, W, NC, st));
     CKDA_CHECK(hipGetLastError());
 #undef CKDA_CHECK

@@ -78,9 +78,9 @@ def seg_bytes(nsslots, H, DK, DV):
 
 
 def bwd_block_bytes(DK, DV):
-    """Backward workspace per chunk-head: 9 [64 x DK], 6 [64 x DV], 2 [DK x DV]
+    """Backward workspace per chunk-head: 9 [64 x DK], 6 [64 x DV], 1 [DK x DV]
     and 10 [64 x 64] fp32 matrices, 3 [DK] and 3 [64] vectors."""
-    return 4 * (9 * 64 * DK + 6 * 64 * DV + 2 * DK * DV + 10 * 64 * 64 + 3 * DK + 3 * 64)
+    return 4 * (9 * 64 * DK + 6 * 64 * DV + DK * DV + 10 * 64 * 64 + 3 * DK + 3 * 64)
 
 
 def test_fwd_workspace(L):
