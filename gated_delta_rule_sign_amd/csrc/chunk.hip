@@ -535,8 +535,9 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
 #pragma unroll
             for (int J = 0; J < 4; ++J)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    PR::gstore1s(rec + RC::OFF_W, RC::W_ROW, 16 * J + 4 * gq + i, 16 * ct + n, X[J][i]);
+                for (int i = 0; i < 4; i += 2)
+                    PR::gstore2c(rec + RC::OFF_W, RC::W_PLANE, RC::W_ROW, 16 * J + 4 * gq + i, 16 * ct + n,
+                                 X[J][i], X[J][i + 1]);
         }
     }
 }

@@ -101,22 +101,6 @@ struct Prec<false> {
         return mfma16x3(a.hi, a.lo, b.hi, b.lo, acc);
     }
 
-    // single-plane A operands (a value stored once, already rounded to bf16)
-    typedef bf16x8 A8s;
-    static __device__ __forceinline__ A8s load4x2s(const LdsMat& m, int r, int ca, int cb) {
-        return lds4x2(hp(m, r, ca), hp(m, r, cb));
-    }
-    static __device__ __forceinline__ f32x4 mma8s(const A8s& a, const F8& b, f32x4 acc) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b.lo, acc, 0, 0, 0);
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b.hi, acc, 0, 0, 0);
-    }
-    typedef s16x4 A4s;
-    static __device__ __forceinline__ A4s load4s(const LdsMat& m, int r, int c) { return lds4s(hp(m, r, c)); }
-    static __device__ __forceinline__ f32x4 mma4s(const A4s& a, const F4& b, f32x4 acc) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b.lo, acc, 0, 0, 0);
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b.hi, acc, 0, 0, 0);
-    }
-
     // global (workspace) stores: row-major planes of `row` bytes per row,
     // lo plane `plane` bytes after the hi plane
     static __device__ __forceinline__ void gstore8(unsigned char* base, size_t plane, int row, int r, int c,
@@ -134,9 +118,15 @@ struct Prec<false> {
         *reinterpret_cast<u32x2*>(p) = u32x2{p0.hi, p1.hi};
         *reinterpret_cast<u32x2*>(p + plane) = u32x2{p0.lo, p1.lo};
     }
-    // one element of a single-plane matrix, rounded to bf16
-    static __device__ __forceinline__ void gstore1s(unsigned char* base, int row, int r, int c, float x) {
-        *reinterpret_cast<uint16_t*>(base + static_cast<size_t>(r) * row + 2 * c) = f32_to_bf16(x);
+    // two elements of one column (rows r and r + 1) of a two-plane matrix
+    static __device__ __forceinline__ void gstore2c(unsigned char* base, size_t plane, int row, int r, int c,
+                                                    float x0, float x1) {
+        const SplitPair sp = split2(x0, x1);
+        unsigned char* p = base + static_cast<size_t>(r) * row + 2 * c;
+        *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(sp.hi);
+        *reinterpret_cast<uint16_t*>(p + row) = static_cast<uint16_t>(sp.hi >> 16);
+        *reinterpret_cast<uint16_t*>(p + plane) = static_cast<uint16_t>(sp.lo);
+        *reinterpret_cast<uint16_t*>(p + plane + row) = static_cast<uint16_t>(sp.lo >> 16);
     }
 };
 
@@ -194,16 +184,6 @@ struct Prec<true> {
         return acc;
     }
 
-    typedef F8 A8s;
-    static __device__ __forceinline__ A8s load4x2s(const LdsMat& m, int r, int ca, int cb) { return load4x2(m, r, ca, cb); }
-    static __device__ __forceinline__ f32x4 mma8s(const A8s& x, const F8& y, f32x4 acc) { return mma8(x, y, acc); }
-    typedef f32x4 A4s;
-    static __device__ __forceinline__ A4s load4s(const LdsMat& m, int r, int c) { return ld4(fp(m, r, c)); }
-    static __device__ __forceinline__ f32x4 mma4s(const A4s& x, const F4& y, f32x4 acc) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[j], y.a[j], acc, 0, 0, 0);
-        return acc;
-    }
 
     static __device__ __forceinline__ void gstore8(unsigned char* base, size_t, int row, int r, int c,
                                                    const float (&x)[8]) {
@@ -214,8 +194,11 @@ struct Prec<true> {
     static __device__ __forceinline__ void gstore4(unsigned char* base, size_t, int row, int r, int c, f32x4 x) {
         *reinterpret_cast<float4*>(base + static_cast<size_t>(r) * row + 4 * c) = make_float4(x[0], x[1], x[2], x[3]);
     }
-    static __device__ __forceinline__ void gstore1s(unsigned char* base, int row, int r, int c, float x) {
-        *reinterpret_cast<float*>(base + static_cast<size_t>(r) * row + 4 * c) = x;
+    static __device__ __forceinline__ void gstore2c(unsigned char* base, size_t, int row, int r, int c,
+                                                    float x0, float x1) {
+        float* p = reinterpret_cast<float*>(base + static_cast<size_t>(r) * row + 4 * c);
+        p[0] = x0;
+        *reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(p) + row) = x1;
     }
 };
 

@@ -19,9 +19,12 @@
 // so that one chunk's state step is
 //   U = u - W S,   O = Qh S + M U,   S <- Diag(d) S + KbT U.
 //
-// Storage: bf16 inputs keep Qh, KbT and M as two bf16 planes (hi, then lo
-// = bf16(x - hi)) and W as one bf16 plane; fp32 inputs store every matrix as
-// one fp32 plane.  Every block is a whole number of 16-byte units.
+// Storage: bf16 inputs keep W, Qh, KbT and M as two bf16 planes (hi, then lo
+// = bf16(x - hi)); fp32 inputs store every matrix as one fp32 plane.  (W in
+// one bf16 rounding is enough while the gates decay, but where they do not,
+// e.g. beta = 2 and |alpha| = 1, its rounding error is carried by the state
+// from chunk to chunk and grows with the sequence.)  Every block is a whole
+// number of 16-byte units.
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -31,13 +34,14 @@ namespace ckda {
 template <int DK, int DV, bool F32>
 struct Record {
     static constexpr int ES = F32 ? 4 : 2;   // bytes per element and plane
-    static constexpr int NP = F32 ? 1 : 2;   // planes of Qh, KbT, M
+    static constexpr int NP = F32 ? 1 : 2;   // planes of W, Qh, KbT, M
     static constexpr int W_ROW = DK * ES;    // bytes per row
     static constexpr int Q_ROW = DK * ES;
     static constexpr int K_ROW = 64 * ES;
     static constexpr int M_ROW = 64 * ES;
     static constexpr size_t OFF_W = 0;
-    static constexpr size_t OFF_Q = OFF_W + 64 * W_ROW;
+    static constexpr size_t W_PLANE = 64 * W_ROW;
+    static constexpr size_t OFF_Q = OFF_W + NP * W_PLANE;
     static constexpr size_t Q_PLANE = 64 * Q_ROW;
     static constexpr size_t OFF_K = OFF_Q + NP * Q_PLANE;
     static constexpr size_t K_PLANE = static_cast<size_t>(DK) * K_ROW;

@@ -73,7 +73,7 @@ struct StateShape {
     static constexpr int PKR = (RC::K_ROW + PADB) / ES;
     static constexpr int PMR = (RC::M_ROW + PADB) / ES;
     static constexpr int L_W = 0;
-    static constexpr int L_Q = L_W + 64 * PW * ES;
+    static constexpr int L_Q = L_W + NP * 64 * PW * ES;
     static constexpr int L_K = L_Q + NP * 64 * PQ * ES;
     static constexpr int L_M = L_K + NP * DK * PKR * ES;
     static constexpr int L_D = L_M + NP * 64 * PMR * ES;
@@ -222,7 +222,7 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
         //   barrier 1 (W, Qh of j no longer read) -> write A of j+1, issue A loads of j+2
         //   barrier 2 (chunk j done) -> write B of j+1
         // so only the write of group B lies between two chunks.
-        using StW = Stage<64, RC::W_ROW / 16, SH::PADB, NT>;
+        using StW = Stage<NP * 64, RC::W_ROW / 16, SH::PADB, NT>;
         using StQ = Stage<NP * 64, RC::Q_ROW / 16, SH::PADB, NT>;
         using StK = Stage<NP * DK, RC::K_ROW / 16, SH::PADB, NT>;
         using StM = Stage<NP * 64, RC::M_ROW / 16, SH::PADB, NT>;
@@ -352,7 +352,7 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
         lds_sync();   // 0: record of chunk j in LDS
         {
             unsigned char* const sm = smem + opaque_zero();
-            const LdsMat Wm{sm + SH::L_W, SH::PW, 0};
+            const LdsMat Wm{sm + SH::L_W, SH::PW, 64 * SH::PW};
             const LdsMat Qm{sm + SH::L_Q, SH::PQ, 64 * SH::PQ};
             const LdsMat Km{sm + SH::L_K, SH::PKR, DK * SH::PKR};
             const LdsMat Mm{sm + SH::L_M, SH::PMR, 64 * SH::PMR};
@@ -387,11 +387,11 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
                 Y[R] = X[R];
             }
             {
-                typename PR::A8s wa[2][4];
+                typename PR::F8 wa[2][4];
                 typename PR::F8 qa[2][4];
 #pragma unroll
                 for (int R = 0; R < 4; ++R) {
-                    wa[0][R] = PR::load4x2s(Wm, 16 * R + n, 4 * gq, 16 + 4 * gq);
+                    wa[0][R] = PR::load4x2(Wm, 16 * R + n, 4 * gq, 16 + 4 * gq);
                     if (OUT) qa[0][R] = PR::load4x2(Qm, 16 * R + n, 4 * gq, 16 + 4 * gq);
                 }
 #pragma unroll
@@ -400,14 +400,14 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
                         const int ca = 32 * (ks + 1) + 4 * gq, cb = ca + 16;
 #pragma unroll
                         for (int R = 0; R < 4; ++R) {
-                            wa[(ks + 1) & 1][R] = PR::load4x2s(Wm, 16 * R + n, ca, cb);
+                            wa[(ks + 1) & 1][R] = PR::load4x2(Wm, 16 * R + n, ca, cb);
                             if (OUT) qa[(ks + 1) & 1][R] = PR::load4x2(Qm, 16 * R + n, ca, cb);
                         }
                     }
                     CKDA_FENCE();
 #pragma unroll
                     for (int R = 0; R < 4; ++R) {
-                        X[R] = PR::mma8s(wa[ks & 1][R], Sb[ks], X[R]);
+                        X[R] = PR::mma8(wa[ks & 1][R], Sb[ks], X[R]);
                         if (OUT) Y[R] = PR::mma8(qa[ks & 1][R], Sb[ks], Y[R]);
                     }
                     CKDA_FENCE();

@@ -10,12 +10,12 @@ from tests.gpu_utils import banner, dev_tensor, host, rel_max, require_gpu, tok_
 pytestmark = pytest.mark.gpu
 
 # contract tolerances (max|diff| / RMS of the oracle): fp32 inputs 1e-4,
-# bf16 inputs 1e-2.  For bf16 inputs the chunk records keep Qh, KbT and M as
-# hi/lo bf16 pairs and W as one bf16 rounding; a float64 rounding model of
-# that arithmetic stays near 1.3e-3 at T = 4096, so small cases are also held
-# to a tighter design bound to catch regressions early.
+# bf16 inputs 1e-2.  For bf16 inputs the chunk records keep W, Qh, KbT and M
+# as hi/lo bf16 pairs; a float64 rounding model of that storage gives 1.1e-4
+# at T = 4096 (measured: 1.0e-4 .. 1.4e-4), so small cases are also held to a
+# tighter design bound to catch regressions early.
 TOL = {"f32": 1e-4, "bf16": 1e-2}
-DESIGN = {"f32": 1e-4, "bf16": 2e-3}
+DESIGN = {"f32": 1e-4, "bf16": 5e-4}
 
 
 def gpu_fwd(w, scale=1.0, want_ckpt=False):

@@ -16,11 +16,10 @@ from tests.gpu_utils import banner, dev_tensor, host, rel_max, require_gpu, tok_
 pytestmark = pytest.mark.gpu
 
 # max|diff| / RMS bounds.  The contract is 1e-4 (fp32 inputs) and 1e-2 (bf16
-# inputs).  For bf16 inputs the chunk records hold W in one bf16 rounding and
-# Qh, KbT, M and the state operands as bf16 hi/lo pairs; a float64 model of
-# exactly those roundings gives 2.2e-3 on the head-gate case below (exactly
-# unit keys with one decay per head), so bf16 cases here are held to 3e-3.
-DESIGN = {"f32": 1e-4, "bf16": 3e-3}
+# inputs).  For bf16 inputs the chunk records hold W, Qh, KbT, M and the state
+# operands as bf16 hi/lo pairs (measured here: 7e-5 .. 1.2e-4), so bf16 cases
+# are held to a design bound of 5e-4.
+DESIGN = {"f32": 1e-4, "bf16": 5e-4}
 BWD = {"f32": 1e-4, "bf16": 1e-3}
 
 
