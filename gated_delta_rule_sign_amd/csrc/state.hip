@@ -15,9 +15,10 @@
 // [16w, 16w+16) of the slice and keeps that DK x 16 block of S in MFMA
 // accumulator registers for the whole sequence (value columns of S evolve
 // independently, so the waves never exchange state).  Four more waves only
-// move data: they hold the next chunk's record (W, Qh, KbT, M, d and the
-// slice's u tiles) in registers, read one chunk ahead from HBM, and write it
-// to LDS at the chunk boundary.  A wave that issues global loads stalls
+// move data: they hold the next chunk's record (W, Qh, KbT, M and d) in
+// registers, read one chunk ahead from HBM, and write it to LDS at the chunk
+// boundary.  The u tiles, which only their own wave reads, go from the record
+// straight into that wave's registers, one chunk ahead.  A wave that issues global loads stalls
 // whenever the memory pipe is full; keeping those loads on separate waves
 // lets the matrix-core waves run while the next record streams in.  Products are 16x16x32
 // matrix-core tiles whose 8 K-slots per lane are two 4-row groups of the C/D
@@ -77,8 +78,7 @@ struct StateShape {
     static constexpr int L_K = L_Q + NP * 64 * PQ * ES;
     static constexpr int L_M = L_K + NP * DK * PKR * ES;
     static constexpr int L_D = L_M + NP * 64 * PMR * ES;
-    static constexpr int L_U = L_D + DK * 4;            // u tiles of the slice [4][NWC][64 lanes][4]
-    static constexpr int LDS = L_U + 4 * NWC * 64 * 16;
+    static constexpr int LDS = L_D + DK * 4;
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -210,7 +210,7 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
     }
     // first 16-column tile of the slice (transition slices: columns of P_s)
     const int vt0 = ((trans ? slice - SH::NSLICE : slice) * SH::BV) / 16;
-    const int vtu0 = trans ? 0 : vt0;   // u tiles the loaders stage (unused by transition slices)
+    const int vtu0 = trans ? 0 : vt0;   // u tile of wave 0 (transition slices read tiles of slice 0 and zero them)
     const int slotb = slot0 + jbeg;     // record slot of the first chunk walked
     const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
 
@@ -227,11 +227,10 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
         using StK = Stage<NP * DK, RC::K_ROW / 16, SH::PADB, NT>;
         using StM = Stage<NP * 64, RC::M_ROW / 16, SH::PADB, NT>;
         using StD = Stage<1, DK * 4 / 16, 0, NT>;
-        using StU = Stage<4, NWC * 64, 0, NT>;   // per J: the slice's NWC tiles, 64 lanes each
-        constexpr int NW_ = StW::N, NQ_ = StQ::N, NK_ = StK::N, NM_ = StM::N, ND_ = StD::N, NU_ = StU::N;
+        constexpr int NW_ = StW::N, NQ_ = StQ::N, NK_ = StK::N, NM_ = StM::N, ND_ = StD::N;
         constexpr int O_Q = NW_, NA = NW_ + NQ_;
-        constexpr int O_M = NK_, O_D = O_M + NM_, O_U = O_D + ND_, NB = O_U + NU_;
-        static_assert(StW::FULL && StQ::FULL && StK::FULL && StM::FULL && StU::FULL, "unguarded staging loads");
+        constexpr int O_M = NK_, O_D = O_M + NM_, NB = O_D + ND_;
+        static_assert(StW::FULL && StQ::FULL && StK::FULL && StM::FULL, "unguarded staging loads");
         u32x4 ga[NA], gb[NB];   // native vectors (a struct copy would keep them in scratch)
 #define CKDA_REC(J) reinterpret_cast<const u32x4*>(p.ws + (static_cast<size_t>(slotb + (J)) * H + h) * RC::BYTES + opaque_zero())
 #define CKDA_LOAD_A(J)                                                                                       \
@@ -251,11 +250,6 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
                 _Pragma("unroll") for (int i_ = 0; i_ < NM_; ++i_) gb[O_M + i_] = g_[RC::OFF_M / 16 + t_ + NT * i_]; \
             _Pragma("unroll") for (int i_ = 0; i_ < ND_; ++i_)                                               \
                 if (StD::has(t_, i_)) gb[O_D + i_] = g_[RC::OFF_D / 16 + t_ + NT * i_];                       \
-            _Pragma("unroll") for (int i_ = 0; i_ < NU_; ++i_) {                                             \
-                const int u_ = t_ + NT * i_;                                                                 \
-                const int J_ = u_ / (NWC * 64), r_ = u_ % (NWC * 64);                                        \
-                gb[O_U + i_] = g_[RC::OFF_U / 16 + (J_ * (DV / 16) + vtu0) * 64 + r_];                       \
-            }                                                                                                \
         }
 #define CKDA_STORE_A()                                                                                       \
         {                                                                                                    \
@@ -278,14 +272,6 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
                     StM::put(sm_ + SH::L_M + StM::lds_off(t_, i_), gb[O_M + i_]);                            \
             _Pragma("unroll") for (int i_ = 0; i_ < ND_; ++i_)                                               \
                 if (StD::has(t_, i_)) *reinterpret_cast<u32x4*>(sm_ + SH::L_D + StD::lds_off(t_, i_)) = gb[O_D + i_]; \
-            if (!(SEG && trans))                                                                             \
-                _Pragma("unroll") for (int i_ = 0; i_ < NU_; ++i_)                                           \
-                    *reinterpret_cast<u32x4*>(sm_ + SH::L_U + StU::lds_off(t_, i_)) = gb[O_U + i_];          \
-        }
-        // transition slices build P_s, the maps' linear part: their u is zero
-        if (SEG && trans) {
-            for (int u_ = opaque_tid() - NT; u_ < 4 * NWC * 64; u_ += NT)
-                *reinterpret_cast<u32x4*>(smem + SH::L_U + 16 * u_) = u32x4{0u, 0u, 0u, 0u};
         }
         if (nloop > 0) {
             CKDA_LOAD_A(0)
@@ -346,10 +332,33 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
     const size_t ck0 = p.cu ? static_cast<size_t>(slotb) * H + h
                             : (static_cast<size_t>(sidx) * H + h) * static_cast<size_t>(nchunks) + jbeg;
     const int ckstep = p.cu ? H : 1;
+    // the wave's u tiles (J, vtu0 + wt) of chunk j, in the C/D lane layout,
+    // read straight from the record one chunk ahead (u is the one part of the
+    // record no other wave needs, so it skips LDS); the last chunk re-reads
+    // its own record
+    auto u_src = [&](int jj) {
+        return reinterpret_cast<const f32x4*>(p.ws + (static_cast<size_t>(slotb + jj) * H + h) * RC::BYTES +
+                                              RC::OFF_U + opaque_zero()) +
+               (vtu0 + wt) * 64 + (threadIdx.x & 63);
+    };
+    f32x4 un[4];
+    if (nloop > 0) {
+        const f32x4* us = u_src(0);
+#pragma unroll
+        for (int J = 0; J < 4; ++J) un[J] = us[J * (DV / 16) * 64];
+    }
     for (int j = 0; j < nloop; ++j) {
         const int c0 = 64 * (jbeg + j);
         const int L = min(64, len - c0);
         lds_sync();   // 0: record of chunk j in LDS
+        f32x4 u[4];   // transition slices: u = 0 (P_s is the maps' linear part)
+#pragma unroll
+        for (int J = 0; J < 4; ++J) u[J] = (SEG && trans) ? f32x4{0.f, 0.f, 0.f, 0.f} : un[J];
+        {
+            const f32x4* us = u_src(min(j + 1, nloop - 1));
+#pragma unroll
+            for (int J = 0; J < 4; ++J) un[J] = us[J * (DV / 16) * 64];
+        }
         {
             unsigned char* const sm = smem + opaque_zero();
             const LdsMat Wm{sm + SH::L_W, SH::PW, 64 * SH::PW};
@@ -359,9 +368,6 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
             const float* dl = reinterpret_cast<const float*>(sm + SH::L_D);
             const int l = opaque_tid() & 63, n = l & 15, gq = l >> 4;
             const int col = 16 * vt + n;
-            f32x4 u[4];
-#pragma unroll
-            for (int J = 0; J < 4; ++J) u[J] = *reinterpret_cast<const f32x4*>(sm + SH::L_U + ((J * NWC + wt) * 64 + l) * 16);
             if (CKPT && OUT) {   // the state at the chunk start (waves without columns store nothing)
                 const float* hc = p.h_ckpt + (ck0 + static_cast<size_t>(j) * ckstep) * DK * DV;
                 const __amdgpu_buffer_rsrc_t hrc = buffer_rsrc(hc, has_col ? DK * DV * 4 : 0);
@@ -376,7 +382,10 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
             // next to its use, which would expose every LDS round trip: one
             // wave per SIMD has no other wave to hide it behind).
             constexpr int KS = RT / 2;
-            // W S and Qh S, 32 channels per step
+            // W S and Qh S: 32 channels per k-step, in steps of two 16-token
+            // row blocks; the fragments of step s+1 are read while the 12
+            // products of step s run (two steps in flight keep the operand
+            // buffers at 64 registers)
             typename PR::F8 Sb[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) Sb[ks] = PR::regs8(S[2 * ks], S[2 * ks + 1]);
@@ -387,28 +396,30 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
                 Y[R] = X[R];
             }
             {
-                typename PR::F8 wa[2][4];
-                typename PR::F8 qa[2][4];
+                constexpr int NSTEP = 2 * KS;
+                typename PR::F8 wa[2][2];
+                typename PR::F8 qa[2][2];
 #pragma unroll
-                for (int R = 0; R < 4; ++R) {
-                    wa[0][R] = PR::load4x2(Wm, 16 * R + n, 4 * gq, 16 + 4 * gq);
-                    if (OUT) qa[0][R] = PR::load4x2(Qm, 16 * R + n, 4 * gq, 16 + 4 * gq);
+                for (int r = 0; r < 2; ++r) {
+                    wa[0][r] = PR::load4x2(Wm, 16 * r + n, 4 * gq, 16 + 4 * gq);
+                    if (OUT) qa[0][r] = PR::load4x2(Qm, 16 * r + n, 4 * gq, 16 + 4 * gq);
                 }
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    if (ks + 1 < KS) {
-                        const int ca = 32 * (ks + 1) + 4 * gq, cb = ca + 16;
+                for (int st = 0; st < NSTEP; ++st) {
+                    const int ks = st / 2, R0 = 2 * (st % 2);
+                    if (st + 1 < NSTEP) {
+                        const int ca = 32 * ((st + 1) / 2) + 4 * gq, cb = ca + 16, R1 = 2 * ((st + 1) % 2);
 #pragma unroll
-                        for (int R = 0; R < 4; ++R) {
-                            wa[(ks + 1) & 1][R] = PR::load4x2(Wm, 16 * R + n, ca, cb);
-                            if (OUT) qa[(ks + 1) & 1][R] = PR::load4x2(Qm, 16 * R + n, ca, cb);
+                        for (int r = 0; r < 2; ++r) {
+                            wa[(st + 1) & 1][r] = PR::load4x2(Wm, 16 * (R1 + r) + n, ca, cb);
+                            if (OUT) qa[(st + 1) & 1][r] = PR::load4x2(Qm, 16 * (R1 + r) + n, ca, cb);
                         }
                     }
                     CKDA_FENCE();
 #pragma unroll
-                    for (int R = 0; R < 4; ++R) {
-                        X[R] = PR::mma8(wa[ks & 1][R], Sb[ks], X[R]);
-                        if (OUT) Y[R] = PR::mma8(qa[ks & 1][R], Sb[ks], Y[R]);
+                    for (int r = 0; r < 2; ++r) {
+                        X[R0 + r] = PR::mma8(wa[st & 1][r], Sb[ks], X[R0 + r]);
+                        if (OUT) Y[R0 + r] = PR::mma8(qa[st & 1][r], Sb[ks], Y[R0 + r]);
                     }
                     CKDA_FENCE();
                 }
