@@ -153,3 +153,23 @@ def test_zero_query_and_key_rows(dtype):
     o, _ = check_fwd(w, dtype)
     assert not np.any(host(o)[0, zq])      # a zero query reads exactly zero
     check_bwd(w, dtype, seed=509)
+
+
+@pytest.mark.parametrize("dtype,DK,DV", [("f32", 64, 64), ("bf16", 64, 128)])
+def test_segmented_passes_without_decay(dtype, DK, DV):
+    """beta = 2, g = 0 over 4,160 tokens (65 chunks) with segments of 16
+    chunks forced: five segments, so the scan chains three middle segments
+    whose maps P_s are products of orthogonal chunk maps (nothing shrinks),
+    forward and backward against the oracle."""
+    require_gpu()
+    from gated_delta_rule_sign_amd import ckda
+    banner(f"segments, beta=2 g=0 {dtype} DK={DK} DV={DV}")
+    w = I.make_forward(1, 4160, 1, DK, DV, dtype, seed=510, h0_std=0.3)
+    w.tok.beta[...] = 2.0
+    w.tok.g[...] = 0.0
+    ckda.set_segment_chunks(16)
+    try:
+        check_fwd(w, dtype)
+        check_bwd(w, dtype, seed=511)
+    finally:
+        ckda.set_segment_chunks(0)
