@@ -83,6 +83,15 @@ struct Prec<false> {
     static __device__ __forceinline__ F8 load4x2(const LdsMat& m, int r, int ca, int cb) {
         return F8{lds4x2(hp(m, r, ca), hp(m, r, cb)), lds4x2(lp(m, r, ca), lp(m, r, cb))};
     }
+    // A fragment of the 32-wide k-step at k0 for lane group g (columns
+    // k0 + 4g .. +3 and k0 + 16 + 4g .. +3) from a region staged with those
+    // two column quads side by side at k0 + 8g: one 16-byte read per plane
+    // (a ds_read_b128 moves data at twice the rate of the split
+    // ds_read2_b64 on gfx950)
+    static constexpr bool kPermA = true;
+    static __device__ __forceinline__ F8 loadA(const LdsMat& m, int r, int k0, int g) {
+        return load8(m, r, k0 + 8 * g);
+    }
     static __device__ __forceinline__ F4 load4(const LdsMat& m, int r, int c) {
         return F4{lds4s(hp(m, r, c)), lds4s(lp(m, r, c))};
     }
@@ -167,6 +176,11 @@ struct Prec<true> {
     }
     static __device__ __forceinline__ F8 load4x2(const LdsMat& m, int r, int ca, int cb) {
         return F8{ld4(fp(m, r, ca)), ld4(fp(m, r, cb))};
+    }
+    // fp32 regions are staged unpermuted: two 16-byte reads already
+    static constexpr bool kPermA = false;
+    static __device__ __forceinline__ F8 loadA(const LdsMat& m, int r, int k0, int g) {
+        return load4x2(m, r, k0 + 4 * g, k0 + 16 + 4 * g);
     }
     static __device__ __forceinline__ F4 load4(const LdsMat& m, int r, int c) { return F4{ld4(fp(m, r, c))}; }
     static __device__ __forceinline__ F8 regs8(f32x4 a, f32x4 b) { return F8{a, b}; }

@@ -64,11 +64,11 @@ struct StateShape {
     static constexpr int RT = DK / 16;             // 16-row tiles of S
     static constexpr int ES = RC::ES, NP = RC::NP;
     // Row padding of the staged matrices, chosen from bank-conflict counts on
-    // gfx950: the bf16 fragments are two 8-byte reads 32 bytes apart (merged
-    // into one ds_read2_b64), conflict-free when the row pitch is 2 mod 4
-    // dwords; the fp32 fragments are 16-byte reads, conflict-free at 8 mod 16
-    // dwords.  (Rows of 64 or 32 data dwords plus 6 or 8.)
-    static constexpr int PADB = F32 ? 32 : 24;
+    // gfx950: every fragment is read with 16-byte reads (bf16 regions are
+    // staged with the A-operand column permutation, see Stage::put_a),
+    // conflict-free at a row pitch of 8 mod 16 dwords.  (Rows of 64, 32 or 16
+    // data dwords plus 8.)
+    static constexpr int PADB = 32;
     static constexpr int PW = (RC::W_ROW + PADB) / ES;   // pitches in elements
     static constexpr int PQ = (RC::Q_ROW + PADB) / ES;
     static constexpr int PKR = (RC::K_ROW + PADB) / ES;
@@ -102,6 +102,26 @@ struct Stage {
         } else {
             *reinterpret_cast<u32x2*>(p) = v.xy;
             *reinterpret_cast<u32x2*>(p + 8) = v.zw;
+        }
+    }
+    // write unit (tid, i) of a matrix read as matrix-core A operands into the
+    // region at `base`.  PERM (bf16 elements): in each 32-column group,
+    // columns 4g .. 4g+3 and 16+4g .. 16+4g+3 are stored side by side at 8g,
+    // so that a lane group's fragment is one 16-byte read.  Unit uc holds
+    // columns 32 (uc / 4) + 8q .. +7 (q = uc % 4); its half h belongs to lane
+    // group (2q + h) % 4, in the group's first four slots for q < 2 and its
+    // last four for q >= 2.
+    template <bool PERM>
+    static __device__ __forceinline__ void put_a(unsigned char* base, int tid, int i, u32x4 v) {
+        if constexpr (!PERM) {
+            put(base + lds_off(tid, i), v);
+        } else {
+            static_assert(UPR % 4 == 0 && PAD % 16 == 0, "32-column groups, 16-byte rows");
+            const int u = tid + NT * i;
+            const int uc = u % UPR, q = uc & 3;
+            unsigned char* rb = base + (u / UPR) * (UPR * 16 + PAD) + 64 * (uc >> 2) + 8 * (q >> 1);
+            *reinterpret_cast<u32x2*>(rb + 16 * ((2 * q) & 3)) = v.xy;
+            *reinterpret_cast<u32x2*>(rb + 16 * ((2 * q + 1) & 3)) = v.zw;
         }
     }
 };
@@ -256,20 +276,20 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
             unsigned char* const sm_ = smem + opaque_zero();                                                 \
             const int t_ = opaque_tid() - NT;                                                                \
             _Pragma("unroll") for (int i_ = 0; i_ < NW_; ++i_)                                               \
-                StW::put(sm_ + SH::L_W + StW::lds_off(t_, i_), ga[i_]);                                      \
+                StW::template put_a<PR::kPermA>(sm_ + SH::L_W, t_, i_, ga[i_]);                                \
             if (OUT)                                                                                         \
                 _Pragma("unroll") for (int i_ = 0; i_ < NQ_; ++i_)                                           \
-                    StQ::put(sm_ + SH::L_Q + StQ::lds_off(t_, i_), ga[O_Q + i_]);                            \
+                    StQ::template put_a<PR::kPermA>(sm_ + SH::L_Q, t_, i_, ga[O_Q + i_]);                      \
         }
 #define CKDA_STORE_B()                                                                                       \
         {                                                                                                    \
             unsigned char* const sm_ = smem + opaque_zero();                                                 \
             const int t_ = opaque_tid() - NT;                                                                \
             _Pragma("unroll") for (int i_ = 0; i_ < NK_; ++i_)                                               \
-                StK::put(sm_ + SH::L_K + StK::lds_off(t_, i_), gb[i_]);                                      \
+                StK::template put_a<PR::kPermA>(sm_ + SH::L_K, t_, i_, gb[i_]);                                \
             if (OUT)                                                                                         \
                 _Pragma("unroll") for (int i_ = 0; i_ < NM_; ++i_)                                           \
-                    StM::put(sm_ + SH::L_M + StM::lds_off(t_, i_), gb[O_M + i_]);                            \
+                    StM::template put_a<PR::kPermA>(sm_ + SH::L_M, t_, i_, gb[O_M + i_]);                      \
             _Pragma("unroll") for (int i_ = 0; i_ < ND_; ++i_)                                               \
                 if (StD::has(t_, i_)) *reinterpret_cast<u32x4*>(sm_ + SH::L_D + StD::lds_off(t_, i_)) = gb[O_D + i_]; \
         }
@@ -401,18 +421,18 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
                 typename PR::F8 qa[2][2];
 #pragma unroll
                 for (int r = 0; r < 2; ++r) {
-                    wa[0][r] = PR::load4x2(Wm, 16 * r + n, 4 * gq, 16 + 4 * gq);
-                    if (OUT) qa[0][r] = PR::load4x2(Qm, 16 * r + n, 4 * gq, 16 + 4 * gq);
+                    wa[0][r] = PR::loadA(Wm, 16 * r + n, 0, gq);
+                    if (OUT) qa[0][r] = PR::loadA(Qm, 16 * r + n, 0, gq);
                 }
 #pragma unroll
                 for (int st = 0; st < NSTEP; ++st) {
                     const int ks = st / 2, R0 = 2 * (st % 2);
                     if (st + 1 < NSTEP) {
-                        const int ca = 32 * ((st + 1) / 2) + 4 * gq, cb = ca + 16, R1 = 2 * ((st + 1) % 2);
+                        const int k1 = 32 * ((st + 1) / 2), R1 = 2 * ((st + 1) % 2);
 #pragma unroll
                         for (int r = 0; r < 2; ++r) {
-                            wa[(st + 1) & 1][r] = PR::load4x2(Wm, 16 * (R1 + r) + n, ca, cb);
-                            if (OUT) qa[(st + 1) & 1][r] = PR::load4x2(Qm, 16 * (R1 + r) + n, ca, cb);
+                            wa[(st + 1) & 1][r] = PR::loadA(Wm, 16 * (R1 + r) + n, k1, gq);
+                            if (OUT) qa[(st + 1) & 1][r] = PR::loadA(Qm, 16 * (R1 + r) + n, k1, gq);
                         }
                     }
                     CKDA_FENCE();
@@ -433,11 +453,11 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
                 for (int R = 0, x = 0; R < 4; ++R)
 #pragma unroll
                     for (int kt = 0; kt <= R / 2; ++kt, ++x)
-                        ma[x] = PR::load4x2(Mm, 16 * R + n, 32 * kt + 4 * gq, 32 * kt + 16 + 4 * gq);
+                        ma[x] = PR::loadA(Mm, 16 * R + n, 32 * kt, gq);
             }
             typename PR::F8 ka[2][2];
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) ka[0][kt] = PR::load4x2(Km, n, 32 * kt + 4 * gq, 32 * kt + 16 + 4 * gq);
+            for (int kt = 0; kt < 2; ++kt) ka[0][kt] = PR::loadA(Km, n, 32 * kt, gq);
             CKDA_FENCE();
             // U = u - W S, as B operands over 32 tokens per step
             typename PR::F8 Ub[2];
@@ -467,8 +487,7 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
                 if (rt + 1 < RT) {
 #pragma unroll
                     for (int kt = 0; kt < 2; ++kt)
-                        ka[(rt + 1) & 1][kt] =
-                            PR::load4x2(Km, 16 * (rt + 1) + n, 32 * kt + 4 * gq, 32 * kt + 16 + 4 * gq);
+                        ka[(rt + 1) & 1][kt] = PR::loadA(Km, 16 * (rt + 1) + n, 32 * kt, gq);
                 }
                 const f32x4 dd = *reinterpret_cast<const f32x4*>(dl + 16 * rt + 4 * gq);
                 CKDA_FENCE();
