@@ -237,11 +237,14 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
     if (w >= 4) {
         // ================= loader waves ====================================
         // Two register groups: A = W, Qh (read by the first products of a
-        // chunk), B = KbT, M, d, u (read by the rest).  Per chunk j:
-        //   barrier 0 (record j complete) -> issue B loads of j+1
-        //   barrier 1 (W, Qh of j no longer read) -> write A of j+1, issue A loads of j+2
-        //   barrier 2 (chunk j done) -> write B of j+1
-        // so only the write of group B lies between two chunks.
+        // chunk), B = KbT, M, d (read by the rest).  Two barriers per chunk j:
+        //   X (W, Qh of j no longer read; B of j in LDS) -> write A of j+1,
+        //     issue A loads of j+2
+        //   Y (chunk j done; A of j+1 in LDS) -> write B of j+1, issue B
+        //     loads of j+2
+        // so group A is written while the second half of chunk j runs and
+        // group B while the first half of chunk j+1 runs: no write lies
+        // between two chunks.
         using StW = Stage<NP * 64, RC::W_ROW / 16, SH::PADB, NT>;
         using StQ = Stage<NP * 64, RC::Q_ROW / 16, SH::PADB, NT>;
         using StK = Stage<NP * DK, RC::K_ROW / 16, SH::PADB, NT>;
@@ -299,16 +302,17 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
             CKDA_STORE_A()
             CKDA_STORE_B()
             CKDA_LOAD_A(min(1, nloop - 1))
+            CKDA_LOAD_B(min(1, nloop - 1))
         }
+        lds_sync();   // record 0 in LDS
         // (the last chunks re-read the final record: no branches)
         for (int j = 0; j < nloop; ++j) {
-            lds_sync();   // 0: record j complete in LDS
-            CKDA_LOAD_B(min(j + 1, nloop - 1))
-            lds_sync();   // 1: W, Qh of chunk j consumed
+            lds_sync();   // X: W, Qh of chunk j consumed
             CKDA_STORE_A()
             CKDA_LOAD_A(min(j + 2, nloop - 1))
-            lds_sync();   // 2: chunk j consumed
+            lds_sync();   // Y: chunk j consumed
             CKDA_STORE_B()
+            CKDA_LOAD_B(min(j + 2, nloop - 1))
         }
 #undef CKDA_REC
 #undef CKDA_LOAD_A
@@ -367,10 +371,10 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
 #pragma unroll
         for (int J = 0; J < 4; ++J) un[J] = us[J * (DV / 16) * 64];
     }
+    lds_sync();   // record 0 in LDS
     for (int j = 0; j < nloop; ++j) {
         const int c0 = 64 * (jbeg + j);
         const int L = min(64, len - c0);
-        lds_sync();   // 0: record of chunk j in LDS
         f32x4 u[4];   // transition slices: u = 0 (P_s is the maps' linear part)
 #pragma unroll
         for (int J = 0; J < 4; ++J) u[J] = (SEG && trans) ? f32x4{0.f, 0.f, 0.f, 0.f} : un[J];
@@ -444,7 +448,7 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
                     CKDA_FENCE();
                 }
             }
-            lds_sync();   // 1: W, Qh consumed (the loaders refill them for chunk j+1)
+            lds_sync();   // X: W, Qh consumed (the loaders refill them for chunk j+1); KbT, M, d in LDS
             // M fragments for the output and the first KbT fragments, read
             // while U is formed
             typename PR::F8 ma[6];
@@ -498,7 +502,7 @@ __global__ void __launch_bounds__(512, 2) ckda_state_kernel(StateParams p)
                 CKDA_FENCE();
             }
         }
-        lds_sync();   // 2: chunk j consumed
+        lds_sync();   // Y: chunk j consumed (the loaders refill KbT, M, d for chunk j+1)
     }
 
     // the end state: ht (whole chains; phase 3, a chain's last segment), or
