@@ -94,6 +94,10 @@ struct Gemm {
     // bs[z * sBs + r]: Diag(bs) B for B read as stored, B Diag(bs) for B
     // read transposed), applied while the slab is staged
     const float* bs; long long sBs;
+    // C of batch element z: C + z sC, or with cn1 > 0 the three-level
+    // decomposition z = (z2 cn2 + z1) cn1 + z0 -> C + z0 sC + z1 cs1 + z2 cs2
+    // (a chunk-head's rows straight into a [B,T,H,D] output)
+    int cn1, cn2; long long cs1, cs2;
 };
 
 // One workgroup per batch element: C (64 x N) = A (64 x K) B (K x N), N, K in
@@ -192,7 +196,9 @@ __global__ void __launch_bounds__(256) bgemm_kernel(Gemm p, Gemm q) {
     __shared__ __align__(16) float As[64 * kPK > kKS * kPN ? 64 * kPK : kKS * kPN];
     __shared__ __align__(16) float Bs[128 * kPK > 2 * kKS * kPN ? 128 * kPK : 2 * kKS * kPN];
     const long long z = blockIdx.x;
-    float* C = p.C + z * p.sC;
+    float* C = p.cn1 > 0 ? p.C + (z % p.cn1) * p.sC + ((z / p.cn1) % p.cn2) * p.cs1 +
+                               (z / (static_cast<long long>(p.cn1) * p.cn2)) * p.cs2
+                         : p.C + z * p.sC;
     const float* D = p.D ? p.D + z * p.sD : nullptr;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63, n = l & 15, g = l >> 4;
     f32x4 acc[NT];
@@ -284,6 +290,7 @@ struct BwdParams {
     int ndocs;
     bool head_gate;      // g, s, dg per (token, head)
     bool qk_norm;        // q, k L2-normalised per (token, head) inside the path
+    bool dv_direct;      // the dV products wrote dv itself (equal-length, whole chunks)
     // segmented reverse pass: G chunks per segment, buffers as in
     // ckda_segments.h (start = the dS entering a segment from its later end)
     int G, nsslots;
@@ -1486,7 +1493,7 @@ __global__ void __launch_bounds__(final_threads<DK>()) bwd_final_kernel(BwdParam
             *reinterpret_cast<f32x4*>(p.dg + e) = dgv;
         }
     }
-    for (int u = tid; u < 64 * (DV / 4); u += NTHR) {
+    for (int u = tid; !p.dv_direct && u < 64 * (DV / 4); u += NTHR) {
         const int t = u / (DV / 4), c4 = u % (DV / 4);
         if (t < ci.L)
             *reinterpret_cast<f32x4*>(p.dv + ((trow0 + t) * p.H + ci.h) * DV + 4 * c4) =
@@ -1567,6 +1574,9 @@ hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t st) {
     p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dg = a.dg; p.dbeta = a.dbeta; p.dh0 = a.dh0;
     p.B = a.B; p.T = a.T; p.H = a.H; p.NT = NT; p.cu = a.cu; p.ndocs = a.ndocs; p.head_gate = a.head_gate;
     p.qk_norm = a.qk_norm;
+    // dv straight from the dV products when every chunk is whole (the
+    // products write all 64 rows of a chunk)
+    p.dv_direct = !a.cu && a.T % 64 == 0;
     const size_t blocks = bwd_workspace_bytes(nslots, a.H, DK, DV);
     const size_t seg_off = align256(blocks) + align256(bwd_ckpt_bytes(nslots, a.H, DK, DV));
     {   // segmented reverse pass when the plan takes it and the workspace has room
@@ -1641,7 +1651,13 @@ hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t st) {
     CKDA_CHECK(gemm(mk(64, 64, DV, W.dO, DV, s64v, false, W.U, DV, s64v, true, W.dM, 64, s44, 1.f, nullptr, 0.f, 2), NC, st));
     CKDA_CHECK(gemm(mk(64, DK, DV, W.U, DV, s64v, false, W.dSt, DV, skv, true, W.dKB, DK, s64k), NC, st));
     CKDA_CHECK(gemm(with_em(mk(64, DK, DV, W.dU, DV, s64v, false, ck, DV, skv, true, W.dW, DK, s64k, -1.f)), NC, st));
-    CKDA_CHECK(gemm(mk(64, DV, 64, W.T, 64, s44, true, W.dU, DV, s64v, false, W.dV, DV, s64v), NC, st));
+    if (p.dv_direct) {   // chunk-head (b H + h) NT + j: 64 whole rows of dv from token b T + 64 j
+        Gemm g = mk(64, DV, 64, W.T, 64, s44, true, W.dU, DV, s64v, false, a.dv, a.H * DV, 64LL * a.H * DV);
+        g.cn1 = NT; g.cn2 = a.H; g.cs1 = DV; g.cs2 = static_cast<long long>(a.T) * a.H * DV;
+        CKDA_CHECK(gemm(g, NC, st));
+    } else {
+        CKDA_CHECK(gemm(mk(64, DV, 64, W.T, 64, s44, true, W.dU, DV, s64v, false, W.dV, DV, s64v), NC, st));
+    }
     // dT = dU V^T + dW K1^T
     CKDA_CHECK(gemm2(mk(64, 64, DV, W.dU, DV, s64v, false, W.V, DV, s64v, true, W.dT, 64, s44),
                      mk(64, 64, DK, W.dW, DK, s64k, false, W.K1, DK, s64k, true, W.dT, 64, s44), NC, st));
