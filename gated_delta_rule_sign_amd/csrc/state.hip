@@ -16,9 +16,10 @@
 // accumulator registers for the whole sequence (value columns of S evolve
 // independently, so the waves never exchange state).  Four more waves only
 // move data: they hold the next chunk's record (W, Qh, KbT, M and d) in
-// registers, read one chunk ahead from HBM, and write it to LDS at the chunk
-// boundary.  The u tiles, which only their own wave reads, go from the record
-// straight into that wave's registers, one chunk ahead.  A wave that issues global loads stalls
+// registers, read one chunk ahead from HBM, and write it to LDS in two groups
+// while the matrix-core waves work on the other group.  The u tiles, which
+// only their own wave reads, go from the record straight into that wave's
+// registers, one chunk ahead.  A wave that issues global loads stalls
 // whenever the memory pipe is full; keeping those loads on separate waves
 // lets the matrix-core waves run while the next record streams in.  Products are 16x16x32
 // matrix-core tiles whose 8 K-slots per lane are two 4-row groups of the C/D
