@@ -177,6 +177,7 @@ ckda_status_t ckda_fwd_chunked(int B, int T, int H, int DK, int DV, ckda_dtype_t
     if (too_big(static_cast<long long>(B) * T, H)) return fail(CKDA_ERR_UNSUPPORTED, "tensor too large");
     if (static_cast<long long>(B) * ((T + 63) / 64) * H >= (1LL << 31))
         return fail(CKDA_ERR_UNSUPPORTED, "too many chunks");
+    if (static_cast<long long>(B) * H >= (1LL << 31)) return fail(CKDA_ERR_UNSUPPORTED, "too many heads");
     if (B * H == 0) return ok();
     if (T > 0) { CKDA_REQUIRE(q); CKDA_REQUIRE(k); CKDA_REQUIRE(v); CKDA_REQUIRE(g); CKDA_REQUIRE(s); CKDA_REQUIRE(beta); CKDA_REQUIRE(o); }
     CKDA_ALIGNED(q); CKDA_ALIGNED(k); CKDA_ALIGNED(g); CKDA_ALIGNED(s); CKDA_ALIGNED(workspace);
@@ -304,6 +305,9 @@ ckda_status_t ckda_bwd(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtyp
     if (B < 0 || T < 0 || H < 0) return fail(CKDA_ERR_SHAPE, "negative size (B=%d, T=%d, H=%d)", B, T, H);
     CKDA_TRY(check_heads(DK, DV));
     if (too_big(static_cast<long long>(B) * T, H)) return fail(CKDA_ERR_UNSUPPORTED, "tensor too large");
+    if (static_cast<long long>(B) * ((T + 63) / 64) * H >= (1LL << 31))
+        return fail(CKDA_ERR_UNSUPPORTED, "too many chunks");
+    if (static_cast<long long>(B) * H >= (1LL << 31)) return fail(CKDA_ERR_UNSUPPORTED, "too many heads");
     if (B * H == 0) return ok();
     ckda::BwdArgs a{};
     a.B = B; a.T = T; a.H = H; a.DK = DK; a.DV = DV; a.bf16 = in_dtype == CKDA_BF16;

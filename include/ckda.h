@@ -30,6 +30,10 @@
  *    There is no fallback path: a shape or dtype the kernels do not support
  *    is an error (CKDA_ERR_UNSUPPORTED), never a silent substitute.
  *  - Supported head sizes: DK, DV in {32, 64, 128}.  Chunk length is 64.
+ *  - Size limits (the kernels index chains, chunks and tokens in 32 bits):
+ *    token-heads (B*T*H or T_total*H), chunk-heads and (sequence, head)
+ *    states (B*H or N*H) must each stay below 2^31; larger problems fail
+ *    with CKDA_ERR_UNSUPPORTED before anything is enqueued.
  *  - Outputs must not alias inputs (except the in/out decode state).
  *  - Accuracy: the intra-chunk products factor exp(b_r - b_i) through
  *    anchors at the middle of each half chunk, so every run of 16

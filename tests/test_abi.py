@@ -168,6 +168,29 @@ def test_decode_and_bwd_reject_bad_arguments(L):
     assert L.ckda_chunk_prep(1, 8, 1, 100, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 4
 
 
+def test_size_limits(L):
+    """Token-head, chunk-head and state counts must fit the kernels' 32-bit
+    chain and token indices; larger problems fail before any pointer is used."""
+    f = ctypes.c_float(1.0)
+    assert fwd(L, B=1 << 16, T=1 << 16, H=1) == 4            # 2^32 token-heads
+    assert b"too large" in L.ckda_last_error()
+    assert fwd(L, B=1 << 16, T=0, H=1 << 15) == 4            # 2^31 (sequence, head) states
+    assert b"too many heads" in L.ckda_last_error()
+    cu = (ctypes.c_int32 * 2)(0, 1 << 30)
+    assert L.ckda_fwd_varlen(1, 1 << 30, cu, FAKE, 4, 32, 32, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, f, None,
+                             FAKE, None, None, FAKE, ctypes.c_size_t(BIG), None) == 4
+    assert b"too large" in L.ckda_last_error()
+    assert L.ckda_decode_step(1 << 20, 1 << 11, 32, 32, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, f,
+                              FAKE, FAKE, FAKE, None) == 4
+    assert b"too many heads" in L.ckda_last_error()
+    assert L.ckda_bwd(1 << 16, 1 << 16, 1, 32, 32, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, f, None, FAKE,
+                      FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ctypes.c_size_t(BIG), None) == 4
+    assert b"too large" in L.ckda_last_error()
+    assert L.ckda_bwd(1 << 16, 0, 1 << 15, 32, 32, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, f, None, FAKE,
+                      FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ctypes.c_size_t(BIG), None) == 4
+    assert b"too many heads" in L.ckda_last_error()
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     from gated_delta_rule_sign_amd import ckda
     monkeypatch.setattr(ckda, "_lib", None)
