@@ -46,6 +46,9 @@ CASES = [
     ("f32", 2, 127, 1, 32, 64),
     ("bf16", 1, 333, 2, 64, 128),
     ("f32", 1, 96, 2, 128, 128),
+    ("bf16", 2, 200, 2, 32, 32),
+    ("bf16", 1, 150, 2, 64, 32),
+    ("bf16", 1, 140, 1, 128, 32),
 ]
 
 
