@@ -192,7 +192,7 @@ __device__ __forceinline__ void bgemm_accumulate(const Gemm& p, long long z, flo
 // C = p.alpha * (A1 B1 + (q.alpha / p.alpha) A2 B2) + p.beta * D, masked;
 // the second product only when DUAL
 template <bool aT, bool bT, int NT, bool DUAL = false, bool aT2 = false, bool bT2 = false>
-__global__ void __launch_bounds__(256) bgemm_kernel(Gemm p, Gemm q) {
+__global__ void __launch_bounds__(256, 4) bgemm_kernel(Gemm p, Gemm q) {
     __shared__ __align__(16) float As[64 * kPK > kKS * kPN ? 64 * kPK : kKS * kPN];
     __shared__ __align__(16) float Bs[128 * kPK > 2 * kKS * kPN ? 128 * kPK : 2 * kKS * kPN];
     const long long z = blockIdx.x;
