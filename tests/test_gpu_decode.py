@@ -64,3 +64,52 @@ def test_decode_b256_shortened():
     assert np.array_equal(sp[ni, hi], P_ref.astype(np.int8))
     # the whole output is finite
     assert np.isfinite(o).all() and np.isfinite(st).all()
+
+
+def test_decode_b256_bench_configuration():
+    """decode_b256 as the benchmark times it: 256 sequences x 16 heads, step
+    inputs drawn for 64 steps and used cyclically over 8 + 512 steps, one
+    preallocated output, scale 1.  32 sampled (sequence, head) pairs are
+    checked against the oracle at three steps and for the final state and
+    sign product."""
+    torch = require_gpu()
+    from gated_delta_rule_sign_amd import ckda
+    distinct, total = 64, 8 + 512
+    banner(f"decode_b256 {total} steps over {distinct} distinct inputs")
+    w = I.make_workload("decode_b256", steps=distinct)
+    tok = w.tok
+    N, H, DK, DV = w.h0.shape
+    d = tok_to_dev(tok)
+    state = dev_tensor(w.h0)
+    sp = torch.ones((N, H, DK), dtype=torch.int8, device="cuda:0")
+    o = torch.empty((N, H, DV), dtype=torch.float32, device="cuda:0")
+    checked = (63, 300, total - 1)
+    kept = {}
+    for t in range(total):
+        j = t % distinct
+        ckda.decode_step(d["q"][j], d["k"][j], d["v"][j], d["g"][j], d["s"][j], d["beta"][j], state, sp, o=o)
+        if t in checked:
+            kept[t] = o.clone()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    ni = rng.integers(0, N, 32)
+    hi = rng.integers(0, H, 32)
+    cyc = np.arange(total) % distinct
+
+    def pick(x):   # [distinct, N, H, ...] -> [total, 32, 1, ...] for the sampled pairs
+        return np.ascontiguousarray(np.asarray(x)[:, ni, hi][cyc][:, :, None])
+
+    o_ref, S_ref, P_ref = oracle.decode(q=I.widen(pick(tok.q)), k=I.widen(pick(tok.k)), v=I.widen(pick(tok.v)),
+                                        g=pick(tok.g).astype(np.float64), s=pick(tok.s).astype(np.float64),
+                                        beta=pick(tok.beta).astype(np.float64),
+                                        state0=w.h0[ni, hi][:, None].astype(np.float64))
+    for t in checked:
+        e = rel_max(host(kept[t])[ni, hi], o_ref[t])
+        print(f"  o at step {t}: {e:.2e}")
+        assert e < 1e-3
+    true_gpu = host(sp)[ni, hi][:, :, None].astype(np.float64) * host(state)[ni, hi]
+    e = rel_max(true_gpu, S_ref)
+    print(f"  final state: {e:.2e}")
+    assert e < 1e-3
+    assert np.array_equal(host(sp)[ni, hi], P_ref.astype(np.int8))
+    assert np.isfinite(host(state)).all()
