@@ -1,0 +1,76 @@
+"""Host logic of bench.py (CPU): the one-GPU guard, the algorithmic byte
+counts the roofline is priced on, and the rule that measured traffic is
+reported only for the kernel sources it was measured on."""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from gated_delta_rule_sign_amd import inputs as I  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
+
+
+def _size(dtype):
+    return {"bf16": 2, "f32": 4}[dtype]
+
+
+def test_forward_bytes_per_token_head():
+    """Inputs read once and outputs written once, from the workload's own
+    shapes and storage types: q, k, v in the input dtype, g fp32 and s int8
+    per key channel, beta fp32 per head, o fp32 per value channel."""
+    c = I.WORKLOADS["layer_bf16"]
+    DK, DV, e = c["DK"], c["DV"], _size(c["dtype"])
+    expect = (2 * DK + DV) * e + DK * (np.dtype(np.float32).itemsize + np.dtype(np.int8).itemsize) + 4 + DV * 4
+    assert bench.FWD_BYTES_PER_TOKEN_HEAD == expect == 1924
+    # head-scalar gate: one g and one s per token-head
+    assert bench.FWD_HG_BYTES_PER_TOKEN_HEAD == (2 * DK + DV) * e + 4 + 1 + 4 + DV * 4
+
+
+def test_decode_bytes_per_head_step():
+    """The fp32 state read and written once, the int8 sign product read and
+    written once, one token's q, k, v (input dtype), g, s, beta, and o."""
+    c = I.WORKLOADS["decode_b256"]
+    DK, DV, e = c["DK"], c["DV"], _size(c["dtype"])
+    expect = 2 * DK * DV * 4 + 2 * DK * 1 + (2 * DK + DV) * e + DK * 4 + DK * 1 + 4 + DV * 4
+    assert bench.DEC_BYTES_PER_HEAD_STEP == expect == 133252
+
+
+def test_backward_bytes_per_token_head():
+    """q, k, v, do (bf16), g, s, beta, the chunk-start checkpoints (one
+    DK x DV fp32 state per 64 tokens), and dq, dk, dv, dg, dbeta out."""
+    c = I.WORKLOADS["layer_bf16"]
+    DK, DV, e = c["DK"], c["DV"], _size(c["dtype"])
+    expect = ((2 * DK + 2 * DV) * e + DK * 4 + DK + 4 + DK * DV * 4 // 64
+              + (2 * DK + DV + DK) * 4 + 4)
+    assert bench.BWD_BYTES_PER_TOKEN_HEAD == expect == 4744
+
+
+def test_traffic_is_reported_only_for_the_measured_sources(tmp_path, monkeypatch):
+    rec = json.load(open(bench.TRAFFIC_FILE))
+    for f in rec["sources"]:
+        assert os.path.exists(os.path.join(ROOT, "gated_delta_rule_sign_amd", "csrc", f)), f
+    got = bench.measured_traffic()
+    # either the committed counters match the kernel sources, or bench reports null
+    assert got is None or got == float(rec["traffic_bytes_per_call"])
+    # a record taken on other sources is never used
+    stale = dict(rec, sources_sha256="0" * 64)
+    p = tmp_path / "traffic.json"
+    p.write_text(json.dumps(stale))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(p))
+    assert bench.measured_traffic() is None
+    # and a missing record gives null as well
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "absent.json"))
+    assert bench.measured_traffic() is None
