@@ -62,7 +62,8 @@ struct ChunkShape {
     static constexpr int L_TOTP = L_TOTB + 4 * DK * 4;        // uint32 [4][DK/4]
     static constexpr int L_BETA = L_TOTP + 4 * (DK / 4) * 4;  // float [64]
     static constexpr int L_NRM = L_BETA + 64 * 4;             // float2 [NCG][64]: sum k^2, sum q^2
-    static constexpr int L_COLK = L_NRM + NCG * 64 * 8;       // operand [64][PC]
+    static constexpr int L_FLAG = L_NRM + NCG * 64 * 8;       // uint32 [16]: per-wave envelope flags
+    static constexpr int L_COLK = L_FLAG + 64;                // operand [64][PC]
     static constexpr int L_COLKF = L_COLK + 64 * PC * 4;      // operand [32][PC]
     static constexpr int L_PART = L_COLKF + 32 * PC * 4;      // f32x4 [20][64]
     static constexpr int SZ_PART = NCG > 1 ? 20 * 64 * 16 : 0;
@@ -76,7 +77,23 @@ struct ChunkShape {
     static_assert(LDS <= 80 * 1024, "two workgroups per CU");
     static_assert((L_COLK % 16) == 0 && (L_COLKF % 16) == 0 && (L_PART % 16) == 0 && (L_LDIAG % 16) == 0 &&
                   (L_LOFF % 16) == 0 && (L_Y % 16) == 0, "align");
+    // exact path (phase A only): kf and b (log2 units) of every token as fp32
+    // rows of XP floats, over the operand and partial-tile areas
+    static constexpr int XP = DK + 8;
+    static constexpr int L_XK = L_COLK;
+    static constexpr int L_XB = L_XK + 64 * XP * 4;
+    static constexpr int L_XEND = L_XB + 64 * XP * 4;
+    static constexpr int LDS_EX = L_XEND > LDS ? L_XEND : LDS;
+    static_assert(LDS_EX <= 80 * 1024 && (L_XB % 16) == 0, "two workgroups per CU");
 };
+
+// Largest |in-tile prefix of the log-gate| (log2 units) the anchored
+// factoring takes.  With g <= 0 every anchored exponent x = b - m of a token
+// is bounded by its 16-token tile's total, so the row and column factors e^x,
+// e^-x stay within [2^-96, 2^96], and a product term flushed below fp32's
+// normal range is at most 2^-30 of the entries it feeds.  A chunk beyond it in
+// any channel (or with any g > 0) is redone by the exact path.
+constexpr float kEnvelope = 96.f;
 
 // off-diagonal 16x16 block index of (J, K), K < J
 __device__ __forceinline__ int loff_index(int J, int K) { return (J * (J - 1)) / 2 + K; }
@@ -93,22 +110,22 @@ struct ChunkParams {
     int T, H, ndocs;
 };
 
-// HG: one gate per (token, head) (g, s [.., H]), broadcast over the channels;
-// NQK: q and k normalised per (token, head) over the key channels
-template <typename Tin, int DK, int DV, bool HG, bool NQK>
-// second bound: waves per SIMD (two 8-wave workgroups per CU -> 4, at most 128 VGPRs)
-__global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(ChunkParams p)
+// One (chunk slot, head).  HG: one gate per (token, head) (g, s [.., H]),
+// broadcast over the channels; NQK: q and k normalised per (token, head) over
+// the key channels.  EX = false: the anchored fast path, which writes the
+// record's flag and leaves the record to the exact path when the chunk's
+// gates leave the anchors' range; EX = true: the exact path (A and M entry by
+// entry), run only on flagged chunks.
+template <typename Tin, int DK, int DV, bool HG, bool NQK, bool EX>
+__device__ __forceinline__ void chunk_body(const ChunkParams& p, const int slot, const int h, unsigned char* smem)
 {
     using SH = ChunkShape<DK>;
     constexpr bool F32 = sizeof(Tin) == 4;
     using PR = Prec<F32>;
     using RC = Record<DK, DV, F32>;
     constexpr int NW = SH::NW, KSW = SH::KSW, NE = SH::NE, CG = SH::CG, PC = SH::PC;
-    extern __shared__ __align__(16) unsigned char smem[];
 
     const int H = p.H;
-    const int h = blockIdx.x % H;        // heads fastest: neighbouring workgroups share token rows
-    const int slot = blockIdx.x / H;
     int tok0, L;
     if (p.cu) {
         // the document whose slot range holds this slot (slot bases increase with d)
@@ -133,7 +150,9 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
     const Tin* __restrict__ k = static_cast<const Tin*>(p.k);
     const Tin* __restrict__ v = static_cast<const Tin*>(p.v);
 
-    const int tid = threadIdx.x;
+    // (the exact kernel runs this body in a loop: an opaque thread index keeps
+    // the lane-derived addresses from being hoisted out of it into registers)
+    const int tid = EX ? opaque_tid() : static_cast<int>(threadIdx.x);
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int R = w & 3;            // token tile of the prep and of the A/M rows
     const int cgi = w >> 2;         // channel group
@@ -206,6 +225,11 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
         sq += __shfl_xor(sq, 32, 64);
         if (gq == 0) nrm[cgi * 64 + t] = make_float2(sk, sq);
     }
+    bool outside = false;   // g > 0 anywhere in the lane's elements
+    if constexpr (!EX) {
+#pragma unroll
+        for (int i = 0; i < (HG ? 1 : NE); ++i) outside |= bs[i] > 0.f;
+    }
     // ---- 1. in-tile scans (log2 units), tile totals to LDS -----------------
     if constexpr (HG) {   // every channel carries the head's gate: one scan per lane
         const float b1 = row_scan_add(bs[0] * kLog2e);
@@ -220,6 +244,12 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
 #pragma unroll
         for (int i = 0; i < 2 * KSW; ++i) par[i] = row_scan_xor(par[i]);
     }
+    if constexpr (!EX) {   // envelope of the anchored factoring, one flag per wave
+#pragma unroll
+        for (int i = 0; i < NE; ++i) outside |= !(fabsf(bs[i]) <= kEnvelope);
+        const unsigned long long any = __ballot(outside);
+        if (l == 0) reinterpret_cast<uint32_t*>(smem + SH::L_FLAG)[w] = any != 0ull ? 1u : 0u;
+    }
     if (n == 15) {
 #pragma unroll
         for (int ks = 0; ks < KSW; ++ks) {
@@ -231,6 +261,14 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
         }
     }
     lds_sync();
+    if constexpr (!EX) {   // the flag decides for the whole workgroup
+        const uint32_t* fw = reinterpret_cast<const uint32_t*>(smem + SH::L_FLAG);
+        uint32_t f = 0;
+#pragma unroll
+        for (int x = 0; x < NW; ++x) f |= fw[x];
+        if (tid == 0) *reinterpret_cast<uint32_t*>(rec + RC::OFF_FLAG) = f;
+        if (f) return;
+    }
 
     // ---- 2. exponentials and operands -------------------------------------
     float ik = 1.f, iq = 1.f;   // 1 / ||k||, 1 / ||q|| (a zero vector stays zero)
@@ -245,6 +283,10 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
         iq = inv_norm(a.y);
     }
     typename PR::F8 rkB[KSW], rqB[KSW];   // row operands (B side of the A/M tiles)
+    float qfr[KSW][8];                    // exact path: the token's qf
+    float* const xk = reinterpret_cast<float*>(smem + SH::L_XK);
+    float* const xb = reinterpret_cast<float*>(smem + SH::L_XB);
+    constexpr int XP = SH::XP;
 #pragma unroll
     for (int ks = 0; ks < KSW; ++ks) {
         const int c0 = CG * cgi + 32 * ks + 8 * gq;
@@ -302,23 +344,35 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
         }
         CKDA_FENCE();
         float x[8];
+        if constexpr (!EX) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = fminf(fmaxf(b[e] - mh[e], -126.f), 126.f);
-        {   // column operand kf e^{m - b}
-            float ck[8];
+            for (int e = 0; e < 8; ++e) x[e] = fminf(fmaxf(b[e] - mh[e], -126.f), 126.f);
+            {   // column operand kf e^{m - b}
+                float ck[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ck[e] = kf[e] * __builtin_amdgcn_exp2f(-x[e]);
-            PR::store8(colk, t, c0, ck);
-        }
-        if (R < 2) {   // its cross-half version kf e^{m1 - b} for the half-1 rows
-            float ckf[8];
+                for (int e = 0; e < 8; ++e) ck[e] = kf[e] * __builtin_amdgcn_exp2f(-x[e]);
+                PR::store8(colk, t, c0, ck);
+            }
+            if (R < 2) {   // its cross-half version kf e^{m1 - b} for the half-1 rows
+                float ckf[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ckf[e] = kf[e] * __builtin_amdgcn_exp2f(fminf(m1[e] - b[e], 126.f));
-            PR::store8(colkf, t, c0, ckf);
+                for (int e = 0; e < 8; ++e) ckf[e] = kf[e] * __builtin_amdgcn_exp2f(fminf(m1[e] - b[e], 126.f));
+                PR::store8(colkf, t, c0, ckf);
+            }
+        } else {   // kf and b of the token, unscaled, for the entry-by-entry products
+            float4* pk = reinterpret_cast<float4*>(xk + t * XP + c0);
+            float4* pb = reinterpret_cast<float4*>(xb + t * XP + c0);
+            pk[0] = make_float4(kf[0], kf[1], kf[2], kf[3]);
+            pk[1] = make_float4(kf[4], kf[5], kf[6], kf[7]);
+            pb[0] = make_float4(b[0], b[1], b[2], b[3]);
+            pb[1] = make_float4(b[4], b[5], b[6], b[7]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qfr[ks][e] = qf[e];
         }
         CKDA_FENCE();
+        float e0[8];   // e^b
         {   // Qh = qf e^b to the record; d = P_L e^{b_L} from token 63
-            float qh[8], e0[8];
+            float qh[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 e0[e] = __builtin_amdgcn_exp2f(fminf(b[e], 126.f));
@@ -338,7 +392,7 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
             }
         }
         CKDA_FENCE();
-        {   // row operands kf e^{b - m}, qf e^{b - m} (registers)
+        if constexpr (!EX) {   // row operands kf e^{b - m}, qf e^{b - m} (registers)
             float rk[8], rq[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -361,11 +415,21 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
         const float m = (tg >= 4) ? (B0 + B1 + B2) : B0;
         const uint32_t pw = totp[c / 4] ^ totp[DK / 4 + c / 4] ^ totp[DK / 2 + c / 4] ^ totp[3 * (DK / 4) + c / 4];
         const uint32_t sgn = (pw << (24 - 8 * (c & 3))) & 0x80000000u;
-        const float f = __uint_as_float(
-            __float_as_uint(__builtin_amdgcn_exp2f(fminf(B0 + B1 + B2 + B3 - m, 126.f))) ^ sgn);
         float x[8];
+        if constexpr (!EX) {
+            const float f = __uint_as_float(
+                __float_as_uint(__builtin_amdgcn_exp2f(fminf(B0 + B1 + B2 + B3 - m, 126.f))) ^ sgn);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = f * PR::get1(colk, 8 * tg + j, c);
+            for (int j = 0; j < 8; ++j) x[j] = f * PR::get1(colk, 8 * tg + j, c);
+        } else {   // kf e^{b_L - b} with the exponent taken whole
+            const float bL = B0 + B1 + B2 + B3;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int tt = 8 * tg + j;
+                const float v = xk[tt * XP + c] * __builtin_amdgcn_exp2f(fminf(bL - xb[tt * XP + c], 126.f));
+                x[j] = __uint_as_float(__float_as_uint(v) ^ sgn);
+            }
+        }
         PR::gstore8(rec + RC::OFF_K, RC::K_PLANE, RC::K_ROW, c, 8 * tg, x);
     }
 
@@ -377,18 +441,98 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
         accA[I] = f32x4{0.f, 0.f, 0.f, 0.f};
         accM[I] = accA[I];
     }
+    if constexpr (!EX) {
 #pragma unroll
-    for (int ks = 0; ks < KSW; ++ks) {
-        const int c0 = CG * cgi + 32 * ks + 8 * gq;
+        for (int ks = 0; ks < KSW; ++ks) {
+            const int c0 = CG * cgi + 32 * ks + 8 * gq;
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                if (I <= R) {
+                    const bool cross = (R >= 2) && (I < 2);
+                    const typename PR::F8 a = PR::load8(cross ? colkf : colk, 16 * I + n, c0);
+                    accA[I] = PR::mma8(a, rkB[ks], accA[I]);
+                    accM[I] = PR::mma8(a, rqB[ks], accM[I]);
+                }
+            }
+        }
+    } else {
+        // exact path: the row token t against tokens 16I .. 16I + 15, each
+        // entry sum_c kf_tc kf_ic e^{b_tc - b_ic} (and qf_tc for M) with the
+        // exponent taken whole, over the lane's channels; then summed over
+        // the four lanes that hold the row's other channel octets.  Entries
+        // above the diagonal come out as garbage and are masked below.  Eight
+        // columns at a time: lane (n, g) keeps columns 16I + 4g .. +3 (the
+        // C/D layout), so half hj serves the lanes with g = 2hj, 2hj + 1.
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             if (I <= R) {
-                const bool cross = (R >= 2) && (I < 2);
-                const typename PR::F8 a = PR::load8(cross ? colkf : colk, 16 * I + n, c0);
-                accA[I] = PR::mma8(a, rkB[ks], accA[I]);
-                accM[I] = PR::mma8(a, rqB[ks], accM[I]);
+#pragma unroll
+                for (int hj = 0; hj < 2; ++hj) {
+                    float pa[8], pm[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        pa[j] = 0.f;
+                        pm[j] = 0.f;
+                    }
+#pragma unroll
+                    for (int ks = 0; ks < KSW; ++ks) {
+                        const int c0 = CG * cgi + 32 * ks + 8 * gq;
+                        float kr[8], br[8];
+                        {
+                            const float4* pk = reinterpret_cast<const float4*>(xk + t * XP + c0);
+                            const float4* pb = reinterpret_cast<const float4*>(xb + t * XP + c0);
+                            const float4 k0 = pk[0], k1 = pk[1], b0 = pb[0], b1 = pb[1];
+                            kr[0] = k0.x; kr[1] = k0.y; kr[2] = k0.z; kr[3] = k0.w;
+                            kr[4] = k1.x; kr[5] = k1.y; kr[6] = k1.z; kr[7] = k1.w;
+                            br[0] = b0.x; br[1] = b0.y; br[2] = b0.z; br[3] = b0.w;
+                            br[4] = b1.x; br[5] = b1.y; br[6] = b1.z; br[7] = b1.w;
+                        }
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const int i = 16 * I + 8 * hj + j;
+                            const float4* pk = reinterpret_cast<const float4*>(xk + i * XP + c0);
+                            const float4* pb = reinterpret_cast<const float4*>(xb + i * XP + c0);
+                            const float4 k0 = pk[0], k1 = pk[1], b0 = pb[0], b1 = pb[1];
+                            const float ki[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+                            const float bi[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                const float u = ki[e] * __builtin_amdgcn_exp2f(fminf(br[e] - bi[e], 126.f));
+                                pa[j] = fmaf(kr[e], u, pa[j]);
+                                pm[j] = fmaf(qfr[ks][e], u, pm[j]);
+                            }
+                            CKDA_FENCE();   // one column's loads in flight at a time
+                        }
+                    }
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        pa[j] += __shfl_xor(pa[j], 16, 64);
+                        pa[j] += __shfl_xor(pa[j], 32, 64);
+                        pm[j] += __shfl_xor(pm[j], 16, 64);
+                        pm[j] += __shfl_xor(pm[j], 32, 64);
+                    }
+                    if ((gq >> 1) == hj) {
+                        const int o = 4 * (gq & 1);
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) {
+                            accA[I][jj] = o ? pa[4 + jj] : pa[jj];
+                            accM[I][jj] = o ? pm[4 + jj] : pm[jj];
+                        }
+                    }
+                }
             }
         }
+        // kf e^b itself: the right-hand side of W, with no anchor
+#pragma unroll
+        for (int ks = 0; ks < KSW; ++ks) {
+            const int c0 = CG * cgi + 32 * ks + 8 * gq;
+            float rk[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                rk[e] = xk[t * XP + c0 + e] * __builtin_amdgcn_exp2f(fminf(xb[t * XP + c0 + e], 126.f));
+            rkB[ks] = PR::regs8(f32x4{rk[0], rk[1], rk[2], rk[3]}, f32x4{rk[4], rk[5], rk[6], rk[7]});
+        }
+        lds_sync();   // the partial-tile area overlaps kf and b
     }
     f32x4* const part = reinterpret_cast<f32x4*>(smem + SH::L_PART);
     if (SH::NCG > 1 && cgi == 1) {
@@ -523,8 +667,8 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
             // kf e^b = (kf e^{b - m}) e^m, m the anchor of the token's half
             const int c = 16 * ct + n;
             const float m0 = totb[c], m1 = m0 + totb[DK + c] + totb[2 * DK + c];
-            const float em0 = __builtin_amdgcn_exp2f(fminf(m0, 126.f));
-            const float em1 = __builtin_amdgcn_exp2f(fminf(m1, 126.f));
+            const float em0 = EX ? 1.f : __builtin_amdgcn_exp2f(fminf(m0, 126.f));
+            const float em1 = EX ? 1.f : __builtin_amdgcn_exp2f(fminf(m1, 126.f));
             float rhs[4][4];
 #pragma unroll
             for (int J = 0; J < 4; ++J)
@@ -542,6 +686,40 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(
     }
 }
 
+// one workgroup per (chunk slot, head); second bound: waves per SIMD (two
+// 8-wave workgroups per CU -> 4, at most 128 VGPRs)
+template <typename Tin, int DK, int DV, bool HG, bool NQK>
+__global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(ChunkParams p)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    // heads fastest: neighbouring workgroups share token rows
+    chunk_body<Tin, DK, DV, HG, NQK, false>(p, blockIdx.x / p.H, blockIdx.x % p.H, smem);
+}
+
+// The exact path over the records the fast kernel flagged: workgroup x looks
+// at chunk-heads x*per .. x*per + per - 1 (per <= 64; record index = slot * H
+// + head), whose flags one wave-wide load gathers, and redoes the flagged ones
+// in turn.  With nothing flagged the launch reads one word per chunk-head.
+template <typename Tin, int DK, int DV, bool HG, bool NQK>
+__global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_exact_kernel(ChunkParams p, int nch, int per)
+{
+    using RC = Record<DK, DV, sizeof(Tin) == 4>;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int c0 = blockIdx.x * per;
+    const int l = threadIdx.x & 63;
+    bool f = false;
+    if (l < per && c0 + l < nch)
+        f = *reinterpret_cast<const uint32_t*>(p.ws + static_cast<size_t>(c0 + l) * RC::BYTES + RC::OFF_FLAG) != 0u;
+    unsigned long long mask = __ballot(f);   // the same in every wave
+    while (mask != 0ull) {
+        const int j = __builtin_ctzll(mask);
+        mask &= mask - 1ull;
+        const int ch = c0 + j;
+        chunk_body<Tin, DK, DV, HG, NQK, true>(p, ch / p.H, ch % p.H, smem);
+        lds_sync();   // before the next chunk-head reuses LDS
+    }
+}
+
 template <typename Tin, int DK, int DV, bool HG, bool NQK>
 static hipError_t launch_chunk_t(const FwdArgs& A, int nslots, hipStream_t stream) {
     using SH = ChunkShape<DK>;
@@ -555,6 +733,17 @@ static hipError_t launch_chunk_t(const FwdArgs& A, int nslots, hipStream_t strea
                                        hipFuncAttributeMaxDynamicSharedMemorySize, SH::LDS);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(SH::NW * 64), SH::LDS, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // exact path: about 512 workgroups (two per CU), each over up to 64 chunk-heads
+    auto kx = ckda_chunk_exact_kernel<Tin, DK, DV, HG, NQK>;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kx), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            SH::LDS_EX);
+    if (e != hipSuccess) return e;
+    const int per = static_cast<int>(grid > 512 * 64LL ? 64 : (grid + 511) / 512);
+    const long long gx = (grid + per - 1) / per;
+    hipLaunchKernelGGL(kx, dim3(static_cast<unsigned>(gx)), dim3(SH::NW * 64), SH::LDS_EX, stream, p,
+                       static_cast<int>(grid), per);
     return hipGetLastError();
 }
 

@@ -15,6 +15,7 @@
 //   u   = X^{-1} Diag(beta) V                  [64][DV]  float32, stored as
 //         16x16 tiles (J, vt) in the MFMA C/D lane layout: element
 //         (16J + 4g + i, 16vt + n) at ((J*DV/16 + vt)*64 + 16g + n)*4 + i
+//   flag                                       uint32 (16-byte slot)
 //
 // so that one chunk's state step is
 //   U = u - W S,   O = Qh S + M U,   S <- Diag(d) S + KbT U.
@@ -50,7 +51,10 @@ struct Record {
     static constexpr size_t OFF_D = OFF_M + NP * M_PLANE;
     static constexpr size_t OFF_U = OFF_D + DK * 4;
     static constexpr size_t STAGED = OFF_U;   // W .. d: staged whole by the state kernel
-    static constexpr size_t BYTES = OFF_U + static_cast<size_t>(64) * DV * 4;
+    // one 32-bit word: nonzero when the chunk's gates leave the anchored
+    // factoring's range and the record comes from the exact path (chunk.hip)
+    static constexpr size_t OFF_FLAG = OFF_U + static_cast<size_t>(64) * DV * 4;
+    static constexpr size_t BYTES = OFF_FLAG + 16;
     static_assert(OFF_U % 16 == 0 && BYTES % 16 == 0, "16-byte units");
 };
 

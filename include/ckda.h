@@ -35,10 +35,18 @@
  *    states (B*H or N*H) must each stay below 2^31; larger problems fail
  *    with CKDA_ERR_UNSUPPORTED before anything is enqueued.
  *  - Outputs must not alias inputs (except the in/out decode state).
- *  - Accuracy: the intra-chunk products factor exp(b_r - b_i) through
- *    anchors at the middle of each half chunk, so every run of 16
- *    consecutive log-gates inside a chunk half should sum to more than -80
- *    per channel (an average |alpha| above ~0.007).  g must be finite.
+ *  - Gate range: g must be finite.  The forward calls are exact over the
+ *    pages' whole range (g <= 0, i.e. |alpha| <= 1, down to any magnitude):
+ *    the intra-chunk products factor exp(b_r - b_i) through anchors inside
+ *    each half chunk while every 16-token run of log-gates in every channel
+ *    stays above about -66.5 (an average |alpha| above about 0.016), and a
+ *    chunk that leaves that range (or has any g > 0) is recomputed entry by
+ *    entry with the exponent taken whole.  g > 0 (|alpha| > 1) lies outside
+ *    the pages' range; it is computed exactly while nothing overflows.
+ *    The backward (ckda_bwd, ckda_bwd_varlen) factors through one anchor per
+ *    chunk: every 32-token run of log-gates in every channel must stay above
+ *    about -80 (an average |alpha| above about 0.08); below that its
+ *    gradients are not accurate.
  */
 #ifndef CKDA_H
 #define CKDA_H

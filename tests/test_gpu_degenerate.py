@@ -1,10 +1,14 @@
 """Degenerate and extreme inputs of the method on the GPU, against the oracle.
 
-- Gates at the documented edge: the forward factors e^{b_r - b_i} through
-  anchors at the middle of each half chunk, so runs of 16 log-gates may sum
-  to no less than -80 per channel; the backward anchors at the chunk middle
-  and needs 32-token partial sums above -80.  Both edges are run here, on
-  half of the channels, the other half keeping ordinary gates.
+- Deep gates (|alpha| far below 1, the whole of the pages' range [-1, 1]):
+  the forward's fast path factors e^{b_r - b_i} through anchors inside each
+  half chunk and is used while every 16-token tile's in-tile log-gate prefix
+  stays within 96 (log2 units, about 66.5 nat); a chunk beyond that takes
+  the exact path, which forms the intra-chunk products entry by entry.  Both
+  sides of that boundary are run, on half of the channels, the other half
+  keeping ordinary gates, with chunks of both kinds in one call.  The
+  backward anchors at the chunk middle and needs 32-token partial sums above
+  -80.
 - beta = 0: nothing is written; the initial state only decays and rotates
   sign (o_t = scale (Diag(alpha_1 ... alpha_t) S0)^T q_t).
 - beta = 2 with |alpha| = 1 (g = 0) and random signs: every transition is
@@ -73,15 +77,90 @@ def check_bwd(w, dtype, seed, scale=1.0):
     assert e < TOL[dtype]
 
 
-@pytest.mark.parametrize("dtype,DK,DV", [("f32", 64, 64), ("bf16", 128, 128)])
-def test_forward_gates_at_the_anchor_limit(dtype, DK, DV):
-    """Even channels decay by e^-4.9 every token (16-token runs sum to -78.4),
-    odd channels keep the workload's gates; signs as drawn."""
+@pytest.mark.parametrize("dtype,DK,DV,gdeep", [("f32", 64, 64, -4.0), ("bf16", 128, 128, -4.0),
+                                              ("f32", 64, 64, -4.9), ("bf16", 128, 128, -4.9),
+                                              ("f32", 128, 128, -8.0), ("bf16", 128, 128, -8.0),
+                                              ("f32", 64, 128, -40.0), ("bf16", 128, 64, -40.0),
+                                              ("f32", 32, 32, -40.0)])
+def test_forward_deep_gates(dtype, DK, DV, gdeep):
+    """Even channels decay by e^gdeep every token, odd channels keep the
+    workload's gates; signs as drawn.  16-token runs of the even channels sum
+    to 16 gdeep: -64 (inside the fast path's envelope of about -66.5), -78.4,
+    -128 and -640 (beyond it: the exact path)."""
     require_gpu()
-    banner(f"fwd strong gates {dtype} DK={DK} DV={DV}")
+    banner(f"fwd deep gates g={gdeep} {dtype} DK={DK} DV={DV}")
     w = I.make_forward(2, 200, 2, DK, DV, dtype, seed=501, h0_std=0.3)
-    w.tok.g[..., 0::2] = -4.9
+    w.tok.g[..., 0::2] = gdeep
     check_fwd(w, dtype, scale=0.8)
+
+
+@pytest.mark.parametrize("dtype,DK,DV", [("f32", 64, 64), ("bf16", 128, 128)])
+def test_forward_deep_bursts_inside_chunks(dtype, DK, DV):
+    """Tokens 20..27 of every second chunk decay by e^-30 on even channels,
+    the rest keeps the workload's gates: pairs across the burst vanish, pairs
+    on either side keep O(1) factors between large cumulative log-gates, and
+    flagged and unflagged chunks meet in one state pass."""
+    require_gpu()
+    banner(f"fwd deep bursts {dtype} DK={DK} DV={DV}")
+    w = I.make_forward(2, 300, 2, DK, DV, dtype, seed=512, h0_std=0.3)
+    for c0 in range(64, 300, 128):
+        w.tok.g[:, c0 + 20:c0 + 28, :, 0::2] = -30.0
+    check_fwd(w, dtype, scale=0.8)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_forward_positive_gates(dtype):
+    """g > 0 (|alpha| > 1) lies outside the pages' range; such chunks take
+    the exact path, which stays exact while nothing overflows: a few tokens
+    with g = +0.4 on some channels."""
+    require_gpu()
+    banner(f"fwd positive gates {dtype}")
+    w = I.make_forward(1, 200, 2, 64, 64, dtype, seed=513, h0_std=0.3)
+    w.tok.g[:, 10::37, :, 0::3] = 0.4
+    check_fwd(w, dtype, scale=0.8)
+
+
+@pytest.mark.parametrize("dtype,DK,DV", [("f32", 64, 64), ("bf16", 128, 128)])
+def test_varlen_deep_gates(dtype, DK, DV):
+    """Ragged documents, the second and fourth with e^-40 decay on even
+    channels (exact path), the others ordinary (fast path)."""
+    torch = require_gpu()
+    from gated_delta_rule_sign_amd import ckda
+    banner(f"varlen deep gates {dtype} DK={DK} DV={DV}")
+    lens = [70, 129, 1, 200, 64]
+    cu = I.cu_from_lengths(lens)
+    Tt, H = int(cu[-1]), 2
+    rng = np.random.default_rng(514)
+    tok = I.draw_tokens(rng, (Tt,), H, DK, DV, dtype)
+    for n in (1, 3):
+        tok.g[cu[n]:cu[n + 1], :, 0::2] = -40.0
+    h0 = I.draw_state(rng, (len(lens), H, DK, DV), 0.3)
+    d = tok_to_dev(tok)
+    o, ht = ckda.fwd_varlen(**d, cu_seqlens=torch.from_numpy(cu), scale=0.9, h0=dev_tensor(h0))
+    torch.cuda.synchronize()
+    o_ref, ht_ref = oracle.varlen(**tok.f64(), cu_seqlens=cu, scale=0.9, h0=h0.astype(np.float64))
+    e_o, e_h = rel_max(host(o), o_ref), rel_max(host(ht), ht_ref)
+    print(f"  o {e_o:.2e}  ht {e_h:.2e}")
+    assert e_o < TOL[dtype] and e_h < TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_head_gate_deep(dtype):
+    """One gate per (token, head), e^-40 on the first head, ordinary on the
+    second."""
+    require_gpu()
+    banner(f"fwd head gate deep {dtype}")
+    w = I.make_forward(1, 200, 2, 64, 64, dtype, seed=515, h0_std=0.3, gate="head")
+    w.tok.g[:, :, 0] = -40.0
+    o, ht, _ = run_fwd(w, 0.8)
+    tok = w.tok.f64()
+    DK = w.tok.q.shape[-1]
+    tok["g"] = np.repeat(tok["g"][..., None], DK, axis=-1)
+    tok["s"] = np.repeat(tok["s"][..., None], DK, axis=-1)
+    o_ref, ht_ref = oracle.fwd(**tok, scale=0.8, h0=w.h0.astype(np.float64))
+    e_o, e_h = rel_max(host(o), o_ref), rel_max(host(ht), ht_ref)
+    print(f"  o {e_o:.2e}  ht {e_h:.2e}")
+    assert e_o < TOL[dtype] and e_h < TOL[dtype]
 
 
 @pytest.mark.parametrize("dtype,DK,DV", [("f32", 64, 64), ("bf16", 128, 128)])
