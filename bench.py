@@ -45,15 +45,18 @@ DEC_BYTES_PER_HEAD_STEP = 2 * 128 * 128 * 4 + 3 * 256 + 512 + 128 + 2 * 128 + 4 
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ckda_fwd_traffic__layer_bf16.json")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_traffic__decode_b256.json")
 
 
-def measured_traffic():
-    """HBM bytes per forward call from the committed FETCH_SIZE / WRITE_SIZE
-    runs (calibrated on a plain copy), or None when the forward kernel sources
-    have changed since those counters were taken."""
+def measured_traffic(path=None):
+    """HBM bytes per call (forward, the default record) or per step (decode)
+    from the committed FETCH_SIZE / WRITE_SIZE runs (calibrated on a plain
+    copy), or None when the kernel sources have changed since those counters
+    were taken."""
     import hashlib
+    path = TRAFFIC_FILE if path is None else path
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(path))
     except (OSError, ValueError):
         return None
     h = hashlib.sha256()
@@ -63,6 +66,27 @@ def measured_traffic():
     if h.hexdigest() != rec.get("sources_sha256"):
         return None
     return float(rec["traffic_bytes_per_call"])
+
+
+MFMA_FILE = os.path.join(ROOT, "profiles", "ckda_fwd_mfma__layer_bf16.json")
+
+
+def measured_mfma():
+    """Executed bf16 matrix-core flops per forward call and per kernel
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 from the committed counter run), or
+    None when the forward kernel sources have changed since then."""
+    import hashlib
+    try:
+        rec = json.load(open(MFMA_FILE))
+    except (OSError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in rec.get("sources", []):
+        with open(os.path.join(ROOT, "gated_delta_rule_sign_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != rec.get("sources_sha256"):
+        return None
+    return rec
 
 
 def log(msg):
@@ -206,8 +230,34 @@ def bench_decode(torch, nsteps=512, distinct=64):
     wall, per = time_kernel_launches(torch, step, nsteps, 8)
     per_step = wall / nsteps
     bytes_step = N * H * DEC_BYTES_PER_HEAD_STEP
+    # the same nsteps steps captured in one graph and replayed: the host
+    # launches nothing per step, so wall time per step is the kernels' own
+    # rate (plus the graph's dispatch gaps)
+    log("timing decode as one graph of all steps")
+    it[0] = 0
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm the allocator and the library on the capture stream
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    it[0] = 0
+    with torch.cuda.graph(graph):
+        for _ in range(nsteps):
+            step()
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = 3
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_step = (time.perf_counter() - t0) * 1e3 / (reps * nsteps)
     return dict(ms_per_step=per_step, launch_ms=float(np.mean(per)), bytes_per_step=bytes_step,
                 gbs=bytes_step / (float(np.mean(per)) * 1e-3) / 1e9,
+                graph_ms_per_step=graph_step, graph_gbs=bytes_step / (graph_step * 1e-3) / 1e9,
+                wall_gbs=bytes_step / (per_step * 1e-3) / 1e9,
                 seq_steps_per_s=N / (per_step * 1e-3), steps=nsteps)
 
 
@@ -361,6 +411,14 @@ def main():
 
     achieved = fw["bytes"] / (fw["launch_ms"] * 1e-3) / 1e9
     value = fw["tokens"] / (fw["ms"] * 1e-3)
+    mf = measured_mfma()
+    mfma_exec = None if mf is None else {
+        "frac": mf["executed_bf16_flops_per_call"] / (fw["launch_ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "executed_tflop_per_call": mf["executed_bf16_flops_per_call"] / 1e12,
+        "basis": "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 per call (committed counter run), over this run's mean "
+                 "launch time, against 2.5 PFLOP/s; includes the hi/lo split's three products per pair",
+        "busy_frac_per_kernel": {k: v["mfma_busy_frac"] for k, v in mf["kernels"].items()
+                                 if v["executed_bf16_flops"] > 0}}
     line = {
         "metric": METRIC,
         "value": value,
@@ -384,9 +442,18 @@ def main():
                      "algorithmic_bytes_per_launch": fw["bytes"],
                      "avg_launch_ms": fw["launch_ms"],
                      "workspace_bytes": fw["workspace_bytes"],
-                     "mfma_algorithmic_frac": fw["flops"] / (fw["launch_ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+                     "mfma_algorithmic_frac": fw["flops"] / (fw["launch_ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                     "mfma_executed_frac": None if mfma_exec is None else mfma_exec["frac"],
+                     "mfma_executed": mfma_exec},
         "decode": {"workload": "decode_b256: 256 seqs x 16 heads, dk=dv=128, 512 steps",
                    "unit": "GB/s", "value": dec["gbs"], "frac_of_hbm_peak": dec["gbs"] / HBM_PEAK_GBS,
+                   "basis": "mean HIP-event time of one step's kernel",
+                   "graph_gbs": dec["graph_gbs"], "graph_frac_of_hbm_peak": dec["graph_gbs"] / HBM_PEAK_GBS,
+                   "graph_ms_per_step": dec["graph_ms_per_step"],
+                   "graph_basis": "wall time of the 512 steps captured in one HIP graph and replayed",
+                   "wall_gbs": dec["wall_gbs"],
+                   "wall_basis": "wall time of 512 host-launched steps (launch gaps included)",
+                   "traffic": measured_traffic(DECODE_TRAFFIC_FILE),
                    "ms_per_step": dec["ms_per_step"], "seq_steps_per_s": dec["seq_steps_per_s"],
                    "algorithmic_bytes_per_step": dec["bytes_per_step"]},
         "backward": {"workload": "layer_bwd: layer_bf16 shapes, bf16 upstream gradient, checkpointed states",

@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 
 #include "ckda_launch.h"
 
@@ -92,6 +93,42 @@ ckda_status_t check_cu(int N, int T_total, const int32_t* cu) {
     return CKDA_OK;
 }
 
+// A device buffer as the host sees it: [p, p + n) bytes.
+struct Span {
+    const void* p;
+    size_t n;
+    const char* name;
+};
+
+bool overlaps(const Span& a, const Span& b) {
+    if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+// Outputs (the workspace among them) must not overlap an input or each other:
+// the kernels read inputs after other workgroups have started writing.
+ckda_status_t check_no_alias(std::initializer_list<Span> outs, std::initializer_list<Span> ins) {
+    for (const Span* o = outs.begin(); o != outs.end(); ++o) {
+        for (const Span& i : ins)
+            if (overlaps(*o, i)) return fail(CKDA_ERR_UNSUPPORTED, "output '%s' overlaps input '%s'", o->name, i.name);
+        for (const Span* o2 = o + 1; o2 != outs.end(); ++o2)
+            if (overlaps(*o, *o2)) return fail(CKDA_ERR_UNSUPPORTED, "outputs '%s' and '%s' overlap", o->name, o2->name);
+    }
+    return CKDA_OK;
+}
+
+// byte sizes of the token tensors of one call: n token-heads
+struct TokBytes {
+    size_t qk, v, g, s, beta, o;
+    TokBytes(long long n, int DK, int DV, bool bf16, bool head_gate) {
+        const size_t es = bf16 ? 2 : 4, nn = static_cast<size_t>(n);
+        qk = nn * DK * es; v = nn * DV * es;
+        g = nn * (head_gate ? 1 : DK) * 4; s = nn * (head_gate ? 1 : DK);
+        beta = nn * 4; o = nn * DV * 4;
+    }
+};
+
 ckda_status_t check_varlen_sizes(int N, int T_total, int H) {
     if (too_big(T_total, H)) return fail(CKDA_ERR_UNSUPPORTED, "tensor too large");
     if (static_cast<long long>(N) * H >= (1LL << 31) / 2) return fail(CKDA_ERR_UNSUPPORTED, "too many documents");
@@ -165,11 +202,15 @@ ckda_status_t ckda_set_segment_chunks(int G) {
     return ok();
 }
 
-ckda_status_t ckda_fwd_chunked(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype,
-                               ckda_flags_t flags, const void* q, const void* k, const void* v,
-                               const float* g, const int8_t* s, const float* beta, float scale,
-                               const float* h0, float* o, float* ht, float* h_ckpt, void* workspace,
-                               size_t workspace_bytes, ckda_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// ckda_fwd_chunked: checks, then the chunk-local and state passes.
+ckda_status_t fwd_chunked_common(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype, ckda_flags_t flags,
+                                 const void* q, const void* k, const void* v, const float* g, const int8_t* s,
+                                 const float* beta, float scale, const float* h0, float* o, float* ht,
+                                 float* h_ckpt, void* workspace, size_t workspace_bytes, ckda_stream_t stream) {
     CKDA_TRY(check_dtype(in_dtype));
     CKDA_TRY(check_flags(flags));
     if (B < 0 || T < 0 || H < 0) return fail(CKDA_ERR_SHAPE, "negative size (B=%d, T=%d, H=%d)", B, T, H);
@@ -194,7 +235,28 @@ ckda_status_t ckda_fwd_chunked(int B, int T, int H, int DK, int DV, ckda_dtype_t
     a.q = q; a.k = k; a.v = v; a.g = g; a.s = s; a.beta = beta; a.scale = scale;
     a.h0 = h0; a.o = o; a.ht = ht; a.h_ckpt = h_ckpt; a.cu = nullptr; a.cu_host = nullptr; a.ndocs = 0;
     a.ws = workspace; a.ws_bytes = workspace_bytes;
+    {
+        const TokBytes tb(static_cast<long long>(B) * T * H, DK, DV, a.bf16, a.head_gate);
+        const size_t st = static_cast<size_t>(B) * H * DK * DV * 4;
+        CKDA_TRY(check_no_alias({{o, tb.o, "o"}, {ht, st, "ht"}, {h_ckpt, static_cast<size_t>(nslots) * H * DK * DV * 4, "h_ckpt"},
+                                 {workspace, workspace_bytes, "workspace"}},
+                                {{q, tb.qk, "q"}, {k, tb.qk, "k"}, {v, tb.v, "v"}, {g, tb.g, "g"}, {s, tb.s, "s"},
+                                 {beta, tb.beta, "beta"}, {h0, st, "h0"}}));
+    }
     return hip_status(ckda::launch_fwd(a, nslots, static_cast<hipStream_t>(stream)), "ckda_fwd_chunked launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+ckda_status_t ckda_fwd_chunked(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype,
+                               ckda_flags_t flags, const void* q, const void* k, const void* v,
+                               const float* g, const int8_t* s, const float* beta, float scale,
+                               const float* h0, float* o, float* ht, float* h_ckpt, void* workspace,
+                               size_t workspace_bytes, ckda_stream_t stream) {
+    return fwd_chunked_common(B, T, H, DK, DV, in_dtype, flags, q, k, v, g, s, beta, scale, h0, o, ht, h_ckpt,
+                              workspace, workspace_bytes, stream);
 }
 
 ckda_status_t ckda_fwd_varlen(int N, int T_total, const int32_t* cu, const int32_t* cu_dev, int H,
@@ -226,6 +288,14 @@ ckda_status_t ckda_fwd_varlen(int N, int T_total, const int32_t* cu, const int32
     a.q = q; a.k = k; a.v = v; a.g = g; a.s = s; a.beta = beta; a.scale = scale;
     a.h0 = h0; a.o = o; a.ht = ht; a.h_ckpt = h_ckpt;
     a.cu = cu_dev; a.cu_host = cu; a.ndocs = N; a.ws = workspace; a.ws_bytes = workspace_bytes;
+    {
+        const TokBytes tb(static_cast<long long>(T_total) * H, DK, DV, a.bf16, a.head_gate);
+        const size_t st = static_cast<size_t>(N) * H * DK * DV * 4;
+        CKDA_TRY(check_no_alias({{o, tb.o, "o"}, {ht, st, "ht"}, {h_ckpt, static_cast<size_t>(nslots) * H * DK * DV * 4, "h_ckpt"},
+                                 {workspace, workspace_bytes, "workspace"}},
+                                {{q, tb.qk, "q"}, {k, tb.qk, "k"}, {v, tb.v, "v"}, {g, tb.g, "g"}, {s, tb.s, "s"},
+                                 {beta, tb.beta, "beta"}, {h0, st, "h0"}, {cu_dev, (static_cast<size_t>(N) + 1) * 4, "cu_seqlens"}}));
+    }
     return hip_status(ckda::launch_fwd(a, nslots, static_cast<hipStream_t>(stream)), "ckda_fwd_varlen launch");
 }
 
@@ -246,6 +316,14 @@ ckda_status_t ckda_decode_step(int N, int H, int DK, int DV, ckda_dtype_t in_dty
     ckda::DecodeArgs a{N, H, DK, DV, in_dtype == CKDA_BF16, (flags & CKDA_GATE_HEAD) != 0,
                        (flags & CKDA_QK_L2NORM) != 0, q, k, v, g, s, beta,
                        scale, state, sign_prod, o};
+    {   // state and sign_prod are updated in place: outputs here
+        const TokBytes tb(static_cast<long long>(N) * H, DK, DV, a.bf16, a.head_gate);
+        const size_t st = static_cast<size_t>(N) * H * DK * DV * 4;
+        CKDA_TRY(check_no_alias({{o, tb.o, "o"}, {state, st, "state"},
+                                 {sign_prod, static_cast<size_t>(N) * H * DK, "sign_prod"}},
+                                {{q, tb.qk, "q"}, {k, tb.qk, "k"}, {v, tb.v, "v"}, {g, tb.g, "g"}, {s, tb.s, "s"},
+                                 {beta, tb.beta, "beta"}}));
+    }
     return hip_status(ckda::launch_decode(a, static_cast<hipStream_t>(stream)), "ckda_decode_step launch");
 }
 
@@ -289,6 +367,20 @@ ckda_status_t bwd_common(ckda::BwdArgs& a, int nslots, bool any_tokens, const vo
     }
     a.ws = const_cast<void*>(workspace);
     a.ws_bytes = workspace_bytes;
+    {
+        const long long n = static_cast<long long>(a.B) * a.T * a.H;
+        const TokBytes tb(n, a.DK, a.DV, a.bf16, a.head_gate);
+        const size_t st = static_cast<size_t>(a.cu ? a.ndocs : a.B) * a.H * a.DK * a.DV * 4;
+        const size_t ck = static_cast<size_t>(nslots) * a.H * a.DK * a.DV * 4;
+        const size_t dob = tb.v;   // dout: the input dtype, [.., DV]
+        CKDA_TRY(check_no_alias({{a.dq, static_cast<size_t>(n) * a.DK * 4, "dq"}, {a.dk, static_cast<size_t>(n) * a.DK * 4, "dk"},
+                                 {a.dv, tb.o, "dv"}, {a.dg, tb.g, "dg"}, {a.dbeta, tb.beta, "dbeta"},
+                                 {a.dh0, st, "dh0"}, {workspace, workspace_bytes, "workspace"}},
+                                {{a.q, tb.qk, "q"}, {a.k, tb.qk, "k"}, {a.v, tb.v, "v"}, {a.g, tb.g, "g"}, {a.s, tb.s, "s"},
+                                 {a.beta, tb.beta, "beta"}, {a.h0, st, "h0"}, {a.h_ckpt, ck, "h_ckpt"},
+                                 {a.dout, dob, "dout"}, {a.dht, st, "dht"},
+                                 {a.cu, a.cu ? (static_cast<size_t>(a.ndocs) + 1) * 4 : 0, "cu_seqlens"}}));
+    }
     return hip_status(ckda::launch_bwd(a, nslots, static_cast<hipStream_t>(stream)), what);
 }
 

@@ -1587,7 +1587,7 @@ hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t st) {
         };
         const int BVr = DV < 64 ? DV : 64;
         p.G = plan_segments(chain_chunks(a.cu_host, varlen, a.ndocs, a.B, a.T), a.H, DV / BVr,
-                            (DK + BVr - 1) / BVr, kReverseCost, fits);
+                            (DK + BVr - 1) / BVr, kReverseCost, device_cus(st), fits);
         if (p.G > 0) {
             p.nsslots = seg_slots(varlen, a.B, a.T, a.ndocs, p.G);
             float* sb = reinterpret_cast<float*>(static_cast<unsigned char*>(a.ws) + seg_off);

@@ -15,7 +15,7 @@
 //   u   = X^{-1} Diag(beta) V                  [64][DV]  float32, stored as
 //         16x16 tiles (J, vt) in the MFMA C/D lane layout: element
 //         (16J + 4g + i, 16vt + n) at ((J*DV/16 + vt)*64 + 16g + n)*4 + i
-//   flag                                       uint32 (16-byte slot)
+//   flag                                       uint32, then padding to 256 bytes
 //
 // so that one chunk's state step is
 //   U = u - W S,   O = Qh S + M U,   S <- Diag(d) S + KbT U.
@@ -52,10 +52,13 @@ struct Record {
     static constexpr size_t OFF_U = OFF_D + DK * 4;
     static constexpr size_t STAGED = OFF_U;   // W .. d: staged whole by the state kernel
     // one 32-bit word: nonzero when the chunk's gates leave the anchored
-    // factoring's range and the record comes from the exact path (chunk.hip)
+    // factoring's range and the record comes from the exact path (chunk.hip).
+    // The record is then padded to a multiple of 256 bytes, so every record
+    // starts on a cache-line boundary: a record that straddles lines turns
+    // its stores into partial-line writes.
     static constexpr size_t OFF_FLAG = OFF_U + static_cast<size_t>(64) * DV * 4;
-    static constexpr size_t BYTES = OFF_FLAG + 16;
-    static_assert(OFF_U % 16 == 0 && BYTES % 16 == 0, "16-byte units");
+    static constexpr size_t BYTES = (OFF_FLAG + 4 + 255) / 256 * 256;
+    static_assert(OFF_U % 16 == 0 && OFF_FLAG % 16 == 0, "16-byte units");
 };
 
 // chunk slot of chunk j of document d (varlen): floor(cu[d]/64) + d + j.

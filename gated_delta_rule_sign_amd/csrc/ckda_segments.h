@@ -147,7 +147,9 @@ inline std::vector<int> chain_chunks(const int32_t* cu_host, bool varlen, int nd
     return nch;
 }
 
-int device_cus();   // compute units of the current device
+// compute units of the device that `stream` belongs to (the current device
+// for the null stream)
+int device_cus(hipStream_t stream);
 
 // Per-pass constants of the cost model below, in units of one chunk-step of
 // a workgroup that has its CU to itself.
@@ -165,16 +167,16 @@ struct SegCost {
 // no_out of a full step) + phase 3 (every segment: W again, in items of at
 // most G chunks) + the scan + launch gaps.  The segment plan is taken when
 // it is below 0.8 of the whole-chain estimate.  fits(G): the workspace holds
-// the segment buffers.
+// the segment buffers; cus: compute units of the GPU that runs the passes.
 template <typename Fits>
-int plan_segments(const std::vector<int>& nch, int H, int nslice, int ntrans, const SegCost& c, Fits fits) {
+int plan_segments(const std::vector<int>& nch, int H, int nslice, int ntrans, const SegCost& c, int cus, Fits fits) {
     const int forced = segment_chunks();
     if (forced < 0 || H == 0 || nch.empty()) return 0;
     int maxn = 0;
     double tot = 0;
     for (int n : nch) { maxn = n > maxn ? n : maxn; tot += n; }
     if (forced > 0) return (maxn > forced && fits(forced)) ? forced : 0;
-    const double R = c.cu_rate * device_cus();
+    const double R = c.cu_rate * cus;
     const double W = tot * H * nslice;
     const double t0 = std::max(static_cast<double>(maxn), W / R);
     int best = 0;

@@ -569,7 +569,7 @@ hipError_t launch_state_c(const FwdArgs& A, size_t rec_bytes, hipStream_t stream
         return seg_buffer_bytes(seg_slots(varlen, A.B, A.T, A.ndocs, G), A.H, DK, DV) <= avail;
     };
     const int G = plan_segments(chain_chunks(A.cu_host, varlen, A.ndocs, A.B, A.T), A.H, SH::NSLICE, NTS,
-                                kStateCost, fits);
+                                kStateCost, device_cus(stream), fits);
     if (G == 0) return launch_state_kernel<Tin, DK, DV, CKPT, false, true>(p, nchains * SH::NSLICE, stream);
     p.G = G;
     p.nsslots = seg_slots(varlen, A.B, A.T, A.ndocs, G);
@@ -631,10 +631,13 @@ void set_segment_chunks(int G) { g_seg_chunks.store(G); }
 int segment_chunks() { return g_seg_chunks.load(); }
 int segment_min_chunks() { return kSegMinChunks; }
 
-int device_cus() {
+int device_cus(hipStream_t stream) {
     static std::atomic<int> cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    hipDevice_t dev = 0;
+    if (stream == nullptr || hipStreamGetDevice(stream, &dev) != hipSuccess) {
+        if (hipGetDevice(&dev) != hipSuccess) return 256;
+    }
+    if (dev < 0 || dev >= 64) return 256;
     int n = cached[dev].load();
     if (n <= 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;

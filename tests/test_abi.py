@@ -85,8 +85,9 @@ def bwd_block_bytes(DK, DV):
 
 def test_fwd_workspace(L):
     need = L.ckda_fwd_workspace_bytes(2, 100, 3, 64, 32, 1)
-    # one record per (chunk, head): bf16 keeps W, Qh, KbT and M as hi/lo planes
-    rec = 2 * (64 * 64 * 2) * 4 + 64 * 4 + 64 * 32 * 4
+    # one record per (chunk, head): bf16 keeps W, Qh, KbT and M as hi/lo planes,
+    # then d, u and a flag word, padded to a multiple of 256 bytes
+    rec = align256(2 * (64 * 64 * 2) * 4 + 64 * 4 + 64 * 32 * 4 + 4)
     # then the segment buffers for segments of 16 chunks: ceil(2/16) per sequence
     assert need == align256(2 * 2 * 3 * rec) + seg_bytes(2 * 1, 3, 64, 32)
     # fp32 records hold every matrix element in 4 bytes too (one fp32 plane)
@@ -98,8 +99,8 @@ def test_fwd_workspace(L):
         align256((2 + 3) * 3 * rec) + seg_bytes(1 + 3, 3, 64, 32)
     assert fwd(L, ws=None) == 1
     assert b"workspace" in L.ckda_last_error()
-    # below the records (fp32, DK = DV = 32: W, Qh, KbT, M, d, u) the call fails
-    rec32 = 64 * 32 * 4 * 3 + 64 * 64 * 4 + 32 * 4 + 64 * 32 * 4
+    # below the records (fp32, DK = DV = 32: W, Qh, KbT, M, d, u, flag) the call fails
+    rec32 = align256(64 * 32 * 4 * 3 + 64 * 64 * 4 + 32 * 4 + 64 * 32 * 4 + 4)
     assert fwd(L, wsb=rec32 - 16) == 6
     assert fwd(L, ws=P(0x1008)) == 4             # misaligned workspace
 
@@ -189,6 +190,37 @@ def test_size_limits(L):
     assert L.ckda_bwd(1 << 16, 0, 1 << 15, 32, 32, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, f, None, FAKE,
                       FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ctypes.c_size_t(BIG), None) == 4
     assert b"too many heads" in L.ckda_last_error()
+
+
+def test_outputs_must_not_alias_inputs(L):
+    """Overlapping output and input ranges are refused on the host, before
+    any launch (the pointers below are never dereferenced)."""
+    f = ctypes.c_float(1.0)
+    B, T, H, D = 1, 8, 1, 32
+    n = B * T * H * D * 4                 # one fp32 token tensor
+    base = 0x100000
+    q, k, v, g, s, beta = (P(base + i * 0x10000) for i in range(6))
+    o = P(base + 6 * 0x10000)
+    ws = P(base + 8 * 0x10000)
+    wsb = ctypes.c_size_t(0x100000)
+
+    def call(o_=o, q_=q, ws_=ws, ht=None, h0=None):
+        return L.ckda_fwd_chunked(B, T, H, D, D, 0, 0, q_, k, v, g, s, beta, f, h0, o_, ht, None, ws_, wsb, None)
+    assert call(o_=P(q.value + n - 16)) == 4          # o overlaps the end of q
+    assert b"'o'" in L.ckda_last_error() and b"'q'" in L.ckda_last_error()
+    assert call(ws_=P(base + 0x10000)) == 4           # workspace over k
+    assert call(ht=P(o.value + 64)) == 4              # two outputs overlap
+    assert call(h0=P(o.value)) == 4                   # input state over an output
+    # decode: o over the in/out state, and sign_prod over q
+    st = P(base + 0x40000)
+    assert L.ckda_decode_step(1, 1, D, D, 0, 0, q, k, v, g, s, beta, f, st, P(base + 0x50000), P(st.value + 128),
+                              None) == 4
+    assert L.ckda_decode_step(1, 1, D, D, 0, 0, q, k, v, g, s, beta, f, st, q, o, None) == 4
+    # backward: dq over dout
+    assert L.ckda_bwd(B, T, H, D, D, 0, 0, q, k, v, g, s, beta, f, None, P(base + 0x60000), P(base + 0x70000), None,
+                      P(base + 0x70000), P(base + 0x80000), P(base + 0x90000), P(base + 0xa0000), P(base + 0xb0000),
+                      None, P(base + 0x200000), ctypes.c_size_t(1 << 24), None) == 4
+    assert b"'dq'" in L.ckda_last_error() and b"'dout'" in L.ckda_last_error()
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

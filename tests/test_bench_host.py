@@ -74,3 +74,21 @@ def test_traffic_is_reported_only_for_the_measured_sources(tmp_path, monkeypatch
     # and a missing record gives null as well
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "absent.json"))
     assert bench.measured_traffic() is None
+
+
+def test_decode_traffic_and_mfma_records_follow_the_same_rule(tmp_path, monkeypatch):
+    """The decode traffic and the forward's executed matrix-core work come from
+    committed counter runs too, and are used only while their sources match."""
+    rec = json.load(open(bench.DECODE_TRAFFIC_FILE))
+    got = bench.measured_traffic(bench.DECODE_TRAFFIC_FILE)
+    assert got is None or got == float(rec["traffic_bytes_per_call"])
+    p = tmp_path / "dec.json"
+    p.write_text(json.dumps(dict(rec, sources_sha256="0" * 64)))
+    assert bench.measured_traffic(str(p)) is None
+    m = json.load(open(bench.MFMA_FILE))
+    got = bench.measured_mfma()
+    assert got is None or got["executed_bf16_flops_per_call"] == m["executed_bf16_flops_per_call"]
+    q = tmp_path / "mfma.json"
+    q.write_text(json.dumps(dict(m, sources_sha256="0" * 64)))
+    monkeypatch.setattr(bench, "MFMA_FILE", str(q))
+    assert bench.measured_mfma() is None

@@ -31,6 +31,10 @@ CASES = [
     ("bf16", 1, 200, 2, 128, 128),
     ("f32", 1, 1, 1, 32, 32),
     ("f32", 1, 96, 1, 128, 32),
+    # whole chunks with several sequences and heads: the gradients go straight
+    # into their [B, T, H, D] places
+    ("f32", 2, 128, 2, 64, 64),
+    ("bf16", 2, 128, 2, 128, 128),
 ]
 
 
@@ -60,17 +64,26 @@ def test_backward_small(dtype, B, T, H, DK, DV):
 
 
 def test_layer_bwd_sampled():
-    """B=8, T=4096, H=16, d=128 bf16 with a bf16 upstream gradient; whole
-    backward on the GPU, two (sequence, head) chains against the oracle."""
+    """B=8, T=4096, H=16, d=128 bf16 with a bf16 upstream gradient, plus a
+    nonzero initial state and final-state gradient; whole backward on the GPU,
+    four (sequence, head) chains (the first, the last and two inside) against
+    the oracle, dh0 included."""
     require_gpu()
     banner("bwd layer_bwd full size, sampled")
     w = I.make_workload("layer_bwd")
-    r = gpu_bwd(w, w.do)
-    for name in NAMES:
+    B, T, H, DK = w.tok.q.shape
+    DV = w.tok.v.shape[-1]
+    rng = np.random.default_rng(4096)
+    h0 = I.draw_state(rng, (B, H, DK, DV), 0.02)
+    dht = (0.05 * rng.standard_normal((B, H, DK, DV))).astype(np.float32)
+    w.h0 = h0
+    r = gpu_bwd(w, w.do, dht)
+    for name in NAMES + ("dh0",):
         assert np.isfinite(r[name].cpu().numpy()).all(), name
-    chains = [(1, 3), (6, 14)]
+    chains = [(0, 0), (1, 3), (6, 14), (B - 1, H - 1)]
     f = w.tok.f64()
-    ref = oracle.bwd(**f, do=I.widen(w.do), chains=chains)
+    ref = oracle.bwd(**f, do=I.widen(w.do), h0=h0.astype(np.float64), dht=dht.astype(np.float64),
+                     chains=chains)
     bi = [c[0] for c in chains]; hi = [c[1] for c in chains]
     for name in NAMES:
         g = host(r[name])
@@ -78,6 +91,9 @@ def test_layer_bwd_sampled():
         e = rel_max(g, ref[name])
         print(f"  layer_bwd {name}: {e:.2e}")
         assert e < TOL["bf16"], (name, e)
+    e = rel_max(host(r["dh0"])[bi, hi], ref["dh0"])
+    print(f"  layer_bwd dh0: {e:.2e}")
+    assert e < TOL["bf16"]
 
 
 @pytest.mark.parametrize("dtype,DK,DV", [("f32", 64, 64), ("bf16", 128, 128)])
