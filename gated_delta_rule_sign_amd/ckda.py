@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
     L.ckda_fwd_varlen_workspace_bytes.restype = S
     L.ckda_fwd_chunked.argtypes = [I, I, I, I, I, I, U, P, P, P, P, P, P, F, P, P, P, P, P, S, P]
     L.ckda_fwd_chunked.restype = I
+    L.ckda_fwd_chunked_noalloc.argtypes = [I, I, I, I, I, I, U, P, P, P, P, P, P, F, P, P, P, P, P]
+    L.ckda_fwd_chunked_noalloc.restype = I
     L.ckda_fwd_varlen.argtypes = [I, I, P, P, I, I, I, I, U, P, P, P, P, P, P, F, P, P, P, P, P, S, P]
     L.ckda_fwd_varlen.restype = I
     L.ckda_varlen_chunk_slots.argtypes = [I, I]
@@ -204,6 +206,24 @@ def fwd(q, k, v, g, s, beta, scale: float = 1.0, h0=None, want_ht: bool = True,
     _check(lib().ckda_fwd_chunked(B, T, H, DK, DV, dt, _flags(g, (B, T), qk_norm), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
                                   _ptr(beta), float(scale), _ptr(h0), _ptr(o), _ptr(ht),
                                   _ptr(h_ckpt), _ptr(workspace), wsb, _stream()))
+    return o, ht, h_ckpt
+
+
+def fwd_noalloc(q, k, v, g, s, beta, o, ht=None, h0=None, h_ckpt=None, scale: float = 1.0,
+                qk_norm: bool = False):
+    """ckda_fwd_chunked_noalloc: the chunked forward with the records in the
+    library's fixed device scratch (no workspace, nothing allocated by the
+    library or here).  The caller passes every output tensor (o, and ht /
+    h_ckpt when wanted); returns (o, ht, h_ckpt)."""
+    B, T = q.shape[0], q.shape[1]
+    dt, H, DK, DV, dev = _token_inputs(q, k, v, g, s, beta, (B, T))
+    _need(h0, "h0", torch.float32, (B, H, DK, DV), dev)
+    _need(o, "o", torch.float32, (B, T, H, DV), dev)
+    _need(ht, "ht", torch.float32, (B, H, DK, DV), dev)
+    _need(h_ckpt, "h_ckpt", torch.float32, (B, H, (T + CHUNK - 1) // CHUNK, DK, DV), dev)
+    _check(lib().ckda_fwd_chunked_noalloc(B, T, H, DK, DV, dt, _flags(g, (B, T), qk_norm), _ptr(q), _ptr(k),
+                                          _ptr(v), _ptr(g), _ptr(s), _ptr(beta), float(scale), _ptr(h0),
+                                          _ptr(o), _ptr(ht), _ptr(h_ckpt), _stream()))
     return o, ht, h_ckpt
 
 

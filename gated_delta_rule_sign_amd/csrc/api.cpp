@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 
 #include "ckda_launch.h"
 
@@ -129,6 +130,41 @@ struct TokBytes {
     }
 };
 
+// The chunk records of ckda_fwd_chunked_noalloc.  Host code never uses the
+// array's name as an address: its device address, per device, comes from
+// hipGetSymbolAddress with that device current, on the first call there.
+__device__ __align__(256) unsigned char scratch[CKDA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(hipStream_t stream, void** out) {
+    hipDevice_t dev = 0;
+    if (stream == nullptr || hipStreamGetDevice(stream, &dev) != hipSuccess) {
+        const hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 ckda_status_t check_varlen_sizes(int N, int T_total, int H) {
     if (too_big(T_total, H)) return fail(CKDA_ERR_UNSUPPORTED, "tensor too large");
     if (static_cast<long long>(N) * H >= (1LL << 31) / 2) return fail(CKDA_ERR_UNSUPPORTED, "too many documents");
@@ -206,11 +242,13 @@ ckda_status_t ckda_set_segment_chunks(int G) {
 
 namespace {
 
-// ckda_fwd_chunked: checks, then the chunk-local and state passes.
+// ckda_fwd_chunked and its no-allocation variant.  ws == nullptr selects the
+// fixed scratch array (whole chains; records only).
 ckda_status_t fwd_chunked_common(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype, ckda_flags_t flags,
                                  const void* q, const void* k, const void* v, const float* g, const int8_t* s,
                                  const float* beta, float scale, const float* h0, float* o, float* ht,
-                                 float* h_ckpt, void* workspace, size_t workspace_bytes, ckda_stream_t stream) {
+                                 float* h_ckpt, void* workspace, size_t workspace_bytes, bool noalloc,
+                                 ckda_stream_t stream) {
     CKDA_TRY(check_dtype(in_dtype));
     CKDA_TRY(check_flags(flags));
     if (B < 0 || T < 0 || H < 0) return fail(CKDA_ERR_SHAPE, "negative size (B=%d, T=%d, H=%d)", B, T, H);
@@ -224,7 +262,18 @@ ckda_status_t fwd_chunked_common(int B, int T, int H, int DK, int DV, ckda_dtype
     CKDA_ALIGNED(q); CKDA_ALIGNED(k); CKDA_ALIGNED(g); CKDA_ALIGNED(s); CKDA_ALIGNED(workspace);
     const int nslots = fwd_slots(B, T);
     const size_t need = ckda::fwd_workspace_bytes(nslots, H, DK, DV, in_dtype == CKDA_BF16);
-    if (need > 0) {
+    if (noalloc) {
+        if (need > CKDA_NOALLOC_SCRATCH_BYTES)
+            return fail(CKDA_ERR_UNSUPPORTED,
+                        "ckda_fwd_chunked_noalloc: the records of %d chunk-heads need %zu bytes, more than its "
+                        "fixed %zu-byte scratch; use ckda_fwd_chunked with a workspace",
+                        nslots * H, need, static_cast<size_t>(CKDA_NOALLOC_SCRATCH_BYTES));
+        if (need > 0) {
+            CKDA_TRY(hip_status(scratch_address(static_cast<hipStream_t>(stream), &workspace),
+                                "ckda_fwd_chunked_noalloc scratch address"));
+            workspace_bytes = need;   // records only: the state pass keeps whole chains
+        }
+    } else if (need > 0) {
         CKDA_REQUIRE(workspace);
         if (workspace_bytes < need)
             return fail(CKDA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
@@ -243,7 +292,8 @@ ckda_status_t fwd_chunked_common(int B, int T, int H, int DK, int DV, ckda_dtype
                                 {{q, tb.qk, "q"}, {k, tb.qk, "k"}, {v, tb.v, "v"}, {g, tb.g, "g"}, {s, tb.s, "s"},
                                  {beta, tb.beta, "beta"}, {h0, st, "h0"}}));
     }
-    return hip_status(ckda::launch_fwd(a, nslots, static_cast<hipStream_t>(stream)), "ckda_fwd_chunked launch");
+    return hip_status(ckda::launch_fwd(a, nslots, static_cast<hipStream_t>(stream)),
+                      noalloc ? "ckda_fwd_chunked_noalloc launch" : "ckda_fwd_chunked launch");
 }
 
 }  // namespace
@@ -256,7 +306,16 @@ ckda_status_t ckda_fwd_chunked(int B, int T, int H, int DK, int DV, ckda_dtype_t
                                const float* h0, float* o, float* ht, float* h_ckpt, void* workspace,
                                size_t workspace_bytes, ckda_stream_t stream) {
     return fwd_chunked_common(B, T, H, DK, DV, in_dtype, flags, q, k, v, g, s, beta, scale, h0, o, ht, h_ckpt,
-                              workspace, workspace_bytes, stream);
+                              workspace, workspace_bytes, false, stream);
+}
+
+ckda_status_t ckda_fwd_chunked_noalloc(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype,
+                                       ckda_flags_t flags, const void* q, const void* k, const void* v,
+                                       const float* g, const int8_t* s, const float* beta, float scale,
+                                       const float* h0, float* o, float* ht, float* h_ckpt,
+                                       ckda_stream_t stream) {
+    return fwd_chunked_common(B, T, H, DK, DV, in_dtype, flags, q, k, v, g, s, beta, scale, h0, o, ht, h_ckpt,
+                              nullptr, 0, true, stream);
 }
 
 ckda_status_t ckda_fwd_varlen(int N, int T_total, const int32_t* cu, const int32_t* cu_dev, int H,

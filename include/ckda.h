@@ -150,6 +150,28 @@ ckda_status_t ckda_fwd_chunked(int B, int T, int H, int DK, int DV, ckda_dtype_t
                                void* workspace, size_t workspace_bytes, ckda_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * ckda_fwd_chunked for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid device allocation.
+ * Same arguments and results as ckda_fwd_chunked (whole-chain state pass),
+ * without the workspace: the chunk records go to a fixed device array that
+ * the library holds on every GPU it runs on until the process ends
+ * (CKDA_NOALLOC_SCRATCH_BYTES = 160 MiB, e.g. B * ceil(T/64) * H = 1,024
+ * chunk-heads of DK = DV = 128: one 4,096-token sequence of 16 heads).  A
+ * call whose records need more (ckda_fwd_workspace_bytes without the
+ * segment buffers) fails with CKDA_ERR_UNSUPPORTED before anything is
+ * enqueued.  The call allocates nothing: the array's device address is
+ * looked up once per device, on the first call there.  Every call on one GPU
+ * shares the array, so calls that overlap in time on one GPU (other streams,
+ * other threads) race and must be serialised by the caller.
+ * ---------------------------------------------------------------------- */
+#define CKDA_NOALLOC_SCRATCH_BYTES ((size_t)160 << 20)
+ckda_status_t ckda_fwd_chunked_noalloc(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype,
+                                       ckda_flags_t flags, const void* q, const void* k, const void* v,
+                                       const float* g, const int8_t* s, const float* beta, float scale,
+                                       const float* h0, float* o, float* ht, float* h_ckpt,
+                                       ckda_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Segment length of the forward's state pass and of the backward's reverse
  * (state-gradient) pass, process-wide (all devices).
  * Per chunk the state map is affine, S' = A_c S + B_c, and the columns of
