@@ -12,7 +12,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libckda.so")
-SOURCES = ["api.cpp", "decode.hip", "chunk.hip", "state.hip", "bwd.hip"]
+SOURCES = ["api.cpp", "decode.hip", "chunk.hip", "chunk_rev.hip", "chunk_grad.hip", "state.hip", "bwd.hip",
+           "rev.hip", "grad.hip"]
 ARCH = os.environ.get("CKDA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -80,6 +80,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 __device__ __forceinline__ void buffer_store_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float x) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, static_cast<int>(byte_off), 0, 0);
 }
+__device__ __forceinline__ void buffer_store_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, static_cast<int>(voff), static_cast<int>(soff), 0);
+}
+// loads through a raw buffer resource: a per-lane byte offset plus a uniform
+// one (kept in a scalar register); out-of-range bytes read as 0
+__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(voff), static_cast<int>(soff), 0));
+}
+__device__ __forceinline__ uint32_t buffer_load_u16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(voff), static_cast<int>(soff), 0);
+}
+__device__ __forceinline__ int buffer_load_i8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return static_cast<int8_t>(__builtin_amdgcn_raw_buffer_load_b8(r, static_cast<int>(voff), static_cast<int>(soff), 0));
+}
+__device__ __forceinline__ u32x2 buffer_load_u32x2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(voff), static_cast<int>(soff), 0));
+}
+__device__ __forceinline__ u32x4 buffer_load_u32x4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), 0));
+}
+// an element of a token tensor (bf16 or fp32) as fp32
+template <typename T>
+__device__ __forceinline__ float buffer_load_elem(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    if constexpr (sizeof(T) == 4) return buffer_load_f32(r, voff, soff);
+    else return bf16_to_f32(static_cast<uint16_t>(buffer_load_u16(r, voff, soff)));
+}
 
 // exp(x) through the hardware base-2 exponential; the argument is clamped so
 // that no infinity can be produced (exp2(126) is finite in fp32)

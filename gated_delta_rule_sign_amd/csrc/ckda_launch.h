@@ -68,6 +68,50 @@ void set_segment_chunks(int G);
 int segment_chunks();
 int segment_min_chunks();
 hipError_t launch_chunk(const FwdArgs& a, int nslots, hipStream_t stream);
+// the chunk-local pass writing the backward's reverse-pass records (RevRecord)
+// and a compact envelope flag per (slot, head) into flags
+hipError_t launch_chunk_rev(const FwdArgs& a, uint32_t* flags, int nslots, hipStream_t stream);
+
+// the backward's first chunk-parallel gradient phase (chunk.hip, kModeGrad)
+struct Grad1Args {
+    const uint32_t* flags;   // from launch_chunk_rev on the same inputs
+    const float* h_ckpt;     // chunk-start states: [B,H,NT,DK,DV] (varlen [slot][H][DK][DV])
+    const float* dU;         // [slot][H] blocks of 64 x DV from the reverse pass
+    const void* dout;
+    float* dv;
+    float* dbeta;
+    unsigned char* gout;     // [slot][H] blocks of gout_bytes (dA, dM, U)
+    size_t gout_bytes;
+};
+hipError_t launch_grad1(const FwdArgs& a, const Grad1Args& g, int nslots, hipStream_t stream);
+size_t grad_out_bytes(int DK, int DV, bool bf16);
+// the backward's second chunk-parallel gradient phase (grad.hip): dq, dk, dg
+struct Grad2Args {
+    const uint32_t* flags;          // as for Grad1Args
+    const float* h_ckpt;            // as for Grad1Args
+    const float* G;                 // [slot][H] blocks of DK x DV: dL/dS at each chunk's end
+    const unsigned char* gout;      // the first phase's blocks
+    size_t gout_bytes;
+    const void* dout;
+    const float* dv;                // the first phase's dv
+    float *dq, *dk, *dg;
+};
+hipError_t launch_grad2(const FwdArgs& a, const Grad2Args& g, int nslots, hipStream_t stream);
+// the backward's reverse (state-gradient) pass (rev.hip), over the records of
+// launch_chunk_rev: one chain per (sequence or document, head)
+struct RevParams {
+    const unsigned char* ws;   // reverse records, [slot][H] blocks of rev_record_bytes
+    const void* dout;          // dO [.., T, H, DV] (input dtype)
+    const float* dht;          // [chains][H][DK][DV] or nullptr (zero)
+    float* dh0;                // [chains][H][DK][DV] or nullptr
+    float* dU;                 // [slot][H] blocks of 64 x DV, C/D tiles
+    float* G;                  // [slot][H][DK][DV]: G at each chunk's end
+    const int32_t* cu;         // varlen document starts (device), or nullptr
+    float scale;
+    int B, T, H, ndocs;
+};
+hipError_t launch_rev(const RevParams& p, int nchains, int DK, int DV, bool bf16, hipStream_t stream);
+size_t rev_record_bytes(int DK, int DV, bool bf16);
 hipError_t launch_state(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, int nslots, hipStream_t stream);
 

@@ -99,6 +99,10 @@ struct Prec<false> {
         const Split8 s = split8(a, b);
         return F8{s.hi, s.lo};
     }
+    // slot e of a fragment back as one float (hi + lo)
+    static __device__ __forceinline__ float get8(const F8& f, int e) {
+        return static_cast<float>(f.hi[e]) + static_cast<float>(f.lo[e]);
+    }
     static __device__ __forceinline__ F4 regs4(f32x4 a) {
         const Split4 s = split4(a);
         return F4{s.hi, s.lo};
@@ -136,6 +140,21 @@ struct Prec<false> {
         *reinterpret_cast<uint16_t*>(p + row) = static_cast<uint16_t>(sp.hi >> 16);
         *reinterpret_cast<uint16_t*>(p + plane) = static_cast<uint16_t>(sp.lo);
         *reinterpret_cast<uint16_t*>(p + plane + row) = static_cast<uint16_t>(sp.lo >> 16);
+    }
+    // N elements of one column c (rows r0 .. r0 + N - 1) of a two-plane matrix
+    template <int N>
+    static __device__ __forceinline__ void gstore_col(unsigned char* base, size_t plane, int row, int r0, int c,
+                                                      const float* x) {
+        unsigned char* p = base + static_cast<size_t>(r0) * row + 2 * c;
+#pragma unroll
+        for (int i = 0; i < N; i += 2) {
+            const SplitPair sp = split2(x[i], x[i + 1]);
+            *reinterpret_cast<uint16_t*>(p + static_cast<size_t>(i) * row) = static_cast<uint16_t>(sp.hi);
+            *reinterpret_cast<uint16_t*>(p + static_cast<size_t>(i + 1) * row) = static_cast<uint16_t>(sp.hi >> 16);
+            *reinterpret_cast<uint16_t*>(p + plane + static_cast<size_t>(i) * row) = static_cast<uint16_t>(sp.lo);
+            *reinterpret_cast<uint16_t*>(p + plane + static_cast<size_t>(i + 1) * row) =
+                static_cast<uint16_t>(sp.lo >> 16);
+        }
     }
 };
 
@@ -184,6 +203,7 @@ struct Prec<true> {
     }
     static __device__ __forceinline__ F4 load4(const LdsMat& m, int r, int c) { return F4{ld4(fp(m, r, c))}; }
     static __device__ __forceinline__ F8 regs8(f32x4 a, f32x4 b) { return F8{a, b}; }
+    static __device__ __forceinline__ float get8(const F8& f, int e) { return e < 4 ? f.a[e] : f.b[e - 4]; }
     static __device__ __forceinline__ F4 regs4(f32x4 a) { return F4{a}; }
     static __device__ __forceinline__ f32x4 mma8(const F8& x, const F8& y, f32x4 acc) {
 #pragma unroll
@@ -213,6 +233,13 @@ struct Prec<true> {
         float* p = reinterpret_cast<float*>(base + static_cast<size_t>(r) * row + 4 * c);
         p[0] = x0;
         *reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(p) + row) = x1;
+    }
+    template <int N>
+    static __device__ __forceinline__ void gstore_col(unsigned char* base, size_t, int row, int r0, int c,
+                                                      const float* x) {
+        unsigned char* p = base + static_cast<size_t>(r0) * row + 4 * c;
+#pragma unroll
+        for (int i = 0; i < N; ++i) *reinterpret_cast<float*>(p + static_cast<size_t>(i) * row) = x[i];
     }
 };
 

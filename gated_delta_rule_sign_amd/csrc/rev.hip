@@ -1,0 +1,401 @@
+// rev.hip -- reverse (state-gradient) pass of the CKDA backward.
+//
+// The chunked forward's state step is affine in the state,
+//   U = u - W S,   O = scale (Qh S + M U),   S' = Diag(d) S + KbT U,
+// so the gradient G = dL/dS' at a chunk's end (true frame) goes back through
+// the chunk by the adjoint step
+//   dU = scale M^T dO + KbT^T G,   G_start = Diag(d) G + scale Qh^T dO - W^T dU
+// (WY/UT chunk form of the recurrence, Complex KDA paper page, section 2
+// "Linear RNNs"; the backward is the plain derivative of the forward since the
+// pages' own backward convention is in an appendix they do not include).  The
+// chunk quantities come from the reverse record (RevRecord, written by the
+// chunk-local kernel in its REV mode: KB = KbT^T, QT = Qh^T, WT = W^T,
+// MT = M^T, d), so the pass only runs these state-gradient products, one
+// chain at a time, from the chain's last chunk to its first.
+//
+// Work decomposition (gfx950): as the forward's state pass, one 512-thread
+// workgroup per (sequence or document, head, 64-wide value slice).  Waves
+// 0..3 own 16 value columns each and keep that DK x 16 block of G in MFMA
+// accumulator registers; waves 4..7 only move data, holding the next chunk's
+// record in registers (read one chunk ahead) and writing it to LDS in two
+// groups (A = KB, MT for the first products; B = QT, WT, d for the update)
+// while the matrix-core waves work on the other group.  Each compute wave
+// reads its dO tiles (16 tokens x 16 columns per tile, the C/D lane layout)
+// straight from the input one chunk ahead.
+//
+// Outputs per chunk (in the chunk's record slot, for the chunk-parallel
+// gradient pass): dU [64][DV] in C/D tiles and G at the chunk's end
+// [DK][DV]; per chain dh0 = G at its start.
+#include "ckda_device.h"
+#include "ckda_launch.h"
+#include "ckda_mfma.h"
+#include "ckda_prec.h"
+#include "ckda_record.h"
+#include "ckda_sync.h"
+
+namespace ckda {
+
+template <typename Tin, int DK, int DV>
+struct RevShape {
+    static constexpr bool F32 = sizeof(Tin) == 4;
+    using RC = RevRecord<DK, DV, F32>;
+    static constexpr int NT = 256;                 // threads per role
+    static constexpr int BV = DV < 64 ? DV : 64;   // value columns per workgroup
+    static constexpr int NSLICE = DV / BV;
+    static constexpr int NWC = BV / 16;            // waves that own columns
+    static constexpr int RT = DK / 16;             // 16-row tiles of G
+    static constexpr int ES = RC::ES, NP = RC::NP;
+    // rows padded by 32 bytes: 16-byte fragment reads conflict-free at a
+    // pitch of 8 mod 16 dwords (as in the forward's state pass)
+    static constexpr int PADB = 32;
+    static constexpr int PKB = (RC::KB_ROW + PADB) / ES;
+    static constexpr int PMT = (RC::MT_ROW + PADB) / ES;
+    static constexpr int PQT = (RC::QT_ROW + PADB) / ES;
+    static constexpr int PWT = (RC::WT_ROW + PADB) / ES;
+    static constexpr int L_KB = 0;
+    static constexpr int L_MT = L_KB + NP * 64 * PKB * ES;
+    static constexpr int L_QT = L_MT + NP * 64 * PMT * ES;
+    static constexpr int L_WT = L_QT + NP * DK * PQT * ES;
+    static constexpr int L_D = L_WT + NP * DK * PWT * ES;
+    static constexpr int LDS = L_D + DK * 4;
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+// the forward state pass's staging helper, over the reverse record
+template <int ROWS, int UPR, int PAD, int NT>
+struct RStage {
+    static constexpr int UNITS = ROWS * UPR;
+    static constexpr int N = (UNITS + NT - 1) / NT;
+    static constexpr bool FULL = (UNITS % NT) == 0;
+    static __device__ __forceinline__ bool has(int tid, int i) { return FULL || tid + NT * i < UNITS; }
+    static __device__ __forceinline__ int lds_off(int tid, int i) {
+        const int u = tid + NT * i;
+        return (u / UPR) * (UPR * 16 + PAD) + (u % UPR) * 16;
+    }
+    // unit (tid, i) of a matrix read as A operands; PERM (bf16): in each
+    // 32-column group, columns 4g .. 4g+3 and 16+4g .. 16+4g+3 side by side at
+    // 8g, so a lane group's fragment is one 16-byte read
+    template <bool PERM>
+    static __device__ __forceinline__ void put_a(unsigned char* base, int tid, int i, u32x4 v) {
+        if constexpr (!PERM) {
+            *reinterpret_cast<u32x4*>(base + lds_off(tid, i)) = v;
+        } else {
+            static_assert(UPR % 4 == 0 && PAD % 16 == 0, "32-column groups, 16-byte rows");
+            const int u = tid + NT * i;
+            const int uc = u % UPR, q = uc & 3;
+            unsigned char* rb = base + (u / UPR) * (UPR * 16 + PAD) + 64 * (uc >> 2) + 8 * (q >> 1);
+            *reinterpret_cast<u32x2*>(rb + 16 * ((2 * q) & 3)) = v.xy;
+            *reinterpret_cast<u32x2*>(rb + 16 * ((2 * q + 1) & 3)) = v.zw;
+        }
+    }
+};
+
+template <typename Tin, int DK, int DV>
+__global__ void __launch_bounds__(512, 2) ckda_rev_kernel(RevParams p)
+{
+    using SH = RevShape<Tin, DK, DV>;
+    using RC = typename SH::RC;
+    using PR = Prec<SH::F32>;
+    constexpr int RT = SH::RT, NP = SH::NP, NT = SH::NT, NWC = SH::NWC, NS = SH::NSLICE;
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const int H = p.H;
+    const int nitems = p.cu ? p.ndocs * H : p.B * H;
+    int item, slice;
+    {
+        const int bid = blockIdx.x;
+        if (NS == 1) {
+            item = bid;
+            slice = 0;
+        } else {   // the slices of one item on one XCD (its L2 serves the second read of the record)
+            const int grp = 8 * NS;
+            const int full = (nitems / 8) * grp;
+            if (bid < full) {
+                const int r = bid % grp;
+                item = (bid / grp) * 8 + (r % 8);
+                slice = r / 8;
+            } else {
+                const int r = bid - full;
+                item = (nitems / 8) * 8 + r / NS;
+                slice = r % NS;
+            }
+        }
+    }
+    const int h = item % H, sidx = item / H;
+    const int NTC = (p.T + 63) / 64;
+    int tok0, len, slot0;
+    if (p.cu) {
+        tok0 = p.cu[sidx];
+        len = p.cu[sidx + 1] - tok0;
+        slot0 = varlen_slot(tok0, sidx, 0);
+    } else {
+        tok0 = sidx * p.T;
+        len = p.T;
+        slot0 = sidx * NTC;
+    }
+    const int nloop = (len + 63) / 64;
+    const int vt0 = (slice * SH::BV) / 16;
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+
+    // walk step j covers chunk nloop - 1 - j
+    if (w >= 4) {
+        // ================= loader waves (as in the forward's state pass) ======
+        using StKB = RStage<NP * 64, RC::KB_ROW / 16, SH::PADB, NT>;
+        using StMT = RStage<NP * 64, RC::MT_ROW / 16, SH::PADB, NT>;
+        using StQT = RStage<NP * DK, RC::QT_ROW / 16, SH::PADB, NT>;
+        using StWT = RStage<NP * DK, RC::WT_ROW / 16, SH::PADB, NT>;
+        using StD = RStage<1, DK * 4 / 16, 0, NT>;
+        constexpr int NKB = StKB::N, NMT = StMT::N, NQT = StQT::N, NWT = StWT::N, ND_ = StD::N;
+        constexpr int O_MT = NKB, NA = NKB + NMT;
+        constexpr int O_WT = NQT, O_D = O_WT + NWT, NB = O_D + ND_;
+        static_assert(StKB::FULL && StMT::FULL && StQT::FULL && StWT::FULL, "unguarded staging loads");
+        u32x4 ga[NA], gb[NB];
+#define CKDA_RREC(J) reinterpret_cast<const u32x4*>(p.ws + (static_cast<size_t>(slot0 + nloop - 1 - (J)) * H + h) * RC::BYTES + opaque_zero())
+#define CKDA_RLOAD_A(J)                                                                                      \
+        {                                                                                                    \
+            const u32x4* g_ = CKDA_RREC(J);                                                                  \
+            const int t_ = opaque_tid() - NT;                                                                \
+            _Pragma("unroll") for (int i_ = 0; i_ < NKB; ++i_) ga[i_] = g_[RC::OFF_KB / 16 + t_ + NT * i_];  \
+            _Pragma("unroll") for (int i_ = 0; i_ < NMT; ++i_) ga[O_MT + i_] = g_[RC::OFF_MT / 16 + t_ + NT * i_]; \
+        }
+#define CKDA_RLOAD_B(J)                                                                                      \
+        {                                                                                                    \
+            const u32x4* g_ = CKDA_RREC(J);                                                                  \
+            const int t_ = opaque_tid() - NT;                                                                \
+            _Pragma("unroll") for (int i_ = 0; i_ < NQT; ++i_) gb[i_] = g_[RC::OFF_QT / 16 + t_ + NT * i_];  \
+            _Pragma("unroll") for (int i_ = 0; i_ < NWT; ++i_) gb[O_WT + i_] = g_[RC::OFF_WT / 16 + t_ + NT * i_]; \
+            _Pragma("unroll") for (int i_ = 0; i_ < ND_; ++i_)                                               \
+                if (StD::has(t_, i_)) gb[O_D + i_] = g_[RC::OFF_D / 16 + t_ + NT * i_];                       \
+        }
+#define CKDA_RSTORE_A()                                                                                      \
+        {                                                                                                    \
+            unsigned char* const sm_ = smem + opaque_zero();                                                 \
+            const int t_ = opaque_tid() - NT;                                                                \
+            _Pragma("unroll") for (int i_ = 0; i_ < NKB; ++i_)                                               \
+                StKB::template put_a<PR::kPermA>(sm_ + SH::L_KB, t_, i_, ga[i_]);                              \
+            _Pragma("unroll") for (int i_ = 0; i_ < NMT; ++i_)                                               \
+                StMT::template put_a<PR::kPermA>(sm_ + SH::L_MT, t_, i_, ga[O_MT + i_]);                       \
+        }
+#define CKDA_RSTORE_B()                                                                                      \
+        {                                                                                                    \
+            unsigned char* const sm_ = smem + opaque_zero();                                                 \
+            const int t_ = opaque_tid() - NT;                                                                \
+            _Pragma("unroll") for (int i_ = 0; i_ < NQT; ++i_)                                               \
+                StQT::template put_a<PR::kPermA>(sm_ + SH::L_QT, t_, i_, gb[i_]);                              \
+            _Pragma("unroll") for (int i_ = 0; i_ < NWT; ++i_)                                               \
+                StWT::template put_a<PR::kPermA>(sm_ + SH::L_WT, t_, i_, gb[O_WT + i_]);                       \
+            _Pragma("unroll") for (int i_ = 0; i_ < ND_; ++i_)                                               \
+                if (StD::has(t_, i_)) *reinterpret_cast<u32x4*>(sm_ + SH::L_D + StD::lds_off(t_, i_)) = gb[O_D + i_]; \
+        }
+        if (nloop > 0) {
+            CKDA_RLOAD_A(0)
+            CKDA_RLOAD_B(0)
+            CKDA_RSTORE_A()
+            CKDA_RSTORE_B()
+            CKDA_RLOAD_A(min(1, nloop - 1))
+            CKDA_RLOAD_B(min(1, nloop - 1))
+        }
+        lds_sync();   // record of walk step 0 in LDS
+        for (int j = 0; j < nloop; ++j) {
+            lds_sync();   // X: KB, MT of step j consumed
+            CKDA_RSTORE_A()
+            CKDA_RLOAD_A(min(j + 2, nloop - 1))
+            lds_sync();   // Y: step j consumed
+            CKDA_RSTORE_B()
+            CKDA_RLOAD_B(min(j + 2, nloop - 1))
+        }
+#undef CKDA_RREC
+#undef CKDA_RLOAD_A
+#undef CKDA_RLOAD_B
+#undef CKDA_RSTORE_A
+#undef CKDA_RSTORE_B
+        return;
+    }
+
+    // ================= compute waves ==========================================
+    const size_t st_off = (static_cast<size_t>(sidx) * H + h) * DK * DV;
+    const bool has_col = w < NWC;
+    const int wt = min(w, NWC - 1);
+    const int vt = vt0 + wt;
+    const int lane = threadIdx.x & 63;
+
+    // G: lane (n, g) holds rows 16rt + 4g + i of column 16vt + n; starts at dht
+    f32x4 G[RT];
+    {
+        const int gq = lane >> 4, col = 16 * vt + (lane & 15);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * rt + 4 * gq + i;
+                G[rt][i] = (has_col && p.dht) ? p.dht[st_off + static_cast<size_t>(row) * DV + col] : 0.f;
+            }
+    }
+    // dO tiles of walk step jj: lane (n, g) holds rows 16J + 4g + i of column
+    // 16vt + n (the C/D layout), zero past the chunk's end; the address is
+    // clamped into the chunk so every load is unconditional
+    const Tin* dO = static_cast<const Tin*>(p.dout);
+    auto load_do = [&](int jj, f32x4 (&x)[4]) {
+        const int c0 = 64 * (nloop - 1 - jj);
+        const int L = min(64, len - c0);
+        const int gq = (opaque_tid() & 63) >> 4, col = 16 * vt + (lane & 15);
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tt = 16 * J + 4 * gq + i;
+                const size_t idx = (static_cast<size_t>(tok0 + c0 + min(tt, L - 1)) * H + h) * DV + col;
+                const float v = Elem<Tin>::load(dO, idx);
+                x[J][i] = tt < L ? v : 0.f;
+            }
+    };
+    f32x4 dn[4];
+    if (nloop > 0) load_do(0, dn);
+    lds_sync();   // record of step 0 in LDS
+    for (int j = 0; j < nloop; ++j) {
+        const int jc = nloop - 1 - j;    // chunk index within the chain
+        const size_t rslot = static_cast<size_t>(slot0 + jc) * H + h;
+        f32x4 dOv[4];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) dOv[J] = dn[J] * p.scale;
+        load_do(min(j + 1, nloop - 1), dn);
+        {
+            unsigned char* const sm = smem + opaque_zero();
+            const LdsMat KBm{sm + SH::L_KB, SH::PKB, 64 * SH::PKB};
+            const LdsMat MTm{sm + SH::L_MT, SH::PMT, 64 * SH::PMT};
+            const LdsMat QTm{sm + SH::L_QT, SH::PQT, DK * SH::PQT};
+            const LdsMat WTm{sm + SH::L_WT, SH::PWT, DK * SH::PWT};
+            const float* dl = reinterpret_cast<const float*>(sm + SH::L_D);
+            const int l = opaque_tid() & 63, n = l & 15, gq = l >> 4;
+            const int col = 16 * vt + n;
+            {   // G at this chunk's end, for the chunk-parallel pass
+                const __amdgpu_buffer_rsrc_t grc = buffer_rsrc(p.G + rslot * DK * DV, has_col ? DK * DV * 4 : 0);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        buffer_store_f32(grc, static_cast<uint32_t>(((16 * rt + 4 * gq + i) * DV + col) * 4), G[rt][i]);
+            }
+            constexpr int KS = RT / 2;
+            // X = KB G (32 channels per k-step, two 16-token row blocks at a
+            // time; the next step's fragments are read while these products run)
+            typename PR::F8 Gb[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) Gb[ks] = PR::regs8(G[2 * ks], G[2 * ks + 1]);
+            f32x4 X[4];
+#pragma unroll
+            for (int R = 0; R < 4; ++R) X[R] = f32x4{0.f, 0.f, 0.f, 0.f};
+            {
+                constexpr int NSTEP = 2 * KS;
+                typename PR::F8 ka[2][2];
+#pragma unroll
+                for (int r = 0; r < 2; ++r) ka[0][r] = PR::loadA(KBm, 16 * r + n, 0, gq);
+#pragma unroll
+                for (int st = 0; st < NSTEP; ++st) {
+                    const int ks = st / 2, R0 = 2 * (st % 2);
+                    if (st + 1 < NSTEP) {
+                        const int k1 = 32 * ((st + 1) / 2), R1 = 2 * ((st + 1) % 2);
+#pragma unroll
+                        for (int r = 0; r < 2; ++r) ka[(st + 1) & 1][r] = PR::loadA(KBm, 16 * (R1 + r) + n, k1, gq);
+                    }
+                    CKDA_FENCE();
+#pragma unroll
+                    for (int r = 0; r < 2; ++r) X[R0 + r] = PR::mma8(ka[st & 1][r], Gb[ks], X[R0 + r]);
+                    CKDA_FENCE();
+                }
+            }
+            // dU = X + (scale dO)^T-side product M^T (scale dO): rows i of
+            // 16-block R take tokens r >= i, i.e. the 32-token steps kt >= R / 2
+            // (M^T is zero left of its diagonal, also in the blocks those
+            // steps read)
+            typename PR::F8 Db[2];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) Db[kt] = PR::regs8(dOv[2 * kt], dOv[2 * kt + 1]);
+            f32x4 dU[4];
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+                f32x4 acc = X[R];
+#pragma unroll
+                for (int kt = R / 2; kt < 2; ++kt) acc = PR::mma8(PR::loadA(MTm, 16 * R + n, 32 * kt, gq), Db[kt], acc);
+                dU[R] = acc;
+            }
+            lds_sync();   // X: KB, MT consumed (the loaders refill them); QT, WT, d in LDS
+            {   // dU of this chunk (C/D tiles (R, vt), as u in the forward record)
+                float* du = p.dU + rslot * 64 * DV;
+                const __amdgpu_buffer_rsrc_t urc = buffer_rsrc(du, has_col ? 64 * DV * 4 : 0);
+#pragma unroll
+                for (int R = 0; R < 4; ++R)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        buffer_store_f32(urc, static_cast<uint32_t>((((R * (DV / 16) + vt) * 64 + l) * 4 + i) * 4), dU[R][i]);
+            }
+            // G <- Diag(d) G + Qh^T (scale dO) - W^T dU
+            typename PR::F8 Nb[2];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) Nb[kt] = PR::regs8(-dU[2 * kt], -dU[2 * kt + 1]);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const f32x4 dd = *reinterpret_cast<const f32x4*>(dl + 16 * rt + 4 * gq);
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+                    acc = PR::mma8(PR::loadA(QTm, 16 * rt + n, 32 * kt, gq), Db[kt], acc);
+                    acc = PR::mma8(PR::loadA(WTm, 16 * rt + n, 32 * kt, gq), Nb[kt], acc);
+                }
+                G[rt] = dd * G[rt] + acc;
+            }
+        }
+        lds_sync();   // Y: step j consumed (the loaders refill QT, WT, d)
+    }
+    if (p.dh0 && has_col) {
+        const int gq = lane >> 4, col = 16 * vt + (lane & 15);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                p.dh0[opaque_zero() + st_off + static_cast<size_t>(16 * rt + 4 * gq + i) * DV + col] = G[rt][i];
+    }
+}
+
+template <typename Tin, int DK, int DV>
+static hipError_t launch_rev_t(const RevParams& p, int nchains, hipStream_t stream) {
+    using SH = RevShape<Tin, DK, DV>;
+    const long long grid = static_cast<long long>(nchains) * SH::NSLICE;
+    if (grid == 0) return hipSuccess;
+    auto kern = ckda_rev_kernel<Tin, DK, DV>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, SH::LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(512), SH::LDS, stream, p);
+    return hipGetLastError();
+}
+
+template <typename Tin>
+static hipError_t launch_rev_dt(const RevParams& p, int nchains, int DK, int DV, hipStream_t stream) {
+#define CKDA_REV(DK_, DV_) \
+    if (DK == DK_ && DV == DV_) return launch_rev_t<Tin, DK_, DV_>(p, nchains, stream);
+    CKDA_REV(32, 32) CKDA_REV(32, 64) CKDA_REV(32, 128)
+    CKDA_REV(64, 32) CKDA_REV(64, 64) CKDA_REV(64, 128)
+    CKDA_REV(128, 32) CKDA_REV(128, 64) CKDA_REV(128, 128)
+#undef CKDA_REV
+    return hipErrorInvalidValue;
+}
+
+}  // namespace ckda
+
+namespace ckda {
+size_t rev_record_bytes(int DK, int DV, bool bf16) {
+#define CKDA_RB(DK_, DV_) \
+    if (DK == DK_ && DV == DV_) return bf16 ? RevRecord<DK_, DV_, false>::BYTES : RevRecord<DK_, DV_, true>::BYTES;
+    CKDA_RB(32, 32) CKDA_RB(32, 64) CKDA_RB(32, 128)
+    CKDA_RB(64, 32) CKDA_RB(64, 64) CKDA_RB(64, 128)
+    CKDA_RB(128, 32) CKDA_RB(128, 64) CKDA_RB(128, 128)
+#undef CKDA_RB
+    return 0;
+}
+
+// reverse pass over nchains chains: records from launch_chunk_rev in p.ws
+hipError_t launch_rev(const RevParams& p, int nchains, int DK, int DV, bool bf16, hipStream_t stream) {
+    return bf16 ? launch_rev_dt<bf16_t>(p, nchains, DK, DV, stream) : launch_rev_dt<float>(p, nchains, DK, DV, stream);
+}
+}  // namespace ckda

@@ -35,18 +35,15 @@
  *    states (B*H or N*H) must each stay below 2^31; larger problems fail
  *    with CKDA_ERR_UNSUPPORTED before anything is enqueued.
  *  - Outputs must not alias inputs (except the in/out decode state).
- *  - Gate range: g must be finite.  The forward calls are exact over the
- *    pages' whole range (g <= 0, i.e. |alpha| <= 1, down to any magnitude):
- *    the intra-chunk products factor exp(b_r - b_i) through anchors inside
- *    each half chunk while every 16-token run of log-gates in every channel
- *    stays above about -66.5 (an average |alpha| above about 0.016), and a
- *    chunk that leaves that range (or has any g > 0) is recomputed entry by
- *    entry with the exponent taken whole.  g > 0 (|alpha| > 1) lies outside
- *    the pages' range; it is computed exactly while nothing overflows.
- *    The backward (ckda_bwd, ckda_bwd_varlen) factors through one anchor per
- *    chunk: every 32-token run of log-gates in every channel must stay above
- *    about -80 (an average |alpha| above about 0.08); below that its
- *    gradients are not accurate.
+ *  - Gate range: g must be finite.  The forward and backward calls are exact
+ *    over the pages' whole range (g <= 0, i.e. |alpha| <= 1, down to any
+ *    magnitude): the intra-chunk products factor exp(b_r - b_i) through
+ *    anchors inside each half chunk while every 16-token run of log-gates in
+ *    every channel stays above about -66.5 (an average |alpha| above about
+ *    0.016), and a chunk that leaves that range (or has any g > 0) is
+ *    recomputed entry by entry with the exponent taken whole.  g > 0
+ *    (|alpha| > 1) lies outside the pages' range; it is computed exactly
+ *    while nothing overflows.
  */
 #ifndef CKDA_H
 #define CKDA_H
@@ -58,7 +55,7 @@
 extern "C" {
 #endif
 
-#define CKDA_ABI_VERSION 7
+#define CKDA_ABI_VERSION 8
 
 typedef enum {
     CKDA_OK = 0,
@@ -246,12 +243,11 @@ ckda_status_t ckda_decode_step(int N, int H, int DK, int DV, ckda_dtype_t in_dty
  *   (flags & CKDA_GATE_HEAD: g, s and dg are [B,T,H]; dg is then the sum
  *   over channels of the channel-gate gradient)
  *   dh0: [B,H,DK,DV] f32 or NULL
- *   workspace: ckda_bwd_workspace_bytes(...) bytes of device memory: the
- *           per-(chunk, head) blocks of the chunk-parallel passes, room for
- *           recomputed checkpoints, then the segment buffers of the reverse
- *           pass (see ckda_set_segment_chunks).  Less is accepted down to the
- *           blocks (plus the checkpoint room when h_ckpt is NULL); the
- *           reverse pass then walks whole chains.
+ *   workspace: ckda_bwd_workspace_bytes(...) bytes of device memory: per
+ *           (chunk, head) the blocks of the chunk-parallel passes and the
+ *           reverse pass's dU and chunk-end state gradient, then room for
+ *           recomputed checkpoints.  Less is accepted down to the part before
+ *           that room when h_ckpt is given.
  * dg is the gradient w.r.t. g = log|alpha| (alpha * dL/dalpha); s gets none.
  * ---------------------------------------------------------------------- */
 size_t ckda_bwd_workspace_bytes(int B, int T, int H, int DK, int DV);

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.ckda_abi_version() == 7
+    assert L.ckda_abi_version() == 8
     assert L.ckda_status_string(0) == b"ok"
     for st in range(1, 8):
         assert L.ckda_status_string(st) not in (b"ok", b"unknown status")
@@ -77,10 +77,19 @@ def seg_bytes(nsslots, H, DK, DV):
     return nsslots * H * (2 * DK * DV + DK * DK) * 4
 
 
-def bwd_block_bytes(DK, DV):
-    """Backward workspace per chunk-head: 9 [64 x DK], 6 [64 x DV], 1 [DK x DV]
-    and 10 [64 x 64] fp32 matrices, 3 [DK] and 3 [64] vectors."""
-    return 4 * (9 * 64 * DK + 6 * 64 * DV + DK * DV + 10 * 64 * 64 + 3 * DK + 3 * 64)
+def bwd_layout(NC, DK, DV):
+    """Backward workspace for NC chunk-heads: (bytes without checkpoint room,
+    checkpoint room).  Per chunk-head one block of the larger of the reverse
+    record (KB [64 x DK], Qh^T and W^T [DK x 64], M^T [64 x 64] at 4 bytes an
+    element, d [DK] fp32, a flag word) and the first gradient phase's output
+    (dA, dM [64 x 64] and U [64 x DV] at 4 bytes), each padded to 256 bytes;
+    then dU [64 x DV], G [max(DK, 64) x DV] and a flag word per chunk-head;
+    then the checkpoints [DK x DV], fp32, each region 256-byte aligned."""
+    rev = align256(4 * (3 * 64 * DK + 64 * 64) + 4 * DK + 4)
+    go = align256(4 * (2 * 64 * 64 + 64 * DV))
+    base = (align256(NC * max(rev, go)) + align256(NC * 64 * DV * 4) + align256(NC * max(DK, 64) * DV * 4)
+            + align256(NC * 4))
+    return base, align256(NC * DK * DV * 4)
 
 
 def test_fwd_workspace(L):
@@ -135,14 +144,10 @@ def test_varlen_backward_boundary(L):
     # chunk slots: ceil(T_total / 64) + N; one workspace block per (slot, head)
     assert L.ckda_varlen_chunk_slots(3, 100) == 2 + 3
     assert L.ckda_varlen_chunk_slots(-1, 100) == 0
-    # one backward workspace block per (chunk slot, head), then the segment
-    # buffers of the reverse pass (segments of 16 chunks)
-    # then room for recomputed checkpoints (one DK x DV state per block)
-    one = bwd_block_bytes(64, 32)
-    assert L.ckda_bwd_workspace_bytes(1, 64, 1, 64, 32) == \
-        align256(one) + align256(64 * 32 * 4) + seg_bytes(1, 1, 64, 32)
-    assert L.ckda_bwd_varlen_workspace_bytes(3, 100, 2, 64, 32) == \
-        align256((2 + 3) * 2 * one) + align256((2 + 3) * 2 * 64 * 32 * 4) + seg_bytes(1 + 3, 2, 64, 32)
+    # per-chunk-head blocks and buffers, then room for recomputed checkpoints
+    assert L.ckda_bwd_workspace_bytes(1, 64, 1, 64, 32) == sum(bwd_layout(1, 64, 32))
+    assert L.ckda_bwd_workspace_bytes(2, 100, 3, 32, 128) == sum(bwd_layout(2 * 2 * 3, 32, 128))
+    assert L.ckda_bwd_varlen_workspace_bytes(3, 100, 2, 64, 32) == sum(bwd_layout((2 + 3) * 2, 64, 32))
     assert L.ckda_bwd_varlen_workspace_bytes(3, 100, 2, 48, 32) == 0
     assert bwd_varlen(L, [1, 5], 1, 5) == 5                       # does not start at 0
     assert bwd_varlen(L, [0, 5, 3], 2, 3) == 5                    # decreasing
@@ -150,11 +155,11 @@ def test_varlen_backward_boundary(L):
     assert bwd_varlen(L, [0, 5], 1, 5, DK=96) == 4
     assert bwd_varlen(L, [0, 5], 1, 5, dt=9) == 3
     # no checkpoints: recomputed, which needs room for them beyond the blocks
-    assert bwd_varlen(L, [0, 5], 1, 5, hc=None, wsb=2 * bwd_block_bytes(32, 32)) == 6
+    assert bwd_varlen(L, [0, 5], 1, 5, hc=None, wsb=bwd_layout(2, 32, 32)[0]) == 6
     assert b"recomputed" in L.ckda_last_error()
     assert bwd_varlen(L, [0, 5], 1, 5, q=P(0x1004)) == 4          # misaligned
     # below the per-chunk blocks (2 chunk slots) the call fails before any launch
-    assert bwd_varlen(L, [0, 5], 1, 5, wsb=2 * bwd_block_bytes(32, 32) - 16) == 6
+    assert bwd_varlen(L, [0, 5], 1, 5, wsb=bwd_layout(2, 32, 32)[0] - 16) == 6
     assert bwd_varlen(L, [0], 0, 0) == 0                          # no documents
 
 

@@ -7,8 +7,8 @@
   the exact path, which forms the intra-chunk products entry by entry.  Both
   sides of that boundary are run, on half of the channels, the other half
   keeping ordinary gates, with chunks of both kinds in one call.  The
-  backward anchors at the chunk middle and needs 32-token partial sums above
-  -80.
+  backward's chunk-parallel passes use the same anchors, envelope and exact
+  path, and are run over the same gates.
 - beta = 0: nothing is written; the initial state only decays and rotates
   sign (o_t = scale (Diag(alpha_1 ... alpha_t) S0)^T q_t).
 - beta = 2 with |alpha| = 1 (g = 0) and random signs: every transition is
@@ -163,15 +163,127 @@ def test_head_gate_deep(dtype):
     assert e_o < TOL[dtype] and e_h < TOL[dtype]
 
 
-@pytest.mark.parametrize("dtype,DK,DV", [("f32", 64, 64), ("bf16", 128, 128)])
-def test_backward_gates_at_the_anchor_limit(dtype, DK, DV):
-    """Even channels decay by e^-2.45 every token (32-token runs sum to
-    -78.4): the backward's own anchor limit."""
+@pytest.mark.parametrize("dtype,DK,DV,gdeep", [("f32", 64, 64, -2.45), ("bf16", 128, 128, -2.45),
+                                              ("f32", 64, 64, -4.0), ("bf16", 128, 128, -4.0),
+                                              ("f32", 64, 64, -4.9), ("bf16", 128, 128, -4.9),
+                                              ("f32", 128, 128, -8.0), ("bf16", 128, 128, -8.0),
+                                              ("f32", 64, 128, -40.0), ("bf16", 128, 64, -40.0),
+                                              ("f32", 32, 32, -40.0)])
+def test_backward_deep_gates(dtype, DK, DV, gdeep):
+    """The backward over the forward's deep-gate cases: even channels decay by
+    e^gdeep every token (16-token runs of -39.2, -64, -78.4, -128, -640),
+    odd channels keep the workload's gates; every gradient and dh0 against
+    the oracle."""
     require_gpu()
-    banner(f"bwd strong gates {dtype} DK={DK} DV={DV}")
-    w = I.make_forward(1, 200, 2, DK, DV, dtype, seed=502, h0_std=0.3)
-    w.tok.g[..., 0::2] = -2.45
+    banner(f"bwd deep gates g={gdeep} {dtype} DK={DK} DV={DV}")
+    w = I.make_forward(2, 200, 2, DK, DV, dtype, seed=502, h0_std=0.3)
+    w.tok.g[..., 0::2] = gdeep
     check_bwd(w, dtype, seed=503, scale=0.8)
+
+
+@pytest.mark.parametrize("dtype,DK,DV", [("f32", 64, 64), ("bf16", 128, 128)])
+def test_backward_deep_bursts_inside_chunks(dtype, DK, DV):
+    """Tokens 20..27 of every second chunk decay by e^-30 on even channels:
+    flagged and unflagged chunks meet in one reverse pass."""
+    require_gpu()
+    banner(f"bwd deep bursts {dtype} DK={DK} DV={DV}")
+    w = I.make_forward(2, 300, 2, DK, DV, dtype, seed=512, h0_std=0.3)
+    for c0 in range(64, 300, 128):
+        w.tok.g[:, c0 + 20:c0 + 28, :, 0::2] = -30.0
+    check_bwd(w, dtype, seed=516, scale=0.8)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_positive_gates(dtype):
+    """g > 0 on a few tokens and channels (outside the pages' range): the
+    exact variants of the backward's chunk passes."""
+    require_gpu()
+    banner(f"bwd positive gates {dtype}")
+    w = I.make_forward(1, 200, 2, 64, 64, dtype, seed=513, h0_std=0.3)
+    w.tok.g[:, 10::37, :, 0::3] = 0.4
+    check_bwd(w, dtype, seed=517, scale=0.8)
+
+
+@pytest.mark.parametrize("dtype,DK,DV", [("f32", 64, 64), ("bf16", 128, 128)])
+def test_varlen_backward_deep_gates(dtype, DK, DV):
+    """Ragged documents, the second and fourth with e^-40 decay on even
+    channels (exact variants), the others ordinary; per document against the
+    oracle's backward on that document alone."""
+    torch = require_gpu()
+    from gated_delta_rule_sign_amd import ckda
+    banner(f"varlen backward deep gates {dtype} DK={DK} DV={DV}")
+    lens = [70, 129, 1, 200, 64]
+    cu = I.cu_from_lengths(lens)
+    Tt, H, N = int(cu[-1]), 2, len(lens)
+    rng = np.random.default_rng(518)
+    tok = I.draw_tokens(rng, (Tt,), H, DK, DV, dtype)
+    for n in (1, 3):
+        tok.g[cu[n]:cu[n + 1], :, 0::2] = -40.0
+    h0 = I.draw_state(rng, (N, H, DK, DV), 0.3)
+    do = I.to_storage(rng.standard_normal((Tt, H, DV)), dtype)
+    dht = rng.standard_normal((N, H, DK, DV)).astype(np.float32)
+    d = tok_to_dev(tok)
+    cu_t = torch.from_numpy(cu)
+    _, _, hc = ckda.fwd_varlen(**d, cu_seqlens=cu_t, scale=0.9, h0=dev_tensor(h0), want_ckpt=True)
+    r = ckda.bwd_varlen(**d, cu_seqlens=cu_t, h_ckpt=hc, do=dev_tensor(do), scale=0.9, h0=dev_tensor(h0),
+                        dht=dev_tensor(dht))
+    torch.cuda.synchronize()
+    got = {k: host(v) for k, v in r.items()}
+    f = tok.f64()
+    dof = I.widen(do)
+    names = ("dq", "dk", "dv", "dg", "dbeta")
+    g_all = {k: [] for k in names}
+    r_all = {k: [] for k in names}
+    for n in range(N):
+        a, b = int(cu[n]), int(cu[n + 1])
+        sl = {k: f[k][a:b][None] for k in ("q", "k", "v", "g", "s", "beta")}
+        ref = oracle.bwd(**sl, do=dof[a:b][None], scale=0.9, h0=h0[n][None].astype(np.float64),
+                         dht=dht[n][None].astype(np.float64))
+        for k in names:   # oracle chains are (0, h): [H, len, ...] -> [len, H, ...]
+            g_all[k].append(got[k][a:b])
+            r_all[k].append(np.moveaxis(ref[k], 0, 1))
+        e = rel_max(got["dh0"][n], ref["dh0"])
+        assert e < TOL[dtype], ("dh0", n, e)
+    for k in names:
+        e = rel_max(np.concatenate(g_all[k]), np.concatenate(r_all[k]))
+        print(f"  {k}: {e:.2e}")
+        assert e < TOL[dtype], (k, e)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_head_gate_backward_deep(dtype):
+    """One gate per (token, head), e^-40 on the first head, ordinary on the
+    second: dg per (token, head) against the oracle's channel-gate gradient
+    summed over the channels."""
+    import torch
+    from gated_delta_rule_sign_amd import ckda
+    require_gpu()
+    banner(f"bwd head gate deep {dtype}")
+    w = I.make_forward(1, 200, 2, 64, 64, dtype, seed=519, h0_std=0.3, gate="head")
+    w.tok.g[:, :, 0] = -40.0
+    B, T, H, DK = w.tok.q.shape
+    DV = w.tok.v.shape[-1]
+    rng = np.random.default_rng(520)
+    do = I.to_storage(rng.standard_normal((B, T, H, DV)), dtype)
+    d = tok_to_dev(w.tok)
+    h0 = dev_tensor(w.h0)
+    _, _, hc = ckda.fwd(**d, scale=0.8, h0=h0, want_ckpt=True)
+    r = ckda.bwd(**d, h_ckpt=hc, do=dev_tensor(do), scale=0.8, h0=h0)
+    torch.cuda.synchronize()
+    tok = w.tok.f64()
+    tok["g"] = np.repeat(tok["g"][..., None], DK, axis=-1)
+    tok["s"] = np.repeat(tok["s"][..., None], DK, axis=-1)
+    ref = oracle.bwd(**tok, do=I.widen(do), scale=0.8, h0=w.h0.astype(np.float64))
+    bi = [0, 0]; hi = [0, 1]
+    for name in ("dq", "dk", "dv", "dbeta"):
+        g = host(r[name])
+        g = g[bi, :, hi] if g.ndim == 3 else g[bi, :, hi, :]
+        e = rel_max(g, ref[name])
+        print(f"  {name}: {e:.2e}")
+        assert e < TOL[dtype], (name, e)
+    e = rel_max(host(r["dg"])[bi, :, hi], ref["dg"].sum(axis=-1))
+    print(f"  dg (head): {e:.2e}")
+    assert e < TOL[dtype]
 
 
 @pytest.mark.parametrize("dtype,DK,DV", [("f32", 64, 128), ("bf16", 128, 64)])
