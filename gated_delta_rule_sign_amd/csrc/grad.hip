@@ -34,6 +34,8 @@
 // 47, as in the chunk-local forward; chunks outside that envelope (flagged by
 // the reverse-record pass) are skipped here and redone by the exact variant,
 // which forms the Gamma-weighted sums entry by entry.
+#include <type_traits>
+
 #include "ckda_device.h"
 #include "ckda_launch.h"
 #include "ckda_mfma.h"
@@ -43,9 +45,9 @@
 
 namespace ckda {
 
-template <int DK, int DV, bool EX>
+template <int DK, int DV, bool EX, int CW = DK>
 struct Grad2Shape {
-    static constexpr int NW = DK / 16;   // waves: one 16-channel tile each
+    static constexpr int NW = CW / 16;   // waves: one 16-channel tile each
     static constexpr int PA = 64 + 8;    // dA, dM pitch (elements)
     static constexpr int PV = DV + 8;    // dV, U pitch
     // phase a: dV and U, the A operands over the value channels
@@ -105,10 +107,14 @@ __device__ __forceinline__ DF df_add(DF a, DF b) {
 // e^x for x in natural units, clamped like exp2_clamped
 __device__ __forceinline__ float ex2n(float x) { return __builtin_amdgcn_exp2f(fminf(x * kLog2e, 126.f)); }
 
-template <typename Tin, int DK, int DV, bool HG, bool NQK, bool EX>
-__device__ __forceinline__ void grad2_body(const Grad2Params& p, const int slot, const int h, unsigned char* smem)
+// CW: key channels per workgroup (DK, or 64 of DK = 128 when no per-token sum
+// over all channels is needed: two workgroups per chunk-head, part 0 and 1)
+template <typename Tin, int DK, int DV, bool HG, bool NQK, bool EX, int CW>
+__device__ __forceinline__ void grad2_body(const Grad2Params& p, const int slot, const int h, const int part,
+                                           unsigned char* smem)
 {
-    using SH = Grad2Shape<DK, DV, EX>;
+    static_assert(CW == DK || (!HG && !NQK && !EX), "sums over all channels need the whole head in one workgroup");
+    using SH = Grad2Shape<DK, DV, EX, CW>;
     constexpr bool F32 = sizeof(Tin) == 4;
     using PR = Prec<F32>;
     using GO = GradOut<DK, DV, F32>;
@@ -140,7 +146,7 @@ __device__ __forceinline__ void grad2_body(const Grad2Params& p, const int slot,
     const int tid = EX ? opaque_tid() : static_cast<int>(threadIdx.x);
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63, n = l & 15, gq = l >> 4;
-    const int c = 16 * w + n;
+    const int c = CW * part + 16 * w + n;
     const unsigned char* const go = p.gout + ch * p.gout_bytes;
     float* const red = reinterpret_cast<float*>(smem + SH::L_RED);
     float* const inv = reinterpret_cast<float*>(smem + SH::L_INV);
@@ -155,24 +161,40 @@ __device__ __forceinline__ void grad2_body(const Grad2Params& p, const int slot,
     const size_t row0 = static_cast<size_t>(tok0) * H + h;
     const uint32_t rows = static_cast<uint32_t>((L - 1) * H + 1);   // token-head rows spanned
     constexpr int ES_IN = sizeof(Tin);
-    for (int u = tid; u < 64 * (DV / 8); u += NT) {
-        const int t = u / (DV / 8), v0 = 8 * (u % (DV / 8));
-        const float* src = p.dv + (row0 + static_cast<size_t>(min(t, L - 1)) * H) * DV + v0;
-        const float4 a = reinterpret_cast<const float4*>(src)[0], b = reinterpret_cast<const float4*>(src)[1];
-        float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        if (t >= L) {
+    {   // every load first, then the LDS writes (rows past the chunk read as 0)
+        constexpr int NV = 64 * (DV / 8);                      // dV: 8-element units
+        constexpr int UPR = DV * GO::ES / 16;                  // U: 16-byte units per row and plane
+        constexpr int NU = GO::NP * 64 * UPR;
+        constexpr int KV = (NV + NT - 1) / NT, KU = (NU + NT - 1) / NT;
+        const __amdgpu_buffer_rsrc_t rdv = buffer_rsrc(p.dv + row0 * DV, rows * DV * 4);
+        u32x4 xv[KV][2], xu[KU];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        for (int k = 0; k < KV; ++k) {
+            const int u = tid + k * NT, t = (u / (DV / 8)) & 63, v0 = 8 * (u % (DV / 8));
+            const uint32_t off = static_cast<uint32_t>(t * H * DV + v0) * 4;
+            xv[k][0] = buffer_load_u32x4(rdv, off, 0);
+            xv[k][1] = buffer_load_u32x4(rdv, off, 16);
         }
-        PR::store8(dvm, t, v0, x);
-    }
-    {
-        constexpr int UPR = DV * GO::ES / 16;   // 16-byte units per row and plane
-        for (int u = tid; u < GO::NP * 64 * UPR; u += NT) {
+#pragma unroll
+        for (int k = 0; k < KU; ++k) {
+            const int u = min(tid + k * NT, NU - 1);
             const int pl = u / (64 * UPR), rr = (u / UPR) % 64, cu = u % UPR;
-            *reinterpret_cast<u32x4*>(smem + SH::L_U + (pl * 64 + rr) * SH::PV * GO::ES + cu * 16) =
-                *reinterpret_cast<const u32x4*>(go + GO::OFF_U + pl * GO::U_PLANE + static_cast<size_t>(rr) * GO::U_ROW +
-                                                cu * 16);
+            xu[k] = *reinterpret_cast<const u32x4*>(go + GO::OFF_U + pl * GO::U_PLANE + static_cast<size_t>(rr) * GO::U_ROW +
+                                                    cu * 16);
+        }
+#pragma unroll
+        for (int k = 0; k < KV; ++k) {
+            const int u = tid + k * NT, t = (u / (DV / 8)) & 63, v0 = 8 * (u % (DV / 8));
+            const f32x4 a = __builtin_bit_cast(f32x4, xv[k][0]), b = __builtin_bit_cast(f32x4, xv[k][1]);
+            const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+            if (NV % NT == 0 || u < NV) PR::store8(dvm, t, v0, x);
+        }
+#pragma unroll
+        for (int k = 0; k < KU; ++k) {
+            const int u = tid + k * NT;
+            const int pl = u / (64 * UPR), rr = (u / UPR) % 64, cu = u % UPR;
+            if (NU % NT == 0 || u < NU)
+                *reinterpret_cast<u32x4*>(smem + SH::L_U + (pl * 64 + rr) * SH::PV * GO::ES + cu * 16) = xu[k];
         }
     }
 
@@ -191,25 +213,47 @@ __device__ __forceinline__ void grad2_body(const Grad2Params& p, const int slot,
         aB[J] = aQ[J];
     }
     float sgs = 0.f;   // sum over the lane's value slots of G S0 (its channel)
+    // S0, G and dO of value step kv (two 4-slot halves each), loaded one step
+    // ahead of the products that use them
+    constexpr int NKV = DV / 32;
+    using DOF = std::conditional_t<F32, f32x4, u32x2>;
+    f32x4 sv[2][2], gv[2][2];
+    DOF ov[2][4][2];
+    auto load_kv = [&](int kv, int slot) {
+        sv[slot][0] = __builtin_bit_cast(f32x4, buffer_load_u32x4(rS0, vS, 128 * kv));
+        sv[slot][1] = __builtin_bit_cast(f32x4, buffer_load_u32x4(rS0, vS, 128 * kv + 64));
+        gv[slot][0] = __builtin_bit_cast(f32x4, buffer_load_u32x4(rG, vS, 128 * kv));
+        gv[slot][1] = __builtin_bit_cast(f32x4, buffer_load_u32x4(rG, vS, 128 * kv + 64));
 #pragma unroll
-    for (int kv = 0; kv < DV / 32; ++kv) {
+        for (int J = 0; J < 4; ++J) {
+            const uint32_t so = static_cast<uint32_t>(16 * J * H * DV + 32 * kv) * ES_IN;
+            if constexpr (F32) {
+                ov[slot][J][0] = __builtin_bit_cast(f32x4, buffer_load_u32x4(rdO, vO, so));
+                ov[slot][J][1] = __builtin_bit_cast(f32x4, buffer_load_u32x4(rdO, vO, so + 64));
+            } else {
+                ov[slot][J][0] = buffer_load_u32x2(rdO, vO, so);
+                ov[slot][J][1] = buffer_load_u32x2(rdO, vO, so + 32);
+            }
+        }
+    };
+    load_kv(0, 0);
+#pragma unroll
+    for (int kv = 0; kv < NKV; ++kv) {
+        const int cur = kv & 1;
+        if (kv + 1 < NKV) load_kv(kv + 1, cur ^ 1);
         const int va = 32 * kv + 4 * gq, vb = va + 16;
-        const f32x4 s0a = __builtin_bit_cast(f32x4, buffer_load_u32x4(rS0, vS, 128 * kv));
-        const f32x4 s0b = __builtin_bit_cast(f32x4, buffer_load_u32x4(rS0, vS, 128 * kv + 64));
-        const f32x4 ga = __builtin_bit_cast(f32x4, buffer_load_u32x4(rG, vS, 128 * kv));
-        const f32x4 gb = __builtin_bit_cast(f32x4, buffer_load_u32x4(rG, vS, 128 * kv + 64));
+        const f32x4 s0a = sv[cur][0], s0b = sv[cur][1], ga = gv[cur][0], gb = gv[cur][1];
 #pragma unroll
         for (int e = 0; e < 4; ++e) sgs += s0a[e] * ga[e] + s0b[e] * gb[e];
         const typename PR::F8 BS = PR::regs8(s0a, s0b), BG = PR::regs8(ga, gb);
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
-            const uint32_t so = static_cast<uint32_t>(16 * J * H * DV + 32 * kv) * ES_IN;
             typename PR::F8 Ao;   // dO row 16J + n (bf16 inputs: exact in the hi plane)
             if constexpr (F32) {
-                Ao.a = __builtin_bit_cast(f32x4, buffer_load_u32x4(rdO, vO, so));
-                Ao.b = __builtin_bit_cast(f32x4, buffer_load_u32x4(rdO, vO, so + 64));
+                Ao.a = ov[cur][J][0];
+                Ao.b = ov[cur][J][1];
             } else {
-                const u32x2 x0 = buffer_load_u32x2(rdO, vO, so), x1 = buffer_load_u32x2(rdO, vO, so + 32);
+                const u32x2 x0 = ov[cur][J][0], x1 = ov[cur][J][1];
                 Ao.hi = __builtin_bit_cast(bf16x8, u32x4{x0.x, x0.y, x1.x, x1.y});
                 Ao.lo = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
             }
@@ -395,28 +439,60 @@ __device__ __forceinline__ void grad2_body(const Grad2Params& p, const int slot,
     const LdsMat dmm{smem + SH::L_DM, SH::PA, 64 * SH::PA};
     const LdsMat datm{smem + SH::L_DAT, SH::PA, 64 * SH::PA};
     const LdsMat dmtm{smem + SH::L_DMT, SH::PA, 64 * SH::PA};
-    {   // dA, dM as stored (row = output token), and transposed (fast variant)
-        constexpr int EPU = 16 / GO::ES;   // elements per 16-byte unit
-        constexpr int UPR = 64 / EPU;      // units per row
-        for (int u = tid; u < 2 * GO::NP * 64 * UPR; u += NT) {
-            const int mat = u / (GO::NP * 64 * UPR), rem = u % (GO::NP * 64 * UPR);
-            const int pl = rem / (64 * UPR), rr = (rem / UPR) % 64, cu = rem % UPR;
-            if (rr < 32 && cu >= UPR / 2) continue;   // block (0..31, 32..63): never read, never written
-            const u32x4 v = *reinterpret_cast<const u32x4*>(go + (mat ? GO::OFF_DM : GO::OFF_DA) + pl * GO::A_PLANE +
-                                                            static_cast<size_t>(rr) * GO::A_ROW + cu * 16);
+    {   // dA, dM as stored (row = output token) and, fast variant, transposed.
+        // The block (0..31, 32..63) is never written nor read.  Lanes walk
+        // rows, so the transposed writes (one row of the transpose per element
+        // column) go to consecutive words: bf16 packs rows 2r, 2r+1 of one
+        // column into one word; 32 row pairs of two 16-byte column units per
+        // wave meet 64 distinct banks at the 72-element pitch.
+        constexpr int EPU = 16 / GO::ES;                      // elements per 16-byte unit
+        constexpr int UPR = 64 / EPU;                         // units per row
+        constexpr int RPT = F32 ? 1 : 2;                      // rows per task
+        constexpr int RG = 64 / RPT;                          // row groups per unit column
+        constexpr int NTK = 2 * GO::NP * RG * UPR;            // tasks (both matrices, all planes)
+        constexpr int KT = (NTK + NT - 1) / NT;
+        u32x4 x[KT][RPT];
+        auto task = [&](int q, int& mat, int& pl, int& r0, int& cu) {
+            const int rg = q % RG;
+            cu = (q / RG) % UPR;
+            pl = (q / (RG * UPR)) % GO::NP;
+            mat = q / (RG * UPR * GO::NP);
+            r0 = RPT * rg;
+        };
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+            int mat, pl, r0, cu;
+            task(min(tid + k * NT, NTK - 1), mat, pl, r0, cu);
+            const unsigned char* src = go + (mat ? GO::OFF_DM : GO::OFF_DA) + pl * GO::A_PLANE + cu * 16;
+#pragma unroll
+            for (int r = 0; r < RPT; ++r)
+                x[k][r] = (r0 < 32 && cu >= UPR / 2)
+                              ? u32x4{0u, 0u, 0u, 0u}
+                              : *reinterpret_cast<const u32x4*>(src + static_cast<size_t>(r0 + r) * GO::A_ROW);
+        }
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+            const int q = tid + k * NT;
+            int mat, pl, r0, cu;
+            task(q, mat, pl, r0, cu);
+            if ((NTK % NT != 0 && q >= NTK) || (r0 < 32 && cu >= UPR / 2)) continue;
             unsigned char* const nat = smem + (mat ? SH::L_DM : SH::L_DA) + pl * 64 * SH::PA * GO::ES;
-            *reinterpret_cast<u32x4*>(nat + rr * SH::PA * GO::ES + cu * 16) = v;
+#pragma unroll
+            for (int r = 0; r < RPT; ++r)
+                *reinterpret_cast<u32x4*>(nat + (r0 + r) * SH::PA * GO::ES + cu * 16) = x[k][r];
             if constexpr (!EX) {
                 unsigned char* const tr = smem + (mat ? SH::L_DMT : SH::L_DAT) + pl * 64 * SH::PA * GO::ES;
                 if constexpr (F32) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        *reinterpret_cast<uint32_t*>(tr + (EPU * cu + e) * SH::PA * 4 + rr * 4) = v[e];
+                        *reinterpret_cast<uint32_t*>(tr + (EPU * cu + e) * SH::PA * 4 + r0 * 4) = x[k][0][e];
                 } else {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        *reinterpret_cast<uint16_t*>(tr + (EPU * cu + e) * SH::PA * 2 + rr * 2) =
-                            static_cast<uint16_t>(v[e >> 1] >> (16 * (e & 1)));
+                    for (int e = 0; e < 8; ++e) {
+                        const uint32_t lo = (x[k][0][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                        const uint32_t hi = (x[k][1][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                        *reinterpret_cast<uint32_t*>(tr + (EPU * cu + e) * SH::PA * 2 + r0 * 2) = lo | (hi << 16);
+                    }
                 }
             }
         }
@@ -649,17 +725,32 @@ __device__ __forceinline__ void grad2_body(const Grad2Params& p, const int slot,
     }
 }
 
-// one workgroup per (chunk slot, head), heads fastest
+// channels per workgroup of the fast kernel
+template <int DK, bool HG, bool NQK>
+constexpr int grad2_cw() { return (HG || NQK || DK <= 64) ? DK : 64; }
+
+// one workgroup per (chunk slot, head) and group of CW key channels, heads
+// fastest.  With two channel groups, groups of eight chunk-heads take eight
+// consecutive workgroups per channel group, so both halves of a chunk-head
+// land on the same XCD (workgroups go to the XCDs in turn), where the
+// operands both stage share its L2.
 template <typename Tin, int DK, int DV, bool HG, bool NQK>
-__global__ void __launch_bounds__(DK * 4, 2) ckda_grad2_kernel(Grad2Params p)
+__global__ void __launch_bounds__((grad2_cw<DK, HG, NQK>() * 4), 2) ckda_grad2_kernel(Grad2Params p, int nch)
 {
     extern __shared__ __align__(16) unsigned char smem[];
-    grad2_body<Tin, DK, DV, HG, NQK, false>(p, blockIdx.x / p.H, blockIdx.x % p.H, smem);
+    constexpr int CW = grad2_cw<DK, HG, NQK>();
+    int chh = blockIdx.x, part = 0;
+    if constexpr (CW < DK) {
+        chh = (blockIdx.x / 16) * 8 + (blockIdx.x & 7);
+        part = (blockIdx.x >> 3) & 1;
+        if (chh >= nch) return;
+    }
+    grad2_body<Tin, DK, DV, HG, NQK, false, CW>(p, chh / p.H, chh % p.H, part, smem);
 }
 
-// the exact variant over the flagged chunk-heads: workgroup x looks at
-// chunk-heads x*per .. x*per + per - 1 (per <= 64) and redoes the flagged
-// ones in turn
+// the exact variant over the flagged chunk-heads (whole heads): workgroup x
+// looks at chunk-heads x*per .. x*per + per - 1 (per <= 64) and redoes the
+// flagged ones in turn
 template <typename Tin, int DK, int DV, bool HG, bool NQK>
 __global__ void __launch_bounds__(DK * 4, 2) ckda_grad2_exact_kernel(Grad2Params p, int nch, int per)
 {
@@ -672,30 +763,32 @@ __global__ void __launch_bounds__(DK * 4, 2) ckda_grad2_exact_kernel(Grad2Params
         const int j = __builtin_ctzll(mask);
         mask &= mask - 1ull;
         const int chh = c0 + j;
-        grad2_body<Tin, DK, DV, HG, NQK, true>(p, chh / p.H, chh % p.H, smem);
+        grad2_body<Tin, DK, DV, HG, NQK, true, DK>(p, chh / p.H, chh % p.H, 0, smem);
         lds_sync();   // before the next chunk-head reuses LDS
     }
 }
 
 template <typename Tin, int DK, int DV, bool HG, bool NQK>
 static hipError_t launch_grad2_t(const Grad2Params& p, int nslots, hipStream_t stream) {
-    constexpr int LDS = Grad2Shape<DK, DV, false>::LDS, LDS_EX = Grad2Shape<DK, DV, true>::LDS;
-    const long long grid = static_cast<long long>(nslots) * p.H;
-    if (grid == 0) return hipSuccess;
+    constexpr int CW = grad2_cw<DK, HG, NQK>();
+    constexpr int LDS = Grad2Shape<DK, DV, false, CW>::LDS, LDS_EX = Grad2Shape<DK, DV, true>::LDS;
+    const long long nch = static_cast<long long>(nslots) * p.H;
+    if (nch == 0) return hipSuccess;
+    const long long grid = CW == DK ? nch : (nch + 7) / 8 * 16;
     auto kern = ckda_grad2_kernel<Tin, DK, DV, HG, NQK>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(DK * 4), LDS, stream, p);
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(CW * 4), LDS, stream, p, static_cast<int>(nch));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     auto kx = ckda_grad2_exact_kernel<Tin, DK, DV, HG, NQK>;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kx), hipFuncAttributeMaxDynamicSharedMemorySize, LDS_EX);
     if (e != hipSuccess) return e;
-    const int per = static_cast<int>(grid > 512 * 64LL ? 64 : (grid + 511) / 512);
-    const long long gx = (grid + per - 1) / per;
+    const int per = static_cast<int>(nch > 512 * 64LL ? 64 : (nch + 511) / 512);
+    const long long gx = (nch + per - 1) / per;
     hipLaunchKernelGGL(kx, dim3(static_cast<unsigned>(gx)), dim3(DK * 4), LDS_EX, stream, p,
-                       static_cast<int>(grid), per);
+                       static_cast<int>(nch), per);
     return hipGetLastError();
 }
 
