@@ -31,7 +31,10 @@
 //   flags   NC words;
 //   ckpt    NC x DK x DV floats, only when h_ckpt is NULL: the checkpoints of
 //           a forward pass run in the call (its records over blocks and dU,
-//           which a forward record never exceeds).
+//           which a forward record never exceeds);
+//   seg     the segment buffers of the reverse pass (segment mode, when the
+//           plan takes it and they fit): per segment slot and head its end G,
+//           H_s and P_s.
 #include "ckda_device.h"
 #include "ckda_launch.h"
 #include "ckda_record.h"
@@ -72,11 +75,10 @@ size_t bwd_ckpt_bytes(int nslots, int H, int DK, int DV) {
     return l.end_ckpt - l.off_ckpt;
 }
 
-// the whole layout, checkpoint room included (the reverse pass walks whole
-// chains, so no segment buffers follow)
+// the whole layout: checkpoint room, then the segment buffers for up to
+// nsslots_max segment slots
 size_t bwd_workspace_bytes_full(int nslots, int nsslots_max, int H, int DK, int DV) {
-    (void)nsslots_max;
-    return BwdLayout(nslots, H, DK, DV).end_ckpt;
+    return BwdLayout(nslots, H, DK, DV).end_ckpt + seg_buffer_bytes(nsslots_max, H, DK, DV);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t st) {
@@ -125,6 +127,19 @@ hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t st) {
     RevParams rp{};
     rp.ws = ws; rp.dout = a.dout; rp.dht = a.dht; rp.dh0 = a.dh0; rp.dU = du; rp.G = gg;
     rp.cu = a.cu; rp.scale = a.scale; rp.B = a.B; rp.T = a.T; rp.H = a.H; rp.ndocs = a.ndocs;
+    {   // segmented reverse pass when the plan takes it and the workspace has room
+        const bool varlen = a.cu != nullptr;
+        const size_t room = a.ws_bytes > lay.end_ckpt ? a.ws_bytes - lay.end_ckpt : 0;
+        rp.seg_len = rev_segment_plan(a.cu_host, varlen, a.ndocs, a.B, a.T, a.H, DK, DV, room, st);
+        if (rp.seg_len > 0) {
+            rp.nsslots = seg_slots(varlen, a.B, a.T, a.ndocs, rp.seg_len);
+            float* sb = reinterpret_cast<float*>(ws + lay.end_ckpt);
+            const size_t per = static_cast<size_t>(rp.nsslots) * a.H * DK * DV;
+            rp.seg_start = sb;
+            rp.seg_h = sb + per;
+            rp.seg_p = sb + 2 * per;
+        }
+    }
     CKDA_CHECK(launch_rev(rp, nchains, DK, DV, a.bf16, st));
     Grad1Args g1{};
     g1.flags = flags; g1.h_ckpt = ck; g1.dU = du; g1.dout = a.dout; g1.dv = a.dv; g1.dbeta = a.dbeta;

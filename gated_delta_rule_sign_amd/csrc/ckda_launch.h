@@ -109,7 +109,14 @@ struct RevParams {
     const int32_t* cu;         // varlen document starts (device), or nullptr
     float scale;
     int B, T, H, ndocs;
+    // segment mode (seg_len > 0 chunks per segment): per segment slot and
+    // head the end G of each segment, H_s (DK x DV) and P_s (DK x DK)
+    int seg_len, nsslots;
+    float *seg_start, *seg_h, *seg_p;
 };
+// the reverse pass's cost constants for plan_segments
+int rev_segment_plan(const int32_t* cu_host, bool varlen, int ndocs, int B, int T, int H, int DK, int DV,
+                     size_t seg_room, hipStream_t stream);
 hipError_t launch_rev(const RevParams& p, int nchains, int DK, int DV, bool bf16, hipStream_t stream);
 size_t rev_record_bytes(int DK, int DV, bool bf16);
 hipError_t launch_state(const FwdArgs& a, hipStream_t stream);

@@ -31,6 +31,7 @@
 #include "ckda_mfma.h"
 #include "ckda_prec.h"
 #include "ckda_record.h"
+#include "ckda_segments.h"
 #include "ckda_sync.h"
 
 namespace ckda {
@@ -42,6 +43,7 @@ struct RevShape {
     static constexpr int NT = 256;                 // threads per role
     static constexpr int BV = DV < 64 ? DV : 64;   // value columns per workgroup
     static constexpr int NSLICE = DV / BV;
+    static constexpr int NTS = (DK + BV - 1) / BV; // transition slices over the DK columns of P_s
     static constexpr int NWC = BV / 16;            // waves that own columns
     static constexpr int RT = DK / 16;             // 16-row tiles of G
     static constexpr int ES = RC::ES, NP = RC::NP;
@@ -90,17 +92,25 @@ struct RStage {
     }
 };
 
-template <typename Tin, int DK, int DV>
+// SEG: segment mode (phase 3 with OUT, phase 1 without); otherwise (OUT set)
+// whole chains.  Segment phase 1 walks every segment but a chain's first
+// (its value columns from zero, or from dht for the chain's last segment;
+// for the middle ones also DK transition columns from the identity with dO
+// switched off) and writes the segment's start G (last segment: into the
+// previous segment's end slot), H_s or P_s; phase 3 walks every segment from
+// its end G and writes the per-chunk outputs (and dh0 at the chain's start).
+template <typename Tin, int DK, int DV, bool SEG, bool OUT>
 __global__ void __launch_bounds__(512, 2) ckda_rev_kernel(RevParams p)
 {
     using SH = RevShape<Tin, DK, DV>;
     using RC = typename SH::RC;
     using PR = Prec<SH::F32>;
-    constexpr int RT = SH::RT, NP = SH::NP, NT = SH::NT, NWC = SH::NWC, NS = SH::NSLICE;
+    constexpr int RT = SH::RT, NP = SH::NP, NT = SH::NT, NWC = SH::NWC;
+    constexpr int NS = (SEG && !OUT) ? SH::NSLICE + SH::NTS : SH::NSLICE;
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int H = p.H;
-    const int nitems = p.cu ? p.ndocs * H : p.B * H;
+    const int nitems = SEG ? p.nsslots * H : (p.cu ? p.ndocs * H : p.B * H);
     int item, slice;
     {
         const int bid = blockIdx.x;
@@ -121,8 +131,27 @@ __global__ void __launch_bounds__(512, 2) ckda_rev_kernel(RevParams p)
             }
         }
     }
-    const int h = item % H, sidx = item / H;
+    const int h = item % H;
     const int NTC = (p.T + 63) / 64;
+    int sidx, seg = 0, ss = 0;
+    if (!SEG) {
+        sidx = item / H;
+    } else {
+        ss = item / H;
+        if (p.cu) {   // the document whose segment slots hold ss
+            int lo = 0, hi = p.ndocs - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (seg_slot0(p.cu[mid], mid, p.seg_len) <= ss) lo = mid; else hi = mid - 1;
+            }
+            sidx = lo;
+            seg = ss - seg_slot0(p.cu[lo], lo, p.seg_len);
+        } else {
+            const int nsegT = (NTC + p.seg_len - 1) / p.seg_len;
+            sidx = ss / nsegT;
+            seg = ss - sidx * nsegT;
+        }
+    }
     int tok0, len, slot0;
     if (p.cu) {
         tok0 = p.cu[sidx];
@@ -133,8 +162,22 @@ __global__ void __launch_bounds__(512, 2) ckda_rev_kernel(RevParams p)
         len = p.T;
         slot0 = sidx * NTC;
     }
-    const int nloop = (len + 63) / 64;
-    const int vt0 = (slice * SH::BV) / 16;
+    const int nchunks = (len + 63) / 64;
+    int jbeg = 0, nloop = nchunks, nseg = 1;
+    bool trans = false;
+    if (SEG) {
+        nseg = (nchunks + p.seg_len - 1) / p.seg_len;
+        trans = slice >= SH::NSLICE;
+        // phase 1: every segment but the first (transition slices: the middle
+        // ones); phase 3: every segment (a chain of no chunks has one)
+        const bool run = OUT ? seg < max(nseg, 1) : (seg > 0 && seg < nseg && (seg < nseg - 1 || !trans));
+        if (!run) return;   // the whole workgroup, before any barrier
+        jbeg = seg * p.seg_len;
+        nloop = max(0, min(p.seg_len, nchunks - jbeg));
+    }
+    const bool last = !SEG || seg >= nseg - 1;   // the walk starts at the chain's end (dht)
+    // first 16-column tile of the slice (transition slices: columns of P_s)
+    const int vt0 = ((trans ? slice - SH::NSLICE : slice) * SH::BV) / 16;
     const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
 
     // walk step j covers chunk nloop - 1 - j
@@ -150,7 +193,7 @@ __global__ void __launch_bounds__(512, 2) ckda_rev_kernel(RevParams p)
         constexpr int O_WT = NQT, O_D = O_WT + NWT, NB = O_D + ND_;
         static_assert(StKB::FULL && StMT::FULL && StQT::FULL && StWT::FULL, "unguarded staging loads");
         u32x4 ga[NA], gb[NB];
-#define CKDA_RREC(J) reinterpret_cast<const u32x4*>(p.ws + (static_cast<size_t>(slot0 + nloop - 1 - (J)) * H + h) * RC::BYTES + opaque_zero())
+#define CKDA_RREC(J) reinterpret_cast<const u32x4*>(p.ws + (static_cast<size_t>(slot0 + jbeg + nloop - 1 - (J)) * H + h) * RC::BYTES + opaque_zero())
 #define CKDA_RLOAD_A(J)                                                                                      \
         {                                                                                                    \
             const u32x4* g_ = CKDA_RREC(J);                                                                  \
@@ -219,16 +262,21 @@ __global__ void __launch_bounds__(512, 2) ckda_rev_kernel(RevParams p)
     const int vt = vt0 + wt;
     const int lane = threadIdx.x & 63;
 
-    // G: lane (n, g) holds rows 16rt + 4g + i of column 16vt + n; starts at dht
+    // G: lane (n, g) holds rows 16rt + 4g + i of column 16vt + n; starts at
+    // dht (the chain's end), at the segment's end G (phase 3), at zero (phase
+    // 1, middle segments) or at the identity (transition columns)
     f32x4 G[RT];
     {
         const int gq = lane >> 4, col = 16 * vt + (lane & 15);
+        const float* src = last ? p.dht : (OUT ? p.seg_start + (static_cast<size_t>(ss) * H + h) * DK * DV : nullptr);
+        const size_t soff = last ? st_off : 0;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * rt + 4 * gq + i;
-                G[rt][i] = (has_col && p.dht) ? p.dht[st_off + static_cast<size_t>(row) * DV + col] : 0.f;
+                G[rt][i] = trans ? (row == col ? 1.f : 0.f)
+                                 : ((has_col && src) ? src[soff + static_cast<size_t>(row) * DV + col] : 0.f);
             }
     }
     // dO tiles of walk step jj: lane (n, g) holds rows 16J + 4g + i of column
@@ -236,7 +284,7 @@ __global__ void __launch_bounds__(512, 2) ckda_rev_kernel(RevParams p)
     // clamped into the chunk so every load is unconditional
     const Tin* dO = static_cast<const Tin*>(p.dout);
     auto load_do = [&](int jj, f32x4 (&x)[4]) {
-        const int c0 = 64 * (nloop - 1 - jj);
+        const int c0 = 64 * (jbeg + nloop - 1 - jj);
         const int L = min(64, len - c0);
         const int gq = (opaque_tid() & 63) >> 4, col = 16 * vt + (lane & 15);
 #pragma unroll
@@ -246,14 +294,14 @@ __global__ void __launch_bounds__(512, 2) ckda_rev_kernel(RevParams p)
                 const int tt = 16 * J + 4 * gq + i;
                 const size_t idx = (static_cast<size_t>(tok0 + c0 + min(tt, L - 1)) * H + h) * DV + col;
                 const float v = Elem<Tin>::load(dO, idx);
-                x[J][i] = tt < L ? v : 0.f;
+                x[J][i] = (tt < L && !trans) ? v : 0.f;
             }
     };
     f32x4 dn[4];
     if (nloop > 0) load_do(0, dn);
     lds_sync();   // record of step 0 in LDS
     for (int j = 0; j < nloop; ++j) {
-        const int jc = nloop - 1 - j;    // chunk index within the chain
+        const int jc = jbeg + nloop - 1 - j;   // chunk index within the chain
         const size_t rslot = static_cast<size_t>(slot0 + jc) * H + h;
         f32x4 dOv[4];
 #pragma unroll
@@ -268,7 +316,7 @@ __global__ void __launch_bounds__(512, 2) ckda_rev_kernel(RevParams p)
             const float* dl = reinterpret_cast<const float*>(sm + SH::L_D);
             const int l = opaque_tid() & 63, n = l & 15, gq = l >> 4;
             const int col = 16 * vt + n;
-            {   // G at this chunk's end, for the chunk-parallel pass
+            if (OUT) {   // G at this chunk's end, for the chunk-parallel pass
                 const __amdgpu_buffer_rsrc_t grc = buffer_rsrc(p.G + rslot * DK * DV, has_col ? DK * DV * 4 : 0);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
@@ -320,7 +368,7 @@ __global__ void __launch_bounds__(512, 2) ckda_rev_kernel(RevParams p)
                 dU[R] = acc;
             }
             lds_sync();   // X: KB, MT consumed (the loaders refill them); QT, WT, d in LDS
-            {   // dU of this chunk (C/D tiles (R, vt), as u in the forward record)
+            if (OUT) {   // dU of this chunk (C/D tiles (R, vt), as u in the forward record)
                 float* du = p.dU + rslot * 64 * DV;
                 const __amdgpu_buffer_rsrc_t urc = buffer_rsrc(du, has_col ? 64 * DV * 4 : 0);
 #pragma unroll
@@ -347,27 +395,59 @@ __global__ void __launch_bounds__(512, 2) ckda_rev_kernel(RevParams p)
         }
         lds_sync();   // Y: step j consumed (the loaders refill QT, WT, d)
     }
-    if (p.dh0 && has_col) {
+    // where G at the walk's start goes: dh0 (the chain's start); phase 1: the
+    // previous segment's end G (the chain's last segment), H_s or P_s
+    float* dst = nullptr;
+    size_t pitch = DV;
+    if (!SEG || (OUT && seg == 0)) {
+        dst = p.dh0 ? p.dh0 + st_off : nullptr;
+    } else if (!OUT) {
+        if (seg == nseg - 1) {
+            dst = p.seg_start + (static_cast<size_t>(ss - 1) * H + h) * DK * DV;
+        } else if (trans) {
+            dst = p.seg_p + (static_cast<size_t>(ss) * H + h) * DK * DK;
+            pitch = DK;
+        } else {
+            dst = p.seg_h + (static_cast<size_t>(ss) * H + h) * DK * DV;
+        }
+    }
+    if (dst && has_col) {
         const int gq = lane >> 4, col = 16 * vt + (lane & 15);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                p.dh0[opaque_zero() + st_off + static_cast<size_t>(16 * rt + 4 * gq + i) * DV + col] = G[rt][i];
+                dst[opaque_zero() + static_cast<size_t>(16 * rt + 4 * gq + i) * pitch + col] = G[rt][i];
     }
 }
 
-template <typename Tin, int DK, int DV>
-static hipError_t launch_rev_t(const RevParams& p, int nchains, hipStream_t stream) {
+template <typename Tin, int DK, int DV, bool SEG, bool OUT>
+static hipError_t launch_rev_k(const RevParams& p, long long grid, hipStream_t stream) {
     using SH = RevShape<Tin, DK, DV>;
-    const long long grid = static_cast<long long>(nchains) * SH::NSLICE;
     if (grid == 0) return hipSuccess;
-    auto kern = ckda_rev_kernel<Tin, DK, DV>;
+    auto kern = ckda_rev_kernel<Tin, DK, DV, SEG, OUT>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, SH::LDS);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(512), SH::LDS, stream, p);
     return hipGetLastError();
+}
+
+// whole chains (p.seg_len == 0) or segments in three launches: phase 1, the
+// scan of the segment ends (from the chain's end backwards), phase 3
+template <typename Tin, int DK, int DV>
+static hipError_t launch_rev_t(const RevParams& p, int nchains, hipStream_t stream) {
+    using SH = RevShape<Tin, DK, DV>;
+    if (p.seg_len == 0) return launch_rev_k<Tin, DK, DV, false, true>(p, static_cast<long long>(nchains) * SH::NSLICE, stream);
+    const long long items = static_cast<long long>(p.nsslots) * p.H;
+    hipError_t e = launch_rev_k<Tin, DK, DV, true, false>(p, items * (SH::NSLICE + SH::NTS), stream);
+    if (e != hipSuccess) return e;
+    const SegScanParams sp{p.cu, p.T, p.H, p.seg_len, p.seg_start, p.seg_h, p.seg_p, 1};
+    hipLaunchKernelGGL((ckda_seg_scan_kernel<DK, DV>), dim3(static_cast<unsigned>(nchains * (DV / kScanCols))), dim3(256),
+                       0, stream, sp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_rev_k<Tin, DK, DV, true, true>(p, items * SH::NSLICE, stream);
 }
 
 template <typename Tin>
@@ -392,6 +472,20 @@ size_t rev_record_bytes(int DK, int DV, bool bf16) {
     CKDA_RB(128, 32) CKDA_RB(128, 64) CKDA_RB(128, 128)
 #undef CKDA_RB
     return 0;
+}
+
+// measured on MI355X (dk = dv = 128, bf16 records), in units of a lone
+// chain's chunk-step: about 0.45 workgroup chunk-steps per CU and unit when
+// every CU runs one; a phase-1 step (no per-chunk stores) about 0.9 of one;
+// a scan step about one unit
+constexpr SegCost kRevCost{0.45, 0.9, 1.0};
+
+int rev_segment_plan(const int32_t* cu_host, bool varlen, int ndocs, int B, int T, int H, int DK, int DV,
+                     size_t seg_room, hipStream_t stream) {
+    const int BV = DV < 64 ? DV : 64;
+    auto fits = [&](int G) { return seg_buffer_bytes(seg_slots(varlen, B, T, ndocs, G), H, DK, DV) <= seg_room; };
+    return plan_segments(chain_chunks(cu_host, varlen, ndocs, B, T), H, DV / BV, (DK + BV - 1) / BV, kRevCost,
+                         device_cus(stream), fits);
 }
 
 // reverse pass over nchains chains: records from launch_chunk_rev in p.ws

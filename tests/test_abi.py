@@ -144,10 +144,13 @@ def test_varlen_backward_boundary(L):
     # chunk slots: ceil(T_total / 64) + N; one workspace block per (slot, head)
     assert L.ckda_varlen_chunk_slots(3, 100) == 2 + 3
     assert L.ckda_varlen_chunk_slots(-1, 100) == 0
-    # per-chunk-head blocks and buffers, then room for recomputed checkpoints
-    assert L.ckda_bwd_workspace_bytes(1, 64, 1, 64, 32) == sum(bwd_layout(1, 64, 32))
-    assert L.ckda_bwd_workspace_bytes(2, 100, 3, 32, 128) == sum(bwd_layout(2 * 2 * 3, 32, 128))
-    assert L.ckda_bwd_varlen_workspace_bytes(3, 100, 2, 64, 32) == sum(bwd_layout((2 + 3) * 2, 64, 32))
+    # per-chunk-head blocks and buffers, room for recomputed checkpoints, then
+    # the segment buffers of the reverse pass (segments of 16 chunks)
+    assert L.ckda_bwd_workspace_bytes(1, 64, 1, 64, 32) == sum(bwd_layout(1, 64, 32)) + seg_bytes(1, 1, 64, 32)
+    assert L.ckda_bwd_workspace_bytes(2, 100, 3, 32, 128) == \
+        sum(bwd_layout(2 * 2 * 3, 32, 128)) + seg_bytes(2 * 1, 3, 32, 128)
+    assert L.ckda_bwd_varlen_workspace_bytes(3, 100, 2, 64, 32) == \
+        sum(bwd_layout((2 + 3) * 2, 64, 32)) + seg_bytes(1 + 3, 2, 64, 32)
     assert L.ckda_bwd_varlen_workspace_bytes(3, 100, 2, 48, 32) == 0
     assert bwd_varlen(L, [1, 5], 1, 5) == 5                       # does not start at 0
     assert bwd_varlen(L, [0, 5, 3], 2, 3) == 5                    # decreasing

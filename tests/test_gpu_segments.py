@@ -197,10 +197,10 @@ def test_long_64k_sampled():
 
 @pytest.mark.parametrize("dtype,DK,DV,T", [("f32", 64, 64, 2500), ("bf16", 128, 128, 3300), ("f32", 32, 128, 1100)])
 def test_segmented_reverse_pass(dtype, DK, DV, T):
-    """The segment setting on long chains: the forward's state pass is cut
-    into segments of 16 chunks while the backward's reverse pass walks whole
-    chains, so the gradients must not change with the setting; both against
-    the oracle."""
+    """The backward's reverse (dS) pass cut into segments of 16 chunks (the
+    map G' = A'_c G + B'_c is affine with independent value columns, as in
+    the forward): the same checkpoints, gradients with segments against
+    gradients with whole chains, and both against the oracle."""
     torch = require_gpu()
     from gated_delta_rule_sign_amd import ckda
     B, H = 2, 2
