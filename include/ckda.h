@@ -57,21 +57,22 @@ extern "C" {
 
 #define CKDA_ABI_VERSION 8
 
-typedef enum {
-    CKDA_OK = 0,
-    CKDA_ERR_NULL = 1,        /* a required pointer is NULL */
-    CKDA_ERR_SHAPE = 2,       /* a size is negative / inconsistent */
-    CKDA_ERR_DTYPE = 3,       /* unknown dtype code */
-    CKDA_ERR_UNSUPPORTED = 4, /* valid request the kernels do not implement */
-    CKDA_ERR_SEQLENS = 5,     /* cu_seqlens not 0-based, monotone, ending at T */
-    CKDA_ERR_WORKSPACE = 6,   /* workspace missing or too small */
-    CKDA_ERR_HIP = 7          /* the HIP runtime reported an error */
-} ckda_status_t;
+/* Status codes and dtype codes travel as fixed-width integers (any value a
+ * caller passes is well defined on both sides of the boundary; unknown
+ * values are errors, not undefined behaviour). */
+typedef int32_t ckda_status_t;
+#define CKDA_OK 0
+#define CKDA_ERR_NULL 1        /* a required pointer is NULL */
+#define CKDA_ERR_SHAPE 2       /* a size is negative / inconsistent */
+#define CKDA_ERR_DTYPE 3       /* unknown dtype code */
+#define CKDA_ERR_UNSUPPORTED 4 /* valid request the kernels do not implement */
+#define CKDA_ERR_SEQLENS 5     /* cu_seqlens not 0-based, monotone, ending at T */
+#define CKDA_ERR_WORKSPACE 6   /* workspace missing or too small */
+#define CKDA_ERR_HIP 7         /* the HIP runtime reported an error */
 
-typedef enum {
-    CKDA_F32 = 0,
-    CKDA_BF16 = 1
-} ckda_dtype_t;
+typedef int32_t ckda_dtype_t;
+#define CKDA_F32 0
+#define CKDA_BF16 1
 
 /* Options of the forward, decode and backward calls (bitwise OR; 0 = the
  * defaults):

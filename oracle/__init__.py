@@ -49,9 +49,12 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build(force=True)
-        lib = ctypes.CDLL(_LIB)
+        path = os.environ.get("CKDA_ORACLE_LIB")   # another build of the same source (sanitizer runs)
+        if not path:
+            if not os.path.exists(_LIB):
+                build(force=True)
+            path = _LIB
+        lib = ctypes.CDLL(path)
         dp = ctypes.POINTER(ctypes.c_double)
         i = ctypes.c_int
         lib.ckda_ref_fwd.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp, ctypes.c_double,
