@@ -170,6 +170,48 @@ def l2norm_bwd(x, dy) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# Optional gate map (the CKDA_GATE_MAP option).  The Complex KDA paper page,
+# section 3, paragraph "CKDA.", defines CKDA as KDA with gates in [-1, 1] and
+# the delta-rule coefficient beta in [0, 2], built with a signed gate and a
+# beta range extension after Sarrof et al. (2024) and Grazzi et al. (2025),
+# "with the magnitude floor and backward convention" of an appendix the pages
+# do not include; the formulas themselves did not survive.  Reading taken
+# here (parity unpinned for the floor and the gate's functional form):
+#   alpha = tanh(x)               (a signed gate in (-1, 1))
+#   s     = -1 if x < 0 else +1   (x = 0 counts as +1)
+#   g     = log max(|alpha|, e^GATE_LOG_FLOOR)   (the magnitude floor)
+#   beta  = 2 sigmoid(y)          (beta in (0, 2))
+# and the backward is the plain derivative: dg/dx = (1 - tanh^2 x) / tanh x
+# above the floor, 0 on it; s gets no gradient; dbeta/dy = beta (1 - beta/2).
+# ----------------------------------------------------------------------------
+GATE_LOG_FLOOR = -4.0
+
+
+def gate_map(x, y):
+    """(g, s, beta) from the gate pre-activation x and beta pre-activation y."""
+    x = np.asarray(x, np.float64)
+    y = np.asarray(y, np.float64)
+    t = np.abs(np.tanh(x))
+    with np.errstate(divide="ignore"):
+        g = np.maximum(np.log(t), GATE_LOG_FLOOR)
+    s = np.where(x < 0, -1.0, 1.0)
+    beta = 2.0 / (1.0 + np.exp(-y))
+    return g, s, beta
+
+
+def gate_map_bwd(x, y, dg, dbeta):
+    """(dL/dx, dL/dy) from dL/dg and dL/dbeta through gate_map."""
+    x = np.asarray(x, np.float64)
+    y = np.asarray(y, np.float64)
+    th = np.tanh(x)
+    above = np.abs(th) >= np.exp(GATE_LOG_FLOOR)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        dgdx = np.where(above, (1.0 - th * th) / np.where(above, th, 1.0), 0.0)
+    beta = 2.0 / (1.0 + np.exp(-y))
+    return np.asarray(dg, np.float64) * dgdx, np.asarray(dbeta, np.float64) * beta * (1.0 - 0.5 * beta)
+
+
+# ----------------------------------------------------------------------------
 # tensor-level entry points ([B, T, H, D] layout); qk_norm=True runs the
 # recurrence on l2norm(q), l2norm(k)
 # ----------------------------------------------------------------------------

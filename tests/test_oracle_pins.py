@@ -436,3 +436,46 @@ def test_qk_norm_is_scale_free_and_identity_on_unit_vectors():
     kz = k.copy(); kz[0, 5] = 0.0
     o4, _ = oracle.fwd(q, kz, v, g, s, beta, qk_norm=True)
     assert np.isfinite(o4).all()
+
+
+# ---------------------------------------------------------------------------
+# the optional gate map (a reading of the paper page, section 3 "CKDA.", whose
+# formulas and floor did not survive: parity unpinned for those; pinned here
+# are the ranges the paragraph fixes, the special points and the derivative)
+# ---------------------------------------------------------------------------
+def test_gate_map_ranges_and_special_points():
+    rng = np.random.default_rng(71)
+    x = np.concatenate([rng.standard_normal(4000) * 3.0, [0.0, -0.0, 1e-12, -1e-12, 50.0, -50.0]])
+    y = np.concatenate([rng.standard_normal(4000) * 4.0, [0.0, 0.0, 80.0, -80.0, 1.0, -1.0]])
+    g, s, beta = oracle.gate_map(x, y)
+    alpha = s * np.exp(g)
+    assert np.all(np.abs(alpha) <= 1.0) and np.all(g <= 0.0)            # gates in [-1, 1]
+    assert np.all(g >= oracle.GATE_LOG_FLOOR)                            # the magnitude floor
+    assert np.all((beta >= 0.0) & (beta <= 2.0))                         # beta in [0, 2]
+    assert np.array_equal(s, np.where(x < 0, -1.0, 1.0))                 # the sign of the pre-activation
+    # above the floor alpha is tanh(x) itself, on it |alpha| is the floor
+    keep = np.abs(np.tanh(x)) >= np.exp(oracle.GATE_LOG_FLOOR)
+    assert np.allclose(alpha[keep], np.tanh(x[keep]), rtol=1e-15, atol=0)
+    assert np.allclose(np.abs(alpha[~keep]), np.exp(oracle.GATE_LOG_FLOOR), rtol=1e-15)
+    assert g[-6] == oracle.GATE_LOG_FLOOR and s[-6] == 1.0               # x = 0: floored, +1
+    assert g[-2] == 0.0 and s[-1] == -1.0 and g[-1] == 0.0               # |x| large: |alpha| = 1
+    assert beta[-6] == 1.0 and abs(beta[-4] - 2.0) < 1e-15 and beta[-3] < 1e-30
+
+
+def test_gate_map_backward_matches_central_finite_differences():
+    rng = np.random.default_rng(72)
+    x = rng.standard_normal(500) * 2.0
+    x = x[np.abs(np.abs(np.tanh(x)) - np.exp(oracle.GATE_LOG_FLOOR)) > 1e-3]   # away from the floor's kink
+    y = rng.standard_normal(x.size) * 3.0
+    dg = rng.standard_normal(x.size)
+    db = rng.standard_normal(x.size)
+    dx, dy = oracle.gate_map_bwd(x, y, dg, db)
+    h = 1e-6
+    gp, _, bp = oracle.gate_map(x + h, y + h)
+    gm, _, bm = oracle.gate_map(x - h, y - h)
+    assert np.allclose(dx, dg * (gp - gm) / (2 * h), rtol=1e-6, atol=1e-8)
+    assert np.allclose(dy, db * (bp - bm) / (2 * h), rtol=1e-6, atol=1e-8)
+    # on the floor the map is flat: no gradient
+    xf = np.array([0.0, 1e-3, -1e-3, 0.01])
+    dxf, _ = oracle.gate_map_bwd(xf, np.zeros(4), np.ones(4), np.zeros(4))
+    assert np.all(dxf == 0.0)
