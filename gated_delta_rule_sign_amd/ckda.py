@@ -117,7 +117,7 @@ def _need(t: Optional[torch.Tensor], name: str, dtype=None, shape=None, device=N
         raise CkdaError(f"{name} must be contiguous")
 
 
-CKDA_GATE_CHANNEL, CKDA_GATE_HEAD, CKDA_QK_L2NORM = 0, 1, 2
+CKDA_GATE_CHANNEL, CKDA_GATE_HEAD, CKDA_QK_L2NORM, CKDA_GATE_MAP = 0, 1, 2, 4
 
 
 def _gate_code(g, lead) -> int:
@@ -125,9 +125,11 @@ def _gate_code(g, lead) -> int:
     return CKDA_GATE_HEAD if g.dim() == len(lead) + 1 else CKDA_GATE_CHANNEL
 
 
-def _flags(g, lead, qk_norm: bool) -> int:
-    """The flags word: gate layout from g's shape, plus CKDA_QK_L2NORM."""
-    return _gate_code(g, lead) | (CKDA_QK_L2NORM if qk_norm else 0)
+def _flags(g, lead, qk_norm: bool, gate_map: bool = False) -> int:
+    """The flags word: gate layout from g's shape, plus CKDA_QK_L2NORM and
+    CKDA_GATE_MAP (g and beta then hold the gate and beta pre-activations and
+    s may be None; the backward's dg and dbeta are taken w.r.t. them)."""
+    return _gate_code(g, lead) | (CKDA_QK_L2NORM if qk_norm else 0) | (CKDA_GATE_MAP if gate_map else 0)
 
 
 def _token_inputs(q, k, v, g, s, beta, lead):
@@ -183,7 +185,7 @@ def _workspace(workspace, need, dev):
 
 def fwd(q, k, v, g, s, beta, scale: float = 1.0, h0=None, want_ht: bool = True,
         want_ckpt: bool = False, o=None, ht=None, h_ckpt=None, workspace=None,
-        qk_norm: bool = False):
+        qk_norm: bool = False, gate_map: bool = False):
     """Chunked forward (ckda_fwd_chunked).  Inputs [B,T,H,D]; returns
     (o [B,T,H,DV] f32, ht [B,H,DK,DV] f32 or None, h_ckpt or None).
     ``workspace`` (uint8 GPU tensor of fwd_workspace_bytes) is allocated per
@@ -203,14 +205,14 @@ def fwd(q, k, v, g, s, beta, scale: float = 1.0, h0=None, want_ht: bool = True,
         h_ckpt = torch.empty((B, H, NT, DK, DV), dtype=torch.float32, device=dev)
     _need(h_ckpt, "h_ckpt", torch.float32, (B, H, NT, DK, DV), dev)
     workspace, wsb = _workspace(workspace, fwd_workspace_bytes(B, T, H, DK, DV, q.dtype), dev)
-    _check(lib().ckda_fwd_chunked(B, T, H, DK, DV, dt, _flags(g, (B, T), qk_norm), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
+    _check(lib().ckda_fwd_chunked(B, T, H, DK, DV, dt, _flags(g, (B, T), qk_norm, gate_map), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
                                   _ptr(beta), float(scale), _ptr(h0), _ptr(o), _ptr(ht),
                                   _ptr(h_ckpt), _ptr(workspace), wsb, _stream()))
     return o, ht, h_ckpt
 
 
 def fwd_noalloc(q, k, v, g, s, beta, o, ht=None, h0=None, h_ckpt=None, scale: float = 1.0,
-                qk_norm: bool = False):
+                qk_norm: bool = False, gate_map: bool = False):
     """ckda_fwd_chunked_noalloc: the chunked forward with the records in the
     library's fixed device scratch (no workspace, nothing allocated by the
     library or here).  The caller passes every output tensor (o, and ht /
@@ -221,7 +223,7 @@ def fwd_noalloc(q, k, v, g, s, beta, o, ht=None, h0=None, h_ckpt=None, scale: fl
     _need(o, "o", torch.float32, (B, T, H, DV), dev)
     _need(ht, "ht", torch.float32, (B, H, DK, DV), dev)
     _need(h_ckpt, "h_ckpt", torch.float32, (B, H, (T + CHUNK - 1) // CHUNK, DK, DV), dev)
-    _check(lib().ckda_fwd_chunked_noalloc(B, T, H, DK, DV, dt, _flags(g, (B, T), qk_norm), _ptr(q), _ptr(k),
+    _check(lib().ckda_fwd_chunked_noalloc(B, T, H, DK, DV, dt, _flags(g, (B, T), qk_norm, gate_map), _ptr(q), _ptr(k),
                                           _ptr(v), _ptr(g), _ptr(s), _ptr(beta), float(scale), _ptr(h0),
                                           _ptr(o), _ptr(ht), _ptr(h_ckpt), _stream()))
     return o, ht, h_ckpt
@@ -240,7 +242,7 @@ def varlen_chunk_slots(N, T_total) -> int:
 
 def fwd_varlen(q, k, v, g, s, beta, cu_seqlens, scale: float = 1.0, h0=None,
                want_ht: bool = True, cu_seqlens_dev=None, o=None, ht=None, workspace=None,
-               want_ckpt: bool = False, qk_norm: bool = False):
+               want_ckpt: bool = False, qk_norm: bool = False, gate_map: bool = False):
     """Packed-document forward (ckda_fwd_varlen).  q etc. are [T_total,H,D]
     (a leading 1 is accepted); cu_seqlens is an int32 CPU tensor [N+1].
     Returns (o, ht), or (o, ht, h_ckpt) with want_ckpt: the chunk-start
@@ -267,14 +269,14 @@ def fwd_varlen(q, k, v, g, s, beta, cu_seqlens, scale: float = 1.0, h0=None,
     if want_ckpt:
         hc = torch.empty((varlen_chunk_slots(N, Tt), H, DK, DV), dtype=torch.float32, device=dev)
     workspace, wsb = _workspace(workspace, fwd_varlen_workspace_bytes(N, Tt, H, DK, DV, q.dtype), dev)
-    _check(lib().ckda_fwd_varlen(N, Tt, _ptr(cu), _ptr(cu_seqlens_dev), H, DK, DV, dt, _flags(g, (Tt,), qk_norm),
+    _check(lib().ckda_fwd_varlen(N, Tt, _ptr(cu), _ptr(cu_seqlens_dev), H, DK, DV, dt, _flags(g, (Tt,), qk_norm, gate_map),
                                  _ptr(q),
                                  _ptr(k), _ptr(v), _ptr(g), _ptr(s), _ptr(beta), float(scale),
                                  _ptr(h0), _ptr(o), _ptr(ht), _ptr(hc), _ptr(workspace), wsb, _stream()))
     return (o, ht, hc) if want_ckpt else (o, ht)
 
 
-def decode_step(q, k, v, g, s, beta, state, sign_prod, scale: float = 1.0, o=None, qk_norm: bool = False):
+def decode_step(q, k, v, g, s, beta, state, sign_prod, scale: float = 1.0, o=None, qk_norm: bool = False, gate_map: bool = False):
     """One recurrent step (ckda_decode_step); state [N,H,DK,DV] f32 and
     sign_prod [N,H,DK] int8 are updated in place.  Returns o [N,H,DV] f32."""
     N = q.shape[0]
@@ -284,7 +286,7 @@ def decode_step(q, k, v, g, s, beta, state, sign_prod, scale: float = 1.0, o=Non
     if o is None:
         o = torch.empty((N, H, DV), dtype=torch.float32, device=dev)
     _need(o, "o", torch.float32, (N, H, DV), dev)
-    _check(lib().ckda_decode_step(N, H, DK, DV, dt, _flags(g, (N,), qk_norm), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
+    _check(lib().ckda_decode_step(N, H, DK, DV, dt, _flags(g, (N,), qk_norm, gate_map), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
                                   _ptr(beta), float(scale), _ptr(state), _ptr(sign_prod), _ptr(o),
                                   _stream()))
     return o
@@ -295,7 +297,7 @@ def bwd_workspace_bytes(B, T, H, DK, DV) -> int:
 
 
 def bwd(q, k, v, g, s, beta, h_ckpt, do, scale: float = 1.0, h0=None, dht=None,
-        want_dh0: bool = True, workspace=None, qk_norm: bool = False):
+        want_dh0: bool = True, workspace=None, qk_norm: bool = False, gate_map: bool = False):
     """Backward (ckda_bwd).  h_ckpt: the checkpoints of fwd(..., want_ckpt=True)
     on the same inputs, or None (the call recomputes them).  Returns dict dq,
     dk, dv, dg, dbeta, dh0 (f32)."""
@@ -316,7 +318,7 @@ def bwd(q, k, v, g, s, beta, h_ckpt, do, scale: float = 1.0, h0=None, dht=None,
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().ckda_bwd(B, T, H, DK, DV, dt, _flags(g, (B, T), qk_norm), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
+    _check(lib().ckda_bwd(B, T, H, DK, DV, dt, _flags(g, (B, T), qk_norm, gate_map), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
                           _ptr(beta), float(scale), _ptr(h0), _ptr(h_ckpt), _ptr(do), _ptr(dht),
                           _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
                           _ptr(out["dbeta"]), _ptr(out["dh0"]), _ptr(workspace), wsb, _stream()))
@@ -328,7 +330,7 @@ def bwd_varlen_workspace_bytes(N, T_total, H, DK, DV) -> int:
 
 
 def bwd_varlen(q, k, v, g, s, beta, cu_seqlens, h_ckpt, do, scale: float = 1.0, h0=None, dht=None,
-               want_dh0: bool = True, cu_seqlens_dev=None, workspace=None, qk_norm: bool = False):
+               want_dh0: bool = True, cu_seqlens_dev=None, workspace=None, qk_norm: bool = False, gate_map: bool = False):
     """Backward of the packed-document forward (ckda_bwd_varlen).  Shapes as
     in fwd_varlen; h_ckpt from fwd_varlen(..., want_ckpt=True), or None
     (recomputed); do
@@ -357,7 +359,7 @@ def bwd_varlen(q, k, v, g, s, beta, cu_seqlens, h_ckpt, do, scale: float = 1.0, 
                dbeta=torch.empty((Tt, H), **f32),
                dh0=torch.empty((N, H, DK, DV), **f32) if want_dh0 else None)
     workspace, wsb = _workspace(workspace, bwd_varlen_workspace_bytes(N, Tt, H, DK, DV), dev)
-    _check(lib().ckda_bwd_varlen(N, Tt, _ptr(cu), _ptr(cu_seqlens_dev), H, DK, DV, dt, _flags(g, (Tt,), qk_norm),
+    _check(lib().ckda_bwd_varlen(N, Tt, _ptr(cu), _ptr(cu_seqlens_dev), H, DK, DV, dt, _flags(g, (Tt,), qk_norm, gate_map),
                                  _ptr(q),
                                  _ptr(k), _ptr(v), _ptr(g), _ptr(s), _ptr(beta), float(scale),
                                  _ptr(h0), _ptr(h_ckpt), _ptr(do), _ptr(dht), _ptr(out["dq"]),

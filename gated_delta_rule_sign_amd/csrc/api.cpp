@@ -48,7 +48,7 @@ ckda_status_t check_dtype(ckda_dtype_t dt) {
 }
 
 ckda_status_t check_flags(ckda_flags_t flags) {
-    if (flags & ~(CKDA_GATE_HEAD | CKDA_QK_L2NORM))
+    if (flags & ~(CKDA_GATE_HEAD | CKDA_QK_L2NORM | CKDA_GATE_MAP))
         return fail(CKDA_ERR_UNSUPPORTED, "unknown option flags 0x%x", unsigned(flags));
     return CKDA_OK;
 }
@@ -258,7 +258,8 @@ ckda_status_t fwd_chunked_common(int B, int T, int H, int DK, int DV, ckda_dtype
         return fail(CKDA_ERR_UNSUPPORTED, "too many chunks");
     if (static_cast<long long>(B) * H >= (1LL << 31)) return fail(CKDA_ERR_UNSUPPORTED, "too many heads");
     if (B * H == 0) return ok();
-    if (T > 0) { CKDA_REQUIRE(q); CKDA_REQUIRE(k); CKDA_REQUIRE(v); CKDA_REQUIRE(g); CKDA_REQUIRE(s); CKDA_REQUIRE(beta); CKDA_REQUIRE(o); }
+    if (T > 0) { CKDA_REQUIRE(q); CKDA_REQUIRE(k); CKDA_REQUIRE(v); CKDA_REQUIRE(g); CKDA_REQUIRE(beta); CKDA_REQUIRE(o); }
+    if (T > 0 && !(flags & CKDA_GATE_MAP)) CKDA_REQUIRE(s);
     CKDA_ALIGNED(q); CKDA_ALIGNED(k); CKDA_ALIGNED(g); CKDA_ALIGNED(s); CKDA_ALIGNED(workspace);
     const int nslots = fwd_slots(B, T);
     const size_t need = ckda::fwd_workspace_bytes(nslots, H, DK, DV, in_dtype == CKDA_BF16);
@@ -281,7 +282,8 @@ ckda_status_t fwd_chunked_common(int B, int T, int H, int DK, int DV, ckda_dtype
     ckda::FwdArgs a{};
     a.B = B; a.T = T; a.H = H; a.DK = DK; a.DV = DV; a.bf16 = in_dtype == CKDA_BF16;
     a.head_gate = (flags & CKDA_GATE_HEAD) != 0; a.qk_norm = (flags & CKDA_QK_L2NORM) != 0;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.s = s; a.beta = beta; a.scale = scale;
+    a.gate_map = (flags & CKDA_GATE_MAP) != 0;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.s = s ? s : reinterpret_cast<const int8_t*>(g); a.beta = beta; a.scale = scale;
     a.h0 = h0; a.o = o; a.ht = ht; a.h_ckpt = h_ckpt; a.cu = nullptr; a.cu_host = nullptr; a.ndocs = 0;
     a.ws = workspace; a.ws_bytes = workspace_bytes;
     {
@@ -332,7 +334,8 @@ ckda_status_t ckda_fwd_varlen(int N, int T_total, const int32_t* cu, const int32
     CKDA_TRY(check_cu(N, T_total, cu));
     if (N * H == 0) return ok();
     CKDA_REQUIRE(cu_dev);
-    if (T_total > 0) { CKDA_REQUIRE(q); CKDA_REQUIRE(k); CKDA_REQUIRE(v); CKDA_REQUIRE(g); CKDA_REQUIRE(s); CKDA_REQUIRE(beta); CKDA_REQUIRE(o); }
+    if (T_total > 0) { CKDA_REQUIRE(q); CKDA_REQUIRE(k); CKDA_REQUIRE(v); CKDA_REQUIRE(g); CKDA_REQUIRE(beta); CKDA_REQUIRE(o); }
+    if (T_total > 0 && !(flags & CKDA_GATE_MAP)) CKDA_REQUIRE(s);
     CKDA_ALIGNED(q); CKDA_ALIGNED(k); CKDA_ALIGNED(g); CKDA_ALIGNED(s); CKDA_ALIGNED(workspace);
     const int nslots = varlen_slots(N, T_total);
     const size_t need = ckda::fwd_workspace_bytes(nslots, H, DK, DV, in_dtype == CKDA_BF16);
@@ -344,7 +347,8 @@ ckda_status_t ckda_fwd_varlen(int N, int T_total, const int32_t* cu, const int32
     ckda::FwdArgs a{};
     a.B = 1; a.T = T_total; a.H = H; a.DK = DK; a.DV = DV; a.bf16 = in_dtype == CKDA_BF16;
     a.head_gate = (flags & CKDA_GATE_HEAD) != 0; a.qk_norm = (flags & CKDA_QK_L2NORM) != 0;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.s = s; a.beta = beta; a.scale = scale;
+    a.gate_map = (flags & CKDA_GATE_MAP) != 0;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.s = s ? s : reinterpret_cast<const int8_t*>(g); a.beta = beta; a.scale = scale;
     a.h0 = h0; a.o = o; a.ht = ht; a.h_ckpt = h_ckpt;
     a.cu = cu_dev; a.cu_host = cu; a.ndocs = N; a.ws = workspace; a.ws_bytes = workspace_bytes;
     {
@@ -369,12 +373,14 @@ ckda_status_t ckda_decode_step(int N, int H, int DK, int DV, ckda_dtype_t in_dty
     CKDA_TRY(check_heads(DK, DV));
     if (static_cast<long long>(N) * H >= (1LL << 31)) return fail(CKDA_ERR_UNSUPPORTED, "too many heads");
     if (N * H == 0) return ok();
-    CKDA_REQUIRE(q); CKDA_REQUIRE(k); CKDA_REQUIRE(v); CKDA_REQUIRE(g); CKDA_REQUIRE(s);
+    CKDA_REQUIRE(q); CKDA_REQUIRE(k); CKDA_REQUIRE(v); CKDA_REQUIRE(g);
+    if (!(flags & CKDA_GATE_MAP)) CKDA_REQUIRE(s);
     CKDA_REQUIRE(beta); CKDA_REQUIRE(state); CKDA_REQUIRE(sign_prod); CKDA_REQUIRE(o);
     CKDA_ALIGNED(state); CKDA_ALIGNED(o);
+    // with the gate map s is never read (a NULL s stands in as g's address)
     ckda::DecodeArgs a{N, H, DK, DV, in_dtype == CKDA_BF16, (flags & CKDA_GATE_HEAD) != 0,
-                       (flags & CKDA_QK_L2NORM) != 0, q, k, v, g, s, beta,
-                       scale, state, sign_prod, o};
+                       (flags & CKDA_QK_L2NORM) != 0, (flags & CKDA_GATE_MAP) != 0, q, k, v, g,
+                       s ? s : reinterpret_cast<const int8_t*>(g), beta, scale, state, sign_prod, o};
     {   // state and sign_prod are updated in place: outputs here
         const TokBytes tb(static_cast<long long>(N) * H, DK, DV, a.bf16, a.head_gate);
         const size_t st = static_cast<size_t>(N) * H * DK * DV * 4;
@@ -406,7 +412,8 @@ namespace {
 ckda_status_t bwd_common(ckda::BwdArgs& a, int nslots, bool any_tokens, const void* workspace,
                          size_t workspace_bytes, ckda_stream_t stream, const char* what) {
     if (any_tokens) {
-        CKDA_REQUIRE(a.q); CKDA_REQUIRE(a.k); CKDA_REQUIRE(a.v); CKDA_REQUIRE(a.g); CKDA_REQUIRE(a.s);
+        CKDA_REQUIRE(a.q); CKDA_REQUIRE(a.k); CKDA_REQUIRE(a.v); CKDA_REQUIRE(a.g);
+        if (!a.gate_map) CKDA_REQUIRE(a.s);
         CKDA_REQUIRE(a.beta); CKDA_REQUIRE(a.dout);
         CKDA_REQUIRE(a.dq); CKDA_REQUIRE(a.dk); CKDA_REQUIRE(a.dv); CKDA_REQUIRE(a.dg); CKDA_REQUIRE(a.dbeta);
     }
@@ -463,7 +470,8 @@ ckda_status_t ckda_bwd(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtyp
     ckda::BwdArgs a{};
     a.B = B; a.T = T; a.H = H; a.DK = DK; a.DV = DV; a.bf16 = in_dtype == CKDA_BF16;
     a.head_gate = (flags & CKDA_GATE_HEAD) != 0; a.qk_norm = (flags & CKDA_QK_L2NORM) != 0;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.s = s; a.beta = beta; a.scale = scale; a.h0 = h0;
+    a.gate_map = (flags & CKDA_GATE_MAP) != 0;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.s = s ? s : reinterpret_cast<const int8_t*>(g); a.beta = beta; a.scale = scale; a.h0 = h0;
     a.h_ckpt = h_ckpt; a.dout = dout; a.dht = dht; a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg;
     a.dbeta = dbeta; a.dh0 = dh0; a.cu = nullptr; a.ndocs = 0;
     return bwd_common(a, fwd_slots(B, T), T > 0, workspace, workspace_bytes, stream, "ckda_bwd launch");
@@ -488,7 +496,8 @@ ckda_status_t ckda_bwd_varlen(int N, int T_total, const int32_t* cu, const int32
     ckda::BwdArgs a{};
     a.B = 1; a.T = T_total; a.H = H; a.DK = DK; a.DV = DV; a.bf16 = in_dtype == CKDA_BF16;
     a.head_gate = (flags & CKDA_GATE_HEAD) != 0; a.qk_norm = (flags & CKDA_QK_L2NORM) != 0;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.s = s; a.beta = beta; a.scale = scale; a.h0 = h0;
+    a.gate_map = (flags & CKDA_GATE_MAP) != 0;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.s = s ? s : reinterpret_cast<const int8_t*>(g); a.beta = beta; a.scale = scale; a.h0 = h0;
     a.h_ckpt = h_ckpt; a.dout = dout; a.dht = dht; a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg;
     a.dbeta = dbeta; a.dh0 = dh0; a.cu = cu_dev; a.cu_host = cu; a.ndocs = N;
     return bwd_common(a, varlen_slots(N, T_total), T_total > 0, workspace, workspace_bytes, stream,

@@ -103,7 +103,7 @@ hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t st) {
 #define CKDA_CHECK(x) do { e = (x); if (e != hipSuccess) return e; } while (0)
     FwdArgs f{};
     f.B = a.B; f.T = a.T; f.H = a.H; f.DK = DK; f.DV = DV; f.bf16 = a.bf16;
-    f.head_gate = a.head_gate; f.qk_norm = a.qk_norm;
+    f.head_gate = a.head_gate; f.qk_norm = a.qk_norm; f.gate_map = a.gate_map;
     f.q = a.q; f.k = a.k; f.v = a.v; f.g = a.g; f.s = a.s; f.beta = a.beta; f.scale = a.scale;
     f.cu = a.cu; f.cu_host = a.cu_host; f.ndocs = a.ndocs;
     const float* ck = a.h_ckpt;

@@ -143,6 +143,7 @@ struct ChunkParams {
     unsigned char* ws;
     const int32_t* cu;   // varlen document starts (device), or nullptr
     int T, H, ndocs;
+    int gate_map;        // g, beta hold pre-activations (CKDA_GATE_MAP); s unused
     // compact envelope flags, one word per (slot, head) record, or nullptr
     // (then each record keeps its own); written by the fast pass, read by
     // the exact pass
@@ -396,6 +397,10 @@ __device__ __forceinline__ void grad_phase1(const ChunkParams& p, const int slot
                 float db = aterm;
 #pragma unroll
                 for (int vt = 0; vt < DV / 16; ++vt) db += dbr[vt * 64 + r];
+                if (p.gate_map) {   // dL/dy of the beta pre-activation
+                    const float bb = beta_s[r];
+                    db *= bb * (1.f - 0.5f * bb);
+                }
                 p.dbeta[static_cast<size_t>(tok0 + r) * H + h] = db;
             }
         }
@@ -490,16 +495,27 @@ __device__ __forceinline__ void chunk_body(const ChunkParams& p, const int slot,
             q8[ks].load(q + base);
             k8[ks].load(k + base);
             if constexpr (HG) {
-                const float gt = p.g[trow];
-                const uint32_t sw = static_cast<uint32_t>(static_cast<uint8_t>(p.s[trow])) * 0x01010101u;
+                const float gx = p.g[trow];
+                const float gt = p.gate_map ? gate_map_g(gx) : gx;
+                const uint32_t sb = p.gate_map ? (gx < 0.f ? 0xFFu : 0x01u) : static_cast<uint8_t>(p.s[trow]);
+                const uint32_t sw = sb * 0x01010101u;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) bs[8 * ks + e] = gt;
                 par[2 * ks] = sw;
                 par[2 * ks + 1] = sw;
             } else {
-                const float4 a = reinterpret_cast<const float4*>(p.g + base)[0];
-                const float4 b = reinterpret_cast<const float4*>(p.g + base)[1];
-                const uint2 sv = *reinterpret_cast<const uint2*>(p.s + base);
+                float4 a = reinterpret_cast<const float4*>(p.g + base)[0];
+                float4 b = reinterpret_cast<const float4*>(p.g + base)[1];
+                uint2 sv;
+                if (p.gate_map) {   // signs from the pre-activations, then the map
+                    auto sb = [](float x, int sh) { return (x < 0.f ? 0xFFu : 0x01u) << sh; };
+                    sv.x = sb(a.x, 0) | sb(a.y, 8) | sb(a.z, 16) | sb(a.w, 24);
+                    sv.y = sb(b.x, 0) | sb(b.y, 8) | sb(b.z, 16) | sb(b.w, 24);
+                    a = make_float4(gate_map_g(a.x), gate_map_g(a.y), gate_map_g(a.z), gate_map_g(a.w));
+                    b = make_float4(gate_map_g(b.x), gate_map_g(b.y), gate_map_g(b.z), gate_map_g(b.w));
+                } else {
+                    sv = *reinterpret_cast<const uint2*>(p.s + base);
+                }
                 bs[8 * ks + 0] = a.x; bs[8 * ks + 1] = a.y; bs[8 * ks + 2] = a.z; bs[8 * ks + 3] = a.w;
                 bs[8 * ks + 4] = b.x; bs[8 * ks + 5] = b.y; bs[8 * ks + 6] = b.z; bs[8 * ks + 7] = b.w;
                 par[2 * ks] = sv.x;
@@ -514,7 +530,7 @@ __device__ __forceinline__ void chunk_body(const ChunkParams& p, const int slot,
                 par[2 * ks + 1] = 0x01010101u;
             }
         }
-        const float bt = p.beta[trow];
+        const float bt = p.gate_map ? gate_map_beta(p.beta[trow]) : p.beta[trow];
         if (cgi == 0 && gq == 0) beta_s[t] = valid ? bt : 0.f;
     }
     float2* const nrm = reinterpret_cast<float2*>(smem + SH::L_NRM);
@@ -1148,6 +1164,7 @@ inline ChunkParams chunk_params(const FwdArgs& A) {
     ChunkParams p{};
     p.q = A.q; p.k = A.k; p.v = A.v; p.g = A.g; p.s = A.s; p.beta = A.beta;
     p.ws = static_cast<unsigned char*>(A.ws); p.cu = A.cu; p.T = A.T; p.H = A.H; p.ndocs = A.ndocs;
+    p.gate_map = A.gate_map ? 1 : 0;
     return p;
 }
 

@@ -113,6 +113,30 @@ __device__ __forceinline__ float exp2_clamped(float x2) {
     return __builtin_amdgcn_exp2f(fminf(x2, 126.0f));
 }
 
+// The optional gate map (CKDA_GATE_MAP): the gate pre-activation x gives the
+// signed gate alpha = tanh(x), carried as g = log max(|alpha|, e^kGateLogFloor)
+// and its sign (x < 0), and the beta pre-activation y gives beta =
+// 2 sigmoid(y) in (0, 2) (a reading of the Complex KDA paper page, section 3
+// "CKDA.": gates in [-1, 1], beta in [0, 2], a magnitude floor).  The floor
+// keeps every 16-token run of log-gates at -64 or above, inside the chunk
+// kernels' anchored fast path.  Backward: dg/dx = (1 - tanh^2 x) / tanh x
+// = 2 / sinh 2x above the floor, 0 on it; dbeta/dy = beta (1 - beta / 2).
+// For |x| >= 1/2, log tanh|x| = log1p(-u) - log1p(u) with u = e^{-2|x|}, and
+// the derivative is taken as 2 / sinh 2x: both keep their relative accuracy
+// where tanh|x| rounds towards 1 (1 - tanh^2 x would cancel).
+constexpr float kGateLogFloor = -4.0f;
+__device__ __forceinline__ float gate_log_tanh(float x) {
+    const float a = fabsf(x);
+    if (a < 0.5f) return logf(tanhf(a));
+    const float u = expf(-2.f * a);
+    return log1pf(-u) - log1pf(u);
+}
+__device__ __forceinline__ float gate_map_g(float x) { return fmaxf(gate_log_tanh(x), kGateLogFloor); }
+__device__ __forceinline__ float gate_map_dgdx(float x) {
+    return gate_log_tanh(x) >= kGateLogFloor ? 2.f / sinhf(2.f * x) : 0.f;
+}
+__device__ __forceinline__ float gate_map_beta(float y) { return 2.f / (1.f + expf(-y)); }
+
 // 1 / sqrt(ss) for a vector's sum of squares ss, through the hardware
 // reciprocal square root (about 1 ulp on normal inputs).  A squared norm below
 // fp32's normal range (the zero vector among them) gives 0, so such a vector

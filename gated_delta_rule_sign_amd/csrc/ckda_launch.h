@@ -12,6 +12,7 @@ struct DecodeArgs {
     bool bf16;
     bool head_gate;   // g, s per head ([N,H]) instead of per channel
     bool qk_norm;     // q, k normalised per head before use
+    bool gate_map;    // g, beta hold pre-activations (the optional gate map); s unused
     const void *q, *k, *v;
     const float* g;
     const int8_t* s;
@@ -41,6 +42,7 @@ struct FwdArgs {
     bool bf16;
     bool head_gate;   // g, s per (token, head) instead of per channel
     bool qk_norm;     // q, k normalised per (token, head) before use
+    bool gate_map;    // g, beta hold pre-activations (the optional gate map); s unused
     const void *q, *k, *v;
     const float* g;
     const int8_t* s;
@@ -127,6 +129,7 @@ struct BwdArgs {
     bool bf16;
     bool head_gate;   // g, s, dg per (token, head) instead of per channel
     bool qk_norm;     // q, k normalised per (token, head); dq, dk w.r.t. the raw q, k
+    bool gate_map;    // g, beta hold pre-activations; dg, dbeta w.r.t. them; s unused
     const void *q, *k, *v;
     const float* g;
     const int8_t* s;

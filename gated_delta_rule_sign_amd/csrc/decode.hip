@@ -35,7 +35,7 @@ __global__ void __launch_bounds__(256, 4)
 decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
                    const float* __restrict__ g, const int8_t* __restrict__ s,
                    const float* __restrict__ beta, float scale, float* __restrict__ state,
-                   int8_t* __restrict__ sign_prod, float* __restrict__ o)
+                   int8_t* __restrict__ sign_prod, float* __restrict__ o, int gate_map)
 {
     constexpr int CG = DV / 4;          // column groups (4 columns each)
     constexpr int RG = 256 / CG;        // row bands
@@ -61,8 +61,10 @@ decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
     // row parameters: every thread loads row min(t, DK - 1) (unconditional, so
     // these loads are issued ahead of the state stream and retire first)
     const int tr = t < DK ? t : DK - 1;
-    const int sp0 = sign_prod[kbase + tr], s0 = HG ? s[nh] : s[kbase + tr];
-    const float g0 = HG ? g[nh] : g[kbase + tr];
+    const float gx = HG ? g[nh] : g[kbase + tr];
+    // the optional gate map: sign and log-magnitude from the pre-activation
+    const int sp0 = sign_prod[kbase + tr], s0 = gate_map ? (gx < 0.f ? -1 : 1) : (HG ? s[nh] : s[kbase + tr]);
+    const float g0 = gate_map ? gate_map_g(gx) : gx;
     const float k0 = Elem<Tin>::load(k, kbase + tr), q0 = Elem<Tin>::load(q, kbase + tr);
     float4 S[R];
 #pragma unroll
@@ -135,7 +137,7 @@ decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
         Y.x *= iq; Y.y *= iq; Y.z *= iq; Y.w *= iq;
         KQ *= ik * iq;
     }
-    const float bt = beta[nh];
+    const float bt = gate_map ? gate_map_beta(beta[nh]) : beta[nh];
     const int c0 = 4 * cg;
     float4 u;
     u.x = bt * (Elem<Tin>::load(v, vbase + c0 + 0) - X.x);
@@ -174,7 +176,7 @@ static hipError_t launch_decode_t(const DecodeArgs& A, hipStream_t stream) {
     hipLaunchKernelGGL(kern, dim3(A.N * A.H), dim3(256), 0, stream,
                        static_cast<const Tin*>(A.q), static_cast<const Tin*>(A.k),
                        static_cast<const Tin*>(A.v), A.g, A.s, A.beta, A.scale, A.state,
-                       A.sign_prod, A.o);
+                       A.sign_prod, A.o, A.gate_map ? 1 : 0);
     return hipGetLastError();
 }
 

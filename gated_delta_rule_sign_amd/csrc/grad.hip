@@ -87,6 +87,7 @@ struct Grad2Params {
     const int32_t* cu;
     float scale;
     int T, H, ndocs;
+    int gate_map;               // g holds the gate pre-activation (s unused); dg w.r.t. it
 };
 
 // Double-float sums (hi + lo, Knuth's two-sum) for the exact variant's
@@ -109,7 +110,8 @@ __device__ __forceinline__ float ex2n(float x) { return __builtin_amdgcn_exp2f(f
 
 // CW: key channels per workgroup (DK, or 64 of DK = 128 when no per-token sum
 // over all channels is needed: two workgroups per chunk-head, part 0 and 1)
-template <typename Tin, int DK, int DV, bool HG, bool NQK, bool EX, int CW>
+// GM: g holds the gate pre-activation (the optional gate map)
+template <typename Tin, int DK, int DV, bool HG, bool NQK, bool EX, int CW, bool GM>
 __device__ __forceinline__ void grad2_body(const Grad2Params& p, const int slot, const int h, const int part,
                                            unsigned char* smem)
 {
@@ -273,7 +275,7 @@ __device__ __forceinline__ void grad2_body(const Grad2Params& p, const int slot,
         const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(static_cast<const Tin*>(p.k) + row0 * DK, rows * DK * ES_IN);
         constexpr int GX = HG ? 1 : DK;   // gate and sign elements per token-head row
         const __amdgpu_buffer_rsrc_t rg = buffer_rsrc(p.g + row0 * GX, rows * GX * 4);
-        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(p.s + row0 * GX, rows * GX);
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(p.s + row0 * GX, GM ? 0u : rows * GX);   // (unread with the map)
         const uint32_t lrow = static_cast<uint32_t>(4 * gq * H);   // the lane's first token row
         const uint32_t vq = (lrow * DK + c) * ES_IN, vg = (lrow * GX + (HG ? 0 : c));
 #pragma unroll
@@ -281,11 +283,20 @@ __device__ __forceinline__ void grad2_body(const Grad2Params& p, const int slot,
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t tr = static_cast<uint32_t>((16 * J + i) * H);   // uniform row step
-                bl[J][i] = buffer_load_f32(rg, 4 * vg, 4 * tr * GX);
-                neg |= buffer_load_i8(rs, vg, tr * GX) < 0 ? (1u << (4 * J + i)) : 0u;
+                bl[J][i] = buffer_load_f32(rg, 4 * vg, 4 * tr * GX);   // padding tokens read 0: no gate
+                neg |= buffer_load_i8(rs, vg, tr * GX) < 0 ? (1u << (4 * J + i)) : 0u;   // (0 with the map)
                 kf[J][i] = buffer_load_elem<Tin>(rk, vq, tr * DK * ES_IN);
                 qf[J][i] = buffer_load_elem<Tin>(rq, vq, tr * DK * ES_IN);
             }
+        if constexpr (GM) {   // the optional gate map, on the loaded pre-activations
+#pragma unroll
+            for (int J = 0; J < 4; ++J)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    neg |= bl[J][i] < 0.f ? (1u << (4 * J + i)) : 0u;
+                    bl[J][i] = 16 * J + 4 * gq + i < L ? gate_map_g(bl[J][i]) : 0.f;
+                }
+        }
     }
     // per-token sums over all channels of two lane values val(J, i, 0 / 1):
     // the wave's 16 channels by a row scan, then 128 threads over the waves'
@@ -508,7 +519,8 @@ __device__ __forceinline__ void grad2_body(const Grad2Params& p, const int slot,
         for (int J = 0; J < 4; ++J) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float gv = buffer_load_f32(rg, 4 * vg, 4 * static_cast<uint32_t>((16 * J + i) * H) * GX);
+                const float gx = buffer_load_f32(rg, 4 * vg, 4 * static_cast<uint32_t>((16 * J + i) * H) * GX);
+                const float gv = GM ? (16 * J + 4 * gq + i < L ? gate_map_g(gx) : 0.f) : gx;
                 bd[J][i] = i == 0 ? DF{gv, 0.f} : df_add(bd[J][i - 1], DF{gv, 0.f});
             }
             lt[J] = bd[J][3];
@@ -701,11 +713,25 @@ __device__ __forceinline__ void grad2_body(const Grad2Params& p, const int slot,
             }
         }
     }
+    if constexpr (!HG) {
+        if constexpr (GM) {   // dL/dx through the optional gate map (x reread, one token tile at a time)
+            const __amdgpu_buffer_rsrc_t rgx = buffer_rsrc(p.g + row0 * DK, rows * DK * 4);
+            const uint32_t vx = (static_cast<uint32_t>(4 * gq * H) * DK + c) * 4;
+#pragma unroll
+            for (int J = 0; J < 4; ++J) {
+                CKDA_FENCE();
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    pdb[J][i] *= gate_map_dgdx(buffer_load_f32(rgx, vx, static_cast<uint32_t>((16 * J + i) * H * DK) * 4));
+            }
+        }
+    }
     // ---- outputs -------------------------------------------------------------
     {
         const __amdgpu_buffer_rsrc_t rdq = buffer_rsrc(p.dq + row0 * DK, rows * DK * 4);
         const __amdgpu_buffer_rsrc_t rdk = buffer_rsrc(p.dk + row0 * DK, rows * DK * 4);
         const __amdgpu_buffer_rsrc_t rdg = buffer_rsrc(p.dg + row0 * DK, HG ? 0u : rows * DK * 4);
+
         const uint32_t vq = (static_cast<uint32_t>(4 * gq * H) * DK + c) * 4;
 #pragma unroll
         for (int J = 0; J < 4; ++J)
@@ -721,7 +747,10 @@ __device__ __forceinline__ void grad2_body(const Grad2Params& p, const int slot,
         float* const sums = reinterpret_cast<float*>(smem + SH::L_SUM);
         lds_sync();
         token_sums([&](int J, int i, int) { return pdb[J][i]; }, sums);
-        if (tid < L) p.dg[row0 + static_cast<size_t>(tid) * H] = sums[tid];
+        if (tid < L) {
+            const size_t o = row0 + static_cast<size_t>(tid) * H;
+            p.dg[o] = GM ? sums[tid] * gate_map_dgdx(p.g[o]) : sums[tid];   // dL/dx with the map
+        }
     }
 }
 
@@ -734,7 +763,7 @@ constexpr int grad2_cw() { return (HG || NQK || DK <= 64) ? DK : 64; }
 // consecutive workgroups per channel group, so both halves of a chunk-head
 // land on the same XCD (workgroups go to the XCDs in turn), where the
 // operands both stage share its L2.
-template <typename Tin, int DK, int DV, bool HG, bool NQK>
+template <typename Tin, int DK, int DV, bool HG, bool NQK, bool GM>
 __global__ void __launch_bounds__((grad2_cw<DK, HG, NQK>() * 4), 2) ckda_grad2_kernel(Grad2Params p, int nch)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -745,13 +774,13 @@ __global__ void __launch_bounds__((grad2_cw<DK, HG, NQK>() * 4), 2) ckda_grad2_k
         part = (blockIdx.x >> 3) & 1;
         if (chh >= nch) return;
     }
-    grad2_body<Tin, DK, DV, HG, NQK, false, CW>(p, chh / p.H, chh % p.H, part, smem);
+    grad2_body<Tin, DK, DV, HG, NQK, false, CW, GM>(p, chh / p.H, chh % p.H, part, smem);
 }
 
 // the exact variant over the flagged chunk-heads (whole heads): workgroup x
 // looks at chunk-heads x*per .. x*per + per - 1 (per <= 64) and redoes the
 // flagged ones in turn
-template <typename Tin, int DK, int DV, bool HG, bool NQK>
+template <typename Tin, int DK, int DV, bool HG, bool NQK, bool GM>
 __global__ void __launch_bounds__(DK * 4, 2) ckda_grad2_exact_kernel(Grad2Params p, int nch, int per)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -763,26 +792,26 @@ __global__ void __launch_bounds__(DK * 4, 2) ckda_grad2_exact_kernel(Grad2Params
         const int j = __builtin_ctzll(mask);
         mask &= mask - 1ull;
         const int chh = c0 + j;
-        grad2_body<Tin, DK, DV, HG, NQK, true, DK>(p, chh / p.H, chh % p.H, 0, smem);
+        grad2_body<Tin, DK, DV, HG, NQK, true, DK, GM>(p, chh / p.H, chh % p.H, 0, smem);
         lds_sync();   // before the next chunk-head reuses LDS
     }
 }
 
-template <typename Tin, int DK, int DV, bool HG, bool NQK>
-static hipError_t launch_grad2_t(const Grad2Params& p, int nslots, hipStream_t stream) {
+template <typename Tin, int DK, int DV, bool HG, bool NQK, bool GM>
+static hipError_t launch_grad2_g(const Grad2Params& p, int nslots, hipStream_t stream) {
     constexpr int CW = grad2_cw<DK, HG, NQK>();
     constexpr int LDS = Grad2Shape<DK, DV, false, CW>::LDS, LDS_EX = Grad2Shape<DK, DV, true>::LDS;
     const long long nch = static_cast<long long>(nslots) * p.H;
     if (nch == 0) return hipSuccess;
     const long long grid = CW == DK ? nch : (nch + 7) / 8 * 16;
-    auto kern = ckda_grad2_kernel<Tin, DK, DV, HG, NQK>;
+    auto kern = ckda_grad2_kernel<Tin, DK, DV, HG, NQK, GM>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(CW * 4), LDS, stream, p, static_cast<int>(nch));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    auto kx = ckda_grad2_exact_kernel<Tin, DK, DV, HG, NQK>;
+    auto kx = ckda_grad2_exact_kernel<Tin, DK, DV, HG, NQK, GM>;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kx), hipFuncAttributeMaxDynamicSharedMemorySize, LDS_EX);
     if (e != hipSuccess) return e;
     const int per = static_cast<int>(nch > 512 * 64LL ? 64 : (nch + 511) / 512);
@@ -790,6 +819,12 @@ static hipError_t launch_grad2_t(const Grad2Params& p, int nslots, hipStream_t s
     hipLaunchKernelGGL(kx, dim3(static_cast<unsigned>(gx)), dim3(DK * 4), LDS_EX, stream, p,
                        static_cast<int>(nch), per);
     return hipGetLastError();
+}
+
+template <typename Tin, int DK, int DV, bool HG, bool NQK>
+static hipError_t launch_grad2_t(const Grad2Params& p, int nslots, hipStream_t stream) {
+    return p.gate_map ? launch_grad2_g<Tin, DK, DV, HG, NQK, true>(p, nslots, stream)
+                      : launch_grad2_g<Tin, DK, DV, HG, NQK, false>(p, nslots, stream);
 }
 
 template <typename Tin>
@@ -814,7 +849,7 @@ hipError_t launch_grad2(const FwdArgs& A, const Grad2Args& G, int nslots, hipStr
     p.q = A.q; p.k = A.k; p.g = A.g; p.s = A.s; p.dout = G.dout; p.dv = G.dv;
     p.h_ckpt = G.h_ckpt; p.G = G.G; p.gout = G.gout; p.gout_bytes = G.gout_bytes; p.flags = G.flags;
     p.dq = G.dq; p.dk = G.dk; p.dg = G.dg; p.cu = A.cu; p.scale = A.scale;
-    p.T = A.T; p.H = A.H; p.ndocs = A.ndocs;
+    p.T = A.T; p.H = A.H; p.ndocs = A.ndocs; p.gate_map = A.gate_map ? 1 : 0;
     return A.bf16 ? launch_grad2_dt<bf16_t>(p, A, nslots, stream) : launch_grad2_dt<float>(p, A, nslots, stream);
 }
 

@@ -176,6 +176,15 @@ def cu_from_lengths(lens) -> np.ndarray:
     return cu
 
 
+def draw_gate_preacts(rng: np.random.Generator, gshape: tuple, bshape: tuple):
+    """Pre-activations for the optional gate map: the gate's x ~ 1.5 N(0,1)
+    (|tanh x| spans the floor up to about 1, both signs) and beta's
+    y ~ N(0,1), both float32."""
+    x = (1.5 * rng.standard_normal(gshape)).astype(np.float32)
+    y = rng.standard_normal(bshape).astype(np.float32)
+    return x, y
+
+
 def decode_steps(seed: int, t0: int, t1: int, N: int, H: int, DK: int, DV: int,
                  dtype: str) -> TokenInputs:
     """Token inputs of decode steps t0..t1-1, stacked as [t1-t0, N, H, D].

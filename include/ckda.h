@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define CKDA_ABI_VERSION 8
+#define CKDA_ABI_VERSION 9
 
 /* Status codes and dtype codes travel as fixed-width integers (any value a
  * caller passes is well defined on both sides of the boundary; unknown
@@ -84,11 +84,24 @@ typedef int32_t ckda_dtype_t;
  *  CKDA_QK_L2NORM: q and k are normalised per (token, head) over the key
  *      channels, x / ||x|| (a zero vector stays zero), before the recurrence
  *      uses them; the unit keys the pages' stability ranges assume.  The
- *      backward returns gradients w.r.t. the raw q and k. */
+ *      backward returns gradients w.r.t. the raw q and k.
+ *  CKDA_GATE_MAP: g and beta hold pre-activations x and y instead of the
+ *      log-gate and beta, and s is not read (it may be NULL): the signed
+ *      gate alpha = tanh(x), carried as g = log max(|alpha|, e^-4) and
+ *      s = -1 where x < 0 (else +1), and beta = 2 sigmoid(y) in (0, 2).  A
+ *      reading of the Complex KDA paper page, section 3 "CKDA." (gates in
+ *      [-1, 1], beta in [0, 2], a signed gate with a magnitude floor after
+ *      Sarrof et al. and Grazzi et al.), whose formulas and floor the pages
+ *      do not carry; the floor e^-4 is this library's choice: it keeps every
+ *      16-token run of log-gates inside the fast path's envelope.  The map
+ *      runs inside the kernels' loads (no extra pass).  The backward then
+ *      returns dg = dL/dx (the plain derivative; 0 on the floor) and
+ *      dbeta = dL/dy. */
 typedef uint32_t ckda_flags_t;
 #define CKDA_GATE_CHANNEL 0u
 #define CKDA_GATE_HEAD 1u
 #define CKDA_QK_L2NORM 2u
+#define CKDA_GATE_MAP 4u
 
 /* opaque HIP stream (hipStream_t); NULL = the default stream */
 typedef void* ckda_stream_t;

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.ckda_abi_version() == 8
+    assert L.ckda_abi_version() == 9
     assert L.ckda_status_string(0) == b"ok"
     for st in range(1, 8):
         assert L.ckda_status_string(st) not in (b"ok", b"unknown status")
@@ -61,7 +61,7 @@ def test_fwd_rejects_bad_arguments(L):
     assert fwd(L, o=None) == 1
     assert fwd(L, T=0, o=None, q=None) != 1      # no tokens: o and q are not needed
     assert fwd(L, g=P(0x1004)) == 4              # misaligned
-    assert fwd(L, gate=4) == 4                   # unknown flag bit
+    assert fwd(L, gate=8) == 4                   # unknown flag bit
     assert fwd(L, gate=0x80000000) == 4          # unknown flag bit
     assert fwd(L, B=0) == 0                      # empty problem: nothing to do
     assert L.ckda_last_error() == b""
@@ -170,7 +170,7 @@ def test_decode_and_bwd_reject_bad_arguments(L):
     f = ctypes.c_float(1.0)
     assert L.ckda_decode_step(4, 2, 96, 32, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, f, FAKE, FAKE, FAKE, None) == 4
     assert L.ckda_decode_step(4, 2, 32, 32, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, f, None, FAKE, FAKE, None) == 1
-    assert L.ckda_decode_step(4, 2, 32, 32, 0, 5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, f, FAKE, FAKE, FAKE, None) == 4
+    assert L.ckda_decode_step(4, 2, 32, 32, 0, 9, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, f, FAKE, FAKE, FAKE, None) == 4
     assert b"flags" in L.ckda_last_error()
     assert L.ckda_bwd(1, 8, 1, 32, 32, 0, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, f, None, None, FAKE, None,
                       FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == 1   # h_ckpt missing
