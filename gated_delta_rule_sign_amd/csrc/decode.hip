@@ -30,12 +30,13 @@ namespace ckda {
 
 // HG: one gate per head (g, s [N,H]), broadcast over the channels;
 // NQK: q and k L2-normalised per (sequence, head)
-template <typename Tin, int DK, int DV, bool HG, bool NQK>
+// GM: g and beta hold pre-activations (the optional gate map; s unread)
+template <typename Tin, int DK, int DV, bool HG, bool NQK, bool GM>
 __global__ void __launch_bounds__(256, 4)
 decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ v,
                    const float* __restrict__ g, const int8_t* __restrict__ s,
                    const float* __restrict__ beta, float scale, float* __restrict__ state,
-                   int8_t* __restrict__ sign_prod, float* __restrict__ o, int gate_map)
+                   int8_t* __restrict__ sign_prod, float* __restrict__ o)
 {
     constexpr int CG = DV / 4;          // column groups (4 columns each)
     constexpr int RG = 256 / CG;        // row bands
@@ -63,8 +64,16 @@ decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
     const int tr = t < DK ? t : DK - 1;
     const float gx = HG ? g[nh] : g[kbase + tr];
     // the optional gate map: sign and log-magnitude from the pre-activation
-    const int sp0 = sign_prod[kbase + tr], s0 = gate_map ? (gx < 0.f ? -1 : 1) : (HG ? s[nh] : s[kbase + tr]);
-    const float g0 = gate_map ? gate_map_g(gx) : gx;
+    int s0;
+    float g0;
+    if constexpr (GM) {
+        s0 = gx < 0.f ? -1 : 1;
+        g0 = gate_map_g(gx);
+    } else {
+        s0 = HG ? s[nh] : s[kbase + tr];
+        g0 = gx;
+    }
+    const int sp0 = sign_prod[kbase + tr];
     const float k0 = Elem<Tin>::load(k, kbase + tr), q0 = Elem<Tin>::load(q, kbase + tr);
     float4 S[R];
 #pragma unroll
@@ -137,7 +146,7 @@ decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
         Y.x *= iq; Y.y *= iq; Y.z *= iq; Y.w *= iq;
         KQ *= ik * iq;
     }
-    const float bt = gate_map ? gate_map_beta(beta[nh]) : beta[nh];
+    const float bt = GM ? gate_map_beta(beta[nh]) : beta[nh];
     const int c0 = 4 * cg;
     float4 u;
     u.x = bt * (Elem<Tin>::load(v, vbase + c0 + 0) - X.x);
@@ -167,17 +176,22 @@ decode_step_kernel(const Tin* __restrict__ q, const Tin* __restrict__ k, const T
     }
 }
 
-template <typename Tin, int DK, int DV>
-static hipError_t launch_decode_t(const DecodeArgs& A, hipStream_t stream) {
-    auto kern = A.qk_norm ? (A.head_gate ? decode_step_kernel<Tin, DK, DV, true, true>
-                                         : decode_step_kernel<Tin, DK, DV, false, true>)
-                          : (A.head_gate ? decode_step_kernel<Tin, DK, DV, true, false>
-                                         : decode_step_kernel<Tin, DK, DV, false, false>);
+template <typename Tin, int DK, int DV, bool GM>
+static hipError_t launch_decode_g(const DecodeArgs& A, hipStream_t stream) {
+    auto kern = A.qk_norm ? (A.head_gate ? decode_step_kernel<Tin, DK, DV, true, true, GM>
+                                         : decode_step_kernel<Tin, DK, DV, false, true, GM>)
+                          : (A.head_gate ? decode_step_kernel<Tin, DK, DV, true, false, GM>
+                                         : decode_step_kernel<Tin, DK, DV, false, false, GM>);
     hipLaunchKernelGGL(kern, dim3(A.N * A.H), dim3(256), 0, stream,
                        static_cast<const Tin*>(A.q), static_cast<const Tin*>(A.k),
                        static_cast<const Tin*>(A.v), A.g, A.s, A.beta, A.scale, A.state,
-                       A.sign_prod, A.o, A.gate_map ? 1 : 0);
+                       A.sign_prod, A.o);
     return hipGetLastError();
+}
+
+template <typename Tin, int DK, int DV>
+static hipError_t launch_decode_t(const DecodeArgs& A, hipStream_t stream) {
+    return A.gate_map ? launch_decode_g<Tin, DK, DV, true>(A, stream) : launch_decode_g<Tin, DK, DV, false>(A, stream);
 }
 
 template <typename Tin>

@@ -268,33 +268,38 @@ __global__ void __launch_bounds__(512, 2) ckda_rev_kernel(RevParams p)
     f32x4 G[RT];
     {
         const int gq = lane >> 4, col = 16 * vt + (lane & 15);
-        const float* src = last ? p.dht : (OUT ? p.seg_start + (static_cast<size_t>(ss) * H + h) * DK * DV : nullptr);
-        const size_t soff = last ? st_off : 0;
+        const float* src = last ? (p.dht ? p.dht + st_off : nullptr)
+                                : (OUT ? p.seg_start + (static_cast<size_t>(ss) * H + h) * DK * DV : nullptr);
+        // unconditional loads (a missing source or column reads 0): all in flight at once
+        const __amdgpu_buffer_rsrc_t grc = buffer_rsrc(src, (has_col && src && !trans) ? DK * DV * 4 : 0);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 16 * rt + 4 * gq + i;
-                G[rt][i] = trans ? (row == col ? 1.f : 0.f)
-                                 : ((has_col && src) ? src[soff + static_cast<size_t>(row) * DV + col] : 0.f);
+                const float v = buffer_load_f32(grc, static_cast<uint32_t>(row * DV + col) * 4, 0);
+                G[rt][i] = trans ? (row == col ? 1.f : 0.f) : v;
             }
     }
     // dO tiles of walk step jj: lane (n, g) holds rows 16J + 4g + i of column
     // 16vt + n (the C/D layout), zero past the chunk's end; the address is
     // clamped into the chunk so every load is unconditional
     const Tin* dO = static_cast<const Tin*>(p.dout);
+    // (buffer loads over the chunk's rows: rows past its end, and every row
+    // of a transition slice, read as 0 with no branch, so all 16 are in
+    // flight together)
     auto load_do = [&](int jj, f32x4 (&x)[4]) {
         const int c0 = 64 * (jbeg + nloop - 1 - jj);
         const int L = min(64, len - c0);
         const int gq = (opaque_tid() & 63) >> 4, col = 16 * vt + (lane & 15);
+        const uint32_t bytes = trans ? 0u : static_cast<uint32_t>(((L - 1) * H + 1) * DV) * sizeof(Tin);
+        const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(dO + (static_cast<size_t>(tok0 + c0) * H + h) * DV, bytes);
 #pragma unroll
         for (int J = 0; J < 4; ++J)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int tt = 16 * J + 4 * gq + i;
-                const size_t idx = (static_cast<size_t>(tok0 + c0 + min(tt, L - 1)) * H + h) * DV + col;
-                const float v = Elem<Tin>::load(dO, idx);
-                x[J][i] = (tt < L && !trans) ? v : 0.f;
+                x[J][i] = buffer_load_elem<Tin>(rc, static_cast<uint32_t>((tt * H * DV + col) * sizeof(Tin)), 0);
             }
     };
     f32x4 dn[4];
