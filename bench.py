@@ -46,10 +46,11 @@ DEC_BYTES_PER_HEAD_STEP = 2 * 128 * 128 * 4 + 3 * 256 + 512 + 128 + 2 * 128 + 4 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ckda_fwd_traffic__layer_bf16.json")
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_step_traffic__decode_b256.json")
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ckda_bwd_traffic__layer_bwd.json")
 
 
 def measured_traffic(path=None):
-    """HBM bytes per call (forward, the default record) or per step (decode)
+    """HBM bytes per call (forward, the default record; backward) or per step (decode)
     from the committed FETCH_SIZE / WRITE_SIZE runs (calibrated on a plain
     copy), or None when the kernel sources have changed since those counters
     were taken."""
@@ -459,7 +460,8 @@ def main():
         "backward": {"workload": "layer_bwd: layer_bf16 shapes, bf16 upstream gradient, checkpointed states",
                      "unit": "tokens/s", "value": bw["tokens_per_s"], "ms": bw["ms"],
                      "algorithmic_bytes": bw["bytes"], "achieved_gbs": bw["gbs"],
-                     "frac_of_hbm_peak": bw["gbs"] / HBM_PEAK_GBS, "workspace_bytes": bw["workspace_bytes"]},
+                     "frac_of_hbm_peak": bw["gbs"] / HBM_PEAK_GBS, "workspace_bytes": bw["workspace_bytes"],
+                     "traffic": measured_traffic(BWD_TRAFFIC_FILE)},
         "forward_head_gate": {"workload": "layer_bf16_head_gate: layer_bf16 with one signed gate per "
                                           "(token, head) (g f32, s int8 [B,T,H])",
                               "unit": "tokens/s", "value": fh["tokens"] / (fh["ms"] * 1e-3), "ms": fh["ms"],

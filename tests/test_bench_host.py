@@ -92,3 +92,36 @@ def test_decode_traffic_and_mfma_records_follow_the_same_rule(tmp_path, monkeypa
     q.write_text(json.dumps(dict(m, sources_sha256="0" * 64)))
     monkeypatch.setattr(bench, "MFMA_FILE", str(q))
     assert bench.measured_mfma() is None
+
+
+def _includes(fname, seen):
+    """fname and every local header it includes, transitively."""
+    import re
+    if fname in seen:
+        return seen
+    seen.add(fname)
+    src = open(os.path.join(ROOT, "gated_delta_rule_sign_amd", "csrc", fname)).read()
+    for inc in re.findall(r'#include "([^"/]+)"', src):
+        _includes(inc, seen)
+    return seen
+
+
+def test_counter_records_hash_every_source_their_kernels_compile_from(tmp_path):
+    """A counter record stays valid only while its kernels are unchanged, so its
+    hash must cover every header the kernels' translation units include (the
+    forward's chunk kernel body lives in a header of its own)."""
+    for path in (bench.TRAFFIC_FILE, bench.MFMA_FILE, bench.DECODE_TRAFFIC_FILE, bench.BWD_TRAFFIC_FILE):
+        rec = json.load(open(path))
+        listed = set(rec["sources"])
+        units = [f for f in rec["sources"] if f.endswith(".hip")]
+        assert units, path
+        need = set()
+        for u in units:
+            _includes(u, need)
+        assert need <= listed, (os.path.basename(path), sorted(need - listed))
+    rec = json.load(open(bench.BWD_TRAFFIC_FILE))
+    got = bench.measured_traffic(bench.BWD_TRAFFIC_FILE)
+    assert got is None or got == float(rec["traffic_bytes_per_call"])
+    p = tmp_path / "bwd.json"
+    p.write_text(json.dumps(dict(rec, sources_sha256="0" * 64)))
+    assert bench.measured_traffic(str(p)) is None
