@@ -280,7 +280,7 @@ def bench_bwd(torch, steps, warmup):
     do = dev_tensor(torch, w.do)
     _, _, hc = ckda.fwd(**d, want_ckpt=True)
     B, T, H, DK = tok.q.shape
-    ws = torch.empty(ckda.bwd_workspace_bytes(B, T, H, DK, DK), dtype=torch.uint8, device="cuda:0")
+    ws = torch.empty(ckda.bwd_workspace_bytes(B, T, H, DK, DK, ckpt_given=True), dtype=torch.uint8, device="cuda:0")
     fn = lambda: ckda.bwd(**d, h_ckpt=hc, do=do, workspace=ws)
     log("timing backward")
     wall, per = time_kernel_launches(torch, fn, steps, warmup)
@@ -306,7 +306,7 @@ def bench_bwd_long(torch, steps=2, warmup=1):
     B, T, H, DK = tok.q.shape
     do = torch.randn((B, T, H, DK), generator=torch.Generator().manual_seed(77)).to(torch.bfloat16).to("cuda:0")
     _, _, hc = ckda.fwd(**d, want_ckpt=True)
-    ws = torch.empty(ckda.bwd_workspace_bytes(B, T, H, DK, DK), dtype=torch.uint8, device="cuda:0")
+    ws = torch.empty(ckda.bwd_workspace_bytes(B, T, H, DK, DK, ckpt_given=True), dtype=torch.uint8, device="cuda:0")
     fn = lambda: ckda.bwd(**d, h_ckpt=hc, do=do, workspace=ws)
     res = {"workload": "long_64k backward", "tokens": B * T, "chains": B * H}
     try:
@@ -353,7 +353,29 @@ def cpu_baseline(w, min_seconds=10.0, max_passes=8):
                 sample=f"the whole forward workload ({len(chains)} (sequence, head) chains x {T} tokens, "
                        f"{f['v'].shape[-1]} value columns), {passes} passes, {dt:.1f} s; float64 token recurrence; "
                        f"value = chain-tokens / {H} heads / seconds",
-                seconds=dt)
+                seconds=dt, tiny_fp32_one_core=cpu_tiny_one_core())
+
+
+def cpu_tiny_one_core(min_seconds=1.0):
+    """The oracle on tiny_fp32 (B=1, T=256, H=2, d=32) on one thread, repeated
+    for about `min_seconds`: the small case's CPU figure beside the layer's."""
+    import oracle
+    from gated_delta_rule_sign_amd import inputs as I
+    f = I.make_workload("tiny_fp32").tok.f64()
+    B, T, H, _ = f["q"].shape
+    n0 = oracle.max_threads()
+    oracle.set_threads(1)
+    try:
+        passes, dt = 0, 0.0
+        while passes == 0 or dt < min_seconds:
+            t0 = time.perf_counter()
+            oracle.fwd(**f)
+            dt += time.perf_counter() - t0
+            passes += 1
+    finally:
+        oracle.set_threads(n0)
+    return dict(value=passes * B * T / dt, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"tiny_fp32 (B={B}, T={T}, H={H}, d=32), {passes} passes, {dt:.2f} s")
 
 
 def main():

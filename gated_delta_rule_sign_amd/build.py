@@ -33,7 +33,7 @@ def _compile(src: str, obj: str, extra=()) -> None:
     subprocess.run(cmd, check=True)
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
+def build(verbose: bool = False, jobs: int = 8) -> str:
     """Compile every source and link libckda.so next to this file."""
     from concurrent.futures import ThreadPoolExecutor
 

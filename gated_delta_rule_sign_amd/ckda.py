@@ -64,11 +64,15 @@ def lib() -> ctypes.CDLL:
     L.ckda_decode_step.restype = I
     L.ckda_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
     L.ckda_bwd_workspace_bytes.restype = S
+    L.ckda_bwd_workspace_bytes_given_ckpt.argtypes = [I, I, I, I, I]
+    L.ckda_bwd_workspace_bytes_given_ckpt.restype = S
     L.ckda_bwd.argtypes = [I, I, I, I, I, I, U, P, P, P, P, P, P, F, P, P, P, P,
                            P, P, P, P, P, P, P, S, P]
     L.ckda_bwd.restype = I
     L.ckda_bwd_varlen_workspace_bytes.argtypes = [I, I, I, I, I]
     L.ckda_bwd_varlen_workspace_bytes.restype = S
+    L.ckda_bwd_varlen_workspace_bytes_given_ckpt.argtypes = [I, I, I, I, I]
+    L.ckda_bwd_varlen_workspace_bytes_given_ckpt.restype = S
     L.ckda_bwd_varlen.argtypes = [I, I, P, P, I, I, I, I, U, P, P, P, P, P, P, F, P, P, P, P,
                                   P, P, P, P, P, P, P, S, P]
     L.ckda_bwd_varlen.restype = I
@@ -292,8 +296,11 @@ def decode_step(q, k, v, g, s, beta, state, sign_prod, scale: float = 1.0, o=Non
     return o
 
 
-def bwd_workspace_bytes(B, T, H, DK, DV) -> int:
-    return int(lib().ckda_bwd_workspace_bytes(B, T, H, DK, DV))
+def bwd_workspace_bytes(B, T, H, DK, DV, ckpt_given: bool = False) -> int:
+    """Backward workspace; ckpt_given: the caller passes the checkpoints
+    (ckda_bwd_workspace_bytes_given_ckpt), else room to recompute them."""
+    f = lib().ckda_bwd_workspace_bytes_given_ckpt if ckpt_given else lib().ckda_bwd_workspace_bytes
+    return int(f(B, T, H, DK, DV))
 
 
 def bwd(q, k, v, g, s, beta, h_ckpt, do, scale: float = 1.0, h0=None, dht=None,
@@ -314,7 +321,7 @@ def bwd(q, k, v, g, s, beta, h_ckpt, do, scale: float = 1.0, h0=None, dht=None,
                dv=torch.empty((B, T, H, DV), **f32), dg=torch.empty(gsh, **f32),
                dbeta=torch.empty((B, T, H), **f32),
                dh0=torch.empty((B, H, DK, DV), **f32) if want_dh0 else None)
-    need = bwd_workspace_bytes(B, T, H, DK, DV)
+    need = bwd_workspace_bytes(B, T, H, DK, DV, ckpt_given=h_ckpt is not None)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -325,8 +332,9 @@ def bwd(q, k, v, g, s, beta, h_ckpt, do, scale: float = 1.0, h0=None, dht=None,
     return out
 
 
-def bwd_varlen_workspace_bytes(N, T_total, H, DK, DV) -> int:
-    return int(lib().ckda_bwd_varlen_workspace_bytes(N, T_total, H, DK, DV))
+def bwd_varlen_workspace_bytes(N, T_total, H, DK, DV, ckpt_given: bool = False) -> int:
+    f = lib().ckda_bwd_varlen_workspace_bytes_given_ckpt if ckpt_given else lib().ckda_bwd_varlen_workspace_bytes
+    return int(f(N, T_total, H, DK, DV))
 
 
 def bwd_varlen(q, k, v, g, s, beta, cu_seqlens, h_ckpt, do, scale: float = 1.0, h0=None, dht=None,
@@ -358,7 +366,8 @@ def bwd_varlen(q, k, v, g, s, beta, cu_seqlens, h_ckpt, do, scale: float = 1.0, 
                dv=torch.empty((Tt, H, DV), **f32), dg=torch.empty(gsh, **f32),
                dbeta=torch.empty((Tt, H), **f32),
                dh0=torch.empty((N, H, DK, DV), **f32) if want_dh0 else None)
-    workspace, wsb = _workspace(workspace, bwd_varlen_workspace_bytes(N, Tt, H, DK, DV), dev)
+    workspace, wsb = _workspace(workspace, bwd_varlen_workspace_bytes(N, Tt, H, DK, DV, ckpt_given=h_ckpt is not None),
+                                dev)
     _check(lib().ckda_bwd_varlen(N, Tt, _ptr(cu), _ptr(cu_seqlens_dev), H, DK, DV, dt, _flags(g, (Tt,), qk_norm, gate_map),
                                  _ptr(q),
                                  _ptr(k), _ptr(v), _ptr(g), _ptr(s), _ptr(beta), float(scale),

@@ -406,6 +406,20 @@ size_t ckda_bwd_varlen_workspace_bytes(int N, int T_total, int H, int DK, int DV
     return ckda::bwd_workspace_bytes_full(varlen_slots(N, T_total), nss, H, DK, DV);
 }
 
+size_t ckda_bwd_workspace_bytes_given_ckpt(int B, int T, int H, int DK, int DV) {
+    if (B < 0 || T < 0 || H < 0 || !head_ok(DK) || !head_ok(DV)) return 0;
+    const int G = ckda::segment_min_chunks();
+    const long long nss = static_cast<long long>(B) * (((T + 63) / 64 + G - 1) / G);
+    return ckda::bwd_workspace_bytes_given_ckpt(fwd_slots(B, T), static_cast<int>(nss), H, DK, DV);
+}
+
+size_t ckda_bwd_varlen_workspace_bytes_given_ckpt(int N, int T_total, int H, int DK, int DV) {
+    if (N < 0 || T_total < 0 || H < 0 || !head_ok(DK) || !head_ok(DV)) return 0;
+    const int G = ckda::segment_min_chunks();
+    const int nss = (T_total + 64 * G - 1) / (64 * G) + N;
+    return ckda::bwd_workspace_bytes_given_ckpt(varlen_slots(N, T_total), nss, H, DK, DV);
+}
+
 namespace {
 
 // shared tail of ckda_bwd / ckda_bwd_varlen: pointer checks, workspace, launch

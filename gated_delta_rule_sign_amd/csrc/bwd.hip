@@ -34,7 +34,9 @@
 //           which a forward record never exceeds);
 //   seg     the segment buffers of the reverse pass (segment mode, when the
 //           plan takes it and they fit): per segment slot and head its end G,
-//           H_s and P_s.
+//           H_s and P_s.  With the caller's checkpoints the ckpt room is
+//           unused and the segment buffers start there; without them they
+//           follow it.
 #include "ckda_device.h"
 #include "ckda_launch.h"
 #include "ckda_record.h"
@@ -79,6 +81,12 @@ size_t bwd_ckpt_bytes(int nslots, int H, int DK, int DV) {
 // nsslots_max segment slots
 size_t bwd_workspace_bytes_full(int nslots, int nsslots_max, int H, int DK, int DV) {
     return BwdLayout(nslots, H, DK, DV).end_ckpt + seg_buffer_bytes(nsslots_max, H, DK, DV);
+}
+
+// the layout when the caller gives the checkpoints: the segment buffers take
+// the checkpoint room's place
+size_t bwd_workspace_bytes_given_ckpt(int nslots, int nsslots_max, int H, int DK, int DV) {
+    return BwdLayout(nslots, H, DK, DV).off_ckpt + seg_buffer_bytes(nsslots_max, H, DK, DV);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t st) {
@@ -129,11 +137,12 @@ hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t st) {
     rp.cu = a.cu; rp.scale = a.scale; rp.B = a.B; rp.T = a.T; rp.H = a.H; rp.ndocs = a.ndocs;
     {   // segmented reverse pass when the plan takes it and the workspace has room
         const bool varlen = a.cu != nullptr;
-        const size_t room = a.ws_bytes > lay.end_ckpt ? a.ws_bytes - lay.end_ckpt : 0;
+        const size_t seg0 = a.h_ckpt ? lay.off_ckpt : lay.end_ckpt;
+        const size_t room = a.ws_bytes > seg0 ? a.ws_bytes - seg0 : 0;
         rp.seg_len = rev_segment_plan(a.cu_host, varlen, a.ndocs, a.B, a.T, a.H, DK, DV, room, st);
         if (rp.seg_len > 0) {
             rp.nsslots = seg_slots(varlen, a.B, a.T, a.ndocs, rp.seg_len);
-            float* sb = reinterpret_cast<float*>(ws + lay.end_ckpt);
+            float* sb = reinterpret_cast<float*>(ws + seg0);
             const size_t per = static_cast<size_t>(rp.nsslots) * a.H * DK * DV;
             rp.seg_start = sb;
             rp.seg_h = sb + per;

@@ -155,6 +155,8 @@ size_t bwd_ckpt_bytes(int nslots, int H, int DK, int DV);
 // blocks, then room for recomputed checkpoints, then the segment buffers for
 // up to nsslots_max segment slots
 size_t bwd_workspace_bytes_full(int nslots, int nsslots_max, int H, int DK, int DV);
+// blocks, then the segment buffers (the caller gives the checkpoints)
+size_t bwd_workspace_bytes_given_ckpt(int nslots, int nsslots_max, int H, int DK, int DV);
 hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t stream);
 
 }  // namespace ckda

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define CKDA_ABI_VERSION 9
+#define CKDA_ABI_VERSION 10
 
 /* Status codes and dtype codes travel as fixed-width integers (any value a
  * caller passes is well defined on both sides of the boundary; unknown
@@ -260,11 +260,16 @@ ckda_status_t ckda_decode_step(int N, int H, int DK, int DV, ckda_dtype_t in_dty
  *   workspace: ckda_bwd_workspace_bytes(...) bytes of device memory: per
  *           (chunk, head) the blocks of the chunk-parallel passes and the
  *           reverse pass's dU and chunk-end state gradient, then room for
- *           recomputed checkpoints.  Less is accepted down to the part before
- *           that room when h_ckpt is given.
+ *           recomputed checkpoints, then the segment buffers of the reverse
+ *           pass over long chains.  With h_ckpt given,
+ *           ckda_bwd_workspace_bytes_given_ckpt(...) bytes suffice (the
+ *           segment buffers take the checkpoint room's place); less is
+ *           accepted down to the part before that room (the reverse pass then
+ *           walks whole chains).
  * dg is the gradient w.r.t. g = log|alpha| (alpha * dL/dalpha); s gets none.
  * ---------------------------------------------------------------------- */
 size_t ckda_bwd_workspace_bytes(int B, int T, int H, int DK, int DV);
+size_t ckda_bwd_workspace_bytes_given_ckpt(int B, int T, int H, int DK, int DV);
 ckda_status_t ckda_bwd(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype,
                        ckda_flags_t flags, const void* q, const void* k, const void* v, const float* g,
                        const int8_t* s, const float* beta, float scale, const float* h0,
@@ -282,10 +287,13 @@ ckda_status_t ckda_bwd(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtyp
  *   dq, dk, dg: [T_total,H,DK] f32;  dv: [T_total,H,DV];  dbeta: [T_total,H]
  *   (flags & CKDA_GATE_HEAD: g, s, dg [T_total,H])
  *   dh0: [N,H,DK,DV] f32 or NULL
- *   workspace: ckda_bwd_varlen_workspace_bytes(...) bytes of device memory
+ *   workspace: ckda_bwd_varlen_workspace_bytes(...) bytes of device memory,
+ *           or ckda_bwd_varlen_workspace_bytes_given_ckpt(...) with h_ckpt
+ *           given
  * Conventions and errors as for ckda_bwd and ckda_fwd_varlen.
  * ---------------------------------------------------------------------- */
 size_t ckda_bwd_varlen_workspace_bytes(int N, int T_total, int H, int DK, int DV);
+size_t ckda_bwd_varlen_workspace_bytes_given_ckpt(int N, int T_total, int H, int DK, int DV);
 ckda_status_t ckda_bwd_varlen(int N, int T_total, const int32_t* cu_seqlens_host,
                               const int32_t* cu_seqlens_dev, int H, int DK, int DV,
                               ckda_dtype_t in_dtype, ckda_flags_t flags, const void* q, const void* k,

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.ckda_abi_version() == 9
+    assert L.ckda_abi_version() == 10
     assert L.ckda_status_string(0) == b"ok"
     for st in range(1, 8):
         assert L.ckda_status_string(st) not in (b"ok", b"unknown status")
@@ -152,6 +152,19 @@ def test_varlen_backward_boundary(L):
     assert L.ckda_bwd_varlen_workspace_bytes(3, 100, 2, 64, 32) == \
         sum(bwd_layout((2 + 3) * 2, 64, 32)) + seg_bytes(1 + 3, 2, 64, 32)
     assert L.ckda_bwd_varlen_workspace_bytes(3, 100, 2, 48, 32) == 0
+    # with the caller's checkpoints the segment buffers take the checkpoint
+    # room's place
+    assert L.ckda_bwd_workspace_bytes_given_ckpt(1, 64, 1, 64, 32) == bwd_layout(1, 64, 32)[0] + seg_bytes(1, 1, 64, 32)
+    assert L.ckda_bwd_workspace_bytes_given_ckpt(2, 100, 3, 32, 128) == \
+        bwd_layout(2 * 2 * 3, 32, 128)[0] + seg_bytes(2 * 1, 3, 32, 128)
+    assert L.ckda_bwd_varlen_workspace_bytes_given_ckpt(3, 100, 2, 64, 32) == \
+        bwd_layout((2 + 3) * 2, 64, 32)[0] + seg_bytes(1 + 3, 2, 64, 32)
+    assert L.ckda_bwd_workspace_bytes_given_ckpt(1, 64, 1, 96, 32) == 0
+    assert L.ckda_bwd_varlen_workspace_bytes_given_ckpt(-1, 100, 2, 64, 32) == 0
+    # layer_bwd (B=8, T=4096, H=16, d=128): the checkpoint room is 0.54 GB
+    full = L.ckda_bwd_workspace_bytes(8, 4096, 16, 128, 128)
+    given = L.ckda_bwd_workspace_bytes_given_ckpt(8, 4096, 16, 128, 128)
+    assert full - given == bwd_layout(8 * 64 * 16, 128, 128)[1] and given < 2 * 10**9
     assert bwd_varlen(L, [1, 5], 1, 5) == 5                       # does not start at 0
     assert bwd_varlen(L, [0, 5, 3], 2, 3) == 5                    # decreasing
     assert bwd_varlen(L, None, 2, 4) == 1

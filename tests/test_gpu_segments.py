@@ -218,10 +218,18 @@ def test_segmented_reverse_pass(dtype, DK, DV, T):
         _, _, hc = ckda.fwd(**d, scale=0.8, h0=h0, want_ckpt=True)
         r_w = ckda.bwd(**d, h_ckpt=hc, do=do, scale=0.8, h0=h0, dht=dev_tensor(dht))
         ckda.set_segment_chunks(16)
+        # the binding sizes the workspace for given checkpoints (segment
+        # buffers in the checkpoint room's place); the full size puts them
+        # after that room: same plan, same results
         r = ckda.bwd(**d, h_ckpt=hc, do=do, scale=0.8, h0=h0, dht=dev_tensor(dht))
+        ws_full = torch.empty(ckda.bwd_workspace_bytes(B, T, H, DK, DV), dtype=torch.uint8, device="cuda:0")
+        r_full = ckda.bwd(**d, h_ckpt=hc, do=do, scale=0.8, h0=h0, dht=dev_tensor(dht), workspace=ws_full)
     finally:
         ckda.set_segment_chunks(0)
     torch.cuda.synchronize()
+    assert ckda.bwd_workspace_bytes(B, T, H, DK, DV, ckpt_given=True) < ws_full.numel()
+    for name in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        assert torch.equal(r[name], r_full[name]), name
     for name in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
         e = rel_max(host(r[name]), host(r_w[name]))
         print(f"  {name} segmented vs whole chains: {e:.2e}")
