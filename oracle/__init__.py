@@ -212,6 +212,98 @@ def gate_map_bwd(x, y, dg, dbeta):
 
 
 # ----------------------------------------------------------------------------
+# Optional short convolution (the width-4 part of the pre-mixer prep).  The
+# "complex-kda-1.3B-100B" model card lists a "short convolution of width 4"
+# among the layer's parts and says nothing more about it.  Reading taken here:
+# a depthwise causal convolution over tokens with one 4-tap filter per channel
+# (channels = heads x head dimension), applied to an input before the mixer,
+# with zero history before each sequence or document unless the caller gives
+# the three inputs that preceded it, optionally followed by SiLU:
+#   z_t[c] = sum_{j=0..3} w[c, j] x_{t-3+j}[c],   y_t = z_t or z_t sigmoid(z_t)
+# (tap 3 takes the current token).  Written out token by token, per document.
+# ----------------------------------------------------------------------------
+CONV_WIDTH = 4
+
+
+def _sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def _conv_docs(x, cu_seqlens):
+    """Documents of x as (start, stop) row ranges of a [T_total, C] view."""
+    x = np.asarray(x, np.float64)
+    if cu_seqlens is None:
+        B, T, C = x.shape
+        return x.reshape(B * T, C), [(b * T, (b + 1) * T) for b in range(B)]
+    cu = [int(c) for c in np.asarray(cu_seqlens)]
+    return x, [(cu[d], cu[d + 1]) for d in range(len(cu) - 1)]
+
+
+def short_conv(x, w, cu_seqlens=None, state0=None, silu=False):
+    """x: [B, T, C] (sequences), or [T_total, C] with cu_seqlens (documents);
+    w: [C, 4]; state0: [nseq, 3, C], the inputs x_{-3}, x_{-2}, x_{-1} before
+    each sequence (None: zeros).  Returns (y shaped like x, state_out
+    [nseq, 3, C]: each sequence's last three inputs, history included)."""
+    xf, docs = _conv_docs(x, cu_seqlens)
+    w = np.asarray(w, np.float64)
+    C = xf.shape[1]
+    y = np.zeros_like(xf)
+    st = np.zeros((len(docs), CONV_WIDTH - 1, C))
+    for d, (a, b) in enumerate(docs):
+        hist = np.zeros((CONV_WIDTH - 1, C)) if state0 is None else np.asarray(state0, np.float64)[d]
+        xx = np.concatenate([hist, xf[a:b]], axis=0)   # row i holds x_{i-3}
+        for t in range(b - a):
+            z = np.zeros(C)
+            for j in range(CONV_WIDTH):
+                z += w[:, j] * xx[t + j]
+            y[a + t] = z * _sigmoid(z) if silu else z
+        st[d] = xx[b - a:]
+    return y.reshape(np.shape(x)), st
+
+
+def short_conv_bwd(x, w, dy, cu_seqlens=None, state0=None, silu=False):
+    """Reverse mode of short_conv: (dx like x, dw [C, 4], dstate0 [nseq, 3, C])."""
+    xf, docs = _conv_docs(x, cu_seqlens)
+    dyf = np.asarray(dy, np.float64).reshape(xf.shape)
+    w = np.asarray(w, np.float64)
+    C = xf.shape[1]
+    dx = np.zeros_like(xf)
+    dw = np.zeros((C, CONV_WIDTH))
+    ds = np.zeros((len(docs), CONV_WIDTH - 1, C))
+    for d, (a, b) in enumerate(docs):
+        hist = np.zeros((CONV_WIDTH - 1, C)) if state0 is None else np.asarray(state0, np.float64)[d]
+        xx = np.concatenate([hist, xf[a:b]], axis=0)
+        dxx = np.zeros_like(xx)
+        for t in range(b - a):
+            z = np.zeros(C)
+            for j in range(CONV_WIDTH):
+                z += w[:, j] * xx[t + j]
+            if silu:
+                sg = _sigmoid(z)
+                dz = dyf[a + t] * sg * (1.0 + z * (1.0 - sg))
+            else:
+                dz = dyf[a + t]
+            for j in range(CONV_WIDTH):
+                dxx[t + j] += w[:, j] * dz
+                dw[:, j] += dz * xx[t + j]
+        dx[a:b] = dxx[CONV_WIDTH - 1:]
+        ds[d] = dxx[:CONV_WIDTH - 1]
+    return dx.reshape(np.shape(x)), dw, ds
+
+
+def short_conv_step(x, w, window, silu=False):
+    """One decode step: x [N, C], window [N, 3, C] (the last three inputs).
+    Returns (y [N, C], the new window)."""
+    x = np.asarray(x, np.float64)
+    xx = np.concatenate([np.asarray(window, np.float64), x[:, None, :]], axis=1)
+    w = np.asarray(w, np.float64)
+    z = np.zeros_like(x)
+    for j in range(CONV_WIDTH):
+        z += w[None, :, j] * xx[:, j]
+    return (z * _sigmoid(z) if silu else z), xx[:, 1:]
+
+
+# ----------------------------------------------------------------------------
 # tensor-level entry points ([B, T, H, D] layout); qk_norm=True runs the
 # recurrence on l2norm(q), l2norm(k)
 # ----------------------------------------------------------------------------
