@@ -15,7 +15,7 @@ state pass, and the long_64k backward with and without the segmented
 reverse pass.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       [--only fwd|fwd_head_gate|fwd_qk_norm|fwd_long|bwd_long|decode|bwd|copy]
+       [--only fwd|fwd_head_gate|fwd_qk_norm|fwd_long|bwd_long|decode|bwd|copy|conv]
 """
 from __future__ import annotations
 
@@ -324,6 +324,33 @@ def bench_bwd_long(torch, steps=2, warmup=1):
     return res
 
 
+def bench_conv(torch, steps, warmup):
+    """The optional short convolution (width 4, SiLU) over one input of the
+    layer workload's shapes (B=8, T=4096, 16 x 128 channels, bf16): forward
+    and backward, one launch sequence each, HBM-bound."""
+    from gated_delta_rule_sign_amd import ckda
+    from gated_delta_rule_sign_amd import inputs as I
+    B, T, C = 8, 4096, 2048
+    log("generating short-conv inputs")
+    x, w, _, dy = I.draw_conv(41, (B, T, C), C, B, "bf16", with_state=False)
+    xd, wd, dyd = dev_tensor(torch, x), dev_tensor(torch, w), dev_tensor(torch, dy)
+    y = torch.empty_like(xd)
+    ws = torch.empty(int(ckda.lib().ckda_short_conv_bwd_workspace_bytes(B * T, C)), dtype=torch.uint8,
+                     device="cuda:0")
+    log("timing short conv")
+    _, per_f = time_kernel_launches(torch, lambda: ckda.short_conv(xd, wd, silu=True, y=y), steps, warmup)
+    _, per_b = time_kernel_launches(torch, lambda: ckda.short_conv_bwd(xd, wd, dyd, silu=True, workspace=ws),
+                                    steps, warmup)
+    n = B * T * C
+    fb = n * (2 + 2) + C * 16            # x read, y written (bf16), taps
+    bb = n * (2 + 4 + 4) + C * 16 * 2    # x and dy read, dx written, taps and dw
+    tf, tb = float(np.mean(per_f)), float(np.mean(per_b))
+    return {"workload": "q of layer_bf16 (B=8, T=4096, 2048 channels, bf16), width 4, SiLU",
+            "fwd_ms": tf, "fwd_gbs": fb / (tf * 1e-3) / 1e9, "fwd_frac_of_hbm_peak": fb / (tf * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "bwd_ms": tb, "bwd_gbs": bb / (tb * 1e-3) / 1e9, "bwd_frac_of_hbm_peak": bb / (tb * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes_fwd": fb, "algorithmic_bytes_bwd": bb}
+
+
 def bench_copy(torch, nbytes=1 << 30, reps=5):
     """A plain device copy of known size (calibration for HBM byte counters)."""
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").uniform_()
@@ -385,7 +412,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", choices=["fwd", "fwd_head_gate", "fwd_qk_norm", "fwd_long", "bwd_long", "decode", "bwd",
-                                       "copy"], default=None)
+                                       "copy", "conv"], default=None)
     ap.add_argument("--decode-steps", type=int, default=512)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -404,6 +431,9 @@ def main():
         return
     if args.only == "decode":
         print(json.dumps(bench_decode(torch, args.decode_steps)))
+        return
+    if args.only == "conv":
+        print(json.dumps(bench_conv(torch, args.steps, args.warmup)))
         return
     if args.only == "bwd":
         print(json.dumps(bench_bwd(torch, args.steps, args.warmup)))
@@ -430,6 +460,7 @@ def main():
     fq = bench_fwd(torch, args.steps, args.warmup, "layer_bf16_qk_norm")
     longs = [bench_fwd_long(torch, max(3, args.steps // 4), 3, wl) for wl in ("varlen_64k", "long_64k")]
     bwl = bench_bwd_long(torch)
+    cv = bench_conv(torch, args.steps, args.warmup)
     cpu = None if args.no_cpu else cpu_baseline(fw["w"])
 
     achieved = fw["bytes"] / (fw["launch_ms"] * 1e-3) / 1e9
@@ -498,6 +529,7 @@ def main():
                             "frac_of_hbm_peak": fq["bytes"] / (fq["launch_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "forward_long_chains": longs,
         "backward_long_chains": bwl,
+        "short_conv": cv,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

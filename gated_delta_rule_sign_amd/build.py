@@ -13,7 +13,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libckda.so")
 SOURCES = ["api.cpp", "decode.hip", "chunk.hip", "chunk_rev.hip", "chunk_grad.hip", "state.hip", "bwd.hip",
-           "rev.hip", "grad.hip"]
+           "rev.hip", "grad.hip", "conv.hip"]
 ARCH = os.environ.get("CKDA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

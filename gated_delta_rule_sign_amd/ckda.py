@@ -78,6 +78,14 @@ def lib() -> ctypes.CDLL:
     L.ckda_bwd_varlen.restype = I
     L.ckda_set_segment_chunks.argtypes = [I]
     L.ckda_set_segment_chunks.restype = I
+    L.ckda_short_conv_fwd.argtypes = [I, I, P, P, I, I, U, P, P, P, P, P, P]
+    L.ckda_short_conv_fwd.restype = I
+    L.ckda_short_conv_bwd_workspace_bytes.argtypes = [I, I]
+    L.ckda_short_conv_bwd_workspace_bytes.restype = S
+    L.ckda_short_conv_bwd.argtypes = [I, I, P, P, I, I, U, P, P, P, P, P, P, P, P, S, P]
+    L.ckda_short_conv_bwd.restype = I
+    L.ckda_short_conv_step.argtypes = [I, I, I, U, P, P, P, P, P]
+    L.ckda_short_conv_step.restype = I
     _lib = L
     return L
 
@@ -375,3 +383,89 @@ def bwd_varlen(q, k, v, g, s, beta, cu_seqlens, h_ckpt, do, scale: float = 1.0, 
                                  _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
                                  _ptr(out["dh0"]), _ptr(workspace), wsb, _stream()))
     return out
+
+
+# ----------------------------------------------------------------------------
+# short convolution (optional width-4 part of the pre-mixer prep)
+# ----------------------------------------------------------------------------
+CKDA_CONV_SILU = 8
+CONV_WIDTH = 4
+
+
+def _conv_seqs(x, cu_seqlens, cu_seqlens_dev):
+    """(N, T_total, C, host cu, device cu) for x [B, T, ...] (B sequences) or
+    x [T_total, ...] with cu_seqlens (an int32 CPU tensor [N+1])."""
+    if cu_seqlens is None:
+        B, T = x.shape[0], x.shape[1]
+        C = int(x[0, 0].numel()) if B * T > 0 else int(torch.tensor(x.shape[2:]).prod())
+        return B, B * T, C, None, None
+    cu = cu_seqlens
+    if cu.is_cuda or cu.dtype != torch.int32 or not cu.is_contiguous():
+        raise CkdaError("cu_seqlens must be a contiguous int32 CPU tensor")
+    N = cu.numel() - 1
+    if cu_seqlens_dev is None:
+        cu_seqlens_dev = cu.to(x.device)
+    _need(cu_seqlens_dev, "cu_seqlens_dev", torch.int32, (N + 1,), x.device)
+    C = int(torch.tensor(x.shape[1:]).prod()) if x.dim() > 1 else 1
+    return N, x.shape[0], C, cu, cu_seqlens_dev
+
+
+def short_conv(x, w, cu_seqlens=None, state0=None, silu: bool = False, want_state: bool = False,
+               cu_seqlens_dev=None, y=None, state_out=None):
+    """Depthwise causal width-4 convolution over tokens (ckda_short_conv_fwd).
+    x: [B, T, ...] (B sequences) or [T_total, ...] with cu_seqlens; channels =
+    the trailing dims (e.g. H x D); w [C, 4] f32; state0 [N, 3, C] (x's dtype)
+    or None.  Returns (y like x, state_out [N, 3, C] or None).  state_out may
+    be state0 (updated in place)."""
+    N, Tt, C, cu, cud = _conv_seqs(x, cu_seqlens, cu_seqlens_dev)
+    dt, dev = _dtype_code(x), x.device
+    _need(x, "x", x.dtype)
+    _need(w, "w", torch.float32, (C, CONV_WIDTH), dev)
+    _need(state0, "state0", x.dtype, (N, CONV_WIDTH - 1, C), dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", x.dtype, tuple(x.shape), dev)
+    if want_state and state_out is None:
+        state_out = torch.empty((N, CONV_WIDTH - 1, C), dtype=x.dtype, device=dev)
+    _need(state_out, "state_out", x.dtype, (N, CONV_WIDTH - 1, C), dev)
+    _check(lib().ckda_short_conv_fwd(N, Tt, _ptr(cu), _ptr(cud), C, dt, CKDA_CONV_SILU if silu else 0, _ptr(x),
+                                     _ptr(w), _ptr(state0), _ptr(y), _ptr(state_out), _stream()))
+    return y, state_out
+
+
+def short_conv_bwd(x, w, dy, cu_seqlens=None, state0=None, silu: bool = False, want_dstate0: bool = False,
+                   cu_seqlens_dev=None, workspace=None):
+    """Backward of short_conv (ckda_short_conv_bwd): dy f32 shaped like x.
+    Returns dict dx (f32 like x), dw [C, 4] f32, dstate0 [N, 3, C] f32 or None."""
+    N, Tt, C, cu, cud = _conv_seqs(x, cu_seqlens, cu_seqlens_dev)
+    dt, dev = _dtype_code(x), x.device
+    _need(x, "x", x.dtype)
+    _need(w, "w", torch.float32, (C, CONV_WIDTH), dev)
+    _need(state0, "state0", x.dtype, (N, CONV_WIDTH - 1, C), dev)
+    _need(dy, "dy", torch.float32, tuple(x.shape), dev)
+    out = dict(dx=torch.empty(tuple(x.shape), dtype=torch.float32, device=dev),
+               dw=torch.empty((C, CONV_WIDTH), dtype=torch.float32, device=dev),
+               dstate0=torch.empty((N, CONV_WIDTH - 1, C), dtype=torch.float32, device=dev) if want_dstate0 else None)
+    workspace, wsb = _workspace(workspace, int(lib().ckda_short_conv_bwd_workspace_bytes(Tt, C)), dev)
+    _check(lib().ckda_short_conv_bwd(N, Tt, _ptr(cu), _ptr(cud), C, dt, CKDA_CONV_SILU if silu else 0, _ptr(x),
+                                     _ptr(w), _ptr(state0), _ptr(dy), _ptr(out["dx"]), _ptr(out["dw"]),
+                                     _ptr(out["dstate0"]), _ptr(workspace), wsb, _stream()))
+    return out
+
+
+def short_conv_step(x, w, window, silu: bool = False, y=None):
+    """One decode step (ckda_short_conv_step): x [N, ...] (C channels after
+    the first dim), window [N, 3, C] updated in place.  Returns y like x."""
+    N = x.shape[0]
+    C = int(x[0].numel()) if N > 0 else int(torch.tensor(x.shape[1:]).prod())
+    dev = x.device
+    _need(x, "x", x.dtype)
+    _need(w, "w", torch.float32, (C, CONV_WIDTH), dev)
+    _need(window, "window", x.dtype, (N, CONV_WIDTH - 1, C), dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", x.dtype, tuple(x.shape), dev)
+    _check(lib().ckda_short_conv_step(N, C, _dtype_code(x), CKDA_CONV_SILU if silu else 0, _ptr(x), _ptr(w),
+                                      _ptr(window), _ptr(y), _stream()))
+    return y
+

@@ -14,6 +14,7 @@
 #include <initializer_list>
 #include <mutex>
 
+#include "ckda_conv.h"
 #include "ckda_launch.h"
 
 namespace {
@@ -516,6 +517,112 @@ ckda_status_t ckda_bwd_varlen(int N, int T_total, const int32_t* cu, const int32
     a.dbeta = dbeta; a.dh0 = dh0; a.cu = cu_dev; a.cu_host = cu; a.ndocs = N;
     return bwd_common(a, varlen_slots(N, T_total), T_total > 0, workspace, workspace_bytes, stream,
                       "ckda_bwd_varlen launch");
+}
+
+
+// ---------------------------------------------------------------------------
+// Short convolution (the optional width-4 part of the pre-mixer prep)
+// ---------------------------------------------------------------------------
+}  // extern "C"
+
+namespace {
+
+// shape, dtype, flag and sequence checks shared by the two sequence calls;
+// fills a's sequence fields
+ckda_status_t conv_common(int N, int T, const int32_t* cu_host, const int32_t* cu_dev, int C,
+                          ckda_dtype_t dt, ckda_flags_t flags, ckda::ConvArgs& a) {
+    CKDA_TRY(check_dtype(dt));
+    if (flags & ~CKDA_CONV_SILU) return fail(CKDA_ERR_UNSUPPORTED, "unknown option flags 0x%x", unsigned(flags));
+    if (N < 0 || T < 0 || C < 0) return fail(CKDA_ERR_SHAPE, "negative size (N=%d, T=%d, C=%d)", N, T, C);
+    if (C % 4 != 0) return fail(CKDA_ERR_UNSUPPORTED, "C=%d channels: a multiple of 4 is required", C);
+    if (static_cast<long long>(T) * C >= (1LL << 40) || C > (1 << 28))
+        return fail(CKDA_ERR_UNSUPPORTED, "tensor too large");
+    if ((cu_host == nullptr) != (cu_dev == nullptr))
+        return fail(CKDA_ERR_SEQLENS, "give both cu_seqlens copies (host and device) or neither");
+    if (cu_host) {
+        CKDA_TRY(check_cu(N, T, cu_host));
+    } else if (T > 0 && (N == 0 || T % N != 0)) {
+        return fail(CKDA_ERR_SHAPE, "without cu_seqlens, T_total=%d must split into N=%d equal sequences", T, N);
+    }
+    a.N = N; a.T = T; a.C = C; a.bf16 = dt == CKDA_BF16; a.silu = (flags & CKDA_CONV_SILU) != 0;
+    a.cu = cu_dev;
+    return CKDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ckda_short_conv_bwd_workspace_bytes(int T_total, int C) {
+    if (T_total < 0 || C < 0 || C % 4 != 0) return 0;
+    return ckda::conv_bwd_workspace_bytes(T_total, C);
+}
+
+ckda_status_t ckda_short_conv_fwd(int N, int T_total, const int32_t* cu_seqlens_host,
+                                  const int32_t* cu_seqlens_dev, int C, ckda_dtype_t in_dtype,
+                                  ckda_flags_t flags, const void* x, const float* w, const void* state0,
+                                  void* y, void* state_out, ckda_stream_t stream) {
+    ckda::ConvArgs a{};
+    CKDA_TRY(conv_common(N, T_total, cu_seqlens_host, cu_seqlens_dev, C, in_dtype, flags, a));
+    if (C == 0 || (T_total == 0 && !state_out)) return ok();
+    if (T_total > 0) { CKDA_REQUIRE(x); CKDA_REQUIRE(w); CKDA_REQUIRE(y); }
+    CKDA_ALIGNED(x); CKDA_ALIGNED(w); CKDA_ALIGNED(state0); CKDA_ALIGNED(y); CKDA_ALIGNED(state_out);
+    const size_t es = a.bf16 ? 2 : 4;
+    const size_t xb = static_cast<size_t>(T_total) * C * es, wb = static_cast<size_t>(C) * 16;
+    const size_t sb = static_cast<size_t>(N) * 3 * C * es;
+    // the outgoing window may be the incoming one (updated in place), or apart from it
+    const void* s0_other = state_out == state0 ? nullptr : state0;
+    CKDA_TRY(check_no_alias({{y, xb, "y"}, {state_out, sb, "state_out"}},
+                            {{x, xb, "x"}, {w, wb, "w"}, {s0_other, sb, "state0"}}));
+    a.x = x; a.w = w; a.state0 = state0; a.y = y; a.state_out = state_out;
+    return hip_status(ckda::launch_conv_fwd(a, static_cast<hipStream_t>(stream)), "ckda_short_conv_fwd launch");
+}
+
+ckda_status_t ckda_short_conv_bwd(int N, int T_total, const int32_t* cu_seqlens_host,
+                                  const int32_t* cu_seqlens_dev, int C, ckda_dtype_t in_dtype,
+                                  ckda_flags_t flags, const void* x, const float* w, const void* state0,
+                                  const float* dy, float* dx, float* dw, float* dstate0, void* workspace,
+                                  size_t workspace_bytes, ckda_stream_t stream) {
+    ckda::ConvArgs a{};
+    CKDA_TRY(conv_common(N, T_total, cu_seqlens_host, cu_seqlens_dev, C, in_dtype, flags, a));
+    if (C == 0) return ok();
+    CKDA_REQUIRE(w); CKDA_REQUIRE(dw);
+    if (T_total > 0) { CKDA_REQUIRE(x); CKDA_REQUIRE(dy); CKDA_REQUIRE(dx); }
+    CKDA_ALIGNED(x); CKDA_ALIGNED(w); CKDA_ALIGNED(state0); CKDA_ALIGNED(dy); CKDA_ALIGNED(dx); CKDA_ALIGNED(dw);
+    CKDA_ALIGNED(dstate0); CKDA_ALIGNED(workspace);
+    const size_t need = ckda::conv_bwd_workspace_bytes(T_total, C);
+    if (need > 0) {
+        CKDA_REQUIRE(workspace);
+        if (workspace_bytes < need)
+            return fail(CKDA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+    }
+    const size_t es = a.bf16 ? 2 : 4;
+    const size_t xb = static_cast<size_t>(T_total) * C * es, fb = static_cast<size_t>(T_total) * C * 4;
+    const size_t wb = static_cast<size_t>(C) * 16, sb = static_cast<size_t>(N) * 3 * C;
+    CKDA_TRY(check_no_alias({{dx, fb, "dx"}, {dw, wb, "dw"}, {dstate0, sb * 4, "dstate0"}, {workspace, workspace_bytes, "workspace"}},
+                            {{x, xb, "x"}, {w, wb, "w"}, {state0, sb * es, "state0"}, {dy, fb, "dy"}}));
+    a.x = x; a.w = w; a.state0 = state0; a.dy = dy; a.dx = dx; a.dw = dw; a.dstate0 = dstate0;
+    a.partial = static_cast<float*>(workspace);
+    return hip_status(ckda::launch_conv_bwd(a, static_cast<hipStream_t>(stream)), "ckda_short_conv_bwd launch");
+}
+
+ckda_status_t ckda_short_conv_step(int N, int C, ckda_dtype_t in_dtype, ckda_flags_t flags, const void* x,
+                                   const float* w, void* window, void* y, ckda_stream_t stream) {
+    CKDA_TRY(check_dtype(in_dtype));
+    if (flags & ~CKDA_CONV_SILU) return fail(CKDA_ERR_UNSUPPORTED, "unknown option flags 0x%x", unsigned(flags));
+    if (N < 0 || C < 0) return fail(CKDA_ERR_SHAPE, "negative size (N=%d, C=%d)", N, C);
+    if (C % 4 != 0) return fail(CKDA_ERR_UNSUPPORTED, "C=%d channels: a multiple of 4 is required", C);
+    if (static_cast<long long>(N) * C >= (1LL << 40) || C > (1 << 28))
+        return fail(CKDA_ERR_UNSUPPORTED, "tensor too large");
+    if (N == 0 || C == 0) return ok();
+    CKDA_REQUIRE(x); CKDA_REQUIRE(w); CKDA_REQUIRE(window); CKDA_REQUIRE(y);
+    CKDA_ALIGNED(x); CKDA_ALIGNED(w); CKDA_ALIGNED(window); CKDA_ALIGNED(y);
+    const size_t es = in_dtype == CKDA_BF16 ? 2 : 4;
+    const size_t xb = static_cast<size_t>(N) * C * es;
+    CKDA_TRY(check_no_alias({{y, xb, "y"}, {window, 3 * xb, "window"}}, {{x, xb, "x"}, {w, static_cast<size_t>(C) * 16, "w"}}));
+    return hip_status(ckda::launch_conv_step(N, C, in_dtype == CKDA_BF16, (flags & CKDA_CONV_SILU) != 0, x, w,
+                                             window, y, static_cast<hipStream_t>(stream)),
+                      "ckda_short_conv_step launch");
 }
 
 }  // extern "C"

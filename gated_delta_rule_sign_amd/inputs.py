@@ -249,3 +249,16 @@ def make_workload(name: str, **override) -> Workload:
         h0 = draw_state(rng, (nd, H, DK, DV), 0.02)
         return Workload(name=name, cfg=cfg, tok=tok, h0=h0, cu_seqlens=cu)
     raise KeyError(name)
+
+
+def draw_conv(seed: int, x_shape: tuple, C: int, nseq: int, dtype: str, with_state: bool = True):
+    """Inputs of the optional short convolution: x ~ N(0,1) shaped x_shape
+    (stored in dtype), per-channel taps w [C, 4] ~ U(-1, 1) / 2 (the scale of a
+    width-4 filter's default uniform init), a window state0 [nseq, 3, C] ~ N(0,1)
+    in dtype (or None), and an upstream gradient dy ~ N(0,1) in float32."""
+    rng = np.random.default_rng(seed)
+    x = to_storage(rng.standard_normal(x_shape), dtype)
+    w = (rng.uniform(-1.0, 1.0, (C, 4)) / 2.0).astype(np.float32)
+    s0 = to_storage(rng.standard_normal((nseq, 3, C)), dtype) if with_state else None
+    dy = rng.standard_normal(x_shape).astype(np.float32)
+    return x, w, s0, dy

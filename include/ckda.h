@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define CKDA_ABI_VERSION 10
+#define CKDA_ABI_VERSION 11
 
 /* Status codes and dtype codes travel as fixed-width integers (any value a
  * caller passes is well defined on both sides of the boundary; unknown
@@ -102,6 +102,9 @@ typedef uint32_t ckda_flags_t;
 #define CKDA_GATE_HEAD 1u
 #define CKDA_QK_L2NORM 2u
 #define CKDA_GATE_MAP 4u
+/*  CKDA_CONV_SILU (the ckda_short_conv_* calls only, which accept no other
+ *      flag): the convolution's output goes through SiLU, z sigmoid(z). */
+#define CKDA_CONV_SILU 8u
 
 /* opaque HIP stream (hipStream_t); NULL = the default stream */
 typedef void* ckda_stream_t;
@@ -302,6 +305,53 @@ ckda_status_t ckda_bwd_varlen(int N, int T_total, const int32_t* cu_seqlens_host
                               const float* dht, float* dq, float* dk, float* dv, float* dg,
                               float* dbeta, float* dh0, void* workspace, size_t workspace_bytes,
                               ckda_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Short convolution: the optional width-4 part of the pre-mixer prep.  The
+ * "complex-kda-1.3B-100B" model card lists a short convolution of width 4
+ * among the layer's parts and nothing more; read here as a depthwise causal
+ * convolution over tokens with one 4-tap filter per channel, applied to an
+ * input of the mixer (q, k or v as [.., H*D] rows), optionally followed by
+ * SiLU (CKDA_CONV_SILU):
+ *     z_t[c] = sum_{j=0..3} w[c][j] x_{t-3+j}[c],   y_t = z_t or z_t sigmoid(z_t)
+ * Before each sequence the history is zero, or the caller's window of the
+ * three inputs that preceded it.
+ *   Sequences: cu_seqlens_host and cu_seqlens_dev (both, [N+1], as in
+ *           ckda_fwd_varlen), or both NULL for N equal sequences of T_total / N
+ *           tokens (T_total a multiple of N)
+ *   C: channels per token row, a multiple of 4 (H * D for a [.., H, D] tensor)
+ *   x: [T_total][C] in_dtype;  w: [C][4] f32 (tap 3 takes the current token)
+ *   state0: [N][3][C] in_dtype (x_{-3}, x_{-2}, x_{-1} of each sequence) or NULL
+ *   y: [T_total][C] in_dtype (rounded to bf16 for bf16 inputs); must not
+ *           overlap x
+ *   state_out: [N][3][C] in_dtype or NULL: each sequence's last three inputs
+ *           (its window rows where it is shorter than three), for a later
+ *           call or ckda_short_conv_step; may be state0 itself (in place)
+ * Every pointer 16-byte aligned.  Errors as for the mixer calls (host checks,
+ * nothing enqueued on failure).
+ * ---------------------------------------------------------------------- */
+ckda_status_t ckda_short_conv_fwd(int N, int T_total, const int32_t* cu_seqlens_host,
+                                  const int32_t* cu_seqlens_dev, int C, ckda_dtype_t in_dtype,
+                                  ckda_flags_t flags, const void* x, const float* w, const void* state0,
+                                  void* y, void* state_out, ckda_stream_t stream);
+
+/* Backward of ckda_short_conv_fwd for an upstream gradient dy ([T_total][C]
+ * f32): dx [T_total][C] f32, dw [C][4] f32 (summed in a fixed order: the
+ * same inputs give the same bits), dstate0 [N][3][C] f32 or NULL.
+ *   workspace: ckda_short_conv_bwd_workspace_bytes(T_total, C) bytes (per
+ *           64-token run and channel, its part of dw). */
+size_t ckda_short_conv_bwd_workspace_bytes(int T_total, int C);
+ckda_status_t ckda_short_conv_bwd(int N, int T_total, const int32_t* cu_seqlens_host,
+                                  const int32_t* cu_seqlens_dev, int C, ckda_dtype_t in_dtype,
+                                  ckda_flags_t flags, const void* x, const float* w, const void* state0,
+                                  const float* dy, float* dx, float* dw, float* dstate0, void* workspace,
+                                  size_t workspace_bytes, ckda_stream_t stream);
+
+/* One decode step of the convolution for N sequences: x, y [N][C] in_dtype,
+ * window [N][3][C] in_dtype (the last three inputs), shifted in place to end
+ * with x. */
+ckda_status_t ckda_short_conv_step(int N, int C, ckda_dtype_t in_dtype, ckda_flags_t flags, const void* x,
+                                   const float* w, void* window, void* y, ckda_stream_t stream);
 
 #ifdef __cplusplus
 }

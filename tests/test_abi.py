@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.ckda_abi_version() == 10
+    assert L.ckda_abi_version() == 11
     assert L.ckda_status_string(0) == b"ok"
     for st in range(1, 8):
         assert L.ckda_status_string(st) not in (b"ok", b"unknown status")
@@ -250,3 +250,39 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ckda, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ckda.CkdaError):
         ckda.lib()
+
+
+def test_short_conv_rejects_bad_arguments(L):
+    """Host checks of the short convolution: nothing is launched on failure."""
+    u = ctypes.c_uint32
+    cu = (ctypes.c_int32 * 3)(0, 5, 9)
+    def fwd(N=2, T=8, cuh=None, cud=None, C=8, dt=0, flags=0, x=FAKE, y=P(0x20000), so=None, s0=None):
+        return L.ckda_short_conv_fwd(N, T, cuh, cud, C, dt, u(flags), x, FAKE, s0, y, so, None)
+    assert fwd(C=6) == 4                                   # channels not a multiple of 4
+    assert fwd(flags=1) == 4 and fwd(flags=2) == 4          # mixer flags are not conv flags
+    assert fwd(dt=7) == 3
+    assert fwd(T=9) == 2                                    # 9 tokens do not split into 2 sequences
+    assert fwd(N=0, T=8) == 2
+    assert fwd(cuh=cu, cud=None, T=9) == 5                  # one copy of cu_seqlens only
+    assert fwd(N=2, T=10, cuh=cu, cud=FAKE) == 5            # cu_seqlens[N] != T_total
+    assert fwd(x=None) == 1
+    assert fwd(x=P(0x1008)) == 4                            # misaligned
+    assert fwd(y=FAKE) == 4 and b"overlaps" in L.ckda_last_error()
+    assert fwd(T=0, N=0) == 0 and fwd(C=0) == 0             # nothing to do
+    # the outgoing window may be the incoming one, but not overlap it otherwise
+    assert fwd(N=2, T=0, so=P(0x40000), s0=P(0x40010)) == 4
+    # backward: workspace per 64-token run and channel (4 taps, f32)
+    assert L.ckda_short_conv_bwd_workspace_bytes(130, 8) == 3 * 8 * 4 * 4
+    assert L.ckda_short_conv_bwd_workspace_bytes(130, 6) == 0
+    def bwd(ws=P(0x80000), wsb=BIG, C=8, T=8, dx=P(0x30000)):
+        return L.ckda_short_conv_bwd(2, T, None, None, C, 0, u(0), FAKE, P(0x50000), None, P(0x60000), dx,
+                                     P(0x70000), None, ws, ctypes.c_size_t(wsb), None)
+    assert bwd(ws=None) == 1
+    assert bwd(wsb=8 * 4 * 4 - 16) == 6
+    assert bwd(dx=FAKE) == 4                                # dx over x
+    assert bwd(C=10) == 4
+    # decode step
+    assert L.ckda_short_conv_step(2, 6, 0, u(0), FAKE, FAKE, FAKE, FAKE, None) == 4
+    assert L.ckda_short_conv_step(2, 8, 0, u(4), FAKE, FAKE, FAKE, FAKE, None) == 4
+    assert L.ckda_short_conv_step(2, 8, 0, u(0), FAKE, FAKE, None, FAKE, None) == 1
+    assert L.ckda_short_conv_step(0, 8, 0, u(0), None, None, None, None, None) == 0
