@@ -426,7 +426,7 @@ __device__ __forceinline__ void grad_phase1(const ChunkParams& p, const int slot
 // its substitution; kModeGrad writes no record and hands the chunk's A, the
 // diagonal inverses and Ke = kf e^b over to the backward's first
 // chunk-parallel gradient phase (grad.hip).
-template <typename Tin, int DK, int DV, bool HG, bool NQK, bool EX, int MODE>
+template <typename Tin, int DK, int DV, bool HG, bool NQK, bool EX, int MODE, bool GM>
 __device__ __forceinline__ void chunk_body(const ChunkParams& p, const int slot, const int h, unsigned char* smem)
 {
     using SH = ChunkShape<DK>;
@@ -496,8 +496,8 @@ __device__ __forceinline__ void chunk_body(const ChunkParams& p, const int slot,
             k8[ks].load(k + base);
             if constexpr (HG) {
                 const float gx = p.g[trow];
-                const float gt = p.gate_map ? gate_map_g(gx) : gx;
-                const uint32_t sb = p.gate_map ? (gx < 0.f ? 0xFFu : 0x01u) : static_cast<uint8_t>(p.s[trow]);
+                const float gt = GM ? gate_map_g(gx) : gx;
+                const uint32_t sb = GM ? (gx < 0.f ? 0xFFu : 0x01u) : static_cast<uint8_t>(p.s[trow]);
                 const uint32_t sw = sb * 0x01010101u;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) bs[8 * ks + e] = gt;
@@ -507,7 +507,7 @@ __device__ __forceinline__ void chunk_body(const ChunkParams& p, const int slot,
                 float4 a = reinterpret_cast<const float4*>(p.g + base)[0];
                 float4 b = reinterpret_cast<const float4*>(p.g + base)[1];
                 uint2 sv;
-                if (p.gate_map) {   // signs from the pre-activations, then the map
+                if constexpr (GM) {   // signs from the pre-activations, then the map
                     auto sb = [](float x, int sh) { return (x < 0.f ? 0xFFu : 0x01u) << sh; };
                     sv.x = sb(a.x, 0) | sb(a.y, 8) | sb(a.z, 16) | sb(a.w, 24);
                     sv.y = sb(b.x, 0) | sb(b.y, 8) | sb(b.z, 16) | sb(b.w, 24);
@@ -530,7 +530,7 @@ __device__ __forceinline__ void chunk_body(const ChunkParams& p, const int slot,
                 par[2 * ks + 1] = 0x01010101u;
             }
         }
-        const float bt = p.gate_map ? gate_map_beta(p.beta[trow]) : p.beta[trow];
+        const float bt = GM ? gate_map_beta(p.beta[trow]) : p.beta[trow];
         if (cgi == 0 && gq == 0) beta_s[t] = valid ? bt : 0.f;
     }
     float2* const nrm = reinterpret_cast<float2*>(smem + SH::L_NRM);
@@ -1085,19 +1085,19 @@ __device__ __forceinline__ void chunk_body(const ChunkParams& p, const int slot,
 
 // one workgroup per (chunk slot, head); second bound: waves per SIMD (two
 // 8-wave workgroups per CU -> 4, at most 128 VGPRs)
-template <typename Tin, int DK, int DV, bool HG, bool NQK, int MODE>
+template <typename Tin, int DK, int DV, bool HG, bool NQK, int MODE, bool GM>
 __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_kernel(ChunkParams p)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     // heads fastest: neighbouring workgroups share token rows
-    chunk_body<Tin, DK, DV, HG, NQK, false, MODE>(p, blockIdx.x / p.H, blockIdx.x % p.H, smem);
+    chunk_body<Tin, DK, DV, HG, NQK, false, MODE, GM>(p, blockIdx.x / p.H, blockIdx.x % p.H, smem);
 }
 
 // The exact path over the records the fast kernel flagged: workgroup x looks
 // at chunk-heads x*per .. x*per + per - 1 (per <= 64; record index = slot * H
 // + head), whose flags one wave-wide load gathers, and redoes the flagged ones
 // in turn.  With nothing flagged the launch reads one word per chunk-head.
-template <typename Tin, int DK, int DV, bool HG, bool NQK, int MODE>
+template <typename Tin, int DK, int DV, bool HG, bool NQK, int MODE, bool GM>
 __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_exact_kernel(ChunkParams p, int nch, int per)
 {
     using RC = std::conditional_t<MODE != kModeFwd, RevRecord<DK, DV, sizeof(Tin) == 4>, Record<DK, DV, sizeof(Tin) == 4>>;
@@ -1113,19 +1113,19 @@ __global__ void __launch_bounds__(ChunkShape<DK>::NW * 64, 4) ckda_chunk_exact_k
         const int j = __builtin_ctzll(mask);
         mask &= mask - 1ull;
         const int ch = c0 + j;
-        chunk_body<Tin, DK, DV, HG, NQK, true, MODE>(p, ch / p.H, ch % p.H, smem);
+        chunk_body<Tin, DK, DV, HG, NQK, true, MODE, GM>(p, ch / p.H, ch % p.H, smem);
         lds_sync();   // before the next chunk-head reuses LDS
     }
 }
 
-template <typename Tin, int DK, int DV, bool HG, bool NQK, int MODE>
-static hipError_t launch_chunk_t(const ChunkParams& p, int nslots, hipStream_t stream) {
+template <typename Tin, int DK, int DV, bool HG, bool NQK, int MODE, bool GM>
+static hipError_t launch_chunk_g(const ChunkParams& p, int nslots, hipStream_t stream) {
     using SH = ChunkShape<DK>;
     constexpr int LDS = MODE == kModeGrad ? GradShape<DK, DV>::LDS : SH::LDS;
     constexpr int LDS_EX = MODE == kModeGrad ? GradShape<DK, DV>::LDS : SH::LDS_EX;
     const long long grid = static_cast<long long>(nslots) * p.H;
     if (grid == 0) return hipSuccess;
-    auto kern = ckda_chunk_kernel<Tin, DK, DV, HG, NQK, MODE>;
+    auto kern = ckda_chunk_kernel<Tin, DK, DV, HG, NQK, MODE, GM>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
     if (e != hipSuccess) return e;
@@ -1133,7 +1133,7 @@ static hipError_t launch_chunk_t(const ChunkParams& p, int nslots, hipStream_t s
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     // exact path: about 512 workgroups (two per CU), each over up to 64 chunk-heads
-    auto kx = ckda_chunk_exact_kernel<Tin, DK, DV, HG, NQK, MODE>;
+    auto kx = ckda_chunk_exact_kernel<Tin, DK, DV, HG, NQK, MODE, GM>;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kx), hipFuncAttributeMaxDynamicSharedMemorySize, LDS_EX);
     if (e != hipSuccess) return e;
     const int per = static_cast<int>(grid > 512 * 64LL ? 64 : (grid + 511) / 512);
@@ -1141,6 +1141,14 @@ static hipError_t launch_chunk_t(const ChunkParams& p, int nslots, hipStream_t s
     hipLaunchKernelGGL(kx, dim3(static_cast<unsigned>(gx)), dim3(SH::NW * 64), LDS_EX, stream, p,
                        static_cast<int>(grid), per);
     return hipGetLastError();
+}
+
+// the optional gate map as a template parameter: the plain kernels carry none
+// of its code
+template <typename Tin, int DK, int DV, bool HG, bool NQK, int MODE>
+static hipError_t launch_chunk_t(const ChunkParams& p, int nslots, hipStream_t stream) {
+    return p.gate_map ? launch_chunk_g<Tin, DK, DV, HG, NQK, MODE, true>(p, nslots, stream)
+                      : launch_chunk_g<Tin, DK, DV, HG, NQK, MODE, false>(p, nslots, stream);
 }
 
 template <typename Tin, int MODE>
