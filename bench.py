@@ -278,17 +278,28 @@ def bench_bwd(torch, steps, warmup):
     tok = w.tok
     d = {k: dev_tensor(torch, getattr(tok, k)) for k in ("q", "k", "v", "g", "s", "beta")}
     do = dev_tensor(torch, w.do)
-    _, _, hc = ckda.fwd(**d, want_ckpt=True)
     B, T, H, DK = tok.q.shape
+    # the forward with checkpoints, its workspace (chunk records) kept for the
+    # backward that reads them
+    fws = torch.empty(ckda.fwd_workspace_bytes(B, T, H, DK, DK, torch.bfloat16), dtype=torch.uint8, device="cuda:0")
+    fwd_ck = lambda: ckda.fwd(**d, want_ckpt=True, workspace=fws)
+    _, _, hc = fwd_ck()
     ws = torch.empty(ckda.bwd_workspace_bytes(B, T, H, DK, DK, ckpt_given=True), dtype=torch.uint8, device="cuda:0")
     fn = lambda: ckda.bwd(**d, h_ckpt=hc, do=do, workspace=ws)
+    fn_rec = lambda: ckda.bwd(**d, h_ckpt=hc, do=do, workspace=ws, fwd_workspace=fws)
     log("timing backward")
     wall, per = time_kernel_launches(torch, fn, steps, warmup)
+    log("timing backward reading the forward's records")
+    wall_rec, _ = time_kernel_launches(torch, fn_rec, steps, warmup)
+    log("timing the forward with checkpoints")
+    wall_fck, _ = time_kernel_launches(torch, fwd_ck, steps, warmup)
     th = B * T * H
     ms = wall / steps
+    ms_rec = wall_rec / steps
     return dict(ms=ms, tokens_per_s=B * T / (ms * 1e-3), bytes=th * BWD_BYTES_PER_TOKEN_HEAD,
                 gbs=th * BWD_BYTES_PER_TOKEN_HEAD / (ms * 1e-3) / 1e9,
-                workspace_bytes=int(ws.numel()))
+                workspace_bytes=int(ws.numel()), ms_with_fwd_records=ms_rec,
+                fwd_ckpt_ms=wall_fck / steps, fwd_records_bytes=int(fws.numel()))
 
 
 def bench_bwd_long(torch, steps=2, warmup=1):
@@ -514,7 +525,17 @@ def main():
                      "unit": "tokens/s", "value": bw["tokens_per_s"], "ms": bw["ms"],
                      "algorithmic_bytes": bw["bytes"], "achieved_gbs": bw["gbs"],
                      "frac_of_hbm_peak": bw["gbs"] / HBM_PEAK_GBS, "workspace_bytes": bw["workspace_bytes"],
-                     "traffic": measured_traffic(BWD_TRAFFIC_FILE)},
+                     "traffic": measured_traffic(BWD_TRAFFIC_FILE),
+                     "with_forward_records": {
+                         "ms": bw["ms_with_fwd_records"],
+                         "frac_of_hbm_peak": bw["bytes"] / (bw["ms_with_fwd_records"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "basis": "ckda_bwd_with_records: the backward reads the chunk records the forward with "
+                                  "checkpoints left in its workspace (kept between the calls) instead of writing "
+                                  "its own",
+                         "kept_bytes": bw["fwd_records_bytes"]},
+                     "training_step_ms": {"forward_with_checkpoints": bw["fwd_ckpt_ms"],
+                                          "plus_backward": bw["fwd_ckpt_ms"] + bw["ms"],
+                                          "plus_backward_with_forward_records": bw["fwd_ckpt_ms"] + bw["ms_with_fwd_records"]}},
         "forward_head_gate": {"workload": "layer_bf16_head_gate: layer_bf16 with one signed gate per "
                                           "(token, head) (g f32, s int8 [B,T,H])",
                               "unit": "tokens/s", "value": fh["tokens"] / (fh["ms"] * 1e-3), "ms": fh["ms"],

@@ -69,6 +69,9 @@ def lib() -> ctypes.CDLL:
     L.ckda_bwd.argtypes = [I, I, I, I, I, I, U, P, P, P, P, P, P, F, P, P, P, P,
                            P, P, P, P, P, P, P, S, P]
     L.ckda_bwd.restype = I
+    L.ckda_bwd_with_records.argtypes = [I, I, I, I, I, I, U, P, P, P, P, P, P, F, P, P, P, S, P, P,
+                                        P, P, P, P, P, P, P, S, P]
+    L.ckda_bwd_with_records.restype = I
     L.ckda_bwd_varlen_workspace_bytes.argtypes = [I, I, I, I, I]
     L.ckda_bwd_varlen_workspace_bytes.restype = S
     L.ckda_bwd_varlen_workspace_bytes_given_ckpt.argtypes = [I, I, I, I, I]
@@ -76,6 +79,9 @@ def lib() -> ctypes.CDLL:
     L.ckda_bwd_varlen.argtypes = [I, I, P, P, I, I, I, I, U, P, P, P, P, P, P, F, P, P, P, P,
                                   P, P, P, P, P, P, P, S, P]
     L.ckda_bwd_varlen.restype = I
+    L.ckda_bwd_varlen_with_records.argtypes = [I, I, P, P, I, I, I, I, U, P, P, P, P, P, P, F, P, P, P, S, P, P,
+                                               P, P, P, P, P, P, P, S, P]
+    L.ckda_bwd_varlen_with_records.restype = I
     L.ckda_set_segment_chunks.argtypes = [I]
     L.ckda_set_segment_chunks.restype = I
     L.ckda_short_conv_fwd.argtypes = [I, I, P, P, I, I, U, P, P, P, P, P, P]
@@ -312,10 +318,13 @@ def bwd_workspace_bytes(B, T, H, DK, DV, ckpt_given: bool = False) -> int:
 
 
 def bwd(q, k, v, g, s, beta, h_ckpt, do, scale: float = 1.0, h0=None, dht=None,
-        want_dh0: bool = True, workspace=None, qk_norm: bool = False, gate_map: bool = False):
+        want_dh0: bool = True, workspace=None, qk_norm: bool = False, gate_map: bool = False,
+        fwd_workspace=None):
     """Backward (ckda_bwd).  h_ckpt: the checkpoints of fwd(..., want_ckpt=True)
-    on the same inputs, or None (the call recomputes them).  Returns dict dq,
-    dk, dv, dg, dbeta, dh0 (f32)."""
+    on the same inputs, or None (the call recomputes them).  fwd_workspace:
+    that forward call's workspace, kept unchanged (ckda_bwd_with_records: the
+    backward reads its chunk records instead of writing its own).  Returns
+    dict dq, dk, dv, dg, dbeta, dh0 (f32)."""
     B, T = q.shape[0], q.shape[1]
     dt, H, DK, DV, dev = _token_inputs(q, k, v, g, s, beta, (B, T))
     NT = (T + CHUNK - 1) // CHUNK
@@ -333,6 +342,15 @@ def bwd(q, k, v, g, s, beta, h_ckpt, do, scale: float = 1.0, h0=None, dht=None,
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if fwd_workspace is not None:
+        _need(fwd_workspace, "fwd_workspace", device=dev)
+        fb = fwd_workspace.numel() * fwd_workspace.element_size()
+        _check(lib().ckda_bwd_with_records(
+            B, T, H, DK, DV, dt, _flags(g, (B, T), qk_norm, gate_map), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
+            _ptr(beta), float(scale), _ptr(h0), _ptr(h_ckpt), _ptr(fwd_workspace), ctypes.c_size_t(fb), _ptr(do),
+            _ptr(dht), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
+            _ptr(out["dh0"]), _ptr(workspace), ctypes.c_size_t(wsb), _stream()))
+        return out
     _check(lib().ckda_bwd(B, T, H, DK, DV, dt, _flags(g, (B, T), qk_norm, gate_map), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(s),
                           _ptr(beta), float(scale), _ptr(h0), _ptr(h_ckpt), _ptr(do), _ptr(dht),
                           _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
@@ -346,10 +364,12 @@ def bwd_varlen_workspace_bytes(N, T_total, H, DK, DV, ckpt_given: bool = False) 
 
 
 def bwd_varlen(q, k, v, g, s, beta, cu_seqlens, h_ckpt, do, scale: float = 1.0, h0=None, dht=None,
-               want_dh0: bool = True, cu_seqlens_dev=None, workspace=None, qk_norm: bool = False, gate_map: bool = False):
+               want_dh0: bool = True, cu_seqlens_dev=None, workspace=None, qk_norm: bool = False, gate_map: bool = False,
+               fwd_workspace=None):
     """Backward of the packed-document forward (ckda_bwd_varlen).  Shapes as
     in fwd_varlen; h_ckpt from fwd_varlen(..., want_ckpt=True), or None
-    (recomputed); do
+    (recomputed); fwd_workspace: that call's workspace, kept unchanged
+    (ckda_bwd_varlen_with_records); do
     [T_total,H,DV]; dht, dh0 [N,H,DK,DV].  Returns dict dq, dk, dv, dg,
     dbeta, dh0 (f32)."""
     if q.dim() == 4:
@@ -376,6 +396,15 @@ def bwd_varlen(q, k, v, g, s, beta, cu_seqlens, h_ckpt, do, scale: float = 1.0, 
                dh0=torch.empty((N, H, DK, DV), **f32) if want_dh0 else None)
     workspace, wsb = _workspace(workspace, bwd_varlen_workspace_bytes(N, Tt, H, DK, DV, ckpt_given=h_ckpt is not None),
                                 dev)
+    if fwd_workspace is not None:
+        _need(fwd_workspace, "fwd_workspace", device=dev)
+        fb = fwd_workspace.numel() * fwd_workspace.element_size()
+        _check(lib().ckda_bwd_varlen_with_records(
+            N, Tt, _ptr(cu), _ptr(cu_seqlens_dev), H, DK, DV, dt, _flags(g, (Tt,), qk_norm, gate_map), _ptr(q), _ptr(k),
+            _ptr(v), _ptr(g), _ptr(s), _ptr(beta), float(scale), _ptr(h0), _ptr(h_ckpt), _ptr(fwd_workspace),
+            ctypes.c_size_t(fb), _ptr(do), _ptr(dht), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+            _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dh0"]), _ptr(workspace), ctypes.c_size_t(wsb), _stream()))
+        return out
     _check(lib().ckda_bwd_varlen(N, Tt, _ptr(cu), _ptr(cu_seqlens_dev), H, DK, DV, dt, _flags(g, (Tt,), qk_norm, gate_map),
                                  _ptr(q),
                                  _ptr(k), _ptr(v), _ptr(g), _ptr(s), _ptr(beta), float(scale),

@@ -423,6 +423,22 @@ size_t ckda_bwd_varlen_workspace_bytes_given_ckpt(int N, int T_total, int H, int
 
 namespace {
 
+// the forward's workspace as the backward's reverse records: checkpoints
+// given, the records' whole area present and aligned
+ckda_status_t check_fwd_records(ckda::BwdArgs& a, int nslots, bool any_tokens, const void* fwd_ws, size_t fwd_ws_bytes) {
+    if (!any_tokens) return CKDA_OK;
+    if (!a.h_ckpt)
+        return fail(CKDA_ERR_NULL, "the forward records go with that call's checkpoints: h_ckpt is NULL");
+    CKDA_REQUIRE(fwd_ws);
+    CKDA_ALIGNED(fwd_ws);
+    const size_t need = ckda::fwd_workspace_bytes(nslots, a.H, a.DK, a.DV, a.bf16);
+    if (fwd_ws_bytes < need)
+        return fail(CKDA_ERR_WORKSPACE, "forward workspace %zu bytes, its records take %zu", fwd_ws_bytes, need);
+    a.fwd_records = fwd_ws;
+    a.fwd_records_bytes = need;
+    return CKDA_OK;
+}
+
 // shared tail of ckda_bwd / ckda_bwd_varlen: pointer checks, workspace, launch
 ckda_status_t bwd_common(ckda::BwdArgs& a, int nslots, bool any_tokens, const void* workspace,
                          size_t workspace_bytes, ckda_stream_t stream, const char* what) {
@@ -459,7 +475,7 @@ ckda_status_t bwd_common(ckda::BwdArgs& a, int nslots, bool any_tokens, const vo
                                  {a.dh0, st, "dh0"}, {workspace, workspace_bytes, "workspace"}},
                                 {{a.q, tb.qk, "q"}, {a.k, tb.qk, "k"}, {a.v, tb.v, "v"}, {a.g, tb.g, "g"}, {a.s, tb.s, "s"},
                                  {a.beta, tb.beta, "beta"}, {a.h0, st, "h0"}, {a.h_ckpt, ck, "h_ckpt"},
-                                 {a.dout, dob, "dout"}, {a.dht, st, "dht"},
+                                 {a.dout, dob, "dout"}, {a.dht, st, "dht"}, {a.fwd_records, a.fwd_records_bytes, "fwd_workspace"},
                                  {a.cu, a.cu ? (static_cast<size_t>(a.ndocs) + 1) * 4 : 0, "cu_seqlens"}}));
     }
     return hip_status(ckda::launch_bwd(a, nslots, static_cast<hipStream_t>(stream)), what);
@@ -467,12 +483,13 @@ ckda_status_t bwd_common(ckda::BwdArgs& a, int nslots, bool any_tokens, const vo
 
 }  // namespace
 
-ckda_status_t ckda_bwd(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype, ckda_flags_t flags,
-                       const void* q, const void* k, const void* v, const float* g, const int8_t* s,
-                       const float* beta, float scale, const float* h0, const float* h_ckpt,
-                       const void* dout, const float* dht, float* dq, float* dk, float* dv,
-                       float* dg, float* dbeta, float* dh0, void* workspace, size_t workspace_bytes,
-                       ckda_stream_t stream) {
+static ckda_status_t bwd_equal(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype, ckda_flags_t flags,
+                               const void* q, const void* k, const void* v, const float* g, const int8_t* s,
+                               const float* beta, float scale, const float* h0, const float* h_ckpt,
+                               const void* fwd_ws, size_t fwd_ws_bytes, bool with_records,
+                               const void* dout, const float* dht, float* dq, float* dk, float* dv,
+                               float* dg, float* dbeta, float* dh0, void* workspace, size_t workspace_bytes,
+                               ckda_stream_t stream) {
     CKDA_TRY(check_dtype(in_dtype));
     CKDA_TRY(check_flags(flags));
     if (B < 0 || T < 0 || H < 0) return fail(CKDA_ERR_SHAPE, "negative size (B=%d, T=%d, H=%d)", B, T, H);
@@ -489,14 +506,38 @@ ckda_status_t ckda_bwd(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtyp
     a.q = q; a.k = k; a.v = v; a.g = g; a.s = s ? s : reinterpret_cast<const int8_t*>(g); a.beta = beta; a.scale = scale; a.h0 = h0;
     a.h_ckpt = h_ckpt; a.dout = dout; a.dht = dht; a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg;
     a.dbeta = dbeta; a.dh0 = dh0; a.cu = nullptr; a.ndocs = 0;
-    return bwd_common(a, fwd_slots(B, T), T > 0, workspace, workspace_bytes, stream, "ckda_bwd launch");
+    if (with_records) CKDA_TRY(check_fwd_records(a, fwd_slots(B, T), T > 0, fwd_ws, fwd_ws_bytes));
+    return bwd_common(a, fwd_slots(B, T), T > 0, workspace, workspace_bytes, stream,
+                      with_records ? "ckda_bwd_with_records launch" : "ckda_bwd launch");
 }
 
-ckda_status_t ckda_bwd_varlen(int N, int T_total, const int32_t* cu, const int32_t* cu_dev, int H,
+ckda_status_t ckda_bwd(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype, ckda_flags_t flags,
+                       const void* q, const void* k, const void* v, const float* g, const int8_t* s,
+                       const float* beta, float scale, const float* h0, const float* h_ckpt,
+                       const void* dout, const float* dht, float* dq, float* dk, float* dv,
+                       float* dg, float* dbeta, float* dh0, void* workspace, size_t workspace_bytes,
+                       ckda_stream_t stream) {
+    return bwd_equal(B, T, H, DK, DV, in_dtype, flags, q, k, v, g, s, beta, scale, h0, h_ckpt, nullptr, 0, false,
+                     dout, dht, dq, dk, dv, dg, dbeta, dh0, workspace, workspace_bytes, stream);
+}
+
+ckda_status_t ckda_bwd_with_records(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype, ckda_flags_t flags,
+                                    const void* q, const void* k, const void* v, const float* g, const int8_t* s,
+                                    const float* beta, float scale, const float* h0, const float* h_ckpt,
+                                    const void* fwd_workspace, size_t fwd_workspace_bytes, const void* dout,
+                                    const float* dht, float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                                    float* dh0, void* workspace, size_t workspace_bytes, ckda_stream_t stream) {
+    return bwd_equal(B, T, H, DK, DV, in_dtype, flags, q, k, v, g, s, beta, scale, h0, h_ckpt, fwd_workspace,
+                     fwd_workspace_bytes, true, dout, dht, dq, dk, dv, dg, dbeta, dh0, workspace, workspace_bytes,
+                     stream);
+}
+
+static ckda_status_t bwd_docs(int N, int T_total, const int32_t* cu, const int32_t* cu_dev, int H,
                               int DK, int DV, ckda_dtype_t in_dtype, ckda_flags_t flags, const void* q,
                               const void* k,
                               const void* v, const float* g, const int8_t* s, const float* beta,
-                              float scale, const float* h0, const float* h_ckpt, const void* dout,
+                              float scale, const float* h0, const float* h_ckpt,
+                              const void* fwd_ws, size_t fwd_ws_bytes, bool with_records, const void* dout,
                               const float* dht, float* dq, float* dk, float* dv, float* dg,
                               float* dbeta, float* dh0, void* workspace, size_t workspace_bytes,
                               ckda_stream_t stream) {
@@ -515,8 +556,33 @@ ckda_status_t ckda_bwd_varlen(int N, int T_total, const int32_t* cu, const int32
     a.q = q; a.k = k; a.v = v; a.g = g; a.s = s ? s : reinterpret_cast<const int8_t*>(g); a.beta = beta; a.scale = scale; a.h0 = h0;
     a.h_ckpt = h_ckpt; a.dout = dout; a.dht = dht; a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg;
     a.dbeta = dbeta; a.dh0 = dh0; a.cu = cu_dev; a.cu_host = cu; a.ndocs = N;
+    if (with_records) CKDA_TRY(check_fwd_records(a, varlen_slots(N, T_total), T_total > 0, fwd_ws, fwd_ws_bytes));
     return bwd_common(a, varlen_slots(N, T_total), T_total > 0, workspace, workspace_bytes, stream,
-                      "ckda_bwd_varlen launch");
+                      with_records ? "ckda_bwd_varlen_with_records launch" : "ckda_bwd_varlen launch");
+}
+
+ckda_status_t ckda_bwd_varlen(int N, int T_total, const int32_t* cu, const int32_t* cu_dev, int H,
+                              int DK, int DV, ckda_dtype_t in_dtype, ckda_flags_t flags, const void* q,
+                              const void* k, const void* v, const float* g, const int8_t* s, const float* beta,
+                              float scale, const float* h0, const float* h_ckpt, const void* dout,
+                              const float* dht, float* dq, float* dk, float* dv, float* dg,
+                              float* dbeta, float* dh0, void* workspace, size_t workspace_bytes,
+                              ckda_stream_t stream) {
+    return bwd_docs(N, T_total, cu, cu_dev, H, DK, DV, in_dtype, flags, q, k, v, g, s, beta, scale, h0, h_ckpt,
+                    nullptr, 0, false, dout, dht, dq, dk, dv, dg, dbeta, dh0, workspace, workspace_bytes, stream);
+}
+
+ckda_status_t ckda_bwd_varlen_with_records(int N, int T_total, const int32_t* cu, const int32_t* cu_dev, int H,
+                                           int DK, int DV, ckda_dtype_t in_dtype, ckda_flags_t flags,
+                                           const void* q, const void* k, const void* v, const float* g,
+                                           const int8_t* s, const float* beta, float scale, const float* h0,
+                                           const float* h_ckpt, const void* fwd_workspace,
+                                           size_t fwd_workspace_bytes, const void* dout, const float* dht,
+                                           float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0,
+                                           void* workspace, size_t workspace_bytes, ckda_stream_t stream) {
+    return bwd_docs(N, T_total, cu, cu_dev, H, DK, DV, in_dtype, flags, q, k, v, g, s, beta, scale, h0, h_ckpt,
+                    fwd_workspace, fwd_workspace_bytes, true, dout, dht, dq, dk, dv, dg, dbeta, dh0, workspace,
+                    workspace_bytes, stream);
 }
 
 

@@ -61,6 +61,26 @@ struct BwdLayout {
     }
 };
 
+// the forward records' flag words (chunks outside the anchors' envelope) as
+// the flag array the gradient phases read
+__global__ void gather_flags_kernel(const unsigned char* rec, size_t bytes, size_t flag_off, uint32_t* flags, int n) {
+    const int i = blockIdx.x * 256 + static_cast<int>(threadIdx.x);
+    if (i < n) flags[i] = *reinterpret_cast<const uint32_t*>(rec + static_cast<size_t>(i) * bytes + flag_off);
+}
+
+void fwd_record_geometry(int DK, int DV, bool bf16, size_t& bytes, size_t& flag_off) {
+    bytes = flag_off = 0;
+#define CKDA_FRG(DK_, DV_)                                                                                  \
+    if (DK == DK_ && DV == DV_) {                                                                          \
+        bytes = bf16 ? Record<DK_, DV_, false>::BYTES : Record<DK_, DV_, true>::BYTES;                     \
+        flag_off = bf16 ? Record<DK_, DV_, false>::OFF_FLAG : Record<DK_, DV_, true>::OFF_FLAG;            \
+    }
+    CKDA_FRG(32, 32) CKDA_FRG(32, 64) CKDA_FRG(32, 128)
+    CKDA_FRG(64, 32) CKDA_FRG(64, 64) CKDA_FRG(64, 128)
+    CKDA_FRG(128, 32) CKDA_FRG(128, 64) CKDA_FRG(128, 128)
+#undef CKDA_FRG
+}
+
 __global__ void copy_or_zero_kernel(float* dst, const float* src, size_t n) {
     for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
          i += static_cast<size_t>(gridDim.x) * blockDim.x)
@@ -131,9 +151,23 @@ hipError_t launch_bwd(const BwdArgs& a, int nslots, hipStream_t st) {
         ck = r.h_ckpt;
     }
     f.ws = ws;
-    CKDA_CHECK(launch_chunk_rev(f, flags, nslots, st));
     RevParams rp{};
-    rp.ws = ws; rp.dout = a.dout; rp.dht = a.dht; rp.dh0 = a.dh0; rp.dU = du; rp.G = gg;
+    if (a.fwd_records) {
+        // the forward's own records: the reverse pass stages them transposed,
+        // and their flags become the gradient phases' flag array
+        size_t rb, fo;
+        fwd_record_geometry(DK, DV, a.bf16, rb, fo);
+        hipLaunchKernelGGL(gather_flags_kernel, dim3(static_cast<unsigned>((NC + 255) / 256)), dim3(256), 0, st,
+                           static_cast<const unsigned char*>(a.fwd_records), rb, fo, flags, NC);
+        CKDA_CHECK(hipGetLastError());
+        rp.ws = static_cast<const unsigned char*>(a.fwd_records);
+        rp.fr = 1;
+    } else {
+        CKDA_CHECK(launch_chunk_rev(f, flags, nslots, st));
+        rp.ws = ws;
+        rp.fr = 0;
+    }
+    rp.dout = a.dout; rp.dht = a.dht; rp.dh0 = a.dh0; rp.dU = du; rp.G = gg;
     rp.cu = a.cu; rp.scale = a.scale; rp.B = a.B; rp.T = a.T; rp.H = a.H; rp.ndocs = a.ndocs;
     {   // segmented reverse pass when the plan takes it and the workspace has room
         const bool varlen = a.cu != nullptr;

@@ -103,6 +103,8 @@ hipError_t launch_grad2(const FwdArgs& a, const Grad2Args& g, int nslots, hipStr
 // launch_chunk_rev: one chain per (sequence or document, head)
 struct RevParams {
     const unsigned char* ws;   // reverse records, [slot][H] blocks of rev_record_bytes
+                               // (fr: the forward's chunk records, [slot][H] Records)
+    int fr;
     const void* dout;          // dO [.., T, H, DV] (input dtype)
     const float* dht;          // [chains][H][DK][DV] or nullptr (zero)
     float* dh0;                // [chains][H][DK][DV] or nullptr
@@ -147,6 +149,10 @@ struct BwdArgs {
     int ndocs;
     void* ws;          // at least bwd_workspace_bytes(nslots, ...) bytes
     size_t ws_bytes;   // its size: room beyond that enables the segmented reverse pass
+    // the chunk records of the forward call on the same inputs (its
+    // workspace), or nullptr: the backward then writes reverse records itself
+    const void* fwd_records;
+    size_t fwd_records_bytes;
 };
 // nslots: chunk slots, as for the forward; the minimum workspace
 size_t bwd_workspace_bytes(int nslots, int H, int DK, int DV);

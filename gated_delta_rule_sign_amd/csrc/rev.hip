@@ -92,6 +92,59 @@ struct RStage {
     }
 };
 
+// Transposed staging of a forward-record matrix X [SR][SC] (planes as in the
+// record) as X^T [SC][SR] in the A-operand layout RStage writes (target rows
+// TPB bytes apart, the lo plane SC rows after the hi plane).  bf16: a task
+// takes two source rows, so each target element pair (columns r, r+1) is one
+// 4-byte LDS word; fp32: one row.  Lanes take consecutive source rows, so the
+// words of one write instruction run along a target row.
+template <int SR, int SC, bool F32, int NT>
+struct TStage {
+    static constexpr int RPT = F32 ? 1 : 2;      // source rows per task
+    static constexpr int EPU = F32 ? 4 : 8;      // elements per 16-byte unit
+    static constexpr int NPL = F32 ? 1 : 2;      // planes
+    static constexpr int ES = F32 ? 4 : 2;
+    static constexpr int RG = SR / RPT, UC = SC / EPU;
+    static constexpr int TASKS = NPL * RG * UC;
+    static constexpr int N = TASKS / NT;         // tasks per thread
+    static_assert(TASKS % NT == 0, "whole tasks per thread");
+    static __device__ __forceinline__ void task(int tid, int i, int& pl, int& u, int& r0) {
+        const int q = tid + NT * i;
+        r0 = RPT * (q % RG);
+        u = (q / RG) % UC;
+        pl = q / (RG * UC);
+    }
+    static __device__ __forceinline__ void load(const unsigned char* src, int tid, int i, u32x4* v) {
+        int pl, u, r0;
+        task(tid, i, pl, u, r0);
+        const unsigned char* a = src + static_cast<size_t>(pl) * SR * SC * ES + static_cast<size_t>(r0) * SC * ES + 16 * u;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) v[r] = *reinterpret_cast<const u32x4*>(a + r * SC * ES);
+    }
+    // storage column of target column c (bf16: the A-operand permutation)
+    static __device__ __forceinline__ int scol(int c) {
+        if constexpr (F32) return c;
+        else return 32 * (c / 32) + 8 * ((c % 16) / 4) + 4 * ((c % 32) / 16) + (c % 4);
+    }
+    static __device__ __forceinline__ void store(unsigned char* dst, int tpb, int tid, int i, const u32x4* v) {
+        int pl, u, r0;
+        task(tid, i, pl, u, r0);
+        unsigned char* b = dst + (pl * SC + EPU * u) * tpb + scol(r0) * ES;
+#pragma unroll
+        for (int e = 0; e < EPU; ++e) {
+            uint32_t w;
+            if constexpr (F32) {
+                w = v[0][e];
+            } else {
+                const uint32_t a = (v[0][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                const uint32_t c = (v[1][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                w = a | (c << 16);
+            }
+            *reinterpret_cast<uint32_t*>(b + e * tpb) = w;
+        }
+    }
+};
+
 // SEG: segment mode (phase 3 with OUT, phase 1 without); otherwise (OUT set)
 // whole chains.  Segment phase 1 walks every segment but a chain's first
 // (its value columns from zero, or from dht for the chain's last segment;
@@ -99,7 +152,9 @@ struct RStage {
 // switched off) and writes the segment's start G (last segment: into the
 // previous segment's end slot), H_s or P_s; phase 3 walks every segment from
 // its end G and writes the per-chunk outputs (and dh0 at the chain's start).
-template <typename Tin, int DK, int DV, bool SEG, bool OUT>
+// FR: p.ws holds the forward's chunk records (ckda_record.h Record), staged
+// transposed; otherwise the reverse records of the backward's first pass
+template <typename Tin, int DK, int DV, bool SEG, bool OUT, bool FR>
 __global__ void __launch_bounds__(512, 2) ckda_rev_kernel(RevParams p)
 {
     using SH = RevShape<Tin, DK, DV>;
@@ -181,7 +236,78 @@ __global__ void __launch_bounds__(512, 2) ckda_rev_kernel(RevParams p)
     const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
 
     // walk step j covers chunk nloop - 1 - j
-    if (w >= 4) {
+    if (FR && w >= 4) {
+        // ============ loader waves over the forward's records (transposed) ====
+        using FRC = Record<DK, DV, SH::F32>;
+        using TKB = TStage<DK, 64, SH::F32, NT>;   // KbT [DK][64] -> KB
+        using TMT = TStage<64, 64, SH::F32, NT>;   // M -> M^T
+        using TQT = TStage<64, DK, SH::F32, NT>;   // Qh [64][DK] -> Qh^T
+        using TWT = TStage<64, DK, SH::F32, NT>;   // W -> W^T
+        using StD = RStage<1, DK * 4 / 16, 0, NT>;
+        constexpr int RPT = TKB::RPT;
+        constexpr int NKB = TKB::N * RPT, NMT = TMT::N * RPT, NQT = TQT::N * RPT, NWT = TWT::N * RPT, ND_ = StD::N;
+        constexpr int O_MT = NKB, NA = NKB + NMT;
+        constexpr int O_WT = NQT, O_D = O_WT + NWT, NB = O_D + ND_;
+        u32x4 ga[NA], gb[NB];
+#define CKDA_FREC(J) (p.ws + (static_cast<size_t>(slot0 + jbeg + nloop - 1 - (J)) * H + h) * FRC::BYTES + opaque_zero())
+#define CKDA_FLOAD_A(J)                                                                                      \
+        {                                                                                                    \
+            const unsigned char* r_ = CKDA_FREC(J);                                                          \
+            const int t_ = opaque_tid() - NT;                                                                \
+            _Pragma("unroll") for (int i_ = 0; i_ < TKB::N; ++i_) TKB::load(r_ + FRC::OFF_K, t_, i_, ga + RPT * i_); \
+            _Pragma("unroll") for (int i_ = 0; i_ < TMT::N; ++i_) TMT::load(r_ + FRC::OFF_M, t_, i_, ga + O_MT + RPT * i_); \
+        }
+#define CKDA_FLOAD_B(J)                                                                                      \
+        {                                                                                                    \
+            const unsigned char* r_ = CKDA_FREC(J);                                                          \
+            const int t_ = opaque_tid() - NT;                                                                \
+            _Pragma("unroll") for (int i_ = 0; i_ < TQT::N; ++i_) TQT::load(r_ + FRC::OFF_Q, t_, i_, gb + RPT * i_); \
+            _Pragma("unroll") for (int i_ = 0; i_ < TWT::N; ++i_) TWT::load(r_ + FRC::OFF_W, t_, i_, gb + O_WT + RPT * i_); \
+            const u32x4* d_ = reinterpret_cast<const u32x4*>(r_ + FRC::OFF_D);                              \
+            _Pragma("unroll") for (int i_ = 0; i_ < ND_; ++i_)                                               \
+                if (StD::has(t_, i_)) gb[O_D + i_] = d_[t_ + NT * i_];                                        \
+        }
+#define CKDA_FSTORE_A()                                                                                      \
+        {                                                                                                    \
+            unsigned char* const sm_ = smem + opaque_zero();                                                 \
+            const int t_ = opaque_tid() - NT;                                                                \
+            _Pragma("unroll") for (int i_ = 0; i_ < TKB::N; ++i_) TKB::store(sm_ + SH::L_KB, SH::PKB * SH::ES, t_, i_, ga + RPT * i_); \
+            _Pragma("unroll") for (int i_ = 0; i_ < TMT::N; ++i_) TMT::store(sm_ + SH::L_MT, SH::PMT * SH::ES, t_, i_, ga + O_MT + RPT * i_); \
+        }
+#define CKDA_FSTORE_B()                                                                                      \
+        {                                                                                                    \
+            unsigned char* const sm_ = smem + opaque_zero();                                                 \
+            const int t_ = opaque_tid() - NT;                                                                \
+            _Pragma("unroll") for (int i_ = 0; i_ < TQT::N; ++i_) TQT::store(sm_ + SH::L_QT, SH::PQT * SH::ES, t_, i_, gb + RPT * i_); \
+            _Pragma("unroll") for (int i_ = 0; i_ < TWT::N; ++i_) TWT::store(sm_ + SH::L_WT, SH::PWT * SH::ES, t_, i_, gb + O_WT + RPT * i_); \
+            _Pragma("unroll") for (int i_ = 0; i_ < ND_; ++i_)                                               \
+                if (StD::has(t_, i_)) *reinterpret_cast<u32x4*>(sm_ + SH::L_D + StD::lds_off(t_, i_)) = gb[O_D + i_]; \
+        }
+        if (nloop > 0) {
+            CKDA_FLOAD_A(0)
+            CKDA_FLOAD_B(0)
+            CKDA_FSTORE_A()
+            CKDA_FSTORE_B()
+            CKDA_FLOAD_A(min(1, nloop - 1))
+            CKDA_FLOAD_B(min(1, nloop - 1))
+        }
+        lds_sync();   // record of walk step 0 in LDS
+        for (int j = 0; j < nloop; ++j) {
+            lds_sync();   // X: KB, MT of step j consumed
+            CKDA_FSTORE_A()
+            CKDA_FLOAD_A(min(j + 2, nloop - 1))
+            lds_sync();   // Y: step j consumed
+            CKDA_FSTORE_B()
+            CKDA_FLOAD_B(min(j + 2, nloop - 1))
+        }
+#undef CKDA_FREC
+#undef CKDA_FLOAD_A
+#undef CKDA_FLOAD_B
+#undef CKDA_FSTORE_A
+#undef CKDA_FSTORE_B
+        return;
+    }
+    if (!FR && w >= 4) {
         // ================= loader waves (as in the forward's state pass) ======
         using StKB = RStage<NP * 64, RC::KB_ROW / 16, SH::PADB, NT>;
         using StMT = RStage<NP * 64, RC::MT_ROW / 16, SH::PADB, NT>;
@@ -430,7 +556,7 @@ template <typename Tin, int DK, int DV, bool SEG, bool OUT>
 static hipError_t launch_rev_k(const RevParams& p, long long grid, hipStream_t stream) {
     using SH = RevShape<Tin, DK, DV>;
     if (grid == 0) return hipSuccess;
-    auto kern = ckda_rev_kernel<Tin, DK, DV, SEG, OUT>;
+    auto kern = p.fr ? ckda_rev_kernel<Tin, DK, DV, SEG, OUT, true> : ckda_rev_kernel<Tin, DK, DV, SEG, OUT, false>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, SH::LDS);
     if (e != hipSuccess) return e;

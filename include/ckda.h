@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define CKDA_ABI_VERSION 11
+#define CKDA_ABI_VERSION 12
 
 /* Status codes and dtype codes travel as fixed-width integers (any value a
  * caller passes is well defined on both sides of the boundary; unknown
@@ -280,6 +280,23 @@ ckda_status_t ckda_bwd(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtyp
                        float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0,
                        void* workspace, size_t workspace_bytes, ckda_stream_t stream);
 
+/* The same backward reading the chunk records of the ckda_fwd_chunked call
+ * that wrote h_ckpt on the same inputs and flags: fwd_workspace is that
+ * call's workspace, unchanged since (its first ckda_fwd_workspace_bytes
+ * bytes hold the records; fwd_workspace_bytes at least that).  The backward
+ * then skips its own pass over the chunks that writes reverse records (the
+ * reverse pass stages the forward's records transposed), trading the memory
+ * the caller keeps between the two calls for that pass.  h_ckpt must be given.
+ * Results agree with ckda_bwd's to rounding (the two record kinds round the
+ * same quantities in different orders). */
+ckda_status_t ckda_bwd_with_records(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtype,
+                                    ckda_flags_t flags, const void* q, const void* k, const void* v,
+                                    const float* g, const int8_t* s, const float* beta, float scale,
+                                    const float* h0, const float* h_ckpt, const void* fwd_workspace,
+                                    size_t fwd_workspace_bytes, const void* dout, const float* dht,
+                                    float* dq, float* dk, float* dv, float* dg, float* dbeta, float* dh0,
+                                    void* workspace, size_t workspace_bytes, ckda_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * Backward of the varlen forward: per document n, gradients of
  * <do, o> + <dht[n], ht[n]> with documents as independent sequences.
@@ -305,6 +322,19 @@ ckda_status_t ckda_bwd_varlen(int N, int T_total, const int32_t* cu_seqlens_host
                               const float* dht, float* dq, float* dk, float* dv, float* dg,
                               float* dbeta, float* dh0, void* workspace, size_t workspace_bytes,
                               ckda_stream_t stream);
+
+/* ckda_bwd_varlen reading the records of the ckda_fwd_varlen call that wrote
+ * h_ckpt (its workspace), as ckda_bwd_with_records does. */
+ckda_status_t ckda_bwd_varlen_with_records(int N, int T_total, const int32_t* cu_seqlens_host,
+                                           const int32_t* cu_seqlens_dev, int H, int DK, int DV,
+                                           ckda_dtype_t in_dtype, ckda_flags_t flags, const void* q,
+                                           const void* k, const void* v, const float* g, const int8_t* s,
+                                           const float* beta, float scale, const float* h0,
+                                           const float* h_ckpt, const void* fwd_workspace,
+                                           size_t fwd_workspace_bytes, const void* dout, const float* dht,
+                                           float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                                           float* dh0, void* workspace, size_t workspace_bytes,
+                                           ckda_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Short convolution: the optional width-4 part of the pre-mixer prep.  The

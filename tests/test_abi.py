@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.ckda_abi_version() == 11
+    assert L.ckda_abi_version() == 12
     assert L.ckda_status_string(0) == b"ok"
     for st in range(1, 8):
         assert L.ckda_status_string(st) not in (b"ok", b"unknown status")
@@ -286,3 +286,29 @@ def test_short_conv_rejects_bad_arguments(L):
     assert L.ckda_short_conv_step(2, 8, 0, u(4), FAKE, FAKE, FAKE, FAKE, None) == 4
     assert L.ckda_short_conv_step(2, 8, 0, u(0), FAKE, FAKE, None, FAKE, None) == 1
     assert L.ckda_short_conv_step(0, 8, 0, u(0), None, None, None, None, None) == 0
+
+
+def test_backward_with_forward_records_host_checks(L):
+    """ckda_bwd_with_records: the forward's checkpoints and its whole record
+    area are required, and no output may overlap the kept forward workspace."""
+    f = ctypes.c_float(1.0)
+    u = ctypes.c_uint32
+    # one sequence of 8 tokens, one head, d = 32, fp32: one chunk record
+    # (a fp32 record: W, Qh, KbT, M, d, u and the flag word, whole 256-byte lines)
+    rec = ((64 * 32 * 3 + 64 * 64 + 32 + 64 * 32) * 4 + 4 + 255) // 256 * 256
+    dq, dk, dv, dg, db = (P(0x100000 * (i + 1)) for i in range(5))
+    ws = P(0x4000000)
+    wsb = L.ckda_bwd_workspace_bytes_given_ckpt(1, 8, 1, 32, 32)
+    def call(hc=P(0x900000), fws=P(0xA00000), fwb=BIG, dq_=dq):
+        return L.ckda_bwd_with_records(1, 8, 1, 32, 32, 0, u(0), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, f, None, hc,
+                                       fws, ctypes.c_size_t(fwb), FAKE, None, dq_, dk, dv, dg, db, None, ws,
+                                       ctypes.c_size_t(wsb), None)
+    assert call(hc=None) == 1 and b"h_ckpt" in L.ckda_last_error()
+    assert call(fws=None) == 1
+    assert call(fwb=rec - 16) == 6 and b"records" in L.ckda_last_error()
+    assert call(fwb=rec, fws=P(0xA00008)) == 4                     # misaligned
+    assert call(fwb=rec, dq_=P(0xA00000)) == 4 and b"fwd_workspace" in L.ckda_last_error()
+    cu = (ctypes.c_int32 * 2)(0, 8)
+    assert L.ckda_bwd_varlen_with_records(1, 8, cu, FAKE, 1, 32, 32, 0, u(0), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                          f, None, P(0x900000), P(0xA00000), ctypes.c_size_t(16), FAKE, None,
+                                          dq, dk, dv, dg, db, None, ws, ctypes.c_size_t(BIG), None) == 6
