@@ -96,8 +96,7 @@ struct RStage {
 // record) as X^T [SC][SR] in the A-operand layout RStage writes (target rows
 // TPB bytes apart, the lo plane SC rows after the hi plane).  bf16: a task
 // takes two source rows, so each target element pair (columns r, r+1) is one
-// 4-byte LDS word; fp32: one row.  Lanes take consecutive source rows, so the
-// words of one write instruction run along a target row.
+// 4-byte LDS word; fp32: one row.
 template <int SR, int SC, bool F32, int NT>
 struct TStage {
     static constexpr int RPT = F32 ? 1 : 2;      // source rows per task
@@ -108,10 +107,17 @@ struct TStage {
     static constexpr int TASKS = NPL * RG * UC;
     static constexpr int N = TASKS / NT;         // tasks per thread
     static_assert(TASKS % NT == 0, "whole tasks per thread");
+    // four lanes take consecutive units of one source row (64 contiguous
+    // bytes), the next lanes the following row pairs: a load instruction
+    // touches half as many cache lines as with one unit per row, for up to
+    // four target rows per bank in a write (measured on layer_bwd: 1.84 ms
+    // per backward against 1.92 ms with lanes walking row pairs only)
+    static constexpr int LU = UC < 4 ? UC : 4;
+    static_assert(UC % LU == 0, "whole lane groups per row");
     static __device__ __forceinline__ void task(int tid, int i, int& pl, int& u, int& r0) {
         const int q = tid + NT * i;
-        r0 = RPT * (q % RG);
-        u = (q / RG) % UC;
+        r0 = RPT * ((q / LU) % RG);
+        u = ((q / (LU * RG)) % (UC / LU)) * LU + q % LU;
         pl = q / (RG * UC);
     }
     static __device__ __forceinline__ void load(const unsigned char* src, int tid, int i, u32x4* v) {
