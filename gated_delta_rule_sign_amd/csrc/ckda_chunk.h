@@ -765,7 +765,9 @@ __device__ __forceinline__ void chunk_body(const ChunkParams& p, const int slot,
     // kf e^{m - b}, so KbT = that times P_L e^{b_L - m}
     if constexpr (MODE == kModeFwd) {
         for (int task = tid; task < DK * 8; task += NW * 64) {
-            const int c = task % DK, tg = task / DK;
+            // four lanes on the 8-token groups of one channel row (64
+            // contiguous bytes per plane), sixteen channels per wave
+            const int c = (task / 4) % DK, tg = 4 * (task / (4 * DK)) + task % 4;
             const float B0 = totb[c], B1 = totb[DK + c], B2 = totb[2 * DK + c], B3 = totb[3 * DK + c];
             const float m = (tg >= 4) ? (B0 + B1 + B2) : B0;
             const uint32_t pw = totp[c / 4] ^ totp[DK / 4 + c / 4] ^ totp[DK / 2 + c / 4] ^ totp[3 * (DK / 4) + c / 4];
