@@ -163,3 +163,40 @@ def test_segmented_reverse_pass_with_records():
         e = rel_max(host(r_rec[name]), host(r_own[name]))
         print(f"  {name} records vs own: {e:.2e}")
         assert e < AGREE["bf16"], (name, e)
+
+
+@pytest.mark.parametrize("option", ["head_gate", "qk_norm", "gate_map"])
+def test_with_records_and_options(option):
+    """The forward's records under each option (one gate per head, q and k
+    normalised in the path, the gate map on pre-activations) feed the same
+    gradients as the backward's own reverse records; those are held to the
+    oracle by the options' own tests."""
+    import torch
+    require_gpu()
+    from gated_delta_rule_sign_amd import ckda
+    B, T, H, DK, DV, dtype = 2, 150, 2, 128, 64, "bf16"
+    banner(f"bwd with forward records, {option}")
+    rng = np.random.default_rng(123)
+    tok = I.draw_tokens(rng, (B, T), H, DK, DV, dtype, gate="head" if option == "head_gate" else "channel",
+                        qk="raw" if option == "qk_norm" else "unit")
+    d = tok_to_dev(tok)
+    kw = {}
+    if option == "qk_norm":
+        kw["qk_norm"] = True
+    if option == "gate_map":
+        x, y = I.draw_gate_preacts(rng, (B, T, H, DK), (B, T, H))
+        d.update(g=dev_tensor(x), s=None, beta=dev_tensor(y))
+        kw["gate_map"] = True
+    h0 = dev_tensor(I.draw_state(rng, (B, H, DK, DV), 0.3))
+    do = dev_tensor(I.to_storage(rng.standard_normal((B, T, H, DV)), dtype))
+    dht = dev_tensor(rng.standard_normal((B, H, DK, DV)).astype(np.float32))
+    ws = torch.empty(ckda.fwd_workspace_bytes(B, T, H, DK, DV, d["q"].dtype), dtype=torch.uint8, device="cuda:0")
+    _, _, hc = ckda.fwd(**d, scale=0.9, h0=h0, want_ckpt=True, workspace=ws, **kw)
+    args = dict(h_ckpt=hc, do=do, scale=0.9, h0=h0, dht=dht, **kw)
+    r_rec = ckda.bwd(**d, **args, fwd_workspace=ws)
+    r_own = ckda.bwd(**d, **args)
+    torch.cuda.synchronize()
+    for name in NAMES:
+        e = rel_max(host(r_rec[name]), host(r_own[name]))
+        print(f"  {name} records vs own: {e:.2e}")
+        assert e < AGREE[dtype], (name, e)
