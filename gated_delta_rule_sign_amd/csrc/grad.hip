@@ -205,8 +205,11 @@ __device__ __forceinline__ void grad2_body(const Grad2Params& p, const int slot,
     const __amdgpu_buffer_rsrc_t rS0 = buffer_rsrc(p.h_ckpt + ck * DK * DV, DK * DV * 4);
     const __amdgpu_buffer_rsrc_t rG = buffer_rsrc(p.G + ch * DK * DV, DK * DV * 4);
     const __amdgpu_buffer_rsrc_t rdO = buffer_rsrc(static_cast<const Tin*>(p.dout) + row0 * DV, rows * DV * ES_IN);
-    const uint32_t vS = static_cast<uint32_t>(c * DV + 4 * gq) * 4;          // S0, G row c, slots 4g..
-    const uint32_t vO = static_cast<uint32_t>(n * H * DV + 4 * gq) * ES_IN;  // dO row n of a tile, slots 4g..
+    // a lane's 8 K-slots of value step kv are the 8 adjacent value columns
+    // 32 kv + 8 g .. +7 (the same in every operand), so a lane's dO row piece
+    // is one 16-byte load
+    const uint32_t vS = static_cast<uint32_t>(c * DV + 8 * gq) * 4;          // S0, G row c, columns 8g..
+    const uint32_t vO = static_cast<uint32_t>(n * H * DV + 8 * gq) * ES_IN;  // dO row n of a tile, columns 8g..
     f32x4 aQ[4], aE[4], aB[4];
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
@@ -218,23 +221,22 @@ __device__ __forceinline__ void grad2_body(const Grad2Params& p, const int slot,
     // S0, G and dO of value step kv (two 4-slot halves each), loaded one step
     // ahead of the products that use them
     constexpr int NKV = DV / 32;
-    using DOF = std::conditional_t<F32, f32x4, u32x2>;
+    using DOF = std::conditional_t<F32, f32x4, u32x4>;
     f32x4 sv[2][2], gv[2][2];
-    DOF ov[2][4][2];
+    DOF ov[2][4][F32 ? 2 : 1];
     auto load_kv = [&](int kv, int slot) {
         sv[slot][0] = __builtin_bit_cast(f32x4, buffer_load_u32x4(rS0, vS, 128 * kv));
-        sv[slot][1] = __builtin_bit_cast(f32x4, buffer_load_u32x4(rS0, vS, 128 * kv + 64));
+        sv[slot][1] = __builtin_bit_cast(f32x4, buffer_load_u32x4(rS0, vS, 128 * kv + 16));
         gv[slot][0] = __builtin_bit_cast(f32x4, buffer_load_u32x4(rG, vS, 128 * kv));
-        gv[slot][1] = __builtin_bit_cast(f32x4, buffer_load_u32x4(rG, vS, 128 * kv + 64));
+        gv[slot][1] = __builtin_bit_cast(f32x4, buffer_load_u32x4(rG, vS, 128 * kv + 16));
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
             const uint32_t so = static_cast<uint32_t>(16 * J * H * DV + 32 * kv) * ES_IN;
             if constexpr (F32) {
                 ov[slot][J][0] = __builtin_bit_cast(f32x4, buffer_load_u32x4(rdO, vO, so));
-                ov[slot][J][1] = __builtin_bit_cast(f32x4, buffer_load_u32x4(rdO, vO, so + 64));
+                ov[slot][J][1] = __builtin_bit_cast(f32x4, buffer_load_u32x4(rdO, vO, so + 16));
             } else {
-                ov[slot][J][0] = buffer_load_u32x2(rdO, vO, so);
-                ov[slot][J][1] = buffer_load_u32x2(rdO, vO, so + 32);
+                ov[slot][J][0] = buffer_load_u32x4(rdO, vO, so);
             }
         }
     };
@@ -243,7 +245,7 @@ __device__ __forceinline__ void grad2_body(const Grad2Params& p, const int slot,
     for (int kv = 0; kv < NKV; ++kv) {
         const int cur = kv & 1;
         if (kv + 1 < NKV) load_kv(kv + 1, cur ^ 1);
-        const int va = 32 * kv + 4 * gq, vb = va + 16;
+        const int va = 32 * kv + 8 * gq, vb = va + 4;
         const f32x4 s0a = sv[cur][0], s0b = sv[cur][1], ga = gv[cur][0], gb = gv[cur][1];
 #pragma unroll
         for (int e = 0; e < 4; ++e) sgs += s0a[e] * ga[e] + s0b[e] * gb[e];
@@ -255,8 +257,7 @@ __device__ __forceinline__ void grad2_body(const Grad2Params& p, const int slot,
                 Ao.a = ov[cur][J][0];
                 Ao.b = ov[cur][J][1];
             } else {
-                const u32x2 x0 = ov[cur][J][0], x1 = ov[cur][J][1];
-                Ao.hi = __builtin_bit_cast(bf16x8, u32x4{x0.x, x0.y, x1.x, x1.y});
+                Ao.hi = __builtin_bit_cast(bf16x8, ov[cur][J][0]);
                 Ao.lo = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
             }
             aQ[J] = PR::mma8(Ao, BS, aQ[J]);
