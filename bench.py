@@ -473,8 +473,11 @@ def main():
     bwl = bench_bwd_long(torch)
     cv = bench_conv(torch, args.steps, args.warmup)
     cpu = None if args.no_cpu else cpu_baseline(fw["w"])
+    cp = bench_copy(torch)
 
     achieved = fw["bytes"] / (fw["launch_ms"] * 1e-3) / 1e9
+    traffic = measured_traffic()
+    traffic_gbs = None if traffic is None else traffic / (fw["launch_ms"] * 1e-3) / 1e9
     value = fw["tokens"] / (fw["ms"] * 1e-3)
     mf = measured_mfma()
     mfma_exec = None if mf is None else {
@@ -501,7 +504,12 @@ def main():
                    "B": 8, "T": 4096, "H": 16, "dk": 128, "dv": 128, "chunk": 64,
                    "inputs": "q,k,v bf16; g,beta f32; s int8", "state_and_outputs": "f32"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "traffic_gbs": traffic_gbs,
+                     "copy_gbs": cp["gbs"],
+                     "traffic_frac_of_copy": None if traffic_gbs is None else traffic_gbs / cp["gbs"],
+                     "copy_basis": "a 1 GiB device copy (torch copy_) timed in this run, read + write bytes; "
+                                   "traffic_gbs = the counted HBM bytes of one call over this run's mean launch time",
                      "kernel": "ckda_fwd_chunked call = ckda_chunk_kernel<bf16,128,128> + "
                                "ckda_state_kernel<bf16,128,128,false>",
                      "algorithmic_bytes_per_launch": fw["bytes"],
