@@ -367,8 +367,13 @@ def bench_copy(torch, nbytes=1 << 30, reps=5):
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").uniform_()
     dst = torch.empty_like(src)
     wall, per = time_kernel_launches(torch, lambda: dst.copy_(src), reps, 2)
-    return dict(bytes_read=nbytes, bytes_written=nbytes, launch_ms=float(np.mean(per)),
-                gbs=2 * nbytes / (float(np.mean(per)) * 1e-3) / 1e9)
+    copy_ms = float(np.mean(per))
+    # a write-only stream of the same size (a fill)
+    _, per_w = time_kernel_launches(torch, lambda: dst.fill_(1.0), reps, 2)
+    write_ms = float(np.mean(per_w))
+    return dict(bytes_read=nbytes, bytes_written=nbytes, launch_ms=copy_ms,
+                gbs=2 * nbytes / (copy_ms * 1e-3) / 1e9,
+                write_only_gbs=nbytes / (write_ms * 1e-3) / 1e9)
 
 
 def cpu_baseline(w, min_seconds=10.0, max_passes=8):
@@ -507,8 +512,10 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "traffic_gbs": traffic_gbs,
                      "copy_gbs": cp["gbs"],
+                     "write_only_gbs": cp["write_only_gbs"],
                      "traffic_frac_of_copy": None if traffic_gbs is None else traffic_gbs / cp["gbs"],
-                     "copy_basis": "a 1 GiB device copy (torch copy_) timed in this run, read + write bytes; "
+                     "copy_basis": "a 1 GiB device copy (torch copy_) timed in this run, read + write bytes; a 1 GiB "
+                                   "fill (write only) beside it; "
                                    "traffic_gbs = the counted HBM bytes of one call over this run's mean launch time",
                      "kernel": "ckda_fwd_chunked call = ckda_chunk_kernel<bf16,128,128> + "
                                "ckda_state_kernel<bf16,128,128,false>",
