@@ -282,8 +282,9 @@ ckda_status_t ckda_bwd(int B, int T, int H, int DK, int DV, ckda_dtype_t in_dtyp
 
 /* The same backward reading the chunk records of the ckda_fwd_chunked call
  * that wrote h_ckpt on the same inputs and flags: fwd_workspace is that
- * call's workspace, unchanged since (its first ckda_fwd_workspace_bytes
- * bytes hold the records; fwd_workspace_bytes at least that).  The backward
+ * call's workspace, unchanged since; its leading part holds the records, and
+ * fwd_workspace_bytes must cover at least that part (the least the forward
+ * itself accepts; less fails with CKDA_ERR_WORKSPACE).  The backward
  * then skips its own pass over the chunks that writes reverse records (the
  * reverse pass stages the forward's records transposed), trading the memory
  * the caller keeps between the two calls for that pass.  h_ckpt must be given.
