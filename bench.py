@@ -15,7 +15,7 @@ state pass, and the long_64k backward with and without the segmented
 reverse pass.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       [--only fwd|fwd_head_gate|fwd_qk_norm|fwd_long|bwd_long|decode|bwd|copy|conv]
+       [--only fwd|fwd_head_gate|fwd_qk_norm|fwd_long|bwd_long|decode|bwd|options|copy|conv]
 """
 from __future__ import annotations
 
@@ -302,6 +302,39 @@ def bench_bwd(torch, steps, warmup):
                 fwd_ckpt_ms=wall_fck / steps, fwd_records_bytes=int(fws.numel()))
 
 
+def bench_options(torch, steps, warmup):
+    """layer_bwd's shapes under the two options that change the per-element
+    arithmetic: the gate map (raw pre-activations x ~ 1.5 N(0,1) for the
+    gate, y ~ N(0,1) for beta, no s) and q, k normalised in the path (the
+    workload's unit rows, which the norm keeps).  Forward with checkpoints
+    and backward, each beside the plain call on the same tensors."""
+    from gated_delta_rule_sign_amd import ckda
+    from gated_delta_rule_sign_amd import inputs as I
+    log("generating layer_bwd inputs (options)")
+    w = I.make_workload("layer_bwd")
+    tok = w.tok
+    d = {k: dev_tensor(torch, getattr(tok, k)) for k in ("q", "k", "v", "g", "s", "beta")}
+    do = dev_tensor(torch, w.do)
+    B, T, H, DK = tok.q.shape
+    x, y = I.draw_gate_preacts(np.random.default_rng(2024), tuple(tok.g.shape), tuple(tok.beta.shape))
+    dm = dict(d, g=dev_tensor(torch, x), s=None, beta=dev_tensor(torch, y))
+    ws = torch.empty(ckda.bwd_workspace_bytes(B, T, H, DK, DK, ckpt_given=True), dtype=torch.uint8, device="cuda:0")
+    res = {"workload": "layer_bwd shapes (B=8, T=4096, H=16, d=128, bf16) under each option", "unit": "ms"}
+    cases = (("plain", d, {}), ("gate_map", dm, {"gate_map": True}), ("qk_norm", d, {"qk_norm": True}))
+    for name, dd, kw in cases:   # every variant loaded and run once before any is timed
+        _, _, hc = ckda.fwd(**dd, want_ckpt=True, **kw)
+        ckda.bwd(**dd, h_ckpt=hc, do=do, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    for name, dd, kw in cases:
+        log(f"timing forward and backward, {name}")
+        wall_f, _ = time_kernel_launches(torch, lambda: ckda.fwd(**dd, want_ckpt=True, **kw), steps, warmup)
+        _, _, hc = ckda.fwd(**dd, want_ckpt=True, **kw)
+        wall_b, _ = time_kernel_launches(torch, lambda: ckda.bwd(**dd, h_ckpt=hc, do=do, workspace=ws, **kw),
+                                         steps, warmup)
+        res[name] = {"fwd_ckpt_ms": wall_f / steps, "bwd_ms": wall_b / steps}
+    return res
+
+
 def bench_bwd_long(torch, steps=2, warmup=1):
     """Backward of long_64k (one 65,536-token sequence x 16 heads, bf16, a
     seeded bf16 upstream gradient): the reverse (dS) pass with the automatic
@@ -427,7 +460,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "fwd_head_gate", "fwd_qk_norm", "fwd_long", "bwd_long", "decode", "bwd",
+    ap.add_argument("--only", choices=["fwd", "fwd_head_gate", "fwd_qk_norm", "fwd_long", "bwd_long", "decode", "bwd", "options",
                                        "copy", "conv"], default=None)
     ap.add_argument("--decode-steps", type=int, default=512)
     args = ap.parse_args()
@@ -454,6 +487,9 @@ def main():
     if args.only == "bwd":
         print(json.dumps(bench_bwd(torch, args.steps, args.warmup)))
         return
+    if args.only == "options":
+        print(json.dumps(bench_options(torch, args.steps, args.warmup)))
+        return
     if args.only == "bwd_long":
         print(json.dumps(bench_bwd_long(torch)))
         return
@@ -477,6 +513,7 @@ def main():
     longs = [bench_fwd_long(torch, max(3, args.steps // 4), 3, wl) for wl in ("varlen_64k", "long_64k")]
     bwl = bench_bwd_long(torch)
     cv = bench_conv(torch, args.steps, args.warmup)
+    opt = bench_options(torch, max(3, args.steps // 4), 1)
     cpu = None if args.no_cpu else cpu_baseline(fw["w"])
     cp = bench_copy(torch)
 
@@ -566,6 +603,7 @@ def main():
         "forward_long_chains": longs,
         "backward_long_chains": bwl,
         "short_conv": cv,
+        "options": opt,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
